@@ -142,16 +142,15 @@ def gdn_linear_branch(q, k, v, a, b, n_sink: int, window: int):
     dv = vh.shape[-1]
     S = np.zeros((B, H, dk, dv))
     o = np.zeros((B, T, H, dv))
-    eye = np.eye(dk)
     for i in range(n_sink, T - window):
         ki = kh[:, i]                                   # [B,H,dk]
         vi = vh[:, i]                                   # [B,H,dv]
         ai = a[:, i][:, :, None, None]                  # [B,H,1,1]
         bi = b[:, i][:, :, None, None]
-        kkT = ki[:, :, :, None] * ki[:, :, None, :]     # [B,H,dk,dk]
-        proj = eye - bi * kkT                           # I - b k k^T
-        S = ai * np.einsum("bhij,bhjv->bhiv", proj, S) \
-            + bi * (ki[:, :, :, None] * vi[:, :, None, :])
+        # (I - b k k^T) S evaluated as S - b k (k^T S)
+        kS = np.einsum("bhk,bhkv->bhv", ki, S)          # k^T S  [B,H,dv]
+        proj_S = S - bi * (ki[:, :, :, None] * kS[:, :, None, :])
+        S = ai * proj_S + bi * (ki[:, :, :, None] * vi[:, :, None, :])
         t = i + window
         o[:, t] = np.einsum("bhkv,bhk->bhv", S, q[:, t])
     return o, S
@@ -328,10 +327,9 @@ def decode_step(q, k, v, a, b, state, k_cache, v_cache, a_cache, b_cache, pos,
             if update == "gdn":
                 ae = ac[bi, r_e][:, None, None]         # [H,1,1]
                 be = bc[bi, r_e][:, None, None]
-                kkT = ke[:, :, None] * ke[:, None, :]
-                proj = np.eye(dk)[None] - be * kkT
-                S[bi] = ae * np.einsum("hij,hjv->hiv", proj, S[bi]) \
-                    + be * (ke[:, :, None] * ve[:, None, :])
+                kS = np.einsum("hk,hkv->hv", ke, S[bi])  # k_e^T S
+                proj_S = S[bi] - be * (ke[:, :, None] * kS[:, None, :])
+                S[bi] = ae * proj_S + be * (ke[:, :, None] * ve[:, None, :])
             else:
                 S[bi] = ac[bi, r_e][:, :, None] * S[bi] \
                     + ke[:, :, None] * ve[:, None, :]
