@@ -1,0 +1,212 @@
+/*
+ * gdn_hybrid.h -- C ABI of the MI355X (gfx950) hybrid attention layer:
+ * a gated delta-rule (GDN) linear recurrence over the tokens outside a fixed
+ * cache budget, plus softmax attention over sink tokens and a sliding window,
+ * the two outputs summed; with the GLA diagonal-gate variant and the fused
+ * RoPE -> short conv -> L2 norm preparation of Q/K/V.
+ *
+ * Sources (cited by page title and section):
+ *   [P1] "The Key to Going Linear: Analysis-Driven Transformer Linearization"
+ *        (summary page of arXiv 2607.07706v1):
+ *        - 线性注意力替换机制: the GLA update S_t = G_t S_{t-1} + k_t v_t^T and
+ *          the GDN update S_t = (I - b_t k_t k_t^T) G_t S_{t-1} + b_t k_t v_t^T;
+ *        - 从 softmax 到 delta 规则的一阶近似: softmax logits q.k / sqrt(d);
+ *        - 填补近似缺口的实用设计: budget = 8 sinks (always attended) + a
+ *          sliding window; the linear path covers all other tokens;
+ *        - 实践建议 items 2-3: fixed budget split; kernel-8 short conv on
+ *          Q/K/V after RoPE and before L2 normalisation.
+ *   [P2] "線性化 Transformer 但不掉品質", section 方法到底怎麼做: sink tokens,
+ *        short convolutions, fixed-budget cache routing.
+ *   [P3] "Untangling Component Imbalance in Hybrid Linear Attention
+ *        Conversion Methods", section 核心思路: the hybrid combines a linear
+ *        branch with sliding-window softmax; linear-only / softmax-only use.
+ *
+ * Definitions used by every entry point (positions t are 0-based, budget
+ * N = n_sink + window, G = H / Hkv, query head h reads KV head h / G):
+ *   softmax set  A(t) = { i <= t : i < n_sink or i > t - window }
+ *   linear set   L(t) = { i : n_sink <= i <= t - window }
+ *   GDN  (per query head, a_i and b_i scalars):
+ *        S_i = a_i (I - b_i k_i k_i^T) S_{i-1} + b_i k_i v_i^T,  i >= n_sink
+ *   GLA  (alpha_i a d_k-vector in (0,1)): S_i = Diag(alpha_i) S_{i-1} + k_i v_i^T
+ *   o_lin[t] = S_{t-window}^T q_t   (0 while t - window < n_sink)
+ *   o_swa[t] = sum_{i in A(t)} softmax_i(q_t . k_i / sqrt(d_k)) v_i
+ *   o[t]     = o_lin[t] + o_swa[t]            (a plain sum)
+ * S is d_k x d_v (column-vector convention); the state starts at zero.
+ *
+ * Conventions of all calls:
+ *   - Every pointer is a DEVICE pointer owned by the caller; the library never
+ *     allocates, frees or retains it, and never synchronises.
+ *   - Tensors are dense, row-major (last index fastest), in the layouts given.
+ *     Outputs must not alias inputs.
+ *   - q/k/v/o and the K/V cache use `dtype` (GDN_F32 or GDN_BF16); gates a, b
+ *     and states are always fp32.  d_k = d_v = d in {64, 128}.
+ *   - `stream` is a hipStream_t (NULL: the null stream).  Calls are
+ *     asynchronous on it.
+ *   - Arguments are validated on the host before anything is launched; on an
+ *     error nothing is launched and no output is touched.  Return values:
+ *     GDN_OK, GDN_EINVAL (bad pointer/shape/flag), GDN_EUNSUPPORTED (valid
+ *     but not implemented, e.g. fp32 linear branch at d = 128),
+ *     GDN_EWORKSPACE (workspace too small), GDN_ELAUNCH (the HIP launch
+ *     failed; hipGetLastError() is reported through gdn_hybrid_last_hip_error).
+ *   - Preconditions the caller guarantees (not checked): keys and queries of
+ *     the GDN path are L2-normalised (or come from shortconv_qkv); a in (0,1],
+ *     b in [0,1]; decode positions pos[b] >= 0 and the cache/state hold the
+ *     sequence's prefix up to pos[b] - 1.
+ *   - No global mutable state besides the last HIP error code: calls are
+ *     thread-safe as far as HIP launches are.
+ */
+#ifndef GDN_HYBRID_H
+#define GDN_HYBRID_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+typedef enum { GDN_DELTA = 0, GDN_GLA = 1 } gdn_update;
+
+/* flags of gdn_hybrid_prefill / gdn_hybrid_decode */
+enum {
+  GDN_BRANCH_LINEAR = 1,   /* add o_lin to o                                   */
+  GDN_BRANCH_SOFTMAX = 2,  /* add o_swa to o                                   */
+  GDN_WRITE_STATE = 4      /* prefill only: write the final state to state_out */
+};
+
+/* flags of shortconv_qkv */
+enum { GDN_ROPE = 1, GDN_L2NORM = 2 };
+
+enum {
+  GDN_OK = 0,
+  GDN_EINVAL = -1,
+  GDN_EUNSUPPORTED = -2,
+  GDN_EWORKSPACE = -3,
+  GDN_ELAUNCH = -4
+};
+
+/* Library version as major*10000 + minor*100 + patch. */
+int gdn_hybrid_version(void);
+
+/* Static text for a return code. */
+const char* gdn_hybrid_strerror(int code);
+
+/* hipError_t of the last failed launch in this process (0 if none). */
+int gdn_hybrid_last_hip_error(void);
+
+/*
+ * Workspace bytes gdn_hybrid_prefill needs for these arguments (written to
+ * *bytes).  The current kernels need none (0): the linear branch writes its
+ * rows of o and the softmax branch adds to them in place.
+ * Errors: GDN_EINVAL if bytes is NULL or the shape arguments are invalid.
+ */
+int gdn_hybrid_prefill_workspace(int B, int T, int H, int Hkv, int dk, int dv,
+                                 int n_sink, int window, int dtype, int update,
+                                 int flags, size_t* bytes);
+
+/*
+ * Prefill of whole sequences starting at position 0 ([P1] 线性注意力替换机制,
+ * 填补近似缺口的实用设计; the sum of the two branches as defined above).
+ *
+ *   q          [B, T, H, dk]    dtype
+ *   k          [B, T, Hkv, dk]  dtype
+ *   v          [B, T, Hkv, dv]  dtype
+ *   a          GDN: [B, T, H] fp32 (scalar gate); GLA: [B, T, H, dk] fp32
+ *   b          GDN: [B, T, H] fp32; GLA: ignored (may be NULL)
+ *   o          [B, T, H, dv]    dtype, written (every row) unless flags has
+ *              neither branch bit (then it may be NULL)
+ *   state_out  [B, H, dk, dv] fp32: S after token T-1-window (zero if none),
+ *              the state a following decode step continues from; written iff
+ *              flags & GDN_WRITE_STATE (else may be NULL)
+ *   n_sink >= 0, window >= 1; flags: any non-empty combination of the
+ *   GDN_BRANCH_* / GDN_WRITE_STATE bits.
+ *   workspace / workspace_bytes: device buffer of at least the size reported
+ *   by gdn_hybrid_prefill_workspace (may be NULL / 0 when that size is 0).
+ * Supported: d in {64, 128} for bf16; the linear branch (or the state) in
+ * fp32 only at d = 64 (GDN_EUNSUPPORTED otherwise).
+ */
+int gdn_hybrid_prefill(const void* q, const void* k, const void* v,
+                       const float* a, const float* b,
+                       void* o, float* state_out,
+                       int B, int T, int H, int Hkv, int dk, int dv,
+                       int n_sink, int window, int dtype, int update, int flags,
+                       void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
+ * One decode step for B sequences, each at its own position t = pos[b]
+ * ([P1] 填补近似缺口的实用设计; [P2] fixed-budget cache routing).
+ * Per sequence: the token e = t - window leaves the window; if e >= n_sink
+ * it is folded into the state with its own cached gates; o_lin = S^T q_t;
+ * o_swa is the softmax over the sinks and the window (t-window, t], the new
+ * token included; o = o_lin + o_swa (as selected by flags); the new k, v and
+ * gates are stored in slot(t); pos[b] += 1.
+ *
+ *   q          [B, H, dk]        dtype
+ *   k, v       [B, Hkv, dk|dv]   dtype    (the new token)
+ *   a          GDN [B, H] fp32; GLA [B, H, dk] fp32
+ *   b          GDN [B, H] fp32; GLA: ignored (may be NULL)
+ *   state      [B, H, dk, dv] fp32, in/out
+ *   k_cache, v_cache [B, Hkv, n_sink + window, d] dtype, in/out.  Token i
+ *              lives in slot i if i < n_sink, else in slot
+ *              n_sink + (i - n_sink) mod window.
+ *   a_cache    GDN [B, window, H] fp32; GLA [B, window, H, dk] fp32, in/out
+ *   b_cache    GDN [B, window, H] fp32 (GLA: ignored, may be NULL), in/out.
+ *              Gates of token i >= n_sink live at ring index
+ *              (i - n_sink) mod window.
+ *   pos        [B] int32, in/out: position of the new token; incremented.
+ *   o          [B, H, dv] dtype, out
+ *   flags      GDN_BRANCH_LINEAR and/or GDN_BRANCH_SOFTMAX (the state and
+ *              cache are updated either way).
+ * Supported: d in {64, 128}; G <= 16; G * (n_sink + window) <= 12288.
+ */
+int gdn_hybrid_decode(const void* q, const void* k, const void* v,
+                      const float* a, const float* b,
+                      float* state,
+                      void* k_cache, void* v_cache,
+                      float* a_cache, float* b_cache,
+                      int* pos, void* o,
+                      int B, int H, int Hkv, int dk, int dv,
+                      int n_sink, int window, int dtype, int update, int flags,
+                      void* stream);
+
+/*
+ * Fill the decode cache after a prefill of T tokens, so decoding resumes at
+ * position T: sinks 0..min(n_sink,T)-1 and window tokens
+ * max(n_sink, T-window)..T-1 go to their slots (layouts as in
+ * gdn_hybrid_decode), their gates to their ring indices; every other slot is
+ * zeroed.  k, v, a, b are the prefill inputs (layouts of gdn_hybrid_prefill).
+ */
+int gdn_hybrid_cache_from_prefill(const void* k, const void* v,
+                                  const float* a, const float* b,
+                                  void* k_cache, void* v_cache,
+                                  float* a_cache, float* b_cache,
+                                  int B, int T, int H, int Hkv, int dk, int dv,
+                                  int n_sink, int window, int dtype, int update,
+                                  void* stream);
+
+/*
+ * Q/K/V preparation ([P1] 实践建议 item 3; [P2] short convolutions):
+ * RoPE (flags & GDN_ROPE; q and k; rotate-half pairs (j, j + d/2),
+ * inv_freq_j = rope_theta^(-2j/d), positions pos0 + t), then a causal
+ * depthwise convolution of kernel size `ksize` on q, k and v
+ * (y[t, c] = sum_{j<ksize} w[c, ksize-1-j] x[t-j, c], zero history, no bias),
+ * then (flags & GDN_L2NORM) x / sqrt(sum x^2 + 1e-6) over each head of q, k.
+ *
+ *   q, q_out   [B, T, H, d]    dtype      channel c = h * d + i
+ *   k, v, k_out, v_out [B, T, Hkv, d] dtype
+ *   wq [H*d, ksize], wk [Hkv*d, ksize], wv [Hkv*d, ksize] fp32
+ * Supported: d in {64, 128}; 1 <= ksize <= 8; rope_theta > 0; pos0 >= 0.
+ */
+int shortconv_qkv(const void* q, const void* k, const void* v,
+                  const float* wq, const float* wk, const float* wv,
+                  void* q_out, void* k_out, void* v_out,
+                  int B, int T, int H, int Hkv, int d, int ksize,
+                  float rope_theta, int pos0, int flags, int dtype,
+                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_HYBRID_H */

@@ -1,0 +1,163 @@
+"""MI355X (gfx950) hybrid attention layer: gated delta rule over the tokens
+outside a fixed budget + softmax over sinks and a sliding window, summed.
+
+This module only marshals torch tensors into the C ABI of
+``libgdn_hybrid.so`` (include/gdn_hybrid.h); every step of the layer runs in
+the library's HIP kernels on the caller's current HIP stream.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import GdnError  # noqa: F401
+
+BRANCH_LINEAR = 1
+BRANCH_SOFTMAX = 2
+WRITE_STATE = 4
+ROPE = 1
+L2NORM = 2
+
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+_UPDATES = {"gdn": 0, "gla": 1}
+
+__all__ = [
+    "hybrid_prefill", "hybrid_decode", "cache_from_prefill", "shortconv_qkv",
+    "version", "GdnError", "BRANCH_LINEAR", "BRANCH_SOFTMAX", "WRITE_STATE",
+    "ROPE", "L2NORM",
+]
+
+
+def version() -> int:
+    return _lib.load().gdn_hybrid_version()
+
+
+def _p(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _io_dtype(*ts):
+    dt = ts[0].dtype
+    for t in ts:
+        if t.dtype != dt:
+            raise ValueError("q, k, v (and outputs/caches) must share one dtype")
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    return _DTYPES[dt]
+
+
+def _f32(*ts):
+    for t in ts:
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError("gates, states and conv weights must be float32")
+
+
+def hybrid_prefill(q, k, v, a, b, n_sink: int, window: int, update: str = "gdn",
+                   flags: int = BRANCH_LINEAR | BRANCH_SOFTMAX, o=None, state_out=None):
+    """Layer output for whole sequences starting at position 0.
+
+    q [B,T,H,d], k/v [B,T,Hkv,d] (fp32 or bf16); a [B,T,H] (GLA: [B,T,H,d])
+    and b [B,T,H] fp32.  Returns (o [B,T,H,d], state [B,H,d,d] fp32 or None).
+    """
+    B, T, H, dk = q.shape
+    Hkv, dv = k.shape[2], v.shape[3]
+    dt = _io_dtype(q, k, v)
+    _f32(a, b)
+    if o is None and flags & (BRANCH_LINEAR | BRANCH_SOFTMAX):
+        o = torch.empty(B, T, H, dv, dtype=q.dtype, device=q.device)
+    if state_out is None and flags & WRITE_STATE:
+        state_out = torch.empty(B, H, dk, dv, dtype=torch.float32, device=q.device)
+    if o is not None:
+        _io_dtype(q, o)
+    _f32(state_out)
+    lib = _lib.load()
+    rc = lib.gdn_hybrid_prefill(_p(q), _p(k), _p(v), _p(a), _p(b), _p(o), _p(state_out),
+                                B, T, H, Hkv, dk, dv, n_sink, window, dt, _UPDATES[update],
+                                flags, None, 0, _stream(q))
+    _lib.check("gdn_hybrid_prefill", rc)
+    return o, state_out
+
+
+def hybrid_decode(q, k, v, a, b, state, k_cache, v_cache, a_cache, b_cache, pos,
+                  n_sink: int, window: int, update: str = "gdn",
+                  flags: int = BRANCH_LINEAR | BRANCH_SOFTMAX, o=None):
+    """One decode step for every sequence (state, caches and pos in place).
+
+    q [B,H,d]; k/v [B,Hkv,d]; a [B,H] (GLA [B,H,d]); b [B,H]; state
+    [B,H,d,d] fp32; k/v_cache [B,Hkv,n_sink+window,d]; a/b_cache
+    [B,window,H] (GLA a: [B,window,H,d]); pos [B] int32.  Returns o [B,H,d].
+    """
+    B, H, dk = q.shape
+    Hkv, dv = k.shape[1], v.shape[2]
+    dt = _io_dtype(q, k, v, k_cache, v_cache)
+    _f32(a, b, state, a_cache, b_cache)
+    if pos.dtype != torch.int32:
+        raise ValueError("pos must be int32")
+    if o is None:
+        o = torch.empty(B, H, dv, dtype=q.dtype, device=q.device)
+    lib = _lib.load()
+    rc = lib.gdn_hybrid_decode(_p(q), _p(k), _p(v), _p(a), _p(b), _p(state), _p(k_cache),
+                               _p(v_cache), _p(a_cache), _p(b_cache), _p(pos), _p(o),
+                               B, H, Hkv, dk, dv, n_sink, window, dt, _UPDATES[update], flags,
+                               _stream(q))
+    _lib.check("gdn_hybrid_decode", rc)
+    return o
+
+
+def cache_from_prefill(k, v, a, b, H: int, n_sink: int, window: int, update: str = "gdn"):
+    """Decode cache after a prefill of k/v [B,T,Hkv,d] with gates a, b.
+
+    Returns (k_cache, v_cache, a_cache, b_cache).
+    """
+    B, T, Hkv, dk = k.shape
+    dv = v.shape[3]
+    dt = _io_dtype(k, v)
+    _f32(a, b)
+    N = n_sink + window
+    dev = k.device
+    kc = torch.empty(B, Hkv, N, dk, dtype=k.dtype, device=dev)
+    vc = torch.empty(B, Hkv, N, dv, dtype=k.dtype, device=dev)
+    ac = torch.empty((B, window, H, dk) if update == "gla" else (B, window, H),
+                     dtype=torch.float32, device=dev)
+    bc = torch.empty(B, window, H, dtype=torch.float32, device=dev)
+    lib = _lib.load()
+    rc = lib.gdn_hybrid_cache_from_prefill(_p(k), _p(v), _p(a), _p(b), _p(kc), _p(vc), _p(ac),
+                                           _p(bc), B, T, H, Hkv, dk, dv, n_sink, window, dt,
+                                           _UPDATES[update], _stream(k))
+    _lib.check("gdn_hybrid_cache_from_prefill", rc)
+    return kc, vc, ac, bc
+
+
+def shortconv_qkv(q, k, v, wq, wk, wv, rope_theta: float = 1e6, pos0: int = 0,
+                  flags: int = ROPE | L2NORM, out=None):
+    """RoPE -> causal depthwise conv -> L2 norm on q, k (conv only on v).
+
+    q [B,T,H,d], k/v [B,T,Hkv,d]; wq [H*d,ks], wk/wv [Hkv*d,ks] fp32.
+    Returns (q_out, k_out, v_out).
+    """
+    B, T, H, d = q.shape
+    Hkv = k.shape[2]
+    ks = wq.shape[1]
+    dt = _io_dtype(q, k, v)
+    _f32(wq, wk, wv)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    qo, ko, vo = out
+    lib = _lib.load()
+    rc = lib.shortconv_qkv(_p(q), _p(k), _p(v), _p(wq), _p(wk), _p(wv), _p(qo), _p(ko), _p(vo),
+                           B, T, H, Hkv, d, ks, float(rope_theta), pos0, flags, dt, _stream(q))
+    _lib.check("shortconv_qkv", rc)
+    return qo, ko, vo

@@ -1,0 +1,150 @@
+// C-ABI front end of the hybrid layer library: host-side validation, then the
+// launches on the caller's stream.  See include/gdn_hybrid.h for the contract.
+
+#include "gdn_hybrid.h"
+
+#include <stdint.h>
+
+#include <atomic>
+
+#include "launch.h"
+
+namespace gdn {
+size_t linear_lds_bytes(int D, int bf16, int gla);
+}
+
+namespace {
+
+std::atomic<int> g_last_hip_error{0};
+
+int launched(hipError_t e) {
+  if (e == hipSuccess) return GDN_OK;
+  g_last_hip_error.store((int)e);
+  return GDN_ELAUNCH;
+}
+
+bool dims_ok(int B, int T, int H, int Hkv, int dk, int dv, int n_sink, int window, int dtype,
+             int update) {
+  if (B < 1 || T < 0 || H < 1 || Hkv < 1 || H % Hkv != 0) return false;
+  if (dk != dv || (dk != 64 && dk != 128)) return false;
+  if (n_sink < 0 || window < 1) return false;
+  if (dtype != GDN_F32 && dtype != GDN_BF16) return false;
+  if (update != GDN_DELTA && update != GDN_GLA) return false;
+  // index arithmetic: (b*T + t) fits int, element counts fit 2^40
+  if ((int64_t)B * T >= (int64_t)1 << 31) return false;
+  if ((int64_t)B * T * H * dk >= (int64_t)1 << 40) return false;
+  if ((int64_t)n_sink + window >= (int64_t)1 << 30) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_hybrid_version(void) { return 10000; }
+
+const char* gdn_hybrid_strerror(int code) {
+  switch (code) {
+    case GDN_OK: return "ok";
+    case GDN_EINVAL: return "invalid argument";
+    case GDN_EUNSUPPORTED: return "unsupported parameter combination";
+    case GDN_EWORKSPACE: return "workspace too small";
+    case GDN_ELAUNCH: return "HIP kernel launch failed";
+    default: return "unknown error";
+  }
+}
+
+int gdn_hybrid_last_hip_error(void) { return g_last_hip_error.load(); }
+
+int gdn_hybrid_prefill_workspace(int B, int T, int H, int Hkv, int dk, int dv, int n_sink,
+                                 int window, int dtype, int update, int flags, size_t* bytes) {
+  if (!bytes) return GDN_EINVAL;
+  if (!dims_ok(B, T, H, Hkv, dk, dv, n_sink, window, dtype, update)) return GDN_EINVAL;
+  if (flags < 1 || flags > 7) return GDN_EINVAL;
+  *bytes = 0;
+  return GDN_OK;
+}
+
+int gdn_hybrid_prefill(const void* q, const void* k, const void* v, const float* a,
+                       const float* b, void* o, float* state_out, int B, int T, int H, int Hkv,
+                       int dk, int dv, int n_sink, int window, int dtype, int update, int flags,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!dims_ok(B, T, H, Hkv, dk, dv, n_sink, window, dtype, update)) return GDN_EINVAL;
+  if (flags < 1 || flags > 7) return GDN_EINVAL;
+  const bool lin = flags & GDN_BRANCH_LINEAR;
+  const bool swa = flags & GDN_BRANCH_SOFTMAX;
+  const bool wst = flags & GDN_WRITE_STATE;
+  const bool needs_rec = lin || wst;
+  if (!q || !k || !v) return GDN_EINVAL;
+  if ((lin || swa) && !o) return GDN_EINVAL;
+  if (needs_rec && !a) return GDN_EINVAL;
+  if (needs_rec && update == GDN_DELTA && !b) return GDN_EINVAL;
+  if (wst && !state_out) return GDN_EINVAL;
+  if (needs_rec && dtype == GDN_F32 && dk != 64) return GDN_EUNSUPPORTED;
+  if (T == 0 && !wst) return GDN_OK;
+
+  gdn::PrefillArgs p{q, k, v, a, b, o, state_out, B, T, H, Hkv, dk, n_sink, window,
+                     dtype == GDN_BF16, update == GDN_GLA, flags};
+  hipStream_t s = (hipStream_t)stream;
+  const int N = n_sink + window;
+  if (wst || (lin && T > N)) {
+    int rc = launched(gdn::launch_linear_prefill(p, s));
+    if (rc) return rc;
+  }
+  if (swa) return launched(gdn::launch_swa_prefill(p, lin && T > N, s));
+  if (lin) return launched(gdn::launch_zero_head_rows(p, s));
+  return GDN_OK;
+}
+
+int gdn_hybrid_decode(const void* q, const void* k, const void* v, const float* a, const float* b,
+                      float* state, void* k_cache, void* v_cache, float* a_cache, float* b_cache,
+                      int* pos, void* o, int B, int H, int Hkv, int dk, int dv, int n_sink,
+                      int window, int dtype, int update, int flags, void* stream) {
+  if (!dims_ok(B, 1, H, Hkv, dk, dv, n_sink, window, dtype, update)) return GDN_EINVAL;
+  if (flags < 1 || flags > 3) return GDN_EINVAL;
+  if (!q || !k || !v || !a || !state || !k_cache || !v_cache || !a_cache || !pos || !o)
+    return GDN_EINVAL;
+  if (update == GDN_DELTA && (!b || !b_cache)) return GDN_EINVAL;
+  const int G = H / Hkv;
+  if (G > 16) return GDN_EUNSUPPORTED;
+  if ((int64_t)G * (n_sink + window) > 12288) return GDN_EUNSUPPORTED;
+  if (gdn::decode_lds_bytes(G, n_sink + window, dk, update == GDN_GLA) > 160 * 1024)
+    return GDN_EUNSUPPORTED;
+  gdn::DecodeArgs p{q, k, v, a, b, state, k_cache, v_cache, a_cache, b_cache, pos, o,
+                    B, H, Hkv, dk, n_sink, window, dtype == GDN_BF16, update == GDN_GLA, flags};
+  return launched(gdn::launch_decode(p, (hipStream_t)stream));
+}
+
+int gdn_hybrid_cache_from_prefill(const void* k, const void* v, const float* a, const float* b,
+                                  void* k_cache, void* v_cache, float* a_cache, float* b_cache,
+                                  int B, int T, int H, int Hkv, int dk, int dv, int n_sink,
+                                  int window, int dtype, int update, void* stream) {
+  if (!dims_ok(B, T, H, Hkv, dk, dv, n_sink, window, dtype, update)) return GDN_EINVAL;
+  if (!k_cache || !v_cache || !a_cache) return GDN_EINVAL;
+  if (update == GDN_DELTA && !b_cache) return GDN_EINVAL;
+  if (T > 0 && (!k || !v || !a)) return GDN_EINVAL;
+  if (T > 0 && update == GDN_DELTA && !b) return GDN_EINVAL;
+  gdn::CacheArgs p{k, v, a, b, k_cache, v_cache, a_cache, b_cache, B, T, H, Hkv, dk,
+                   n_sink, window, dtype == GDN_BF16, update == GDN_GLA};
+  return launched(gdn::launch_cache_from_prefill(p, (hipStream_t)stream));
+}
+
+int shortconv_qkv(const void* q, const void* k, const void* v, const float* wq, const float* wk,
+                  const float* wv, void* q_out, void* k_out, void* v_out, int B, int T, int H,
+                  int Hkv, int d, int ksize, float rope_theta, int pos0, int flags, int dtype,
+                  void* stream) {
+  if (!dims_ok(B, T, H, Hkv, d, d, 0, 1, dtype, GDN_DELTA)) return GDN_EINVAL;
+  if (!q || !k || !v || !wq || !wk || !wv || !q_out || !k_out || !v_out) return GDN_EINVAL;
+  if (ksize < 1 || ksize > 8) return GDN_EUNSUPPORTED;
+  if (flags < 0 || flags > 3) return GDN_EINVAL;
+  if ((flags & GDN_ROPE) && !(rope_theta > 0.f)) return GDN_EINVAL;
+  if (pos0 < 0 || (int64_t)pos0 + T >= (int64_t)1 << 30) return GDN_EINVAL;
+  if (T == 0) return GDN_OK;
+  gdn::ShortConvArgs p{q, k, v, wq, wk, wv, q_out, k_out, v_out, B, T, H, Hkv, d, ksize,
+                       rope_theta, pos0, flags, dtype == GDN_BF16};
+  return launched(gdn::launch_shortconv(p, (hipStream_t)stream));
+}
+
+}  // extern "C"

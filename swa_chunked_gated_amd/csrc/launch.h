@@ -1,0 +1,88 @@
+// Internal launchers shared by the kernel files and the C-ABI front end.
+// Every launcher assumes its arguments were validated by the front end.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace gdn {
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* a;
+  const float* b;
+  void* o;
+  float* state_out;
+  int B, T, H, Hkv, D;
+  int n_sink, window;
+  int bf16;     // 1: q/k/v/o are bf16, 0: fp32
+  int gla;      // 1: GLA diagonal-gate update, 0: gated delta rule
+  int flags;    // GDN_BRANCH_LINEAR | GDN_BRANCH_SOFTMAX | GDN_WRITE_STATE
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* a;
+  const float* b;
+  float* state;
+  void* k_cache;
+  void* v_cache;
+  float* a_cache;
+  float* b_cache;
+  int* pos;
+  void* o;
+  int B, H, Hkv, D;
+  int n_sink, window;
+  int bf16, gla, flags;
+};
+
+struct CacheArgs {
+  const void* k;
+  const void* v;
+  const float* a;
+  const float* b;
+  void* k_cache;
+  void* v_cache;
+  float* a_cache;
+  float* b_cache;
+  int B, T, H, Hkv, D;
+  int n_sink, window;
+  int bf16, gla;
+};
+
+struct ShortConvArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* wq;
+  const float* wk;
+  const float* wv;
+  void* q_out;
+  void* k_out;
+  void* v_out;
+  int B, T, H, Hkv, D, ksize;
+  float rope_theta;
+  int pos0, flags, bf16;
+};
+
+// Linear branch (chunked GDN or GLA): writes o rows t >= n_sink + window
+// (when the linear branch is selected) and the final state (when asked).
+hipError_t launch_linear_prefill(const PrefillArgs& a, hipStream_t s);
+// Softmax branch: writes every row of o; adds the value already in o on
+// rows t >= n_sink + window when add_linear is set.
+hipError_t launch_swa_prefill(const PrefillArgs& a, int add_linear, hipStream_t s);
+// Zero rows t < n_sink + window of o (linear-only output).
+hipError_t launch_zero_head_rows(const PrefillArgs& a, hipStream_t s);
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_cache_from_prefill(const CacheArgs& a, hipStream_t s);
+hipError_t launch_shortconv(const ShortConvArgs& a, hipStream_t s);
+
+// Dynamic LDS bytes the decode kernel needs (the front end checks the limit).
+size_t decode_lds_bytes(int G, int N, int D, int gla);
+
+}  // namespace gdn

@@ -1,0 +1,597 @@
+// Linear branch of the hybrid layer (prefill) on gfx950: chunked gated delta
+// rule, and the chunked GLA variant.
+//
+// Method (page "The Key to Going Linear: Analysis-Driven Transformer
+// Linearization"):
+//  * section 线性注意力替换机制: GDN state update S_i = a_i (I - b_i k_i k_i^T)
+//    S_{i-1} + b_i k_i v_i^T (scalar gate a_i per head); GLA update
+//    S_i = Diag(alpha_i) S_{i-1} + k_i v_i^T.
+//  * section 填补近似缺口的实用设计: the recurrence only covers tokens that
+//    have left the sink + window budget, so query t reads the state after
+//    token t - window: o_lin[t] = S^(t-window)^T q_t, for t >= n_sink + window.
+//
+// Chunk form (64 stream tokens, gates g = inclusive cumsum of log a inside
+// the chunk, gamma = exp(g), incoming state S0; derived from the recurrence
+// by unrolling it over the chunk):
+//   L_rs = b_r gamma_r/gamma_s k_r.k_s (s < r),  Tm = (I + L)^-1
+//   Wm = Tm diag(b gamma) K,  Ut = Tm diag(b) V,  U = Ut - Wm S0
+//   O  = diag(gamma) Q S0 + (gamma_r/gamma_s [s <= r] o Q K^T) U
+//   S  = gamma_C S0 + K^T diag(gamma_C / gamma) U
+// where Q holds the lag-shifted queries (rows i + window).  GLA, with
+// per-channel cumulative log-gates G:
+//   A = [s <= r] o (Q e^G)(K e^-G)^T,  O = (Q e^G) S0 + A V,
+//   S = e^{G_C} o_rows S0 + (K e^{G_C - G})^T V.
+//
+// Work split: one workgroup of 4 waves per (sequence, query head, column
+// slice of the state).  The state's d_v columns are independent in both
+// updates, so each wave owns 16 or 32 columns of S as fp32 MFMA accumulators
+// in registers for the whole sequence, and every S-dependent product of a
+// chunk is wave-local.  The S-independent chunk work (K K^T, Q K^T, the unit
+// lower-triangular inverse, Wm) is shared through LDS.  The inverse: 16x16
+// diagonal blocks by forward substitution in fp32, then the off-diagonal
+// blocks by block recursion on fp32 MFMA (exact fp32 products).
+// Chunk c+1's inputs are loaded into registers while chunk c is computed.
+
+#include <algorithm>
+
+#include "common.h"
+#include "launch.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kC = 64;          // chunk length
+constexpr int kThreads = 256;   // 4 waves
+constexpr int kSL = 68;         // fp32 stride of the 64x64 solve buffer
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// C += A(16x16) B(16x16), both fp32 row-major in LDS.
+__device__ __forceinline__ f32x4 mm16(const float* A, const float* B, f32x4 c, int l16, int lg) {
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) c = mfma4(A[l16 * kSL + 4 * kk + lg], B[(4 * kk + lg) * kSL + l16], c);
+  return c;
+}
+// C += A(16x16, LDS) Y(16x16, accumulator registers of this wave).
+__device__ __forceinline__ f32x4 mm16_acc(const float* A, const f32x4& Y, f32x4 c, int l16, int lg) {
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) c = mfma4(A[l16 * kSL + 4 * lg + kk], Y[kk], c);
+  return c;
+}
+__device__ __forceinline__ void st16(float* blk, const f32x4& x, int l16, int lg) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) blk[(4 * lg + i) * kSL + l16] = x[i];
+}
+
+template <class T, int D, int DW, bool GLA>
+struct Smem {
+  static constexpr int PAD = 16 / sizeof(T);
+  static constexpr int SK = D + PAD;        // stride of [64][D] arrays
+  static constexpr int SC = kC + PAD;       // stride of [*][64] arrays
+  static constexpr int DVS = 4 * DW;        // state columns per workgroup
+  static constexpr int nK = kC * SK;
+  static constexpr int nKT = D * SC;
+  static constexpr int nVT = DVS * SC;
+  static constexpr int nA = kC * SC;
+  // element offsets in units of T
+  static constexpr int oK = 0;
+  static constexpr int oKT = oK + nK;
+  static constexpr int oQ = oKT + nKT;
+  static constexpr int oVT = oQ + nK;
+  static constexpr int oAq = oVT + nVT;
+  static constexpr int oWm = oAq + nA;               // GDN only
+  static constexpr int oTB = oWm + (GLA ? 0 : nK);
+  static constexpr int oTBG = oTB + (GLA ? 0 : nA);
+  static constexpr int nT = oTBG + (GLA ? 0 : nA);
+  static constexpr int bytesT = ((nT * (int)sizeof(T)) + 15) / 16 * 16;
+  // fp32 part
+  static constexpr int nL = GLA ? 0 : kC * kSL;      // solve buffer
+  static constexpr int nAl = GLA ? kC * D : 0;       // GLA cumulative log-gates
+  static constexpr int nGate = GLA ? D : 3 * kC;     // GDN: g, gamma, b; GLA: G_C
+  static constexpr int bytes = bytesT + 4 * (nL + nAl + nGate);
+};
+
+template <class T, int D, int DW, bool GLA>
+__global__ __launch_bounds__(kThreads) void linear_chunk_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ a, const float* __restrict__ b, T* __restrict__ o,
+    float* __restrict__ state_out, int T_, int H, int Hkv, int n_sink, int window, int flags) {
+  using SM = Smem<T, D, DW, GLA>;
+  constexpr int SK = SM::SK;
+  constexpr int SC = SM::SC;
+  constexpr int DVS = SM::DVS;
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int NT = DW / 16;          // 16-column tiles per wave
+  constexpr int MT = D / 16;           // 16-row tiles of the state
+  constexpr int NPK = kC * D / VEC / kThreads;     // K (or Q) 16-byte pieces per thread
+  constexpr int NPV = kC * DVS / VEC / kThreads;   // V pieces per thread
+  constexpr int NPA = GLA ? kC * D / 4 / kThreads : 0;
+  static_assert(NPK >= 1 && NPV >= 1, "tile shape");
+
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  T* sT = reinterpret_cast<T*>(smem_raw);
+  T* Ks = sT + SM::oK;
+  T* KTs = sT + SM::oKT;
+  T* Qs = sT + SM::oQ;
+  T* VTs = sT + SM::oVT;
+  T* Aqs = sT + SM::oAq;
+  T* Wms = sT + SM::oWm;
+  T* TBs = sT + SM::oTB;
+  T* TBGs = sT + SM::oTBG;
+  float* sF = reinterpret_cast<float*>(smem_raw + SM::bytesT);
+  float* Lf = sF;                    // [64][kSL]  L, then Tm (GDN)
+  float* Al = sF + SM::nL;           // [64][D]    cumulative log-gates (GLA)
+  float* gate = Al + SM::nAl;        // GDN: lg[64], gam[64], bet[64]; GLA: GC[D]
+
+  const int sp = blockIdx.x;          // column slice
+  const int h = blockIdx.y;
+  const int bi = blockIdx.z;
+  const int G = H / Hkv;
+  const int g = h / G;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int l16 = lane & 15;
+  const int lg = lane >> 4;
+  const int c0 = sp * DVS;            // first state column of this workgroup
+  const int cw = DW * wv;             // first column of this wave inside the slice
+  const int iend = T_ - window;       // stream tokens are [n_sink, iend)
+  const int nch = iend > n_sink ? (iend - n_sink + kC - 1) / kC : 0;
+
+  // zero the solve buffer and the score tiles once: their strictly upper
+  // parts are never written again
+  for (int i = tid; i < SM::nA; i += kThreads) Aqs[i] = from_f32<T>(0.f);
+  if (!GLA)
+    for (int i = tid; i < SM::nL; i += kThreads) Lf[i] = 0.f;
+
+  f32x4 S[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) S[mt][nt] = zero4();
+
+  // ---------------- register prefetch of one chunk's inputs
+  typedef typename Vec16<T>::type V16;
+  V16 pk[NPK], pq[NPK], pv[NPV];
+  f32x4 pa[GLA ? NPA : 1];
+  float pg = 1.f;   // GDN: a (threads 0..63) or b (threads 64..127)
+
+  auto prefetch = [&](int c) {
+    const int i0 = n_sink + c * kC;
+#pragma unroll
+    for (int n = 0; n < NPK; ++n) {
+      const int j = tid + n * kThreads;
+      const int r = j / (D / VEC);
+      const int cc = (j % (D / VEC)) * VEC;
+      const int tok = i0 + r;
+      if (tok < iend) {
+        pk[n] = *reinterpret_cast<const V16*>(k + ((size_t)(bi * T_ + tok) * Hkv + g) * D + cc);
+        pq[n] = *reinterpret_cast<const V16*>(q + ((size_t)(bi * T_ + tok + window) * H + h) * D + cc);
+      } else {
+#pragma unroll
+        for (int x = 0; x < VEC; ++x) {
+          pk[n][x] = from_f32<T>(0.f);
+          pq[n][x] = from_f32<T>(0.f);
+        }
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NPV; ++n) {
+      const int j = tid + n * kThreads;
+      const int r = j / (DVS / VEC);
+      const int cc = (j % (DVS / VEC)) * VEC;
+      const int tok = i0 + r;
+      if (tok < iend) {
+        pv[n] = *reinterpret_cast<const V16*>(v + ((size_t)(bi * T_ + tok) * Hkv + g) * D + c0 + cc);
+      } else {
+#pragma unroll
+        for (int x = 0; x < VEC; ++x) pv[n][x] = from_f32<T>(0.f);
+      }
+    }
+    if (GLA) {
+#pragma unroll
+      for (int n = 0; n < NPA; ++n) {
+        const int j = tid + n * kThreads;
+        const int r = j / (D / 4);
+        const int cc = (j % (D / 4)) * 4;
+        const int tok = i0 + r;
+        pa[n] = tok < iend ? *reinterpret_cast<const f32x4*>(a + ((size_t)(bi * T_ + tok) * H + h) * D + cc)
+                           : f32x4{1.f, 1.f, 1.f, 1.f};
+      }
+    } else {
+      const int r = tid & 63;
+      const int tok = i0 + r;
+      if (tid < 64) pg = tok < iend ? a[(size_t)(bi * T_ + tok) * H + h] : 1.f;
+      else if (tid < 128) pg = tok < iend ? b[(size_t)(bi * T_ + tok) * H + h] : 0.f;
+    }
+  };
+
+  auto commit = [&]() {
+#pragma unroll
+    for (int n = 0; n < NPK; ++n) {
+      const int j = tid + n * kThreads;
+      const int r = j / (D / VEC);
+      const int cc = (j % (D / VEC)) * VEC;
+      *reinterpret_cast<V16*>(&Ks[r * SK + cc]) = pk[n];
+      *reinterpret_cast<V16*>(&Qs[r * SK + cc]) = pq[n];
+      if (!GLA) {
+#pragma unroll
+        for (int x = 0; x < VEC; ++x) KTs[(cc + x) * SC + r] = pk[n][x];
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NPV; ++n) {
+      const int j = tid + n * kThreads;
+      const int r = j / (DVS / VEC);
+      const int cc = (j % (DVS / VEC)) * VEC;
+#pragma unroll
+      for (int x = 0; x < VEC; ++x) VTs[(cc + x) * SC + r] = pv[n][x];
+    }
+    if (GLA) {
+#pragma unroll
+      for (int n = 0; n < NPA; ++n) {
+        const int j = tid + n * kThreads;
+        const int r = j / (D / 4);
+        const int cc = (j % (D / 4)) * 4;
+        *reinterpret_cast<f32x4*>(&Al[r * D + cc]) = pa[n];
+      }
+    } else {
+      float* lgs = gate;
+      float* gam = gate + kC;
+      float* bet = gate + 2 * kC;
+      if (tid < 64) {
+        float x = logf(pg);
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const float y = __shfl_up(x, off, 64);
+          if (lane >= off) x += y;
+        }
+        lgs[lane] = x;
+        gam[lane] = expf(x);
+      } else if (tid < 128) {
+        bet[lane] = pg;
+      }
+    }
+  };
+
+  if (nch > 0) prefetch(0);
+
+  for (int c = 0; c < nch; ++c) {
+    const int i0 = n_sink + c * kC;
+    const int Cc = min(kC, iend - i0);
+    __syncthreads();          // previous chunk's LDS reads are done
+    commit();
+    __syncthreads();
+    if (c + 1 < nch) prefetch(c + 1);
+
+    if (GLA) {
+      // ---- per-channel cumulative log gates; gate-scaled Q, K, K^T
+      float* GC = gate;
+      if (tid < D) {
+        float x = 0.f;
+        for (int r = 0; r < kC; ++r) {
+          x += logf(Al[r * D + tid]);
+          Al[r * D + tid] = x;
+        }
+        GC[tid] = x;
+      }
+      __syncthreads();
+      for (int i = tid; i < kC * D; i += kThreads) {
+        const int r = i / D;
+        const int cc = i % D;
+        const float G = Al[i];
+        const float kr = to_f32(Ks[r * SK + cc]);
+        Qs[r * SK + cc] = from_f32<T>(to_f32(Qs[r * SK + cc]) * __expf(fminf(G, 80.f)));
+        Ks[r * SK + cc] = from_f32<T>(kr * __expf(fminf(-G, 80.f)));
+        KTs[cc * SC + r] = from_f32<T>(kr * __expf(fminf(GC[cc] - G, 80.f)));
+      }
+      __syncthreads();
+      // ---- A = [s <= r] (Q e^G)(K e^-G)^T on the 10 lower tiles
+      for (int job = wv; job < 10; job += 4) {
+        int mt = 0, nt = job;
+        while (nt > mt) { nt -= mt + 1; ++mt; }
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int p = 0; p < D / 32; ++p)
+          acc = mfma(lds_frag8(&Qs[(16 * mt + l16) * SK + 32 * p + 8 * lg]),
+                     lds_frag8(&Ks[(16 * nt + l16) * SK + 32 * p + 8 * lg]), acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * mt + 4 * lg + i;
+          const int s = 16 * nt + l16;
+          Aqs[r * SC + s] = from_f32<T>(s <= r ? acc[i] : 0.f);
+        }
+      }
+      __syncthreads();
+    } else {
+      const float* lgs = gate;
+      const float* gam = gate + kC;
+      const float* bet = gate + 2 * kC;
+      // ---- K K^T -> L and Q K^T -> A on the 10 lower 16x16 tiles each
+      for (int job = wv; job < 20; job += 4) {
+        const bool isq = job >= 10;
+        int mt = 0, nt = isq ? job - 10 : job;
+        while (nt > mt) { nt -= mt + 1; ++mt; }
+        const T* X = isq ? Qs : Ks;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int p = 0; p < D / 32; ++p)
+          acc = mfma(lds_frag8(&X[(16 * mt + l16) * SK + 32 * p + 8 * lg]),
+                     lds_frag8(&Ks[(16 * nt + l16) * SK + 32 * p + 8 * lg]), acc);
+        const int s = 16 * nt + l16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * mt + 4 * lg + i;
+          const float dec = __expf(fminf(lgs[r] - lgs[s], 0.f));
+          if (isq) Aqs[r * SC + s] = from_f32<T>(s <= r ? dec * acc[i] : 0.f);
+          else Lf[r * kSL + s] = s < r ? bet[r] * dec * acc[i] : 0.f;
+        }
+      }
+      __syncthreads();
+      // ---- diagonal 16x16 blocks of (I + L)^-1 by forward substitution
+      if (wv == 0) {
+        const int blk = lane >> 4;
+        const int j = l16;
+        float* Lb = Lf + 16 * blk * kSL + 16 * blk;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float acc = r == j ? 1.f : 0.f;
+#pragma unroll
+          for (int s2 = 0; s2 < r; ++s2) acc -= Lb[r * kSL + s2] * x[s2];
+          x[r] = acc;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Lb[r * kSL + j] = x[r];
+      }
+      __syncthreads();
+      // ---- level 1: X10 = -X11 L10 X00, X32 = -X33 L32 X22
+      if (wv < 2) {
+        const int o0 = wv == 0 ? 0 : 32;
+        const float* L10 = Lf + (o0 + 16) * kSL + o0;
+        const float* X00 = Lf + o0 * kSL + o0;
+        const float* X11 = Lf + (o0 + 16) * kSL + o0 + 16;
+        f32x4 y = mm16(L10, X00, zero4(), l16, lg);
+        f32x4 xo = -mm16_acc(X11, y, zero4(), l16, lg);
+        st16(Lf + (o0 + 16) * kSL + o0, xo, l16, lg);
+      }
+      __syncthreads();
+      // ---- level 2: bottom-left 32x32 block = -X_BR (L_BL X_TL)
+      {
+        const int br = 32 + 16 * (wv >> 1);   // block row of Y / X
+        const int bc = 16 * (wv & 1);         // block column
+        // Y_{br,bc} = sum_k L_{br,k} X_{k,bc}, k over the top-left blocks >= bc
+        f32x4 y = zero4();
+        for (int kb = bc; kb < 32; kb += 16) y = mm16(Lf + br * kSL + kb, Lf + kb * kSL + bc, y, l16, lg);
+        __syncthreads();
+        st16(Lf + br * kSL + bc, y, l16, lg);
+        __syncthreads();
+        // X_{br,bc} = -sum_k X_{br,k} Y_{k,bc}, k over bottom-right blocks <= br
+        f32x4 xo = zero4();
+        for (int kb = 32; kb <= br; kb += 16) xo = mm16(Lf + br * kSL + kb, Lf + kb * kSL + bc, xo, l16, lg);
+        __syncthreads();
+        st16(Lf + br * kSL + bc, -xo, l16, lg);
+        __syncthreads();
+      }
+      // ---- Tm diag(b) and Tm diag(b gamma)
+      for (int i = tid; i < kC * kC; i += kThreads) {
+        const int r = i >> 6;
+        const int s = i & 63;
+        const float tm = Lf[r * kSL + s];
+        TBs[r * SC + s] = from_f32<T>(tm * bet[s]);
+        TBGs[r * SC + s] = from_f32<T>(tm * bet[s] * gam[s]);
+      }
+      __syncthreads();
+      // ---- Wm^T = K^T (Tm diag(b gamma))^T, stored as -Wm [token][dk]
+      for (int job = wv; job < MT * 4; job += 4) {
+        const int mt = job >> 2;    // dk tile
+        const int nt = job & 3;     // token tile
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          acc = mfma(lds_frag8(&KTs[(16 * mt + l16) * SC + 32 * p + 8 * lg]),
+                     lds_frag8(&TBGs[(16 * nt + l16) * SC + 32 * p + 8 * lg]), acc);
+        store4(&Wms[(16 * nt + l16) * SK + 16 * mt + 4 * lg], -acc);
+      }
+      __syncthreads();
+    }
+
+    // ================= per-wave S-dependent products on columns [cw, cw+DW)
+    Frag<T> sf[D / 32][NT];
+#pragma unroll
+    for (int p = 0; p < D / 32; ++p)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) sf[p][nt] = frag_from_acc<T>(S[2 * p][nt], S[2 * p + 1][nt]);
+
+    f32x4 ot[NT][4];    // O^T tiles: [dv tile][query tile]
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) ot[dt][rt] = zero4();
+    // O^T = S^T Q^T (+ gate scaling) ...
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+      for (int p = 0; p < D / 32; ++p) {
+        const T* qrow = &Qs[(16 * rt + l16) * SK + 32 * p + 4 * lg];
+        Frag<T> qf = lds_frag44(qrow, qrow + 16);
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt) ot[dt][rt] = mfma(sf[p][dt], qf, ot[dt][rt]);
+      }
+    }
+
+    if (GLA) {
+      // ... + V^T A^T
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          Frag<T> af = lds_frag8(&Aqs[(16 * rt + l16) * SC + 32 * p + 8 * lg]);
+#pragma unroll
+          for (int dt = 0; dt < NT; ++dt)
+            ot[dt][rt] = mfma(lds_frag8(&VTs[(cw + 16 * dt + l16) * SC + 32 * p + 8 * lg]), af, ot[dt][rt]);
+        }
+      }
+      // S = e^{G_C} o_rows S + (K e^{G_C - G})^T V
+      const float* GC = gate;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 dec;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dec[i] = __expf(GC[16 * mt + 4 * lg + i]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) S[mt][nt] *= dec;
+      }
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        Frag<T> vf[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) vf[nt] = lds_frag8(&VTs[(cw + 16 * nt + l16) * SC + 32 * p + 8 * lg]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          Frag<T> kf = lds_frag8(&KTs[(16 * mt + l16) * SC + 32 * p + 8 * lg]);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) S[mt][nt] = mfma(kf, vf[nt], S[mt][nt]);
+        }
+      }
+    } else {
+      const float* gam = gate + kC;
+      // U = Tm diag(b) V - Wm S   (tokens x columns)
+      f32x4 U[4][NT];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) U[mt][nt] = zero4();
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          Frag<T> tf = lds_frag8(&TBs[(16 * mt + l16) * SC + 32 * p + 8 * lg]);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            U[mt][nt] = mfma(tf, lds_frag8(&VTs[(cw + 16 * nt + l16) * SC + 32 * p + 8 * lg]), U[mt][nt]);
+        }
+#pragma unroll
+        for (int p = 0; p < D / 32; ++p) {
+          const T* wrow = &Wms[(16 * mt + l16) * SK + 32 * p + 4 * lg];
+          Frag<T> wf = lds_frag44(wrow, wrow + 16);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) U[mt][nt] = mfma(wf, sf[p][nt], U[mt][nt]);
+        }
+      }
+      // O^T: scale the S^T Q^T part by gamma of each query column, then + U^T A^T
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const float gq = gam[16 * rt + l16];
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt) ot[dt][rt] *= gq;
+      }
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        Frag<T> uf[NT];
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt) uf[dt] = frag_from_acc<T>(U[2 * pp][dt], U[2 * pp + 1][dt]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const T* arow = &Aqs[(16 * rt + l16) * SC + 32 * pp + 4 * lg];
+          Frag<T> af = lds_frag44(arow, arow + 16);
+#pragma unroll
+          for (int dt = 0; dt < NT; ++dt) ot[dt][rt] = mfma(uf[dt], af, ot[dt][rt]);
+        }
+      }
+      // S = gamma_C S + K^T diag(gamma_C / gamma) U
+      const float gC = gam[kC - 1];
+      const float lgC = gate[kC - 1];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) S[mt][nt] *= gC;
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        f32x4 s0, s1;   // gamma_C / gamma_s as exp of a log difference (<= 1)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          s0[i] = __expf(fminf(lgC - gate[32 * pp + 4 * lg + i], 0.f));
+          s1[i] = __expf(fminf(lgC - gate[32 * pp + 16 + 4 * lg + i], 0.f));
+        }
+        Frag<T> uf[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) uf[nt] = frag_from_acc_scaled<T>(U[2 * pp][nt], U[2 * pp + 1][nt], s0, s1);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const T* krow = &KTs[(16 * mt + l16) * SC + 32 * pp + 4 * lg];
+          Frag<T> kf = lds_frag44(krow, krow + 16);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) S[mt][nt] = mfma(kf, uf[nt], S[mt][nt]);
+        }
+      }
+    }
+
+    // ---- store the chunk's linear output rows
+    if (flags & 1) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int r = 16 * rt + l16;
+        if (r < Cc) {
+          T* orow = o + ((size_t)(bi * T_ + i0 + r + window) * H + h) * D + c0 + cw;
+#pragma unroll
+          for (int dt = 0; dt < NT; ++dt) store4(orow + 16 * dt + 4 * lg, ot[dt][rt]);
+        }
+      }
+    }
+  }
+
+  if (flags & 4) {
+    float* Sg = state_out + (size_t)(bi * H + h) * D * D;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          Sg[(size_t)(16 * mt + 4 * lg + i) * D + c0 + cw + 16 * nt + l16] = S[mt][nt][i];
+  }
+}
+
+template <class T, int D, int DW, bool GLA>
+hipError_t launch_linear_t(const PrefillArgs& p, hipStream_t s) {
+  using SM = Smem<T, D, DW, GLA>;
+  auto kern = linear_chunk_kernel<T, D, DW, GLA>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, SM::bytes);
+  if (e != hipSuccess) return e;
+  const dim3 grid(D / (4 * DW), p.H, p.B);
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), SM::bytes, s, (const T*)p.q, (const T*)p.k,
+                     (const T*)p.v, p.a, p.b, (T*)p.o, p.state_out, p.T, p.H, p.Hkv, p.n_sink,
+                     p.window, p.flags);
+  return hipGetLastError();
+}
+
+// Columns per wave: 32 when there are enough chains to fill the GPU with one
+// workgroup per chain, else 16 (two workgroups per chain).
+template <class T, bool GLA>
+hipError_t launch_linear_d(const PrefillArgs& p, hipStream_t s) {
+  if (p.D == 64) return launch_linear_t<T, 64, 16, GLA>(p, s);
+  if ((size_t)p.B * p.H >= 256) return launch_linear_t<T, 128, 32, GLA>(p, s);
+  return launch_linear_t<T, 128, 16, GLA>(p, s);
+}
+
+}  // namespace
+
+size_t linear_lds_bytes(int D, int bf16, int gla) {
+  if (bf16) {
+    if (D == 64) return gla ? Smem<gdn::bf16, 64, 16, true>::bytes : Smem<gdn::bf16, 64, 16, false>::bytes;
+    return gla ? Smem<gdn::bf16, 128, 32, true>::bytes : Smem<gdn::bf16, 128, 32, false>::bytes;
+  }
+  if (D == 64) return gla ? Smem<float, 64, 16, true>::bytes : Smem<float, 64, 16, false>::bytes;
+  return gla ? Smem<float, 128, 32, true>::bytes : Smem<float, 128, 32, false>::bytes;
+}
+
+hipError_t launch_linear_prefill(const PrefillArgs& p, hipStream_t s) {
+  if (p.bf16) return p.gla ? launch_linear_d<bf16, true>(p, s) : launch_linear_d<bf16, false>(p, s);
+  if (p.D != 64) return hipErrorInvalidValue;   // fp32 state tiles fit LDS only at d = 64
+  return p.gla ? launch_linear_t<float, 64, 16, true>(p, s) : launch_linear_t<float, 64, 16, false>(p, s);
+}
+
+}  // namespace gdn

@@ -1,0 +1,164 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function declared in
+include/gdn_hybrid.h, and reject invalid arguments on the host with the
+documented codes before anything is launched.  Only calls that fail
+validation (or pure queries) are made here, so no GPU is touched.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn_hybrid.h")
+
+from swa_chunked_gated_amd import _lib  # noqa: E402
+
+OK, EINVAL, EUNSUP, EWS, ELAUNCH = 0, -1, -2, -3, -4
+F32, BF16 = 0, 1
+DELTA, GLA = 0, 1
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for n in ("gdn_hybrid_prefill", "gdn_hybrid_decode", "shortconv_qkv",
+              "gdn_hybrid_cache_from_prefill", "gdn_hybrid_prefill_workspace"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, n
+
+
+def test_version_and_strerror(lib):
+    assert lib.gdn_hybrid_version() >= 10000
+    for c in (OK, EINVAL, EUNSUP, EWS, ELAUNCH):
+        assert lib.gdn_hybrid_strerror(c)
+    assert lib.gdn_hybrid_strerror(123) == b"unknown error"
+
+
+def ws(lib, *args):
+    n = ctypes.c_size_t(99)
+    rc = lib.gdn_hybrid_prefill_workspace(*args, ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_query(lib):
+    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 3) == (OK, 0)
+    assert ws(lib, 1, 4096, 32, 7, 128, 128, 8, 56, BF16, DELTA, 3)[0] == EINVAL   # H % Hkv
+    assert ws(lib, 1, 4096, 32, 8, 96, 96, 8, 56, BF16, DELTA, 3)[0] == EINVAL     # d
+    assert ws(lib, 1, 4096, 32, 8, 128, 64, 8, 56, BF16, DELTA, 3)[0] == EINVAL    # dk != dv
+    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 0, BF16, DELTA, 3)[0] == EINVAL    # window
+    assert ws(lib, 1, 4096, 32, 8, 128, 128, -1, 56, BF16, DELTA, 3)[0] == EINVAL  # n_sink
+    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, 2, DELTA, 3)[0] == EINVAL      # dtype
+    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, 2, 3)[0] == EINVAL       # update
+    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 0)[0] == EINVAL   # flags
+    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 8)[0] == EINVAL
+    assert lib.gdn_hybrid_prefill_workspace(1, 64, 2, 2, 64, 64, 8, 56, 0, 0, 3, None) == EINVAL
+
+
+def prefill(lib, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, o=FAKE, st=FAKE, B=1, T=64, H=2,
+            Hkv=2, dk=64, dv=64, ns=8, w=56, dt=BF16, up=DELTA, flags=3):
+    return lib.gdn_hybrid_prefill(q, k, v, a, b, o, st, B, T, H, Hkv, dk, dv, ns, w, dt, up,
+                                  flags, None, 0, None)
+
+
+def test_prefill_validation(lib):
+    assert prefill(lib, q=None) == EINVAL
+    assert prefill(lib, k=None) == EINVAL
+    assert prefill(lib, v=None) == EINVAL
+    assert prefill(lib, o=None) == EINVAL
+    assert prefill(lib, a=None) == EINVAL                       # linear branch needs a
+    assert prefill(lib, b=None) == EINVAL                       # GDN needs b
+    assert prefill(lib, st=None, flags=7) == EINVAL             # state requested
+    assert prefill(lib, B=0) == EINVAL
+    assert prefill(lib, T=-1) == EINVAL
+    assert prefill(lib, H=3, Hkv=2) == EINVAL
+    assert prefill(lib, dk=128, dv=64) == EINVAL
+    assert prefill(lib, dk=32, dv=32) == EINVAL
+    assert prefill(lib, w=0) == EINVAL
+    assert prefill(lib, flags=0) == EINVAL
+    assert prefill(lib, flags=9) == EINVAL
+    assert prefill(lib, dt=F32, dk=128, dv=128) == EUNSUP      # fp32 linear branch at d=128
+    assert prefill(lib, dt=F32, dk=128, dv=128, flags=4) == EUNSUP
+    # fp32 softmax-only at d=128 is supported, so only the missing pointer fails here
+    assert prefill(lib, dt=F32, dk=128, dv=128, flags=2, q=None) == EINVAL
+    assert prefill(lib, B=1 << 16, T=1 << 16) == EINVAL          # B*T overflows int
+
+
+def test_prefill_zero_length_is_a_noop(lib):
+    # T = 0 with no state requested returns before any launch
+    assert prefill(lib, T=0) == OK
+
+
+def decode(lib, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, st=FAKE, kc=FAKE, vc=FAKE, ac=FAKE,
+           bc=FAKE, pos=FAKE, o=FAKE, B=2, H=4, Hkv=2, dk=128, dv=128, ns=8, w=56, dt=BF16,
+           up=DELTA, flags=3):
+    return lib.gdn_hybrid_decode(q, k, v, a, b, st, kc, vc, ac, bc, pos, o, B, H, Hkv, dk, dv,
+                                 ns, w, dt, up, flags, None)
+
+
+def test_decode_validation(lib):
+    for name in ("q", "k", "v", "a", "st", "kc", "vc", "ac", "pos", "o"):
+        assert decode(lib, **{name: None}) == EINVAL, name
+    assert decode(lib, b=None) == EINVAL
+    assert decode(lib, bc=None) == EINVAL
+    assert decode(lib, flags=0) == EINVAL
+    assert decode(lib, flags=4) == EINVAL                        # no state output in decode
+    assert decode(lib, H=5, Hkv=2) == EINVAL
+    assert decode(lib, H=34, Hkv=2) == EUNSUP                    # G = 17 > 16
+    assert decode(lib, H=16, Hkv=1, w=1000) == EUNSUP            # G * N too large
+    assert decode(lib, w=0) == EINVAL
+
+
+def shortconv(lib, q=FAKE, k=FAKE, v=FAKE, wq=FAKE, wk=FAKE, wv=FAKE, qo=FAKE, ko=FAKE, vo=FAKE,
+              B=1, T=16, H=2, Hkv=1, d=64, ks=8, theta=1e6, pos0=0, flags=3, dt=BF16):
+    return lib.shortconv_qkv(q, k, v, wq, wk, wv, qo, ko, vo, B, T, H, Hkv, d, ks, theta, pos0,
+                             flags, dt, None)
+
+
+def test_shortconv_validation(lib):
+    for name in ("q", "k", "v", "wq", "wk", "wv", "qo", "ko", "vo"):
+        assert shortconv(lib, **{name: None}) == EINVAL, name
+    assert shortconv(lib, ks=0) == EUNSUP
+    assert shortconv(lib, ks=9) == EUNSUP
+    assert shortconv(lib, d=96) == EINVAL
+    assert shortconv(lib, theta=0.0) == EINVAL
+    assert shortconv(lib, theta=0.0, flags=2, T=0) == OK           # no RoPE: theta unused
+    assert shortconv(lib, flags=4) == EINVAL
+    assert shortconv(lib, pos0=-1) == EINVAL
+    assert shortconv(lib, T=0) == OK
+
+
+def test_cache_fill_validation(lib):
+    f = lib.gdn_hybrid_cache_from_prefill
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1, 8, 2, 2, 64, 64, 8, 56, BF16, DELTA, None) == EINVAL
+    assert f(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 2, 64, 64, 8, 56, BF16, DELTA, None) == EINVAL
+    assert f(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 2, 64, 64, 8, 56, BF16, DELTA, None) == EINVAL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 3, 2, 64, 64, 8, 56, BF16, DELTA, None) == EINVAL
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError, match="not built"):
+        _lib.load()

@@ -1,0 +1,365 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Tolerances: fp32 inputs, max-abs error <= 1e-4; bf16 inputs with fp32
+state, max-abs error <= 2e-2 * max|o_ref| over the compared outputs.  Index
+masks are checked exactly (mask probe).  Full-size workloads are compared on
+sampled (sequence, head) chains and rows that the oracle computes one by one.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import swa_chunked_gated_amd as gl
+from oracle import hybrid as O
+from workloads import WORKLOADS, Workload, make_decode_inputs, make_prefill_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+ALL = gl.BRANCH_LINEAR | gl.BRANCH_SOFTMAX
+
+
+def f64(t):
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def assert_close(got, ref, fp32: bool, what=""):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    err = np.max(np.abs(got - ref)) if got.size else 0.0
+    if fp32:
+        bound = 1e-4
+    else:
+        bound = 2e-2 * max(np.max(np.abs(ref)), 1e-30)
+    assert err <= bound, f"{what}: max abs err {err:.3e} > {bound:.3e}"
+    return err
+
+
+def to_dev(inp):
+    return {k: v.to(DEV) for k, v in inp.items()}
+
+
+def small(name="s", **kw):
+    base = dict(name=name, B=2, H=4, Hkv=2, d=128, n_sink=8, window=56, T=257, sigma=0.5,
+                dtype="bf16")
+    base.update(kw)
+    return Workload(**base)
+
+
+def run_prefill(inp, w: Workload, flags=ALL | gl.WRITE_STATE):
+    o, st = gl.hybrid_prefill(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], w.n_sink,
+                              w.window, update=w.update, flags=flags)
+    torch.cuda.synchronize()
+    return o, st
+
+
+def oracle_subset(inp, w: Workload, bsel, heads, rows=None, flags=ALL | gl.WRITE_STATE):
+    """Oracle on sequences `bsel` and query heads `heads` (all in one KV group)."""
+    G = w.H // w.Hkv
+    g = heads[0] // G
+    assert all(h // G == g for h in heads)
+    q = f64(inp["q"][bsel][:, :, heads])
+    k = f64(inp["k"][bsel][:, :, g:g + 1])
+    v = f64(inp["v"][bsel][:, :, g:g + 1])
+    a = f64(inp["a"][bsel][:, :, heads])
+    b = f64(inp["b"][bsel][:, :, heads])
+    o = np.zeros(q.shape)
+    S = None
+    if flags & (gl.BRANCH_LINEAR | gl.WRITE_STATE):
+        if w.update == "gdn":
+            o_lin, S = O.gdn_linear_branch(q, k, v, a, b, w.n_sink, w.window)
+        else:
+            o_lin, S = O.gla_linear_branch(q, k, v, a, w.n_sink, w.window)
+        if flags & gl.BRANCH_LINEAR:
+            o = o + o_lin
+    if flags & gl.BRANCH_SOFTMAX:
+        o = o + O.swa_branch(q, k, v, w.n_sink, w.window, rows=rows)
+    return o, S
+
+
+# ------------------------------------------------------------------ prefill
+
+def test_tiny_fp32_layer_full():
+    w = WORKLOADS["tiny_fp32"]
+    inp = to_dev(make_prefill_inputs(w))
+    o, st = run_prefill(inp, w)
+    ref, S = O.hybrid_prefill(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["a"]),
+                              f64(inp["b"]), w.n_sink, w.window)
+    assert_close(f64(o), ref, True, "o")
+    assert_close(f64(st), S, True, "state")
+
+
+@pytest.mark.parametrize("T", [1, 7, 63, 64, 65, 100, 127, 128, 129, 257, 700])
+def test_bf16_ragged_lengths(T):
+    w = small(T=T)
+    inp = to_dev(make_prefill_inputs(w, seed=T))
+    o, st = run_prefill(inp, w)
+    ref, S = O.hybrid_prefill(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["a"]),
+                              f64(inp["b"]), w.n_sink, w.window)
+    assert_close(f64(o), ref, False, "o")
+    assert_close(f64(st), S, False, "state")
+
+
+@pytest.mark.parametrize("T,n_sink,window", [(65, 8, 56), (257, 8, 56), (300, 3, 20), (200, 0, 64),
+                                             (130, 8, 120)])
+def test_fp32_d64_shapes(T, n_sink, window):
+    w = small(T=T, d=64, dtype="f32", n_sink=n_sink, window=window, H=4, Hkv=1)
+    inp = to_dev(make_prefill_inputs(w, seed=11))
+    o, st = run_prefill(inp, w)
+    ref, S = O.hybrid_prefill(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["a"]),
+                              f64(inp["b"]), w.n_sink, w.window)
+    assert_close(f64(o), ref, True, "o")
+    assert_close(f64(st), S, True, "state")
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 4), (8, 1), (16, 2)])
+def test_head_groupings(H, Hkv):
+    w = small(T=200, H=H, Hkv=Hkv, B=1)
+    inp = to_dev(make_prefill_inputs(w, seed=5))
+    o, st = run_prefill(inp, w)
+    ref, S = O.hybrid_prefill(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["a"]),
+                              f64(inp["b"]), w.n_sink, w.window)
+    assert_close(f64(o), ref, False, "o")
+    assert_close(f64(st), S, False, "state")
+
+
+@pytest.mark.parametrize("flags", [gl.BRANCH_LINEAR, gl.BRANCH_SOFTMAX, gl.WRITE_STATE,
+                                   gl.BRANCH_LINEAR | gl.WRITE_STATE])
+def test_branch_flags(flags):
+    w = small(T=300)
+    inp = to_dev(make_prefill_inputs(w, seed=2))
+    o, st = run_prefill(inp, w, flags=flags)
+    ref, S = O.hybrid_prefill(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["a"]),
+                              f64(inp["b"]), w.n_sink, w.window, flags=flags)
+    if flags & ALL:
+        assert_close(f64(o), ref, False, "o")
+    else:
+        assert o is None
+    if flags & gl.WRITE_STATE:
+        assert_close(f64(st), S, False, "state")
+
+
+@pytest.mark.parametrize("n_sink,window,T", [(8, 56, 300), (8, 120, 400), (3, 20, 150), (0, 64, 200)])
+def test_mask_probe_exact(n_sink, window, T):
+    """Softmax-only with q = 0: weights are exactly uniform over A(t), and a
+    one-hot v (dimension i mod d) turns every output row into exact counts of
+    the attended positions per residue class."""
+    d = 128
+    B, H = 1, 1
+    q = torch.zeros(B, T, H, d, dtype=torch.bfloat16, device=DEV)
+    k = torch.randn(B, T, H, d, device=DEV).to(torch.bfloat16)
+    v = torch.nn.functional.one_hot(torch.arange(T, device=DEV) % d, d).to(torch.bfloat16)
+    v = v.view(1, T, 1, d).contiguous()
+    a = torch.ones(B, T, H, device=DEV)
+    b = torch.ones(B, T, H, device=DEV)
+    o, _ = gl.hybrid_prefill(q, k, v, a, b, n_sink, window, flags=gl.BRANCH_SOFTMAX)
+    torch.cuda.synchronize()
+    o = f64(o)[0, :, 0]
+    for t in range(T):
+        A = O.softmax_index_set(t, n_sink, window)
+        want = np.bincount(A % d, minlength=d)
+        got = np.rint(o[t] * len(A)).astype(np.int64)
+        assert np.array_equal(got, want), f"row {t}"
+
+
+def test_llama8b_t4096_sampled_heads():
+    w = WORKLOADS["llama8b_t4096"]
+    inp = to_dev(make_prefill_inputs(w, device=DEV))
+    o, st = run_prefill(inp, w)
+    for heads in ([0, 1, 2, 3], [29, 31]):
+        ref, S = oracle_subset(inp, w, [0], heads)
+        assert_close(f64(o[:, :, heads]), ref, False, f"o heads {heads}")
+        assert_close(f64(st[:, heads]), S, False, f"state heads {heads}")
+
+
+def test_longctx_b8_t32768_sampled():
+    w = WORKLOADS["longctx_b8_t32768"]
+    inp = to_dev(make_prefill_inputs(w, device=DEV))
+    o, st = run_prefill(inp, w)
+    rng = np.random.default_rng(0)
+    rows = sorted(set([0, 7, 8, 127, 128, 129, 255, 256, w.T - 1]) |
+                  set(rng.integers(0, w.T, 40).tolist()))
+    for bsel, heads in (([0], [0]), ([7], [31]), ([3], [13, 14])):
+        ref, S = oracle_subset(inp, w, bsel, heads, rows=rows)
+        got = f64(o[bsel][:, rows][:, :, heads])
+        assert_close(got, ref[:, rows], False, f"o b{bsel} h{heads}")
+        assert_close(f64(st[bsel][:, heads]), S, False, f"state b{bsel} h{heads}")
+
+
+# ---------------------------------------------------------------- GLA
+
+@pytest.mark.parametrize("T,dtype,d", [(257, "bf16", 128), (130, "bf16", 128), (700, "bf16", 64),
+                                       (257, "f32", 64), (65, "f32", 64)])
+def test_gla_prefill(T, dtype, d):
+    w = small(T=T, d=d, dtype=dtype, update="gla")
+    inp = to_dev(make_prefill_inputs(w, seed=3))
+    o, st = run_prefill(inp, w)
+    ref, S = O.hybrid_prefill(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["a"]),
+                              None, w.n_sink, w.window, update="gla")
+    assert_close(f64(o), ref, dtype == "f32", "o")
+    assert_close(f64(st), S, dtype == "f32", "state")
+
+
+# ------------------------------------------------------------- short conv
+
+@pytest.mark.parametrize("dtype,d,T,flags", [("bf16", 128, 200, 3), ("f32", 64, 77, 3),
+                                             ("f32", 128, 70, 1), ("bf16", 64, 130, 2),
+                                             ("f32", 64, 9, 0)])
+def test_shortconv_small(dtype, d, T, flags):
+    w = small(T=T, d=d, dtype=dtype, shortconv=True, H=4, Hkv=2, B=2)
+    inp = to_dev(make_prefill_inputs(w, seed=4))
+    qo, ko, vo = gl.shortconv_qkv(inp["q"], inp["k"], inp["v"], inp["wq"], inp["wk"], inp["wv"],
+                                  rope_theta=1e6, pos0=3, flags=flags)
+    torch.cuda.synchronize()
+    rq, rk, rv = O.shortconv_qkv(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["wq"]),
+                                 f64(inp["wk"]), f64(inp["wv"]), 1e6, 3, flags=flags)
+    fp32 = dtype == "f32"
+    assert_close(f64(qo), rq, fp32, "q")
+    assert_close(f64(ko), rk, fp32, "k")
+    assert_close(f64(vo), rv, fp32, "v")
+
+
+def test_qwen32b_full_stack_sampled():
+    """Config with RoPE -> conv -> L2 norm, budget 896, GDN and GLA layers."""
+    for name in ("qwen32b_t8192_gdn", "qwen32b_t8192_gla"):
+        w = WORKLOADS[name]
+        raw = to_dev(make_prefill_inputs(w, device=DEV))
+        qc, kc, vc = gl.shortconv_qkv(raw["q"], raw["k"], raw["v"], raw["wq"], raw["wk"], raw["wv"],
+                                      rope_theta=w.rope_theta, pos0=0, flags=gl.ROPE | gl.L2NORM)
+        inp = dict(q=qc, k=kc, v=vc, a=raw["a"], b=raw["b"])
+        o, st = run_prefill(inp, w)
+        G = w.H // w.Hkv
+        rows = [0, 7, 8, 895, 896, 897, 1000, 4095, 4096, w.T - 1]
+        for bsel, heads, g in (([0], [0, 5], 0), ([1], [63], 7)):
+            # short conv of the sampled channels
+            cq = slice(heads[0], heads[-1] + 1)
+            rq, rk, rv = O.shortconv_qkv(
+                f64(raw["q"][bsel][:, :, cq]), f64(raw["k"][bsel][:, :, g:g + 1]),
+                f64(raw["v"][bsel][:, :, g:g + 1]),
+                f64(raw["wq"].view(w.H, w.d, -1)[cq].reshape(-1, w.conv_ks)),
+                f64(raw["wk"].view(w.Hkv, w.d, -1)[g]), f64(raw["wv"].view(w.Hkv, w.d, -1)[g]),
+                w.rope_theta, 0, flags=3)
+            assert_close(f64(qc[bsel][:, :, cq]), rq, False, "conv q")
+            assert_close(f64(kc[bsel][:, :, g:g + 1]), rk, False, "conv k")
+            assert_close(f64(vc[bsel][:, :, g:g + 1]), rv, False, "conv v")
+            # the layer on the GPU's conv outputs
+            ref, S = oracle_subset(inp, w, bsel, heads, rows=rows)
+            assert_close(f64(o[bsel][:, rows][:, :, heads]), ref[:, rows], False, f"{name} o")
+            assert_close(f64(st[bsel][:, heads]), S, False, f"{name} state")
+            assert heads[0] // G == g
+
+
+# ------------------------------------------------------------------ decode
+
+def run_decode(step_inp, st, w, flags=ALL):
+    o = gl.hybrid_decode(step_inp["q"], step_inp["k"], step_inp["v"], step_inp["a"],
+                         step_inp.get("b"), st["state"], st["k_cache"], st["v_cache"],
+                         st["a_cache"], st["b_cache"], st["pos"], w.n_sink, w.window,
+                         update=w.update, flags=flags)
+    torch.cuda.synchronize()
+    return o
+
+
+@pytest.mark.parametrize("update", ["gdn", "gla"])
+@pytest.mark.parametrize("pos0", [0, 2, 6, 60, 63, 64, 65, 500])
+def test_decode_steps_small(update, pos0):
+    w = Workload("dec", B=3, H=4, Hkv=2, d=128, n_sink=3, window=61, update=update, pos0=pos0,
+                 steps=6)
+    inp = make_decode_inputs(w, device=DEV, seed=pos0)
+    st = {k: inp[k].clone() for k in ("state", "k_cache", "v_cache", "a_cache", "b_cache", "pos")}
+    ref = {k: f64(st[k]) for k in st}
+    ref["pos"] = st["pos"].cpu().numpy().astype(np.int64)
+    for s in range(w.steps):
+        step = {k: inp[k][s] for k in ("q", "k", "v", "a", "b")}
+        o = run_decode(step, st, w)
+        ro, ref["state"], ref["k_cache"], ref["v_cache"], ref["a_cache"], ref["b_cache"], ref["pos"] = \
+            O.decode_step(f64(step["q"]), f64(step["k"]), f64(step["v"]), f64(step["a"]),
+                          f64(step["b"]), ref["state"], ref["k_cache"], ref["v_cache"],
+                          ref["a_cache"], ref["b_cache"], ref["pos"], w.n_sink, w.window,
+                          update=update)
+        assert_close(f64(o), ro, False, f"o step {s}")
+        assert_close(f64(st["state"]), ref["state"], False, f"state step {s}")
+        assert np.array_equal(st["pos"].cpu().numpy(), ref["pos"])
+        # caches are copies of bf16 / fp32 inputs: exact
+        assert np.array_equal(f64(st["k_cache"]), ref["k_cache"])
+        assert np.array_equal(f64(st["v_cache"]), ref["v_cache"])
+        assert np.array_equal(f64(st["a_cache"]), ref["a_cache"])
+        if update == "gdn":
+            assert np.array_equal(f64(st["b_cache"]), ref["b_cache"])
+
+
+def test_decode_b256_sampled_sequences():
+    w = WORKLOADS["decode_b256"]
+    inp = make_decode_inputs(w, device=DEV, steps=3)
+    st = {k: inp[k].clone() for k in ("state", "k_cache", "v_cache", "a_cache", "b_cache", "pos")}
+    bsel = [0, 1, 128, 255]
+    ref = {k: f64(st[k][bsel]) for k in st if k != "pos"}
+    ref["pos"] = st["pos"][bsel].cpu().numpy().astype(np.int64)
+    for s in range(3):
+        step = {k: inp[k][s] for k in ("q", "k", "v", "a", "b")}
+        o = run_decode(step, st, w)
+        ro, ref["state"], ref["k_cache"], ref["v_cache"], ref["a_cache"], ref["b_cache"], ref["pos"] = \
+            O.decode_step(*(f64(step[k][bsel]) for k in ("q", "k", "v", "a", "b")), ref["state"],
+                          ref["k_cache"], ref["v_cache"], ref["a_cache"], ref["b_cache"],
+                          ref["pos"], w.n_sink, w.window)
+        assert_close(f64(o[bsel]), ro, False, f"o step {s}")
+        assert_close(f64(st["state"][bsel]), ref["state"], False, f"state step {s}")
+    assert torch.all(st["pos"] == w.pos0 + 3)
+
+
+@pytest.mark.parametrize("update", ["gdn", "gla"])
+@pytest.mark.parametrize("T0", [62, 63, 64, 65, 200])
+def test_prefill_then_decode_matches_longer_prefill(update, T0):
+    n = 9
+    w = small(T=T0 + n, B=2, H=4, Hkv=2, update=update)
+    inp = to_dev(make_prefill_inputs(w, seed=T0))
+    o_full, _ = run_prefill(inp, w)
+    pre = {k: inp[k][:, :T0].contiguous() for k in ("q", "k", "v", "a", "b")}
+    _, state = run_prefill(pre, w)
+    kc, vc, ac, bc = gl.cache_from_prefill(pre["k"], pre["v"], pre["a"], pre["b"], w.H,
+                                           w.n_sink, w.window, update=update)
+    st = dict(state=state, k_cache=kc, v_cache=vc, a_cache=ac, b_cache=bc,
+              pos=torch.full((w.B,), T0, dtype=torch.int32, device=DEV))
+    ref_full, _ = O.hybrid_prefill(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["a"]),
+                                   f64(inp["b"]), w.n_sink, w.window, update=update)
+    for t in range(T0, T0 + n):
+        step = {k: inp[k][:, t].contiguous() for k in ("q", "k", "v", "a", "b")}
+        o = run_decode(step, st, w)
+        assert_close(f64(o), ref_full[:, t], False, f"decode t={t}")
+        assert_close(f64(o), f64(o_full[:, t]), False, f"decode vs prefill t={t}")
+    kc2, vc2, ac2, bc2 = gl.cache_from_prefill(inp["k"], inp["v"], inp["a"], inp["b"], w.H,
+                                               w.n_sink, w.window, update=update)
+    assert torch.equal(st["k_cache"], kc2) and torch.equal(st["v_cache"], vc2)
+    assert torch.equal(st["a_cache"], ac2)
+    if update == "gdn":
+        assert torch.equal(st["b_cache"], bc2)
+
+
+# ---------------------------------------------------------- invariants
+
+def test_bitwise_deterministic_and_linear_in_v():
+    w = WORKLOADS["llama8b_t4096"]
+    inp = to_dev(make_prefill_inputs(w, device=DEV, seed=1))
+    o1, s1 = run_prefill(inp, w)
+    o2, s2 = run_prefill(inp, w)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    inp2 = dict(inp)
+    inp2["v"] = inp["v"] * 2
+    o3, s3 = run_prefill(inp2, w)
+    assert torch.equal(o3, o1 * 2) and torch.equal(s3, s1 * 2)
+
+
+def test_decode_bitwise_deterministic():
+    w = WORKLOADS["decode_b256"]
+    inp = make_decode_inputs(w, device=DEV, steps=1, B=32)
+    outs = []
+    for _ in range(2):
+        st = {k: inp[k].clone() for k in ("state", "k_cache", "v_cache", "a_cache", "b_cache", "pos")}
+        step = {k: inp[k][0] for k in ("q", "k", "v", "a", "b")}
+        outs.append((run_decode(step, st, w), st["state"]))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
