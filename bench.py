@@ -1,0 +1,323 @@
+#!/usr/bin/env python3
+"""Benchmark of the hybrid GDN + sink/SWA layer on one MI355X.
+
+Headline (the printed JSON line): prefill throughput of one layer with the
+LLaMA3.1-8B attention shape (B=1, 32 query / 8 KV heads, d=128, T=4096,
+budget 8 sinks + 56 window, bf16 inputs, fp32 state).  One step = one
+layer pass over the sequence: the chunked GDN kernel, then the sink+SWA
+softmax kernel adding its branch (two ABI calls, each launching exactly one
+kernel, so HIP events between them time each kernel on the stream it runs
+on).  Inputs are resident in HBM before the timed region.
+
+Secondary figures in "also": decode steps/s (B=256, 1000 consecutive steps),
+long-context prefill (B=8, T=32768, budget 128, final state out) and the
+Qwen3-32B-shaped full stack (short conv + GDN, short conv + GLA, budget 896).
+
+Roofline: algorithmic FLOPs (or bytes) per launch of the dominant kernel
+divided by its mean event-timed duration, against the MI355X peaks (bf16
+dense MFMA 2.5 PFLOP/s, HBM 8 TB/s).  cpu_baseline: the fp64 NumPy oracle
+timed on this host on a bounded sample (16 of the 32 heads, one thread),
+scaled to the whole layer.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--only main|decode|...]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2.5e15      # dense bf16 MFMA FLOP/s
+PEAK_HBM = 8.0e12       # bytes/s
+CHUNK = 64
+
+
+def gdn_flops(w, T=None):
+    """Algorithmic FLOPs of the chunked GDN linear branch (one layer)."""
+    T = w.T if T is None else T
+    stream = max(0, T - w.budget)
+    d = w.d
+    per = 6 * d * d + 2 * CHUNK * (3 * d + 2 * d)
+    return w.B * w.H * stream * per
+
+
+def gla_flops(w, T=None):
+    T = w.T if T is None else T
+    stream = max(0, T - w.budget)
+    d = w.d
+    per = 4 * d * d + 2 * CHUNK * (d + d)
+    return w.B * w.H * stream * per
+
+
+def swa_flops(w, T=None):
+    T = w.T if T is None else T
+    t = np.arange(T)
+    return w.B * w.H * int(np.sum(4 * np.minimum(t + 1, w.budget))) * w.d
+
+
+def prefill_bytes(w, elt=2, state=False):
+    d = w.d
+    b = w.B * w.T * (w.H * d * elt * 2 + 2 * w.Hkv * d * elt)      # q, o, k, v
+    b += w.B * w.T * w.H * 4 * (d if w.update == "gla" else 2)     # gates
+    if state:
+        b += w.B * w.H * d * d * 4
+    return b
+
+
+def decode_bytes(w, elt=2):
+    d, B, H, Hkv, N = w.d, w.B, w.H, w.Hkv, w.budget
+    b = 2 * B * H * d * d * 4                 # state read + write
+    b += B * Hkv * N * d * elt * 2            # cached K and V read
+    b += B * Hkv * d * elt * 2 * 2            # new k, v read + written to the cache
+    b += B * H * d * elt * 2                  # q in, o out
+    b += B * H * 4 * 2 * 2                    # new a, b in; cached a, b of the evicted slot
+    b += B * H * 4 * 2                        # new a, b stored
+    b += B * 4 * 2                            # pos
+    return b
+
+
+def timed(fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+# ------------------------------------------------------------- headline
+
+def bench_main(steps, warmup):
+    import swa_chunked_gated_amd as gl
+    from workloads import WORKLOADS, make_prefill_inputs
+
+    w = WORKLOADS["llama8b_t4096"]
+    inp = make_prefill_inputs(w, device="cuda")
+    o = torch.empty(w.B, w.T, w.H, w.d, dtype=torch.bfloat16, device="cuda")
+    q, k, v, a, b = (inp[x] for x in ("q", "k", "v", "a", "b"))
+    n = steps + warmup
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+
+    def step(i):
+        e = ev[i]
+        e[0].record()
+        gl.hybrid_prefill(q, k, v, a, b, w.n_sink, w.window, flags=gl.BRANCH_LINEAR, o=o)
+        e[1].record()
+        gl.hybrid_prefill(q, k, v, a, b, w.n_sink, w.window,
+                          flags=gl.BRANCH_SOFTMAX | gl.ACCUMULATE, o=o)
+        e[2].record()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(warmup, n):
+        step(i)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    lin_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(warmup, n)]))
+    swa_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(warmup, n)]))
+    f_lin, f_swa = gdn_flops(w), swa_flops(w)
+    if lin_ms >= swa_ms:
+        dom = ("linear_chunk_kernel (chunked GDN)", f_lin, lin_ms)
+    else:
+        dom = ("swa_kernel (sink + window softmax)", f_swa, swa_ms)
+    achieved = dom[1] / (dom[2] * 1e-3)
+    res = {
+        "w": w, "sec": sec,
+        "kernels_ms": {"linear_chunk_kernel": lin_ms, "swa_kernel": swa_ms},
+        "roofline": {
+            "kernel": dom[0], "bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,
+            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16, "traffic": None,
+            "algorithmic_flops_per_launch": dom[1],
+        },
+        "layer_frac_mfma": (f_lin + f_swa) / sec / PEAK_BF16,
+        "inputs": inp,
+    }
+    return res
+
+
+def cpu_baseline(inp, w, heads_per_sample=16):
+    """fp64 oracle on the first `heads_per_sample` query heads (whole T),
+    scaled to all heads; one thread."""
+    from threadpoolctl import threadpool_limits
+    from oracle import hybrid as O
+
+    G = w.H // w.Hkv
+    ng = heads_per_sample // G
+    f = {x: inp[x][:, :, : (heads_per_sample if x in ("q", "a", "b") else ng)].double().cpu().numpy()
+         for x in ("q", "k", "v", "a", "b")}
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        O.hybrid_prefill(f["q"], f["k"], f["v"], f["a"], f["b"], w.n_sink, w.window, flags=3)
+        dt = time.perf_counter() - t0
+    full = dt * w.H / heads_per_sample
+    return {
+        "value": w.B * w.T / full, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        "sample": f"layer prefill on {heads_per_sample} of {w.H} query heads "
+                  f"({ng} KV groups), B={w.B}, T={w.T}, fp64 NumPy, one thread; "
+                  f"{dt:.1f} s measured, scaled x{w.H / heads_per_sample:g} to all heads",
+        "cpu": platform.processor() or platform.machine(),
+        "host_cores_allowed": len(os.sched_getaffinity(0)),
+    }
+
+
+# ------------------------------------------------------------ secondary
+
+def bench_decode(steps=1000, warmup=10):
+    import swa_chunked_gated_amd as gl
+    from workloads import WORKLOADS, make_decode_inputs
+
+    w = WORKLOADS["decode_b256"]
+    inp = make_decode_inputs(w, device="cuda", steps=steps)
+    keys = ("state", "k_cache", "v_cache", "a_cache", "b_cache", "pos")
+    o = torch.empty(w.B, w.H, w.d, dtype=torch.bfloat16, device="cuda")
+
+    def run(st, s):
+        gl.hybrid_decode(inp["q"][s], inp["k"][s], inp["v"][s], inp["a"][s], inp["b"][s],
+                         st["state"], st["k_cache"], st["v_cache"], st["a_cache"], st["b_cache"],
+                         st["pos"], w.n_sink, w.window, o=o)
+
+    scratch = {x: inp[x].clone() for x in keys}
+    for s in range(warmup):
+        run(scratch, s)
+    del scratch
+    st = {x: inp[x].clone() for x in keys}
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for s in range(steps):
+        run(st, s)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    ev_ms = e0.elapsed_time(e1) / steps
+    byts = decode_bytes(w)
+    return {
+        "workload": "decode_b256 (B=256, H=32, Hkv=8, d=128, cache 8+56, t=4096..5095)",
+        "steps": steps, "ms_per_step": sec * 1e3, "steps_per_s": 1.0 / sec,
+        "tokens_per_s": w.B / sec, "event_ms_per_step": ev_ms,
+        "roofline": {"kernel": "decode_kernel + advance_pos_kernel", "bound": "hbm",
+                     "achieved": byts / (ev_ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9,
+                     "unit": "GB/s", "frac": byts / (ev_ms * 1e-3) / PEAK_HBM,
+                     "algorithmic_bytes_per_step": byts},
+    }
+
+
+def bench_prefill_cfg(name, steps=5, warmup=2):
+    import swa_chunked_gated_amd as gl
+    from workloads import WORKLOADS, make_prefill_inputs
+
+    w = WORKLOADS[name]
+    inp = make_prefill_inputs(w, device="cuda")
+    flags = gl.BRANCH_LINEAR | gl.BRANCH_SOFTMAX | (gl.WRITE_STATE if w.write_state else 0)
+    o = torch.empty(w.B, w.T, w.H, w.d, dtype=torch.bfloat16, device="cuda")
+    st = torch.empty(w.B, w.H, w.d, w.d, dtype=torch.float32, device="cuda") if w.write_state else None
+    if w.shortconv:
+        qc, kc, vc = (torch.empty_like(inp[x]) for x in ("q", "k", "v"))
+
+    def layer():
+        if w.shortconv:
+            gl.shortconv_qkv(inp["q"], inp["k"], inp["v"], inp["wq"], inp["wk"], inp["wv"],
+                             rope_theta=w.rope_theta, flags=gl.ROPE | gl.L2NORM, out=(qc, kc, vc))
+            q, k, v = qc, kc, vc
+        else:
+            q, k, v = inp["q"], inp["k"], inp["v"]
+        gl.hybrid_prefill(q, k, v, inp["a"], inp["b"], w.n_sink, w.window, update=w.update,
+                          flags=flags, o=o, state_out=st)
+
+    sec = timed(layer, steps, warmup)
+    f = (gdn_flops(w) if w.update == "gdn" else gla_flops(w)) + swa_flops(w)
+    res = {"workload": name, "B": w.B, "T": w.T, "H": w.H, "Hkv": w.Hkv, "budget": w.budget,
+           "update": w.update, "ms_per_step": sec * 1e3, "tokens_per_s": w.B * w.T / sec,
+           "algorithmic_gflop": f / 1e9, "layer_frac_mfma": f / sec / PEAK_BF16}
+    if w.shortconv:
+        def conv():
+            gl.shortconv_qkv(inp["q"], inp["k"], inp["v"], inp["wq"], inp["wk"], inp["wv"],
+                             rope_theta=w.rope_theta, flags=gl.ROPE | gl.L2NORM, out=(qc, kc, vc))
+        csec = timed(conv, steps, warmup)
+        cbytes = 2 * sum(inp[x].numel() * inp[x].element_size() for x in ("q", "k", "v"))
+        res["shortconv_ms"] = csec * 1e3
+        res["shortconv_frac_hbm"] = cbytes / csec / PEAK_HBM
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only", default="all",
+                    choices=["all", "main", "decode", "longctx", "qwen32b"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    if args.only == "decode":
+        print(json.dumps(bench_decode()), flush=True)
+        return
+    if args.only in ("longctx", "qwen32b"):
+        names = ["longctx_b8_t32768"] if args.only == "longctx" else \
+            ["qwen32b_t8192_gdn", "qwen32b_t8192_gla"]
+        for n in names:
+            print(json.dumps(bench_prefill_cfg(n, steps=args.steps, warmup=args.warmup)), flush=True)
+        return
+
+    m = bench_main(args.steps, args.warmup)
+    w = m["w"]
+    also = {}
+    if args.only == "all":
+        also["decode"] = bench_decode()
+        also["longctx_b8_t32768"] = bench_prefill_cfg("longctx_b8_t32768")
+        also["qwen32b_t8192_gdn"] = bench_prefill_cfg("qwen32b_t8192_gdn")
+        also["qwen32b_t8192_gla"] = bench_prefill_cfg("qwen32b_t8192_gla")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(m["inputs"], w)
+    line = {
+        "metric": "hybrid GDN+sink/SWA layer prefill tokens/s (LLaMA3.1-8B attention shape)",
+        "value": w.B * w.T / m["sec"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": m["sec"] * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes and distributions of the workload, no weights)",
+        "config": {"workload": "llama8b_t4096 prefill", "B": w.B, "T": w.T, "H": w.H,
+                   "Hkv": w.Hkv, "d": w.d, "n_sink": w.n_sink, "window": w.window,
+                   "update": "gdn", "state": "fp32"},
+        "roofline": m["roofline"],
+        "cpu_baseline": cpu,
+        "kernels_ms": m["kernels_ms"],
+        "layer_frac_mfma": m["layer_frac_mfma"],
+        "also": also,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

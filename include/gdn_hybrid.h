@@ -71,7 +71,9 @@ typedef enum { GDN_DELTA = 0, GDN_GLA = 1 } gdn_update;
 enum {
   GDN_BRANCH_LINEAR = 1,   /* add o_lin to o                                   */
   GDN_BRANCH_SOFTMAX = 2,  /* add o_swa to o                                   */
-  GDN_WRITE_STATE = 4      /* prefill only: write the final state to state_out */
+  GDN_WRITE_STATE = 4,     /* prefill only: write the final state to state_out */
+  GDN_ACCUMULATE = 8       /* prefill only: add the selected branches to the
+                              values o already holds instead of overwriting */
 };
 
 /* flags of shortconv_qkv */
@@ -118,8 +120,12 @@ int gdn_hybrid_prefill_workspace(int B, int T, int H, int Hkv, int dk, int dv,
  *   state_out  [B, H, dk, dv] fp32: S after token T-1-window (zero if none),
  *              the state a following decode step continues from; written iff
  *              flags & GDN_WRITE_STATE (else may be NULL)
- *   n_sink >= 0, window >= 1; flags: any non-empty combination of the
- *   GDN_BRANCH_* / GDN_WRITE_STATE bits.
+ *   n_sink >= 0, window >= 1; flags: any combination of GDN_BRANCH_LINEAR,
+ *   GDN_BRANCH_SOFTMAX, GDN_WRITE_STATE (at least one) and GDN_ACCUMULATE.
+ *   With GDN_ACCUMULATE, o must hold initialised values and receives
+ *   o += (selected branches); calling once with GDN_BRANCH_LINEAR and once
+ *   with GDN_BRANCH_SOFTMAX | GDN_ACCUMULATE gives the same o as one call
+ *   with both branches (each call then launches a single kernel).
  *   workspace / workspace_bytes: device buffer of at least the size reported
  *   by gdn_hybrid_prefill_workspace (may be NULL / 0 when that size is 0).
  * Supported: d in {64, 128} for bf16; the linear branch (or the state) in

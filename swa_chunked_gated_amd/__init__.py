@@ -18,6 +18,7 @@ from ._lib import GdnError  # noqa: F401
 BRANCH_LINEAR = 1
 BRANCH_SOFTMAX = 2
 WRITE_STATE = 4
+ACCUMULATE = 8
 ROPE = 1
 L2NORM = 2
 
@@ -26,7 +27,7 @@ _UPDATES = {"gdn": 0, "gla": 1}
 
 __all__ = [
     "hybrid_prefill", "hybrid_decode", "cache_from_prefill", "shortconv_qkv",
-    "version", "GdnError", "BRANCH_LINEAR", "BRANCH_SOFTMAX", "WRITE_STATE",
+    "version", "GdnError", "BRANCH_LINEAR", "BRANCH_SOFTMAX", "WRITE_STATE", "ACCUMULATE",
     "ROPE", "L2NORM",
 ]
 
@@ -71,7 +72,10 @@ def hybrid_prefill(q, k, v, a, b, n_sink: int, window: int, update: str = "gdn",
 
     q [B,T,H,d], k/v [B,T,Hkv,d] (fp32 or bf16); a [B,T,H] (GLA: [B,T,H,d])
     and b [B,T,H] fp32.  Returns (o [B,T,H,d], state [B,H,d,d] fp32 or None).
+    With ACCUMULATE in flags, ``o`` must be given and receives o += branches.
     """
+    if flags & ACCUMULATE and o is None:
+        raise ValueError("ACCUMULATE needs an initialised output tensor o")
     B, T, H, dk = q.shape
     Hkv, dv = k.shape[2], v.shape[3]
     dt = _io_dtype(q, k, v)

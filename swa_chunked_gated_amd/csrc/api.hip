@@ -60,7 +60,7 @@ int gdn_hybrid_prefill_workspace(int B, int T, int H, int Hkv, int dk, int dv, i
                                  int window, int dtype, int update, int flags, size_t* bytes) {
   if (!bytes) return GDN_EINVAL;
   if (!dims_ok(B, T, H, Hkv, dk, dv, n_sink, window, dtype, update)) return GDN_EINVAL;
-  if (flags < 1 || flags > 7) return GDN_EINVAL;
+  if (flags < 1 || flags > 15 || (flags & 7) == 0) return GDN_EINVAL;
   *bytes = 0;
   return GDN_OK;
 }
@@ -72,10 +72,11 @@ int gdn_hybrid_prefill(const void* q, const void* k, const void* v, const float*
   (void)workspace;
   (void)workspace_bytes;
   if (!dims_ok(B, T, H, Hkv, dk, dv, n_sink, window, dtype, update)) return GDN_EINVAL;
-  if (flags < 1 || flags > 7) return GDN_EINVAL;
+  if (flags < 1 || flags > 15 || (flags & 7) == 0) return GDN_EINVAL;
   const bool lin = flags & GDN_BRANCH_LINEAR;
   const bool swa = flags & GDN_BRANCH_SOFTMAX;
   const bool wst = flags & GDN_WRITE_STATE;
+  const bool acc = flags & GDN_ACCUMULATE;
   const bool needs_rec = lin || wst;
   if (!q || !k || !v) return GDN_EINVAL;
   if ((lin || swa) && !o) return GDN_EINVAL;
@@ -89,12 +90,19 @@ int gdn_hybrid_prefill(const void* q, const void* k, const void* v, const float*
                      dtype == GDN_BF16, update == GDN_GLA, flags};
   hipStream_t s = (hipStream_t)stream;
   const int N = n_sink + window;
-  if (wst || (lin && T > N)) {
+  // The linear kernel writes (or adds) rows t >= N and, for a linear-only
+  // overwrite, zeroes rows t < N itself; the softmax kernel then adds what o
+  // holds on rows t >= add_from.
+  const bool run_linear = wst || (lin && T > N);
+  if (run_linear) {
     int rc = launched(gdn::launch_linear_prefill(p, s));
     if (rc) return rc;
   }
-  if (swa) return launched(gdn::launch_swa_prefill(p, lin && T > N, s));
-  if (lin) return launched(gdn::launch_zero_head_rows(p, s));
+  if (swa) {
+    const int add_from = acc ? 0 : ((lin && T > N) ? N : T);
+    return launched(gdn::launch_swa_prefill(p, add_from, s));
+  }
+  if (lin && !acc && !run_linear) return launched(gdn::launch_zero_head_rows(p, s));
   return GDN_OK;
 }
 

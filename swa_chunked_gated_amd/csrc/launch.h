@@ -69,12 +69,14 @@ struct ShortConvArgs {
   int pos0, flags, bf16;
 };
 
-// Linear branch (chunked GDN or GLA): writes o rows t >= n_sink + window
-// (when the linear branch is selected) and the final state (when asked).
+// Linear branch (chunked GDN or GLA): writes (GDN_ACCUMULATE: adds to) o rows
+// t >= n_sink + window when the linear branch is selected, zeroes rows
+// t < n_sink + window for a linear-only overwrite, and writes the final
+// state when asked.
 hipError_t launch_linear_prefill(const PrefillArgs& a, hipStream_t s);
-// Softmax branch: writes every row of o; adds the value already in o on
-// rows t >= n_sink + window when add_linear is set.
-hipError_t launch_swa_prefill(const PrefillArgs& a, int add_linear, hipStream_t s);
+// Softmax branch: writes every row of o, adding the value o already holds
+// on rows t >= add_from.
+hipError_t launch_swa_prefill(const PrefillArgs& a, int add_from, hipStream_t s);
 // Zero rows t < n_sink + window of o (linear-only output).
 hipError_t launch_zero_head_rows(const PrefillArgs& a, hipStream_t s);
 

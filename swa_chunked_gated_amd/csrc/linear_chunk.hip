@@ -529,17 +529,32 @@ __global__ __launch_bounds__(kThreads) void linear_chunk_kernel(
       }
     }
 
-    // ---- store the chunk's linear output rows
+    // ---- store (or add) the chunk's linear output rows
     if (flags & 1) {
+      const bool accumulate = (flags & 8) != 0;
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         const int r = 16 * rt + l16;
         if (r < Cc) {
           T* orow = o + ((size_t)(bi * T_ + i0 + r + window) * H + h) * D + c0 + cw;
 #pragma unroll
-          for (int dt = 0; dt < NT; ++dt) store4(orow + 16 * dt + 4 * lg, ot[dt][rt]);
+          for (int dt = 0; dt < NT; ++dt) {
+            f32x4 val = ot[dt][rt];
+            if (accumulate) val += load4(orow + 16 * dt + 4 * lg);
+            store4(orow + 16 * dt + 4 * lg, val);
+          }
         }
       }
+    }
+  }
+
+  // linear-only overwrite: rows t < n_sink + window carry no linear output
+  if ((flags & 1) && !(flags & 2) && !(flags & 8)) {
+    const int rows = min(n_sink + window, T_);
+    for (int i = tid; i < rows * (DVS / 4); i += kThreads) {
+      const int t = i / (DVS / 4);
+      const int cc = (i % (DVS / 4)) * 4;
+      store4(o + ((size_t)(bi * T_ + t) * H + h) * D + c0 + cc, zero4());
     }
   }
 

@@ -22,8 +22,9 @@
 // Exponentials use exp2 with log2(e) folded into the scale.  A 16-key tile
 // that no query of the wave can see is skipped.
 //
-// Epilogue: o = O / l, plus (add_linear) the linear-branch value already in o
-// on rows t >= n_sink + window, cast to the output type.
+// Epilogue: o = O / l, plus the value o already holds on rows t >= add_from
+// (the linear branch, or the caller's values when accumulating), cast to the
+// output type.
 
 #include "common.h"
 #include "launch.h"
@@ -38,7 +39,7 @@ template <class T, int D>
 __global__ __launch_bounds__(512) void swa_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                   const T* __restrict__ v, T* __restrict__ o,
                                                   int T_, int H, int Hkv, int HPW, int QT,
-                                                  int n_sink, int window, int add_linear) {
+                                                  int n_sink, int window, int add_from) {
   constexpr int PAD = 16 / sizeof(T);
   constexpr int SK = D + PAD;      // Ks row stride
   constexpr int SV = kKB + PAD;    // VTs row stride
@@ -63,7 +64,6 @@ __global__ __launch_bounds__(512) void swa_kernel(const T* __restrict__ q, const
   const int t0 = tile * QT;
   const int qb = t0 + (wv % NWQ) * 16 * kNQ;      // first query row of this wave
   const int t_end = min(t0 + QT, T_);
-  const int N = n_sink + window;
   const float scale = kLog2e / sqrtf((float)D);
 
   // query fragments (B operand of S^T = K Q^T, "linear" set over d)
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(512) void swa_kernel(const T* __restrict__ q, const
     if (t >= T_) continue;
     const float inv = 1.0f / l;
     T* orow = o + ((size_t)(bi * T_ + t) * H + h) * D;
-    const bool addl = add_linear && t >= N;
+    const bool addl = t >= add_from;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       f32x4 val = oacc[dt][nq] * inv;
@@ -234,7 +234,7 @@ __global__ void zero_head_rows_kernel(T* __restrict__ o, int T_, int H, int D, i
 }
 
 template <class T, int D>
-hipError_t launch_swa_t(const PrefillArgs& p, int add_linear, hipStream_t s) {
+hipError_t launch_swa_t(const PrefillArgs& p, int add_from, hipStream_t s) {
   const int G = p.H / p.Hkv;
   int HPW = 1;
   for (int c = 1; c <= 8; ++c)
@@ -244,15 +244,15 @@ hipError_t launch_swa_t(const PrefillArgs& p, int add_linear, hipStream_t s) {
   const dim3 grid((p.T + QT - 1) / QT, p.H / HPW, p.B);
   hipLaunchKernelGGL((swa_kernel<T, D>), grid, dim3(64 * waves), 0, s, (const T*)p.q,
                      (const T*)p.k, (const T*)p.v, (T*)p.o, p.T, p.H, p.Hkv, HPW, QT, p.n_sink,
-                     p.window, add_linear);
+                     p.window, add_from);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_swa_prefill(const PrefillArgs& p, int add_linear, hipStream_t s) {
-  if (p.bf16) return p.D == 64 ? launch_swa_t<bf16, 64>(p, add_linear, s) : launch_swa_t<bf16, 128>(p, add_linear, s);
-  return p.D == 64 ? launch_swa_t<float, 64>(p, add_linear, s) : launch_swa_t<float, 128>(p, add_linear, s);
+hipError_t launch_swa_prefill(const PrefillArgs& p, int add_from, hipStream_t s) {
+  if (p.bf16) return p.D == 64 ? launch_swa_t<bf16, 64>(p, add_from, s) : launch_swa_t<bf16, 128>(p, add_from, s);
+  return p.D == 64 ? launch_swa_t<float, 64>(p, add_from, s) : launch_swa_t<float, 128>(p, add_from, s);
 }
 
 hipError_t launch_zero_head_rows(const PrefillArgs& p, hipStream_t s) {

@@ -73,6 +73,7 @@ def test_workspace_query(lib):
     assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, 2, 3)[0] == EINVAL       # update
     assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 0)[0] == EINVAL   # flags
     assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 8)[0] == EINVAL
+    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 16)[0] == EINVAL
     assert lib.gdn_hybrid_prefill_workspace(1, 64, 2, 2, 64, 64, 8, 56, 0, 0, 3, None) == EINVAL
 
 
@@ -97,7 +98,8 @@ def test_prefill_validation(lib):
     assert prefill(lib, dk=32, dv=32) == EINVAL
     assert prefill(lib, w=0) == EINVAL
     assert prefill(lib, flags=0) == EINVAL
-    assert prefill(lib, flags=9) == EINVAL
+    assert prefill(lib, flags=8) == EINVAL                       # accumulate alone
+    assert prefill(lib, flags=16) == EINVAL
     assert prefill(lib, dt=F32, dk=128, dv=128) == EUNSUP      # fp32 linear branch at d=128
     assert prefill(lib, dt=F32, dk=128, dv=128, flags=4) == EUNSUP
     # fp32 softmax-only at d=128 is supported, so only the missing pointer fails here

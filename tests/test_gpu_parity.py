@@ -363,3 +363,25 @@ def test_decode_bitwise_deterministic():
         step = {k: inp[k][0] for k in ("q", "k", "v", "a", "b")}
         outs.append((run_decode(step, st, w), st["state"]))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_split_calls_equal_fused_call_and_accumulate():
+    """LINEAR then SOFTMAX|ACCUMULATE reproduces the fused call bit for bit,
+    and ACCUMULATE adds the layer to what o holds."""
+    w = small(T=333, B=2, H=8, Hkv=2)
+    inp = to_dev(make_prefill_inputs(w, seed=9))
+    fused, _ = run_prefill(inp, w, flags=ALL)
+    o, _ = gl.hybrid_prefill(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], w.n_sink, w.window,
+                             flags=gl.BRANCH_LINEAR)
+    gl.hybrid_prefill(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], w.n_sink, w.window,
+                      flags=gl.BRANCH_SOFTMAX | gl.ACCUMULATE, o=o)
+    torch.cuda.synchronize()
+    assert torch.equal(o, fused)
+    base = torch.randn_like(fused, dtype=torch.float32).to(fused.dtype)
+    acc = base.clone()
+    gl.hybrid_prefill(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], w.n_sink, w.window,
+                      flags=ALL | gl.ACCUMULATE, o=acc)
+    torch.cuda.synchronize()
+    ref, _ = O.hybrid_prefill(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["a"]),
+                              f64(inp["b"]), w.n_sink, w.window)
+    assert_close(f64(acc), f64(base) + ref, False, "accumulate")
