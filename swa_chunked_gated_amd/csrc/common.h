@@ -164,7 +164,59 @@ __device__ __forceinline__ f32x4 load4(const bf16* p) {
                static_cast<float>(v[3])};
 }
 
+// Transposed staging: w[j] holds one dword (EPD = 4 / sizeof(T) elements) of
+// row j of a row-major tile, for N consecutive rows.  Store element e of
+// every dword contiguously at dst (one column of the transposed tile), as
+// whole 8- or 16-byte writes.
+template <class T, int N>
+__device__ __forceinline__ void store_column(T* dst, const uint32_t (&w)[N], int e) {
+  if constexpr (sizeof(T) == 2) {
+    uint32_t packed[N / 2];
+#pragma unroll
+    for (int m = 0; m < N / 2; ++m) {
+      const uint32_t lo = (w[2 * m] >> (16 * e)) & 0xFFFFu;
+      const uint32_t hi = (w[2 * m + 1] >> (16 * e)) & 0xFFFFu;
+      packed[m] = lo | (hi << 16);
+    }
+    if constexpr (N % 8 == 0) {
+#pragma unroll
+      for (int m = 0; m < N / 8; ++m)
+        *reinterpret_cast<uint4*>(dst + 8 * m) =
+            uint4{packed[4 * m], packed[4 * m + 1], packed[4 * m + 2], packed[4 * m + 3]};
+    } else {
+      static_assert(N == 4, "column length");
+      *reinterpret_cast<uint2*>(dst) = uint2{packed[0], packed[1]};
+    }
+  } else {
+    static_assert(N % 4 == 0, "column length");
+#pragma unroll
+    for (int m = 0; m < N / 4; ++m)
+      *reinterpret_cast<uint4*>(dst + 4 * m) = uint4{w[4 * m], w[4 * m + 1], w[4 * m + 2], w[4 * m + 3]};
+  }
+}
+
+// ------------------------------------------------------------ barriers
+
+// Workgroup barrier for LDS hazards only.  __syncthreads() also fences global
+// memory, which on gfx9 waits for every outstanding global load (vmcnt(0))
+// and so turns register prefetches of the next tile into stalls.  Here each
+// wave waits for its own LDS operations (lgkmcnt(0); encoding keeps vmcnt
+// and expcnt at their maxima) and then meets the others at s_barrier; the
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ------------------------------------------------------------ wave helpers
+
+// Wave index inside the workgroup as a scalar (wave-uniform) value, so that
+// branches and loops on it compile to scalar control flow.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
 
 __device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
 

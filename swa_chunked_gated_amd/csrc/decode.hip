@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
   const int N = n_sink + window;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = wave_id();
   const int t = pos[bi];
   if (t < 0) return;   // outside the contract (pos >= 0); never index a negative slot
   const int e = t - window;
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     if (!GLA)
       for (int i = tid; i < G; i += kDecThreads) be[i] = bc[gb + i];
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- k_e . q_h per head
   if (evict) {
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
       for (int hh = 0; hh < kMaxG; ++hh)
         if (hh < G) lg[hh * N + j] = valid ? acc[hh] * scale : -INFINITY;
     }
-    __syncthreads();
+    lds_barrier();
     for (int hh = wv; hh < G; hh += kDecThreads / 64) {
       float m = -INFINITY;
       for (int j = lane; j < N; j += 64) m = fmaxf(m, lg[hh * N + j]);
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
       const float inv = 1.0f / s;
       for (int j = lane; j < N; j += 64) lg[hh * N + j] *= inv;
     }
-    __syncthreads();
+    lds_barrier();
     {
       const int c = tid % D;
       const int hg = tid / D;
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
 #pragma unroll
     for (int r = 0; r < M::R; ++r)
       s[r] = *reinterpret_cast<const f32x4*>(Sg + (size_t)(rg + M::RG * r) * D + 4 * cg);
-    __syncthreads();   // osw / kq / previous head's `red` reads are complete
+    lds_barrier();   // osw / kq / previous head's `red` reads are complete
     float p1[4] = {0.f, 0.f, 0.f, 0.f};
     float p2[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         red[(wv * M::CG + cg) * 8 + 4 + x] = p2[x];
       }
     }
-    __syncthreads();
+    lds_barrier();
     float c1[4], c2[4];
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
   }
 
   // ---- store the new token into its slot (every head has read the old entry)
-  __syncthreads();
+  lds_barrier();
   for (int i = tid; i < D; i += kDecThreads) {
     kc[kvbase + (size_t)slot * D + i] = k[tokkv + i];
     vc[kvbase + (size_t)slot * D + i] = v[tokkv + i];

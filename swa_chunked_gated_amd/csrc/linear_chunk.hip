@@ -41,8 +41,10 @@ namespace gdn {
 namespace {
 
 constexpr int kC = 64;          // chunk length
-constexpr int kThreads = 256;   // 4 waves
 constexpr int kSL = 68;         // fp32 stride of the 64x64 solve buffer
+// the 10 lower-triangular 16x16 tiles (row, col) of a 64x64 matrix
+__constant__ const int kTileM[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+__constant__ const int kTileN[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -65,12 +67,12 @@ __device__ __forceinline__ void st16(float* blk, const f32x4& x, int l16, int lg
   for (int i = 0; i < 4; ++i) blk[(4 * lg + i) * kSL + l16] = x[i];
 }
 
-template <class T, int D, int DW, bool GLA>
+template <class T, int D, int NW, int DW, bool GLA>
 struct Smem {
   static constexpr int PAD = 16 / sizeof(T);
   static constexpr int SK = D + PAD;        // stride of [64][D] arrays
   static constexpr int SC = kC + PAD;       // stride of [*][64] arrays
-  static constexpr int DVS = 4 * DW;        // state columns per workgroup
+  static constexpr int DVS = NW * DW;       // state columns per workgroup
   static constexpr int nK = kC * SK;
   static constexpr int nKT = D * SC;
   static constexpr int nVT = DVS * SC;
@@ -93,22 +95,33 @@ struct Smem {
   static constexpr int bytes = bytesT + 4 * (nL + nAl + nGate);
 };
 
-template <class T, int D, int DW, bool GLA>
-__global__ __launch_bounds__(kThreads) void linear_chunk_kernel(
+template <class T, int D, int NW, int DW, bool GLA>
+__global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ a, const float* __restrict__ b, T* __restrict__ o,
     float* __restrict__ state_out, int T_, int H, int Hkv, int n_sink, int window, int flags) {
-  using SM = Smem<T, D, DW, GLA>;
+  using SM = Smem<T, D, NW, DW, GLA>;
+  constexpr int kThreads = 64 * NW;
   constexpr int SK = SM::SK;
   constexpr int SC = SM::SC;
   constexpr int DVS = SM::DVS;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int NT = DW / 16;          // 16-column tiles per wave
   constexpr int MT = D / 16;           // 16-row tiles of the state
-  constexpr int NPK = kC * D / VEC / kThreads;     // K (or Q) 16-byte pieces per thread
-  constexpr int NPV = kC * DVS / VEC / kThreads;   // V pieces per thread
+  // K and V are fetched as dwords: each wave covers 64/NW tokens, each lane
+  // one dword column of TPT consecutive tokens, so a thread can write whole
+  // 16-byte runs of the transposed tiles K^T and V^T.
+  constexpr int EPD = 4 / sizeof(T);              // elements per dword
+  constexpr int TPW = kC / NW;                    // tokens per wave
+  constexpr int DPR = D / EPD;                    // dwords per K row
+  constexpr int TPT = TPW * DPR / 64;             // tokens per thread (K)
+  constexpr int DPRV = DVS / EPD;                 // dwords per V-slice row
+  constexpr int TPTV = TPW * DPRV / 64;           // tokens per thread (V)
+  static_assert(MT % NW == 0 || NW % MT == 0, "wave split of the state rows");
+  constexpr int NPQ = kC * D / VEC / kThreads;    // Q 16-byte pieces per thread
   constexpr int NPA = GLA ? kC * D / 4 / kThreads : 0;
-  static_assert(NPK >= 1 && NPV >= 1, "tile shape");
+  static_assert(DPR <= 64 && 64 % DPR == 0 && DPRV <= 64 && 64 % DPRV == 0, "row shape");
+  static_assert(TPT % 8 == 0 && TPTV % 8 == 0 && NPQ >= 1, "tile shape");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   T* sT = reinterpret_cast<T*>(smem_raw);
@@ -132,13 +145,18 @@ __global__ __launch_bounds__(kThreads) void linear_chunk_kernel(
   const int g = h / G;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = wave_id();
   const int l16 = lane & 15;
   const int lg = lane >> 4;
   const int c0 = sp * DVS;            // first state column of this workgroup
   const int cw = DW * wv;             // first column of this wave inside the slice
   const int iend = T_ - window;       // stream tokens are [n_sink, iend)
   const int nch = iend > n_sink ? (iend - n_sink + kC - 1) / kC : 0;
+  // dword staging coordinates
+  const int kdc = lane % DPR;                       // K dword column
+  const int kr0 = TPW * wv + TPT * (lane / DPR);    // first token row
+  const int vdc = lane % DPRV;
+  const int vr0 = TPW * wv + TPTV * (lane / DPRV);
 
   // zero the solve buffer and the score tiles once: their strictly upper
   // parts are never written again
@@ -154,40 +172,42 @@ __global__ __launch_bounds__(kThreads) void linear_chunk_kernel(
 
   // ---------------- register prefetch of one chunk's inputs
   typedef typename Vec16<T>::type V16;
-  V16 pk[NPK], pq[NPK], pv[NPV];
+  uint32_t pk[TPT], pv[TPTV];
+  V16 pq[NPQ];
   f32x4 pa[GLA ? NPA : 1];
   float pg = 1.f;   // GDN: a (threads 0..63) or b (threads 64..127)
 
+  const size_t kvstride = (size_t)Hkv * D;           // elements between tokens
+  const size_t qstride = (size_t)H * D;
   auto prefetch = [&](int c) {
     const int i0 = n_sink + c * kC;
+    const bool full = i0 + kC <= iend;               // uniform: no masking needed
+    const T* kp = k + ((size_t)(bi * T_ + i0 + kr0) * Hkv + g) * D + kdc * EPD;
+    const T* vp = v + ((size_t)(bi * T_ + i0 + vr0) * Hkv + g) * D + c0 + vdc * EPD;
+    if (full) {
 #pragma unroll
-    for (int n = 0; n < NPK; ++n) {
+      for (int j = 0; j < TPT; ++j) pk[j] = *reinterpret_cast<const uint32_t*>(kp + j * kvstride);
+#pragma unroll
+      for (int j = 0; j < TPTV; ++j) pv[j] = *reinterpret_cast<const uint32_t*>(vp + j * kvstride);
+    } else {
+#pragma unroll
+      for (int j = 0; j < TPT; ++j)
+        pk[j] = i0 + kr0 + j < iend ? *reinterpret_cast<const uint32_t*>(kp + j * kvstride) : 0u;
+#pragma unroll
+      for (int j = 0; j < TPTV; ++j)
+        pv[j] = i0 + vr0 + j < iend ? *reinterpret_cast<const uint32_t*>(vp + j * kvstride) : 0u;
+    }
+    const T* qp = q + ((size_t)(bi * T_ + i0 + window) * H + h) * D;
+#pragma unroll
+    for (int n = 0; n < NPQ; ++n) {
       const int j = tid + n * kThreads;
       const int r = j / (D / VEC);
       const int cc = (j % (D / VEC)) * VEC;
-      const int tok = i0 + r;
-      if (tok < iend) {
-        pk[n] = *reinterpret_cast<const V16*>(k + ((size_t)(bi * T_ + tok) * Hkv + g) * D + cc);
-        pq[n] = *reinterpret_cast<const V16*>(q + ((size_t)(bi * T_ + tok + window) * H + h) * D + cc);
+      if (full || i0 + r < iend) {
+        pq[n] = *reinterpret_cast<const V16*>(qp + r * qstride + cc);
       } else {
 #pragma unroll
-        for (int x = 0; x < VEC; ++x) {
-          pk[n][x] = from_f32<T>(0.f);
-          pq[n][x] = from_f32<T>(0.f);
-        }
-      }
-    }
-#pragma unroll
-    for (int n = 0; n < NPV; ++n) {
-      const int j = tid + n * kThreads;
-      const int r = j / (DVS / VEC);
-      const int cc = (j % (DVS / VEC)) * VEC;
-      const int tok = i0 + r;
-      if (tok < iend) {
-        pv[n] = *reinterpret_cast<const V16*>(v + ((size_t)(bi * T_ + tok) * Hkv + g) * D + c0 + cc);
-      } else {
-#pragma unroll
-        for (int x = 0; x < VEC; ++x) pv[n][x] = from_f32<T>(0.f);
+        for (int x = 0; x < VEC; ++x) pq[n][x] = from_f32<T>(0.f);
       }
     }
     if (GLA) {
@@ -209,25 +229,19 @@ __global__ __launch_bounds__(kThreads) void linear_chunk_kernel(
   };
 
   auto commit = [&]() {
+    // K row-major (one dword per token) and transposed (16-byte runs)
 #pragma unroll
-    for (int n = 0; n < NPK; ++n) {
+    for (int j = 0; j < TPT; ++j) *reinterpret_cast<uint32_t*>(&Ks[(kr0 + j) * SK + kdc * EPD]) = pk[j];
+#pragma unroll
+    for (int e = 0; e < EPD; ++e) store_column<T, TPT>(&KTs[(kdc * EPD + e) * SC + kr0], pk, e);
+#pragma unroll
+    for (int e = 0; e < EPD; ++e) store_column<T, TPTV>(&VTs[(vdc * EPD + e) * SC + vr0], pv, e);
+#pragma unroll
+    for (int n = 0; n < NPQ; ++n) {
       const int j = tid + n * kThreads;
       const int r = j / (D / VEC);
       const int cc = (j % (D / VEC)) * VEC;
-      *reinterpret_cast<V16*>(&Ks[r * SK + cc]) = pk[n];
       *reinterpret_cast<V16*>(&Qs[r * SK + cc]) = pq[n];
-      if (!GLA) {
-#pragma unroll
-        for (int x = 0; x < VEC; ++x) KTs[(cc + x) * SC + r] = pk[n][x];
-      }
-    }
-#pragma unroll
-    for (int n = 0; n < NPV; ++n) {
-      const int j = tid + n * kThreads;
-      const int r = j / (DVS / VEC);
-      const int cc = (j % (DVS / VEC)) * VEC;
-#pragma unroll
-      for (int x = 0; x < VEC; ++x) VTs[(cc + x) * SC + r] = pv[n][x];
     }
     if (GLA) {
 #pragma unroll
@@ -261,9 +275,9 @@ __global__ __launch_bounds__(kThreads) void linear_chunk_kernel(
   for (int c = 0; c < nch; ++c) {
     const int i0 = n_sink + c * kC;
     const int Cc = min(kC, iend - i0);
-    __syncthreads();          // previous chunk's LDS reads are done
+    lds_barrier();          // previous chunk's LDS reads are done
     commit();
-    __syncthreads();
+    lds_barrier();
     if (c + 1 < nch) prefetch(c + 1);
 
     if (GLA) {
@@ -277,21 +291,45 @@ __global__ __launch_bounds__(kThreads) void linear_chunk_kernel(
         }
         GC[tid] = x;
       }
-      __syncthreads();
-      for (int i = tid; i < kC * D; i += kThreads) {
-        const int r = i / D;
-        const int cc = i % D;
-        const float G = Al[i];
-        const float kr = to_f32(Ks[r * SK + cc]);
-        Qs[r * SK + cc] = from_f32<T>(to_f32(Qs[r * SK + cc]) * __expf(fminf(G, 80.f)));
-        Ks[r * SK + cc] = from_f32<T>(kr * __expf(fminf(-G, 80.f)));
-        KTs[cc * SC + r] = from_f32<T>(kr * __expf(fminf(GC[cc] - G, 80.f)));
+      lds_barrier();
+      // row-major Q e^G and K e^-G, 4 channels per task
+      for (int i = tid; i < kC * D / 4; i += kThreads) {
+        const int r = i / (D / 4);
+        const int cc = (i % (D / 4)) * 4;
+        const f32x4 G4 = *reinterpret_cast<const f32x4*>(&Al[r * D + cc]);
+        const f32x4 q4 = load4(&Qs[r * SK + cc]);
+        const f32x4 k4 = load4(&Ks[r * SK + cc]);
+        f32x4 qo, ko;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          qo[x] = q4[x] * __expf(fminf(G4[x], 80.f));
+          ko[x] = k4[x] * __expf(fminf(-G4[x], 80.f));
+        }
+        store4(&Qs[r * SK + cc], qo);
+        store4(&Ks[r * SK + cc], ko);
       }
-      __syncthreads();
+      // transposed K e^{G_C - G}, 8 tokens of one channel per task
+      for (int i = tid; i < D * (kC / 8); i += kThreads) {
+        const int cc = i % D;
+        const int r0 = 8 * (i / D);
+        T* kt = &KTs[cc * SC + r0];
+        const f32x4 k0 = load4(kt);
+        const f32x4 k1 = load4(kt + 4);
+        const float gc = GC[cc];
+        f32x4 o0, o1;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          o0[x] = k0[x] * __expf(fminf(gc - Al[(r0 + x) * D + cc], 80.f));
+          o1[x] = k1[x] * __expf(fminf(gc - Al[(r0 + 4 + x) * D + cc], 80.f));
+        }
+        store4(kt, o0);
+        store4(kt + 4, o1);
+      }
+      lds_barrier();
       // ---- A = [s <= r] (Q e^G)(K e^-G)^T on the 10 lower tiles
-      for (int job = wv; job < 10; job += 4) {
-        int mt = 0, nt = job;
-        while (nt > mt) { nt -= mt + 1; ++mt; }
+      for (int job = wv; job < 10; job += NW) {
+        const int mt = kTileM[job];
+        const int nt = kTileN[job];
         f32x4 acc = zero4();
 #pragma unroll
         for (int p = 0; p < D / 32; ++p)
@@ -304,32 +342,41 @@ __global__ __launch_bounds__(kThreads) void linear_chunk_kernel(
           Aqs[r * SC + s] = from_f32<T>(s <= r ? acc[i] : 0.f);
         }
       }
-      __syncthreads();
+      lds_barrier();
     } else {
       const float* lgs = gate;
       const float* gam = gate + kC;
       const float* bet = gate + 2 * kC;
       // ---- K K^T -> L and Q K^T -> A on the 10 lower 16x16 tiles each
-      for (int job = wv; job < 20; job += 4) {
+      for (int job = wv; job < 20; job += NW) {
         const bool isq = job >= 10;
-        int mt = 0, nt = isq ? job - 10 : job;
-        while (nt > mt) { nt -= mt + 1; ++mt; }
+        const int mt = kTileM[isq ? job - 10 : job];
+        const int nt = kTileN[isq ? job - 10 : job];
         const T* X = isq ? Qs : Ks;
+        // gates of this lane's 4 rows and its column, read before the MFMAs
+        const int r0 = 16 * mt + 4 * lg;
+        const int s = 16 * nt + l16;
+        const f32x4 lr = *reinterpret_cast<const f32x4*>(&lgs[r0]);
+        const f32x4 br = *reinterpret_cast<const f32x4*>(&bet[r0]);
+        const float ls = lgs[s];
+        Frag<T> xa[D / 32], xb[D / 32];
+#pragma unroll
+        for (int p = 0; p < D / 32; ++p) {
+          xa[p] = lds_frag8(&X[(16 * mt + l16) * SK + 32 * p + 8 * lg]);
+          xb[p] = lds_frag8(&Ks[(16 * nt + l16) * SK + 32 * p + 8 * lg]);
+        }
         f32x4 acc = zero4();
 #pragma unroll
-        for (int p = 0; p < D / 32; ++p)
-          acc = mfma(lds_frag8(&X[(16 * mt + l16) * SK + 32 * p + 8 * lg]),
-                     lds_frag8(&Ks[(16 * nt + l16) * SK + 32 * p + 8 * lg]), acc);
-        const int s = 16 * nt + l16;
+        for (int p = 0; p < D / 32; ++p) acc = mfma(xa[p], xb[p], acc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 16 * mt + 4 * lg + i;
-          const float dec = __expf(fminf(lgs[r] - lgs[s], 0.f));
+          const int r = r0 + i;
+          const float dec = __expf(fminf(lr[i] - ls, 0.f));
           if (isq) Aqs[r * SC + s] = from_f32<T>(s <= r ? dec * acc[i] : 0.f);
-          else Lf[r * kSL + s] = s < r ? bet[r] * dec * acc[i] : 0.f;
+          else Lf[r * kSL + s] = s < r ? br[i] * dec * acc[i] : 0.f;
         }
       }
-      __syncthreads();
+      lds_barrier();
       // ---- diagonal 16x16 blocks of (I + L)^-1 by forward substitution
       if (wv == 0) {
         const int blk = lane >> 4;
@@ -346,7 +393,7 @@ __global__ __launch_bounds__(kThreads) void linear_chunk_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) Lb[r * kSL + j] = x[r];
       }
-      __syncthreads();
+      lds_barrier();
       // ---- level 1: X10 = -X11 L10 X00, X32 = -X33 L32 X22
       if (wv < 2) {
         const int o0 = wv == 0 ? 0 : 32;
@@ -357,48 +404,70 @@ __global__ __launch_bounds__(kThreads) void linear_chunk_kernel(
         f32x4 xo = -mm16_acc(X11, y, zero4(), l16, lg);
         st16(Lf + (o0 + 16) * kSL + o0, xo, l16, lg);
       }
-      __syncthreads();
+      lds_barrier();
       // ---- level 2: bottom-left 32x32 block = -X_BR (L_BL X_TL)
       {
-        const int br = 32 + 16 * (wv >> 1);   // block row of Y / X
-        const int bc = 16 * (wv & 1);         // block column
+        const bool act = wv < 4;               // one wave per bottom-left block
+        const int br = 32 + 16 * ((wv >> 1) & 1);   // block row of Y / X
+        const int bc = 16 * (wv & 1);               // block column
         // Y_{br,bc} = sum_k L_{br,k} X_{k,bc}, k over the top-left blocks >= bc
         f32x4 y = zero4();
-        for (int kb = bc; kb < 32; kb += 16) y = mm16(Lf + br * kSL + kb, Lf + kb * kSL + bc, y, l16, lg);
-        __syncthreads();
-        st16(Lf + br * kSL + bc, y, l16, lg);
-        __syncthreads();
+        if (act)
+          for (int kb = bc; kb < 32; kb += 16) y = mm16(Lf + br * kSL + kb, Lf + kb * kSL + bc, y, l16, lg);
+        lds_barrier();
+        if (act) st16(Lf + br * kSL + bc, y, l16, lg);
+        lds_barrier();
         // X_{br,bc} = -sum_k X_{br,k} Y_{k,bc}, k over bottom-right blocks <= br
         f32x4 xo = zero4();
-        for (int kb = 32; kb <= br; kb += 16) xo = mm16(Lf + br * kSL + kb, Lf + kb * kSL + bc, xo, l16, lg);
-        __syncthreads();
-        st16(Lf + br * kSL + bc, -xo, l16, lg);
-        __syncthreads();
+        if (act)
+          for (int kb = 32; kb <= br; kb += 16) xo = mm16(Lf + br * kSL + kb, Lf + kb * kSL + bc, xo, l16, lg);
+        lds_barrier();
+        if (act) st16(Lf + br * kSL + bc, -xo, l16, lg);
+        lds_barrier();
       }
-      // ---- Tm diag(b) and Tm diag(b gamma)
-      for (int i = tid; i < kC * kC; i += kThreads) {
-        const int r = i >> 6;
-        const int s = i & 63;
-        const float tm = Lf[r * kSL + s];
-        TBs[r * SC + s] = from_f32<T>(tm * bet[s]);
-        TBGs[r * SC + s] = from_f32<T>(tm * bet[s] * gam[s]);
+      // ---- Tm diag(b) and Tm diag(b gamma), 4 columns per task
+      for (int i = tid; i < kC * kC / 4; i += kThreads) {
+        const int r = i >> 4;
+        const int s0 = (i & 15) * 4;
+        const f32x4 tm = *reinterpret_cast<const f32x4*>(&Lf[r * kSL + s0]);
+        const f32x4 bb = *reinterpret_cast<const f32x4*>(&bet[s0]);
+        const f32x4 gg = *reinterpret_cast<const f32x4*>(&gam[s0]);
+        const f32x4 tb = tm * bb;
+        store4(&TBs[r * SC + s0], tb);
+        store4(&TBGs[r * SC + s0], tb * gg);
       }
-      __syncthreads();
-      // ---- Wm^T = K^T (Tm diag(b gamma))^T, stored as -Wm [token][dk]
-      for (int job = wv; job < MT * 4; job += 4) {
-        const int mt = job >> 2;    // dk tile
-        const int nt = job & 3;     // token tile
-        f32x4 acc = zero4();
+      lds_barrier();
+      // ---- Wm^T = K^T (Tm diag(b gamma))^T, stored as -Wm [token][dk];
+      // each wave owns MT/NW dk tiles and reuses the TBG fragments
+      if (wv < MT) {
+        Frag<T> tbg[4][2];
 #pragma unroll
-        for (int p = 0; p < 2; ++p)
-          acc = mfma(lds_frag8(&KTs[(16 * mt + l16) * SC + 32 * p + 8 * lg]),
-                     lds_frag8(&TBGs[(16 * nt + l16) * SC + 32 * p + 8 * lg]), acc);
-        store4(&Wms[(16 * nt + l16) * SK + 16 * mt + 4 * lg], -acc);
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int p = 0; p < 2; ++p) tbg[nt][p] = lds_frag8(&TBGs[(16 * nt + l16) * SC + 32 * p + 8 * lg]);
+        constexpr int MPW = MT >= NW ? MT / NW : 1;
+#pragma unroll
+        for (int mi = 0; mi < MPW; ++mi) {
+          const int mt = wv * MPW + mi;
+          Frag<T> kf[2];
+#pragma unroll
+          for (int p = 0; p < 2; ++p) kf[p] = lds_frag8(&KTs[(16 * mt + l16) * SC + 32 * p + 8 * lg]);
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int p = 0; p < 2; ++p) acc = mfma(kf[p], tbg[nt][p], acc);
+            store4(&Wms[(16 * nt + l16) * SK + 16 * mt + 4 * lg], -acc);
+          }
+        }
       }
-      __syncthreads();
+      lds_barrier();
     }
 
     // ================= per-wave S-dependent products on columns [cw, cw+DW)
+    // Each block below first loads all the LDS fragments it needs and then
+    // issues its MFMAs into independent accumulators, so the LDS latency is
+    // paid once per block rather than once per MFMA.
     Frag<T> sf[D / 32][NT];
 #pragma unroll
     for (int p = 0; p < D / 32; ++p)
@@ -410,29 +479,42 @@ __global__ __launch_bounds__(kThreads) void linear_chunk_kernel(
     for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) ot[dt][rt] = zero4();
-    // O^T = S^T Q^T (+ gate scaling) ...
+    // O^T = S^T Q^T (+ gate scaling) ..., two 32-wide k-steps per block
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
+    for (int ph = 0; ph < D / 64; ++ph) {
+      Frag<T> qf[4][2];
 #pragma unroll
-      for (int p = 0; p < D / 32; ++p) {
-        const T* qrow = &Qs[(16 * rt + l16) * SK + 32 * p + 4 * lg];
-        Frag<T> qf = lds_frag44(qrow, qrow + 16);
+      for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int dt = 0; dt < NT; ++dt) ot[dt][rt] = mfma(sf[p][dt], qf, ot[dt][rt]);
-      }
+        for (int pp = 0; pp < 2; ++pp) {
+          const T* qrow = &Qs[(16 * rt + l16) * SK + 64 * ph + 32 * pp + 4 * lg];
+          qf[rt][pp] = lds_frag44(qrow, qrow + 16);
+        }
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int dt = 0; dt < NT; ++dt) ot[dt][rt] = mfma(sf[2 * ph + pp][dt], qf[rt][pp], ot[dt][rt]);
     }
 
     if (GLA) {
       // ... + V^T A^T
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
+      {
+        Frag<T> vf[NT][2], af[4][2];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          Frag<T> af = lds_frag8(&Aqs[(16 * rt + l16) * SC + 32 * p + 8 * lg]);
 #pragma unroll
-          for (int dt = 0; dt < NT; ++dt)
-            ot[dt][rt] = mfma(lds_frag8(&VTs[(cw + 16 * dt + l16) * SC + 32 * p + 8 * lg]), af, ot[dt][rt]);
+          for (int dt = 0; dt < NT; ++dt) vf[dt][p] = lds_frag8(&VTs[(cw + 16 * dt + l16) * SC + 32 * p + 8 * lg]);
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) af[rt][p] = lds_frag8(&Aqs[(16 * rt + l16) * SC + 32 * p + 8 * lg]);
         }
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int dt = 0; dt < NT; ++dt) ot[dt][rt] = mfma(vf[dt][p], af[rt][p], ot[dt][rt]);
       }
       // S = e^{G_C} o_rows S + (K e^{G_C - G})^T V
       const float* GC = gate;
@@ -444,17 +526,24 @@ __global__ __launch_bounds__(kThreads) void linear_chunk_kernel(
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) S[mt][nt] *= dec;
       }
+      Frag<T> vb[2][NT];
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        Frag<T> vf[NT];
+      for (int p = 0; p < 2; ++p)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) vf[nt] = lds_frag8(&VTs[(cw + 16 * nt + l16) * SC + 32 * p + 8 * lg]);
+        for (int nt = 0; nt < NT; ++nt) vb[p][nt] = lds_frag8(&VTs[(cw + 16 * nt + l16) * SC + 32 * p + 8 * lg]);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          Frag<T> kf = lds_frag8(&KTs[(16 * mt + l16) * SC + 32 * p + 8 * lg]);
+      for (int m4 = 0; m4 < MT / 4; ++m4) {
+        Frag<T> kf[4][2];
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) S[mt][nt] = mfma(kf, vf[nt], S[mt][nt]);
-        }
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int p = 0; p < 2; ++p) kf[i][p] = lds_frag8(&KTs[(16 * (4 * m4 + i) + l16) * SC + 32 * p + 8 * lg]);
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) S[4 * m4 + i][nt] = mfma(kf[i][p], vb[p][nt], S[4 * m4 + i][nt]);
       }
     } else {
       const float* gam = gate + kC;
@@ -464,22 +553,38 @@ __global__ __launch_bounds__(kThreads) void linear_chunk_kernel(
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) U[mt][nt] = zero4();
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      {
+        Frag<T> vf[2][NT], tf[4][2];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          Frag<T> tf = lds_frag8(&TBs[(16 * mt + l16) * SC + 32 * p + 8 * lg]);
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            U[mt][nt] = mfma(tf, lds_frag8(&VTs[(cw + 16 * nt + l16) * SC + 32 * p + 8 * lg]), U[mt][nt]);
+          for (int nt = 0; nt < NT; ++nt) vf[p][nt] = lds_frag8(&VTs[(cw + 16 * nt + l16) * SC + 32 * p + 8 * lg]);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) tf[mt][p] = lds_frag8(&TBs[(16 * mt + l16) * SC + 32 * p + 8 * lg]);
         }
 #pragma unroll
-        for (int p = 0; p < D / 32; ++p) {
-          const T* wrow = &Wms[(16 * mt + l16) * SK + 32 * p + 4 * lg];
-          Frag<T> wf = lds_frag44(wrow, wrow + 16);
+        for (int p = 0; p < 2; ++p)
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) U[mt][nt] = mfma(wf, sf[p][nt], U[mt][nt]);
-        }
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) U[mt][nt] = mfma(tf[mt][p], vf[p][nt], U[mt][nt]);
+      }
+#pragma unroll
+      for (int ph = 0; ph < D / 64; ++ph) {
+        Frag<T> wf[4][2];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp) {
+            const T* wrow = &Wms[(16 * mt + l16) * SK + 64 * ph + 32 * pp + 4 * lg];
+            wf[mt][pp] = lds_frag44(wrow, wrow + 16);
+          }
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) U[mt][nt] = mfma(wf[mt][pp], sf[2 * ph + pp][nt], U[mt][nt]);
       }
       // O^T: scale the S^T Q^T part by gamma of each query column, then + U^T A^T
 #pragma unroll
@@ -488,44 +593,60 @@ __global__ __launch_bounds__(kThreads) void linear_chunk_kernel(
 #pragma unroll
         for (int dt = 0; dt < NT; ++dt) ot[dt][rt] *= gq;
       }
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        Frag<T> uf[NT];
-#pragma unroll
-        for (int dt = 0; dt < NT; ++dt) uf[dt] = frag_from_acc<T>(U[2 * pp][dt], U[2 * pp + 1][dt]);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          const T* arow = &Aqs[(16 * rt + l16) * SC + 32 * pp + 4 * lg];
-          Frag<T> af = lds_frag44(arow, arow + 16);
-#pragma unroll
-          for (int dt = 0; dt < NT; ++dt) ot[dt][rt] = mfma(uf[dt], af, ot[dt][rt]);
-        }
-      }
-      // S = gamma_C S + K^T diag(gamma_C / gamma) U
       const float gC = gam[kC - 1];
       const float lgC = gate[kC - 1];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) S[mt][nt] *= gC;
+      Frag<T> uf[2][NT], us[2][NT];   // U as operand: plain, and scaled by gamma_C / gamma_s
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
-        f32x4 s0, s1;   // gamma_C / gamma_s as exp of a log difference (<= 1)
+        f32x4 s0, s1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           s0[i] = __expf(fminf(lgC - gate[32 * pp + 4 * lg + i], 0.f));
           s1[i] = __expf(fminf(lgC - gate[32 * pp + 16 + 4 * lg + i], 0.f));
         }
-        Frag<T> uf[NT];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) uf[nt] = frag_from_acc_scaled<T>(U[2 * pp][nt], U[2 * pp + 1][nt], s0, s1);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const T* krow = &KTs[(16 * mt + l16) * SC + 32 * pp + 4 * lg];
-          Frag<T> kf = lds_frag44(krow, krow + 16);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) S[mt][nt] = mfma(kf, uf[nt], S[mt][nt]);
+        for (int nt = 0; nt < NT; ++nt) {
+          uf[pp][nt] = frag_from_acc<T>(U[2 * pp][nt], U[2 * pp + 1][nt]);
+          us[pp][nt] = frag_from_acc_scaled<T>(U[2 * pp][nt], U[2 * pp + 1][nt], s0, s1);
         }
+      }
+      {
+        Frag<T> af[4][2];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp) {
+            const T* arow = &Aqs[(16 * rt + l16) * SC + 32 * pp + 4 * lg];
+            af[rt][pp] = lds_frag44(arow, arow + 16);
+          }
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int dt = 0; dt < NT; ++dt) ot[dt][rt] = mfma(uf[pp][dt], af[rt][pp], ot[dt][rt]);
+      }
+      // S = gamma_C S + K^T diag(gamma_C / gamma) U
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) S[mt][nt] *= gC;
+#pragma unroll
+      for (int m4 = 0; m4 < MT / 4; ++m4) {
+        Frag<T> kf[4][2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp) {
+            const T* krow = &KTs[(16 * (4 * m4 + i) + l16) * SC + 32 * pp + 4 * lg];
+            kf[i][pp] = lds_frag44(krow, krow + 16);
+          }
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) S[4 * m4 + i][nt] = mfma(kf[i][pp], us[pp][nt], S[4 * m4 + i][nt]);
       }
     }
 
@@ -570,43 +691,43 @@ __global__ __launch_bounds__(kThreads) void linear_chunk_kernel(
   }
 }
 
-template <class T, int D, int DW, bool GLA>
+template <class T, int D, int NW, int DW, bool GLA>
 hipError_t launch_linear_t(const PrefillArgs& p, hipStream_t s) {
-  using SM = Smem<T, D, DW, GLA>;
-  auto kern = linear_chunk_kernel<T, D, DW, GLA>;
+  using SM = Smem<T, D, NW, DW, GLA>;
+  auto kern = linear_chunk_kernel<T, D, NW, DW, GLA>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, SM::bytes);
   if (e != hipSuccess) return e;
-  const dim3 grid(D / (4 * DW), p.H, p.B);
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), SM::bytes, s, (const T*)p.q, (const T*)p.k,
+  const dim3 grid(D / SM::DVS, p.H, p.B);
+  hipLaunchKernelGGL(kern, grid, dim3(64 * NW), SM::bytes, s, (const T*)p.q, (const T*)p.k,
                      (const T*)p.v, p.a, p.b, (T*)p.o, p.state_out, p.T, p.H, p.Hkv, p.n_sink,
                      p.window, p.flags);
   return hipGetLastError();
 }
 
-// Columns per wave: 32 when there are enough chains to fill the GPU with one
-// workgroup per chain, else 16 (two workgroups per chain).
+// 16 state columns per wave.  d = 128: one workgroup of 8 waves per chain
+// when there are enough chains to fill the GPU, else two workgroups of 4
+// waves per chain.  d = 64: one workgroup of 4 waves.
 template <class T, bool GLA>
 hipError_t launch_linear_d(const PrefillArgs& p, hipStream_t s) {
-  if (p.D == 64) return launch_linear_t<T, 64, 16, GLA>(p, s);
-  if ((size_t)p.B * p.H >= 256) return launch_linear_t<T, 128, 32, GLA>(p, s);
-  return launch_linear_t<T, 128, 16, GLA>(p, s);
+  if (p.D == 64) return launch_linear_t<T, 64, 4, 16, GLA>(p, s);
+  if ((size_t)p.B * p.H >= 256) return launch_linear_t<T, 128, 8, 16, GLA>(p, s);
+  return launch_linear_t<T, 128, 4, 16, GLA>(p, s);
 }
 
 }  // namespace
 
 size_t linear_lds_bytes(int D, int bf16, int gla) {
   if (bf16) {
-    if (D == 64) return gla ? Smem<gdn::bf16, 64, 16, true>::bytes : Smem<gdn::bf16, 64, 16, false>::bytes;
-    return gla ? Smem<gdn::bf16, 128, 32, true>::bytes : Smem<gdn::bf16, 128, 32, false>::bytes;
+    if (D == 64) return gla ? Smem<gdn::bf16, 64, 4, 16, true>::bytes : Smem<gdn::bf16, 64, 4, 16, false>::bytes;
+    return gla ? Smem<gdn::bf16, 128, 8, 16, true>::bytes : Smem<gdn::bf16, 128, 8, 16, false>::bytes;
   }
-  if (D == 64) return gla ? Smem<float, 64, 16, true>::bytes : Smem<float, 64, 16, false>::bytes;
-  return gla ? Smem<float, 128, 32, true>::bytes : Smem<float, 128, 32, false>::bytes;
+  return gla ? Smem<float, 64, 4, 16, true>::bytes : Smem<float, 64, 4, 16, false>::bytes;
 }
 
 hipError_t launch_linear_prefill(const PrefillArgs& p, hipStream_t s) {
   if (p.bf16) return p.gla ? launch_linear_d<bf16, true>(p, s) : launch_linear_d<bf16, false>(p, s);
   if (p.D != 64) return hipErrorInvalidValue;   // fp32 state tiles fit LDS only at d = 64
-  return p.gla ? launch_linear_t<float, 64, 16, true>(p, s) : launch_linear_t<float, 64, 16, false>(p, s);
+  return p.gla ? launch_linear_t<float, 64, 4, 16, true>(p, s) : launch_linear_t<float, 64, 4, 16, false>(p, s);
 }
 
 }  // namespace gdn

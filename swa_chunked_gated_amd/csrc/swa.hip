@@ -32,20 +32,29 @@
 namespace gdn {
 namespace {
 
-constexpr int kKB = 64;   // keys per LDS block
 constexpr int kNQ = 2;    // 16-query tiles per wave
 
-template <class T, int D>
-__global__ __launch_bounds__(512) void swa_kernel(const T* __restrict__ q, const T* __restrict__ k,
-                                                  const T* __restrict__ v, T* __restrict__ o,
-                                                  int T_, int H, int Hkv, int HPW, int QT,
-                                                  int n_sink, int window, int add_from) {
+// Keys per LDS block: 64 for bf16, 32 for fp32 (keeps the register prefetch
+// of a block small).
+template <class T> struct KeyBlock { static constexpr int n = sizeof(T) == 2 ? 64 : 32; };
+
+template <class T, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void swa_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                      const T* __restrict__ v, T* __restrict__ o,
+                                                      int T_, int H, int Hkv, int HPW, int QT,
+                                                      int n_sink, int window, int add_from) {
+  constexpr int KB = KeyBlock<T>::n;
+  constexpr int NTH = 64 * NW;
   constexpr int PAD = 16 / sizeof(T);
   constexpr int SK = D + PAD;      // Ks row stride
-  constexpr int SV = kKB + PAD;    // VTs row stride
-  constexpr int VEC = 16 / sizeof(T);
-  __shared__ __attribute__((aligned(16))) T Ks[kKB * SK];
-  __shared__ __attribute__((aligned(16))) T VTs[D * SV];
+  constexpr int SV = KB + PAD;     // VTs row stride
+  // staging: each thread owns one dword column of KPT consecutive keys
+  constexpr int EPD = 4 / sizeof(T);
+  constexpr int DPR = D / EPD;
+  constexpr int KPT = KB * DPR / NTH;
+  static_assert(NTH % DPR == 0 && KPT >= 4 && KPT % 4 == 0, "staging shape");
+  __shared__ __attribute__((aligned(16))) T Ks[2][KB * SK];
+  __shared__ __attribute__((aligned(16))) T VTs[2][D * SV];
 
   const int tile = blockIdx.x;
   const int hgrp = blockIdx.y;
@@ -53,10 +62,9 @@ __global__ __launch_bounds__(512) void swa_kernel(const T* __restrict__ q, const
   const int G = H / Hkv;
   const int h0 = hgrp * HPW;
   const int g = h0 / G;
-  const int nthreads = blockDim.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = wave_id();
   const int l16 = lane & 15;
   const int lg = lane >> 4;
   const int NWQ = QT / (16 * kNQ);
@@ -65,6 +73,8 @@ __global__ __launch_bounds__(512) void swa_kernel(const T* __restrict__ q, const
   const int qb = t0 + (wv % NWQ) * 16 * kNQ;      // first query row of this wave
   const int t_end = min(t0 + QT, T_);
   const float scale = kLog2e / sqrtf((float)D);
+  const int sdc = tid % DPR;                       // staging dword column
+  const int sk0 = (tid / DPR) * KPT;               // staging first key of the block
 
   // query fragments (B operand of S^T = K Q^T, "linear" set over d)
   Frag<T> qf[kNQ][D / 32];
@@ -94,43 +104,53 @@ __global__ __launch_bounds__(512) void swa_kernel(const T* __restrict__ q, const
 
   const int sink_end = min(n_sink, t_end);
   const int win_lo = max(n_sink, t0 - window + 1);
-  const int nb_sink = (sink_end + kKB - 1) / kKB;
-  const int nb_win = t_end > win_lo ? (t_end - win_lo + kKB - 1) / kKB : 0;
+  const int nb_sink = (sink_end + KB - 1) / KB;
+  const int nb_win = t_end > win_lo ? (t_end - win_lo + KB - 1) / KB : 0;
+  const int nb = nb_sink + nb_win;
   const int qlast = qb + 16 * kNQ - 1;
 
-  for (int blk = 0; blk < nb_sink + nb_win; ++blk) {
+  // ---- register prefetch of a key block and its commit to an LDS buffer
+  uint32_t pk[KPT], pv[KPT];
+  const size_t kvstride = (size_t)Hkv * D;
+  auto prefetch = [&](int blk) {
     const bool sinkph = blk < nb_sink;
-    const int kb0 = sinkph ? blk * kKB : win_lo + (blk - nb_sink) * kKB;
+    const int kb0 = sinkph ? blk * KB : win_lo + (blk - nb_sink) * KB;
     const int kend = sinkph ? sink_end : t_end;
-
-    // ---- stage K (row-major) and V (transposed) for keys [kb0, kb0 + kKB)
-    for (int i = tid; i < kKB * D / VEC; i += nthreads) {
-      const int r = i / (D / VEC);
-      const int c = (i % (D / VEC)) * VEC;
-      const int key = kb0 + r;
-      typename Vec16<T>::type kv, vv;
-      if (key < kend) {
-        const size_t src = ((size_t)(bi * T_ + key) * Hkv + g) * D + c;
-        kv = *reinterpret_cast<const typename Vec16<T>::type*>(k + src);
-        vv = *reinterpret_cast<const typename Vec16<T>::type*>(v + src);
-      } else {
+    const size_t off = ((size_t)(bi * T_ + kb0 + sk0) * Hkv + g) * D + sdc * EPD;
 #pragma unroll
-        for (int x = 0; x < VEC; ++x) {
-          kv[x] = from_f32<T>(0.f);
-          vv[x] = from_f32<T>(0.f);
-        }
-      }
-      *reinterpret_cast<typename Vec16<T>::type*>(&Ks[r * SK + c]) = kv;
-#pragma unroll
-      for (int x = 0; x < VEC; ++x) VTs[(c + x) * SV + r] = vv[x];
+    for (int j = 0; j < KPT; ++j) {
+      const bool ok = kb0 + sk0 + j < kend;
+      pk[j] = ok ? *reinterpret_cast<const uint32_t*>(k + off + j * kvstride) : 0u;
+      pv[j] = ok ? *reinterpret_cast<const uint32_t*>(v + off + j * kvstride) : 0u;
     }
-    __syncthreads();
-
-    // ---- S^T tiles for this wave
-    bool tile_on[kKB / 16];
-    f32x4 sacc[kKB / 16][kNQ];
+  };
+  auto commit = [&](int buf) {
 #pragma unroll
-    for (int kt = 0; kt < kKB / 16; ++kt) {
+    for (int j = 0; j < KPT; ++j) *reinterpret_cast<uint32_t*>(&Ks[buf][(sk0 + j) * SK + sdc * EPD]) = pk[j];
+#pragma unroll
+    for (int e = 0; e < EPD; ++e) store_column<T, KPT>(&VTs[buf][(sdc * EPD + e) * SV + sk0], pv, e);
+  };
+
+  if (nb > 0) {
+    prefetch(0);
+    commit(0);
+  }
+  lds_barrier();
+
+  for (int blk = 0; blk < nb; ++blk) {
+    const int buf = blk & 1;
+    const bool sinkph = blk < nb_sink;
+    const int kb0 = sinkph ? blk * KB : win_lo + (blk - nb_sink) * KB;
+    const int kend = sinkph ? sink_end : t_end;
+    if (blk + 1 < nb) prefetch(blk + 1);
+    const T* Kb = Ks[buf];
+    const T* Vb = VTs[buf];
+
+    // ---- S^T tiles for this wave (tiles no query of the wave sees are skipped)
+    bool tile_on[KB / 16];
+    f32x4 sacc[KB / 16][kNQ];
+#pragma unroll
+    for (int kt = 0; kt < KB / 16; ++kt) {
       const int k0 = kb0 + 16 * kt;
       bool on = k0 < kend && k0 <= qlast && qb < T_;
       if (!sinkph) on = on && (k0 + 15 > qb - window);
@@ -138,12 +158,13 @@ __global__ __launch_bounds__(512) void swa_kernel(const T* __restrict__ q, const
 #pragma unroll
       for (int nq = 0; nq < kNQ; ++nq) sacc[kt][nq] = zero4();
       if (on) {
+        Frag<T> af[D / 32];
 #pragma unroll
-        for (int p = 0; p < D / 32; ++p) {
-          Frag<T> af = lds_frag8(&Ks[(16 * kt + l16) * SK + 32 * p + 8 * lg]);
+        for (int p = 0; p < D / 32; ++p) af[p] = lds_frag8(&Kb[(16 * kt + l16) * SK + 32 * p + 8 * lg]);
 #pragma unroll
-          for (int nq = 0; nq < kNQ; ++nq) sacc[kt][nq] = mfma(af, qf[nq][p], sacc[kt][nq]);
-        }
+        for (int p = 0; p < D / 32; ++p)
+#pragma unroll
+          for (int nq = 0; nq < kNQ; ++nq) sacc[kt][nq] = mfma(af[p], qf[nq][p], sacc[kt][nq]);
       }
     }
 
@@ -153,15 +174,15 @@ __global__ __launch_bounds__(512) void swa_kernel(const T* __restrict__ q, const
       const int t = qb + 16 * nq + l16;
       float mloc = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < kKB / 16; ++kt) {
+      for (int kt = 0; kt < KB / 16; ++kt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = kb0 + 16 * kt + 4 * lg + i;
           bool valid = tile_on[kt] && key < kend && key <= t && t < T_;
           if (!sinkph) valid = valid && key > t - window;
-          const float s = valid ? sacc[kt][nq][i] * scale : -INFINITY;
-          sacc[kt][nq][i] = s;
-          mloc = fmaxf(mloc, s);
+          const float sc = valid ? sacc[kt][nq][i] * scale : -INFINITY;
+          sacc[kt][nq][i] = sc;
+          mloc = fmaxf(mloc, sc);
         }
       }
       mloc = fmaxf(mloc, shfl_xor(mloc, 16));
@@ -170,11 +191,11 @@ __global__ __launch_bounds__(512) void swa_kernel(const T* __restrict__ q, const
       const float alpha = mnew == -INFINITY ? 1.f : exp2f(mrun[nq] - mnew);
       float psum = 0.f;
 #pragma unroll
-      for (int kt = 0; kt < kKB / 16; ++kt) {
+      for (int kt = 0; kt < KB / 16; ++kt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float s = sacc[kt][nq][i];
-          const float pr = s == -INFINITY ? 0.f : exp2f(s - mnew);
+          const float sc = sacc[kt][nq][i];
+          const float pr = sc == -INFINITY ? 0.f : exp2f(sc - mnew);
           sacc[kt][nq][i] = pr;
           psum += pr;
         }
@@ -187,20 +208,25 @@ __global__ __launch_bounds__(512) void swa_kernel(const T* __restrict__ q, const
 
     // ---- O^T += V^T P^T
 #pragma unroll
-    for (int pp = 0; pp < kKB / 32; ++pp) {
+    for (int pp = 0; pp < KB / 32; ++pp) {
       if (!(tile_on[2 * pp] || tile_on[2 * pp + 1])) continue;
       Frag<T> pf[kNQ];
 #pragma unroll
       for (int nq = 0; nq < kNQ; ++nq) pf[nq] = frag_from_acc<T>(sacc[2 * pp][nq], sacc[2 * pp + 1][nq]);
+      Frag<T> vf[D / 16];
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
-        const T* vrow = &VTs[(16 * dt + l16) * SV + 32 * pp + 4 * lg];
-        Frag<T> vf = lds_frag44(vrow, vrow + 16);
-#pragma unroll
-        for (int nq = 0; nq < kNQ; ++nq) oacc[dt][nq] = mfma(vf, pf[nq], oacc[dt][nq]);
+        const T* vrow = &Vb[(16 * dt + l16) * SV + 32 * pp + 4 * lg];
+        vf[dt] = lds_frag44(vrow, vrow + 16);
       }
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+        for (int nq = 0; nq < kNQ; ++nq) oacc[dt][nq] = mfma(vf[dt], pf[nq], oacc[dt][nq]);
     }
-    __syncthreads();
+
+    if (blk + 1 < nb) commit(buf ^ 1);
+    lds_barrier();
   }
 
   // ---- epilogue
@@ -235,16 +261,21 @@ __global__ void zero_head_rows_kernel(T* __restrict__ o, int T_, int H, int D, i
 
 template <class T, int D>
 hipError_t launch_swa_t(const PrefillArgs& p, int add_from, hipStream_t s) {
+  // heads per workgroup: the largest power of two (<= 8) dividing G
   const int G = p.H / p.Hkv;
   int HPW = 1;
-  for (int c = 1; c <= 8; ++c)
-    if (G % c == 0) HPW = c;
+  while (HPW < 8 && G % (2 * HPW) == 0) HPW *= 2;
   const int QT = HPW <= 4 ? 64 : 32;
   const int waves = HPW * (QT / (16 * kNQ));
   const dim3 grid((p.T + QT - 1) / QT, p.H / HPW, p.B);
-  hipLaunchKernelGGL((swa_kernel<T, D>), grid, dim3(64 * waves), 0, s, (const T*)p.q,
-                     (const T*)p.k, (const T*)p.v, (T*)p.o, p.T, p.H, p.Hkv, HPW, QT, p.n_sink,
-                     p.window, add_from);
+#define GDN_SWA_LAUNCH(NWV)                                                                         \
+  hipLaunchKernelGGL((swa_kernel<T, D, NWV>), grid, dim3(64 * NWV), 0, s, (const T*)p.q,           \
+                     (const T*)p.k, (const T*)p.v, (T*)p.o, p.T, p.H, p.Hkv, HPW, QT, p.n_sink,    \
+                     p.window, add_from)
+  if (waves == 2) GDN_SWA_LAUNCH(2);
+  else if (waves == 4) GDN_SWA_LAUNCH(4);
+  else GDN_SWA_LAUNCH(8);
+#undef GDN_SWA_LAUNCH
   return hipGetLastError();
 }
 
