@@ -217,6 +217,25 @@ def bench_decode(steps=1000, warmup=10):
     }
 
 
+def bench_copy(mib=1024, reps=3):
+    """A plain device copy of known size: the reference the HBM byte counters
+    (FETCH_SIZE, WRITE_SIZE) are scaled by, and the practical read+write roof."""
+    n = mib * 2**20 // 4
+    x = torch.randn(n, device="cuda")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"workload": f"device copy of {mib} MiB (fp32)", "bytes_read": 4 * n, "bytes_written": 4 * n,
+            "us_per_copy": ms * 1e3, "read_plus_write_GBps": 8 * n / (ms * 1e-3) / 1e9}
+
+
 def bench_prefill_cfg(name, steps=5, warmup=2):
     import swa_chunked_gated_amd as gl
     from workloads import WORKLOADS, make_prefill_inputs
@@ -261,7 +280,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default="all",
-                    choices=["all", "main", "decode", "longctx", "qwen32b"])
+                    choices=["all", "main", "decode", "longctx", "qwen32b", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -274,7 +293,10 @@ def main():
     torch.cuda.set_device(0)
 
     if args.only == "decode":
-        print(json.dumps(bench_decode()), flush=True)
+        print(json.dumps(bench_decode(steps=args.steps, warmup=args.warmup)), flush=True)
+        return
+    if args.only == "copy":
+        print(json.dumps(bench_copy()), flush=True)
         return
     if args.only in ("longctx", "qwen32b"):
         names = ["longctx_b8_t32768"] if args.only == "longctx" else \

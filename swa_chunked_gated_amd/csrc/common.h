@@ -15,6 +15,12 @@
 // without leaving registers, either as the B operand of (.)X or as the A
 // operand of X^T(.).
 //
+// LDS tiles store their reduction dimension in "acc order": inside each
+// 32-wide block, logical index c = 16h + 4g + i sits at position 8g + 4h + i.
+// The "acc" set of lane group g is then the 8 contiguous positions 8g..8g+7,
+// so every operand read from LDS is one 16-byte access, and any product
+// whose two LDS operands share that order reduces over the same indices.
+//
 // fp32 inputs use a split-bf16 product: x = hi + lo with hi = bf16(x),
 // lo = bf16(x - hi), and a*b ~ hi*hi + hi*lo + lo*hi (relative error about
 // 2^-16), keeping one code path and one operand layout for both precisions.
@@ -33,6 +39,18 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// logical index -> position in acc order, and back
+__host__ __device__ __forceinline__ constexpr int acc_pos(int c) {
+  return (c & ~31) | ((c & 12) << 1) | ((c & 16) >> 2) | (c & 3);
+}
+__host__ __device__ __forceinline__ constexpr int acc_idx(int p) {
+  return (p & ~31) | ((p & 4) << 2) | ((p & 24) >> 1) | (p & 3);
+}
+static_assert(acc_pos(0) == 0 && acc_pos(4) == 8 && acc_pos(16) == 4 && acc_pos(20) == 12 &&
+              acc_pos(31) == 31 && acc_pos(45) == 57, "acc order");
+static_assert(acc_idx(acc_pos(7)) == 7 && acc_idx(acc_pos(29)) == 29 && acc_idx(acc_pos(63)) == 63,
+              "acc order inverse");
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
@@ -192,6 +210,25 @@ __device__ __forceinline__ void store_column(T* dst, const uint32_t (&w)[N], int
 #pragma unroll
     for (int m = 0; m < N / 4; ++m)
       *reinterpret_cast<uint4*>(dst + 4 * m) = uint4{w[4 * m], w[4 * m + 1], w[4 * m + 2], w[4 * m + 3]};
+  }
+}
+
+// Same, for a tile whose reduction dimension is kept in acc order: the N
+// logical rows key0 .. key0+N-1 (key0 a multiple of 4) are written as runs
+// of 4, each contiguous at position acc_pos(key0 + 4m) of the column.
+template <class T, int N>
+__device__ __forceinline__ void store_column_acc(T* col, int key0, const uint32_t (&w)[N], int e) {
+  static_assert(N % 4 == 0, "column length");
+#pragma unroll
+  for (int m = 0; m < N / 4; ++m) {
+    T* dst = col + acc_pos(key0 + 4 * m);
+    if constexpr (sizeof(T) == 2) {
+      uint32_t p0 = ((w[4 * m] >> (16 * e)) & 0xFFFFu) | (((w[4 * m + 1] >> (16 * e)) & 0xFFFFu) << 16);
+      uint32_t p1 = ((w[4 * m + 2] >> (16 * e)) & 0xFFFFu) | (((w[4 * m + 3] >> (16 * e)) & 0xFFFFu) << 16);
+      *reinterpret_cast<uint2*>(dst) = uint2{p0, p1};
+    } else {
+      *reinterpret_cast<uint4*>(dst) = uint4{w[4 * m], w[4 * m + 1], w[4 * m + 2], w[4 * m + 3]};
+    }
   }
 }
 

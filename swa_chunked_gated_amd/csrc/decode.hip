@@ -8,13 +8,13 @@
 // e = t - window, is folded into the per-head recurrent state with its own
 // gates, and the state is read with q_t.  The two outputs are summed.
 //
-// Work split: one workgroup per (sequence, KV head).  It reads the evicted
-// ring slot and every cached key/value once for the G query heads of the
-// group, then streams each head's d x d fp32 state through registers exactly
-// once (one read, one write).  The new token is written into the freed ring
-// slot only after a workgroup barrier, so every head of the group has read
-// the evicted entry first.  `pos` is advanced by a second tiny kernel so that
-// no workgroup can see another's increment.
+// Work split: one workgroup per (sequence, query head).  Its d x d fp32
+// state is streamed through registers exactly once (one read, one write);
+// the loads are issued first so they overlap the softmax over the cached
+// rows.  The G heads of a KV group are mapped to one XCD so the cached rows
+// they share are fetched from HBM once.  A second small kernel (one
+// workgroup per sequence) then writes the new token into the freed slot and
+// advances pos, after every head has read the evicted entry.
 //
 // Gated delta rule in one pass over the old state S (a, b: evicted gates):
 //   c1 = S^T k_e, c2 = S^T q, u = b (v_e - a c1)
@@ -29,6 +29,7 @@ namespace {
 
 constexpr int kDecThreads = 256;
 constexpr int kMaxG = 16;
+constexpr int kSlotChunk = 64;   // cache rows staged in LDS at a time
 
 template <int D>
 struct StateMap {
@@ -41,13 +42,26 @@ template <class T, bool GLA, int D>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ a, const float* __restrict__ b, float* __restrict__ state,
-    T* __restrict__ kc, T* __restrict__ vc, float* __restrict__ ac, float* __restrict__ bc,
-    const int* __restrict__ pos, T* __restrict__ o, int H, int Hkv, int n_sink, int window,
-    int flags) {
+    const T* __restrict__ kc, const T* __restrict__ vc, const float* __restrict__ ac,
+    const float* __restrict__ bc, const int* __restrict__ pos, T* __restrict__ o, int B, int H,
+    int Hkv, int n_sink, int window, int flags) {
   using M = StateMap<D>;
-  const int g = blockIdx.x;
-  const int bi = blockIdx.y;
   const int G = H / Hkv;
+  // block -> (KV group, head in group); the G heads of a group share
+  // blockIdx.x mod 8 so they run on one XCD and share its L2 for the cache rows
+  const int NG = B * Hkv;
+  int grp, hh;
+  const int x = blockIdx.x;
+  if (NG % 8 == 0) {
+    grp = (x / (8 * G)) * 8 + x % 8;
+    hh = (x / 8) % G;
+  } else {
+    grp = x / G;
+    hh = x % G;
+  }
+  const int bi = grp / Hkv;
+  const int g = grp % Hkv;
+  const int h = g * G + hh;
   const int N = n_sink + window;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -59,27 +73,36 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
   const int slot = t < n_sink ? t : n_sink + (t - n_sink) % window;
   const int ring = t < n_sink ? -1 : (t - n_sink) % window;
 
+  // ---- the head's state is streamed once: issue its loads before anything else
+  const int cg = tid % M::CG;
+  const int rg = tid / M::CG;
+  float* Sg = state + (size_t)(bi * H + h) * D * D;
+  f32x4 s[M::R];
+#pragma unroll
+  for (int r = 0; r < M::R; ++r)
+    s[r] = *reinterpret_cast<const f32x4*>(Sg + (size_t)(rg + M::RG * r) * D + 4 * cg);
+
   extern __shared__ float sm[];
-  float* qs = sm;                       // [G][D]   queries of the group
-  float* kt = qs + G * D;               // [D]      new key
-  float* vt = kt + D;                   // [D]      new value
-  float* ke = vt + D;                   // [D]      evicted key
-  float* ve = ke + D;                   // [D]      evicted value
-  float* ae = ve + D;                   // [G] or [G][D] evicted a
-  float* be = ae + (GLA ? G * D : G);   // [G]      evicted b
-  float* kq = be + G;                   // [G]      k_e . q_h
-  float* osw = kq + G;                  // [G][D]   softmax output
-  float* red = osw + G * D;             // [4][CG][8] cross-wave partials
-  float* lg = red + 4 * M::CG * 8;      // [G][N]   logits, then probabilities
+  float* qs = sm;                       // [D]   query of this head
+  float* kt = qs + D;                   // [D]   new key
+  float* vt = kt + D;                   // [D]   new value
+  float* ke = vt + D;                   // [D]   evicted key
+  float* ve = ke + D;                   // [D]   evicted value
+  float* ae = ve + D;                   // [D]   evicted a (GLA: per channel; GDN: ae[0])
+  float* misc = ae + D;                 // [4]   b_e, k_e . q
+  float* osw = misc + 4;                // [D]   softmax output
+  float* red = osw + D;                 // [4][CG][8] cross-wave partials
+  float* lg = red + 4 * M::CG * 8;      // [N]   logits, then probabilities
+  int* slot_state = reinterpret_cast<int*>(lg + N);                      // [N]
+  // [64][D + pad] staged cache rows, 16-byte aligned
+  T* kvs = reinterpret_cast<T*>((reinterpret_cast<uintptr_t>(slot_state + N) + 15) & ~(uintptr_t)15);
 
   const size_t kvbase = (size_t)(bi * Hkv + g) * N * D;     // cache [B][Hkv][N][D]
   const size_t tokkv = (size_t)(bi * Hkv + g) * D;          // k, v  [B][Hkv][D]
-  const int h0 = g * G;
 
   // ---- stage the small per-step vectors in LDS
-  for (int i = tid; i < G * D; i += kDecThreads)
-    qs[i] = to_f32(q[(size_t)(bi * H + h0) * D + i]);
   for (int i = tid; i < D; i += kDecThreads) {
+    qs[i] = to_f32(q[(size_t)(bi * H + h) * D + i]);
     kt[i] = to_f32(k[tokkv + i]);
     vt[i] = to_f32(v[tokkv + i]);
     if (evict) {
@@ -88,248 +111,256 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     }
   }
   if (evict) {
-    const size_t gb = ((size_t)bi * window + ring) * H + h0;   // gate cache [B][W][H](,D)
+    const size_t gb = ((size_t)bi * window + ring) * H + h;   // gate cache [B][W][H](,D)
     if (GLA) {
-      for (int i = tid; i < G * D; i += kDecThreads) ae[i] = ac[gb * D + i];
-    } else {
-      for (int i = tid; i < G; i += kDecThreads) ae[i] = ac[gb + i];
+      for (int i = tid; i < D; i += kDecThreads) ae[i] = ac[gb * D + i];
+    } else if (tid == 0) {
+      ae[0] = ac[gb];
+      misc[0] = bc[gb];
     }
-    if (!GLA)
-      for (int i = tid; i < G; i += kDecThreads) be[i] = bc[gb + i];
   }
   lds_barrier();
-
-  // ---- k_e . q_h per head
-  if (evict) {
-    for (int hh = wv; hh < G; hh += kDecThreads / 64) {
-      float s = 0.f;
-      for (int i = lane; i < D; i += 64) s += ke[i] * qs[hh * D + i];
-      s = wave_sum(s);
-      if (lane == 0) kq[hh] = s;
-    }
+  if (evict && wv == 0) {
+    float acc = 0.f;
+    for (int i = lane; i < D; i += 64) acc += ke[i] * qs[i];
+    acc = wave_sum(acc);
+    if (lane == 0) misc[1] = acc;   // k_e . q
   }
 
-  // ---- softmax branch: logits over the N cache slots (new token in its slot)
+  // ---- softmax branch over the N cache slots (the new token in its slot).
+  // Slot states are computed once; cached K and V rows are staged through
+  // LDS 64 slots at a time with coalesced 16-byte loads.
   const bool do_swa = (flags & 2) != 0;
   if (do_swa) {
     const float scale = 1.0f / sqrtf((float)D);
     for (int j = tid; j < N; j += kDecThreads) {
-      bool valid;
-      bool isnew;
+      int st;   // -1: not attended, 0: cached entry, 1: the new token
       if (j < n_sink) {
-        valid = j <= t;
-        isnew = j == t;
+        st = j < t ? 0 : (j == t ? 1 : -1);
       } else if (t < n_sink) {
-        valid = false;
-        isnew = false;
+        st = -1;
       } else {
         const int r = j - n_sink;
         const int back = ((t - n_sink - r) % window + window) % window;
-        const int tok = t - back;               // latest token of this ring slot
-        valid = tok >= n_sink;
-        isnew = back == 0;
+        st = back == 0 ? 1 : (t - back >= n_sink ? 0 : -1);   // latest token of this ring slot
       }
-      float acc[kMaxG];
-#pragma unroll
-      for (int hh = 0; hh < kMaxG; ++hh) acc[hh] = 0.f;
-      if (valid) {
-        for (int d0 = 0; d0 < D; d0 += 4) {
-          float kk[4];
-          if (isnew) {
-#pragma unroll
-            for (int x = 0; x < 4; ++x) kk[x] = kt[d0 + x];
-          } else {
-            f32x4 t4 = load4(kc + kvbase + (size_t)j * D + d0);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) kk[x] = t4[x];
-          }
-#pragma unroll
-          for (int hh = 0; hh < kMaxG; ++hh) {
-            if (hh < G) {
-#pragma unroll
-              for (int x = 0; x < 4; ++x) acc[hh] += kk[x] * qs[hh * D + d0 + x];
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int hh = 0; hh < kMaxG; ++hh)
-        if (hh < G) lg[hh * N + j] = valid ? acc[hh] * scale : -INFINITY;
+      slot_state[j] = st;
     }
     lds_barrier();
-    for (int hh = wv; hh < G; hh += kDecThreads / 64) {
-      float m = -INFINITY;
-      for (int j = lane; j < N; j += 64) m = fmaxf(m, lg[hh * N + j]);
-      m = wave_max(m);
-      float s = 0.f;
-      for (int j = lane; j < N; j += 64) {
-        const float x = lg[hh * N + j];
-        const float p = x == -INFINITY ? 0.f : __expf(x - m);
-        lg[hh * N + j] = p;
-        s += p;
-      }
-      s = wave_sum(s);
-      const float inv = 1.0f / s;
-      for (int j = lane; j < N; j += 64) lg[hh * N + j] *= inv;
-    }
-    lds_barrier();
-    {
-      const int c = tid % D;
-      const int hg = tid / D;
-      constexpr int HS = kDecThreads / D;
-      float acc[kMaxG];
-#pragma unroll
-      for (int x = 0; x < kMaxG; ++x) acc[x] = 0.f;
-      for (int j = 0; j < N; ++j) {
-        // probability 0 marks invalid slots; skip their (possibly unwritten) rows
-        bool any = false;
-        for (int hh = hg; hh < G; hh += HS) any |= lg[hh * N + j] != 0.f;
-        if (!any) continue;
-        bool isnew;
-        if (j < n_sink) {
-          isnew = j == t;
+    constexpr int VEC = 16 / sizeof(T);
+    for (int j0 = 0; j0 < N; j0 += kSlotChunk) {
+      const int nj = min(kSlotChunk, N - j0);
+      for (int i = tid; i < nj * (D / VEC); i += kDecThreads) {
+        const int jj = i / (D / VEC);
+        const int c = (i % (D / VEC)) * VEC;
+        const int st = slot_state[j0 + jj];
+        typename Vec16<T>::type kv;
+        if (st == 0) {
+          kv = *reinterpret_cast<const typename Vec16<T>::type*>(kc + kvbase + (size_t)(j0 + jj) * D + c);
         } else {
-          const int r = j - n_sink;
-          isnew = ((t - n_sink - r) % window + window) % window == 0;
-        }
-        const float vv = isnew ? vt[c] : to_f32(vc[kvbase + (size_t)j * D + c]);
 #pragma unroll
-        for (int x = 0; x < kMaxG; ++x) {
-          const int hh = hg + x * HS;
-          if (hh < G) acc[x] += lg[hh * N + j] * vv;
+          for (int xx = 0; xx < VEC; ++xx) kv[xx] = from_f32<T>(st == 1 ? kt[c + xx] : 0.f);
         }
+        *reinterpret_cast<typename Vec16<T>::type*>(&kvs[jj * (D + VEC) + c]) = kv;
       }
+      lds_barrier();
+      // 4 threads per slot, each a quarter of the dot product (all 256 threads
+      // take part: nj * 4 <= 256, and inactive slots compute on zeros)
+      {
+        const int jj = tid >> 2;
+        const int part = tid & 3;
+        float acc = 0.f;
+        if (jj < nj) {
+#pragma unroll 8
+          for (int d = part * (D / 4); d < (part + 1) * (D / 4); ++d)
+            acc += to_f32(kvs[jj * (D + VEC) + d]) * qs[d];
+        }
+        acc += shfl_xor(acc, 1);
+        acc += shfl_xor(acc, 2);
+        if (part == 0 && jj < nj) lg[j0 + jj] = slot_state[j0 + jj] >= 0 ? acc * scale : -INFINITY;
+      }
+      lds_barrier();
+    }
+    if (wv == 0) {
+      float m = -INFINITY;
+      for (int j = lane; j < N; j += 64) m = fmaxf(m, lg[j]);
+      m = wave_max(m);
+      float sum = 0.f;
+      for (int j = lane; j < N; j += 64) {
+        const float xv = lg[j];
+        const float pr = xv == -INFINITY ? 0.f : __expf(xv - m);
+        lg[j] = pr;
+        sum += pr;
+      }
+      sum = wave_sum(sum);
+      const float inv = 1.0f / sum;
+      for (int j = lane; j < N; j += 64) lg[j] *= inv;
+    }
+    {
+      // 256 threads: column c and slot phase sph (256 / D phases), reduced at the end
+      constexpr int SPH = kDecThreads / D;
+      const int c = tid % D;
+      const int sph = tid / D;
+      float acc = 0.f;
+      for (int j0 = 0; j0 < N; j0 += kSlotChunk) {
+        const int nj = min(kSlotChunk, N - j0);
+        lds_barrier();   // probabilities are final / previous chunk's reads are done
+        for (int i = tid; i < nj * (D / VEC); i += kDecThreads) {
+          const int jj = i / (D / VEC);
+          const int cc = (i % (D / VEC)) * VEC;
+          const int st = slot_state[j0 + jj];
+          typename Vec16<T>::type vv;
+          if (st == 0) {
+            vv = *reinterpret_cast<const typename Vec16<T>::type*>(vc + kvbase + (size_t)(j0 + jj) * D + cc);
+          } else {
 #pragma unroll
-      for (int x = 0; x < kMaxG; ++x) {
-        const int hh = hg + x * HS;
-        if (hh < G) osw[hh * D + c] = acc[x];
+            for (int xx = 0; xx < VEC; ++xx) vv[xx] = from_f32<T>(st == 1 ? vt[cc + xx] : 0.f);
+          }
+          *reinterpret_cast<typename Vec16<T>::type*>(&kvs[jj * (D + VEC) + cc]) = vv;
+        }
+        lds_barrier();
+        for (int jj = sph; jj < nj; jj += SPH) acc += lg[j0 + jj] * to_f32(kvs[jj * (D + VEC) + c]);
+      }
+      lds_barrier();
+      red[tid] = acc;
+      lds_barrier();
+      if (tid < D) {
+        float tot = 0.f;
+        for (int p2 = 0; p2 < SPH; ++p2) tot += red[p2 * D + tid];
+        osw[tid] = tot;
       }
     }
   }
+  lds_barrier();   // osw, misc and the red buffer are settled
 
-  // ---- linear branch: stream each head's state once
-  const int cg = tid % M::CG;
-  const int rg = tid / M::CG;
-  for (int hh = 0; hh < G; ++hh) {
-    const int h = h0 + hh;
-    float* Sg = state + (size_t)(bi * H + h) * D * D;
-    f32x4 s[M::R];
+  // ---- linear branch: one pass over the state held in registers
+  float p1[4] = {0.f, 0.f, 0.f, 0.f};
+  float p2[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < M::R; ++r) {
+    const int row = rg + M::RG * r;
+    float qr = qs[row];
+    if (GLA && evict) qr *= ae[row];
+    const float kr = evict ? ke[row] : 0.f;
+#pragma unroll
+    for (int xx = 0; xx < 4; ++xx) {
+      p1[xx] += s[r][xx] * kr;
+      p2[xx] += s[r][xx] * qr;
+    }
+  }
+  // reduce over row groups: inside the wave, then across the 4 waves
+#pragma unroll
+  for (int m = M::CG; m < 64; m <<= 1) {
+#pragma unroll
+    for (int xx = 0; xx < 4; ++xx) {
+      p1[xx] += shfl_xor(p1[xx], m);
+      p2[xx] += shfl_xor(p2[xx], m);
+    }
+  }
+  lds_barrier();   // the softmax's use of `red` is over
+  if (lane < M::CG) {
+#pragma unroll
+    for (int xx = 0; xx < 4; ++xx) {
+      red[(wv * M::CG + cg) * 8 + xx] = p1[xx];
+      red[(wv * M::CG + cg) * 8 + 4 + xx] = p2[xx];
+    }
+  }
+  lds_barrier();
+  float c1[4], c2[4];
+#pragma unroll
+  for (int xx = 0; xx < 4; ++xx) {
+    c1[xx] = 0.f;
+    c2[xx] = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      c1[xx] += red[(w * M::CG + cg) * 8 + xx];
+      c2[xx] += red[(w * M::CG + cg) * 8 + 4 + xx];
+    }
+  }
+  float olin[4];
+  if (evict) {
+    const float kqh = misc[1];
+    if (GLA) {
+#pragma unroll
+      for (int xx = 0; xx < 4; ++xx) olin[xx] = c2[xx] + ve[4 * cg + xx] * kqh;
+#pragma unroll
+      for (int r = 0; r < M::R; ++r) {
+        const int row = rg + M::RG * r;
+        const float al = ae[row];
+        const float kr = ke[row];
+#pragma unroll
+        for (int xx = 0; xx < 4; ++xx) s[r][xx] = al * s[r][xx] + kr * ve[4 * cg + xx];
+      }
+    } else {
+      const float al = ae[0];
+      const float bt = misc[0];
+      float u[4];
+#pragma unroll
+      for (int xx = 0; xx < 4; ++xx) {
+        u[xx] = bt * (ve[4 * cg + xx] - al * c1[xx]);
+        olin[xx] = al * c2[xx] + u[xx] * kqh;
+      }
+#pragma unroll
+      for (int r = 0; r < M::R; ++r) {
+        const float kr = ke[rg + M::RG * r];
+#pragma unroll
+        for (int xx = 0; xx < 4; ++xx) s[r][xx] = al * s[r][xx] + kr * u[xx];
+      }
+    }
 #pragma unroll
     for (int r = 0; r < M::R; ++r)
-      s[r] = *reinterpret_cast<const f32x4*>(Sg + (size_t)(rg + M::RG * r) * D + 4 * cg);
-    lds_barrier();   // osw / kq / previous head's `red` reads are complete
-    float p1[4] = {0.f, 0.f, 0.f, 0.f};
-    float p2[4] = {0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(Sg + (size_t)(rg + M::RG * r) * D + 4 * cg) = s[r];
+  } else {
 #pragma unroll
-    for (int r = 0; r < M::R; ++r) {
-      const int row = rg + M::RG * r;
-      float qr = qs[hh * D + row];
-      if (GLA && evict) qr *= ae[hh * D + row];
-      const float kr = evict ? ke[row] : 0.f;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        p1[x] += s[r][x] * kr;
-        p2[x] += s[r][x] * qr;
-      }
-    }
-    // reduce over row groups: inside the wave, then across the 4 waves
-#pragma unroll
-    for (int m = M::CG; m < 64; m <<= 1) {
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        p1[x] += shfl_xor(p1[x], m);
-        p2[x] += shfl_xor(p2[x], m);
-      }
-    }
-    if (lane < M::CG) {
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        red[(wv * M::CG + cg) * 8 + x] = p1[x];
-        red[(wv * M::CG + cg) * 8 + 4 + x] = p2[x];
-      }
-    }
-    lds_barrier();
-    float c1[4], c2[4];
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      c1[x] = 0.f;
-      c2[x] = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        c1[x] += red[(w * M::CG + cg) * 8 + x];
-        c2[x] += red[(w * M::CG + cg) * 8 + 4 + x];
-      }
-    }
-    float olin[4];
-    if (evict) {
-      const float kqh = kq[hh];
-      if (GLA) {
-#pragma unroll
-        for (int x = 0; x < 4; ++x) olin[x] = c2[x] + ve[4 * cg + x] * kqh;
-#pragma unroll
-        for (int r = 0; r < M::R; ++r) {
-          const int row = rg + M::RG * r;
-          const float al = ae[hh * D + row];
-          const float kr = ke[row];
-#pragma unroll
-          for (int x = 0; x < 4; ++x) s[r][x] = al * s[r][x] + kr * ve[4 * cg + x];
-        }
-      } else {
-        const float al = ae[hh];
-        const float bt = be[hh];
-        float u[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          u[x] = bt * (ve[4 * cg + x] - al * c1[x]);
-          olin[x] = al * c2[x] + u[x] * kqh;
-        }
-#pragma unroll
-        for (int r = 0; r < M::R; ++r) {
-          const float kr = ke[rg + M::RG * r];
-#pragma unroll
-          for (int x = 0; x < 4; ++x) s[r][x] = al * s[r][x] + kr * u[x];
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < M::R; ++r)
-        *reinterpret_cast<f32x4*>(Sg + (size_t)(rg + M::RG * r) * D + 4 * cg) = s[r];
-    } else {
-#pragma unroll
-      for (int x = 0; x < 4; ++x) olin[x] = c2[x];
-    }
-    if (rg == 0) {
-      f32x4 out;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        float val = 0.f;
-        if (flags & 1) val += olin[x];
-        if (do_swa) val += osw[hh * D + 4 * cg + x];
-        out[x] = val;
-      }
-      store4(o + (size_t)(bi * H + h) * D + 4 * cg, out);
-    }
+    for (int xx = 0; xx < 4; ++xx) olin[xx] = c2[xx];
   }
-
-  // ---- store the new token into its slot (every head has read the old entry)
-  lds_barrier();
-  for (int i = tid; i < D; i += kDecThreads) {
-    kc[kvbase + (size_t)slot * D + i] = k[tokkv + i];
-    vc[kvbase + (size_t)slot * D + i] = v[tokkv + i];
-  }
-  if (ring >= 0) {
-    const size_t gb = ((size_t)bi * window + ring) * H + h0;
-    if (GLA) {
-      for (int i = tid; i < G * D; i += kDecThreads) ac[gb * D + i] = a[(size_t)(bi * H + h0) * D + i];
-    } else {
-      for (int i = tid; i < G; i += kDecThreads) ac[gb + i] = a[bi * H + h0 + i];
-      for (int i = tid; i < G; i += kDecThreads) bc[gb + i] = b[bi * H + h0 + i];
+  if (rg == 0) {
+    f32x4 out;
+#pragma unroll
+    for (int xx = 0; xx < 4; ++xx) {
+      float val = 0.f;
+      if (flags & 1) val += olin[xx];
+      if (do_swa) val += osw[4 * cg + xx];
+      out[xx] = val;
     }
+    store4(o + (size_t)(bi * H + h) * D + 4 * cg, out);
   }
 }
 
-__global__ void advance_pos_kernel(int* __restrict__ pos, int B) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < B) pos[i] += 1;
+// After every head has read the evicted entry: store the new token in its
+// slot (and its gates at its ring index) and advance pos.  One workgroup per
+// sequence.
+template <class T, bool GLA>
+__global__ __launch_bounds__(256) void decode_commit_kernel(
+    const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ a,
+    const float* __restrict__ b, T* __restrict__ kc, T* __restrict__ vc, float* __restrict__ ac,
+    float* __restrict__ bc, int* __restrict__ pos, int H, int Hkv, int D, int n_sink, int window) {
+  const int bi = blockIdx.x;
+  const int t = pos[bi];
+  if (t < 0) return;
+  const int N = n_sink + window;
+  const int slot = t < n_sink ? t : n_sink + (t - n_sink) % window;
+  for (int i = threadIdx.x; i < Hkv * D; i += blockDim.x) {
+    const int g = i / D;
+    const int d = i % D;
+    const size_t dst = ((size_t)(bi * Hkv + g) * N + slot) * D + d;
+    kc[dst] = k[(size_t)bi * Hkv * D + i];
+    vc[dst] = v[(size_t)bi * Hkv * D + i];
+  }
+  if (t >= n_sink) {
+    const int ring = (t - n_sink) % window;
+    const size_t gb = ((size_t)bi * window + ring) * H;
+    if (GLA) {
+      for (int i = threadIdx.x; i < H * D; i += blockDim.x) ac[gb * D + i] = a[(size_t)bi * H * D + i];
+    } else {
+      for (int i = threadIdx.x; i < H; i += blockDim.x) {
+        ac[gb + i] = a[(size_t)bi * H + i];
+        bc[gb + i] = b[(size_t)bi * H + i];
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) pos[bi] = t + 1;
 }
 
 // Cache contents after a prefill of T tokens: sinks 0..min(n_sink,T)-1 in
@@ -391,13 +422,15 @@ hipError_t launch_decode_t(const DecodeArgs& p, hipStream_t s) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_kernel<T, GLA, D>), dim3(p.Hkv, p.B), dim3(kDecThreads), lds, s,
+  hipLaunchKernelGGL((decode_kernel<T, GLA, D>), dim3(p.B * p.H), dim3(kDecThreads), lds, s,
                      (const T*)p.q, (const T*)p.k, (const T*)p.v, p.a, p.b, p.state,
-                     (T*)p.k_cache, (T*)p.v_cache, p.a_cache, p.b_cache, p.pos, (T*)p.o, p.H,
-                     p.Hkv, p.n_sink, p.window, p.flags);
+                     (const T*)p.k_cache, (const T*)p.v_cache, p.a_cache, p.b_cache, p.pos, (T*)p.o,
+                     p.B, p.H, p.Hkv, p.n_sink, p.window, p.flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(advance_pos_kernel, dim3((p.B + 255) / 256), dim3(256), 0, s, p.pos, p.B);
+  hipLaunchKernelGGL((decode_commit_kernel<T, GLA>), dim3(p.B), dim3(256), 0, s, (const T*)p.k,
+                     (const T*)p.v, p.a, p.b, (T*)p.k_cache, (T*)p.v_cache, p.a_cache, p.b_cache,
+                     p.pos, p.H, p.Hkv, D, p.n_sink, p.window);
   return hipGetLastError();
 }
 
@@ -410,9 +443,12 @@ hipError_t launch_decode_d(const DecodeArgs& p, hipStream_t s) {
 }  // namespace
 
 size_t decode_lds_bytes(int G, int N, int D, int gla) {
-  const size_t floats = (size_t)G * D + 4 * (size_t)D + (gla ? (size_t)G * D : (size_t)G) + 2 * (size_t)G +
-                        (size_t)G * D + 4 * (size_t)(D / 4) * 8 + (size_t)G * N;
-  return floats * sizeof(float);
+  (void)G;
+  (void)gla;
+  const size_t floats = 8 * (size_t)D + 4 + 4 * (size_t)(D / 4) * 8 + (size_t)N;
+  const size_t ints = (size_t)N;
+  const size_t staging = (size_t)kSlotChunk * (D + 8) * sizeof(float);   // fp32 worst case
+  return floats * sizeof(float) + ints * sizeof(int) + 16 + staging;
 }
 
 hipError_t launch_decode(const DecodeArgs& p, hipStream_t s) {

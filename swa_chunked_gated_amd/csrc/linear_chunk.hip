@@ -31,6 +31,8 @@
 // diagonal blocks by forward substitution in fp32, then the off-diagonal
 // blocks by block recursion on fp32 MFMA (exact fp32 products).
 // Chunk c+1's inputs are loaded into registers while chunk c is computed.
+// Every LDS tile keeps its reduction dimension in acc order (see common.h),
+// so all MFMA operand reads are single 16-byte LDS accesses.
 
 #include <algorithm>
 
@@ -229,19 +231,30 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
   };
 
   auto commit = [&]() {
-    // K row-major (one dword per token) and transposed (16-byte runs)
+    // K row-major (one dword per token, columns in acc order) and transposed
+    // (tokens in acc order, runs of 4)
 #pragma unroll
-    for (int j = 0; j < TPT; ++j) *reinterpret_cast<uint32_t*>(&Ks[(kr0 + j) * SK + kdc * EPD]) = pk[j];
+    for (int j = 0; j < TPT; ++j)
+      *reinterpret_cast<uint32_t*>(&Ks[(kr0 + j) * SK + acc_pos(kdc * EPD)]) = pk[j];
 #pragma unroll
-    for (int e = 0; e < EPD; ++e) store_column<T, TPT>(&KTs[(kdc * EPD + e) * SC + kr0], pk, e);
+    for (int e = 0; e < EPD; ++e) store_column_acc<T, TPT>(&KTs[(kdc * EPD + e) * SC], kr0, pk, e);
 #pragma unroll
-    for (int e = 0; e < EPD; ++e) store_column<T, TPTV>(&VTs[(vdc * EPD + e) * SC + vr0], pv, e);
+    for (int e = 0; e < EPD; ++e) store_column_acc<T, TPTV>(&VTs[(vdc * EPD + e) * SC], vr0, pv, e);
 #pragma unroll
     for (int n = 0; n < NPQ; ++n) {
       const int j = tid + n * kThreads;
       const int r = j / (D / VEC);
       const int cc = (j % (D / VEC)) * VEC;
-      *reinterpret_cast<V16*>(&Qs[r * SK + cc]) = pq[n];
+      // runs of 4 logical columns stay contiguous in acc order
+#pragma unroll
+      for (int m = 0; m < VEC / 4; ++m) {
+        T* dst = &Qs[r * SK + acc_pos(cc + 4 * m)];
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<bf16x4*>(dst) = bf16x4{pq[n][4 * m], pq[n][4 * m + 1], pq[n][4 * m + 2], pq[n][4 * m + 3]};
+        } else {
+          *reinterpret_cast<V16*>(dst) = pq[n];
+        }
+      }
     }
     if (GLA) {
 #pragma unroll
@@ -296,19 +309,20 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
       for (int i = tid; i < kC * D / 4; i += kThreads) {
         const int r = i / (D / 4);
         const int cc = (i % (D / 4)) * 4;
+        const int pc = acc_pos(cc);
         const f32x4 G4 = *reinterpret_cast<const f32x4*>(&Al[r * D + cc]);
-        const f32x4 q4 = load4(&Qs[r * SK + cc]);
-        const f32x4 k4 = load4(&Ks[r * SK + cc]);
+        const f32x4 q4 = load4(&Qs[r * SK + pc]);
+        const f32x4 k4 = load4(&Ks[r * SK + pc]);
         f32x4 qo, ko;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           qo[x] = q4[x] * __expf(fminf(G4[x], 80.f));
           ko[x] = k4[x] * __expf(fminf(-G4[x], 80.f));
         }
-        store4(&Qs[r * SK + cc], qo);
-        store4(&Ks[r * SK + cc], ko);
+        store4(&Qs[r * SK + pc], qo);
+        store4(&Ks[r * SK + pc], ko);
       }
-      // transposed K e^{G_C - G}, 8 tokens of one channel per task
+      // transposed K e^{G_C - G}, 8 tokens (acc order) of one channel per task
       for (int i = tid; i < D * (kC / 8); i += kThreads) {
         const int cc = i % D;
         const int r0 = 8 * (i / D);
@@ -319,8 +333,8 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
         f32x4 o0, o1;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          o0[x] = k0[x] * __expf(fminf(gc - Al[(r0 + x) * D + cc], 80.f));
-          o1[x] = k1[x] * __expf(fminf(gc - Al[(r0 + 4 + x) * D + cc], 80.f));
+          o0[x] = k0[x] * __expf(fminf(gc - Al[acc_idx(r0 + x) * D + cc], 80.f));
+          o1[x] = k1[x] * __expf(fminf(gc - Al[acc_idx(r0 + 4 + x) * D + cc], 80.f));
         }
         store4(kt, o0);
         store4(kt + 4, o1);
@@ -339,7 +353,7 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * mt + 4 * lg + i;
           const int s = 16 * nt + l16;
-          Aqs[r * SC + s] = from_f32<T>(s <= r ? acc[i] : 0.f);
+          Aqs[r * SC + acc_pos(s)] = from_f32<T>(s <= r ? acc[i] : 0.f);
         }
       }
       lds_barrier();
@@ -372,7 +386,7 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
         for (int i = 0; i < 4; ++i) {
           const int r = r0 + i;
           const float dec = __expf(fminf(lr[i] - ls, 0.f));
-          if (isq) Aqs[r * SC + s] = from_f32<T>(s <= r ? dec * acc[i] : 0.f);
+          if (isq) Aqs[r * SC + acc_pos(s)] = from_f32<T>(s <= r ? dec * acc[i] : 0.f);
           else Lf[r * kSL + s] = s < r ? br[i] * dec * acc[i] : 0.f;
         }
       }
@@ -433,8 +447,8 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
         const f32x4 bb = *reinterpret_cast<const f32x4*>(&bet[s0]);
         const f32x4 gg = *reinterpret_cast<const f32x4*>(&gam[s0]);
         const f32x4 tb = tm * bb;
-        store4(&TBs[r * SC + s0], tb);
-        store4(&TBGs[r * SC + s0], tb * gg);
+        store4(&TBs[r * SC + acc_pos(s0)], tb);
+        store4(&TBGs[r * SC + acc_pos(s0)], tb * gg);
       }
       lds_barrier();
       // ---- Wm^T = K^T (Tm diag(b gamma))^T, stored as -Wm [token][dk];
@@ -457,7 +471,7 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
             f32x4 acc = zero4();
 #pragma unroll
             for (int p = 0; p < 2; ++p) acc = mfma(kf[p], tbg[nt][p], acc);
-            store4(&Wms[(16 * nt + l16) * SK + 16 * mt + 4 * lg], -acc);
+            store4(&Wms[(16 * nt + l16) * SK + acc_pos(16 * mt + 4 * lg)], -acc);
           }
         }
       }
@@ -487,8 +501,7 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
-          const T* qrow = &Qs[(16 * rt + l16) * SK + 64 * ph + 32 * pp + 4 * lg];
-          qf[rt][pp] = lds_frag44(qrow, qrow + 16);
+          qf[rt][pp] = lds_frag8(&Qs[(16 * rt + l16) * SK + 64 * ph + 32 * pp + 8 * lg]);
         }
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp)
@@ -576,8 +589,7 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int pp = 0; pp < 2; ++pp) {
-            const T* wrow = &Wms[(16 * mt + l16) * SK + 64 * ph + 32 * pp + 4 * lg];
-            wf[mt][pp] = lds_frag44(wrow, wrow + 16);
+            wf[mt][pp] = lds_frag8(&Wms[(16 * mt + l16) * SK + 64 * ph + 32 * pp + 8 * lg]);
           }
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp)
@@ -616,8 +628,7 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
           for (int pp = 0; pp < 2; ++pp) {
-            const T* arow = &Aqs[(16 * rt + l16) * SC + 32 * pp + 4 * lg];
-            af[rt][pp] = lds_frag44(arow, arow + 16);
+            af[rt][pp] = lds_frag8(&Aqs[(16 * rt + l16) * SC + 32 * pp + 8 * lg]);
           }
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp)
@@ -638,8 +649,7 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int pp = 0; pp < 2; ++pp) {
-            const T* krow = &KTs[(16 * (4 * m4 + i) + l16) * SC + 32 * pp + 4 * lg];
-            kf[i][pp] = lds_frag44(krow, krow + 16);
+            kf[i][pp] = lds_frag8(&KTs[(16 * (4 * m4 + i) + l16) * SC + 32 * pp + 8 * lg]);
           }
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp)

@@ -8,8 +8,10 @@
 // current one included.  Logits are q.k / sqrt(d) (section 从 softmax 到
 // delta 规则的一阶近似, Lemma 1).
 //
-// Work split: one workgroup per (sequence, group of query heads sharing one
-// KV head, tile of QT query rows); each wave owns 32 query rows of one head.
+// Work split: one workgroup per (sequence, up to 4 query heads sharing one
+// KV head, run of TPW consecutive tiles of QT query rows); each wave owns 32
+// query rows of one head.  The next key block is fetched into registers
+// while the current one is used from LDS (two LDS buffers), across tiles.
 // Keys are visited in two phases, the sinks [0, n_sink) and then the window
 // [max(n_sink, t0 - window + 1), t_end), so a key in both ranges is counted
 // once.  64-key blocks of K (row-major) and V (transposed) are staged in LDS
@@ -39,9 +41,9 @@ constexpr int kNQ = 2;    // 16-query tiles per wave
 template <class T> struct KeyBlock { static constexpr int n = sizeof(T) == 2 ? 64 : 32; };
 
 template <class T, int D, int NW>
-__global__ __launch_bounds__(64 * NW) void swa_kernel(const T* __restrict__ q, const T* __restrict__ k,
+__global__ __launch_bounds__(64 * NW, 2) void swa_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                       const T* __restrict__ v, T* __restrict__ o,
-                                                      int T_, int H, int Hkv, int HPW, int QT,
+                                                      int T_, int H, int Hkv, int HPW, int QT, int TPW,
                                                       int n_sink, int window, int add_from) {
   constexpr int KB = KeyBlock<T>::n;
   constexpr int NTH = 64 * NW;
@@ -56,7 +58,6 @@ __global__ __launch_bounds__(64 * NW) void swa_kernel(const T* __restrict__ q, c
   __shared__ __attribute__((aligned(16))) T Ks[2][KB * SK];
   __shared__ __attribute__((aligned(16))) T VTs[2][D * SV];
 
-  const int tile = blockIdx.x;
   const int hgrp = blockIdx.y;
   const int bi = blockIdx.z;
   const int G = H / Hkv;
@@ -69,57 +70,49 @@ __global__ __launch_bounds__(64 * NW) void swa_kernel(const T* __restrict__ q, c
   const int lg = lane >> 4;
   const int NWQ = QT / (16 * kNQ);
   const int h = h0 + wv / NWQ;
-  const int t0 = tile * QT;
-  const int qb = t0 + (wv % NWQ) * 16 * kNQ;      // first query row of this wave
-  const int t_end = min(t0 + QT, T_);
+  const int tile0 = blockIdx.x * TPW;                 // first query tile of this workgroup
+  const int ntile = min(TPW, (T_ + QT - 1) / QT - tile0);
   const float scale = kLog2e / sqrtf((float)D);
   const int sdc = tid % DPR;                       // staging dword column
   const int sk0 = (tid / DPR) * KPT;               // staging first key of the block
 
-  // query fragments (B operand of S^T = K Q^T, "linear" set over d)
-  Frag<T> qf[kNQ][D / 32];
-#pragma unroll
-  for (int nq = 0; nq < kNQ; ++nq) {
-    const int t = qb + 16 * nq + l16;
-#pragma unroll
-    for (int p = 0; p < D / 32; ++p) {
-      if (t < T_)
-        qf[nq][p] = gbl_frag8(q + ((size_t)(bi * T_ + t) * H + h) * D + 32 * p + 8 * lg);
-      else
-        qf[nq][p] = zero_frag<T>();
+  // Key blocks of query tile t0: sinks [0, min(n_sink, t_end)) then the
+  // window [max(n_sink, t0 - window + 1), t_end), KB keys per block.
+  struct Blk { int kb0, kend, sink; };
+  auto tile_blocks = [&](int t0, int& nbs, int& nbw, int& sink_end, int& win_lo, int& t_end) {
+    t_end = min(t0 + QT, T_);
+    sink_end = min(n_sink, t_end);
+    win_lo = max(n_sink, t0 - window + 1);
+    nbs = (sink_end + KB - 1) / KB;
+    nbw = t_end > win_lo ? (t_end - win_lo + KB - 1) / KB : 0;
+  };
+  // flat block index over the workgroup's tiles -> block description
+  auto block_at = [&](int flat, Blk& bl) -> bool {
+    for (int ti = 0; ti < ntile; ++ti) {
+      int nbs, nbw, se, wl, te;
+      tile_blocks((tile0 + ti) * QT, nbs, nbw, se, wl, te);
+      if (flat < nbs + nbw) {
+        const bool sk = flat < nbs;
+        bl.kb0 = sk ? flat * KB : wl + (flat - nbs) * KB;
+        bl.kend = sk ? se : te;
+        bl.sink = sk;
+        return true;
+      }
+      flat -= nbs + nbw;
     }
-  }
-
-  f32x4 oacc[D / 16][kNQ];
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-    for (int nq = 0; nq < kNQ; ++nq) oacc[dt][nq] = zero4();
-  float mrun[kNQ], lrun[kNQ];
-#pragma unroll
-  for (int nq = 0; nq < kNQ; ++nq) {
-    mrun[nq] = -INFINITY;
-    lrun[nq] = 0.f;
-  }
-
-  const int sink_end = min(n_sink, t_end);
-  const int win_lo = max(n_sink, t0 - window + 1);
-  const int nb_sink = (sink_end + KB - 1) / KB;
-  const int nb_win = t_end > win_lo ? (t_end - win_lo + KB - 1) / KB : 0;
-  const int nb = nb_sink + nb_win;
-  const int qlast = qb + 16 * kNQ - 1;
+    return false;
+  };
 
   // ---- register prefetch of a key block and its commit to an LDS buffer
   uint32_t pk[KPT], pv[KPT];
   const size_t kvstride = (size_t)Hkv * D;
-  auto prefetch = [&](int blk) {
-    const bool sinkph = blk < nb_sink;
-    const int kb0 = sinkph ? blk * KB : win_lo + (blk - nb_sink) * KB;
-    const int kend = sinkph ? sink_end : t_end;
-    const size_t off = ((size_t)(bi * T_ + kb0 + sk0) * Hkv + g) * D + sdc * EPD;
+  // a thread stages KPT consecutive keys of one dword column; the transposed
+  // V tile keeps its key dimension in acc order (written in runs of 4 keys)
+  auto prefetch = [&](const Blk& bl) {
+    const size_t off = ((size_t)(bi * T_ + bl.kb0 + sk0) * Hkv + g) * D + sdc * EPD;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const bool ok = kb0 + sk0 + j < kend;
+      const bool ok = bl.kb0 + sk0 + j < bl.kend;
       pk[j] = ok ? *reinterpret_cast<const uint32_t*>(k + off + j * kvstride) : 0u;
       pv[j] = ok ? *reinterpret_cast<const uint32_t*>(v + off + j * kvstride) : 0u;
     }
@@ -128,124 +121,196 @@ __global__ __launch_bounds__(64 * NW) void swa_kernel(const T* __restrict__ q, c
 #pragma unroll
     for (int j = 0; j < KPT; ++j) *reinterpret_cast<uint32_t*>(&Ks[buf][(sk0 + j) * SK + sdc * EPD]) = pk[j];
 #pragma unroll
-    for (int e = 0; e < EPD; ++e) store_column<T, KPT>(&VTs[buf][(sdc * EPD + e) * SV + sk0], pv, e);
+    for (int e = 0; e < EPD; ++e) store_column_acc<T, KPT>(&VTs[buf][(sdc * EPD + e) * SV], sk0, pv, e);
   };
 
-  if (nb > 0) {
-    prefetch(0);
-    commit(0);
+  int flat = 0;   // running block counter (selects the LDS buffer)
+  {
+    Blk b0;
+    if (block_at(0, b0)) {
+      prefetch(b0);
+      commit(0);
+    }
   }
   lds_barrier();
 
-  for (int blk = 0; blk < nb; ++blk) {
-    const int buf = blk & 1;
-    const bool sinkph = blk < nb_sink;
-    const int kb0 = sinkph ? blk * KB : win_lo + (blk - nb_sink) * KB;
-    const int kend = sinkph ? sink_end : t_end;
-    if (blk + 1 < nb) prefetch(blk + 1);
-    const T* Kb = Ks[buf];
-    const T* Vb = VTs[buf];
+  for (int ti = 0; ti < ntile; ++ti) {
+    const int t0 = (tile0 + ti) * QT;
+    const int qb = t0 + (wv % NWQ) * 16 * kNQ;      // first query row of this wave
+    const int qlast = qb + 16 * kNQ - 1;
+    int nbs, nbw, sink_end, win_lo, t_end;
+    tile_blocks(t0, nbs, nbw, sink_end, win_lo, t_end);
 
-    // ---- S^T tiles for this wave (tiles no query of the wave sees are skipped)
-    bool tile_on[KB / 16];
-    f32x4 sacc[KB / 16][kNQ];
-#pragma unroll
-    for (int kt = 0; kt < KB / 16; ++kt) {
-      const int k0 = kb0 + 16 * kt;
-      bool on = k0 < kend && k0 <= qlast && qb < T_;
-      if (!sinkph) on = on && (k0 + 15 > qb - window);
-      tile_on[kt] = on;
-#pragma unroll
-      for (int nq = 0; nq < kNQ; ++nq) sacc[kt][nq] = zero4();
-      if (on) {
-        Frag<T> af[D / 32];
-#pragma unroll
-        for (int p = 0; p < D / 32; ++p) af[p] = lds_frag8(&Kb[(16 * kt + l16) * SK + 32 * p + 8 * lg]);
-#pragma unroll
-        for (int p = 0; p < D / 32; ++p)
-#pragma unroll
-          for (int nq = 0; nq < kNQ; ++nq) sacc[kt][nq] = mfma(af[p], qf[nq][p], sacc[kt][nq]);
-      }
-    }
-
-    // ---- mask, online softmax (per lane = per query, 4 lane groups)
+    // query fragments (B operand of S^T = K Q^T, "linear" set over d),
+    // pre-multiplied by log2(e) / sqrt(d) so the scores come out of the MFMA
+    // already in exp2 units
+    Frag<T> qf[kNQ][D / 32];
 #pragma unroll
     for (int nq = 0; nq < kNQ; ++nq) {
       const int t = qb + 16 * nq + l16;
-      float mloc = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < KB / 16; ++kt) {
+      for (int p = 0; p < D / 32; ++p) {
+        float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (t < T_) {
+          const T* qp = q + ((size_t)(bi * T_ + t) * H + h) * D + 32 * p + 8 * lg;
+          const f32x4 a = load4(qp);
+          const f32x4 b = load4(qp + 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kb0 + 16 * kt + 4 * lg + i;
-          bool valid = tile_on[kt] && key < kend && key <= t && t < T_;
-          if (!sinkph) valid = valid && key > t - window;
-          const float sc = valid ? sacc[kt][nq][i] * scale : -INFINITY;
-          sacc[kt][nq][i] = sc;
-          mloc = fmaxf(mloc, sc);
+          for (int i = 0; i < 4; ++i) {
+            x[i] = a[i] * scale;
+            x[4 + i] = b[i] * scale;
+          }
         }
+        qf[nq][p] = frag_from8<T>(x);
       }
-      mloc = fmaxf(mloc, shfl_xor(mloc, 16));
-      mloc = fmaxf(mloc, shfl_xor(mloc, 32));
-      const float mnew = fmaxf(mrun[nq], mloc);
-      const float alpha = mnew == -INFINITY ? 1.f : exp2f(mrun[nq] - mnew);
-      float psum = 0.f;
+    }
+    f32x4 oacc[D / 16][kNQ];
 #pragma unroll
-      for (int kt = 0; kt < KB / 16; ++kt) {
+    for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float sc = sacc[kt][nq][i];
-          const float pr = sc == -INFINITY ? 0.f : exp2f(sc - mnew);
-          sacc[kt][nq][i] = pr;
-          psum += pr;
-        }
-      }
-      mrun[nq] = mnew;
-      lrun[nq] = lrun[nq] * alpha + psum;
+      for (int nq = 0; nq < kNQ; ++nq) oacc[dt][nq] = zero4();
+    float mrun[kNQ], lrun[kNQ];
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) oacc[dt][nq] *= alpha;
+    for (int nq = 0; nq < kNQ; ++nq) {
+      mrun[nq] = -INFINITY;
+      lrun[nq] = 0.f;
     }
 
-    // ---- O^T += V^T P^T
+    for (int blk = 0; blk < nbs + nbw; ++blk, ++flat) {
+      const int buf = flat & 1;
+      const bool sinkph = blk < nbs;
+      const int kb0 = sinkph ? blk * KB : win_lo + (blk - nbs) * KB;
+      const int kend = sinkph ? sink_end : t_end;
+      Blk nx;
+      const bool has_next = block_at(flat + 1, nx);
+      if (has_next) prefetch(nx);
+      const T* Kb = Ks[buf];
+      const T* Vb = VTs[buf];
+
+      // ---- S^T tiles for this wave (tiles no query of the wave sees are skipped)
+      bool tile_on[KB / 16];
+      f32x4 sacc[KB / 16][kNQ];
 #pragma unroll
-    for (int pp = 0; pp < KB / 32; ++pp) {
-      if (!(tile_on[2 * pp] || tile_on[2 * pp + 1])) continue;
-      Frag<T> pf[kNQ];
+      for (int kt = 0; kt < KB / 16; ++kt) {
+        const int k0 = kb0 + 16 * kt;
+        bool on = k0 < kend && k0 <= qlast && qb < T_;
+        if (!sinkph) on = on && (k0 + 15 > qb - window);
+        tile_on[kt] = on;
 #pragma unroll
-      for (int nq = 0; nq < kNQ; ++nq) pf[nq] = frag_from_acc<T>(sacc[2 * pp][nq], sacc[2 * pp + 1][nq]);
-      Frag<T> vf[D / 16];
+        for (int nq = 0; nq < kNQ; ++nq) sacc[kt][nq] = zero4();
+        if (on) {
+          Frag<T> af[D / 32];
+#pragma unroll
+          for (int p = 0; p < D / 32; ++p) af[p] = lds_frag8(&Kb[(16 * kt + l16) * SK + 32 * p + 8 * lg]);
+#pragma unroll
+          for (int p = 0; p < D / 32; ++p)
+#pragma unroll
+            for (int nq = 0; nq < kNQ; ++nq) sacc[kt][nq] = mfma(af[p], qf[nq][p], sacc[kt][nq]);
+        }
+      }
+
+      // ---- mask, online softmax (per lane = per query, 4 lane groups).
+      // A 16x16 tile whose keys are all visible to all its queries skips the
+      // per-element mask.  The running max is only moved (and O rescaled)
+      // when a block raises it by more than 8 in log2 units, which keeps
+      // every exponent <= 2^8 while sparing most rescales.
+#pragma unroll
+      for (int nq = 0; nq < kNQ; ++nq) {
+        const int q0 = qb + 16 * nq;
+        const int t = q0 + l16;
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < KB / 16; ++kt) {
+          const int k0 = kb0 + 16 * kt;
+          const bool full = tile_on[kt] && k0 + 15 < kend && k0 + 15 <= q0 && q0 + 15 < T_ &&
+                            (sinkph || k0 > q0 + 15 - window);
+          if (full) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, sacc[kt][nq][i]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = k0 + 4 * lg + i;
+              bool valid = tile_on[kt] && key < kend && key <= t && t < T_;
+              if (!sinkph) valid = valid && key > t - window;
+              const float sc = valid ? sacc[kt][nq][i] : -INFINITY;
+              sacc[kt][nq][i] = sc;
+              mloc = fmaxf(mloc, sc);
+            }
+          }
+        }
+        mloc = fmaxf(mloc, shfl_xor(mloc, 16));
+        mloc = fmaxf(mloc, shfl_xor(mloc, 32));
+        float mref = mrun[nq];
+        if (__any(mloc > mref + 8.f)) {   // some query of the wave needs a new reference
+          const float mnew = fmaxf(mref, mloc);
+          const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref - mnew);
+          lrun[nq] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < D / 16; ++dt) oacc[dt][nq] *= alpha;
+          mref = mnew;
+          mrun[nq] = mnew;
+        }
+        // a lane that has seen no key yet only holds -inf scores: any finite
+        // reference sends them to exp2(-inf) = 0
+        const float mexp = mref == -INFINITY ? 0.f : mref;
+        float psum = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < KB / 16; ++kt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pr = __builtin_amdgcn_exp2f(sacc[kt][nq][i] - mexp);
+            sacc[kt][nq][i] = pr;
+            psum += pr;
+          }
+        }
+        lrun[nq] += psum;
+      }
+
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int pp = 0; pp < KB / 32; ++pp) {
+        if (!(tile_on[2 * pp] || tile_on[2 * pp + 1])) continue;
+        Frag<T> pf[kNQ];
+#pragma unroll
+        for (int nq = 0; nq < kNQ; ++nq) pf[nq] = frag_from_acc<T>(sacc[2 * pp][nq], sacc[2 * pp + 1][nq]);
+        // V fragments in two halves to bound the live registers
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          Frag<T> vf[D / 32];
+#pragma unroll
+          for (int dd = 0; dd < D / 32; ++dd)
+            vf[dd] = lds_frag8(&Vb[(16 * (hf * D / 32 + dd) + l16) * SV + 32 * pp + 8 * lg]);
+#pragma unroll
+          for (int dd = 0; dd < D / 32; ++dd)
+#pragma unroll
+            for (int nq = 0; nq < kNQ; ++nq)
+              oacc[hf * D / 32 + dd][nq] = mfma(vf[dd], pf[nq], oacc[hf * D / 32 + dd][nq]);
+        }
+      }
+
+      if (has_next) commit(buf ^ 1);
+      lds_barrier();
+    }
+
+    // ---- epilogue of this query tile
+#pragma unroll
+    for (int nq = 0; nq < kNQ; ++nq) {
+      float l = lrun[nq];
+      l += shfl_xor(l, 16);
+      l += shfl_xor(l, 32);
+      const int t = qb + 16 * nq + l16;
+      if (t >= T_) continue;
+      const float inv = 1.0f / l;
+      T* orow = o + ((size_t)(bi * T_ + t) * H + h) * D;
+      const bool addl = t >= add_from;
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
-        const T* vrow = &Vb[(16 * dt + l16) * SV + 32 * pp + 4 * lg];
-        vf[dt] = lds_frag44(vrow, vrow + 16);
+        f32x4 val = oacc[dt][nq] * inv;
+        const int d0 = 16 * dt + 4 * lg;
+        if (addl) val += load4(orow + d0);
+        store4(orow + d0, val);
       }
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-        for (int nq = 0; nq < kNQ; ++nq) oacc[dt][nq] = mfma(vf[dt], pf[nq], oacc[dt][nq]);
-    }
-
-    if (blk + 1 < nb) commit(buf ^ 1);
-    lds_barrier();
-  }
-
-  // ---- epilogue
-#pragma unroll
-  for (int nq = 0; nq < kNQ; ++nq) {
-    float l = lrun[nq];
-    l += shfl_xor(l, 16);
-    l += shfl_xor(l, 32);
-    const int t = qb + 16 * nq + l16;
-    if (t >= T_) continue;
-    const float inv = 1.0f / l;
-    T* orow = o + ((size_t)(bi * T_ + t) * H + h) * D;
-    const bool addl = t >= add_from;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      f32x4 val = oacc[dt][nq] * inv;
-      const int d0 = 16 * dt + 4 * lg;
-      if (addl) val += load4(orow + d0);
-      store4(orow + d0, val);
     }
   }
 }
@@ -261,20 +326,27 @@ __global__ void zero_head_rows_kernel(T* __restrict__ o, int T_, int H, int D, i
 
 template <class T, int D>
 hipError_t launch_swa_t(const PrefillArgs& p, int add_from, hipStream_t s) {
-  // heads per workgroup: the largest power of two (<= 8) dividing G
+  // heads per workgroup: the largest power of two (<= 4) dividing G; one
+  // wave per head and 32 query rows (two waves when a group has one head),
+  // so two 4-wave workgroups fit on a CU.  Each workgroup walks TPW
+  // consecutive query tiles with one continuous K/V prefetch pipeline.
   const int G = p.H / p.Hkv;
   int HPW = 1;
-  while (HPW < 8 && G % (2 * HPW) == 0) HPW *= 2;
-  const int QT = HPW <= 4 ? 64 : 32;
+  while (HPW < 4 && G % (2 * HPW) == 0) HPW *= 2;
+  const int QT = HPW == 1 ? 64 : 32;
   const int waves = HPW * (QT / (16 * kNQ));
-  const dim3 grid((p.T + QT - 1) / QT, p.H / HPW, p.B);
+  const int ntiles = (p.T + QT - 1) / QT;
+  const int groups = p.H / HPW;
+  // keep at least ~4 workgroups per CU of work before batching tiles
+  int TPW = 1;
+  while (TPW < 8 && (size_t)((ntiles + 2 * TPW - 1) / (2 * TPW)) * groups * p.B >= 2048) TPW *= 2;
+  const dim3 grid((ntiles + TPW - 1) / TPW, groups, p.B);
 #define GDN_SWA_LAUNCH(NWV)                                                                         \
   hipLaunchKernelGGL((swa_kernel<T, D, NWV>), grid, dim3(64 * NWV), 0, s, (const T*)p.q,           \
-                     (const T*)p.k, (const T*)p.v, (T*)p.o, p.T, p.H, p.Hkv, HPW, QT, p.n_sink,    \
-                     p.window, add_from)
+                     (const T*)p.k, (const T*)p.v, (T*)p.o, p.T, p.H, p.Hkv, HPW, QT, TPW,         \
+                     p.n_sink, p.window, add_from)
   if (waves == 2) GDN_SWA_LAUNCH(2);
-  else if (waves == 4) GDN_SWA_LAUNCH(4);
-  else GDN_SWA_LAUNCH(8);
+  else GDN_SWA_LAUNCH(4);
 #undef GDN_SWA_LAUNCH
   return hipGetLastError();
 }
