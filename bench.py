@@ -15,9 +15,10 @@ Qwen3-32B-shaped full stack (short conv + GDN, short conv + GLA, budget 896).
 
 Roofline: algorithmic FLOPs (or bytes) per launch of the dominant kernel
 divided by its mean event-timed duration, against the MI355X peaks (bf16
-dense MFMA 2.5 PFLOP/s, HBM 8 TB/s).  cpu_baseline: the fp64 NumPy oracle
-timed on this host on a bounded sample (16 of the 32 heads, one thread),
-scaled to the whole layer.
+dense MFMA 2.5 PFLOP/s, HBM 8 TB/s); traffic from the committed rocprofv3
+counter reading when it was taken on the current kernel sources.
+cpu_baseline: the fp64 NumPy oracle timed on this host over the whole layer,
+one thread, repeated to at least 10 s.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--only main|decode|...]
 """
@@ -131,17 +132,20 @@ def bench_main(steps, warmup):
     swa_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(warmup, n)]))
     f_lin, f_swa = gdn_flops(w), swa_flops(w)
     if lin_ms >= swa_ms:
-        dom = ("linear_chunk_kernel (chunked GDN)", f_lin, lin_ms)
+        dom = ("linear_chunk_kernel", f_lin, lin_ms, LINEAR_SOURCES)
     else:
-        dom = ("swa_kernel (sink + window softmax)", f_swa, swa_ms)
+        dom = ("swa_kernel", f_swa, swa_ms, SWA_SOURCES)
     achieved = dom[1] / (dom[2] * 1e-3)
     res = {
         "w": w, "sec": sec,
         "kernels_ms": {"linear_chunk_kernel": lin_ms, "swa_kernel": swa_ms},
         "roofline": {
             "kernel": dom[0], "bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,
-            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16, "traffic": None,
+            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16,
+            "traffic": stored_traffic(dom[0], w.name, dom[3]),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "algorithmic_flops_per_launch": dom[1],
+            "algorithmic_bytes_per_launch": prefill_bytes(w),
         },
         "layer_frac_mfma": (f_lin + f_swa) / sec / PEAK_BF16,
         "inputs": inp,
@@ -149,29 +153,81 @@ def bench_main(steps, warmup):
     return res
 
 
-def cpu_baseline(inp, w, heads_per_sample=16):
-    """fp64 oracle on the first `heads_per_sample` query heads (whole T),
-    scaled to all heads; one thread."""
+def cpu_baseline(inp, w, min_seconds=10.0, max_reps=6):
+    """fp64 oracle over the whole layer (all heads, whole T), one thread,
+    repeated until at least `min_seconds` of CPU work; mean time per layer."""
     from threadpoolctl import threadpool_limits
     from oracle import hybrid as O
 
-    G = w.H // w.Hkv
-    ng = heads_per_sample // G
-    f = {x: inp[x][:, :, : (heads_per_sample if x in ("q", "a", "b") else ng)].double().cpu().numpy()
-         for x in ("q", "k", "v", "a", "b")}
+    f = {x: inp[x].double().cpu().numpy() for x in ("q", "k", "v", "a", "b")}
+    times = []
     with threadpool_limits(1):
-        t0 = time.perf_counter()
-        O.hybrid_prefill(f["q"], f["k"], f["v"], f["a"], f["b"], w.n_sink, w.window, flags=3)
-        dt = time.perf_counter() - t0
-    full = dt * w.H / heads_per_sample
+        while sum(times) < min_seconds and len(times) < max_reps:
+            t0 = time.perf_counter()
+            O.hybrid_prefill(f["q"], f["k"], f["v"], f["a"], f["b"], w.n_sink, w.window, flags=3)
+            times.append(time.perf_counter() - t0)
+    per = sum(times) / len(times)
     return {
-        "value": w.B * w.T / full, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-        "sample": f"layer prefill on {heads_per_sample} of {w.H} query heads "
-                  f"({ng} KV groups), B={w.B}, T={w.T}, fp64 NumPy, one thread; "
-                  f"{dt:.1f} s measured, scaled x{w.H / heads_per_sample:g} to all heads",
-        "cpu": platform.processor() or platform.machine(),
+        "value": w.B * w.T / per, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        "sample": f"whole layer prefill (B={w.B}, T={w.T}, {w.H} query / {w.Hkv} KV heads, "
+                  f"both branches), fp64 NumPy oracle on one thread, {len(times)} repetitions, "
+                  f"{sum(times):.1f} s total, {per:.2f} s per layer",
+        "cpu": _cpu_model(),
         "host_cores_allowed": len(os.sched_getaffinity(0)),
     }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def kernel_sources_sha256(files):
+    """Digest of the sources a kernel is compiled from; a stored counter
+    reading only applies while this digest is unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+LINEAR_SOURCES = ("swa_chunked_gated_amd/csrc/linear_chunk.hip", "swa_chunked_gated_amd/csrc/common.h")
+SWA_SOURCES = ("swa_chunked_gated_amd/csrc/swa.hip", "swa_chunked_gated_amd/csrc/common.h")
+DECODE_SOURCES = ("swa_chunked_gated_amd/csrc/decode.hip", "swa_chunked_gated_amd/csrc/common.h")
+
+
+def stored_traffic(kernel, workload, sources):
+    """HBM bytes per launch from profiles/hbm_traffic.txt: rocprofv3 FETCH_SIZE
+    and WRITE_SIZE (KiB per dispatch) times the factors a plain device copy of
+    known size gives.  None when no reading exists for the current sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    digest = kernel_sources_sha256(sources)
+    fac = {}
+    rows = []
+    with open(path) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            kv = dict(tok.split("=", 1) for tok in line.split() if "=" in tok)
+            if kv.get("kind") == "copy":
+                fac = {"fetch": float(kv["fetch_factor"]), "write": float(kv["write_factor"])}
+            elif kv.get("kind") == "kernel":
+                rows.append(kv)
+    for kv in rows:
+        if kv["kernel"] == kernel and kv["workload"] == workload and kv["sources_sha256"] == digest and fac:
+            return (float(kv["fetch_kib"]) * fac["fetch"] + float(kv["write_kib"]) * fac["write"]) * 1024.0
+    return None
 
 
 # ------------------------------------------------------------ secondary
@@ -210,10 +266,11 @@ def bench_decode(steps=1000, warmup=10):
         "workload": "decode_b256 (B=256, H=32, Hkv=8, d=128, cache 8+56, t=4096..5095)",
         "steps": steps, "ms_per_step": sec * 1e3, "steps_per_s": 1.0 / sec,
         "tokens_per_s": w.B / sec, "event_ms_per_step": ev_ms,
-        "roofline": {"kernel": "decode_kernel + advance_pos_kernel", "bound": "hbm",
+        "roofline": {"kernel": "decode_kernel + decode_commit_kernel", "bound": "hbm",
                      "achieved": byts / (ev_ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9,
                      "unit": "GB/s", "frac": byts / (ev_ms * 1e-3) / PEAK_HBM,
-                     "algorithmic_bytes_per_step": byts},
+                     "algorithmic_bytes_per_step": byts,
+                     "traffic": stored_traffic("decode_kernel", w.name, DECODE_SOURCES)},
     }
 
 
