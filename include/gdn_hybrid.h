@@ -130,6 +130,11 @@ int gdn_hybrid_prefill_workspace(int B, int T, int H, int Hkv, int dk, int dv,
  *   by gdn_hybrid_prefill_workspace (may be NULL / 0 when that size is 0).
  * Supported: d in {64, 128} for bf16; the linear branch (or the state) in
  * fp32 only at d = 64 (GDN_EUNSUPPORTED otherwise).
+ * Preconditions (not checked): gates a in (0, 1], b in [0, 1].  GDN gates
+ * may decay at any rate.  GLA operands are formed relative to a reference
+ * token every 16 tokens, so results are exact (to rounding) while the
+ * product of any 8 consecutive gates of one channel stays above e^-80
+ * (a mean gate above about 5e-5).
  */
 int gdn_hybrid_prefill(const void* q, const void* k, const void* v,
                        const float* a, const float* b,

@@ -85,16 +85,17 @@ struct Smem {
   static constexpr int oQ = oKT + nKT;
   static constexpr int oVT = oQ + nK;
   static constexpr int oAq = oVT + nVT;
-  static constexpr int oWm = oAq + nA;               // GDN only
-  static constexpr int oTB = oWm + (GLA ? 0 : nK);
+  static constexpr int oWm = oAq + nA;               // GDN: Wm; GLA: Q at tile references
+  static constexpr int oTB = oWm + nK;
   static constexpr int oTBG = oTB + (GLA ? 0 : nA);
   static constexpr int nT = oTBG + (GLA ? 0 : nA);
   static constexpr int bytesT = ((nT * (int)sizeof(T)) + 15) / 16 * 16;
   // fp32 part
   static constexpr int nL = GLA ? 0 : kC * kSL;      // solve buffer
   static constexpr int nAl = GLA ? kC * D : 0;       // GLA cumulative log-gates
+  static constexpr int nMf = GLA ? 6 * D : 0;        // GLA tile-pair factors
   static constexpr int nGate = GLA ? D : 3 * kC;     // GDN: g, gamma, b; GLA: G_C
-  static constexpr int bytes = bytesT + 4 * (nL + nAl + nGate);
+  static constexpr int bytes = bytesT + 4 * (nL + nAl + nMf + nGate);
 };
 
 template <class T, int D, int NW, int DW, bool GLA>
@@ -138,7 +139,9 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
   float* sF = reinterpret_cast<float*>(smem_raw + SM::bytesT);
   float* Lf = sF;                    // [64][kSL]  L, then Tm (GDN)
   float* Al = sF + SM::nL;           // [64][D]    cumulative log-gates (GLA)
-  float* gate = Al + SM::nAl;        // GDN: lg[64], gam[64], bet[64]; GLA: GC[D]
+  float* Mf = Al + SM::nAl;          // [6][D]     GLA tile-pair factors (acc order)
+  float* gate = Mf + SM::nMf;        // GDN: lg[64], gam[64], bet[64]; GLA: GC[D]
+  T* QDs = Wms;                      // GLA: q scaled to its tile's reference point
 
   const int sp = blockIdx.x;          // column slice
   const int h = blockIdx.y;
@@ -305,22 +308,40 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
         GC[tid] = x;
       }
       lds_barrier();
-      // row-major Q e^G and K e^-G, 4 channels per task
+      // Every product of phase A needs exp(G_r - G_s) for s <= r.  Split as
+      // e^{G_r} e^{-G_s} it leaves the float range once a chunk decays by
+      // more than e^88, so each 16-row tile j gets its own reference point
+      // M_j = G at row 16j + 7: the operands q_r e^{G_r - M_j} and
+      // k_s e^{M_j - G_s} grow by at most the decay of 8 tokens (clamped at
+      // e^80), and a pair of different tiles (mt > nt) takes the per-channel
+      // factor e^{M_mt - M_nt} <= 1 on its key operand.  Q e^G (for O) and
+      // K e^{G_C - G} (for the state update) are bounded by 1 as they are.
       for (int i = tid; i < kC * D / 4; i += kThreads) {
         const int r = i / (D / 4);
         const int cc = (i % (D / 4)) * 4;
         const int pc = acc_pos(cc);
         const f32x4 G4 = *reinterpret_cast<const f32x4*>(&Al[r * D + cc]);
+        const f32x4 M4 = *reinterpret_cast<const f32x4*>(&Al[((r & ~15) + 7) * D + cc]);
         const f32x4 q4 = load4(&Qs[r * SK + pc]);
         const f32x4 k4 = load4(&Ks[r * SK + pc]);
-        f32x4 qo, ko;
+        f32x4 qo, qd, kd;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          qo[x] = q4[x] * __expf(fminf(G4[x], 80.f));
-          ko[x] = k4[x] * __expf(fminf(-G4[x], 80.f));
+          qo[x] = q4[x] * __expf(G4[x]);
+          qd[x] = q4[x] * __expf(fminf(G4[x] - M4[x], 80.f));
+          kd[x] = k4[x] * __expf(fminf(M4[x] - G4[x], 80.f));
         }
         store4(&Qs[r * SK + pc], qo);
-        store4(&Ks[r * SK + pc], ko);
+        store4(&QDs[r * SK + pc], qd);
+        store4(&Ks[r * SK + pc], kd);
+      }
+      // tile-pair factors e^{M_mt - M_nt}, pair index mt (mt - 1) / 2 + nt
+      for (int i = tid; i < 6 * D; i += kThreads) {
+        const int pr = i / D;
+        const int cc = i % D;
+        const int mt = pr < 1 ? 1 : (pr < 3 ? 2 : 3);
+        const int nt = pr - mt * (mt - 1) / 2;
+        Mf[pr * D + acc_pos(cc)] = __expf(Al[(16 * mt + 7) * D + cc] - Al[(16 * nt + 7) * D + cc]);
       }
       // transposed K e^{G_C - G}, 8 tokens (acc order) of one channel per task
       for (int i = tid; i < D * (kC / 8); i += kThreads) {
@@ -333,22 +354,31 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
         f32x4 o0, o1;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          o0[x] = k0[x] * __expf(fminf(gc - Al[acc_idx(r0 + x) * D + cc], 80.f));
-          o1[x] = k1[x] * __expf(fminf(gc - Al[acc_idx(r0 + 4 + x) * D + cc], 80.f));
+          o0[x] = k0[x] * __expf(fminf(gc - Al[acc_idx(r0 + x) * D + cc], 0.f));
+          o1[x] = k1[x] * __expf(fminf(gc - Al[acc_idx(r0 + 4 + x) * D + cc], 0.f));
         }
         store4(kt, o0);
         store4(kt + 4, o1);
       }
       lds_barrier();
-      // ---- A = [s <= r] (Q e^G)(K e^-G)^T on the 10 lower tiles
+      // ---- A = [s <= r] exp(G_r - G_s) o (Q K^T) on the 10 lower tiles
       for (int job = wv; job < 10; job += NW) {
         const int mt = kTileM[job];
         const int nt = kTileN[job];
         f32x4 acc = zero4();
+        if (mt == nt) {
 #pragma unroll
-        for (int p = 0; p < D / 32; ++p)
-          acc = mfma(lds_frag8(&Qs[(16 * mt + l16) * SK + 32 * p + 8 * lg]),
-                     lds_frag8(&Ks[(16 * nt + l16) * SK + 32 * p + 8 * lg]), acc);
+          for (int p = 0; p < D / 32; ++p)
+            acc = mfma(lds_frag8(&QDs[(16 * mt + l16) * SK + 32 * p + 8 * lg]),
+                       lds_frag8(&Ks[(16 * nt + l16) * SK + 32 * p + 8 * lg]), acc);
+        } else {
+          const float* mf = Mf + (mt * (mt - 1) / 2 + nt) * D;
+#pragma unroll
+          for (int p = 0; p < D / 32; ++p)
+            acc = mfma(lds_frag8(&QDs[(16 * mt + l16) * SK + 32 * p + 8 * lg]),
+                       lds_frag8_scaled(&Ks[(16 * nt + l16) * SK + 32 * p + 8 * lg], mf + 32 * p + 8 * lg),
+                       acc);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * mt + 4 * lg + i;

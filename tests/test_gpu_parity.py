@@ -205,6 +205,23 @@ def test_gla_prefill(T, dtype, d):
     assert_close(f64(st), S, dtype == "f32", "state")
 
 
+@pytest.mark.parametrize("update,dtype,d,gate_mean", [("gla", "bf16", 128, 1.0), ("gla", "bf16", 128, 3.0),
+                                                    ("gla", "f32", 64, 1.0), ("gdn", "bf16", 128, 1.0),
+                                                    ("gdn", "f32", 64, 3.0)])
+def test_strong_forget_gates(update, dtype, d, gate_mean):
+    """Gates far below 1 (mean about 0.27 or 0.05 per token): a 64-token
+    chunk then decays by e^-80 to e^-190, beyond the float range if the
+    decay between two tokens were split into one factor per token."""
+    w = small(T=300, d=d, dtype=dtype, update=update, gate_mean=gate_mean)
+    inp = to_dev(make_prefill_inputs(w, seed=11))
+    o, st = run_prefill(inp, w)
+    ref, S = O.hybrid_prefill(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["a"]),
+                              f64(inp["b"]) if update == "gdn" else None, w.n_sink, w.window,
+                              update=update)
+    assert_close(f64(o), ref, dtype == "f32", "o")
+    assert_close(f64(st), S, dtype == "f32", "state")
+
+
 # ------------------------------------------------------------- short conv
 
 @pytest.mark.parametrize("dtype,d,T,flags", [("bf16", 128, 200, 3), ("f32", 64, 77, 3),

@@ -49,6 +49,7 @@ class Workload:
     state_var: float = 0.02    # decode: variance of the random initial state
     pos0: int = 0              # decode: position of the first new token
     steps: int = 0             # decode: number of consecutive steps
+    gate_mean: float = -4.0    # mean of the forget-gate logit: a = exp(-softplus(N(gate_mean, 1)))
 
     @property
     def budget(self) -> int:
@@ -111,11 +112,11 @@ def make_prefill_inputs(w: Workload, device="cpu", seed: int = 0, T: int | None 
     knoise = torch.randn(B, T, w.Hkv, d, **f32)
     v = torch.randn(B, T, w.Hkv, d, **f32)
     b_logit = torch.randn(B, T, w.H, **f32)
-    a_logit = torch.randn(B, T, w.H, **f32) - 4.0
+    a_logit = torch.randn(B, T, w.H, **f32) + w.gate_mean
     k = mu[None, None] + w.sigma * knoise
     out = {}
     if w.update == "gla":
-        a_logit = torch.randn(B, T, w.H, d, **f32) - 4.0
+        a_logit = torch.randn(B, T, w.H, d, **f32) + w.gate_mean
     if w.shortconv:
         ks = w.conv_ks
         std = 1.0 / math.sqrt(ks)
@@ -158,7 +159,7 @@ def make_decode_inputs(w: Workload, device="cpu", seed: int = 0, steps: int | No
                      + w.sigma * torch.randn(*lead, d, **f32))
 
     def gate_a(*shape):
-        return torch.exp(-torch.nn.functional.softplus(torch.randn(*shape, **f32) - 4.0))
+        return torch.exp(-torch.nn.functional.softplus(torch.randn(*shape, **f32) + w.gate_mean))
 
     state = torch.randn(B, H, d, d, **f32) * math.sqrt(w.state_var)
     k_cache = keys(B, N, Hkv).permute(0, 2, 1, 3).to(dt).contiguous()
