@@ -4,10 +4,10 @@
 Headline (the printed JSON line): prefill throughput of one layer with the
 LLaMA3.1-8B attention shape (B=1, 32 query / 8 KV heads, d=128, T=4096,
 budget 8 sinks + 56 window, bf16 inputs, fp32 state).  One step = one
-layer pass over the sequence: the chunked GDN kernel, then the sink+SWA
-softmax kernel adding its branch (two ABI calls, each launching exactly one
-kernel, so HIP events between them time each kernel on the stream it runs
-on).  Inputs are resident in HBM before the timed region.
+layer pass over the sequence: the linear branch (chunk preparation kernel,
+then the chunked GDN scan kernel), then the sink+SWA softmax kernel adding
+its branch; two ABI calls, so HIP events between them time each branch on
+the stream it runs on.  Inputs are resident in HBM before the timed region.
 
 Secondary figures in "also": decode steps/s (B=256, 1000 consecutive steps),
 long-context prefill (B=8, T=32768, budget 128, final state out) and the
@@ -108,13 +108,17 @@ def bench_main(steps, warmup):
     inp = make_prefill_inputs(w, device="cuda")
     o = torch.empty(w.B, w.T, w.H, w.d, dtype=torch.bfloat16, device="cuda")
     q, k, v, a, b = (inp[x] for x in ("q", "k", "v", "a", "b"))
+    ws = torch.empty(gl.prefill_workspace_bytes(w.B, w.T, w.H, w.Hkv, w.d, w.n_sink, w.window,
+                                                torch.bfloat16, flags=gl.BRANCH_LINEAR),
+                     dtype=torch.uint8, device="cuda")
     n = steps + warmup
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
 
     def step(i):
         e = ev[i]
         e[0].record()
-        gl.hybrid_prefill(q, k, v, a, b, w.n_sink, w.window, flags=gl.BRANCH_LINEAR, o=o)
+        gl.hybrid_prefill(q, k, v, a, b, w.n_sink, w.window, flags=gl.BRANCH_LINEAR, o=o,
+                          workspace=ws)
         e[1].record()
         gl.hybrid_prefill(q, k, v, a, b, w.n_sink, w.window,
                           flags=gl.BRANCH_SOFTMAX | gl.ACCUMULATE, o=o)
@@ -132,13 +136,13 @@ def bench_main(steps, warmup):
     swa_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(warmup, n)]))
     f_lin, f_swa = gdn_flops(w), swa_flops(w)
     if lin_ms >= swa_ms:
-        dom = ("linear_chunk_kernel", f_lin, lin_ms, LINEAR_SOURCES)
+        dom = ("gdn_prep_kernel+linear_chunk_kernel", f_lin, lin_ms, LINEAR_SOURCES)
     else:
         dom = ("swa_kernel", f_swa, swa_ms, SWA_SOURCES)
     achieved = dom[1] / (dom[2] * 1e-3)
     res = {
         "w": w, "sec": sec,
-        "kernels_ms": {"linear_chunk_kernel": lin_ms, "swa_kernel": swa_ms},
+        "kernels_ms": {"gdn_prep_kernel+linear_chunk_kernel": lin_ms, "swa_kernel": swa_ms},
         "roofline": {
             "kernel": dom[0], "bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,
             "unit": "TFLOP/s", "frac": achieved / PEAK_BF16,
@@ -199,7 +203,8 @@ def kernel_sources_sha256(files):
     return h.hexdigest()
 
 
-LINEAR_SOURCES = ("swa_chunked_gated_amd/csrc/linear_chunk.hip", "swa_chunked_gated_amd/csrc/common.h")
+LINEAR_SOURCES = ("swa_chunked_gated_amd/csrc/gdn_prep.hip", "swa_chunked_gated_amd/csrc/linear_chunk.hip",
+                  "swa_chunked_gated_amd/csrc/common.h")
 SWA_SOURCES = ("swa_chunked_gated_amd/csrc/swa.hip", "swa_chunked_gated_amd/csrc/common.h")
 DECODE_SOURCES = ("swa_chunked_gated_amd/csrc/decode.hip", "swa_chunked_gated_amd/csrc/common.h")
 
@@ -304,6 +309,9 @@ def bench_prefill_cfg(name, steps=5, warmup=2):
     st = torch.empty(w.B, w.H, w.d, w.d, dtype=torch.float32, device="cuda") if w.write_state else None
     if w.shortconv:
         qc, kc, vc = (torch.empty_like(inp[x]) for x in ("q", "k", "v"))
+    nws = gl.prefill_workspace_bytes(w.B, w.T, w.H, w.Hkv, w.d, w.n_sink, w.window,
+                                     torch.bfloat16, update=w.update, flags=flags)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
 
     def layer():
         if w.shortconv:
@@ -313,7 +321,7 @@ def bench_prefill_cfg(name, steps=5, warmup=2):
         else:
             q, k, v = inp["q"], inp["k"], inp["v"]
         gl.hybrid_prefill(q, k, v, inp["a"], inp["b"], w.n_sink, w.window, update=w.update,
-                          flags=flags, o=o, state_out=st)
+                          flags=flags, o=o, state_out=st, workspace=ws)
 
     sec = timed(layer, steps, warmup)
     f = (gdn_flops(w) if w.update == "gdn" else gla_flops(w)) + swa_flops(w)

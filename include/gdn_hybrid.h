@@ -98,8 +98,15 @@ int gdn_hybrid_last_hip_error(void);
 
 /*
  * Workspace bytes gdn_hybrid_prefill needs for these arguments (written to
- * *bytes).  The current kernels need none (0): the linear branch writes its
- * rows of o and the softmax branch adds to them in place.
+ * *bytes).  Non-zero only for the gated delta rule (update GDN_DELTA) when
+ * the linear branch or the state is requested and T > n_sink + window: the
+ * state-independent part of every 64-token chunk (the inverse of the chunk's
+ * unit lower-triangular system scaled by b and by b * gamma, and the gate
+ * prefix sums) is computed for all chunks in parallel and stored there, so
+ * the sequential scan over chunks only does the state-dependent products.
+ * Size: B * H * nch * (2 * 64 * 64 * elt + 128 * 4) bytes with
+ * nch = ceil((T - window - n_sink) / 64) and elt the size of `dtype`
+ * (about 34 MB for B=1, H=32, T=4096, bf16).
  * Errors: GDN_EINVAL if bytes is NULL or the shape arguments are invalid.
  */
 int gdn_hybrid_prefill_workspace(int B, int T, int H, int Hkv, int dk, int dv,
@@ -127,7 +134,10 @@ int gdn_hybrid_prefill_workspace(int B, int T, int H, int Hkv, int dk, int dv,
  *   with GDN_BRANCH_SOFTMAX | GDN_ACCUMULATE gives the same o as one call
  *   with both branches (each call then launches a single kernel).
  *   workspace / workspace_bytes: device buffer of at least the size reported
- *   by gdn_hybrid_prefill_workspace (may be NULL / 0 when that size is 0).
+ *   by gdn_hybrid_prefill_workspace, 256-byte aligned, owned by the caller
+ *   and free for reuse once the call's work on `stream` is done (may be
+ *   NULL / 0 when that size is 0).  GDN_EWORKSPACE if it is missing or too
+ *   small, GDN_EINVAL if misaligned.
  * Supported: d in {64, 128} for bf16; the linear branch (or the state) in
  * fp32 only at d = 64 (GDN_EUNSUPPORTED otherwise).
  * Preconditions (not checked): gates a in (0, 1], b in [0, 1].  GDN gates

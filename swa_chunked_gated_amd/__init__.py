@@ -27,6 +27,7 @@ _UPDATES = {"gdn": 0, "gla": 1}
 
 __all__ = [
     "hybrid_prefill", "hybrid_decode", "cache_from_prefill", "shortconv_qkv",
+    "prefill_workspace_bytes",
     "version", "GdnError", "BRANCH_LINEAR", "BRANCH_SOFTMAX", "WRITE_STATE", "ACCUMULATE",
     "ROPE", "L2NORM",
 ]
@@ -66,13 +67,28 @@ def _f32(*ts):
             raise ValueError("gates, states and conv weights must be float32")
 
 
+def prefill_workspace_bytes(B: int, T: int, H: int, Hkv: int, d: int, n_sink: int, window: int,
+                            dtype, update: str = "gdn",
+                            flags: int = BRANCH_LINEAR | BRANCH_SOFTMAX) -> int:
+    """Device workspace (bytes) ``hybrid_prefill`` needs for these arguments."""
+    dt = _DTYPES[dtype]
+    n = ctypes.c_size_t(0)
+    rc = _lib.load().gdn_hybrid_prefill_workspace(B, T, H, Hkv, d, d, n_sink, window, dt,
+                                                  _UPDATES[update], flags, ctypes.byref(n))
+    _lib.check("gdn_hybrid_prefill_workspace", rc)
+    return n.value
+
+
 def hybrid_prefill(q, k, v, a, b, n_sink: int, window: int, update: str = "gdn",
-                   flags: int = BRANCH_LINEAR | BRANCH_SOFTMAX, o=None, state_out=None):
+                   flags: int = BRANCH_LINEAR | BRANCH_SOFTMAX, o=None, state_out=None,
+                   workspace=None):
     """Layer output for whole sequences starting at position 0.
 
     q [B,T,H,d], k/v [B,T,Hkv,d] (fp32 or bf16); a [B,T,H] (GLA: [B,T,H,d])
     and b [B,T,H] fp32.  Returns (o [B,T,H,d], state [B,H,d,d] fp32 or None).
     With ACCUMULATE in flags, ``o`` must be given and receives o += branches.
+    ``workspace``: a uint8 device tensor of at least
+    ``prefill_workspace_bytes(...)`` bytes; allocated here when omitted.
     """
     if flags & ACCUMULATE and o is None:
         raise ValueError("ACCUMULATE needs an initialised output tensor o")
@@ -88,9 +104,16 @@ def hybrid_prefill(q, k, v, a, b, n_sink: int, window: int, update: str = "gdn",
         _io_dtype(q, o)
     _f32(state_out)
     lib = _lib.load()
+    need = ctypes.c_size_t(0)
+    rc = lib.gdn_hybrid_prefill_workspace(B, T, H, Hkv, dk, dv, n_sink, window, dt,
+                                          _UPDATES[update], flags, ctypes.byref(need))
+    _lib.check("gdn_hybrid_prefill_workspace", rc)
+    if need.value > 0 and workspace is None:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib.gdn_hybrid_prefill(_p(q), _p(k), _p(v), _p(a), _p(b), _p(o), _p(state_out),
                                 B, T, H, Hkv, dk, dv, n_sink, window, dt, _UPDATES[update],
-                                flags, None, 0, _stream(q))
+                                flags, _p(workspace), ws_bytes, _stream(q))
     _lib.check("gdn_hybrid_prefill", rc)
     return o, state_out
 

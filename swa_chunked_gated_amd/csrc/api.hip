@@ -56,12 +56,25 @@ const char* gdn_hybrid_strerror(int code) {
 
 int gdn_hybrid_last_hip_error(void) { return g_last_hip_error.load(); }
 
+namespace {
+// Workspace the linear branch of this call needs (0 unless the gated delta
+// rule recurrence runs over at least one chunk).
+size_t prefill_workspace_bytes(int B, int T, int H, int n_sink, int window, int dtype, int update,
+                               int flags) {
+  const bool rec = (flags & GDN_BRANCH_LINEAR) || (flags & GDN_WRITE_STATE);
+  if (!rec || update != GDN_DELTA) return 0;
+  const int nch = gdn::gdn_stream_chunks(T, n_sink, window);
+  if (nch == 0) return 0;
+  return gdn::gdn_workspace_layout(nullptr, B, H, nch, dtype == GDN_BF16 ? 2 : 4).bytes;
+}
+}  // namespace
+
 int gdn_hybrid_prefill_workspace(int B, int T, int H, int Hkv, int dk, int dv, int n_sink,
                                  int window, int dtype, int update, int flags, size_t* bytes) {
   if (!bytes) return GDN_EINVAL;
   if (!dims_ok(B, T, H, Hkv, dk, dv, n_sink, window, dtype, update)) return GDN_EINVAL;
   if (flags < 1 || flags > 15 || (flags & 7) == 0) return GDN_EINVAL;
-  *bytes = 0;
+  *bytes = prefill_workspace_bytes(B, T, H, n_sink, window, dtype, update, flags);
   return GDN_OK;
 }
 
@@ -69,8 +82,6 @@ int gdn_hybrid_prefill(const void* q, const void* k, const void* v, const float*
                        const float* b, void* o, float* state_out, int B, int T, int H, int Hkv,
                        int dk, int dv, int n_sink, int window, int dtype, int update, int flags,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (!dims_ok(B, T, H, Hkv, dk, dv, n_sink, window, dtype, update)) return GDN_EINVAL;
   if (flags < 1 || flags > 15 || (flags & 7) == 0) return GDN_EINVAL;
   const bool lin = flags & GDN_BRANCH_LINEAR;
@@ -84,10 +95,13 @@ int gdn_hybrid_prefill(const void* q, const void* k, const void* v, const float*
   if (needs_rec && update == GDN_DELTA && !b) return GDN_EINVAL;
   if (wst && !state_out) return GDN_EINVAL;
   if (needs_rec && dtype == GDN_F32 && dk != 64) return GDN_EUNSUPPORTED;
+  const size_t need = prefill_workspace_bytes(B, T, H, n_sink, window, dtype, update, flags);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_EWORKSPACE;
+  if (need > 0 && ((uintptr_t)workspace & 255u) != 0) return GDN_EINVAL;
   if (T == 0 && !wst) return GDN_OK;
 
   gdn::PrefillArgs p{q, k, v, a, b, o, state_out, B, T, H, Hkv, dk, n_sink, window,
-                     dtype == GDN_BF16, update == GDN_GLA, flags};
+                     dtype == GDN_BF16, update == GDN_GLA, flags, workspace};
   hipStream_t s = (hipStream_t)stream;
   const int N = n_sink + window;
   // The linear kernel writes (or adds) rows t >= N and, for a linear-only

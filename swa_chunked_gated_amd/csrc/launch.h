@@ -20,7 +20,24 @@ struct PrefillArgs {
   int bf16;     // 1: q/k/v/o are bf16, 0: fp32
   int gla;      // 1: GLA diagonal-gate update, 0: gated delta rule
   int flags;    // GDN_BRANCH_LINEAR | GDN_BRANCH_SOFTMAX | GDN_WRITE_STATE
+  void* workspace;   // chunk preparation results (gated delta rule), see GdnWorkspace
 };
+
+// Workspace of the gated delta rule prefill: for each (sequence, head, chunk)
+// TB and TBG (64 x 64 elements of the I/O type, rows with columns in acc
+// order) and g, gamma (2 x 64 fp32), as three consecutive arrays.
+struct GdnWorkspace {
+  void* tb;
+  void* tbg;
+  float* g;
+  size_t bytes;
+};
+GdnWorkspace gdn_workspace_layout(void* base, int B, int H, int nch, size_t elt);
+// Chunks of the linear stream of a sequence of length T.
+inline int gdn_stream_chunks(int T, int n_sink, int window) {
+  const long long n = (long long)T - window - n_sink;
+  return n > 0 ? (int)((n + 63) / 64) : 0;
+}
 
 struct DecodeArgs {
   const void* q;
@@ -74,6 +91,8 @@ struct ShortConvArgs {
 // t < n_sink + window for a linear-only overwrite, and writes the final
 // state when asked.
 hipError_t launch_linear_prefill(const PrefillArgs& a, hipStream_t s);
+// Chunk preparation of the gated delta rule into a.workspace (nch chunks).
+hipError_t launch_gdn_prep(const PrefillArgs& a, int nch, hipStream_t s);
 // Softmax branch: writes every row of o, adding the value o already holds
 // on rows t >= add_from.
 hipError_t launch_swa_prefill(const PrefillArgs& a, int add_from, hipStream_t s);

@@ -43,31 +43,9 @@ namespace gdn {
 namespace {
 
 constexpr int kC = 64;          // chunk length
-constexpr int kSL = 68;         // fp32 stride of the 64x64 solve buffer
 // the 10 lower-triangular 16x16 tiles (row, col) of a 64x64 matrix
 __constant__ const int kTileM[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
 __constant__ const int kTileN[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// C += A(16x16) B(16x16), both fp32 row-major in LDS.
-__device__ __forceinline__ f32x4 mm16(const float* A, const float* B, f32x4 c, int l16, int lg) {
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) c = mfma4(A[l16 * kSL + 4 * kk + lg], B[(4 * kk + lg) * kSL + l16], c);
-  return c;
-}
-// C += A(16x16, LDS) Y(16x16, accumulator registers of this wave).
-__device__ __forceinline__ f32x4 mm16_acc(const float* A, const f32x4& Y, f32x4 c, int l16, int lg) {
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) c = mfma4(A[l16 * kSL + 4 * lg + kk], Y[kk], c);
-  return c;
-}
-__device__ __forceinline__ void st16(float* blk, const f32x4& x, int l16, int lg) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) blk[(4 * lg + i) * kSL + l16] = x[i];
-}
 
 template <class T, int D, int NW, int DW, bool GLA>
 struct Smem {
@@ -91,18 +69,18 @@ struct Smem {
   static constexpr int nT = oTBG + (GLA ? 0 : nA);
   static constexpr int bytesT = ((nT * (int)sizeof(T)) + 15) / 16 * 16;
   // fp32 part
-  static constexpr int nL = GLA ? 0 : kC * kSL;      // solve buffer
   static constexpr int nAl = GLA ? kC * D : 0;       // GLA cumulative log-gates
   static constexpr int nMf = GLA ? 6 * D : 0;        // GLA tile-pair factors
-  static constexpr int nGate = GLA ? D : 3 * kC;     // GDN: g, gamma, b; GLA: G_C
-  static constexpr int bytes = bytesT + 4 * (nL + nAl + nMf + nGate);
+  static constexpr int nGate = GLA ? D : 2 * kC;     // GDN: g (log2), gamma; GLA: G_C
+  static constexpr int bytes = bytesT + 4 * (nAl + nMf + nGate);
 };
 
 template <class T, int D, int NW, int DW, bool GLA>
 __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const float* __restrict__ a, const float* __restrict__ b, T* __restrict__ o,
-    float* __restrict__ state_out, int T_, int H, int Hkv, int n_sink, int window, int flags) {
+    const float* __restrict__ a, const T* __restrict__ wtb, const T* __restrict__ wtbg,
+    const float* __restrict__ wg, T* __restrict__ o, float* __restrict__ state_out, int T_, int H,
+    int Hkv, int n_sink, int window, int flags) {
   using SM = Smem<T, D, NW, DW, GLA>;
   constexpr int kThreads = 64 * NW;
   constexpr int SK = SM::SK;
@@ -137,10 +115,9 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
   T* TBs = sT + SM::oTB;
   T* TBGs = sT + SM::oTBG;
   float* sF = reinterpret_cast<float*>(smem_raw + SM::bytesT);
-  float* Lf = sF;                    // [64][kSL]  L, then Tm (GDN)
-  float* Al = sF + SM::nL;           // [64][D]    cumulative log-gates (GLA)
+  float* Al = sF;                    // [64][D]    cumulative log-gates (GLA)
   float* Mf = Al + SM::nAl;          // [6][D]     GLA tile-pair factors (acc order)
-  float* gate = Mf + SM::nMf;        // GDN: lg[64], gam[64], bet[64]; GLA: GC[D]
+  float* gate = Mf + SM::nMf;        // GDN: g[64] (log2), gam[64]; GLA: GC[D]
   T* QDs = Wms;                      // GLA: q scaled to its tile's reference point
 
   const int sp = blockIdx.x;          // column slice
@@ -163,11 +140,8 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
   const int vdc = lane % DPRV;
   const int vr0 = TPW * wv + TPTV * (lane / DPRV);
 
-  // zero the solve buffer and the score tiles once: their strictly upper
-  // parts are never written again
+  // zero the score tiles once: their strictly upper parts are never written
   for (int i = tid; i < SM::nA; i += kThreads) Aqs[i] = from_f32<T>(0.f);
-  if (!GLA)
-    for (int i = tid; i < SM::nL; i += kThreads) Lf[i] = 0.f;
 
   f32x4 S[MT][NT];
 #pragma unroll
@@ -180,7 +154,13 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
   uint32_t pk[TPT], pv[TPTV];
   V16 pq[NPQ];
   f32x4 pa[GLA ? NPA : 1];
-  float pg = 1.f;   // GDN: a (threads 0..63) or b (threads 64..127)
+  // GDN: the chunk's TB, TBG rows (16-byte pieces) and g, gamma from the
+  // chunk preparation
+  constexpr int NPT = GLA ? 1 : kC * kC / VEC / kThreads;
+  static_assert(GLA || (kC * kC / VEC) % kThreads == 0, "TB staging");
+  V16 ptb[NPT], ptbg[NPT];
+  f32x4 pgm = zero4();
+  const size_t chain = (size_t)bi * H + h;
 
   const size_t kvstride = (size_t)Hkv * D;           // elements between tokens
   const size_t qstride = (size_t)H * D;
@@ -226,10 +206,15 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
                            : f32x4{1.f, 1.f, 1.f, 1.f};
       }
     } else {
-      const int r = tid & 63;
-      const int tok = i0 + r;
-      if (tid < 64) pg = tok < iend ? a[(size_t)(bi * T_ + tok) * H + h] : 1.f;
-      else if (tid < 128) pg = tok < iend ? b[(size_t)(bi * T_ + tok) * H + h] : 0.f;
+      const size_t ci = chain * nch + c;
+      const V16* tb = reinterpret_cast<const V16*>(wtb + ci * (kC * kC));
+      const V16* tbg = reinterpret_cast<const V16*>(wtbg + ci * (kC * kC));
+#pragma unroll
+      for (int n = 0; n < NPT; ++n) {
+        ptb[n] = tb[tid + n * kThreads];
+        ptbg[n] = tbg[tid + n * kThreads];
+      }
+      if (tid < 2 * kC / 4) pgm = reinterpret_cast<const f32x4*>(wg + ci * (2 * kC))[tid];
     }
   };
 
@@ -268,21 +253,15 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
         *reinterpret_cast<f32x4*>(&Al[r * D + cc]) = pa[n];
       }
     } else {
-      float* lgs = gate;
-      float* gam = gate + kC;
-      float* bet = gate + 2 * kC;
-      if (tid < 64) {
-        float x = logf(pg);
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const float y = __shfl_up(x, off, 64);
-          if (lane >= off) x += y;
-        }
-        lgs[lane] = x;
-        gam[lane] = expf(x);
-      } else if (tid < 128) {
-        bet[lane] = pg;
+      for (int n = 0; n < NPT; ++n) {
+        const int j = tid + n * kThreads;           // 16-byte piece of the 64 x 64 tile
+        const int r = j / (kC / VEC);
+        const int pc = (j % (kC / VEC)) * VEC;      // already in acc order
+        *reinterpret_cast<V16*>(&TBs[r * SC + pc]) = ptb[n];
+        *reinterpret_cast<V16*>(&TBGs[r * SC + pc]) = ptbg[n];
       }
+      if (tid < 2 * kC / 4) *reinterpret_cast<f32x4*>(&gate[4 * tid]) = pgm;
     }
   };
 
@@ -389,24 +368,20 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
       lds_barrier();
     } else {
       const float* lgs = gate;
-      const float* gam = gate + kC;
-      const float* bet = gate + 2 * kC;
-      // ---- K K^T -> L and Q K^T -> A on the 10 lower 16x16 tiles each
-      for (int job = wv; job < 20; job += NW) {
-        const bool isq = job >= 10;
-        const int mt = kTileM[isq ? job - 10 : job];
-        const int nt = kTileN[isq ? job - 10 : job];
-        const T* X = isq ? Qs : Ks;
-        // gates of this lane's 4 rows and its column, read before the MFMAs
+      // ---- Q K^T -> A (decayed, masked s <= r) on the 10 lower 16x16 tiles;
+      // the rest of the chunk's state-independent work comes from the chunk
+      // preparation (TB, TBG, g, gamma)
+      for (int job = wv; job < 10; job += NW) {
+        const int mt = kTileM[job];
+        const int nt = kTileN[job];
         const int r0 = 16 * mt + 4 * lg;
         const int s = 16 * nt + l16;
         const f32x4 lr = *reinterpret_cast<const f32x4*>(&lgs[r0]);
-        const f32x4 br = *reinterpret_cast<const f32x4*>(&bet[r0]);
         const float ls = lgs[s];
         Frag<T> xa[D / 32], xb[D / 32];
 #pragma unroll
         for (int p = 0; p < D / 32; ++p) {
-          xa[p] = lds_frag8(&X[(16 * mt + l16) * SK + 32 * p + 8 * lg]);
+          xa[p] = lds_frag8(&Qs[(16 * mt + l16) * SK + 32 * p + 8 * lg]);
           xb[p] = lds_frag8(&Ks[(16 * nt + l16) * SK + 32 * p + 8 * lg]);
         }
         f32x4 acc = zero4();
@@ -415,72 +390,10 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = r0 + i;
-          const float dec = __expf(fminf(lr[i] - ls, 0.f));
-          if (isq) Aqs[r * SC + acc_pos(s)] = from_f32<T>(s <= r ? dec * acc[i] : 0.f);
-          else Lf[r * kSL + s] = s < r ? br[i] * dec * acc[i] : 0.f;
+          const float dec = __builtin_amdgcn_exp2f(fminf(lr[i] - ls, 0.f));
+          Aqs[r * SC + acc_pos(s)] = from_f32<T>(s <= r ? dec * acc[i] : 0.f);
         }
       }
-      lds_barrier();
-      // ---- diagonal 16x16 blocks of (I + L)^-1 by forward substitution
-      if (wv == 0) {
-        const int blk = lane >> 4;
-        const int j = l16;
-        float* Lb = Lf + 16 * blk * kSL + 16 * blk;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float acc = r == j ? 1.f : 0.f;
-#pragma unroll
-          for (int s2 = 0; s2 < r; ++s2) acc -= Lb[r * kSL + s2] * x[s2];
-          x[r] = acc;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Lb[r * kSL + j] = x[r];
-      }
-      lds_barrier();
-      // ---- level 1: X10 = -X11 L10 X00, X32 = -X33 L32 X22
-      if (wv < 2) {
-        const int o0 = wv == 0 ? 0 : 32;
-        const float* L10 = Lf + (o0 + 16) * kSL + o0;
-        const float* X00 = Lf + o0 * kSL + o0;
-        const float* X11 = Lf + (o0 + 16) * kSL + o0 + 16;
-        f32x4 y = mm16(L10, X00, zero4(), l16, lg);
-        f32x4 xo = -mm16_acc(X11, y, zero4(), l16, lg);
-        st16(Lf + (o0 + 16) * kSL + o0, xo, l16, lg);
-      }
-      lds_barrier();
-      // ---- level 2: bottom-left 32x32 block = -X_BR (L_BL X_TL)
-      {
-        const bool act = wv < 4;               // one wave per bottom-left block
-        const int br = 32 + 16 * ((wv >> 1) & 1);   // block row of Y / X
-        const int bc = 16 * (wv & 1);               // block column
-        // Y_{br,bc} = sum_k L_{br,k} X_{k,bc}, k over the top-left blocks >= bc
-        f32x4 y = zero4();
-        if (act)
-          for (int kb = bc; kb < 32; kb += 16) y = mm16(Lf + br * kSL + kb, Lf + kb * kSL + bc, y, l16, lg);
-        lds_barrier();
-        if (act) st16(Lf + br * kSL + bc, y, l16, lg);
-        lds_barrier();
-        // X_{br,bc} = -sum_k X_{br,k} Y_{k,bc}, k over bottom-right blocks <= br
-        f32x4 xo = zero4();
-        if (act)
-          for (int kb = 32; kb <= br; kb += 16) xo = mm16(Lf + br * kSL + kb, Lf + kb * kSL + bc, xo, l16, lg);
-        lds_barrier();
-        if (act) st16(Lf + br * kSL + bc, -xo, l16, lg);
-        lds_barrier();
-      }
-      // ---- Tm diag(b) and Tm diag(b gamma), 4 columns per task
-      for (int i = tid; i < kC * kC / 4; i += kThreads) {
-        const int r = i >> 4;
-        const int s0 = (i & 15) * 4;
-        const f32x4 tm = *reinterpret_cast<const f32x4*>(&Lf[r * kSL + s0]);
-        const f32x4 bb = *reinterpret_cast<const f32x4*>(&bet[s0]);
-        const f32x4 gg = *reinterpret_cast<const f32x4*>(&gam[s0]);
-        const f32x4 tb = tm * bb;
-        store4(&TBs[r * SC + acc_pos(s0)], tb);
-        store4(&TBGs[r * SC + acc_pos(s0)], tb * gg);
-      }
-      lds_barrier();
       // ---- Wm^T = K^T (Tm diag(b gamma))^T, stored as -Wm [token][dk];
       // each wave owns MT/NW dk tiles and reuses the TBG fragments
       if (wv < MT) {
@@ -643,8 +556,8 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
         f32x4 s0, s1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          s0[i] = __expf(fminf(lgC - gate[32 * pp + 4 * lg + i], 0.f));
-          s1[i] = __expf(fminf(lgC - gate[32 * pp + 16 + 4 * lg + i], 0.f));
+          s0[i] = __builtin_amdgcn_exp2f(fminf(lgC - gate[32 * pp + 4 * lg + i], 0.f));
+          s1[i] = __builtin_amdgcn_exp2f(fminf(lgC - gate[32 * pp + 16 + 4 * lg + i], 0.f));
         }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -738,9 +651,19 @@ hipError_t launch_linear_t(const PrefillArgs& p, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, SM::bytes);
   if (e != hipSuccess) return e;
   const dim3 grid(D / SM::DVS, p.H, p.B);
+  const T* wtb = nullptr;
+  const T* wtbg = nullptr;
+  const float* wg = nullptr;
+  if (!GLA) {
+    const GdnWorkspace w =
+        gdn_workspace_layout(p.workspace, p.B, p.H, gdn_stream_chunks(p.T, p.n_sink, p.window), sizeof(T));
+    wtb = (const T*)w.tb;
+    wtbg = (const T*)w.tbg;
+    wg = w.g;
+  }
   hipLaunchKernelGGL(kern, grid, dim3(64 * NW), SM::bytes, s, (const T*)p.q, (const T*)p.k,
-                     (const T*)p.v, p.a, p.b, (T*)p.o, p.state_out, p.T, p.H, p.Hkv, p.n_sink,
-                     p.window, p.flags);
+                     (const T*)p.v, p.a, wtb, wtbg, wg, (T*)p.o, p.state_out, p.T, p.H, p.Hkv,
+                     p.n_sink, p.window, p.flags);
   return hipGetLastError();
 }
 
@@ -765,6 +688,13 @@ size_t linear_lds_bytes(int D, int bf16, int gla) {
 }
 
 hipError_t launch_linear_prefill(const PrefillArgs& p, hipStream_t s) {
+  if (!p.gla) {
+    const int nch = gdn_stream_chunks(p.T, p.n_sink, p.window);
+    if (nch > 0) {
+      const hipError_t e = launch_gdn_prep(p, nch, s);
+      if (e != hipSuccess) return e;
+    }
+  }
   if (p.bf16) return p.gla ? launch_linear_d<bf16, true>(p, s) : launch_linear_d<bf16, false>(p, s);
   if (p.D != 64) return hipErrorInvalidValue;   // fp32 state tiles fit LDS only at d = 64
   return p.gla ? launch_linear_t<float, 64, 4, 16, true>(p, s) : launch_linear_t<float, 64, 4, 16, false>(p, s);

@@ -63,7 +63,16 @@ def ws(lib, *args):
 
 
 def test_workspace_query(lib):
-    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 3) == (OK, 0)
+    # gated delta rule: per (sequence, head, 64-token chunk of the linear
+    # stream) two 64x64 tiles of the I/O type and 128 fp32 gate values
+    nch = (4096 - 64 + 63) // 64
+    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 3) == (OK, 32 * nch * (2 * 4096 * 2 + 512))
+    assert ws(lib, 2, 300, 4, 2, 64, 64, 8, 56, F32, DELTA, 5) == (OK, 2 * 4 * 4 * (2 * 4096 * 4 + 512))
+    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 4)[1] > 0          # state only
+    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 2) == (OK, 0)     # softmax only
+    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, GLA, 3) == (OK, 0)       # GLA: none
+    assert ws(lib, 1, 64, 32, 8, 128, 128, 8, 56, BF16, DELTA, 3) == (OK, 0)       # T <= budget
+    assert ws(lib, 1, 65, 32, 8, 128, 128, 8, 56, BF16, DELTA, 3)[1] > 0
     assert ws(lib, 1, 4096, 32, 7, 128, 128, 8, 56, BF16, DELTA, 3)[0] == EINVAL   # H % Hkv
     assert ws(lib, 1, 4096, 32, 8, 96, 96, 8, 56, BF16, DELTA, 3)[0] == EINVAL     # d
     assert ws(lib, 1, 4096, 32, 8, 128, 64, 8, 56, BF16, DELTA, 3)[0] == EINVAL    # dk != dv
@@ -105,6 +114,19 @@ def test_prefill_validation(lib):
     # fp32 softmax-only at d=128 is supported, so only the missing pointer fails here
     assert prefill(lib, dt=F32, dk=128, dv=128, flags=2, q=None) == EINVAL
     assert prefill(lib, B=1 << 16, T=1 << 16) == EINVAL          # B*T overflows int
+
+
+def test_prefill_workspace_checks(lib):
+    # T = 200 > budget: the gated delta rule needs its chunk workspace
+    assert prefill(lib, T=200) == EWS
+    big = ctypes.c_void_p(FAKE.value)
+    assert lib.gdn_hybrid_prefill(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 200, 2, 2, 64, 64,
+                                  8, 56, BF16, DELTA, 3, big, 16, None) == EWS    # too small
+    assert lib.gdn_hybrid_prefill(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 200, 2, 2, 64, 64,
+                                  8, 56, BF16, DELTA, 3, ctypes.c_void_p(FAKE.value + 8), 1 << 30,
+                                  None) == EINVAL                                  # misaligned
+    # a GLA call needs none: with q missing it fails on q, not on the workspace
+    assert prefill(lib, T=200, up=GLA, b=None, q=None) == EINVAL
 
 
 def test_prefill_zero_length_is_a_noop(lib):
