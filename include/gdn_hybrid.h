@@ -98,15 +98,17 @@ int gdn_hybrid_last_hip_error(void);
 
 /*
  * Workspace bytes gdn_hybrid_prefill needs for these arguments (written to
- * *bytes).  Non-zero only for the gated delta rule (update GDN_DELTA) when
- * the linear branch or the state is requested and T > n_sink + window: the
- * state-independent part of every 64-token chunk (the inverse of the chunk's
- * unit lower-triangular system scaled by b and by b * gamma, and the gate
- * prefix sums) is computed for all chunks in parallel and stored there, so
- * the sequential scan over chunks only does the state-dependent products.
- * Size: B * H * nch * (2 * 64 * 64 * elt + 128 * 4) bytes with
- * nch = ceil((T - window - n_sink) / 64) and elt the size of `dtype`
- * (about 34 MB for B=1, H=32, T=4096, bf16).
+ * *bytes).  Non-zero when the linear branch or the state is requested and
+ * T > n_sink + window: the state-independent part of every 64-token chunk is
+ * computed for all chunks in parallel and stored there, so the sequential
+ * scan over chunks only does the state-dependent products.  With
+ * nch = ceil((T - window - n_sink) / 64) and elt the size of `dtype`:
+ *   GDN_DELTA: B * H * nch * (2 * 64 * 64 * elt + 128 * 4) bytes (the inverse
+ *     of the chunk's unit lower-triangular system scaled by b and by
+ *     b * gamma, and the gate prefix sums; about 34 MB for B=1, H=32,
+ *     T=4096, bf16);
+ *   GDN_GLA: B * H * nch * ((2 * 64 * dk + 64 * 64) * elt + dk * 4) bytes
+ *     (gate-scaled Q and K^T, the intra-chunk scores, the chunk decay).
  * Errors: GDN_EINVAL if bytes is NULL or the shape arguments are invalid.
  */
 int gdn_hybrid_prefill_workspace(int B, int T, int H, int Hkv, int dk, int dv,

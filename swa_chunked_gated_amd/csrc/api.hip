@@ -59,13 +59,15 @@ int gdn_hybrid_last_hip_error(void) { return g_last_hip_error.load(); }
 namespace {
 // Workspace the linear branch of this call needs (0 unless the gated delta
 // rule recurrence runs over at least one chunk).
-size_t prefill_workspace_bytes(int B, int T, int H, int n_sink, int window, int dtype, int update,
-                               int flags) {
+size_t prefill_workspace_bytes(int B, int T, int H, int dk, int n_sink, int window, int dtype,
+                               int update, int flags) {
   const bool rec = (flags & GDN_BRANCH_LINEAR) || (flags & GDN_WRITE_STATE);
-  if (!rec || update != GDN_DELTA) return 0;
+  if (!rec) return 0;
   const int nch = gdn::gdn_stream_chunks(T, n_sink, window);
   if (nch == 0) return 0;
-  return gdn::gdn_workspace_layout(nullptr, B, H, nch, dtype == GDN_BF16 ? 2 : 4).bytes;
+  const size_t elt = dtype == GDN_BF16 ? 2 : 4;
+  if (update == GDN_GLA) return gdn::gla_workspace_layout(nullptr, B, H, nch, dk, elt).bytes;
+  return gdn::gdn_workspace_layout(nullptr, B, H, nch, elt).bytes;
 }
 }  // namespace
 
@@ -74,7 +76,7 @@ int gdn_hybrid_prefill_workspace(int B, int T, int H, int Hkv, int dk, int dv, i
   if (!bytes) return GDN_EINVAL;
   if (!dims_ok(B, T, H, Hkv, dk, dv, n_sink, window, dtype, update)) return GDN_EINVAL;
   if (flags < 1 || flags > 15 || (flags & 7) == 0) return GDN_EINVAL;
-  *bytes = prefill_workspace_bytes(B, T, H, n_sink, window, dtype, update, flags);
+  *bytes = prefill_workspace_bytes(B, T, H, dk, n_sink, window, dtype, update, flags);
   return GDN_OK;
 }
 
@@ -95,7 +97,7 @@ int gdn_hybrid_prefill(const void* q, const void* k, const void* v, const float*
   if (needs_rec && update == GDN_DELTA && !b) return GDN_EINVAL;
   if (wst && !state_out) return GDN_EINVAL;
   if (needs_rec && dtype == GDN_F32 && dk != 64) return GDN_EUNSUPPORTED;
-  const size_t need = prefill_workspace_bytes(B, T, H, n_sink, window, dtype, update, flags);
+  const size_t need = prefill_workspace_bytes(B, T, H, dk, n_sink, window, dtype, update, flags);
   if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_EWORKSPACE;
   if (need > 0 && ((uintptr_t)workspace & 255u) != 0) return GDN_EINVAL;
   if (T == 0 && !wst) return GDN_OK;

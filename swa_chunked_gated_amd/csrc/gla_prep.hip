@@ -1,0 +1,288 @@
+// Chunk preparation for the chunked GLA variant (prefill): everything about a
+// 64-token chunk that does not depend on the recurrent state, done for every
+// chunk at once so that the sequential scan only keeps the state products.
+//
+// Method (page "The Key to Going Linear: Analysis-Driven Transformer
+// Linearization", section 线性注意力替换机制): GLA update
+// S_i = Diag(alpha_i) S_{i-1} + k_i v_i^T with a per-channel forget gate.
+// Over a chunk with G_r = inclusive cumsum of log2 alpha (per channel), the
+// chunk is exact with
+//   O   = (Q 2^G) S0 + A V,   A_rs = [s <= r] sum_c q_r[c] k_s[c] 2^{G_r[c] - G_s[c]}
+//   S   = 2^{G_C} o_rows S0 + (K 2^{G_C - G})^T V.
+// Outputs per chunk (workspace, element type T unless noted):
+//   QG  [64][D]   Q 2^G, columns in acc order (the scan's Q tile layout);
+//   KTG [D][64]   (K 2^{G_C - G})^T, tokens in acc order;
+//   A   [64][64]  the masked intra-chunk scores, columns in acc order;
+//   EGC [D] fp32  2^{G_C}.
+// All three operand tiles are bounded by 1 per channel factor.  A needs
+// 2^{G_r - G_s}, which would leave the float range if split as
+// 2^{G_r} 2^{-G_s} against the chunk start, so each 16-row tile j takes the
+// cumulative gate at its row 16j + 7 as reference point M_j: the operands
+// q_r 2^{G_r - M_j} and k_s 2^{M_j - G_s} grow by at most the decay of 8
+// tokens (clamped at 2^115), and a pair of different tiles (mt > nt) takes the
+// per-channel factor 2^{M_mt - M_nt} <= 1 on its key operand.
+//
+// One workgroup of 8 waves per (chunk, query head, sequence).
+
+#include "common.h"
+#include "launch.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kC = 64;
+__constant__ const int kGlaTileM[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+__constant__ const int kGlaTileN[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+
+template <class T, int D>
+struct GlaPrepSmem {
+  static constexpr int PAD = 16 / sizeof(T);
+  static constexpr int SK = D + PAD;      // stride of [64][D] tiles
+  static constexpr int SC = kC + PAD;     // stride of [*][64] tiles
+  static constexpr int oQD = 0;                       // q 2^{G - M}
+  static constexpr int oKD = oQD + kC * SK;           // k 2^{M - G}
+  static constexpr int oKT = oKD + kC * SK;           // K^T 2^{G_C - G}
+  static constexpr int oA = oKT + D * SC;             // A
+  static constexpr int nT = oA + kC * SC;
+  static constexpr int bytesT = (nT * (int)sizeof(T) + 15) / 16 * 16;
+  static constexpr int nG = kC * D;                   // cumulative log2 gates
+  static constexpr int nMf = 6 * D;                   // tile-pair factors
+  static constexpr int bytes = bytesT + 4 * (nG + nMf);
+};
+
+template <class T, int D>
+__global__ __launch_bounds__(512) void gla_prep_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ a,
+    T* __restrict__ wqg, T* __restrict__ wktg, T* __restrict__ wa, float* __restrict__ wegc,
+    int T_, int H, int Hkv, int n_sink, int window, int nch) {
+  using SM = GlaPrepSmem<T, D>;
+  constexpr int NTH = 512;
+  constexpr int SK = SM::SK;
+  constexpr int SC = SM::SC;
+  constexpr int VEC = 16 / (int)sizeof(T);
+  typedef typename Vec16<T>::type V16;
+
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  T* sT = reinterpret_cast<T*>(smem_raw);
+  T* QDs = sT + SM::oQD;
+  T* KDs = sT + SM::oKD;
+  T* KTs = sT + SM::oKT;
+  T* As = sT + SM::oA;
+  float* Gl = reinterpret_cast<float*>(smem_raw + SM::bytesT);   // [64][D]
+  float* Mf = Gl + SM::nG;                                        // [6][D], acc order
+
+  const int c = blockIdx.x;
+  const int h = blockIdx.y;
+  const int bi = blockIdx.z;
+  const int g = h / (H / Hkv);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = wave_id();
+  const int l16 = lane & 15;
+  const int lg = lane >> 4;
+  const int iend = T_ - window;
+  const int i0 = n_sink + c * kC;
+  const size_t ci = ((size_t)bi * H + h) * nch + c;
+
+  // ---- all global loads of the chunk first (gates, q rows, k rows), so
+  // their latency overlaps
+  constexpr int NA4 = kC * D / 4 / NTH;            // f32x4 gate pieces per thread
+  constexpr int NPC = kC * D / VEC / NTH;          // 16-byte q / k pieces per thread
+  static_assert(kC * D / 4 % NTH == 0 && kC * D / VEC % NTH == 0, "staging");
+  f32x4 ga[NA4];
+  V16 qv[NPC], kv[NPC];
+  const T* qbase = q + ((size_t)(bi * T_ + i0 + window) * H + h) * D;
+  const T* kbase = k + ((size_t)(bi * T_ + i0) * Hkv + g) * D;
+#pragma unroll
+  for (int j = 0; j < NA4; ++j) {
+    const int idx = tid + j * NTH;
+    const int r = idx / (D / 4);
+    const int cc = (idx % (D / 4)) * 4;
+    ga[j] = i0 + r < iend ? *reinterpret_cast<const f32x4*>(a + ((size_t)(bi * T_ + i0 + r) * H + h) * D + cc)
+                          : f32x4{1.f, 1.f, 1.f, 1.f};
+  }
+#pragma unroll
+  for (int j = 0; j < NPC; ++j) {
+    const int idx = tid + j * NTH;
+    const int r = idx / (D / VEC);
+    const int cc = (idx % (D / VEC)) * VEC;
+    if (i0 + r < iend) {
+      qv[j] = *reinterpret_cast<const V16*>(qbase + (size_t)r * H * D + cc);
+      kv[j] = *reinterpret_cast<const V16*>(kbase + (size_t)r * Hkv * D + cc);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        qv[j][e] = from_f32<T>(0.f);
+        kv[j][e] = from_f32<T>(0.f);
+      }
+    }
+  }
+
+  // ---- log2 gates, then the per-channel inclusive prefix over the 64 rows:
+  // each thread owns one channel and a run of rows
+  constexpr int SEG = NTH / D;             // row segments per channel
+  constexpr int RPS = kC / SEG;            // rows per segment
+#pragma unroll
+  for (int j = 0; j < NA4; ++j) {
+    const int idx = tid + j * NTH;
+    const int r = idx / (D / 4);
+    const int cc = (idx % (D / 4)) * 4;
+    f32x4 x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = __builtin_amdgcn_logf(ga[j][e]);
+    *reinterpret_cast<f32x4*>(&Gl[r * D + cc]) = x;
+  }
+  __syncthreads();
+  {
+    const int cc = tid % D;
+    const int seg = tid / D;
+    float run = 0.f;
+    float vals[RPS];
+#pragma unroll
+    for (int j = 0; j < RPS; ++j) vals[j] = Gl[(seg * RPS + j) * D + cc];
+#pragma unroll
+    for (int j = 0; j < RPS; ++j) {
+      run += vals[j];
+      vals[j] = run;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < RPS; ++j) Gl[(seg * RPS + j) * D + cc] = vals[j];
+    __syncthreads();
+    float off = 0.f;
+    for (int s2 = 0; s2 < seg; ++s2) off += Gl[((s2 + 1) * RPS - 1) * D + cc];
+    __syncthreads();
+    if (seg > 0) {
+#pragma unroll
+      for (int j = 0; j < RPS; ++j) Gl[(seg * RPS + j) * D + cc] = vals[j] + off;
+    }
+  }
+  __syncthreads();
+
+  // ---- scaled operands: Q 2^G (to the workspace), q 2^{G - M}, k 2^{M - G}
+  // (LDS, for A) and K^T 2^{G_C - G} (LDS, copied out below); VEC channels of
+  // one row per piece, written as runs of 4 (contiguous in acc order)
+  T* qg = wqg + ci * (kC * D);
+#pragma unroll
+  for (int j = 0; j < NPC; ++j) {
+    const int idx = tid + j * NTH;
+    const int r = idx / (D / VEC);
+    const int cb = (idx % (D / VEC)) * VEC;
+#pragma unroll
+    for (int m = 0; m < VEC / 4; ++m) {
+      const int cc = cb + 4 * m;
+      const int pc = acc_pos(cc);
+      const f32x4 G4 = *reinterpret_cast<const f32x4*>(&Gl[r * D + cc]);
+      const f32x4 M4 = *reinterpret_cast<const f32x4*>(&Gl[((r & ~15) + 7) * D + cc]);
+      const f32x4 C4 = *reinterpret_cast<const f32x4*>(&Gl[(kC - 1) * D + cc]);
+      f32x4 qo, qd, kd, kt;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const float qx = to_f32(qv[j][4 * m + x]);
+        const float kx = to_f32(kv[j][4 * m + x]);
+        qo[x] = qx * __builtin_amdgcn_exp2f(G4[x]);
+        qd[x] = qx * __builtin_amdgcn_exp2f(fminf(G4[x] - M4[x], 115.f));
+        kd[x] = kx * __builtin_amdgcn_exp2f(fminf(M4[x] - G4[x], 115.f));
+        kt[x] = kx * __builtin_amdgcn_exp2f(fminf(C4[x] - G4[x], 0.f));
+      }
+      store4(qg + r * D + pc, qo);
+      store4(&QDs[r * SK + pc], qd);
+      store4(&KDs[r * SK + pc], kd);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) KTs[(cc + x) * SC + acc_pos(r)] = from_f32<T>(kt[x]);
+    }
+  }
+  // tile-pair factors 2^{M_mt - M_nt}, pair index mt (mt - 1) / 2 + nt
+  for (int i = tid; i < 6 * D; i += NTH) {
+    const int pr = i / D;
+    const int cc = i % D;
+    const int mt = pr < 1 ? 1 : (pr < 3 ? 2 : 3);
+    const int nt = pr - mt * (mt - 1) / 2;
+    Mf[pr * D + acc_pos(cc)] = __builtin_amdgcn_exp2f(Gl[(16 * mt + 7) * D + cc] - Gl[(16 * nt + 7) * D + cc]);
+  }
+  if (tid < D) wegc[ci * D + tid] = __builtin_amdgcn_exp2f(Gl[(kC - 1) * D + tid]);
+  __syncthreads();
+
+  // ---- A = [s <= r] 2^{G_r - G_s} o (Q K^T) on the 10 lower tiles
+  for (int job = wv; job < 10; job += NTH / 64) {
+    const int mt = kGlaTileM[job];
+    const int nt = kGlaTileN[job];
+    f32x4 acc = zero4();
+    if (mt == nt) {
+#pragma unroll
+      for (int p = 0; p < D / 32; ++p)
+        acc = mfma(lds_frag8(&QDs[(16 * mt + l16) * SK + 32 * p + 8 * lg]),
+                   lds_frag8(&KDs[(16 * nt + l16) * SK + 32 * p + 8 * lg]), acc);
+    } else {
+      const float* mf = Mf + (mt * (mt - 1) / 2 + nt) * D;
+#pragma unroll
+      for (int p = 0; p < D / 32; ++p)
+        acc = mfma(lds_frag8(&QDs[(16 * mt + l16) * SK + 32 * p + 8 * lg]),
+                   lds_frag8_scaled(&KDs[(16 * nt + l16) * SK + 32 * p + 8 * lg], mf + 32 * p + 8 * lg),
+                   acc);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * mt + 4 * lg + i;
+      const int s = 16 * nt + l16;
+      As[r * SC + acc_pos(s)] = from_f32<T>(s <= r ? acc[i] : 0.f);
+    }
+  }
+  // the strictly upper tiles of A are zero
+  for (int i = tid; i < 6 * 16 * 16; i += NTH) {
+    const int pr = i / 256;
+    const int e = i % 256;
+    const int mt = pr < 3 ? 0 : (pr < 5 ? 1 : 2);
+    const int nt = pr < 3 ? pr + 1 : (pr < 5 ? pr - 1 : 3);
+    As[(16 * mt + e / 16) * SC + acc_pos(16 * nt + e % 16)] = from_f32<T>(0.f);
+  }
+  __syncthreads();
+
+  // ---- copy K^T 2^{G_C - G} and A out as 16-byte pieces
+  T* ktg = wktg + ci * (D * kC);
+  T* aa = wa + ci * (kC * kC);
+  for (int i = tid; i < D * kC / VEC; i += NTH) {
+    const int r = i / (kC / VEC);
+    const int pc = (i % (kC / VEC)) * VEC;
+    *reinterpret_cast<V16*>(ktg + r * kC + pc) = *reinterpret_cast<const V16*>(&KTs[r * SC + pc]);
+  }
+  for (int i = tid; i < kC * kC / VEC; i += NTH) {
+    const int r = i / (kC / VEC);
+    const int pc = (i % (kC / VEC)) * VEC;
+    *reinterpret_cast<V16*>(aa + r * kC + pc) = *reinterpret_cast<const V16*>(&As[r * SC + pc]);
+  }
+}
+
+template <class T, int D>
+hipError_t launch_gla_prep_t(const PrefillArgs& p, int nch, hipStream_t s) {
+  using SM = GlaPrepSmem<T, D>;
+  auto kern = gla_prep_kernel<T, D>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, SM::bytes);
+  if (e != hipSuccess) return e;
+  const GlaWorkspace w = gla_workspace_layout(p.workspace, p.B, p.H, nch, D, sizeof(T));
+  hipLaunchKernelGGL(kern, dim3(nch, p.H, p.B), dim3(512), SM::bytes, s, (const T*)p.q,
+                     (const T*)p.k, p.a, (T*)w.qg, (T*)w.ktg, (T*)w.a, w.egc, p.T, p.H, p.Hkv,
+                     p.n_sink, p.window, nch);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+GlaWorkspace gla_workspace_layout(void* base, int B, int H, int nch, int D, size_t elt) {
+  GlaWorkspace w;
+  const size_t n = (size_t)B * H * nch;
+  unsigned char* p = static_cast<unsigned char*>(base);
+  w.qg = p;
+  w.ktg = p + n * kC * D * elt;
+  w.a = p + 2 * n * kC * D * elt;
+  w.egc = reinterpret_cast<float*>(p + 2 * n * kC * D * elt + n * kC * kC * elt);
+  w.bytes = 2 * n * kC * D * elt + n * kC * kC * elt + n * D * sizeof(float);
+  return w;
+}
+
+hipError_t launch_gla_prep(const PrefillArgs& p, int nch, hipStream_t s) {
+  if (p.bf16) return p.D == 64 ? launch_gla_prep_t<bf16, 64>(p, nch, s) : launch_gla_prep_t<bf16, 128>(p, nch, s);
+  return p.D == 64 ? launch_gla_prep_t<float, 64>(p, nch, s) : launch_gla_prep_t<float, 128>(p, nch, s);
+}
+
+}  // namespace gdn

@@ -33,6 +33,17 @@ struct GdnWorkspace {
   size_t bytes;
 };
 GdnWorkspace gdn_workspace_layout(void* base, int B, int H, int nch, size_t elt);
+// Workspace of the GLA prefill: for each (sequence, head, chunk) Q 2^G
+// [64][D], (K 2^{G_C - G})^T [D][64], A [64][64] (I/O type, reduction index in
+// acc order) and 2^{G_C} [D] fp32, as four consecutive arrays.
+struct GlaWorkspace {
+  void* qg;
+  void* ktg;
+  void* a;
+  float* egc;
+  size_t bytes;
+};
+GlaWorkspace gla_workspace_layout(void* base, int B, int H, int nch, int D, size_t elt);
 // Chunks of the linear stream of a sequence of length T.
 inline int gdn_stream_chunks(int T, int n_sink, int window) {
   const long long n = (long long)T - window - n_sink;
@@ -91,8 +102,9 @@ struct ShortConvArgs {
 // t < n_sink + window for a linear-only overwrite, and writes the final
 // state when asked.
 hipError_t launch_linear_prefill(const PrefillArgs& a, hipStream_t s);
-// Chunk preparation of the gated delta rule into a.workspace (nch chunks).
+// Chunk preparation of the gated delta rule / of GLA into a.workspace (nch chunks).
 hipError_t launch_gdn_prep(const PrefillArgs& a, int nch, hipStream_t s);
+hipError_t launch_gla_prep(const PrefillArgs& a, int nch, hipStream_t s);
 // Softmax branch: writes every row of o, adding the value o already holds
 // on rows t >= add_from.
 hipError_t launch_swa_prefill(const PrefillArgs& a, int add_from, hipStream_t s);

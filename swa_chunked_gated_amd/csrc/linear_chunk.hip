@@ -57,30 +57,31 @@ struct Smem {
   static constexpr int nKT = D * SC;
   static constexpr int nVT = DVS * SC;
   static constexpr int nA = kC * SC;
-  // element offsets in units of T
+  // element offsets in units of T (GLA keeps only Q 2^G, K^T 2^{G_C-G}, V^T, A)
   static constexpr int oK = 0;
-  static constexpr int oKT = oK + nK;
+  static constexpr int oKT = oK + (GLA ? 0 : nK);
   static constexpr int oQ = oKT + nKT;
   static constexpr int oVT = oQ + nK;
   static constexpr int oAq = oVT + nVT;
-  static constexpr int oWm = oAq + nA;               // GDN: Wm; GLA: Q at tile references
-  static constexpr int oTB = oWm + nK;
+  static constexpr int oWm = oAq + nA;
+  static constexpr int oTB = oWm + (GLA ? 0 : nK);
   static constexpr int oTBG = oTB + (GLA ? 0 : nA);
   static constexpr int nT = oTBG + (GLA ? 0 : nA);
   static constexpr int bytesT = ((nT * (int)sizeof(T)) + 15) / 16 * 16;
-  // fp32 part
-  static constexpr int nAl = GLA ? kC * D : 0;       // GLA cumulative log-gates
-  static constexpr int nMf = GLA ? 6 * D : 0;        // GLA tile-pair factors
-  static constexpr int nGate = GLA ? D : 2 * kC;     // GDN: g (log2), gamma; GLA: G_C
-  static constexpr int bytes = bytesT + 4 * (nAl + nMf + nGate);
+  // fp32 part: GDN g (log2), gamma [64 each]; GLA 2^{G_C} [D]
+  static constexpr int nGate = GLA ? D : 2 * kC;
+  static constexpr int bytes = bytesT + 4 * nGate;
 };
 
 template <class T, int D, int NW, int DW, bool GLA>
 __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const float* __restrict__ a, const T* __restrict__ wtb, const T* __restrict__ wtbg,
-    const float* __restrict__ wg, T* __restrict__ o, float* __restrict__ state_out, int T_, int H,
+    const T* __restrict__ w0, const T* __restrict__ w1, const T* __restrict__ w2,
+    const float* __restrict__ wf, T* __restrict__ o, float* __restrict__ state_out, int T_, int H,
     int Hkv, int n_sink, int window, int flags) {
+  // chunk preparation results (workspace), per (sequence, head, chunk):
+  //   GDN: w0 = Tm diag(b), w1 = Tm diag(b gamma), wf = g (log2), gamma
+  //   GLA: w0 = Q 2^G, w1 = (K 2^{G_C - G})^T, w2 = A, wf = 2^{G_C}
   using SM = Smem<T, D, NW, DW, GLA>;
   constexpr int kThreads = 64 * NW;
   constexpr int SK = SM::SK;
@@ -100,7 +101,9 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
   constexpr int TPTV = TPW * DPRV / 64;           // tokens per thread (V)
   static_assert(MT % NW == 0 || NW % MT == 0, "wave split of the state rows");
   constexpr int NPQ = kC * D / VEC / kThreads;    // Q 16-byte pieces per thread
-  constexpr int NPA = GLA ? kC * D / 4 / kThreads : 0;
+  constexpr int NPK = D * kC / VEC / kThreads;    // GLA: K^T pieces per thread
+  constexpr int NPA = kC * kC / VEC / kThreads;   // GLA: A pieces per thread
+  static_assert(!GLA || ((D * kC / VEC) % kThreads == 0 && NPA >= 1), "GLA staging");
   static_assert(DPR <= 64 && 64 % DPR == 0 && DPRV <= 64 && 64 % DPRV == 0, "row shape");
   static_assert(TPT % 8 == 0 && TPTV % 8 == 0 && NPQ >= 1, "tile shape");
 
@@ -114,11 +117,7 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
   T* Wms = sT + SM::oWm;
   T* TBs = sT + SM::oTB;
   T* TBGs = sT + SM::oTBG;
-  float* sF = reinterpret_cast<float*>(smem_raw + SM::bytesT);
-  float* Al = sF;                    // [64][D]    cumulative log-gates (GLA)
-  float* Mf = Al + SM::nAl;          // [6][D]     GLA tile-pair factors (acc order)
-  float* gate = Mf + SM::nMf;        // GDN: g[64] (log2), gam[64]; GLA: GC[D]
-  T* QDs = Wms;                      // GLA: q scaled to its tile's reference point
+  float* gate = reinterpret_cast<float*>(smem_raw + SM::bytesT);   // GDN: g[64], gam[64]; GLA: 2^{G_C}[D]
 
   const int sp = blockIdx.x;          // column slice
   const int h = blockIdx.y;
@@ -151,14 +150,14 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
 
   // ---------------- register prefetch of one chunk's inputs
   typedef typename Vec16<T>::type V16;
-  uint32_t pk[TPT], pv[TPTV];
+  // V (dword columns, both updates); GDN: K (dword columns), Q (16-byte row
+  // pieces), TB / TBG and g, gamma from the workspace; GLA: Q 2^G, K^T 2^{G_C-G},
+  // A and 2^{G_C} from the workspace
+  uint32_t pk[GLA ? 1 : TPT], pv[TPTV];
   V16 pq[NPQ];
-  f32x4 pa[GLA ? NPA : 1];
-  // GDN: the chunk's TB, TBG rows (16-byte pieces) and g, gamma from the
-  // chunk preparation
   constexpr int NPT = GLA ? 1 : kC * kC / VEC / kThreads;
   static_assert(GLA || (kC * kC / VEC) % kThreads == 0, "TB staging");
-  V16 ptb[NPT], ptbg[NPT];
+  V16 ptb[GLA ? NPK : NPT], ptbg[GLA ? NPA : NPT];
   f32x4 pgm = zero4();
   const size_t chain = (size_t)bi * H + h;
 
@@ -167,92 +166,107 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
   auto prefetch = [&](int c) {
     const int i0 = n_sink + c * kC;
     const bool full = i0 + kC <= iend;               // uniform: no masking needed
-    const T* kp = k + ((size_t)(bi * T_ + i0 + kr0) * Hkv + g) * D + kdc * EPD;
     const T* vp = v + ((size_t)(bi * T_ + i0 + vr0) * Hkv + g) * D + c0 + vdc * EPD;
     if (full) {
-#pragma unroll
-      for (int j = 0; j < TPT; ++j) pk[j] = *reinterpret_cast<const uint32_t*>(kp + j * kvstride);
 #pragma unroll
       for (int j = 0; j < TPTV; ++j) pv[j] = *reinterpret_cast<const uint32_t*>(vp + j * kvstride);
     } else {
 #pragma unroll
-      for (int j = 0; j < TPT; ++j)
-        pk[j] = i0 + kr0 + j < iend ? *reinterpret_cast<const uint32_t*>(kp + j * kvstride) : 0u;
-#pragma unroll
       for (int j = 0; j < TPTV; ++j)
         pv[j] = i0 + vr0 + j < iend ? *reinterpret_cast<const uint32_t*>(vp + j * kvstride) : 0u;
     }
-    const T* qp = q + ((size_t)(bi * T_ + i0 + window) * H + h) * D;
+    const size_t ci = chain * nch + c;
+    if constexpr (GLA) {
+      const V16* qg = reinterpret_cast<const V16*>(w0 + ci * (kC * D));
+      const V16* ktg = reinterpret_cast<const V16*>(w1 + ci * (D * kC));
+      const V16* aa = reinterpret_cast<const V16*>(w2 + ci * (kC * kC));
 #pragma unroll
-    for (int n = 0; n < NPQ; ++n) {
-      const int j = tid + n * kThreads;
-      const int r = j / (D / VEC);
-      const int cc = (j % (D / VEC)) * VEC;
-      if (full || i0 + r < iend) {
-        pq[n] = *reinterpret_cast<const V16*>(qp + r * qstride + cc);
+      for (int n = 0; n < NPQ; ++n) pq[n] = qg[tid + n * kThreads];
+#pragma unroll
+      for (int n = 0; n < NPK; ++n) ptb[n] = ktg[tid + n * kThreads];
+#pragma unroll
+      for (int n = 0; n < NPA; ++n) ptbg[n] = aa[tid + n * kThreads];
+      if (tid < D / 4) pgm = reinterpret_cast<const f32x4*>(wf + ci * D)[tid];
+    } else {
+      const T* kp = k + ((size_t)(bi * T_ + i0 + kr0) * Hkv + g) * D + kdc * EPD;
+      if (full) {
+#pragma unroll
+        for (int j = 0; j < TPT; ++j) pk[j] = *reinterpret_cast<const uint32_t*>(kp + j * kvstride);
       } else {
 #pragma unroll
-        for (int x = 0; x < VEC; ++x) pq[n][x] = from_f32<T>(0.f);
+        for (int j = 0; j < TPT; ++j)
+          pk[j] = i0 + kr0 + j < iend ? *reinterpret_cast<const uint32_t*>(kp + j * kvstride) : 0u;
       }
-    }
-    if (GLA) {
+      const T* qp = q + ((size_t)(bi * T_ + i0 + window) * H + h) * D;
 #pragma unroll
-      for (int n = 0; n < NPA; ++n) {
+      for (int n = 0; n < NPQ; ++n) {
         const int j = tid + n * kThreads;
-        const int r = j / (D / 4);
-        const int cc = (j % (D / 4)) * 4;
-        const int tok = i0 + r;
-        pa[n] = tok < iend ? *reinterpret_cast<const f32x4*>(a + ((size_t)(bi * T_ + tok) * H + h) * D + cc)
-                           : f32x4{1.f, 1.f, 1.f, 1.f};
+        const int r = j / (D / VEC);
+        const int cc = (j % (D / VEC)) * VEC;
+        if (full || i0 + r < iend) {
+          pq[n] = *reinterpret_cast<const V16*>(qp + r * qstride + cc);
+        } else {
+#pragma unroll
+          for (int x = 0; x < VEC; ++x) pq[n][x] = from_f32<T>(0.f);
+        }
       }
-    } else {
-      const size_t ci = chain * nch + c;
-      const V16* tb = reinterpret_cast<const V16*>(wtb + ci * (kC * kC));
-      const V16* tbg = reinterpret_cast<const V16*>(wtbg + ci * (kC * kC));
+      const V16* tb = reinterpret_cast<const V16*>(w0 + ci * (kC * kC));
+      const V16* tbg = reinterpret_cast<const V16*>(w1 + ci * (kC * kC));
 #pragma unroll
       for (int n = 0; n < NPT; ++n) {
         ptb[n] = tb[tid + n * kThreads];
         ptbg[n] = tbg[tid + n * kThreads];
       }
-      if (tid < 2 * kC / 4) pgm = reinterpret_cast<const f32x4*>(wg + ci * (2 * kC))[tid];
+      if (tid < 2 * kC / 4) pgm = reinterpret_cast<const f32x4*>(wf + ci * (2 * kC))[tid];
     }
   };
 
   auto commit = [&]() {
-    // K row-major (one dword per token, columns in acc order) and transposed
-    // (tokens in acc order, runs of 4)
-#pragma unroll
-    for (int j = 0; j < TPT; ++j)
-      *reinterpret_cast<uint32_t*>(&Ks[(kr0 + j) * SK + acc_pos(kdc * EPD)]) = pk[j];
-#pragma unroll
-    for (int e = 0; e < EPD; ++e) store_column_acc<T, TPT>(&KTs[(kdc * EPD + e) * SC], kr0, pk, e);
+    // V transposed (tokens in acc order, runs of 4)
 #pragma unroll
     for (int e = 0; e < EPD; ++e) store_column_acc<T, TPTV>(&VTs[(vdc * EPD + e) * SC], vr0, pv, e);
+    if constexpr (GLA) {
+      // workspace tiles are already in the LDS orders: 16-byte copies
 #pragma unroll
-    for (int n = 0; n < NPQ; ++n) {
-      const int j = tid + n * kThreads;
-      const int r = j / (D / VEC);
-      const int cc = (j % (D / VEC)) * VEC;
-      // runs of 4 logical columns stay contiguous in acc order
-#pragma unroll
-      for (int m = 0; m < VEC / 4; ++m) {
-        T* dst = &Qs[r * SK + acc_pos(cc + 4 * m)];
-        if constexpr (sizeof(T) == 2) {
-          *reinterpret_cast<bf16x4*>(dst) = bf16x4{pq[n][4 * m], pq[n][4 * m + 1], pq[n][4 * m + 2], pq[n][4 * m + 3]};
-        } else {
-          *reinterpret_cast<V16*>(dst) = pq[n];
-        }
+      for (int n = 0; n < NPQ; ++n) {
+        const int j = tid + n * kThreads;
+        *reinterpret_cast<V16*>(&Qs[(j / (D / VEC)) * SK + (j % (D / VEC)) * VEC]) = pq[n];
       }
-    }
-    if (GLA) {
+#pragma unroll
+      for (int n = 0; n < NPK; ++n) {
+        const int j = tid + n * kThreads;
+        *reinterpret_cast<V16*>(&KTs[(j / (kC / VEC)) * SC + (j % (kC / VEC)) * VEC]) = ptb[n];
+      }
 #pragma unroll
       for (int n = 0; n < NPA; ++n) {
         const int j = tid + n * kThreads;
-        const int r = j / (D / 4);
-        const int cc = (j % (D / 4)) * 4;
-        *reinterpret_cast<f32x4*>(&Al[r * D + cc]) = pa[n];
+        *reinterpret_cast<V16*>(&Aqs[(j / (kC / VEC)) * SC + (j % (kC / VEC)) * VEC]) = ptbg[n];
       }
+      if (tid < D / 4) *reinterpret_cast<f32x4*>(&gate[4 * tid]) = pgm;
     } else {
+      // K row-major (one dword per token, columns in acc order) and
+      // transposed (tokens in acc order, runs of 4)
+#pragma unroll
+      for (int j = 0; j < TPT; ++j)
+        *reinterpret_cast<uint32_t*>(&Ks[(kr0 + j) * SK + acc_pos(kdc * EPD)]) = pk[j];
+#pragma unroll
+      for (int e = 0; e < EPD; ++e) store_column_acc<T, TPT>(&KTs[(kdc * EPD + e) * SC], kr0, pk, e);
+#pragma unroll
+      for (int n = 0; n < NPQ; ++n) {
+        const int j = tid + n * kThreads;
+        const int r = j / (D / VEC);
+        const int cc = (j % (D / VEC)) * VEC;
+        // runs of 4 logical columns stay contiguous in acc order
+#pragma unroll
+        for (int m = 0; m < VEC / 4; ++m) {
+          T* dst = &Qs[r * SK + acc_pos(cc + 4 * m)];
+          if constexpr (sizeof(T) == 2) {
+            *reinterpret_cast<bf16x4*>(dst) = bf16x4{pq[n][4 * m], pq[n][4 * m + 1], pq[n][4 * m + 2], pq[n][4 * m + 3]};
+          } else {
+            *reinterpret_cast<V16*>(dst) = pq[n];
+          }
+        }
+      }
 #pragma unroll
       for (int n = 0; n < NPT; ++n) {
         const int j = tid + n * kThreads;           // 16-byte piece of the 64 x 64 tile
@@ -275,98 +289,7 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
     lds_barrier();
     if (c + 1 < nch) prefetch(c + 1);
 
-    if (GLA) {
-      // ---- per-channel cumulative log gates; gate-scaled Q, K, K^T
-      float* GC = gate;
-      if (tid < D) {
-        float x = 0.f;
-        for (int r = 0; r < kC; ++r) {
-          x += logf(Al[r * D + tid]);
-          Al[r * D + tid] = x;
-        }
-        GC[tid] = x;
-      }
-      lds_barrier();
-      // Every product of phase A needs exp(G_r - G_s) for s <= r.  Split as
-      // e^{G_r} e^{-G_s} it leaves the float range once a chunk decays by
-      // more than e^88, so each 16-row tile j gets its own reference point
-      // M_j = G at row 16j + 7: the operands q_r e^{G_r - M_j} and
-      // k_s e^{M_j - G_s} grow by at most the decay of 8 tokens (clamped at
-      // e^80), and a pair of different tiles (mt > nt) takes the per-channel
-      // factor e^{M_mt - M_nt} <= 1 on its key operand.  Q e^G (for O) and
-      // K e^{G_C - G} (for the state update) are bounded by 1 as they are.
-      for (int i = tid; i < kC * D / 4; i += kThreads) {
-        const int r = i / (D / 4);
-        const int cc = (i % (D / 4)) * 4;
-        const int pc = acc_pos(cc);
-        const f32x4 G4 = *reinterpret_cast<const f32x4*>(&Al[r * D + cc]);
-        const f32x4 M4 = *reinterpret_cast<const f32x4*>(&Al[((r & ~15) + 7) * D + cc]);
-        const f32x4 q4 = load4(&Qs[r * SK + pc]);
-        const f32x4 k4 = load4(&Ks[r * SK + pc]);
-        f32x4 qo, qd, kd;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          qo[x] = q4[x] * __expf(G4[x]);
-          qd[x] = q4[x] * __expf(fminf(G4[x] - M4[x], 80.f));
-          kd[x] = k4[x] * __expf(fminf(M4[x] - G4[x], 80.f));
-        }
-        store4(&Qs[r * SK + pc], qo);
-        store4(&QDs[r * SK + pc], qd);
-        store4(&Ks[r * SK + pc], kd);
-      }
-      // tile-pair factors e^{M_mt - M_nt}, pair index mt (mt - 1) / 2 + nt
-      for (int i = tid; i < 6 * D; i += kThreads) {
-        const int pr = i / D;
-        const int cc = i % D;
-        const int mt = pr < 1 ? 1 : (pr < 3 ? 2 : 3);
-        const int nt = pr - mt * (mt - 1) / 2;
-        Mf[pr * D + acc_pos(cc)] = __expf(Al[(16 * mt + 7) * D + cc] - Al[(16 * nt + 7) * D + cc]);
-      }
-      // transposed K e^{G_C - G}, 8 tokens (acc order) of one channel per task
-      for (int i = tid; i < D * (kC / 8); i += kThreads) {
-        const int cc = i % D;
-        const int r0 = 8 * (i / D);
-        T* kt = &KTs[cc * SC + r0];
-        const f32x4 k0 = load4(kt);
-        const f32x4 k1 = load4(kt + 4);
-        const float gc = GC[cc];
-        f32x4 o0, o1;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          o0[x] = k0[x] * __expf(fminf(gc - Al[acc_idx(r0 + x) * D + cc], 0.f));
-          o1[x] = k1[x] * __expf(fminf(gc - Al[acc_idx(r0 + 4 + x) * D + cc], 0.f));
-        }
-        store4(kt, o0);
-        store4(kt + 4, o1);
-      }
-      lds_barrier();
-      // ---- A = [s <= r] exp(G_r - G_s) o (Q K^T) on the 10 lower tiles
-      for (int job = wv; job < 10; job += NW) {
-        const int mt = kTileM[job];
-        const int nt = kTileN[job];
-        f32x4 acc = zero4();
-        if (mt == nt) {
-#pragma unroll
-          for (int p = 0; p < D / 32; ++p)
-            acc = mfma(lds_frag8(&QDs[(16 * mt + l16) * SK + 32 * p + 8 * lg]),
-                       lds_frag8(&Ks[(16 * nt + l16) * SK + 32 * p + 8 * lg]), acc);
-        } else {
-          const float* mf = Mf + (mt * (mt - 1) / 2 + nt) * D;
-#pragma unroll
-          for (int p = 0; p < D / 32; ++p)
-            acc = mfma(lds_frag8(&QDs[(16 * mt + l16) * SK + 32 * p + 8 * lg]),
-                       lds_frag8_scaled(&Ks[(16 * nt + l16) * SK + 32 * p + 8 * lg], mf + 32 * p + 8 * lg),
-                       acc);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * mt + 4 * lg + i;
-          const int s = 16 * nt + l16;
-          Aqs[r * SC + acc_pos(s)] = from_f32<T>(s <= r ? acc[i] : 0.f);
-        }
-      }
-      lds_barrier();
-    } else {
+    if constexpr (!GLA) {
       const float* lgs = gate;
       // ---- Q K^T -> A (decayed, masked s <= r) on the 10 lower 16x16 tiles;
       // the rest of the chunk's state-independent work comes from the chunk
@@ -472,13 +395,10 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
 #pragma unroll
             for (int dt = 0; dt < NT; ++dt) ot[dt][rt] = mfma(vf[dt][p], af[rt][p], ot[dt][rt]);
       }
-      // S = e^{G_C} o_rows S + (K e^{G_C - G})^T V
-      const float* GC = gate;
+      // S = 2^{G_C} o_rows S + (K 2^{G_C - G})^T V
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        f32x4 dec;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dec[i] = __expf(GC[16 * mt + 4 * lg + i]);
+        const f32x4 dec = *reinterpret_cast<const f32x4*>(&gate[16 * mt + 4 * lg]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) S[mt][nt] *= dec;
       }
@@ -651,18 +571,25 @@ hipError_t launch_linear_t(const PrefillArgs& p, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, SM::bytes);
   if (e != hipSuccess) return e;
   const dim3 grid(D / SM::DVS, p.H, p.B);
-  const T* wtb = nullptr;
-  const T* wtbg = nullptr;
-  const float* wg = nullptr;
-  if (!GLA) {
-    const GdnWorkspace w =
-        gdn_workspace_layout(p.workspace, p.B, p.H, gdn_stream_chunks(p.T, p.n_sink, p.window), sizeof(T));
-    wtb = (const T*)w.tb;
-    wtbg = (const T*)w.tbg;
-    wg = w.g;
+  const int nch = gdn_stream_chunks(p.T, p.n_sink, p.window);
+  const T* w0;
+  const T* w1;
+  const T* w2 = nullptr;
+  const float* wf;
+  if (GLA) {
+    const GlaWorkspace w = gla_workspace_layout(p.workspace, p.B, p.H, nch, D, sizeof(T));
+    w0 = (const T*)w.qg;
+    w1 = (const T*)w.ktg;
+    w2 = (const T*)w.a;
+    wf = w.egc;
+  } else {
+    const GdnWorkspace w = gdn_workspace_layout(p.workspace, p.B, p.H, nch, sizeof(T));
+    w0 = (const T*)w.tb;
+    w1 = (const T*)w.tbg;
+    wf = w.g;
   }
   hipLaunchKernelGGL(kern, grid, dim3(64 * NW), SM::bytes, s, (const T*)p.q, (const T*)p.k,
-                     (const T*)p.v, p.a, wtb, wtbg, wg, (T*)p.o, p.state_out, p.T, p.H, p.Hkv,
+                     (const T*)p.v, w0, w1, w2, wf, (T*)p.o, p.state_out, p.T, p.H, p.Hkv,
                      p.n_sink, p.window, p.flags);
   return hipGetLastError();
 }
@@ -688,12 +615,10 @@ size_t linear_lds_bytes(int D, int bf16, int gla) {
 }
 
 hipError_t launch_linear_prefill(const PrefillArgs& p, hipStream_t s) {
-  if (!p.gla) {
-    const int nch = gdn_stream_chunks(p.T, p.n_sink, p.window);
-    if (nch > 0) {
-      const hipError_t e = launch_gdn_prep(p, nch, s);
-      if (e != hipSuccess) return e;
-    }
+  const int nch = gdn_stream_chunks(p.T, p.n_sink, p.window);
+  if (nch > 0) {
+    const hipError_t e = p.gla ? launch_gla_prep(p, nch, s) : launch_gdn_prep(p, nch, s);
+    if (e != hipSuccess) return e;
   }
   if (p.bf16) return p.gla ? launch_linear_d<bf16, true>(p, s) : launch_linear_d<bf16, false>(p, s);
   if (p.D != 64) return hipErrorInvalidValue;   // fp32 state tiles fit LDS only at d = 64

@@ -70,7 +70,8 @@ def test_workspace_query(lib):
     assert ws(lib, 2, 300, 4, 2, 64, 64, 8, 56, F32, DELTA, 5) == (OK, 2 * 4 * 4 * (2 * 4096 * 4 + 512))
     assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 4)[1] > 0          # state only
     assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 2) == (OK, 0)     # softmax only
-    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, GLA, 3) == (OK, 0)       # GLA: none
+    # GLA: Q 2^G [64][d], (K 2^{G_C-G})^T [d][64], A [64][64] and 2^{G_C} [d] fp32
+    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, GLA, 3) == (OK, 32 * nch * (2 * 64 * 128 * 2 + 64 * 64 * 2 + 128 * 4))
     assert ws(lib, 1, 64, 32, 8, 128, 128, 8, 56, BF16, DELTA, 3) == (OK, 0)       # T <= budget
     assert ws(lib, 1, 65, 32, 8, 128, 128, 8, 56, BF16, DELTA, 3)[1] > 0
     assert ws(lib, 1, 4096, 32, 7, 128, 128, 8, 56, BF16, DELTA, 3)[0] == EINVAL   # H % Hkv
@@ -125,8 +126,9 @@ def test_prefill_workspace_checks(lib):
     assert lib.gdn_hybrid_prefill(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 200, 2, 2, 64, 64,
                                   8, 56, BF16, DELTA, 3, ctypes.c_void_p(FAKE.value + 8), 1 << 30,
                                   None) == EINVAL                                  # misaligned
-    # a GLA call needs none: with q missing it fails on q, not on the workspace
-    assert prefill(lib, T=200, up=GLA, b=None, q=None) == EINVAL
+    assert prefill(lib, T=200, up=GLA, b=None) == EWS
+    # a softmax-only call needs none: with q missing it fails on q, not on the workspace
+    assert prefill(lib, T=200, flags=2, q=None) == EINVAL
 
 
 def test_prefill_zero_length_is_a_noop(lib):
