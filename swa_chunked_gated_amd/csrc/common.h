@@ -271,6 +271,25 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// ------------------------------------------------------ workgroup mapping
+
+// Workgroup ids are handed to the 8 XCDs round-robin, so ids id, id + 8,
+// id + 16, ... run on one XCD and share its L2.  For launches over `units`
+// work units of G members each that read common data (the query heads of one
+// KV head), this maps a 1-D id so that the G members of a unit are
+// consecutive on one XCD.  Launch 8 * G * ceil(units / 8) workgroups; ids
+// that map past the last unit return false.
+__device__ __forceinline__ bool xcd_grouped(int id, int G, int units, int& unit, int& member) {
+  const int x = id & 7;
+  const int s = id >> 3;
+  member = s % G;
+  unit = (s / G) * 8 + x;
+  return unit < units;
+}
+__host__ __forceinline__ unsigned xcd_grouped_grid(long long units, int G) {
+  return (unsigned)(8LL * G * ((units + 7) / 8));
+}
+
 // ------------------------------------------------------------ wave helpers
 
 // Wave index inside the workgroup as a scalar (wave-uniform) value, so that

@@ -73,24 +73,104 @@ __device__ __forceinline__ float wave_prefix_sum(float x, int lane) {
   return x + off;
 }
 
-template <class T, int D>
-__global__ __launch_bounds__(256) void gdn_prep_kernel(
-    const T* __restrict__ k, const float* __restrict__ a, const float* __restrict__ b,
-    T* __restrict__ wtb, T* __restrict__ wtbg, float* __restrict__ wg, int T_, int H, int Hkv,
+// (I + L)^-1 in place for the strictly lower 64 x 64 L in Lf (fp32, unit
+// diagonal implied): 16x16 diagonal blocks by forward substitution, then the
+// off-diagonal blocks by block recursion on fp32 MFMA.  Needs >= 4 waves;
+// every wave of the workgroup must call it (it contains barriers).
+__device__ __forceinline__ void unit_lower_inverse(float* Lf, int wv, int lane) {
+  const int l16 = lane & 15;
+  const int lg = lane >> 4;
+  if (wv == 0) {
+    // lane (block, column j): column j of the block's inverse by column-
+    // oriented substitution: once x_s is final it is subtracted from every
+    // later row, so the dependent chain is 16 steps long
+    const int blk = lane >> 4;
+    const int j = l16;
+    float* Lb = Lf + 16 * blk * kSL + 16 * blk;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = r == j ? 1.f : 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < 15; ++s2)
+#pragma unroll
+      for (int r = s2 + 1; r < 16; ++r) x[r] -= Lb[r * kSL + s2] * x[s2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Lb[r * kSL + j] = x[r];
+  }
+  __syncthreads();
+  // level 1: X10 = -X11 L10 X00, X32 = -X33 L32 X22
+  if (wv < 2) {
+    const int o0 = wv == 0 ? 0 : 32;
+    const float* L10 = Lf + (o0 + 16) * kSL + o0;
+    const float* X00 = Lf + o0 * kSL + o0;
+    const float* X11 = Lf + (o0 + 16) * kSL + o0 + 16;
+    f32x4 y = mm16(L10, X00, zero4(), l16, lg);
+    f32x4 xo = -mm16_acc(X11, y, zero4(), l16, lg);
+    st16(Lf + (o0 + 16) * kSL + o0, xo, l16, lg);
+  }
+  __syncthreads();
+  // level 2: bottom-left 32x32 block = -X_BR (L_BL X_TL), one wave per 16x16 block
+  const bool act = wv < 4;
+  const int br = 32 + 16 * ((wv >> 1) & 1);
+  const int bc = 16 * (wv & 1);
+  f32x4 y = zero4();
+  if (act)
+    for (int kb = bc; kb < 32; kb += 16) y = mm16(Lf + br * kSL + kb, Lf + kb * kSL + bc, y, l16, lg);
+  __syncthreads();
+  if (act) st16(Lf + br * kSL + bc, y, l16, lg);
+  __syncthreads();
+  f32x4 xo = zero4();
+  if (act)
+    for (int kb = 32; kb <= br; kb += 16) xo = mm16(Lf + br * kSL + kb, Lf + kb * kSL + bc, xo, l16, lg);
+  __syncthreads();
+  if (act) st16(Lf + br * kSL + bc, -xo, l16, lg);
+  __syncthreads();
+}
+
+template <class T, int D, bool FULL>
+struct PrepSmem {
+  static constexpr int PAD = 16 / sizeof(T);
+  static constexpr int SK = D + PAD;        // [64][D] rows
+  static constexpr int SC = kC + PAD;       // [*][64] rows
+  static constexpr int oK = 0;                              // K rows (natural order)
+  static constexpr int oQ = oK + kC * SK;                   // Q rows (full)
+  static constexpr int oKT = oQ + (FULL ? kC * SK : 0);     // K^T, tokens in acc order (full)
+  static constexpr int oTBG = oKT + (FULL ? D * SC : 0);    // Tm diag(b gamma) (full)
+  static constexpr int oA = oTBG + (FULL ? kC * SC : 0);    // scores (full)
+  static constexpr int nT = oA + (FULL ? kC * SC : 0);
+  static constexpr int bytesT = (nT * (int)sizeof(T) + 15) / 16 * 16;
+  static constexpr int nL = kC * kSL;                       // solve buffer; -Wm staging (full)
+  static_assert(!FULL || kC * SK * (int)sizeof(T) <= nL * 4, "Wm staging fits the solve buffer");
+  static constexpr int bytes = bytesT + 4 * (nL + 4 * kC);  // + g, gamma, b, KTg factors
+};
+
+template <class T, int D, int NW, bool FULL>
+__global__ __launch_bounds__(64 * NW) void gdn_prep_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ a,
+    const float* __restrict__ b, T* __restrict__ wtb, T* __restrict__ wtbg, T* __restrict__ wwm,
+    T* __restrict__ wktg, T* __restrict__ wa, float* __restrict__ wg, int T_, int H, int Hkv,
     int n_sink, int window, int nch) {
-  constexpr int NTH = 256;
+  using SM = PrepSmem<T, D, FULL>;
+  constexpr int NTH = 64 * NW;
   constexpr int EPC = 16 / (int)sizeof(T);     // elements per 16-byte chunk
-  constexpr int SK = D + EPC;                  // Ks row stride (one chunk of padding)
-  constexpr int CH = D / EPC;                  // chunks per K row
-  constexpr int NPK = kC * CH / NTH;
-  static_assert(kC * CH % NTH == 0, "K staging");
+  constexpr int SK = SM::SK;
+  constexpr int SC = SM::SC;
+  constexpr int CH = D / EPC;                  // chunks per row
   typedef typename Vec16<T>::type V16;
 
-  __shared__ __attribute__((aligned(16))) T Ks[kC * SK];
-  __shared__ __attribute__((aligned(16))) float Lf[kC * kSL];
-  __shared__ __attribute__((aligned(16))) float lgs[kC];
-  __shared__ __attribute__((aligned(16))) float gam[kC];
-  __shared__ __attribute__((aligned(16))) float bet[kC];
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  T* sT = reinterpret_cast<T*>(smem_raw);
+  T* Ks = sT + SM::oK;
+  T* Qs = sT + SM::oQ;
+  T* KTs = sT + SM::oKT;
+  T* TBGs = sT + SM::oTBG;
+  T* As = sT + SM::oA;
+  float* Lf = reinterpret_cast<float*>(smem_raw + SM::bytesT);
+  float* lgs = Lf + SM::nL;
+  float* gam = lgs + kC;
+  float* bet = gam + kC;
+  float* fac = bet + kC;                       // 2^{g_C - g} in acc position order
+  T* Wms = reinterpret_cast<T*>(Lf);           // -Wm staging once Tm is consumed (full)
 
   const int c = blockIdx.x;
   const int h = blockIdx.y;
@@ -104,22 +184,50 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
   const int iend = T_ - window;                // stream tokens are [n_sink, iend)
   const int i0 = n_sink + c * kC;
   const size_t ci = ((size_t)bi * H + h) * nch + c;
+  const T* kbase = k + ((size_t)(bi * T_ + i0) * Hkv + g) * D;
+  const T* qbase = q + ((size_t)(bi * T_ + i0 + window) * H + h) * D;
+  V16 zero;
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) zero[e] = from_f32<T>(0.f);
 
-  // K rows of the chunk (zero past the stream end), natural column order:
-  // K K^T reads both operands from the same rows, so any order is consistent
+  if constexpr (FULL) {
+    // K as pieces of EPC tokens (one acc-order position group) x EPC dims:
+    // rows to Ks, and transposed in registers to K^T rows of EPC positions
+    constexpr int NPC = (kC / EPC) * CH;
+    for (int pc = tid; pc < NPC; pc += NTH) {
+      const int pg = pc % (kC / EPC);
+      const int cb = (pc / (kC / EPC)) * EPC;
+      V16 x[EPC];
 #pragma unroll
-  for (int j = 0; j < NPK; ++j) {
-    const int idx = tid + j * NTH;
-    const int r = idx / CH;
-    const int cc = (idx % CH) * EPC;
-    V16 x;
-    if (i0 + r < iend) {
-      x = *reinterpret_cast<const V16*>(k + ((size_t)(bi * T_ + i0 + r) * Hkv + g) * D + cc);
-    } else {
+      for (int i = 0; i < EPC; ++i) {
+        const int r = acc_idx(EPC * pg + i);
+        x[i] = i0 + r < iend ? *reinterpret_cast<const V16*>(kbase + (size_t)r * Hkv * D + cb) : zero;
+      }
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) x[e] = from_f32<T>(0.f);
+      for (int i = 0; i < EPC; ++i) *reinterpret_cast<V16*>(&Ks[acc_idx(EPC * pg + i) * SK + cb]) = x[i];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        V16 y;
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) y[i] = x[i][e];
+        *reinterpret_cast<V16*>(&KTs[(cb + e) * SC + EPC * pg]) = y;
+      }
     }
-    *reinterpret_cast<V16*>(&Ks[r * SK + cc]) = x;
+    for (int idx = tid; idx < kC * CH; idx += NTH) {
+      const int r = idx / CH;
+      const int cb = (idx % CH) * EPC;
+      *reinterpret_cast<V16*>(&Qs[r * SK + cb]) =
+          i0 + r < iend ? *reinterpret_cast<const V16*>(qbase + (size_t)r * H * D + cb) : zero;
+    }
+  } else {
+    // K rows of the chunk (zero past the stream end), natural column order:
+    // K K^T reads both operands from the same rows, so any order is consistent
+    for (int idx = tid; idx < kC * CH; idx += NTH) {
+      const int r = idx / CH;
+      const int cb = (idx % CH) * EPC;
+      *reinterpret_cast<V16*>(&Ks[r * SK + cb]) =
+          i0 + r < iend ? *reinterpret_cast<const V16*>(kbase + (size_t)r * Hkv * D + cb) : zero;
+    }
   }
   for (int i = tid; i < kC * kSL; i += NTH) Lf[i] = 0.f;
   // gates: g = inclusive cumsum of log2 a (a = 1 past the stream end), b
@@ -135,19 +243,22 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
   }
   __syncthreads();
 
-  // ---- L = strictly lower (b_r 2^{g_r - g_s} k_r.k_s) on the 10 lower tiles
-  for (int job = wv; job < 10; job += 4) {
-    const int mt = kPrepTileM[job];
-    const int nt = kPrepTileN[job];
+  // ---- L = strictly lower (b_r 2^{g_r - g_s} k_r.k_s) on the 10 lower tiles;
+  // full: also A = [s <= r] 2^{g_r - g_s} q_r.k_s
+  for (int job = wv; job < (FULL ? 20 : 10); job += NW) {
+    const bool isq = job >= 10;
+    const int mt = kPrepTileM[isq ? job - 10 : job];
+    const int nt = kPrepTileN[isq ? job - 10 : job];
     const int r0 = 16 * mt + 4 * lg;
     const int s = 16 * nt + l16;
     const f32x4 lr = *reinterpret_cast<const f32x4*>(&lgs[r0]);
     const f32x4 br = *reinterpret_cast<const f32x4*>(&bet[r0]);
     const float ls = lgs[s];
+    const T* X = isq ? Qs : Ks;
     Frag<T> xa[D / 32], xb[D / 32];
 #pragma unroll
     for (int p = 0; p < D / 32; ++p) {
-      xa[p] = lds_frag8(&Ks[(16 * mt + l16) * SK + 32 * p + 8 * lg]);
+      xa[p] = lds_frag8(&X[(16 * mt + l16) * SK + 32 * p + 8 * lg]);
       xb[p] = lds_frag8(&Ks[(16 * nt + l16) * SK + 32 * p + 8 * lg]);
     }
     f32x4 acc = zero4();
@@ -157,57 +268,27 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
     for (int i = 0; i < 4; ++i) {
       const int r = r0 + i;
       const float dec = __builtin_amdgcn_exp2f(fminf(lr[i] - ls, 0.f));
-      Lf[r * kSL + s] = s < r ? br[i] * dec * acc[i] : 0.f;
+      if (isq) As[r * SC + acc_pos(s)] = from_f32<T>(s <= r ? dec * acc[i] : 0.f);
+      else Lf[r * kSL + s] = s < r ? br[i] * dec * acc[i] : 0.f;
     }
   }
-  __syncthreads();
-  // ---- diagonal 16x16 blocks of (I + L)^-1 by forward substitution
-  if (wv == 0) {
-    const int blk = lane >> 4;
-    const int j = l16;
-    float* Lb = Lf + 16 * blk * kSL + 16 * blk;
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float acc = r == j ? 1.f : 0.f;
-#pragma unroll
-      for (int s2 = 0; s2 < r; ++s2) acc -= Lb[r * kSL + s2] * x[s2];
-      x[r] = acc;
+  if (FULL) {
+    // the strictly upper tiles of A are zero
+    for (int i = tid; i < 6 * 256; i += NTH) {
+      const int pr = i / 256;
+      const int e = i % 256;
+      const int mt = pr < 3 ? 0 : (pr < 5 ? 1 : 2);
+      const int nt = pr < 3 ? pr + 1 : (pr < 5 ? pr - 1 : 3);
+      As[(16 * mt + e / 16) * SC + acc_pos(16 * nt + e % 16)] = from_f32<T>(0.f);
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) Lb[r * kSL + j] = x[r];
+    if (tid < kC) fac[tid] = __builtin_amdgcn_exp2f(fminf(lgs[kC - 1] - lgs[acc_idx(tid)], 0.f));
   }
   __syncthreads();
-  // ---- level 1: X10 = -X11 L10 X00, X32 = -X33 L32 X22
-  if (wv < 2) {
-    const int o0 = wv == 0 ? 0 : 32;
-    const float* L10 = Lf + (o0 + 16) * kSL + o0;
-    const float* X00 = Lf + o0 * kSL + o0;
-    const float* X11 = Lf + (o0 + 16) * kSL + o0 + 16;
-    f32x4 y = mm16(L10, X00, zero4(), l16, lg);
-    f32x4 xo = -mm16_acc(X11, y, zero4(), l16, lg);
-    st16(Lf + (o0 + 16) * kSL + o0, xo, l16, lg);
-  }
-  __syncthreads();
-  // ---- level 2: bottom-left 32x32 block = -X_BR (L_BL X_TL), one wave per 16x16 block
-  {
-    const int br = 32 + 16 * ((wv >> 1) & 1);   // block row
-    const int bc = 16 * (wv & 1);               // block column
-    f32x4 y = zero4();
-    for (int kb = bc; kb < 32; kb += 16) y = mm16(Lf + br * kSL + kb, Lf + kb * kSL + bc, y, l16, lg);
-    __syncthreads();
-    st16(Lf + br * kSL + bc, y, l16, lg);
-    __syncthreads();
-    f32x4 xo = zero4();
-    for (int kb = 32; kb <= br; kb += 16) xo = mm16(Lf + br * kSL + kb, Lf + kb * kSL + bc, xo, l16, lg);
-    __syncthreads();
-    st16(Lf + br * kSL + bc, -xo, l16, lg);
-    __syncthreads();
-  }
-  // ---- TB = Tm diag(b), TBG = Tm diag(b gamma): row r, columns s0..s0+3 at
-  // positions acc_pos(s0)..+3 of the row
+  unit_lower_inverse(Lf, wv, lane);
+
+  // ---- TB = Tm diag(b) (and TBG = Tm diag(b gamma)): row r, columns
+  // s0..s0+3 at positions acc_pos(s0)..+3 of the row
   T* tb = wtb + ci * (kC * kC);
-  T* tbg = wtbg + ci * (kC * kC);
   for (int i = tid; i < kC * kC / 4; i += NTH) {
     const int r = i >> 4;
     const int s0 = (i & 15) * 4;
@@ -216,36 +297,111 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
     const f32x4 gg = *reinterpret_cast<const f32x4*>(&gam[s0]);
     const f32x4 x = tm * bb;
     store4(tb + r * kC + acc_pos(s0), x);
-    store4(tbg + r * kC + acc_pos(s0), x * gg);
+    if (FULL) store4(&TBGs[r * SC + acc_pos(s0)], x * gg);
+    else store4(wtbg + ci * (kC * kC) + r * kC + acc_pos(s0), x * gg);
   }
   if (tid < 64) wg[ci * (2 * kC) + tid] = lgs[tid];
   else if (tid < 128) wg[ci * (2 * kC) + tid] = gam[tid - 64];
+  if constexpr (FULL) {
+    __syncthreads();
+    // ---- -Wm = -(TBG K): per 16-row dk tile, Wm^T = K^T TBG^T on MFMA,
+    // staged in the (now free) solve buffer as [token][dk in acc order]
+    constexpr int MT = D / 16;
+    for (int mt = wv; mt < MT; mt += NW) {
+      Frag<T> kf[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) kf[p] = lds_frag8(&KTs[(16 * mt + l16) * SC + 32 * p + 8 * lg]);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int p = 0; p < 2; ++p) acc = mfma(kf[p], lds_frag8(&TBGs[(16 * nt + l16) * SC + 32 * p + 8 * lg]), acc);
+        store4(&Wms[(16 * nt + l16) * SK + acc_pos(16 * mt + 4 * lg)], -acc);
+      }
+    }
+    __syncthreads();
+    // ---- copy out: -Wm [64][D], K^T 2^{g_C - g} [D][64], A [64][64]
+    T* wm = wwm + ci * (kC * D);
+    T* ktg = wktg + ci * (D * kC);
+    T* aa = wa + ci * (kC * kC);
+    for (int i = tid; i < kC * CH; i += NTH) {
+      const int r = i / CH;
+      const int pc = (i % CH) * EPC;
+      *reinterpret_cast<V16*>(wm + r * D + pc) = *reinterpret_cast<const V16*>(&Wms[r * SK + pc]);
+    }
+    for (int i = tid; i < D * (kC / EPC); i += NTH) {
+      const int r = i / (kC / EPC);
+      const int pc = (i % (kC / EPC)) * EPC;
+      const V16 x = *reinterpret_cast<const V16*>(&KTs[r * SC + pc]);
+      V16 y;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) y[e] = from_f32<T>(to_f32(x[e]) * fac[pc + e]);
+      *reinterpret_cast<V16*>(ktg + r * kC + pc) = y;
+    }
+    for (int i = tid; i < kC * (kC / EPC); i += NTH) {
+      const int r = i / (kC / EPC);
+      const int pc = (i % (kC / EPC)) * EPC;
+      *reinterpret_cast<V16*>(aa + r * kC + pc) = *reinterpret_cast<const V16*>(&As[r * SC + pc]);
+    }
+  }
+}
+
+template <class T, int D, bool FULL>
+hipError_t launch_prep_t(const PrefillArgs& p, int nch, hipStream_t s) {
+  using SM = PrepSmem<T, D, FULL>;
+  constexpr int NW = FULL ? 8 : 4;
+  auto kern = gdn_prep_kernel<T, D, NW, FULL>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, SM::bytes);
+  if (e != hipSuccess) return e;
+  const GdnWorkspace w = gdn_workspace_layout(p.workspace, p.B, p.H, nch, D, sizeof(T), FULL);
+  hipLaunchKernelGGL(kern, dim3(nch, p.H, p.B), dim3(64 * NW), SM::bytes, s, (const T*)p.q,
+                     (const T*)p.k, p.a, p.b, (T*)w.tb, (T*)w.tbg, (T*)w.wm, (T*)w.ktg, (T*)w.a, w.g,
+                     p.T, p.H, p.Hkv, p.n_sink, p.window, nch);
+  return hipGetLastError();
 }
 
 template <class T, int D>
-hipError_t launch_prep_t(const PrefillArgs& p, int nch, hipStream_t s) {
-  const GdnWorkspace w = gdn_workspace_layout(p.workspace, p.B, p.H, nch, sizeof(T));
-  hipLaunchKernelGGL((gdn_prep_kernel<T, D>), dim3(nch, p.H, p.B), dim3(256), 0, s, (const T*)p.k,
-                     p.a, p.b, (T*)w.tb, (T*)w.tbg, w.g, p.T, p.H, p.Hkv, p.n_sink, p.window, nch);
-  return hipGetLastError();
+hipError_t launch_prep_d(const PrefillArgs& p, int nch, hipStream_t s) {
+  if constexpr (sizeof(T) == 4 && D == 128) {
+    return hipErrorInvalidValue;   // fp32 linear branch runs at d = 64 only
+  } else {
+    return gdn_full_prep(p.B, p.H, p.D) ? launch_prep_t<T, D, true>(p, nch, s)
+                                        : launch_prep_t<T, D, false>(p, nch, s);
+  }
 }
 
 }  // namespace
 
-GdnWorkspace gdn_workspace_layout(void* base, int B, int H, int nch, size_t elt) {
+bool gdn_full_prep(int B, int H, int D) {
+  // the scan fills fewer workgroups than the GPU has compute units: every
+  // state-independent product comes from the preparation kernel
+  return (long long)B * H * (D == 128 ? 2 : 1) < 256;
+}
+
+GdnWorkspace gdn_workspace_layout(void* base, int B, int H, int nch, int D, size_t elt, bool full) {
   GdnWorkspace w;
   const size_t n = (size_t)B * H * nch;
   unsigned char* p = static_cast<unsigned char*>(base);
-  w.tb = p;
-  w.tbg = p + n * kC * kC * elt;
-  w.g = reinterpret_cast<float*>(p + 2 * n * kC * kC * elt);
-  w.bytes = 2 * n * kC * kC * elt + n * 2 * kC * sizeof(float);
+  size_t off = 0;
+  w.tb = p + off;
+  off += n * kC * kC * elt;
+  w.tbg = full ? nullptr : p + off;
+  off += full ? 0 : n * kC * kC * elt;
+  w.wm = full ? p + off : nullptr;
+  off += full ? n * kC * D * elt : 0;
+  w.ktg = full ? p + off : nullptr;
+  off += full ? n * D * kC * elt : 0;
+  w.a = full ? p + off : nullptr;
+  off += full ? n * kC * kC * elt : 0;
+  w.g = reinterpret_cast<float*>(p + off);
+  off += n * 2 * kC * sizeof(float);
+  w.bytes = off;
   return w;
 }
 
 hipError_t launch_gdn_prep(const PrefillArgs& p, int nch, hipStream_t s) {
-  if (p.bf16) return p.D == 64 ? launch_prep_t<bf16, 64>(p, nch, s) : launch_prep_t<bf16, 128>(p, nch, s);
-  return p.D == 64 ? launch_prep_t<float, 64>(p, nch, s) : launch_prep_t<float, 128>(p, nch, s);
+  if (p.bf16) return p.D == 64 ? launch_prep_d<bf16, 64>(p, nch, s) : launch_prep_d<bf16, 128>(p, nch, s);
+  return p.D == 64 ? launch_prep_d<float, 64>(p, nch, s) : launch_prep_d<float, 128>(p, nch, s);
 }
 
 }  // namespace gdn

@@ -54,7 +54,7 @@ template <class T, int D>
 __global__ __launch_bounds__(512) void gla_prep_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ a,
     T* __restrict__ wqg, T* __restrict__ wktg, T* __restrict__ wa, float* __restrict__ wegc,
-    int T_, int H, int Hkv, int n_sink, int window, int nch) {
+    int B_, int T_, int H, int Hkv, int n_sink, int window, int nch) {
   using SM = GlaPrepSmem<T, D>;
   constexpr int NTH = 512;
   constexpr int SK = SM::SK;
@@ -71,10 +71,14 @@ __global__ __launch_bounds__(512) void gla_prep_kernel(
   float* Gl = reinterpret_cast<float*>(smem_raw + SM::bytesT);   // [64][D]
   float* Mf = Gl + SM::nG;                                        // [6][D], acc order
 
-  const int c = blockIdx.x;
-  const int h = blockIdx.y;
-  const int bi = blockIdx.z;
-  const int g = h / (H / Hkv);
+  // the query heads of one KV head run back to back on one XCD (shared K)
+  const int G = H / Hkv;
+  int unit, member;
+  if (!xcd_grouped(blockIdx.x, G, B_ * Hkv * nch, unit, member)) return;
+  const int c = unit % nch;
+  const int g = (unit / nch) % Hkv;
+  const int bi = unit / (nch * Hkv);
+  const int h = g * G + member;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = wave_id();
@@ -260,8 +264,8 @@ hipError_t launch_gla_prep_t(const PrefillArgs& p, int nch, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, SM::bytes);
   if (e != hipSuccess) return e;
   const GlaWorkspace w = gla_workspace_layout(p.workspace, p.B, p.H, nch, D, sizeof(T));
-  hipLaunchKernelGGL(kern, dim3(nch, p.H, p.B), dim3(512), SM::bytes, s, (const T*)p.q,
-                     (const T*)p.k, p.a, (T*)w.qg, (T*)w.ktg, (T*)w.a, w.egc, p.T, p.H, p.Hkv,
+  hipLaunchKernelGGL(kern, dim3(xcd_grouped_grid((long long)p.B * p.Hkv * nch, p.H / p.Hkv)), dim3(512), SM::bytes, s, (const T*)p.q,
+                     (const T*)p.k, p.a, (T*)w.qg, (T*)w.ktg, (T*)w.a, w.egc, p.B, p.T, p.H, p.Hkv,
                      p.n_sink, p.window, nch);
   return hipGetLastError();
 }

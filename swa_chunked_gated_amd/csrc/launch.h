@@ -23,16 +23,25 @@ struct PrefillArgs {
   void* workspace;   // chunk preparation results (gated delta rule), see GdnWorkspace
 };
 
-// Workspace of the gated delta rule prefill: for each (sequence, head, chunk)
-// TB and TBG (64 x 64 elements of the I/O type, rows with columns in acc
-// order) and g, gamma (2 x 64 fp32), as three consecutive arrays.
+// Workspace of the gated delta rule prefill, per (sequence, head, chunk), as
+// consecutive arrays (I/O element type, reduction index in acc order):
+//   TB = Tm diag(b) [64][64]; then either (light preparation) TBG =
+//   Tm diag(b gamma) [64][64], or (full preparation) -Wm [64][D],
+//   K^T 2^{g_C - g} [D][64] and the scores A [64][64]; then g, gamma
+//   [2][64] fp32.
 struct GdnWorkspace {
   void* tb;
   void* tbg;
+  void* wm;
+  void* ktg;
+  void* a;
   float* g;
   size_t bytes;
 };
-GdnWorkspace gdn_workspace_layout(void* base, int B, int H, int nch, size_t elt);
+// Full preparation (everything state-independent precomputed) when the scan
+// alone cannot fill the GPU.
+bool gdn_full_prep(int B, int H, int D);
+GdnWorkspace gdn_workspace_layout(void* base, int B, int H, int nch, int D, size_t elt, bool full);
 // Workspace of the GLA prefill: for each (sequence, head, chunk) Q 2^G
 // [64][D], (K 2^{G_C - G})^T [D][64], A [64][64] (I/O type, reduction index in
 // acc order) and 2^{G_C} [D] fp32, as four consecutive arrays.

@@ -63,11 +63,20 @@ def ws(lib, *args):
 
 
 def test_workspace_query(lib):
-    # gated delta rule: per (sequence, head, 64-token chunk of the linear
-    # stream) two 64x64 tiles of the I/O type and 128 fp32 gate values
+    # gated delta rule, per (sequence, head, 64-token chunk of the linear
+    # stream): with few chains (B*H*(d/64) < 256) the full preparation,
+    # Tm diag(b), -Wm, K^T 2^{g_C-g} and A; else Tm diag(b), Tm diag(b gamma);
+    # plus 128 fp32 gate values
+    def gdn_bytes(B, T, H, d, elt, n=64):
+        nch = -(-(T - n) // 64)
+        full = B * H * (2 if d == 128 else 1) < 256
+        tiles = (64 * 64 + 64 * d + d * 64 + 64 * 64) if full else 2 * 64 * 64
+        return B * H * nch * (tiles * elt + 512)
+    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 3) == (OK, gdn_bytes(1, 4096, 32, 128, 2))
+    assert gdn_bytes(1, 4096, 32, 128, 2) == 2016 * 49664
+    assert ws(lib, 2, 300, 4, 2, 64, 64, 8, 56, F32, DELTA, 5) == (OK, gdn_bytes(2, 300, 4, 64, 4))
+    assert ws(lib, 8, 4096, 32, 8, 128, 128, 8, 120, BF16, DELTA, 5) == (OK, gdn_bytes(8, 4096, 32, 128, 2, 128))
     nch = (4096 - 64 + 63) // 64
-    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 3) == (OK, 32 * nch * (2 * 4096 * 2 + 512))
-    assert ws(lib, 2, 300, 4, 2, 64, 64, 8, 56, F32, DELTA, 5) == (OK, 2 * 4 * 4 * (2 * 4096 * 4 + 512))
     assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 4)[1] > 0          # state only
     assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 2) == (OK, 0)     # softmax only
     # GLA: Q 2^G [64][d], (K 2^{G_C-G})^T [d][64], A [64][64] and 2^{G_C} [d] fp32
