@@ -130,7 +130,7 @@ int gdn_hybrid_decode(const void* q, const void* k, const void* v, const float* 
   const int G = H / Hkv;
   if (G > 16) return GDN_EUNSUPPORTED;
   if ((int64_t)G * (n_sink + window) > 12288) return GDN_EUNSUPPORTED;
-  if (gdn::decode_lds_bytes(G, n_sink + window, dk, update == GDN_GLA) > 160 * 1024)
+  if (gdn::decode_lds_bytes(G, n_sink + window, dk, update == GDN_GLA, dtype == GDN_BF16 ? 2 : 4) > 160 * 1024)
     return GDN_EUNSUPPORTED;
   gdn::DecodeArgs p{q, k, v, a, b, state, k_cache, v_cache, a_cache, b_cache, pos, o,
                     B, H, Hkv, dk, n_sink, window, dtype == GDN_BF16, update == GDN_GLA, flags};

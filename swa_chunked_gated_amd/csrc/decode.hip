@@ -416,7 +416,7 @@ __global__ __launch_bounds__(256) void cache_fill_kernel(
 template <class T, bool GLA, int D>
 hipError_t launch_decode_t(const DecodeArgs& p, hipStream_t s) {
   const int G = p.H / p.Hkv;
-  const size_t lds = decode_lds_bytes(G, p.n_sink + p.window, D, GLA);
+  const size_t lds = decode_lds_bytes(G, p.n_sink + p.window, D, GLA, (int)sizeof(T));
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)decode_kernel<T, GLA, D>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -442,12 +442,12 @@ hipError_t launch_decode_d(const DecodeArgs& p, hipStream_t s) {
 
 }  // namespace
 
-size_t decode_lds_bytes(int G, int N, int D, int gla) {
+size_t decode_lds_bytes(int G, int N, int D, int gla, int elt) {
   (void)G;
   (void)gla;
   const size_t floats = 8 * (size_t)D + 4 + 4 * (size_t)(D / 4) * 8 + (size_t)N;
   const size_t ints = (size_t)N;
-  const size_t staging = (size_t)kSlotChunk * (D + 8) * sizeof(float);   // fp32 worst case
+  const size_t staging = (size_t)kSlotChunk * (D + 16 / elt) * elt;   // cache rows of the I/O type
   return floats * sizeof(float) + ints * sizeof(int) + 16 + staging;
 }
 

@@ -13,10 +13,10 @@
 // so Tm diag(b) and Tm diag(b gamma) (and g, gamma) are all the scan needs
 // from here.
 //
-// One workgroup of 4 waves per (chunk, query head, sequence).  K K^T on MFMA;
-// the unit lower-triangular inverse as 16x16 diagonal blocks by forward
-// substitution in fp32 plus the off-diagonal blocks by block recursion on
-// fp32 MFMA (16x16x4, exact fp32 products).  Outputs per chunk (workspace,
+// One wave per (chunk, query head, sequence).  K K^T on MFMA; the unit
+// lower-triangular inverse as 16x16 diagonal blocks by forward substitution
+// in fp32 plus the off-diagonal blocks by block recursion on fp32 MFMA
+// (16x16x4, exact fp32 products).  Outputs per chunk (workspace,
 // element type T): TB = Tm diag(b) and TBG = Tm diag(b gamma) as 64 rows of
 // 64, each row's columns stored in acc order (the order the scan's LDS tiles
 // use, so the scan copies them with 16-byte moves), and fp32 g[64], gamma[64].
@@ -29,9 +29,6 @@ namespace {
 
 constexpr int kC = 64;          // chunk length
 constexpr int kSL = 68;         // fp32 stride of the 64x64 solve buffer
-// the 10 lower-triangular 16x16 tiles (row, col) of a 64x64 matrix
-__constant__ const int kPrepTileM[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__constant__ const int kPrepTileN[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -74,16 +71,16 @@ __device__ __forceinline__ float wave_prefix_sum(float x, int lane) {
 }
 
 // (I + L)^-1 in place for the strictly lower 64 x 64 L in Lf (fp32, unit
-// diagonal implied): 16x16 diagonal blocks by forward substitution, then the
-// off-diagonal blocks by block recursion on fp32 MFMA.  Needs >= 4 waves;
-// every wave of the workgroup must call it (it contains barriers).
-__device__ __forceinline__ void unit_lower_inverse(float* Lf, int wv, int lane) {
+// diagonal implied, upper part zero), by one wave: 16x16 diagonal blocks by
+// column-oriented forward substitution (lane = block x column; once x_s is
+// final it is subtracted from every later row, a 16-step dependent chain),
+// then the off-diagonal blocks by block recursion on fp32 MFMA (exact fp32
+// products).  A wave's LDS operations complete in program order; lds_barrier
+// (which for a one-wave workgroup only waits on LDS) marks the phases.
+__device__ __forceinline__ void unit_lower_inverse_wave(float* Lf, int lane) {
   const int l16 = lane & 15;
   const int lg = lane >> 4;
-  if (wv == 0) {
-    // lane (block, column j): column j of the block's inverse by column-
-    // oriented substitution: once x_s is final it is subtracted from every
-    // later row, so the dependent chain is 16 steps long
+  {
     const int blk = lane >> 4;
     const int j = l16;
     float* Lb = Lf + 16 * blk * kSL + 16 * blk;
@@ -97,71 +94,77 @@ __device__ __forceinline__ void unit_lower_inverse(float* Lf, int wv, int lane) 
 #pragma unroll
     for (int r = 0; r < 16; ++r) Lb[r * kSL + j] = x[r];
   }
-  __syncthreads();
+  lds_barrier();
   // level 1: X10 = -X11 L10 X00, X32 = -X33 L32 X22
-  if (wv < 2) {
-    const int o0 = wv == 0 ? 0 : 32;
-    const float* L10 = Lf + (o0 + 16) * kSL + o0;
-    const float* X00 = Lf + o0 * kSL + o0;
-    const float* X11 = Lf + (o0 + 16) * kSL + o0 + 16;
-    f32x4 y = mm16(L10, X00, zero4(), l16, lg);
-    f32x4 xo = -mm16_acc(X11, y, zero4(), l16, lg);
-    st16(Lf + (o0 + 16) * kSL + o0, xo, l16, lg);
+  f32x4 x10[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int o0 = 32 * u;
+    const f32x4 y = mm16(Lf + (o0 + 16) * kSL + o0, Lf + o0 * kSL + o0, zero4(), l16, lg);
+    x10[u] = -mm16_acc(Lf + (o0 + 16) * kSL + o0 + 16, y, zero4(), l16, lg);
   }
-  __syncthreads();
-  // level 2: bottom-left 32x32 block = -X_BR (L_BL X_TL), one wave per 16x16 block
-  const bool act = wv < 4;
-  const int br = 32 + 16 * ((wv >> 1) & 1);
-  const int bc = 16 * (wv & 1);
-  f32x4 y = zero4();
-  if (act)
-    for (int kb = bc; kb < 32; kb += 16) y = mm16(Lf + br * kSL + kb, Lf + kb * kSL + bc, y, l16, lg);
-  __syncthreads();
-  if (act) st16(Lf + br * kSL + bc, y, l16, lg);
-  __syncthreads();
-  f32x4 xo = zero4();
-  if (act)
-    for (int kb = 32; kb <= br; kb += 16) xo = mm16(Lf + br * kSL + kb, Lf + kb * kSL + bc, xo, l16, lg);
-  __syncthreads();
-  if (act) st16(Lf + br * kSL + bc, -xo, l16, lg);
-  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) st16(Lf + (32 * u + 16) * kSL + 32 * u, x10[u], l16, lg);
+  lds_barrier();
+  // level 2: bottom-left 32x32 block = -X_BR (L_BL X_TL); every product is
+  // read before any of the four 16x16 blocks is overwritten
+  f32x4 y[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int br = 32 + 16 * (u >> 1);
+    const int bc = 16 * (u & 1);
+    y[u] = zero4();
+    for (int kb = bc; kb < 32; kb += 16) y[u] = mm16(Lf + br * kSL + kb, Lf + kb * kSL + bc, y[u], l16, lg);
+  }
+  lds_barrier();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) st16(Lf + (32 + 16 * (u >> 1)) * kSL + 16 * (u & 1), y[u], l16, lg);
+  lds_barrier();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int br = 32 + 16 * (u >> 1);
+    const int bc = 16 * (u & 1);
+    y[u] = zero4();
+    for (int kb = 32; kb <= br; kb += 16) y[u] = mm16(Lf + br * kSL + kb, Lf + kb * kSL + bc, y[u], l16, lg);
+  }
+  lds_barrier();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) st16(Lf + (32 + 16 * (u >> 1)) * kSL + 16 * (u & 1), -y[u], l16, lg);
+  lds_barrier();
 }
 
 template <class T, int D, bool FULL>
 struct PrepSmem {
   static constexpr int PAD = 16 / sizeof(T);
-  static constexpr int SK = D + PAD;        // [64][D] rows
   static constexpr int SC = kC + PAD;       // [*][64] rows
-  static constexpr int oK = 0;                              // K rows (natural order)
-  static constexpr int oQ = oK + kC * SK;                   // Q rows (full)
-  static constexpr int oKT = oQ + (FULL ? kC * SK : 0);     // K^T, tokens in acc order (full)
-  static constexpr int oTBG = oKT + (FULL ? D * SC : 0);    // Tm diag(b gamma) (full)
-  static constexpr int oA = oTBG + (FULL ? kC * SC : 0);    // scores (full)
+  static constexpr int oKT = 0;                             // K^T, tokens in acc order
+  static constexpr int oTBG = oKT + (FULL ? D * SC : 0);    // Tm diag(b gamma)
+  static constexpr int oA = oTBG + (FULL ? kC * SC : 0);    // scores
   static constexpr int nT = oA + (FULL ? kC * SC : 0);
   static constexpr int bytesT = (nT * (int)sizeof(T) + 15) / 16 * 16;
-  static constexpr int nL = kC * kSL;                       // solve buffer; -Wm staging (full)
-  static_assert(!FULL || kC * SK * (int)sizeof(T) <= nL * 4, "Wm staging fits the solve buffer");
-  static constexpr int bytes = bytesT + 4 * (nL + 4 * kC);  // + g, gamma, b, KTg factors
+  static constexpr int nL = kC * kSL;                       // solve buffer
+  static constexpr int bytes = bytesT + 4 * (nL + 4 * kC);  // + g, gamma, b, K^T factors
 };
 
-template <class T, int D, int NW, bool FULL>
-__global__ __launch_bounds__(64 * NW) void gdn_prep_kernel(
+// One wave per (chunk, query head, sequence): every operand fragment of
+// K K^T (and Q K^T) is loaded straight from global memory into registers, so
+// the only LDS a chunk needs is the 64 x 64 fp32 solve buffer (plus, for the
+// full preparation, K^T, TBG and A staging), and many chunks run per CU.
+template <class T, int D, bool FULL>
+__global__ __launch_bounds__(64) void gdn_prep_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ a,
     const float* __restrict__ b, T* __restrict__ wtb, T* __restrict__ wtbg, T* __restrict__ wwm,
     T* __restrict__ wktg, T* __restrict__ wa, float* __restrict__ wg, int T_, int H, int Hkv,
     int n_sink, int window, int nch) {
   using SM = PrepSmem<T, D, FULL>;
-  constexpr int NTH = 64 * NW;
-  constexpr int EPC = 16 / (int)sizeof(T);     // elements per 16-byte chunk
-  constexpr int SK = SM::SK;
+  constexpr int EPC = 16 / (int)sizeof(T);     // elements per 16-byte piece
+  constexpr int QV = 8 / EPC;                  // 16-byte pieces per fragment
+  constexpr int KS = D / 32;                   // 32-wide k-steps over d
   constexpr int SC = SM::SC;
-  constexpr int CH = D / EPC;                  // chunks per row
   typedef typename Vec16<T>::type V16;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   T* sT = reinterpret_cast<T*>(smem_raw);
-  T* Ks = sT + SM::oK;
-  T* Qs = sT + SM::oQ;
   T* KTs = sT + SM::oKT;
   T* TBGs = sT + SM::oTBG;
   T* As = sT + SM::oA;
@@ -170,15 +173,12 @@ __global__ __launch_bounds__(64 * NW) void gdn_prep_kernel(
   float* gam = lgs + kC;
   float* bet = gam + kC;
   float* fac = bet + kC;                       // 2^{g_C - g} in acc position order
-  T* Wms = reinterpret_cast<T*>(Lf);           // -Wm staging once Tm is consumed (full)
 
   const int c = blockIdx.x;
   const int h = blockIdx.y;
   const int bi = blockIdx.z;
   const int g = h / (H / Hkv);
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = wave_id();
+  const int lane = threadIdx.x;
   const int l16 = lane & 15;
   const int lg = lane >> 4;
   const int iend = T_ - window;                // stream tokens are [n_sink, iend)
@@ -186,110 +186,105 @@ __global__ __launch_bounds__(64 * NW) void gdn_prep_kernel(
   const size_t ci = ((size_t)bi * H + h) * nch + c;
   const T* kbase = k + ((size_t)(bi * T_ + i0) * Hkv + g) * D;
   const T* qbase = q + ((size_t)(bi * T_ + i0 + window) * H + h) * D;
-  V16 zero;
-#pragma unroll
-  for (int e = 0; e < EPC; ++e) zero[e] = from_f32<T>(0.f);
 
-  if constexpr (FULL) {
-    // K as pieces of EPC tokens (one acc-order position group) x EPC dims:
-    // rows to Ks, and transposed in registers to K^T rows of EPC positions
-    constexpr int NPC = (kC / EPC) * CH;
-    for (int pc = tid; pc < NPC; pc += NTH) {
-      const int pg = pc % (kC / EPC);
-      const int cb = (pc / (kC / EPC)) * EPC;
-      V16 x[EPC];
+  // ---- operand pieces: lane holds rows 16 mt + l16, dims 32 p + 8 lg .. +7
+  V16 kr[4][KS][QV];
+  V16 qr[FULL ? 4 : 1][FULL ? KS : 1][QV];
 #pragma unroll
-      for (int i = 0; i < EPC; ++i) {
-        const int r = acc_idx(EPC * pg + i);
-        x[i] = i0 + r < iend ? *reinterpret_cast<const V16*>(kbase + (size_t)r * Hkv * D + cb) : zero;
+  for (int mt = 0; mt < 4; ++mt) {
+    const int r = 16 * mt + l16;
+    const bool live = i0 + r < iend;
+#pragma unroll
+    for (int p = 0; p < KS; ++p)
+#pragma unroll
+      for (int u = 0; u < QV; ++u) {
+        const int col = 32 * p + 8 * lg + u * EPC;
+        if (live) {
+          kr[mt][p][u] = *reinterpret_cast<const V16*>(kbase + (size_t)r * Hkv * D + col);
+          if constexpr (FULL) qr[mt][p][u] = *reinterpret_cast<const V16*>(qbase + (size_t)r * H * D + col);
+        } else {
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) {
+            kr[mt][p][u][e] = from_f32<T>(0.f);
+            if constexpr (FULL) qr[mt][p][u][e] = from_f32<T>(0.f);
+          }
+        }
       }
-#pragma unroll
-      for (int i = 0; i < EPC; ++i) *reinterpret_cast<V16*>(&Ks[acc_idx(EPC * pg + i) * SK + cb]) = x[i];
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) {
-        V16 y;
-#pragma unroll
-        for (int i = 0; i < EPC; ++i) y[i] = x[i][e];
-        *reinterpret_cast<V16*>(&KTs[(cb + e) * SC + EPC * pg]) = y;
-      }
-    }
-    for (int idx = tid; idx < kC * CH; idx += NTH) {
-      const int r = idx / CH;
-      const int cb = (idx % CH) * EPC;
-      *reinterpret_cast<V16*>(&Qs[r * SK + cb]) =
-          i0 + r < iend ? *reinterpret_cast<const V16*>(qbase + (size_t)r * H * D + cb) : zero;
-    }
-  } else {
-    // K rows of the chunk (zero past the stream end), natural column order:
-    // K K^T reads both operands from the same rows, so any order is consistent
-    for (int idx = tid; idx < kC * CH; idx += NTH) {
-      const int r = idx / CH;
-      const int cb = (idx % CH) * EPC;
-      *reinterpret_cast<V16*>(&Ks[r * SK + cb]) =
-          i0 + r < iend ? *reinterpret_cast<const V16*>(kbase + (size_t)r * Hkv * D + cb) : zero;
-    }
   }
-  for (int i = tid; i < kC * kSL; i += NTH) Lf[i] = 0.f;
-  // gates: g = inclusive cumsum of log2 a (a = 1 past the stream end), b
-  if (tid < 64) {
+  auto frag_of = [&](const V16 (&pc)[QV]) {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = to_f32(pc[i / EPC][i % EPC]);
+    return frag_from8<T>(x);
+  };
+
+  // ---- zero the solve buffer; gates: g = inclusive cumsum of log2 a
+  // (a = 1 past the stream end), gamma = 2^g, b
+  for (int i = lane; i < SM::nL / 4; i += 64) reinterpret_cast<f32x4*>(Lf)[i] = zero4();
+  {
     const int tok = i0 + lane;
     const float av = tok < iend ? a[(size_t)(bi * T_ + tok) * H + h] : 1.f;
+    const float bv = tok < iend ? b[(size_t)(bi * T_ + tok) * H + h] : 0.f;
     const float x = wave_prefix_sum(__builtin_amdgcn_logf(av), lane);
     lgs[lane] = x;
     gam[lane] = __builtin_amdgcn_exp2f(x);
-  } else if (tid < 128) {
-    const int tok = i0 + lane;
-    bet[lane] = tok < iend ? b[(size_t)(bi * T_ + tok) * H + h] : 0.f;
+    bet[lane] = bv;
   }
-  __syncthreads();
+  lds_barrier();
+  if (FULL) fac[lane] = __builtin_amdgcn_exp2f(fminf(lgs[kC - 1] - lgs[acc_idx(lane)], 0.f));
 
-  // ---- L = strictly lower (b_r 2^{g_r - g_s} k_r.k_s) on the 10 lower tiles;
-  // full: also A = [s <= r] 2^{g_r - g_s} q_r.k_s
-  for (int job = wv; job < (FULL ? 20 : 10); job += NW) {
-    const bool isq = job >= 10;
-    const int mt = kPrepTileM[isq ? job - 10 : job];
-    const int nt = kPrepTileN[isq ? job - 10 : job];
+  // ---- L = strictly lower (b_r 2^{g_r - g_s} k_r.k_s); full: also
+  // A = [s <= r] 2^{g_r - g_s} q_r.k_s
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
     const int r0 = 16 * mt + 4 * lg;
-    const int s = 16 * nt + l16;
     const f32x4 lr = *reinterpret_cast<const f32x4*>(&lgs[r0]);
     const f32x4 br = *reinterpret_cast<const f32x4*>(&bet[r0]);
-    const float ls = lgs[s];
-    const T* X = isq ? Qs : Ks;
-    Frag<T> xa[D / 32], xb[D / 32];
 #pragma unroll
-    for (int p = 0; p < D / 32; ++p) {
-      xa[p] = lds_frag8(&X[(16 * mt + l16) * SK + 32 * p + 8 * lg]);
-      xb[p] = lds_frag8(&Ks[(16 * nt + l16) * SK + 32 * p + 8 * lg]);
-    }
-    f32x4 acc = zero4();
+    for (int nt = 0; nt <= mt; ++nt) {
+      const int s = 16 * nt + l16;
+      const float ls = lgs[s];
+      f32x4 acc = zero4(), accq = zero4();
 #pragma unroll
-    for (int p = 0; p < D / 32; ++p) acc = mfma(xa[p], xb[p], acc);
+      for (int p = 0; p < KS; ++p) {
+        const Frag<T> kb = frag_of(kr[nt][p]);
+        acc = mfma(frag_of(kr[mt][p]), kb, acc);
+        if constexpr (FULL) accq = mfma(frag_of(qr[mt][p]), kb, accq);
+      }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = r0 + i;
-      const float dec = __builtin_amdgcn_exp2f(fminf(lr[i] - ls, 0.f));
-      if (isq) As[r * SC + acc_pos(s)] = from_f32<T>(s <= r ? dec * acc[i] : 0.f);
-      else Lf[r * kSL + s] = s < r ? br[i] * dec * acc[i] : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + i;
+        const float dec = __builtin_amdgcn_exp2f(fminf(lr[i] - ls, 0.f));
+        Lf[r * kSL + s] = s < r ? br[i] * dec * acc[i] : 0.f;
+        if constexpr (FULL) As[r * SC + acc_pos(s)] = from_f32<T>(s <= r ? dec * accq[i] : 0.f);
+      }
     }
   }
-  if (FULL) {
-    // the strictly upper tiles of A are zero
-    for (int i = tid; i < 6 * 256; i += NTH) {
+  if constexpr (FULL) {
+    // strictly upper tiles of A are zero; K^T (tokens in acc order) from the
+    // row pieces
+    for (int i = lane; i < 6 * 256; i += 64) {
       const int pr = i / 256;
       const int e = i % 256;
       const int mt = pr < 3 ? 0 : (pr < 5 ? 1 : 2);
       const int nt = pr < 3 ? pr + 1 : (pr < 5 ? pr - 1 : 3);
       As[(16 * mt + e / 16) * SC + acc_pos(16 * nt + e % 16)] = from_f32<T>(0.f);
     }
-    if (tid < kC) fac[tid] = __builtin_amdgcn_exp2f(fminf(lgs[kC - 1] - lgs[acc_idx(tid)], 0.f));
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int p = 0; p < KS; ++p)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          KTs[(32 * p + 8 * lg + i) * SC + acc_pos(16 * mt + l16)] = kr[mt][p][i / EPC][i % EPC];
   }
-  __syncthreads();
-  unit_lower_inverse(Lf, wv, lane);
+  lds_barrier();
+  unit_lower_inverse_wave(Lf, lane);
 
   // ---- TB = Tm diag(b) (and TBG = Tm diag(b gamma)): row r, columns
   // s0..s0+3 at positions acc_pos(s0)..+3 of the row
   T* tb = wtb + ci * (kC * kC);
-  for (int i = tid; i < kC * kC / 4; i += NTH) {
+  for (int i = lane; i < kC * kC / 4; i += 64) {
     const int r = i >> 4;
     const int s0 = (i & 15) * 4;
     const f32x4 tm = *reinterpret_cast<const f32x4*>(&Lf[r * kSL + s0]);
@@ -300,14 +295,15 @@ __global__ __launch_bounds__(64 * NW) void gdn_prep_kernel(
     if (FULL) store4(&TBGs[r * SC + acc_pos(s0)], x * gg);
     else store4(wtbg + ci * (kC * kC) + r * kC + acc_pos(s0), x * gg);
   }
-  if (tid < 64) wg[ci * (2 * kC) + tid] = lgs[tid];
-  else if (tid < 128) wg[ci * (2 * kC) + tid] = gam[tid - 64];
+  wg[ci * (2 * kC) + lane] = lgs[lane];
+  wg[ci * (2 * kC) + kC + lane] = gam[lane];
   if constexpr (FULL) {
-    __syncthreads();
+    lds_barrier();
     // ---- -Wm = -(TBG K): per 16-row dk tile, Wm^T = K^T TBG^T on MFMA,
-    // staged in the (now free) solve buffer as [token][dk in acc order]
-    constexpr int MT = D / 16;
-    for (int mt = wv; mt < MT; mt += NW) {
+    // written as [token][dk in acc order]
+    T* wm = wwm + ci * (kC * D);
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) {
       Frag<T> kf[2];
 #pragma unroll
       for (int p = 0; p < 2; ++p) kf[p] = lds_frag8(&KTs[(16 * mt + l16) * SC + 32 * p + 8 * lg]);
@@ -316,20 +312,13 @@ __global__ __launch_bounds__(64 * NW) void gdn_prep_kernel(
         f32x4 acc = zero4();
 #pragma unroll
         for (int p = 0; p < 2; ++p) acc = mfma(kf[p], lds_frag8(&TBGs[(16 * nt + l16) * SC + 32 * p + 8 * lg]), acc);
-        store4(&Wms[(16 * nt + l16) * SK + acc_pos(16 * mt + 4 * lg)], -acc);
+        store4(wm + (16 * nt + l16) * D + acc_pos(16 * mt + 4 * lg), -acc);
       }
     }
-    __syncthreads();
-    // ---- copy out: -Wm [64][D], K^T 2^{g_C - g} [D][64], A [64][64]
-    T* wm = wwm + ci * (kC * D);
+    // ---- K^T 2^{g_C - g} [D][64] and A [64][64], 16-byte pieces
     T* ktg = wktg + ci * (D * kC);
     T* aa = wa + ci * (kC * kC);
-    for (int i = tid; i < kC * CH; i += NTH) {
-      const int r = i / CH;
-      const int pc = (i % CH) * EPC;
-      *reinterpret_cast<V16*>(wm + r * D + pc) = *reinterpret_cast<const V16*>(&Wms[r * SK + pc]);
-    }
-    for (int i = tid; i < D * (kC / EPC); i += NTH) {
+    for (int i = lane; i < D * (kC / EPC); i += 64) {
       const int r = i / (kC / EPC);
       const int pc = (i % (kC / EPC)) * EPC;
       const V16 x = *reinterpret_cast<const V16*>(&KTs[r * SC + pc]);
@@ -338,7 +327,7 @@ __global__ __launch_bounds__(64 * NW) void gdn_prep_kernel(
       for (int e = 0; e < EPC; ++e) y[e] = from_f32<T>(to_f32(x[e]) * fac[pc + e]);
       *reinterpret_cast<V16*>(ktg + r * kC + pc) = y;
     }
-    for (int i = tid; i < kC * (kC / EPC); i += NTH) {
+    for (int i = lane; i < kC * (kC / EPC); i += 64) {
       const int r = i / (kC / EPC);
       const int pc = (i % (kC / EPC)) * EPC;
       *reinterpret_cast<V16*>(aa + r * kC + pc) = *reinterpret_cast<const V16*>(&As[r * SC + pc]);
@@ -349,12 +338,11 @@ __global__ __launch_bounds__(64 * NW) void gdn_prep_kernel(
 template <class T, int D, bool FULL>
 hipError_t launch_prep_t(const PrefillArgs& p, int nch, hipStream_t s) {
   using SM = PrepSmem<T, D, FULL>;
-  constexpr int NW = FULL ? 8 : 4;
-  auto kern = gdn_prep_kernel<T, D, NW, FULL>;
+  auto kern = gdn_prep_kernel<T, D, FULL>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, SM::bytes);
   if (e != hipSuccess) return e;
   const GdnWorkspace w = gdn_workspace_layout(p.workspace, p.B, p.H, nch, D, sizeof(T), FULL);
-  hipLaunchKernelGGL(kern, dim3(nch, p.H, p.B), dim3(64 * NW), SM::bytes, s, (const T*)p.q,
+  hipLaunchKernelGGL(kern, dim3(nch, p.H, p.B), dim3(64), SM::bytes, s, (const T*)p.q,
                      (const T*)p.k, p.a, p.b, (T*)w.tb, (T*)w.tbg, (T*)w.wm, (T*)w.ktg, (T*)w.a, w.g,
                      p.T, p.H, p.Hkv, p.n_sink, p.window, nch);
   return hipGetLastError();

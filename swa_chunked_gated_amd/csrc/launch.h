@@ -125,6 +125,6 @@ hipError_t launch_cache_from_prefill(const CacheArgs& a, hipStream_t s);
 hipError_t launch_shortconv(const ShortConvArgs& a, hipStream_t s);
 
 // Dynamic LDS bytes the decode kernel needs (the front end checks the limit).
-size_t decode_lds_bytes(int G, int N, int D, int gla);
+size_t decode_lds_bytes(int G, int N, int D, int gla, int elt);
 
 }  // namespace gdn
