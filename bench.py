@@ -207,6 +207,8 @@ LINEAR_SOURCES = ("swa_chunked_gated_amd/csrc/gdn_prep.hip", "swa_chunked_gated_
                   "swa_chunked_gated_amd/csrc/common.h")
 SWA_SOURCES = ("swa_chunked_gated_amd/csrc/swa.hip", "swa_chunked_gated_amd/csrc/common.h")
 DECODE_SOURCES = ("swa_chunked_gated_amd/csrc/decode.hip", "swa_chunked_gated_amd/csrc/common.h")
+# one decode step is three launches: softmax branch, state update, cache commit
+DECODE_KERNELS = "decode_swa_kernel+decode_state_kernel+decode_commit_kernel"
 
 
 def stored_traffic(kernel, workload, sources):
@@ -271,11 +273,11 @@ def bench_decode(steps=1000, warmup=10):
         "workload": "decode_b256 (B=256, H=32, Hkv=8, d=128, cache 8+56, t=4096..5095)",
         "steps": steps, "ms_per_step": sec * 1e3, "steps_per_s": 1.0 / sec,
         "tokens_per_s": w.B / sec, "event_ms_per_step": ev_ms,
-        "roofline": {"kernel": "decode_kernel + decode_commit_kernel", "bound": "hbm",
+        "roofline": {"kernel": DECODE_KERNELS, "bound": "hbm",
                      "achieved": byts / (ev_ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9,
                      "unit": "GB/s", "frac": byts / (ev_ms * 1e-3) / PEAK_HBM,
                      "algorithmic_bytes_per_step": byts,
-                     "traffic": stored_traffic("decode_kernel", w.name, DECODE_SOURCES)},
+                     "traffic": stored_traffic(DECODE_KERNELS, w.name, DECODE_SOURCES)},
     }
 
 

@@ -8,13 +8,13 @@
 // e = t - window, is folded into the per-head recurrent state with its own
 // gates, and the state is read with q_t.  The two outputs are summed.
 //
-// Work split: one workgroup per (sequence, query head).  Its d x d fp32
-// state is streamed through registers exactly once (one read, one write);
-// the loads are issued first so they overlap the softmax over the cached
-// rows.  The G heads of a KV group are mapped to one XCD so the cached rows
-// they share are fetched from HBM once.  A second small kernel (one
-// workgroup per sequence) then writes the new token into the freed slot and
-// advances pos, after every head has read the evicted entry.
+// Work split: the softmax branch runs first, one workgroup per (sequence,
+// KV head) for its G query heads, so every cached row is read once; the
+// linear branch then streams each head's d x d fp32 state through registers
+// exactly once (one read, one write), one workgroup per (sequence, query
+// head), and adds its output.  A third small kernel (one workgroup per
+// sequence) writes the new token into the freed slot and advances pos,
+// after every head has read the evicted entry.
 //
 // Gated delta rule in one pass over the old state S (a, b: evicted gates):
 //   c1 = S^T k_e, c2 = S^T q, u = b (v_e - a c1)
@@ -27,41 +27,193 @@
 namespace gdn {
 namespace {
 
-constexpr int kDecThreads = 256;
+constexpr int kSwaThreads = 256;
+constexpr int kStateThreads = 512;
 constexpr int kMaxG = 16;
 constexpr int kSlotChunk = 64;   // cache rows staged in LDS at a time
+
+// Slot state of cache slot j for the new token t: -1 not attended, 0 the
+// cached entry, 1 the new token (its slot is being overwritten this step).
+__device__ __forceinline__ int slot_state_of(int j, int t, int n_sink, int window) {
+  if (j < n_sink) return j < t ? 0 : (j == t ? 1 : -1);
+  if (t < n_sink) return -1;
+  const int r = j - n_sink;
+  const int back = ((t - n_sink - r) % window + window) % window;
+  return back == 0 ? 1 : (t - back >= n_sink ? 0 : -1);   // latest token of this ring slot
+}
+
+// Softmax branch of the decode step for the G query heads of one KV head:
+// each cached K and V row is staged through LDS once (both fetched together)
+// and used by all G heads.  Writes o (I/O type) = the softmax output of each
+// head.
+template <class T, int D>
+__global__ __launch_bounds__(kSwaThreads) void decode_swa_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ kc, const T* __restrict__ vc, const int* __restrict__ pos,
+    T* __restrict__ o, int B, int H, int Hkv, int n_sink, int window) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int SPH = kSwaThreads / D;      // slot phases of the P V sum
+  constexpr int SR = D + VEC;               // staged row stride
+  typedef typename Vec16<T>::type V16;
+  const int G = H / Hkv;
+  const int grp = blockIdx.x;               // (sequence, KV head)
+  const int bi = grp / Hkv;
+  const int g = grp % Hkv;
+  const int N = n_sink + window;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = wave_id();
+  const int t = pos[bi];
+  if (t < 0) return;   // outside the contract (pos >= 0); never index a negative slot
+
+  extern __shared__ float sm[];
+  float* qs = sm;                           // [G][D]
+  float* kt = qs + G * D;                   // [D] new key
+  float* vt = kt + D;                       // [D] new value
+  float* lg = vt + D;                       // [G][N] logits, then probabilities
+  T* ks = reinterpret_cast<T*>((reinterpret_cast<uintptr_t>(lg + G * N) + 15) & ~(uintptr_t)15);
+  T* vs = ks + kSlotChunk * SR;             // [64][SR] staged K and V rows
+
+  const size_t kvbase = (size_t)grp * N * D;     // cache [B][Hkv][N][D]
+  const size_t tokkv = (size_t)grp * D;          // k, v  [B][Hkv][D]
+  // K and V rows of slots j0 .. j0 + nj - 1 (the new token's slot from k, v;
+  // slots not attended as zeros): fetched into registers, then stored to LDS
+  constexpr int PER = (kSlotChunk * (D / VEC) + kSwaThreads - 1) / kSwaThreads;
+  V16 kr[PER], vr[PER];
+  auto fetch = [&](int j0, int nj) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = tid + u * kSwaThreads;
+      const int jj = i / (D / VEC);
+      const int c = (i % (D / VEC)) * VEC;
+      const int st = jj < nj ? slot_state_of(j0 + jj, t, n_sink, window) : -1;
+      if (st == 0) {
+        kr[u] = *reinterpret_cast<const V16*>(kc + kvbase + (size_t)(j0 + jj) * D + c);
+        vr[u] = *reinterpret_cast<const V16*>(vc + kvbase + (size_t)(j0 + jj) * D + c);
+      } else {
+#pragma unroll
+        for (int xx = 0; xx < VEC; ++xx) {
+          kr[u][xx] = from_f32<T>(0.f);
+          vr[u][xx] = from_f32<T>(0.f);
+        }
+      }
+    }
+  };
+  auto store = [&](int j0, int nj) {
+    lds_barrier();   // kt / vt are in place; the previous chunk's reads are done
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = tid + u * kSwaThreads;
+      const int jj = i / (D / VEC);
+      const int c = (i % (D / VEC)) * VEC;
+      if (jj < kSlotChunk) {
+        const int st = jj < nj ? slot_state_of(j0 + jj, t, n_sink, window) : -1;
+        if (st == 1) {
+#pragma unroll
+          for (int xx = 0; xx < VEC; ++xx) {
+            kr[u][xx] = from_f32<T>(kt[c + xx]);
+            vr[u][xx] = from_f32<T>(vt[c + xx]);
+          }
+        }
+        *reinterpret_cast<V16*>(&ks[jj * SR + c]) = kr[u];
+        *reinterpret_cast<V16*>(&vs[jj * SR + c]) = vr[u];
+      }
+    }
+    lds_barrier();
+  };
+  // the first chunk's rows are requested before the small per-step vectors
+  fetch(0, min(kSlotChunk, N));
+  for (int i = tid; i < G * D; i += kSwaThreads) qs[i] = to_f32(q[((size_t)bi * H + g * G) * D + i]);
+  for (int i = tid; i < D; i += kSwaThreads) {
+    kt[i] = to_f32(k[tokkv + i]);
+    vt[i] = to_f32(v[tokkv + i]);
+  }
+
+  // ---- logits: thread (slot, head) takes a whole dot product
+  const float scale = 1.0f / sqrtf((float)D);
+  for (int j0 = 0; j0 < N; j0 += kSlotChunk) {
+    const int nj = min(kSlotChunk, N - j0);
+    if (j0 > 0) fetch(j0, nj);
+    store(j0, nj);
+    for (int i = tid; i < nj * G; i += kSwaThreads) {
+      const int jj = i % nj;
+      const int hh = i / nj;
+      float acc = 0.f;
+#pragma unroll 4
+      for (int d = 0; d < D; d += VEC) {
+        const V16 kx = *reinterpret_cast<const V16*>(&ks[jj * SR + d]);
+#pragma unroll
+        for (int xx = 0; xx < VEC; ++xx) acc += to_f32(kx[xx]) * qs[hh * D + d + xx];
+      }
+      lg[hh * N + j0 + jj] = slot_state_of(j0 + jj, t, n_sink, window) >= 0 ? acc * scale : -INFINITY;
+    }
+  }
+  lds_barrier();
+  // ---- softmax per head (wave w takes heads w, w + 4, ...)
+  for (int hh = wv; hh < G; hh += kSwaThreads / 64) {
+    float* l = lg + hh * N;
+    float m = -INFINITY;
+    for (int j = lane; j < N; j += 64) m = fmaxf(m, l[j]);
+    m = wave_max(m);
+    float sum = 0.f;
+    for (int j = lane; j < N; j += 64) {
+      const float xv = l[j];
+      const float pr = xv == -INFINITY ? 0.f : __expf(xv - m);
+      l[j] = pr;
+      sum += pr;
+    }
+    sum = wave_sum(sum);
+    const float inv = 1.0f / sum;
+    for (int j = lane; j < N; j += 64) l[j] *= inv;
+  }
+  lds_barrier();
+  // ---- o = P V: thread (column c, head hh) sums over the slots; SPH heads
+  // per pass of the workgroup
+  const int c = tid % D;
+  for (int h0 = 0; h0 < G; h0 += SPH) {
+    const int hh = h0 + tid / D;
+    float acc = 0.f;
+    if (N > kSlotChunk) {
+      // several chunks: restage V chunk by chunk (all threads take part)
+      for (int j0 = 0; j0 < N; j0 += kSlotChunk) {
+        const int nj = min(kSlotChunk, N - j0);
+        fetch(j0, nj);
+        store(j0, nj);
+        if (hh < G)
+          for (int jj = 0; jj < nj; ++jj) acc += lg[hh * N + j0 + jj] * to_f32(vs[jj * SR + c]);
+      }
+    } else if (hh < G) {
+#pragma unroll 8
+      for (int jj = 0; jj < N; ++jj) acc += lg[hh * N + jj] * to_f32(vs[jj * SR + c]);
+    }
+    if (hh < G) o[((size_t)bi * H + g * G + hh) * D + c] = from_f32<T>(acc);
+  }
+}
 
 template <int D>
 struct StateMap {
   static constexpr int CG = D / 4;                 // column groups of 4 floats
-  static constexpr int RG = kDecThreads / CG;      // row groups
+  static constexpr int RG = kStateThreads / CG;    // row groups
   static constexpr int R = D / RG;                 // rows per thread
+  static constexpr int NWV = kStateThreads / 64;   // waves
 };
 
+// Linear branch of the decode step, one workgroup per (sequence, query
+// head): the head's d x d fp32 state is streamed through registers exactly
+// once (one read, one write), its loads issued before anything else.  With
+// the softmax branch, o already holds its output and the linear output is
+// added to it.
 template <class T, bool GLA, int D>
-__global__ __launch_bounds__(kDecThreads) void decode_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const float* __restrict__ a, const float* __restrict__ b, float* __restrict__ state,
-    const T* __restrict__ kc, const T* __restrict__ vc, const float* __restrict__ ac,
-    const float* __restrict__ bc, const int* __restrict__ pos, T* __restrict__ o, int B, int H,
-    int Hkv, int n_sink, int window, int flags) {
+__global__ __launch_bounds__(kStateThreads) void decode_state_kernel(
+    const T* __restrict__ q, const float* __restrict__ a, const float* __restrict__ b,
+    float* __restrict__ state, const T* __restrict__ kc, const T* __restrict__ vc,
+    const float* __restrict__ ac, const float* __restrict__ bc, const int* __restrict__ pos,
+    T* __restrict__ o, int B, int H, int Hkv, int n_sink, int window, int flags) {
   using M = StateMap<D>;
-  const int G = H / Hkv;
-  // block -> (KV group, head in group); the G heads of a group share
-  // blockIdx.x mod 8 so they run on one XCD and share its L2 for the cache rows
-  const int NG = B * Hkv;
-  int grp, hh;
-  const int x = blockIdx.x;
-  if (NG % 8 == 0) {
-    grp = (x / (8 * G)) * 8 + x % 8;
-    hh = (x / 8) % G;
-  } else {
-    grp = x / G;
-    hh = x % G;
-  }
-  const int bi = grp / Hkv;
-  const int g = grp % Hkv;
-  const int h = g * G + hh;
+  const int bh = blockIdx.x;
+  const int bi = bh / H;
+  const int h = bh % H;
+  const int g = h / (H / Hkv);
   const int N = n_sink + window;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -76,35 +228,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
   // ---- the head's state is streamed once: issue its loads before anything else
   const int cg = tid % M::CG;
   const int rg = tid / M::CG;
-  float* Sg = state + (size_t)(bi * H + h) * D * D;
+  float* Sg = state + (size_t)bh * D * D;
   f32x4 s[M::R];
 #pragma unroll
   for (int r = 0; r < M::R; ++r)
     s[r] = *reinterpret_cast<const f32x4*>(Sg + (size_t)(rg + M::RG * r) * D + 4 * cg);
 
-  extern __shared__ float sm[];
-  float* qs = sm;                       // [D]   query of this head
-  float* kt = qs + D;                   // [D]   new key
-  float* vt = kt + D;                   // [D]   new value
-  float* ke = vt + D;                   // [D]   evicted key
-  float* ve = ke + D;                   // [D]   evicted value
-  float* ae = ve + D;                   // [D]   evicted a (GLA: per channel; GDN: ae[0])
-  float* misc = ae + D;                 // [4]   b_e, k_e . q
-  float* osw = misc + 4;                // [D]   softmax output
-  float* red = osw + D;                 // [4][CG][8] cross-wave partials
-  float* lg = red + 4 * M::CG * 8;      // [N]   logits, then probabilities
-  int* slot_state = reinterpret_cast<int*>(lg + N);                      // [N]
-  // [64][D + pad] staged cache rows, 16-byte aligned
-  T* kvs = reinterpret_cast<T*>((reinterpret_cast<uintptr_t>(slot_state + N) + 15) & ~(uintptr_t)15);
-
-  const size_t kvbase = (size_t)(bi * Hkv + g) * N * D;     // cache [B][Hkv][N][D]
-  const size_t tokkv = (size_t)(bi * Hkv + g) * D;          // k, v  [B][Hkv][D]
-
-  // ---- stage the small per-step vectors in LDS
-  for (int i = tid; i < D; i += kDecThreads) {
-    qs[i] = to_f32(q[(size_t)(bi * H + h) * D + i]);
-    kt[i] = to_f32(k[tokkv + i]);
-    vt[i] = to_f32(v[tokkv + i]);
+  __shared__ float qs[D], ke[D], ve[D], ae[D], misc[4];
+  __shared__ float red[M::NWV * M::CG * 8];
+  const size_t kvbase = ((size_t)bi * Hkv + g) * N * D;
+  for (int i = tid; i < D; i += kStateThreads) {
+    qs[i] = to_f32(q[(size_t)bh * D + i]);
     if (evict) {
       ke[i] = to_f32(kc[kvbase + (size_t)slot * D + i]);
       ve[i] = to_f32(vc[kvbase + (size_t)slot * D + i]);
@@ -113,7 +247,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
   if (evict) {
     const size_t gb = ((size_t)bi * window + ring) * H + h;   // gate cache [B][W][H](,D)
     if (GLA) {
-      for (int i = tid; i < D; i += kDecThreads) ae[i] = ac[gb * D + i];
+      for (int i = tid; i < D; i += kStateThreads) ae[i] = ac[gb * D + i];
     } else if (tid == 0) {
       ae[0] = ac[gb];
       misc[0] = bc[gb];
@@ -127,113 +261,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     if (lane == 0) misc[1] = acc;   // k_e . q
   }
 
-  // ---- softmax branch over the N cache slots (the new token in its slot).
-  // Slot states are computed once; cached K and V rows are staged through
-  // LDS 64 slots at a time with coalesced 16-byte loads.
-  const bool do_swa = (flags & 2) != 0;
-  if (do_swa) {
-    const float scale = 1.0f / sqrtf((float)D);
-    for (int j = tid; j < N; j += kDecThreads) {
-      int st;   // -1: not attended, 0: cached entry, 1: the new token
-      if (j < n_sink) {
-        st = j < t ? 0 : (j == t ? 1 : -1);
-      } else if (t < n_sink) {
-        st = -1;
-      } else {
-        const int r = j - n_sink;
-        const int back = ((t - n_sink - r) % window + window) % window;
-        st = back == 0 ? 1 : (t - back >= n_sink ? 0 : -1);   // latest token of this ring slot
-      }
-      slot_state[j] = st;
-    }
-    lds_barrier();
-    constexpr int VEC = 16 / sizeof(T);
-    for (int j0 = 0; j0 < N; j0 += kSlotChunk) {
-      const int nj = min(kSlotChunk, N - j0);
-      for (int i = tid; i < nj * (D / VEC); i += kDecThreads) {
-        const int jj = i / (D / VEC);
-        const int c = (i % (D / VEC)) * VEC;
-        const int st = slot_state[j0 + jj];
-        typename Vec16<T>::type kv;
-        if (st == 0) {
-          kv = *reinterpret_cast<const typename Vec16<T>::type*>(kc + kvbase + (size_t)(j0 + jj) * D + c);
-        } else {
-#pragma unroll
-          for (int xx = 0; xx < VEC; ++xx) kv[xx] = from_f32<T>(st == 1 ? kt[c + xx] : 0.f);
-        }
-        *reinterpret_cast<typename Vec16<T>::type*>(&kvs[jj * (D + VEC) + c]) = kv;
-      }
-      lds_barrier();
-      // 4 threads per slot, each a quarter of the dot product (all 256 threads
-      // take part: nj * 4 <= 256, and inactive slots compute on zeros)
-      {
-        const int jj = tid >> 2;
-        const int part = tid & 3;
-        float acc = 0.f;
-        if (jj < nj) {
-#pragma unroll 8
-          for (int d = part * (D / 4); d < (part + 1) * (D / 4); ++d)
-            acc += to_f32(kvs[jj * (D + VEC) + d]) * qs[d];
-        }
-        acc += shfl_xor(acc, 1);
-        acc += shfl_xor(acc, 2);
-        if (part == 0 && jj < nj) lg[j0 + jj] = slot_state[j0 + jj] >= 0 ? acc * scale : -INFINITY;
-      }
-      lds_barrier();
-    }
-    if (wv == 0) {
-      float m = -INFINITY;
-      for (int j = lane; j < N; j += 64) m = fmaxf(m, lg[j]);
-      m = wave_max(m);
-      float sum = 0.f;
-      for (int j = lane; j < N; j += 64) {
-        const float xv = lg[j];
-        const float pr = xv == -INFINITY ? 0.f : __expf(xv - m);
-        lg[j] = pr;
-        sum += pr;
-      }
-      sum = wave_sum(sum);
-      const float inv = 1.0f / sum;
-      for (int j = lane; j < N; j += 64) lg[j] *= inv;
-    }
-    {
-      // 256 threads: column c and slot phase sph (256 / D phases), reduced at the end
-      constexpr int SPH = kDecThreads / D;
-      const int c = tid % D;
-      const int sph = tid / D;
-      float acc = 0.f;
-      for (int j0 = 0; j0 < N; j0 += kSlotChunk) {
-        const int nj = min(kSlotChunk, N - j0);
-        lds_barrier();   // probabilities are final / previous chunk's reads are done
-        for (int i = tid; i < nj * (D / VEC); i += kDecThreads) {
-          const int jj = i / (D / VEC);
-          const int cc = (i % (D / VEC)) * VEC;
-          const int st = slot_state[j0 + jj];
-          typename Vec16<T>::type vv;
-          if (st == 0) {
-            vv = *reinterpret_cast<const typename Vec16<T>::type*>(vc + kvbase + (size_t)(j0 + jj) * D + cc);
-          } else {
-#pragma unroll
-            for (int xx = 0; xx < VEC; ++xx) vv[xx] = from_f32<T>(st == 1 ? vt[cc + xx] : 0.f);
-          }
-          *reinterpret_cast<typename Vec16<T>::type*>(&kvs[jj * (D + VEC) + cc]) = vv;
-        }
-        lds_barrier();
-        for (int jj = sph; jj < nj; jj += SPH) acc += lg[j0 + jj] * to_f32(kvs[jj * (D + VEC) + c]);
-      }
-      lds_barrier();
-      red[tid] = acc;
-      lds_barrier();
-      if (tid < D) {
-        float tot = 0.f;
-        for (int p2 = 0; p2 < SPH; ++p2) tot += red[p2 * D + tid];
-        osw[tid] = tot;
-      }
-    }
-  }
-  lds_barrier();   // osw, misc and the red buffer are settled
-
-  // ---- linear branch: one pass over the state held in registers
+  // ---- one pass over the state held in registers: c1 = S^T k_e, c2 = S^T q
   float p1[4] = {0.f, 0.f, 0.f, 0.f};
   float p2[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -248,7 +276,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
       p2[xx] += s[r][xx] * qr;
     }
   }
-  // reduce over row groups: inside the wave, then across the 4 waves
+  // reduce over row groups: inside the wave, then across the waves
 #pragma unroll
   for (int m = M::CG; m < 64; m <<= 1) {
 #pragma unroll
@@ -257,7 +285,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
       p2[xx] += shfl_xor(p2[xx], m);
     }
   }
-  lds_barrier();   // the softmax's use of `red` is over
   if (lane < M::CG) {
 #pragma unroll
     for (int xx = 0; xx < 4; ++xx) {
@@ -272,7 +299,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     c1[xx] = 0.f;
     c2[xx] = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < M::NWV; ++w) {
       c1[xx] += red[(w * M::CG + cg) * 8 + xx];
       c2[xx] += red[(w * M::CG + cg) * 8 + 4 + xx];
     }
@@ -314,16 +341,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
 #pragma unroll
     for (int xx = 0; xx < 4; ++xx) olin[xx] = c2[xx];
   }
-  if (rg == 0) {
+  if (rg == 0 && (flags & 1)) {
+    T* orow = o + (size_t)bh * D + 4 * cg;
     f32x4 out;
 #pragma unroll
-    for (int xx = 0; xx < 4; ++xx) {
-      float val = 0.f;
-      if (flags & 1) val += olin[xx];
-      if (do_swa) val += osw[4 * cg + xx];
-      out[xx] = val;
-    }
-    store4(o + (size_t)(bi * H + h) * D + 4 * cg, out);
+    for (int xx = 0; xx < 4; ++xx) out[xx] = olin[xx];
+    if (flags & 2) out += load4(orow);
+    store4(orow, out);
   }
 }
 
@@ -416,16 +440,23 @@ __global__ __launch_bounds__(256) void cache_fill_kernel(
 template <class T, bool GLA, int D>
 hipError_t launch_decode_t(const DecodeArgs& p, hipStream_t s) {
   const int G = p.H / p.Hkv;
-  const size_t lds = decode_lds_bytes(G, p.n_sink + p.window, D, GLA, (int)sizeof(T));
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)decode_kernel<T, GLA, D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (p.flags & 2) {
+    const size_t lds = decode_lds_bytes(G, p.n_sink + p.window, D, GLA, (int)sizeof(T));
+    if (lds > 64 * 1024) {
+      hipError_t e = hipFuncSetAttribute((const void*)decode_swa_kernel<T, D>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((decode_swa_kernel<T, D>), dim3(p.B * p.Hkv), dim3(kSwaThreads), lds, s,
+                       (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.k_cache,
+                       (const T*)p.v_cache, p.pos, (T*)p.o, p.B, p.H, p.Hkv, p.n_sink, p.window);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_kernel<T, GLA, D>), dim3(p.B * p.H), dim3(kDecThreads), lds, s,
-                     (const T*)p.q, (const T*)p.k, (const T*)p.v, p.a, p.b, p.state,
-                     (const T*)p.k_cache, (const T*)p.v_cache, p.a_cache, p.b_cache, p.pos, (T*)p.o,
-                     p.B, p.H, p.Hkv, p.n_sink, p.window, p.flags);
+  hipLaunchKernelGGL((decode_state_kernel<T, GLA, D>), dim3(p.B * p.H), dim3(kStateThreads), 0, s,
+                     (const T*)p.q, p.a, p.b, p.state, (const T*)p.k_cache, (const T*)p.v_cache,
+                     p.a_cache, p.b_cache, p.pos, (T*)p.o, p.B, p.H, p.Hkv, p.n_sink, p.window,
+                     p.flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_commit_kernel<T, GLA>), dim3(p.B), dim3(256), 0, s, (const T*)p.k,
@@ -443,11 +474,10 @@ hipError_t launch_decode_d(const DecodeArgs& p, hipStream_t s) {
 }  // namespace
 
 size_t decode_lds_bytes(int G, int N, int D, int gla, int elt) {
-  (void)G;
   (void)gla;
-  const size_t floats = 8 * (size_t)D + 4 + 4 * (size_t)(D / 4) * 8 + (size_t)N;
-  const size_t ints = (size_t)N;
-  const size_t staging = (size_t)kSlotChunk * (D + 16 / elt) * elt;   // cache rows of the I/O type
+  const size_t floats = (size_t)G * D + 2 * (size_t)D + (size_t)G * N;
+  const size_t ints = 0;
+  const size_t staging = 2 * (size_t)kSlotChunk * (D + 16 / elt) * elt;   // K and V rows of the I/O type
   return floats * sizeof(float) + ints * sizeof(int) + 16 + staging;
 }
 
