@@ -63,7 +63,7 @@ size_t prefill_workspace_bytes(int B, int T, int H, int dk, int n_sink, int wind
   if (nch == 0) return 0;
   const size_t elt = dtype == GDN_BF16 ? 2 : 4;
   if (update == GDN_GLA) return gdn::gla_workspace_layout(nullptr, B, H, nch, dk, elt).bytes;
-  return gdn::gdn_workspace_layout(nullptr, B, H, nch, dk, elt, gdn::gdn_full_prep(B, H, dk)).bytes;
+  return gdn::gdn_workspace_layout(nullptr, B, H, nch, dk, elt, gdn::gdn_full_prep(B, H, dk, elt == 2)).bytes;
 }
 }  // namespace
 

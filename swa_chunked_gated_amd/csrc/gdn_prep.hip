@@ -300,7 +300,7 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(
   if constexpr (FULL) {
     lds_barrier();
     // ---- -Wm = -(TBG K): per 16-row dk tile, Wm^T = K^T TBG^T on MFMA,
-    // written as [token][dk in acc order]
+    // written as [token][dk]
     T* wm = wwm + ci * (kC * D);
 #pragma unroll
     for (int mt = 0; mt < D / 16; ++mt) {
@@ -312,16 +312,17 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(
         f32x4 acc = zero4();
 #pragma unroll
         for (int p = 0; p < 2; ++p) acc = mfma(kf[p], lds_frag8(&TBGs[(16 * nt + l16) * SC + 32 * p + 8 * lg]), acc);
-        store4(wm + (16 * nt + l16) * D + acc_pos(16 * mt + 4 * lg), -acc);
+        store4(wm + (16 * nt + l16) * D + 16 * mt + 4 * lg, -acc);
       }
     }
-    // ---- K^T 2^{g_C - g} [D][64] and A [64][64], 16-byte pieces
+    // ---- K^T 2^{g_C - g} [D][64] (row r holds d_k index acc_pos(r), the
+    // state row order of the scan's accumulators) and A [64][64], 16-byte pieces
     T* ktg = wktg + ci * (D * kC);
     T* aa = wa + ci * (kC * kC);
     for (int i = lane; i < D * (kC / EPC); i += 64) {
       const int r = i / (kC / EPC);
       const int pc = (i % (kC / EPC)) * EPC;
-      const V16 x = *reinterpret_cast<const V16*>(&KTs[r * SC + pc]);
+      const V16 x = *reinterpret_cast<const V16*>(&KTs[acc_pos(r) * SC + pc]);
       V16 y;
 #pragma unroll
       for (int e = 0; e < EPC; ++e) y[e] = from_f32<T>(to_f32(x[e]) * fac[pc + e]);
@@ -353,17 +354,19 @@ hipError_t launch_prep_d(const PrefillArgs& p, int nch, hipStream_t s) {
   if constexpr (sizeof(T) == 4 && D == 128) {
     return hipErrorInvalidValue;   // fp32 linear branch runs at d = 64 only
   } else {
-    return gdn_full_prep(p.B, p.H, p.D) ? launch_prep_t<T, D, true>(p, nch, s)
-                                        : launch_prep_t<T, D, false>(p, nch, s);
+    if constexpr (sizeof(T) == 2) {
+      if (gdn_full_prep(p.B, p.H, p.D, 1)) return launch_prep_t<T, D, true>(p, nch, s);
+    }
+    return launch_prep_t<T, D, false>(p, nch, s);
   }
 }
 
 }  // namespace
 
-bool gdn_full_prep(int B, int H, int D) {
-  // the scan fills fewer workgroups than the GPU has compute units: every
-  // state-independent product comes from the preparation kernel
-  return (long long)B * H * (D == 128 ? 2 : 1) < 256;
+bool gdn_full_prep(int B, int H, int D, int bf16) {
+  // bf16 and the scan fills fewer workgroups than the GPU has compute units:
+  // every state-independent product comes from the preparation kernel
+  return bf16 && (long long)B * H * (D == 128 ? 2 : 1) < 256;
 }
 
 GdnWorkspace gdn_workspace_layout(void* base, int B, int H, int nch, int D, size_t elt, bool full) {

@@ -1,0 +1,329 @@
+// State scan of the chunked gated delta rule (prefill, bf16 I/O) for the case
+// where the chunk preparation has already computed every state-independent
+// chunk quantity: few (sequence, head) chains, so the scan alone cannot fill
+// the GPU and its per-chunk latency is what counts.
+//
+// Method (page "The Key to Going Linear: Analysis-Driven Transformer
+// Linearization"): section 线性注意力替换机制 gives the gated delta rule
+// S_i = a_i (I - b_i k_i k_i^T) S_{i-1} + b_i k_i v_i^T; section
+// 填补近似缺口的实用设计 has the recurrence cover only evicted tokens, read
+// with lag `window`: o_lin[t] = S^(t-window)^T q_t.  Chunk form (64 stream
+// tokens, incoming state S; derived by unrolling the recurrence):
+//   U = TB V - Wm S,   O = diag(gamma) Q S + A U,   S <- gamma_C S + KTg U
+// with TB = Tm diag(b), Wm = Tm diag(b gamma) K, KTg = K^T diag(gamma_C /
+// gamma) and A the decayed causal scores, all read from the preparation.
+//
+// Work split: one workgroup per (sequence, head, 16 * NW state columns) with
+// NW compute waves and one loader wave.  Each compute wave owns 16 state
+// columns as fp32 MFMA accumulators for the whole sequence; the accumulator
+// row r of the state holds d_k index acc_pos(r), the order in which MFMA
+// accumulators turn into operands, so that the query and -Wm tiles are read
+// in their natural d_k order (the preparation writes KTg rows to match).  The
+// loader wave streams chunk c+1's tiles (query rows, V rows, TB, -Wm, KTg, A,
+// gates) from global memory straight into the second of two LDS buffers with
+// global-to-LDS loads, while the compute waves run chunk c from the first
+// buffer; one workgroup barrier per chunk hands the buffer over.  The compute
+// waves issue no loads of their own, so their MFMA and LDS work never queues
+// behind the vector-memory traffic of the next chunk.
+
+#include "common.h"
+#include "launch.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kC = 64;   // chunk length
+typedef unsigned short ushort8 __attribute__((ext_vector_type(8)));
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* gbl_void_ptr;
+
+// Lane L of the wave loads 16 (4) bytes at g into LDS at base + 16 L (4 L).
+__device__ __forceinline__ void dma16(const void* g, void* base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_ptr)(void*)g, (lds_void_ptr)base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, void* base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_ptr)(void*)g, (lds_void_ptr)base, 4, 0, 0);
+}
+
+template <int D, int NW>
+struct FullSmem {
+  static constexpr int SK = D + 8;          // row stride of [64][D] tiles (elements)
+  static constexpr int SC = kC + 8;         // row stride of [*][64] tiles
+  static constexpr int DVS = 16 * NW;       // state columns per workgroup
+  static constexpr int SV = DVS + 8;        // row stride of the V slice
+  // one buffer: Q, -Wm, KTg, A, TB, V (bf16), then g (log2), gamma [64 each] fp32
+  static constexpr int oQ = 0;
+  static constexpr int oWm = oQ + kC * SK;
+  static constexpr int oKT = oWm + kC * SK;
+  static constexpr int oA = oKT + D * SC;
+  static constexpr int oTB = oA + kC * SC;
+  static constexpr int oV = oTB + kC * SC;
+  static constexpr int nT = oV + kC * SV;
+  static constexpr int buf_bytes = nT * 2 + 2 * kC * 4;
+  static constexpr int bytes = 2 * buf_bytes;
+  static_assert((nT * 2) % 16 == 0, "16-byte tiles");
+};
+
+// LDS image of a dense [R][8 P] bf16 tile with a one-piece pad per row: slot
+// s = (P + 1) r + p holds piece p of row r; the pad slot repeats piece 0.
+template <int R, int P>
+__device__ __forceinline__ void dma_tile(const bf16* src, bf16* dst, int lane) {
+  static_assert((R * (P + 1)) % 64 == 0, "whole 1 KiB blocks");
+#pragma unroll
+  for (int n = 0; n < R * (P + 1) / 64; ++n) {
+    const int s = 64 * n + lane;
+    const int r = s / (P + 1);
+    const int p = s % (P + 1);
+    dma16(src + (size_t)(r * P + (p < P ? p : 0)) * 8, dst + 512 * n);
+  }
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * (NW + 1)) void gdn_scan_full_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ v, const bf16* __restrict__ w_tb,
+    const bf16* __restrict__ w_wm, const bf16* __restrict__ w_ktg, const bf16* __restrict__ w_a,
+    const float* __restrict__ w_g, bf16* __restrict__ o, float* __restrict__ state_out, int T_,
+    int H, int Hkv, int n_sink, int window, int flags) {
+  using SM = FullSmem<D, NW>;
+  constexpr int SK = SM::SK;
+  constexpr int SC = SM::SC;
+  constexpr int DVS = SM::DVS;
+  constexpr int MT = D / 16;             // 16-row tiles of the state
+  constexpr int P = D / 8;               // 16-byte pieces of a D-wide row
+
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  auto buf = [&](int b) { return reinterpret_cast<bf16*>(smem_raw + b * SM::buf_bytes); };
+
+  const int sp = blockIdx.x;             // column slice
+  const int h = blockIdx.y;
+  const int bi = blockIdx.z;
+  const int g = h / (H / Hkv);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = wave_id();
+  const int l16 = lane & 15;
+  const int lg = lane >> 4;
+  const int c0 = sp * DVS;
+  const int iend = T_ - window;          // stream tokens are [n_sink, iend)
+  const int nch = iend > n_sink ? (iend - n_sink + kC - 1) / kC : 0;
+  const size_t chain = (size_t)bi * H + h;
+
+  if (wv == NW) {
+    // ======================= loader wave
+    constexpr int PV = DVS / 8;                      // 16-byte pieces of a V slice row
+    static_assert((kC * (PV + 1)) % 64 == 0, "V slice shape");
+    auto stage = [&](int c, int b) {
+      bf16* B = buf(b);
+      const int i0 = n_sink + c * kC;
+      const int Cc = min(kC, iend - i0);
+      const size_t ci = chain * nch + c;
+      // query rows i0 + window + r and V rows i0 + r; rows past the stream
+      // repeat its last row (their outputs are never stored, and TB's
+      // columns for them are zero)
+      const bf16* q0 = q + ((size_t)(bi * T_ + i0 + window) * H + h) * D;
+#pragma unroll
+      for (int n = 0; n < kC * (P + 1) / 64; ++n) {
+        const int s = 64 * n + lane;
+        const int r = min(s / (P + 1), Cc - 1);
+        const int p = s % (P + 1);
+        dma16(q0 + (size_t)r * H * D + (p < P ? p : 0) * 8, B + SM::oQ + 512 * n);
+      }
+      const bf16* v0 = v + ((size_t)(bi * T_ + i0) * Hkv + g) * D + c0;
+#pragma unroll
+      for (int n = 0; n < kC * (PV + 1) / 64; ++n) {
+        const int s = 64 * n + lane;
+        const int r = min(s / (PV + 1), Cc - 1);
+        const int p = s % (PV + 1);
+        dma16(v0 + (size_t)r * Hkv * D + (p < PV ? p : 0) * 8, B + SM::oV + 512 * n);
+      }
+      dma_tile<kC, P>(w_wm + ci * (kC * D), B + SM::oWm, lane);
+      dma_tile<D, kC / 8>(w_ktg + ci * (D * kC), B + SM::oKT, lane);
+      dma_tile<kC, kC / 8>(w_a + ci * (kC * kC), B + SM::oA, lane);
+      dma_tile<kC, kC / 8>(w_tb + ci * (kC * kC), B + SM::oTB, lane);
+      float* gate = reinterpret_cast<float*>(B + SM::nT);
+      dma4(w_g + ci * (2 * kC) + lane, gate);
+      dma4(w_g + ci * (2 * kC) + 64 + lane, gate + 64);
+      __builtin_amdgcn_s_waitcnt(0);   // this buffer is complete in LDS
+    };
+    if (nch > 0) stage(0, 0);
+    for (int c = 0; c < nch; ++c) {
+      lds_barrier();                   // buffer c & 1 is handed to the compute waves
+      if (c + 1 < nch) stage(c + 1, (c + 1) & 1);
+    }
+    return;
+  }
+
+  // ======================= compute waves: state columns c0 + cw .. + 15
+  const int cw = 16 * wv;
+  f32x4 S[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) S[mt] = zero4();
+
+  for (int c = 0; c < nch; ++c) {
+    lds_barrier();                     // chunk c's buffer is complete
+    const bf16* B = buf(c & 1);
+    const bf16* Qs = B + SM::oQ;
+    const bf16* Wms = B + SM::oWm;
+    const bf16* KTs = B + SM::oKT;
+    const bf16* Aqs = B + SM::oA;
+    const bf16* TBs = B + SM::oTB;
+    const bf16* Vs = B + SM::oV;
+    const float* gam = reinterpret_cast<const float*>(B + SM::nT) + kC;
+    const int i0 = n_sink + c * kC;
+    const int Cc = min(kC, iend - i0);
+
+    Frag<bf16> sf[D / 32];
+#pragma unroll
+    for (int p = 0; p < D / 32; ++p) sf[p] = frag_from_acc<bf16>(S[2 * p], S[2 * p + 1]);
+
+    // O^T = S^T Q^T (operand slot j of lane group lg is d_k 32 p + 8 lg + j
+    // on both sides)
+    f32x4 ot[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) ot[rt] = zero4();
+#pragma unroll
+    for (int ph = 0; ph < D / 64; ++ph) {
+      Frag<bf16> qf[4][2];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) qf[rt][pp] = lds_frag8(&Qs[(16 * rt + l16) * SK + 64 * ph + 32 * pp + 8 * lg]);
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) ot[rt] = mfma(sf[2 * ph + pp], qf[rt][pp], ot[rt]);
+    }
+
+    // U = TB V - Wm S   (tokens x this wave's 16 columns)
+    f32x4 U[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) U[mt] = zero4();
+    {
+      // V operand of column cw + l16: tokens in acc order, gathered from the
+      // token-major V rows (slot j <-> token 32 p + 16 (j / 4) + 4 lg + j % 4)
+      Frag<bf16> vf[2], tf[4][2];
+      const unsigned short* vcol = reinterpret_cast<const unsigned short*>(Vs) + cw + l16;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        ushort8 x;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = vcol[(32 * p + 16 * (j / 4) + 4 * lg + j % 4) * SM::SV];
+        vf[p].v = __builtin_bit_cast(bf16x8, x);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) tf[mt][p] = lds_frag8(&TBs[(16 * mt + l16) * SC + 32 * p + 8 * lg]);
+      }
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) U[mt] = mfma(tf[mt][p], vf[p], U[mt]);
+    }
+#pragma unroll
+    for (int ph = 0; ph < D / 64; ++ph) {
+      Frag<bf16> wf[4][2];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) wf[mt][pp] = lds_frag8(&Wms[(16 * mt + l16) * SK + 64 * ph + 32 * pp + 8 * lg]);
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) U[mt] = mfma(wf[mt][pp], sf[2 * ph + pp], U[mt]);
+    }
+
+    // O^T: gamma of each query column on the S^T Q^T part, then + U^T A^T
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) ot[rt] *= gam[16 * rt + l16];
+    Frag<bf16> uf[2];
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) uf[pp] = frag_from_acc<bf16>(U[2 * pp], U[2 * pp + 1]);
+    {
+      Frag<bf16> af[4][2];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) af[rt][pp] = lds_frag8(&Aqs[(16 * rt + l16) * SC + 32 * pp + 8 * lg]);
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) ot[rt] = mfma(uf[pp], af[rt][pp], ot[rt]);
+    }
+
+    // S = gamma_C S + KTg U
+    const float gC = gam[kC - 1];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) S[mt] *= gC;
+#pragma unroll
+    for (int m4 = 0; m4 < MT / 4; ++m4) {
+      Frag<bf16> kf[4][2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) kf[i][pp] = lds_frag8(&KTs[(16 * (4 * m4 + i) + l16) * SC + 32 * pp + 8 * lg]);
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[4 * m4 + i] = mfma(kf[i][pp], uf[pp], S[4 * m4 + i]);
+    }
+
+    // store (or add) the chunk's linear output rows
+    if (flags & 1) {
+      const bool accumulate = (flags & 8) != 0;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int r = 16 * rt + l16;
+        if (r < Cc) {
+          bf16* orow = o + ((size_t)(bi * T_ + i0 + r + window) * H + h) * D + c0 + cw + 4 * lg;
+          f32x4 val = ot[rt];
+          if (accumulate) val += load4(orow);
+          store4(orow, val);
+        }
+      }
+    }
+  }
+
+  // linear-only overwrite: rows t < n_sink + window carry no linear output
+  constexpr int kThreads = 64 * NW;
+  if ((flags & 1) && !(flags & 2) && !(flags & 8)) {
+    const int rows = min(n_sink + window, T_);
+    for (int i = tid; i < rows * (DVS / 4); i += kThreads) {
+      const int t = i / (DVS / 4);
+      const int cc = (i % (DVS / 4)) * 4;
+      store4(o + ((size_t)(bi * T_ + t) * H + h) * D + c0 + cc, zero4());
+    }
+  }
+  if (flags & 4) {
+    float* Sg = state_out + chain * D * D;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Sg[(size_t)acc_pos(16 * mt + 4 * lg + i) * D + c0 + cw + l16] = S[mt][i];
+  }
+}
+
+template <int D, int NW>
+hipError_t launch_full_t(const PrefillArgs& p, hipStream_t s) {
+  using SM = FullSmem<D, NW>;
+  auto kern = gdn_scan_full_kernel<D, NW>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, SM::bytes);
+  if (e != hipSuccess) return e;
+  const int nch = gdn_stream_chunks(p.T, p.n_sink, p.window);
+  const GdnWorkspace w = gdn_workspace_layout(p.workspace, p.B, p.H, nch, D, sizeof(bf16), true);
+  const dim3 grid(D / SM::DVS, p.H, p.B);
+  hipLaunchKernelGGL(kern, grid, dim3(64 * (NW + 1)), SM::bytes, s, (const bf16*)p.q,
+                     (const bf16*)p.v, (const bf16*)w.tb, (const bf16*)w.wm, (const bf16*)w.ktg,
+                     (const bf16*)w.a, w.g, (bf16*)p.o, p.state_out, p.T, p.H, p.Hkv, p.n_sink,
+                     p.window, p.flags);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gdn_scan_full(const PrefillArgs& p, hipStream_t s) {
+  if (!p.bf16 || p.gla) return hipErrorInvalidValue;
+  if (p.D == 64) return launch_full_t<64, 4>(p, s);
+  if (p.D == 128) return launch_full_t<128, 4>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

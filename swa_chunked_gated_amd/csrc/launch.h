@@ -24,11 +24,11 @@ struct PrefillArgs {
 };
 
 // Workspace of the gated delta rule prefill, per (sequence, head, chunk), as
-// consecutive arrays (I/O element type, reduction index in acc order):
+// consecutive arrays (I/O element type; token reduction index in acc order):
 //   TB = Tm diag(b) [64][64]; then either (light preparation) TBG =
-//   Tm diag(b gamma) [64][64], or (full preparation) -Wm [64][D],
-//   K^T 2^{g_C - g} [D][64] and the scores A [64][64]; then g, gamma
-//   [2][64] fp32.
+//   Tm diag(b gamma) [64][64], or (full preparation, bf16) -Wm [64][D] with
+//   d_k in natural order, K^T 2^{g_C - g} [D][64] whose row r holds d_k index
+//   acc_pos(r), and the scores A [64][64]; then g, gamma [2][64] fp32.
 struct GdnWorkspace {
   void* tb;
   void* tbg;
@@ -38,10 +38,13 @@ struct GdnWorkspace {
   float* g;
   size_t bytes;
 };
-// Full preparation (everything state-independent precomputed) when the scan
-// alone cannot fill the GPU.
-bool gdn_full_prep(int B, int H, int D);
+// Full preparation (everything state-independent precomputed) for bf16 when
+// the scan alone cannot fill the GPU.
+bool gdn_full_prep(int B, int H, int D, int bf16);
 GdnWorkspace gdn_workspace_layout(void* base, int B, int H, int nch, int D, size_t elt, bool full);
+// State scan over a fully prepared workspace (bf16, d = 64 or 128), with a
+// loader wave streaming the next chunk's tiles into LDS.
+hipError_t launch_gdn_scan_full(const PrefillArgs& p, hipStream_t s);
 // Workspace of the GLA prefill: for each (sequence, head, chunk) Q 2^G
 // [64][D], (K 2^{G_C - G})^T [D][64], A [64][64] (I/O type, reduction index in
 // acc order) and 2^{G_C} [D] fp32, as four consecutive arrays.

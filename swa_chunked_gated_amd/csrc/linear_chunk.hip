@@ -22,14 +22,15 @@
 //   A = [s <= r] o (Q e^G)(K e^-G)^T,  O = (Q e^G) S0 + A V,
 //   S = e^{G_C} o_rows S0 + (K e^{G_C - G})^T V.
 //
-// Work split: one workgroup of 4 waves per (sequence, query head, column
-// slice of the state).  The state's d_v columns are independent in both
-// updates, so each wave owns 16 or 32 columns of S as fp32 MFMA accumulators
-// in registers for the whole sequence, and every S-dependent product of a
-// chunk is wave-local.  The S-independent chunk work (K K^T, Q K^T, the unit
-// lower-triangular inverse, Wm) is shared through LDS.  The inverse: 16x16
-// diagonal blocks by forward substitution in fp32, then the off-diagonal
-// blocks by block recursion on fp32 MFMA (exact fp32 products).
+// Work split: one workgroup per (sequence, query head, column slice of the
+// state).  The state's d_v columns are independent in both updates, so each
+// wave owns 16 columns of S as fp32 MFMA accumulators in registers for the
+// whole sequence, and every S-dependent product of a chunk is wave-local.
+// The chunk preparation kernels (gdn_prep.hip, gla_prep.hip) have already
+// produced the triangular solve (TB, TBG) and the gates (GDN) or every
+// state-independent tile (GLA); the GDN chunk's Q K^T scores and Wm are
+// formed here on MFMA and shared through LDS.  (bf16 GDN with too few chains
+// to fill the GPU runs gdn_scan_full.hip instead.)
 // Chunk c+1's inputs are loaded into registers while chunk c is computed.
 // Every LDS tile keeps its reduction dimension in acc order (see common.h),
 // so all MFMA operand reads are single 16-byte LDS accesses.
@@ -47,7 +48,7 @@ constexpr int kC = 64;          // chunk length
 __constant__ const int kTileM[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
 __constant__ const int kTileN[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 
-template <class T, int D, int NW, int DW, bool GLA, bool FULL>
+template <class T, int D, int NW, int DW, bool GLA>
 struct Smem {
   static constexpr int PAD = 16 / sizeof(T);
   static constexpr int SK = D + PAD;        // stride of [64][D] arrays
@@ -58,34 +59,31 @@ struct Smem {
   static constexpr int nVT = DVS * SC;
   static constexpr int nA = kC * SC;
   // element offsets in units of T (GLA keeps only Q 2^G, K^T 2^{G_C-G}, V^T, A)
-  // GDN with full preparation: Q, K^T 2^{g_C-g}, V^T, A, -Wm, TB (no K rows, no TBG)
   static constexpr int oK = 0;
-  static constexpr int oKT = oK + ((GLA || FULL) ? 0 : nK);
+  static constexpr int oKT = oK + (GLA ? 0 : nK);
   static constexpr int oQ = oKT + nKT;
   static constexpr int oVT = oQ + nK;
   static constexpr int oAq = oVT + nVT;
   static constexpr int oWm = oAq + nA;
   static constexpr int oTB = oWm + (GLA ? 0 : nK);
   static constexpr int oTBG = oTB + (GLA ? 0 : nA);
-  static constexpr int nT = oTBG + ((GLA || FULL) ? 0 : nA);
+  static constexpr int nT = oTBG + (GLA ? 0 : nA);
   static constexpr int bytesT = ((nT * (int)sizeof(T)) + 15) / 16 * 16;
   // fp32 part: GDN g (log2), gamma [64 each]; GLA 2^{G_C} [D]
   static constexpr int nGate = GLA ? D : 2 * kC;
   static constexpr int bytes = bytesT + 4 * nGate;
 };
 
-template <class T, int D, int NW, int DW, bool GLA, bool FULL>
+template <class T, int D, int NW, int DW, bool GLA>
 __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ w0, const T* __restrict__ w1, const T* __restrict__ w2,
-    const T* __restrict__ w3, const float* __restrict__ wf, T* __restrict__ o,
+    const float* __restrict__ wf, T* __restrict__ o,
     float* __restrict__ state_out, int T_, int H, int Hkv, int n_sink, int window, int flags) {
   // chunk preparation results (workspace), per (sequence, head, chunk):
   //   GDN, light: w0 = Tm diag(b), w1 = Tm diag(b gamma), wf = g (log2), gamma
-  //   GDN, full:  w0 = Tm diag(b), w1 = -Wm, w2 = K^T 2^{g_C - g}, w3 = A, wf = g, gamma
   //   GLA:        w0 = Q 2^G, w1 = (K 2^{G_C - G})^T, w2 = A, wf = 2^{G_C}
-  static_assert(!(GLA && FULL), "GLA always reads prepared tiles");
-  using SM = Smem<T, D, NW, DW, GLA, FULL>;
+  using SM = Smem<T, D, NW, DW, GLA>;
   constexpr int kThreads = 64 * NW;
   constexpr int SK = SM::SK;
   constexpr int SC = SM::SC;
@@ -156,12 +154,11 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
   // V (dword columns, both updates); GDN: K (dword columns), Q (16-byte row
   // pieces), TB / TBG and g, gamma from the workspace; GLA: Q 2^G, K^T 2^{G_C-G},
   // A and 2^{G_C} from the workspace
-  uint32_t pk[(GLA || FULL) ? 1 : TPT], pv[TPTV];
+  uint32_t pk[GLA ? 1 : TPT], pv[TPTV];
   V16 pq[NPQ];
   constexpr int NPT = GLA ? 1 : kC * kC / VEC / kThreads;
   static_assert(GLA || (kC * kC / VEC) % kThreads == 0, "TB staging");
-  V16 ptb[GLA ? NPK : NPT], ptbg[GLA ? NPA : (FULL ? NPQ : NPT)];
-  V16 pkt[FULL ? NPK : 1], pat[FULL ? NPA : 1];   // full preparation: K^T 2^{g_C-g}, A
+  V16 ptb[GLA ? NPK : NPT], ptbg[GLA ? NPA : NPT];
   f32x4 pgm = zero4();
   const size_t chain = (size_t)bi * H + h;
 
@@ -192,16 +189,14 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
       for (int n = 0; n < NPA; ++n) ptbg[n] = aa[tid + n * kThreads];
       if (tid < D / 4) pgm = reinterpret_cast<const f32x4*>(wf + ci * D)[tid];
     } else {
-      if constexpr (!FULL) {
-        const T* kp = k + ((size_t)(bi * T_ + i0 + kr0) * Hkv + g) * D + kdc * EPD;
-        if (full) {
+      const T* kp = k + ((size_t)(bi * T_ + i0 + kr0) * Hkv + g) * D + kdc * EPD;
+      if (full) {
 #pragma unroll
-          for (int j = 0; j < TPT; ++j) pk[j] = *reinterpret_cast<const uint32_t*>(kp + j * kvstride);
-        } else {
+        for (int j = 0; j < TPT; ++j) pk[j] = *reinterpret_cast<const uint32_t*>(kp + j * kvstride);
+      } else {
 #pragma unroll
-          for (int j = 0; j < TPT; ++j)
-            pk[j] = i0 + kr0 + j < iend ? *reinterpret_cast<const uint32_t*>(kp + j * kvstride) : 0u;
-        }
+        for (int j = 0; j < TPT; ++j)
+          pk[j] = i0 + kr0 + j < iend ? *reinterpret_cast<const uint32_t*>(kp + j * kvstride) : 0u;
       }
       const T* qp = q + ((size_t)(bi * T_ + i0 + window) * H + h) * D;
 #pragma unroll
@@ -219,21 +214,9 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
       const V16* tb = reinterpret_cast<const V16*>(w0 + ci * (kC * kC));
 #pragma unroll
       for (int n = 0; n < NPT; ++n) ptb[n] = tb[tid + n * kThreads];
-      if constexpr (FULL) {
-        const V16* wm = reinterpret_cast<const V16*>(w1 + ci * (kC * D));
-        const V16* ktg = reinterpret_cast<const V16*>(w2 + ci * (D * kC));
-        const V16* aa = reinterpret_cast<const V16*>(w3 + ci * (kC * kC));
+      const V16* tbg = reinterpret_cast<const V16*>(w1 + ci * (kC * kC));
 #pragma unroll
-        for (int n = 0; n < NPQ; ++n) ptbg[n] = wm[tid + n * kThreads];
-#pragma unroll
-        for (int n = 0; n < NPK; ++n) pkt[n] = ktg[tid + n * kThreads];
-#pragma unroll
-        for (int n = 0; n < NPA; ++n) pat[n] = aa[tid + n * kThreads];
-      } else {
-        const V16* tbg = reinterpret_cast<const V16*>(w1 + ci * (kC * kC));
-#pragma unroll
-        for (int n = 0; n < NPT; ++n) ptbg[n] = tbg[tid + n * kThreads];
-      }
+      for (int n = 0; n < NPT; ++n) ptbg[n] = tbg[tid + n * kThreads];
       if (tid < 2 * kC / 4) pgm = reinterpret_cast<const f32x4*>(wf + ci * (2 * kC))[tid];
     }
   };
@@ -261,15 +244,13 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
       }
       if (tid < D / 4) *reinterpret_cast<f32x4*>(&gate[4 * tid]) = pgm;
     } else {
-      if constexpr (!FULL) {
-        // K row-major (one dword per token, columns in acc order) and
-        // transposed (tokens in acc order, runs of 4)
+      // K row-major (one dword per token, columns in acc order) and
+      // transposed (tokens in acc order, runs of 4)
 #pragma unroll
-        for (int j = 0; j < TPT; ++j)
-          *reinterpret_cast<uint32_t*>(&Ks[(kr0 + j) * SK + acc_pos(kdc * EPD)]) = pk[j];
+      for (int j = 0; j < TPT; ++j)
+        *reinterpret_cast<uint32_t*>(&Ks[(kr0 + j) * SK + acc_pos(kdc * EPD)]) = pk[j];
 #pragma unroll
-        for (int e = 0; e < EPD; ++e) store_column_acc<T, TPT>(&KTs[(kdc * EPD + e) * SC], kr0, pk, e);
-      }
+      for (int e = 0; e < EPD; ++e) store_column_acc<T, TPT>(&KTs[(kdc * EPD + e) * SC], kr0, pk, e);
 #pragma unroll
       for (int n = 0; n < NPQ; ++n) {
         const int j = tid + n * kThreads;
@@ -292,24 +273,7 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
         const int r = j / (kC / VEC);
         const int pc = (j % (kC / VEC)) * VEC;      // already in acc order
         *reinterpret_cast<V16*>(&TBs[r * SC + pc]) = ptb[n];
-        if constexpr (!FULL) *reinterpret_cast<V16*>(&TBGs[r * SC + pc]) = ptbg[n];
-      }
-      if constexpr (FULL) {
-#pragma unroll
-        for (int n = 0; n < NPQ; ++n) {
-          const int j = tid + n * kThreads;
-          *reinterpret_cast<V16*>(&Wms[(j / (D / VEC)) * SK + (j % (D / VEC)) * VEC]) = ptbg[n];
-        }
-#pragma unroll
-        for (int n = 0; n < NPK; ++n) {
-          const int j = tid + n * kThreads;
-          *reinterpret_cast<V16*>(&KTs[(j / (kC / VEC)) * SC + (j % (kC / VEC)) * VEC]) = pkt[n];
-        }
-#pragma unroll
-        for (int n = 0; n < NPA; ++n) {
-          const int j = tid + n * kThreads;
-          *reinterpret_cast<V16*>(&Aqs[(j / (kC / VEC)) * SC + (j % (kC / VEC)) * VEC]) = pat[n];
-        }
+        *reinterpret_cast<V16*>(&TBGs[r * SC + pc]) = ptbg[n];
       }
       if (tid < 2 * kC / 4) *reinterpret_cast<f32x4*>(&gate[4 * tid]) = pgm;
     }
@@ -325,7 +289,7 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
     lds_barrier();
     if (c + 1 < nch) prefetch(c + 1);
 
-    if constexpr (!GLA && !FULL) {
+    if constexpr (!GLA) {
       const float* lgs = gate;
       // ---- Q K^T -> A (decayed, masked s <= r) on the 10 lower 16x16 tiles;
       // the rest of the chunk's state-independent work comes from the chunk
@@ -518,8 +482,7 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           uf[pp][nt] = frag_from_acc<T>(U[2 * pp][nt], U[2 * pp + 1][nt]);
-          // with full preparation the factors live in K^T 2^{g_C - g}
-          if constexpr (!FULL) us[pp][nt] = frag_from_acc_scaled<T>(U[2 * pp][nt], U[2 * pp + 1][nt], s0, s1);
+          us[pp][nt] = frag_from_acc_scaled<T>(U[2 * pp][nt], U[2 * pp + 1][nt], s0, s1);
         }
       }
       {
@@ -557,7 +520,7 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
           for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
-              S[4 * m4 + i][nt] = mfma(kf[i][pp], FULL ? uf[pp][nt] : us[pp][nt], S[4 * m4 + i][nt]);
+              S[4 * m4 + i][nt] = mfma(kf[i][pp], us[pp][nt], S[4 * m4 + i][nt]);
       }
     }
 
@@ -602,10 +565,10 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
   }
 }
 
-template <class T, int D, int NW, int DW, bool GLA, bool FULL>
+template <class T, int D, int NW, int DW, bool GLA>
 hipError_t launch_linear_t(const PrefillArgs& p, hipStream_t s) {
-  using SM = Smem<T, D, NW, DW, GLA, FULL>;
-  auto kern = linear_chunk_kernel<T, D, NW, DW, GLA, FULL>;
+  using SM = Smem<T, D, NW, DW, GLA>;
+  auto kern = linear_chunk_kernel<T, D, NW, DW, GLA>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, SM::bytes);
   if (e != hipSuccess) return e;
   const dim3 grid(D / SM::DVS, p.H, p.B);
@@ -613,7 +576,6 @@ hipError_t launch_linear_t(const PrefillArgs& p, hipStream_t s) {
   const T* w0;
   const T* w1;
   const T* w2 = nullptr;
-  const T* w3 = nullptr;
   const float* wf;
   if (GLA) {
     const GlaWorkspace w = gla_workspace_layout(p.workspace, p.B, p.H, nch, D, sizeof(T));
@@ -622,27 +584,21 @@ hipError_t launch_linear_t(const PrefillArgs& p, hipStream_t s) {
     w2 = (const T*)w.a;
     wf = w.egc;
   } else {
-    const GdnWorkspace w = gdn_workspace_layout(p.workspace, p.B, p.H, nch, D, sizeof(T), FULL);
+    const GdnWorkspace w = gdn_workspace_layout(p.workspace, p.B, p.H, nch, D, sizeof(T), false);
     w0 = (const T*)w.tb;
-    w1 = (const T*)(FULL ? w.wm : w.tbg);
-    w2 = (const T*)w.ktg;
-    w3 = (const T*)w.a;
+    w1 = (const T*)w.tbg;
     wf = w.g;
   }
   hipLaunchKernelGGL(kern, grid, dim3(64 * NW), SM::bytes, s, (const T*)p.q, (const T*)p.k,
-                     (const T*)p.v, w0, w1, w2, w3, wf, (T*)p.o, p.state_out, p.T, p.H, p.Hkv,
+                     (const T*)p.v, w0, w1, w2, wf, (T*)p.o, p.state_out, p.T, p.H, p.Hkv,
                      p.n_sink, p.window, p.flags);
   return hipGetLastError();
 }
 
 template <class T, int D, int NW, bool GLA>
 hipError_t launch_linear_f(const PrefillArgs& p, hipStream_t s) {
-  if constexpr (GLA) {
-    return launch_linear_t<T, D, NW, 16, true, false>(p, s);
-  } else {
-    return gdn_full_prep(p.B, p.H, p.D) ? launch_linear_t<T, D, NW, 16, false, true>(p, s)
-                                        : launch_linear_t<T, D, NW, 16, false, false>(p, s);
-  }
+  if (!GLA && gdn_full_prep(p.B, p.H, p.D, p.bf16)) return launch_gdn_scan_full(p, s);
+  return launch_linear_t<T, D, NW, 16, GLA>(p, s);
 }
 
 // 16 state columns per wave.  d = 128: one workgroup of 8 waves per chain

@@ -69,7 +69,7 @@ def test_workspace_query(lib):
     # plus 128 fp32 gate values
     def gdn_bytes(B, T, H, d, elt, n=64):
         nch = -(-(T - n) // 64)
-        full = B * H * (2 if d == 128 else 1) < 256
+        full = elt == 2 and B * H * (2 if d == 128 else 1) < 256     # bf16, few chains
         tiles = (64 * 64 + 64 * d + d * 64 + 64 * 64) if full else 2 * 64 * 64
         return B * H * nch * (tiles * elt + 512)
     assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 3) == (OK, gdn_bytes(1, 4096, 32, 128, 2))
