@@ -65,20 +65,6 @@ struct FullSmem {
   static_assert((nT * 2) % 16 == 0, "16-byte tiles");
 };
 
-// LDS image of a dense [R][8 P] bf16 tile with a one-piece pad per row: slot
-// s = (P + 1) r + p holds piece p of row r; the pad slot repeats piece 0.
-template <int R, int P>
-__device__ __forceinline__ void dma_tile(const bf16* src, bf16* dst, int lane) {
-  static_assert((R * (P + 1)) % 64 == 0, "whole 1 KiB blocks");
-#pragma unroll
-  for (int n = 0; n < R * (P + 1) / 64; ++n) {
-    const int s = 64 * n + lane;
-    const int r = s / (P + 1);
-    const int p = s % (P + 1);
-    dma16(src + (size_t)(r * P + (p < P ? p : 0)) * 8, dst + 512 * n);
-  }
-}
-
 template <int D, int NW>
 __global__ __launch_bounds__(64 * (NW + 1)) void gdn_scan_full_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ v, const bf16* __restrict__ w_tb,
@@ -111,36 +97,86 @@ __global__ __launch_bounds__(64 * (NW + 1)) void gdn_scan_full_kernel(
 
   if (wv == NW) {
     // ======================= loader wave
-    constexpr int PV = DVS / 8;                      // 16-byte pieces of a V slice row
-    static_assert((kC * (PV + 1)) % 64 == 0, "V slice shape");
+    // Every LDS image is whole 1 KiB blocks of 16-byte slots; slot s = 64 n +
+    // lane of block n holds piece s % (P + 1) of row s / (P + 1) (the last
+    // piece of a row is padding and repeats piece 0).  The per-lane byte
+    // offsets of the source pieces are the same for every chunk, so they are
+    // formed once here and each load is a uniform base plus a lane offset.
+    constexpr int PV = DVS / 8;                      // pieces of a V slice row
+    constexpr int NQ = kC * (P + 1) / 64;            // blocks of the Q and -Wm images
+    constexpr int NV = kC * (PV + 1) / 64;           // blocks of the V image
+    constexpr int NK = D * 9 / 64;                   // blocks of the KTg image ([D][64])
+    constexpr int NS = kC * 9 / 64;                  // blocks of the TB and A images
+    static_assert((kC * (PV + 1)) % 64 == 0 && (D * 9) % 64 == 0, "whole 1 KiB blocks");
+    const size_t qrow = (size_t)H * D * 2;           // bytes between query rows
+    const size_t vrow = (size_t)Hkv * D * 2;         // bytes between V rows
+    auto piece = [&](int n, int pp, int& r, int& p) {
+      const int s = 64 * n + lane;
+      r = s / (pp + 1);
+      p = s % (pp + 1);
+      if (p == pp) p = 0;
+    };
+    uint32_t oq[NQ], ow[NQ], ov[NV], ok[NK];
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+      int r, p;
+      piece(n, P, r, p);
+      oq[n] = (uint32_t)(r * qrow + p * 16);
+      ow[n] = (uint32_t)((r * P + p) * 16);
+    }
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+      int r, p;
+      piece(n, PV, r, p);
+      ov[n] = (uint32_t)(r * vrow + p * 16);
+    }
+#pragma unroll
+    for (int n = 0; n < NK; ++n) {
+      int r, p;
+      piece(n, 8, r, p);
+      ok[n] = (uint32_t)((r * 8 + p) * 16);
+    }
     auto stage = [&](int c, int b) {
       bf16* B = buf(b);
       const int i0 = n_sink + c * kC;
       const int Cc = min(kC, iend - i0);
       const size_t ci = chain * nch + c;
-      // query rows i0 + window + r and V rows i0 + r; rows past the stream
-      // repeat its last row (their outputs are never stored, and TB's
-      // columns for them are zero)
-      const bf16* q0 = q + ((size_t)(bi * T_ + i0 + window) * H + h) * D;
+      // query rows i0 + window + r and V rows i0 + r; in a partial chunk the
+      // rows past the stream repeat its last row (their outputs are never
+      // stored, and TB's columns for them are zero)
+      const char* qb = reinterpret_cast<const char*>(q + ((size_t)(bi * T_ + i0 + window) * H + h) * D);
+      const char* vb = reinterpret_cast<const char*>(v + ((size_t)(bi * T_ + i0) * Hkv + g) * D + c0);
+      if (Cc == kC) {
 #pragma unroll
-      for (int n = 0; n < kC * (P + 1) / 64; ++n) {
-        const int s = 64 * n + lane;
-        const int r = min(s / (P + 1), Cc - 1);
-        const int p = s % (P + 1);
-        dma16(q0 + (size_t)r * H * D + (p < P ? p : 0) * 8, B + SM::oQ + 512 * n);
-      }
-      const bf16* v0 = v + ((size_t)(bi * T_ + i0) * Hkv + g) * D + c0;
+        for (int n = 0; n < NQ; ++n) dma16(qb + oq[n], B + SM::oQ + 512 * n);
 #pragma unroll
-      for (int n = 0; n < kC * (PV + 1) / 64; ++n) {
-        const int s = 64 * n + lane;
-        const int r = min(s / (PV + 1), Cc - 1);
-        const int p = s % (PV + 1);
-        dma16(v0 + (size_t)r * Hkv * D + (p < PV ? p : 0) * 8, B + SM::oV + 512 * n);
+        for (int n = 0; n < NV; ++n) dma16(vb + ov[n], B + SM::oV + 512 * n);
+      } else {
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+          int r, p;
+          piece(n, P, r, p);
+          dma16(qb + min(r, Cc - 1) * qrow + p * 16, B + SM::oQ + 512 * n);
+        }
+#pragma unroll
+        for (int n = 0; n < NV; ++n) {
+          int r, p;
+          piece(n, PV, r, p);
+          dma16(vb + min(r, Cc - 1) * vrow + p * 16, B + SM::oV + 512 * n);
+        }
       }
-      dma_tile<kC, P>(w_wm + ci * (kC * D), B + SM::oWm, lane);
-      dma_tile<D, kC / 8>(w_ktg + ci * (D * kC), B + SM::oKT, lane);
-      dma_tile<kC, kC / 8>(w_a + ci * (kC * kC), B + SM::oA, lane);
-      dma_tile<kC, kC / 8>(w_tb + ci * (kC * kC), B + SM::oTB, lane);
+      const char* wb = reinterpret_cast<const char*>(w_wm + ci * (kC * D));
+      const char* kb = reinterpret_cast<const char*>(w_ktg + ci * (D * kC));
+      const char* ab = reinterpret_cast<const char*>(w_a + ci * (kC * kC));
+      const char* tb = reinterpret_cast<const char*>(w_tb + ci * (kC * kC));
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) dma16(wb + ow[n], B + SM::oWm + 512 * n);
+#pragma unroll
+      for (int n = 0; n < NK; ++n) dma16(kb + ok[n], B + SM::oKT + 512 * n);
+#pragma unroll
+      for (int n = 0; n < NS; ++n) dma16(ab + ok[n], B + SM::oA + 512 * n);
+#pragma unroll
+      for (int n = 0; n < NS; ++n) dma16(tb + ok[n], B + SM::oTB + 512 * n);
       float* gate = reinterpret_cast<float*>(B + SM::nT);
       dma4(w_g + ci * (2 * kC) + lane, gate);
       dma4(w_g + ci * (2 * kC) + 64 + lane, gate + 64);
