@@ -65,13 +65,14 @@ struct FullSmem {
   static_assert((nT * 2) % 16 == 0, "16-byte tiles");
 };
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * (NW + 1)) void gdn_scan_full_kernel(
+template <int D, int NW, int NL>
+__global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ v, const bf16* __restrict__ w_tb,
     const bf16* __restrict__ w_wm, const bf16* __restrict__ w_ktg, const bf16* __restrict__ w_a,
     const float* __restrict__ w_g, bf16* __restrict__ o, float* __restrict__ state_out, int T_,
     int H, int Hkv, int n_sink, int window, int flags) {
   using SM = FullSmem<D, NW>;
+  static_assert(NL == 1 || NL == 2, "one or two loader waves");
   constexpr int SK = SM::SK;
   constexpr int SC = SM::SC;
   constexpr int DVS = SM::DVS;
@@ -95,7 +96,8 @@ __global__ __launch_bounds__(64 * (NW + 1)) void gdn_scan_full_kernel(
   const int nch = iend > n_sink ? (iend - n_sink + kC - 1) / kC : 0;
   const size_t chain = (size_t)bi * H + h;
 
-  if (wv == NW) {
+  if (wv >= NW) {
+    const int ld = wv - NW;                        // loader index: splits the tiles
     // ======================= loader wave
     // Every LDS image is whole 1 KiB blocks of 16-byte slots; slot s = 64 n +
     // lane of block n holds piece s % (P + 1) of row s / (P + 1) (the last
@@ -146,40 +148,46 @@ __global__ __launch_bounds__(64 * (NW + 1)) void gdn_scan_full_kernel(
       // stored, and TB's columns for them are zero)
       const char* qb = reinterpret_cast<const char*>(q + ((size_t)(bi * T_ + i0 + window) * H + h) * D);
       const char* vb = reinterpret_cast<const char*>(v + ((size_t)(bi * T_ + i0) * Hkv + g) * D + c0);
-      if (Cc == kC) {
+      if (ld == 0) {
+        if (Cc == kC) {
 #pragma unroll
-        for (int n = 0; n < NQ; ++n) dma16(qb + oq[n], B + SM::oQ + 512 * n);
+          for (int n = 0; n < NQ; ++n) dma16(qb + oq[n], B + SM::oQ + 512 * n);
 #pragma unroll
-        for (int n = 0; n < NV; ++n) dma16(vb + ov[n], B + SM::oV + 512 * n);
-      } else {
+          for (int n = 0; n < NV; ++n) dma16(vb + ov[n], B + SM::oV + 512 * n);
+        } else {
 #pragma unroll
-        for (int n = 0; n < NQ; ++n) {
-          int r, p;
-          piece(n, P, r, p);
-          dma16(qb + min(r, Cc - 1) * qrow + p * 16, B + SM::oQ + 512 * n);
-        }
+          for (int n = 0; n < NQ; ++n) {
+            int r, p;
+            piece(n, P, r, p);
+            dma16(qb + min(r, Cc - 1) * qrow + p * 16, B + SM::oQ + 512 * n);
+          }
 #pragma unroll
-        for (int n = 0; n < NV; ++n) {
-          int r, p;
-          piece(n, PV, r, p);
-          dma16(vb + min(r, Cc - 1) * vrow + p * 16, B + SM::oV + 512 * n);
+          for (int n = 0; n < NV; ++n) {
+            int r, p;
+            piece(n, PV, r, p);
+            dma16(vb + min(r, Cc - 1) * vrow + p * 16, B + SM::oV + 512 * n);
+          }
         }
       }
       const char* wb = reinterpret_cast<const char*>(w_wm + ci * (kC * D));
       const char* kb = reinterpret_cast<const char*>(w_ktg + ci * (D * kC));
       const char* ab = reinterpret_cast<const char*>(w_a + ci * (kC * kC));
       const char* tb = reinterpret_cast<const char*>(w_tb + ci * (kC * kC));
+      if (ld == NL - 1) {
 #pragma unroll
-      for (int n = 0; n < NQ; ++n) dma16(wb + ow[n], B + SM::oWm + 512 * n);
+        for (int n = 0; n < NQ; ++n) dma16(wb + ow[n], B + SM::oWm + 512 * n);
 #pragma unroll
-      for (int n = 0; n < NK; ++n) dma16(kb + ok[n], B + SM::oKT + 512 * n);
+        for (int n = 0; n < NK; ++n) dma16(kb + ok[n], B + SM::oKT + 512 * n);
+      }
+      if (ld == 0) {
 #pragma unroll
-      for (int n = 0; n < NS; ++n) dma16(ab + ok[n], B + SM::oA + 512 * n);
+        for (int n = 0; n < NS; ++n) dma16(ab + ok[n], B + SM::oA + 512 * n);
 #pragma unroll
-      for (int n = 0; n < NS; ++n) dma16(tb + ok[n], B + SM::oTB + 512 * n);
-      float* gate = reinterpret_cast<float*>(B + SM::nT);
-      dma4(w_g + ci * (2 * kC) + lane, gate);
-      dma4(w_g + ci * (2 * kC) + 64 + lane, gate + 64);
+        for (int n = 0; n < NS; ++n) dma16(tb + ok[n], B + SM::oTB + 512 * n);
+        float* gate = reinterpret_cast<float*>(B + SM::nT);
+        dma4(w_g + ci * (2 * kC) + lane, gate);
+        dma4(w_g + ci * (2 * kC) + 64 + lane, gate + 64);
+      }
       __builtin_amdgcn_s_waitcnt(0);   // this buffer is complete in LDS
     };
     if (nch > 0) stage(0, 0);
@@ -337,16 +345,16 @@ __global__ __launch_bounds__(64 * (NW + 1)) void gdn_scan_full_kernel(
   }
 }
 
-template <int D, int NW>
+template <int D, int NW, int NL>
 hipError_t launch_full_t(const PrefillArgs& p, hipStream_t s) {
   using SM = FullSmem<D, NW>;
-  auto kern = gdn_scan_full_kernel<D, NW>;
+  auto kern = gdn_scan_full_kernel<D, NW, NL>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, SM::bytes);
   if (e != hipSuccess) return e;
   const int nch = gdn_stream_chunks(p.T, p.n_sink, p.window);
   const GdnWorkspace w = gdn_workspace_layout(p.workspace, p.B, p.H, nch, D, sizeof(bf16), true);
   const dim3 grid(D / SM::DVS, p.H, p.B);
-  hipLaunchKernelGGL(kern, grid, dim3(64 * (NW + 1)), SM::bytes, s, (const bf16*)p.q,
+  hipLaunchKernelGGL(kern, grid, dim3(64 * (NW + NL)), SM::bytes, s, (const bf16*)p.q,
                      (const bf16*)p.v, (const bf16*)w.tb, (const bf16*)w.wm, (const bf16*)w.ktg,
                      (const bf16*)w.a, w.g, (bf16*)p.o, p.state_out, p.T, p.H, p.Hkv, p.n_sink,
                      p.window, p.flags);
@@ -357,8 +365,8 @@ hipError_t launch_full_t(const PrefillArgs& p, hipStream_t s) {
 
 hipError_t launch_gdn_scan_full(const PrefillArgs& p, hipStream_t s) {
   if (!p.bf16 || p.gla) return hipErrorInvalidValue;
-  if (p.D == 64) return launch_full_t<64, 4>(p, s);
-  if (p.D == 128) return launch_full_t<128, 4>(p, s);
+  if (p.D == 64) return launch_full_t<64, 4, 2>(p, s);
+  if (p.D == 128) return launch_full_t<128, 4, 2>(p, s);
   return hipErrorInvalidValue;
 }
 
