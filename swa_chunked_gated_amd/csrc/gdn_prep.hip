@@ -72,10 +72,10 @@ __device__ __forceinline__ float wave_prefix_sum(float x, int lane) {
 
 // (I + L)^-1 in place for the strictly lower 64 x 64 L in Lf (fp32, unit
 // diagonal implied, upper part zero), by one wave: 16x16 diagonal blocks by
-// column-oriented forward substitution (lane = block x column; once x_s is
-// final it is subtracted from every later row, a 16-step dependent chain),
-// then the off-diagonal blocks by block recursion on fp32 MFMA (exact fp32
-// products).  A wave's LDS operations complete in program order; lds_barrier
+// forward substitution (lane = block x column j; row r of the block's inverse
+// column is e_j[r] - sum_{s<r} L[r][s] x[s], with L's rows read as 16-byte
+// pieces), then the off-diagonal blocks by block recursion on fp32 MFMA
+// (exact fp32 products).  A wave's LDS operations complete in program order; lds_barrier
 // (which for a one-wave workgroup only waits on LDS) marks the phases.
 __device__ __forceinline__ void unit_lower_inverse_wave(float* Lf, int lane) {
   const int l16 = lane & 15;
@@ -86,11 +86,19 @@ __device__ __forceinline__ void unit_lower_inverse_wave(float* Lf, int lane) {
     float* Lb = Lf + 16 * blk * kSL + 16 * blk;
     float x[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = r == j ? 1.f : 0.f;
+    for (int r = 0; r < 16; ++r) {
+      float lr[16];
 #pragma unroll
-    for (int s2 = 0; s2 < 15; ++s2)
+      for (int q4 = 0; q4 < (r + 3) / 4; ++q4) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(&Lb[r * kSL + 4 * q4]);
 #pragma unroll
-      for (int r = s2 + 1; r < 16; ++r) x[r] -= Lb[r * kSL + s2] * x[s2];
+        for (int e = 0; e < 4; ++e) lr[4 * q4 + e] = t[e];
+      }
+      float acc = r == j ? 1.f : 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < r; ++s2) acc -= lr[s2] * x[s2];
+      x[r] = acc;
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) Lb[r * kSL + j] = x[r];
   }
@@ -187,13 +195,19 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(
   const T* kbase = k + ((size_t)(bi * T_ + i0) * Hkv + g) * D;
   const T* qbase = q + ((size_t)(bi * T_ + i0 + window) * H + h) * D;
 
+  // ---- this chunk's gates first (a = 1, b = 0 past the stream end)
+  const int tok = i0 + lane;
+  const float av = tok < iend ? a[(size_t)(bi * T_ + tok) * H + h] : 1.f;
+  const float bv = tok < iend ? b[(size_t)(bi * T_ + tok) * H + h] : 0.f;
+
   // ---- operand pieces: lane holds rows 16 mt + l16, dims 32 p + 8 lg .. +7
   V16 kr[4][KS][QV];
   V16 qr[FULL ? 4 : 1][FULL ? KS : 1][QV];
+  const bool whole = i0 + kC <= iend;          // uniform: no row past the stream
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int r = 16 * mt + l16;
-    const bool live = i0 + r < iend;
+    const bool live = whole || i0 + r < iend;
 #pragma unroll
     for (int p = 0; p < KS; ++p)
 #pragma unroll
@@ -218,13 +232,21 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(
     return frag_from8<T>(x);
   };
 
-  // ---- zero the solve buffer; gates: g = inclusive cumsum of log2 a
-  // (a = 1 past the stream end), gamma = 2^g, b
+  // ---- zero the solve buffer (and the score tile, whose strictly upper
+  // 16x16 tiles stay zero); gates: g = inclusive cumsum of log2 a, gamma =
+  // 2^g, b
+#pragma unroll
   for (int i = lane; i < SM::nL / 4; i += 64) reinterpret_cast<f32x4*>(Lf)[i] = zero4();
+  if constexpr (FULL) {
+#pragma unroll
+    for (int i = lane; i < kC * SC / EPC; i += 64) {
+      V16 z;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) z[e] = from_f32<T>(0.f);
+      reinterpret_cast<V16*>(As)[i] = z;
+    }
+  }
   {
-    const int tok = i0 + lane;
-    const float av = tok < iend ? a[(size_t)(bi * T_ + tok) * H + h] : 1.f;
-    const float bv = tok < iend ? b[(size_t)(bi * T_ + tok) * H + h] : 0.f;
     const float x = wave_prefix_sum(__builtin_amdgcn_logf(av), lane);
     lgs[lane] = x;
     gam[lane] = __builtin_amdgcn_exp2f(x);
@@ -261,15 +283,7 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(
     }
   }
   if constexpr (FULL) {
-    // strictly upper tiles of A are zero; K^T (tokens in acc order) from the
-    // row pieces
-    for (int i = lane; i < 6 * 256; i += 64) {
-      const int pr = i / 256;
-      const int e = i % 256;
-      const int mt = pr < 3 ? 0 : (pr < 5 ? 1 : 2);
-      const int nt = pr < 3 ? pr + 1 : (pr < 5 ? pr - 1 : 3);
-      As[(16 * mt + e / 16) * SC + acc_pos(16 * nt + e % 16)] = from_f32<T>(0.f);
-    }
+    // K^T (tokens in acc order) from the row pieces
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -284,6 +298,7 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(
   // ---- TB = Tm diag(b) (and TBG = Tm diag(b gamma)): row r, columns
   // s0..s0+3 at positions acc_pos(s0)..+3 of the row
   T* tb = wtb + ci * (kC * kC);
+#pragma unroll 4
   for (int i = lane; i < kC * kC / 4; i += 64) {
     const int r = i >> 4;
     const int s0 = (i & 15) * 4;
@@ -319,6 +334,7 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(
     // state row order of the scan's accumulators) and A [64][64], 16-byte pieces
     T* ktg = wktg + ci * (D * kC);
     T* aa = wa + ci * (kC * kC);
+#pragma unroll 4
     for (int i = lane; i < D * (kC / EPC); i += 64) {
       const int r = i / (kC / EPC);
       const int pc = (i % (kC / EPC)) * EPC;
@@ -328,6 +344,7 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(
       for (int e = 0; e < EPC; ++e) y[e] = from_f32<T>(to_f32(x[e]) * fac[pc + e]);
       *reinterpret_cast<V16*>(ktg + r * kC + pc) = y;
     }
+#pragma unroll
     for (int i = lane; i < kC * (kC / EPC); i += 64) {
       const int r = i / (kC / EPC);
       const int pc = (i % (kC / EPC)) * EPC;
