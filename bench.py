@@ -136,13 +136,13 @@ def bench_main(steps, warmup):
     swa_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(warmup, n)]))
     f_lin, f_swa = gdn_flops(w), swa_flops(w)
     if lin_ms >= swa_ms:
-        dom = ("gdn_prep_kernel+linear_chunk_kernel", f_lin, lin_ms, LINEAR_SOURCES)
+        dom = (LINEAR_KERNELS, f_lin, lin_ms, LINEAR_SOURCES)
     else:
         dom = ("swa_kernel", f_swa, swa_ms, SWA_SOURCES)
     achieved = dom[1] / (dom[2] * 1e-3)
     res = {
         "w": w, "sec": sec,
-        "kernels_ms": {"gdn_prep_kernel+linear_chunk_kernel": lin_ms, "swa_kernel": swa_ms},
+        "kernels_ms": {LINEAR_KERNELS: lin_ms, "swa_kernel": swa_ms},
         "roofline": {
             "kernel": dom[0], "bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,
             "unit": "TFLOP/s", "frac": achieved / PEAK_BF16,
@@ -203,8 +203,11 @@ def kernel_sources_sha256(files):
     return h.hexdigest()
 
 
-LINEAR_SOURCES = ("swa_chunked_gated_amd/csrc/gdn_prep.hip", "swa_chunked_gated_amd/csrc/linear_chunk.hip",
-                  "swa_chunked_gated_amd/csrc/common.h")
+LINEAR_SOURCES = ("swa_chunked_gated_amd/csrc/gdn_prep.hip", "swa_chunked_gated_amd/csrc/gdn_scan_full.hip",
+                  "swa_chunked_gated_amd/csrc/linear_chunk.hip", "swa_chunked_gated_amd/csrc/common.h")
+# the linear launch of the LLaMA-shaped layer (32 chains): chunk preparation,
+# then the loader-wave state scan
+LINEAR_KERNELS = "gdn_prep_kernel+gdn_scan_full_kernel"
 SWA_SOURCES = ("swa_chunked_gated_amd/csrc/swa.hip", "swa_chunked_gated_amd/csrc/common.h")
 DECODE_SOURCES = ("swa_chunked_gated_amd/csrc/decode.hip", "swa_chunked_gated_amd/csrc/common.h")
 # one decode step is three launches: softmax branch, state update, cache commit

@@ -37,7 +37,8 @@
  *   - Every pointer is a DEVICE pointer owned by the caller; the library never
  *     allocates, frees or retains it, and never synchronises.
  *   - Tensors are dense, row-major (last index fastest), in the layouts given.
- *     Outputs must not alias inputs.
+ *     Outputs must not alias inputs.  Every tensor pointer is 16-byte aligned
+ *     (GDN_EINVAL otherwise): the kernels move rows in 16-byte pieces.
  *   - q/k/v/o and the K/V cache use `dtype` (GDN_F32 or GDN_BF16); gates a, b
  *     and states are always fp32.  d_k = d_v = d in {64, 128}.
  *   - `stream` is a hipStream_t (NULL: the null stream).  Calls are
@@ -103,10 +104,13 @@ int gdn_hybrid_last_hip_error(void);
  * computed for all chunks in parallel and stored there, so the sequential
  * scan over chunks only does the state-dependent products.  With
  * nch = ceil((T - window - n_sink) / 64) and elt the size of `dtype`:
- *   GDN_DELTA: B * H * nch * (2 * 64 * 64 * elt + 128 * 4) bytes (the inverse
- *     of the chunk's unit lower-triangular system scaled by b and by
- *     b * gamma, and the gate prefix sums; about 34 MB for B=1, H=32,
- *     T=4096, bf16);
+ *   GDN_DELTA, few chains (bf16 and B * H * dk / 64 < 256): B * H * nch *
+ *     ((2 * 64 * 64 + 2 * 64 * dk) * elt + 128 * 4) bytes (the inverse of the
+ *     chunk's unit lower-triangular system scaled by b, Wm, the decayed K^T,
+ *     the decayed causal scores, the gate prefix sums: every
+ *     state-independent chunk product; about 100 MB for B=1, H=32, T=4096);
+ *   GDN_DELTA otherwise: B * H * nch * (2 * 64 * 64 * elt + 128 * 4) bytes
+ *     (the inverse scaled by b and by b * gamma, the gate prefix sums);
  *   GDN_GLA: B * H * nch * ((2 * 64 * dk + 64 * 64) * elt + dk * 4) bytes
  *     (gate-scaled Q and K^T, the intra-chunk scores, the chunk decay).
  * Errors: GDN_EINVAL if bytes is NULL or the shape arguments are invalid.

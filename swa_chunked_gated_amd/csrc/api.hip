@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <initializer_list>
 
 #include "launch.h"
 
@@ -30,6 +31,15 @@ bool dims_ok(int B, int T, int H, int Hkv, int dk, int dv, int n_sink, int windo
   if ((int64_t)B * T >= (int64_t)1 << 31) return false;
   if ((int64_t)B * T * H * dk >= (int64_t)1 << 40) return false;
   if ((int64_t)n_sink + window >= (int64_t)1 << 30) return false;
+  return true;
+}
+
+// Tensor arguments are read and written with 16-byte vector accesses: every
+// pointer must be 16-byte aligned (NULL passes; whether a NULL is allowed is
+// checked separately).
+bool aligned16(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (((uintptr_t)p & 15u) != 0) return false;
   return true;
 }
 
@@ -92,6 +102,7 @@ int gdn_hybrid_prefill(const void* q, const void* k, const void* v, const float*
   if (needs_rec && !a) return GDN_EINVAL;
   if (needs_rec && update == GDN_DELTA && !b) return GDN_EINVAL;
   if (wst && !state_out) return GDN_EINVAL;
+  if (!aligned16({q, k, v, a, b, o, state_out})) return GDN_EINVAL;
   if (needs_rec && dtype == GDN_F32 && dk != 64) return GDN_EUNSUPPORTED;
   const size_t need = prefill_workspace_bytes(B, T, H, dk, n_sink, window, dtype, update, flags);
   if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_EWORKSPACE;
@@ -127,6 +138,7 @@ int gdn_hybrid_decode(const void* q, const void* k, const void* v, const float* 
   if (!q || !k || !v || !a || !state || !k_cache || !v_cache || !a_cache || !pos || !o)
     return GDN_EINVAL;
   if (update == GDN_DELTA && (!b || !b_cache)) return GDN_EINVAL;
+  if (!aligned16({q, k, v, a, b, state, k_cache, v_cache, a_cache, b_cache, pos, o})) return GDN_EINVAL;
   const int G = H / Hkv;
   if (G > 16) return GDN_EUNSUPPORTED;
   if ((int64_t)G * (n_sink + window) > 12288) return GDN_EUNSUPPORTED;
@@ -146,6 +158,7 @@ int gdn_hybrid_cache_from_prefill(const void* k, const void* v, const float* a, 
   if (update == GDN_DELTA && !b_cache) return GDN_EINVAL;
   if (T > 0 && (!k || !v || !a)) return GDN_EINVAL;
   if (T > 0 && update == GDN_DELTA && !b) return GDN_EINVAL;
+  if (!aligned16({k, v, a, b, k_cache, v_cache, a_cache, b_cache})) return GDN_EINVAL;
   gdn::CacheArgs p{k, v, a, b, k_cache, v_cache, a_cache, b_cache, B, T, H, Hkv, dk,
                    n_sink, window, dtype == GDN_BF16, update == GDN_GLA};
   return launched(gdn::launch_cache_from_prefill(p, (hipStream_t)stream));
@@ -157,6 +170,7 @@ int shortconv_qkv(const void* q, const void* k, const void* v, const float* wq, 
                   void* stream) {
   if (!dims_ok(B, T, H, Hkv, d, d, 0, 1, dtype, GDN_DELTA)) return GDN_EINVAL;
   if (!q || !k || !v || !wq || !wk || !wv || !q_out || !k_out || !v_out) return GDN_EINVAL;
+  if (!aligned16({q, k, v, wq, wk, wv, q_out, k_out, v_out})) return GDN_EINVAL;
   if (ksize < 1 || ksize > 8) return GDN_EUNSUPPORTED;
   if (flags < 0 || flags > 3) return GDN_EINVAL;
   if ((flags & GDN_ROPE) && !(rope_theta > 0.f)) return GDN_EINVAL;

@@ -140,6 +140,17 @@ def test_prefill_workspace_checks(lib):
     assert prefill(lib, T=200, flags=2, q=None) == EINVAL
 
 
+def test_misaligned_tensors_are_rejected(lib):
+    # every tensor pointer must be 16-byte aligned; the check runs before any launch
+    odd = ctypes.c_void_p(FAKE.value + 8)
+    for name in ("q", "k", "v", "a", "b", "o", "st"):
+        assert prefill(lib, T=0, flags=7, **{name: odd}) == EINVAL, name
+    for name in ("q", "k", "v", "a", "b", "st", "kc", "vc", "ac", "bc", "pos", "o"):
+        assert decode(lib, **{name: odd}) == EINVAL, name
+    for name in ("q", "k", "v", "wq", "wk", "wv", "qo", "ko", "vo"):
+        assert shortconv(lib, **{name: odd}) == EINVAL, name
+
+
 def test_prefill_zero_length_is_a_noop(lib):
     # T = 0 with no state requested returns before any launch
     assert prefill(lib, T=0) == OK
