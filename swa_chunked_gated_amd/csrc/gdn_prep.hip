@@ -1,356 +1,28 @@
-// Chunk preparation for the chunked gated delta rule (prefill): the part of
-// each 64-token chunk's work that does not depend on the recurrent state, done
-// for every chunk at once so that the sequential scan over chunks only keeps
+// Chunk preparation kernel of the chunked gated delta rule (prefill): the
+// part of each 64-token chunk's work that does not depend on the recurrent
+// state (gdn_prep.h), done for every chunk at once, one wave per (chunk,
+// query head, sequence), so that the sequential scan over chunks only keeps
 // the state-dependent products.
-//
-// Method (page "The Key to Going Linear: Analysis-Driven Transformer
-// Linearization", section 线性注意力替换机制): GDN update
-// S_i = a_i (I - b_i k_i k_i^T) S_{i-1} + b_i k_i v_i^T.  Unrolled over a chunk
-// of stream tokens with g = inclusive cumsum of log2 a inside the chunk and
-// gamma = 2^g, the chunk is exact with
-//   L_rs = b_r (gamma_r / gamma_s) k_r.k_s  (s < r),   Tm = (I + L)^-1,
-//   U = Tm diag(b) V - Tm diag(b gamma) K S0,  ...
-// so Tm diag(b) and Tm diag(b gamma) (and g, gamma) are all the scan needs
-// from here.
-//
-// One wave per (chunk, query head, sequence).  K K^T on MFMA; the unit
-// lower-triangular inverse as 16x16 diagonal blocks by forward substitution
-// in fp32 plus the off-diagonal blocks by block recursion on fp32 MFMA
-// (16x16x4, exact fp32 products).  Outputs per chunk (workspace,
-// element type T): TB = Tm diag(b) and TBG = Tm diag(b gamma) as 64 rows of
-// 64, each row's columns stored in acc order (the order the scan's LDS tiles
-// use, so the scan copies them with 16-byte moves), and fp32 g[64], gamma[64].
 
 #include "common.h"
+#include "gdn_prep.h"
 #include "launch.h"
 
 namespace gdn {
 namespace {
 
-constexpr int kC = 64;          // chunk length
-constexpr int kSL = 68;         // fp32 stride of the 64x64 solve buffer
+using prep::kC;
+using prep::PrepSmem;
 
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// C += A(16x16) B(16x16), both fp32 row-major in LDS.
-__device__ __forceinline__ f32x4 mm16(const float* A, const float* B, f32x4 c, int l16, int lg) {
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) c = mfma4(A[l16 * kSL + 4 * kk + lg], B[(4 * kk + lg) * kSL + l16], c);
-  return c;
-}
-// C += A(16x16, LDS) Y(16x16, accumulator registers of this wave).
-__device__ __forceinline__ f32x4 mm16_acc(const float* A, const f32x4& Y, f32x4 c, int l16, int lg) {
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) c = mfma4(A[l16 * kSL + 4 * lg + kk], Y[kk], c);
-  return c;
-}
-__device__ __forceinline__ void st16(float* blk, const f32x4& x, int l16, int lg) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) blk[(4 * lg + i) * kSL + l16] = x[i];
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts inside
-// each row of 16 lanes, then the row totals (read as scalars) added on.
-__device__ __forceinline__ float wave_prefix_sum(float x, int lane) {
-  // row_shr:s (dpp control 0x110 + s); lanes with lane % 16 < s receive 0
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, true));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, true));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, true));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, true));
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
-  const int row = lane >> 4;
-  float off = 0.f;
-  if (row >= 1) off = r0;
-  if (row >= 2) off = off + r1;
-  if (row >= 3) off = off + r2;
-  return x + off;
-}
-
-// (I + L)^-1 in place for the strictly lower 64 x 64 L in Lf (fp32, unit
-// diagonal implied, upper part zero), by one wave: 16x16 diagonal blocks by
-// forward substitution (lane = block x column j; row r of the block's inverse
-// column is e_j[r] - sum_{s<r} L[r][s] x[s], with L's rows read as 16-byte
-// pieces), then the off-diagonal blocks by block recursion on fp32 MFMA
-// (exact fp32 products).  A wave's LDS operations complete in program order; lds_barrier
-// (which for a one-wave workgroup only waits on LDS) marks the phases.
-__device__ __forceinline__ void unit_lower_inverse_wave(float* Lf, int lane) {
-  const int l16 = lane & 15;
-  const int lg = lane >> 4;
-  {
-    const int blk = lane >> 4;
-    const int j = l16;
-    float* Lb = Lf + 16 * blk * kSL + 16 * blk;
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float lr[16];
-#pragma unroll
-      for (int q4 = 0; q4 < (r + 3) / 4; ++q4) {
-        const f32x4 t = *reinterpret_cast<const f32x4*>(&Lb[r * kSL + 4 * q4]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) lr[4 * q4 + e] = t[e];
-      }
-      float acc = r == j ? 1.f : 0.f;
-#pragma unroll
-      for (int s2 = 0; s2 < r; ++s2) acc -= lr[s2] * x[s2];
-      x[r] = acc;
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) Lb[r * kSL + j] = x[r];
-  }
-  lds_barrier();
-  // level 1: X10 = -X11 L10 X00, X32 = -X33 L32 X22
-  f32x4 x10[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int o0 = 32 * u;
-    const f32x4 y = mm16(Lf + (o0 + 16) * kSL + o0, Lf + o0 * kSL + o0, zero4(), l16, lg);
-    x10[u] = -mm16_acc(Lf + (o0 + 16) * kSL + o0 + 16, y, zero4(), l16, lg);
-  }
-#pragma unroll
-  for (int u = 0; u < 2; ++u) st16(Lf + (32 * u + 16) * kSL + 32 * u, x10[u], l16, lg);
-  lds_barrier();
-  // level 2: bottom-left 32x32 block = -X_BR (L_BL X_TL); every product is
-  // read before any of the four 16x16 blocks is overwritten
-  f32x4 y[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int br = 32 + 16 * (u >> 1);
-    const int bc = 16 * (u & 1);
-    y[u] = zero4();
-    for (int kb = bc; kb < 32; kb += 16) y[u] = mm16(Lf + br * kSL + kb, Lf + kb * kSL + bc, y[u], l16, lg);
-  }
-  lds_barrier();
-#pragma unroll
-  for (int u = 0; u < 4; ++u) st16(Lf + (32 + 16 * (u >> 1)) * kSL + 16 * (u & 1), y[u], l16, lg);
-  lds_barrier();
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int br = 32 + 16 * (u >> 1);
-    const int bc = 16 * (u & 1);
-    y[u] = zero4();
-    for (int kb = 32; kb <= br; kb += 16) y[u] = mm16(Lf + br * kSL + kb, Lf + kb * kSL + bc, y[u], l16, lg);
-  }
-  lds_barrier();
-#pragma unroll
-  for (int u = 0; u < 4; ++u) st16(Lf + (32 + 16 * (u >> 1)) * kSL + 16 * (u & 1), -y[u], l16, lg);
-  lds_barrier();
-}
-
-template <class T, int D, bool FULL>
-struct PrepSmem {
-  static constexpr int PAD = 16 / sizeof(T);
-  static constexpr int SC = kC + PAD;       // [*][64] rows
-  static constexpr int oKT = 0;                             // K^T, tokens in acc order
-  static constexpr int oTBG = oKT + (FULL ? D * SC : 0);    // Tm diag(b gamma)
-  static constexpr int oA = oTBG + (FULL ? kC * SC : 0);    // scores
-  static constexpr int nT = oA + (FULL ? kC * SC : 0);
-  static constexpr int bytesT = (nT * (int)sizeof(T) + 15) / 16 * 16;
-  static constexpr int nL = kC * kSL;                       // solve buffer
-  static constexpr int bytes = bytesT + 4 * (nL + 4 * kC);  // + g, gamma, b, K^T factors
-};
-
-// One wave per (chunk, query head, sequence): every operand fragment of
-// K K^T (and Q K^T) is loaded straight from global memory into registers, so
-// the only LDS a chunk needs is the 64 x 64 fp32 solve buffer (plus, for the
-// full preparation, K^T, TBG and A staging), and many chunks run per CU.
 template <class T, int D, bool FULL>
 __global__ __launch_bounds__(64) void gdn_prep_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ a,
     const float* __restrict__ b, T* __restrict__ wtb, T* __restrict__ wtbg, T* __restrict__ wwm,
     T* __restrict__ wktg, T* __restrict__ wa, float* __restrict__ wg, int T_, int H, int Hkv,
     int n_sink, int window, int nch) {
-  using SM = PrepSmem<T, D, FULL>;
-  constexpr int EPC = 16 / (int)sizeof(T);     // elements per 16-byte piece
-  constexpr int QV = 8 / EPC;                  // 16-byte pieces per fragment
-  constexpr int KS = D / 32;                   // 32-wide k-steps over d
-  constexpr int SC = SM::SC;
-  typedef typename Vec16<T>::type V16;
-
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  T* sT = reinterpret_cast<T*>(smem_raw);
-  T* KTs = sT + SM::oKT;
-  T* TBGs = sT + SM::oTBG;
-  T* As = sT + SM::oA;
-  float* Lf = reinterpret_cast<float*>(smem_raw + SM::bytesT);
-  float* lgs = Lf + SM::nL;
-  float* gam = lgs + kC;
-  float* bet = gam + kC;
-  float* fac = bet + kC;                       // 2^{g_C - g} in acc position order
-
-  const int c = blockIdx.x;
-  const int h = blockIdx.y;
-  const int bi = blockIdx.z;
-  const int g = h / (H / Hkv);
-  const int lane = threadIdx.x;
-  const int l16 = lane & 15;
-  const int lg = lane >> 4;
-  const int iend = T_ - window;                // stream tokens are [n_sink, iend)
-  const int i0 = n_sink + c * kC;
-  const size_t ci = ((size_t)bi * H + h) * nch + c;
-  const T* kbase = k + ((size_t)(bi * T_ + i0) * Hkv + g) * D;
-  const T* qbase = q + ((size_t)(bi * T_ + i0 + window) * H + h) * D;
-
-  // ---- this chunk's gates first (a = 1, b = 0 past the stream end)
-  const int tok = i0 + lane;
-  const float av = tok < iend ? a[(size_t)(bi * T_ + tok) * H + h] : 1.f;
-  const float bv = tok < iend ? b[(size_t)(bi * T_ + tok) * H + h] : 0.f;
-
-  // ---- operand pieces: lane holds rows 16 mt + l16, dims 32 p + 8 lg .. +7
-  V16 kr[4][KS][QV];
-  V16 qr[FULL ? 4 : 1][FULL ? KS : 1][QV];
-  const bool whole = i0 + kC <= iend;          // uniform: no row past the stream
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int r = 16 * mt + l16;
-    const bool live = whole || i0 + r < iend;
-#pragma unroll
-    for (int p = 0; p < KS; ++p)
-#pragma unroll
-      for (int u = 0; u < QV; ++u) {
-        const int col = 32 * p + 8 * lg + u * EPC;
-        if (live) {
-          kr[mt][p][u] = *reinterpret_cast<const V16*>(kbase + (size_t)r * Hkv * D + col);
-          if constexpr (FULL) qr[mt][p][u] = *reinterpret_cast<const V16*>(qbase + (size_t)r * H * D + col);
-        } else {
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) {
-            kr[mt][p][u][e] = from_f32<T>(0.f);
-            if constexpr (FULL) qr[mt][p][u][e] = from_f32<T>(0.f);
-          }
-        }
-      }
-  }
-  auto frag_of = [&](const V16 (&pc)[QV]) {
-    float x[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = to_f32(pc[i / EPC][i % EPC]);
-    return frag_from8<T>(x);
-  };
-
-  // ---- zero the solve buffer (and the score tile, whose strictly upper
-  // 16x16 tiles stay zero); gates: g = inclusive cumsum of log2 a, gamma =
-  // 2^g, b
-#pragma unroll
-  for (int i = lane; i < SM::nL / 4; i += 64) reinterpret_cast<f32x4*>(Lf)[i] = zero4();
-  if constexpr (FULL) {
-#pragma unroll
-    for (int i = lane; i < kC * SC / EPC; i += 64) {
-      V16 z;
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) z[e] = from_f32<T>(0.f);
-      reinterpret_cast<V16*>(As)[i] = z;
-    }
-  }
-  {
-    const float x = wave_prefix_sum(__builtin_amdgcn_logf(av), lane);
-    lgs[lane] = x;
-    gam[lane] = __builtin_amdgcn_exp2f(x);
-    bet[lane] = bv;
-  }
-  lds_barrier();
-  if (FULL) fac[lane] = __builtin_amdgcn_exp2f(fminf(lgs[kC - 1] - lgs[acc_idx(lane)], 0.f));
-
-  // ---- L = strictly lower (b_r 2^{g_r - g_s} k_r.k_s); full: also
-  // A = [s <= r] 2^{g_r - g_s} q_r.k_s
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int r0 = 16 * mt + 4 * lg;
-    const f32x4 lr = *reinterpret_cast<const f32x4*>(&lgs[r0]);
-    const f32x4 br = *reinterpret_cast<const f32x4*>(&bet[r0]);
-#pragma unroll
-    for (int nt = 0; nt <= mt; ++nt) {
-      const int s = 16 * nt + l16;
-      const float ls = lgs[s];
-      f32x4 acc = zero4(), accq = zero4();
-#pragma unroll
-      for (int p = 0; p < KS; ++p) {
-        const Frag<T> kb = frag_of(kr[nt][p]);
-        acc = mfma(frag_of(kr[mt][p]), kb, acc);
-        if constexpr (FULL) accq = mfma(frag_of(qr[mt][p]), kb, accq);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = r0 + i;
-        const float dec = __builtin_amdgcn_exp2f(fminf(lr[i] - ls, 0.f));
-        Lf[r * kSL + s] = s < r ? br[i] * dec * acc[i] : 0.f;
-        if constexpr (FULL) As[r * SC + acc_pos(s)] = from_f32<T>(s <= r ? dec * accq[i] : 0.f);
-      }
-    }
-  }
-  if constexpr (FULL) {
-    // K^T (tokens in acc order) from the row pieces
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int p = 0; p < KS; ++p)
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          KTs[(32 * p + 8 * lg + i) * SC + acc_pos(16 * mt + l16)] = kr[mt][p][i / EPC][i % EPC];
-  }
-  lds_barrier();
-  unit_lower_inverse_wave(Lf, lane);
-
-  // ---- TB = Tm diag(b) (and TBG = Tm diag(b gamma)): row r, columns
-  // s0..s0+3 at positions acc_pos(s0)..+3 of the row
-  T* tb = wtb + ci * (kC * kC);
-#pragma unroll 4
-  for (int i = lane; i < kC * kC / 4; i += 64) {
-    const int r = i >> 4;
-    const int s0 = (i & 15) * 4;
-    const f32x4 tm = *reinterpret_cast<const f32x4*>(&Lf[r * kSL + s0]);
-    const f32x4 bb = *reinterpret_cast<const f32x4*>(&bet[s0]);
-    const f32x4 gg = *reinterpret_cast<const f32x4*>(&gam[s0]);
-    const f32x4 x = tm * bb;
-    store4(tb + r * kC + acc_pos(s0), x);
-    if (FULL) store4(&TBGs[r * SC + acc_pos(s0)], x * gg);
-    else store4(wtbg + ci * (kC * kC) + r * kC + acc_pos(s0), x * gg);
-  }
-  wg[ci * (2 * kC) + lane] = lgs[lane];
-  wg[ci * (2 * kC) + kC + lane] = gam[lane];
-  if constexpr (FULL) {
-    lds_barrier();
-    // ---- -Wm = -(TBG K): per 16-row dk tile, Wm^T = K^T TBG^T on MFMA,
-    // written as [token][dk]
-    T* wm = wwm + ci * (kC * D);
-#pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt) {
-      Frag<T> kf[2];
-#pragma unroll
-      for (int p = 0; p < 2; ++p) kf[p] = lds_frag8(&KTs[(16 * mt + l16) * SC + 32 * p + 8 * lg]);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int p = 0; p < 2; ++p) acc = mfma(kf[p], lds_frag8(&TBGs[(16 * nt + l16) * SC + 32 * p + 8 * lg]), acc);
-        store4(wm + (16 * nt + l16) * D + 16 * mt + 4 * lg, -acc);
-      }
-    }
-    // ---- K^T 2^{g_C - g} [D][64] (row r holds d_k index acc_pos(r), the
-    // state row order of the scan's accumulators) and A [64][64], 16-byte pieces
-    T* ktg = wktg + ci * (D * kC);
-    T* aa = wa + ci * (kC * kC);
-#pragma unroll 4
-    for (int i = lane; i < D * (kC / EPC); i += 64) {
-      const int r = i / (kC / EPC);
-      const int pc = (i % (kC / EPC)) * EPC;
-      const V16 x = *reinterpret_cast<const V16*>(&KTs[acc_pos(r) * SC + pc]);
-      V16 y;
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) y[e] = from_f32<T>(to_f32(x[e]) * fac[pc + e]);
-      *reinterpret_cast<V16*>(ktg + r * kC + pc) = y;
-    }
-#pragma unroll
-    for (int i = lane; i < kC * (kC / EPC); i += 64) {
-      const int r = i / (kC / EPC);
-      const int pc = (i % (kC / EPC)) * EPC;
-      *reinterpret_cast<V16*>(aa + r * kC + pc) = *reinterpret_cast<const V16*>(&As[r * SC + pc]);
-    }
-  }
+  prep::gdn_prep_chunk<T, D, FULL>(q, k, a, b, wtb, wtbg, wwm, wktg, wa, wg, T_, H, Hkv, n_sink,
+                                   window, nch, blockIdx.x, blockIdx.y, blockIdx.z, smem_raw);
 }
 
 template <class T, int D, bool FULL>
@@ -403,6 +75,8 @@ GdnWorkspace gdn_workspace_layout(void* base, int B, int H, int nch, int D, size
   off += full ? n * kC * kC * elt : 0;
   w.g = reinterpret_cast<float*>(p + off);
   off += n * 2 * kC * sizeof(float);
+  w.ready = full ? reinterpret_cast<uint64_t*>(p + off) : nullptr;
+  off += full ? n * sizeof(uint64_t) : 0;
   w.bytes = off;
   return w;
 }

@@ -26,7 +26,12 @@
 // waves issue no loads of their own, so their MFMA and LDS work never queues
 // behind the vector-memory traffic of the next chunk.
 
+#include <atomic>
+#include <chrono>
+#include <random>
+
 #include "common.h"
+#include "gdn_prep.h"
 #include "launch.h"
 
 namespace gdn {
@@ -39,11 +44,17 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(1))) void* gbl_void_ptr;
 
 // Lane L of the wave loads 16 (4) bytes at g into LDS at base + 16 L (4 L).
+// dma16c / dma4c read at device scope (cache policy sc1): coherent with
+// the device-scope stores of another compute unit in the same kernel (the
+// preparation's tiles); dma16 is a plain load (the layer's inputs).
 __device__ __forceinline__ void dma16(const void* g, void* base) {
   __builtin_amdgcn_global_load_lds((gbl_void_ptr)(void*)g, (lds_void_ptr)base, 16, 0, 0);
 }
-__device__ __forceinline__ void dma4(const void* g, void* base) {
-  __builtin_amdgcn_global_load_lds((gbl_void_ptr)(void*)g, (lds_void_ptr)base, 4, 0, 0);
+__device__ __forceinline__ void dma16c(const void* g, void* base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_ptr)(void*)g, (lds_void_ptr)base, 16, 0, 16);
+}
+__device__ __forceinline__ void dma4c(const void* g, void* base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_ptr)(void*)g, (lds_void_ptr)base, 4, 0, 16);
 }
 
 template <int D, int NW>
@@ -65,14 +76,45 @@ struct FullSmem {
   static_assert((nT * 2) % 16 == 0, "16-byte tiles");
 };
 
+// Waits until the preparation has published chunk `f` (flag == epoch).  The
+// flag is read at device scope and the chunk's tiles are then read with
+// device-scope loads issued after the flag was seen (the wave issues in
+// order; the asm keeps the compiler from moving loads above the loop).
+// Bounded: after about 0.1 s it gives up, so a missing producer can never
+// hang the GPU (the results would then be wrong, never the machine stuck).
+__device__ __forceinline__ void wait_ready(const uint64_t* f, uint64_t epoch) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();          // 100 MHz
+  while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+    __builtin_amdgcn_s_sleep(1);
+    if (__builtin_amdgcn_s_memrealtime() - t0 > 10000000ull) break;
+  }
+  asm volatile("" ::: "memory");
+}
+
+// Preparation waves per preparation workgroup (each needs its own PrepSmem).
+constexpr int kPrepWaves = 2;
+
+// Grid: n_prep preparation workgroups first, then one scan workgroup per
+// (sequence, head, column slice).  With n_prep = 0 the workspace is already
+// complete (the preparation kernel ran before) and nothing waits.  Otherwise
+// preparation waves take (chunk, head, sequence) items in chunk-major order,
+// write the chunk's tiles and then publish flags[(b H + h) nch + c] = epoch
+// (device-scope release); the scan's loader waves wait for that flag before
+// loading the chunk.  Preparation workgroups never wait and come first in the
+// grid, so they are all dispatched before any scan workgroup: the waits
+// always end.
 template <int D, int NW, int NL>
 __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ v, const bf16* __restrict__ w_tb,
-    const bf16* __restrict__ w_wm, const bf16* __restrict__ w_ktg, const bf16* __restrict__ w_a,
-    const float* __restrict__ w_g, bf16* __restrict__ o, float* __restrict__ state_out, int T_,
-    int H, int Hkv, int n_sink, int window, int flags) {
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ a, const float* __restrict__ b, bf16* __restrict__ w_tb,
+    bf16* __restrict__ w_wm, bf16* __restrict__ w_ktg, bf16* __restrict__ w_a,
+    float* __restrict__ w_g, uint64_t* __restrict__ ready, uint64_t epoch, int n_prep,
+    bf16* __restrict__ o, float* __restrict__ state_out, int B, int T_, int H, int Hkv,
+    int n_sink, int window, int flags) {
   using SM = FullSmem<D, NW>;
+  using PS = prep::PrepSmem<bf16, D, true>;
   static_assert(NL == 1 || NL == 2, "one or two loader waves");
+  static_assert(kPrepWaves * PS::bytes <= SM::bytes && PS::bytes % 16 == 0, "preparation LDS");
   constexpr int SK = SM::SK;
   constexpr int SC = SM::SC;
   constexpr int DVS = SM::DVS;
@@ -82,18 +124,41 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   auto buf = [&](int b) { return reinterpret_cast<bf16*>(smem_raw + b * SM::buf_bytes); };
 
-  const int sp = blockIdx.x;             // column slice
-  const int h = blockIdx.y;
-  const int bi = blockIdx.z;
-  const int g = h / (H / Hkv);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = wave_id();
+  const int iend = T_ - window;          // stream tokens are [n_sink, iend)
+  const int nch = iend > n_sink ? (iend - n_sink + kC - 1) / kC : 0;
+
+  if ((int)blockIdx.x < n_prep) {
+    // ======================= preparation workgroup
+    if (wv >= kPrepWaves) return;
+    const int BH = B * H;
+    for (int it = blockIdx.x * kPrepWaves + wv; it < nch * BH; it += n_prep * kPrepWaves) {
+      const int c = it / BH;
+      const int bh = it % BH;
+      prep::gdn_prep_chunk<bf16, D, true, true>(q, k, a, b, w_tb, nullptr, w_wm, w_ktg, w_a, w_g, T_,
+                                                H, Hkv, n_sink, window, nch, c, bh % H, bh / H,
+                                                smem_raw + wv * PS::bytes);
+      // every device-scope tile store of this wave has completed (vmcnt 0)
+      // before the flag is stored
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      asm volatile("" ::: "memory");
+      if (lane == 0)
+        __hip_atomic_store(ready + (size_t)bh * nch + c, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
+
+  const int sw = blockIdx.x - n_prep;
+  const int sp = sw % (D / DVS);         // column slice
+  const int h = (sw / (D / DVS)) % H;
+  const int bi = sw / ((D / DVS) * H);
+  const int g = h / (H / Hkv);
   const int l16 = lane & 15;
   const int lg = lane >> 4;
   const int c0 = sp * DVS;
-  const int iend = T_ - window;          // stream tokens are [n_sink, iend)
-  const int nch = iend > n_sink ? (iend - n_sink + kC - 1) / kC : 0;
   const size_t chain = (size_t)bi * H + h;
 
   if (wv >= NW) {
@@ -143,6 +208,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
       const int i0 = n_sink + c * kC;
       const int Cc = min(kC, iend - i0);
       const size_t ci = chain * nch + c;
+      if (n_prep > 0) wait_ready(ready + ci, epoch);
       // query rows i0 + window + r and V rows i0 + r; in a partial chunk the
       // rows past the stream repeat its last row (their outputs are never
       // stored, and TB's columns for them are zero)
@@ -175,18 +241,18 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
       const char* tb = reinterpret_cast<const char*>(w_tb + ci * (kC * kC));
       if (ld == NL - 1) {
 #pragma unroll
-        for (int n = 0; n < NQ; ++n) dma16(wb + ow[n], B + SM::oWm + 512 * n);
+        for (int n = 0; n < NQ; ++n) dma16c(wb + ow[n], B + SM::oWm + 512 * n);
 #pragma unroll
-        for (int n = 0; n < NK; ++n) dma16(kb + ok[n], B + SM::oKT + 512 * n);
+        for (int n = 0; n < NK; ++n) dma16c(kb + ok[n], B + SM::oKT + 512 * n);
       }
       if (ld == 0) {
 #pragma unroll
-        for (int n = 0; n < NS; ++n) dma16(ab + ok[n], B + SM::oA + 512 * n);
+        for (int n = 0; n < NS; ++n) dma16c(ab + ok[n], B + SM::oA + 512 * n);
 #pragma unroll
-        for (int n = 0; n < NS; ++n) dma16(tb + ok[n], B + SM::oTB + 512 * n);
+        for (int n = 0; n < NS; ++n) dma16c(tb + ok[n], B + SM::oTB + 512 * n);
         float* gate = reinterpret_cast<float*>(B + SM::nT);
-        dma4(w_g + ci * (2 * kC) + lane, gate);
-        dma4(w_g + ci * (2 * kC) + 64 + lane, gate + 64);
+        dma4c(w_g + ci * (2 * kC) + lane, gate);
+        dma4c(w_g + ci * (2 * kC) + 64 + lane, gate + 64);
       }
       __builtin_amdgcn_s_waitcnt(0);   // this buffer is complete in LDS
     };
@@ -345,28 +411,51 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
   }
 }
 
+// Per-call value of the ready flags: a process-wide counter from a random
+// start, so flags left in a reused workspace (or in fresh memory) never match.
+uint64_t next_epoch() {
+  static std::atomic<uint64_t> counter{[] {
+    std::random_device rd;
+    const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+    return (((uint64_t)rd() << 32) ^ (uint64_t)rd() ^ (t * 0x9E3779B97F4A7C15ull)) | 1ull;
+  }()};
+  return counter.fetch_add(2, std::memory_order_relaxed);   // odd: never the zero of cleared memory
+}
+
 template <int D, int NW, int NL>
-hipError_t launch_full_t(const PrefillArgs& p, hipStream_t s) {
+hipError_t launch_full_t(const PrefillArgs& p, int nch, hipStream_t s) {
   using SM = FullSmem<D, NW>;
   auto kern = gdn_scan_full_kernel<D, NW, NL>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, SM::bytes);
   if (e != hipSuccess) return e;
-  const int nch = gdn_stream_chunks(p.T, p.n_sink, p.window);
   const GdnWorkspace w = gdn_workspace_layout(p.workspace, p.B, p.H, nch, D, sizeof(bf16), true);
-  const dim3 grid(D / SM::DVS, p.H, p.B);
-  hipLaunchKernelGGL(kern, grid, dim3(64 * (NW + NL)), SM::bytes, s, (const bf16*)p.q,
-                     (const bf16*)p.v, (const bf16*)w.tb, (const bf16*)w.wm, (const bf16*)w.ktg,
-                     (const bf16*)w.a, w.g, (bf16*)p.o, p.state_out, p.T, p.H, p.Hkv, p.n_sink,
-                     p.window, p.flags);
+  const int n_scan = p.B * p.H * (D / SM::DVS);
+  // Overlap the preparation with the scan when the scan leaves at least half
+  // of the compute units free: each scan workgroup fills a compute unit (LDS),
+  // the preparation workgroups take the rest.
+  int dev = 0, cus = 0;
+  e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  int n_prep = (nch > 0 && 2 * n_scan <= cus) ? cus - n_scan : 0;
+  if (nch > 0 && n_prep == 0) {
+    e = launch_gdn_prep(p, nch, s);
+    if (e != hipSuccess) return e;
+  }
+  const uint64_t epoch = n_prep > 0 ? next_epoch() : 0;
+  hipLaunchKernelGGL(kern, dim3(n_prep + n_scan), dim3(64 * (NW + NL)), SM::bytes, s,
+                     (const bf16*)p.q, (const bf16*)p.k, (const bf16*)p.v, p.a, p.b, (bf16*)w.tb,
+                     (bf16*)w.wm, (bf16*)w.ktg, (bf16*)w.a, w.g, w.ready, epoch, n_prep,
+                     (bf16*)p.o, p.state_out, p.B, p.T, p.H, p.Hkv, p.n_sink, p.window, p.flags);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gdn_scan_full(const PrefillArgs& p, hipStream_t s) {
+hipError_t launch_gdn_full(const PrefillArgs& p, int nch, hipStream_t s) {
   if (!p.bf16 || p.gla) return hipErrorInvalidValue;
-  if (p.D == 64) return launch_full_t<64, 4, 2>(p, s);
-  if (p.D == 128) return launch_full_t<128, 4, 2>(p, s);
+  if (p.D == 64) return launch_full_t<64, 4, 2>(p, nch, s);
+  if (p.D == 128) return launch_full_t<128, 4, 2>(p, nch, s);
   return hipErrorInvalidValue;
 }
 

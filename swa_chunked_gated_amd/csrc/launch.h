@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace gdn {
 
@@ -28,7 +29,8 @@ struct PrefillArgs {
 //   TB = Tm diag(b) [64][64]; then either (light preparation) TBG =
 //   Tm diag(b gamma) [64][64], or (full preparation, bf16) -Wm [64][D] with
 //   d_k in natural order, K^T 2^{g_C - g} [D][64] whose row r holds d_k index
-//   acc_pos(r), and the scores A [64][64]; then g, gamma [2][64] fp32.
+//   acc_pos(r), and the scores A [64][64]; then g, gamma [2][64] fp32; the
+//   full preparation ends with one uint64 ready flag per chunk.
 struct GdnWorkspace {
   void* tb;
   void* tbg;
@@ -36,15 +38,17 @@ struct GdnWorkspace {
   void* ktg;
   void* a;
   float* g;
+  uint64_t* ready;   // full preparation: per-chunk ready flags
   size_t bytes;
 };
 // Full preparation (everything state-independent precomputed) for bf16 when
 // the scan alone cannot fill the GPU.
 bool gdn_full_prep(int B, int H, int D, int bf16);
 GdnWorkspace gdn_workspace_layout(void* base, int B, int H, int nch, int D, size_t elt, bool full);
-// State scan over a fully prepared workspace (bf16, d = 64 or 128), with a
-// loader wave streaming the next chunk's tiles into LDS.
-hipError_t launch_gdn_scan_full(const PrefillArgs& p, hipStream_t s);
+// Full preparation and state scan (bf16, d = 64 or 128): one kernel whose
+// preparation workgroups publish chunks to its scan workgroups when the scan
+// leaves half of the GPU free, else the preparation kernel then the scan.
+hipError_t launch_gdn_full(const PrefillArgs& p, int nch, hipStream_t s);
 // Workspace of the GLA prefill: for each (sequence, head, chunk) Q 2^G
 // [64][D], (K 2^{G_C - G})^T [D][64], A [64][64] (I/O type, reduction index in
 // acc order) and 2^{G_C} [D] fp32, as four consecutive arrays.

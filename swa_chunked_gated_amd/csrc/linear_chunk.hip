@@ -597,7 +597,6 @@ hipError_t launch_linear_t(const PrefillArgs& p, hipStream_t s) {
 
 template <class T, int D, int NW, bool GLA>
 hipError_t launch_linear_f(const PrefillArgs& p, hipStream_t s) {
-  if (!GLA && gdn_full_prep(p.B, p.H, p.D, p.bf16)) return launch_gdn_scan_full(p, s);
   return launch_linear_t<T, D, NW, 16, GLA>(p, s);
 }
 
@@ -615,6 +614,7 @@ hipError_t launch_linear_d(const PrefillArgs& p, hipStream_t s) {
 
 hipError_t launch_linear_prefill(const PrefillArgs& p, hipStream_t s) {
   const int nch = gdn_stream_chunks(p.T, p.n_sink, p.window);
+  if (!p.gla && gdn_full_prep(p.B, p.H, p.D, p.bf16)) return launch_gdn_full(p, nch, s);
   if (nch > 0) {
     const hipError_t e = p.gla ? launch_gla_prep(p, nch, s) : launch_gdn_prep(p, nch, s);
     if (e != hipSuccess) return e;
