@@ -113,7 +113,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
     int n_sink, int window, int flags) {
   using SM = FullSmem<D, NW>;
   using PS = prep::PrepSmem<bf16, D, true>;
-  static_assert(NL == 1 || NL == 2, "one or two loader waves");
+  static_assert(NL >= 1 && NL <= 4, "one to four loader waves");
   static_assert(kPrepWaves * PS::bytes <= SM::bytes && PS::bytes % 16 == 0, "preparation LDS");
   constexpr int SK = SM::SK;
   constexpr int SC = SM::SC;
@@ -162,8 +162,14 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
   const size_t chain = (size_t)bi * H + h;
 
   if (wv >= NW) {
-    const int ld = wv - NW;                        // loader index: splits the tiles
-    // ======================= loader wave
+    // ======================= loader waves: tile t of a chunk is loaded by
+    // loader kOwner[NL - 1][t] (tiles: Q, V, -Wm, KTg, A, TB, gates)
+    constexpr int kOwner[4][7] = {{0, 0, 0, 0, 0, 0, 0},
+                                  {0, 0, 1, 1, 0, 0, 0},
+                                  {0, 0, 1, 2, 1, 2, 2},
+                                  {0, 3, 1, 2, 3, 3, 0}};
+    const int ld = wv - NW;
+    auto mine = [&](int t) { return kOwner[NL - 1][t] == ld; };
     // Every LDS image is whole 1 KiB blocks of 16-byte slots; slot s = 64 n +
     // lane of block n holds piece s % (P + 1) of row s / (P + 1) (the last
     // piece of a row is padding and repeats piece 0).  The per-lane byte
@@ -203,23 +209,28 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
       piece(n, 8, r, p);
       ok[n] = (uint32_t)((r * 8 + p) * 16);
     }
+    // ready flag of the next chunk to stage, read one chunk ahead so that its
+    // latency hides behind the current chunk's loads
+    uint64_t seen = 0;
     auto stage = [&](int c, int b) {
       bf16* B = buf(b);
       const int i0 = n_sink + c * kC;
       const int Cc = min(kC, iend - i0);
       const size_t ci = chain * nch + c;
-      if (n_prep > 0) wait_ready(ready + ci, epoch);
+      if (n_prep > 0) {
+        if (seen != epoch) wait_ready(ready + ci, epoch);
+        asm volatile("" ::: "memory");
+        seen = c + 1 < nch ? __hip_atomic_load(ready + ci + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+      }
       // query rows i0 + window + r and V rows i0 + r; in a partial chunk the
       // rows past the stream repeat its last row (their outputs are never
       // stored, and TB's columns for them are zero)
       const char* qb = reinterpret_cast<const char*>(q + ((size_t)(bi * T_ + i0 + window) * H + h) * D);
       const char* vb = reinterpret_cast<const char*>(v + ((size_t)(bi * T_ + i0) * Hkv + g) * D + c0);
-      if (ld == 0) {
+      if (mine(0)) {
         if (Cc == kC) {
 #pragma unroll
           for (int n = 0; n < NQ; ++n) dma16(qb + oq[n], B + SM::oQ + 512 * n);
-#pragma unroll
-          for (int n = 0; n < NV; ++n) dma16(vb + ov[n], B + SM::oV + 512 * n);
         } else {
 #pragma unroll
           for (int n = 0; n < NQ; ++n) {
@@ -227,6 +238,13 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
             piece(n, P, r, p);
             dma16(qb + min(r, Cc - 1) * qrow + p * 16, B + SM::oQ + 512 * n);
           }
+        }
+      }
+      if (mine(1)) {
+        if (Cc == kC) {
+#pragma unroll
+          for (int n = 0; n < NV; ++n) dma16(vb + ov[n], B + SM::oV + 512 * n);
+        } else {
 #pragma unroll
           for (int n = 0; n < NV; ++n) {
             int r, p;
@@ -239,17 +257,23 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
       const char* kb = reinterpret_cast<const char*>(w_ktg + ci * (D * kC));
       const char* ab = reinterpret_cast<const char*>(w_a + ci * (kC * kC));
       const char* tb = reinterpret_cast<const char*>(w_tb + ci * (kC * kC));
-      if (ld == NL - 1) {
+      if (mine(2)) {
 #pragma unroll
         for (int n = 0; n < NQ; ++n) dma16c(wb + ow[n], B + SM::oWm + 512 * n);
+      }
+      if (mine(3)) {
 #pragma unroll
         for (int n = 0; n < NK; ++n) dma16c(kb + ok[n], B + SM::oKT + 512 * n);
       }
-      if (ld == 0) {
+      if (mine(4)) {
 #pragma unroll
         for (int n = 0; n < NS; ++n) dma16c(ab + ok[n], B + SM::oA + 512 * n);
+      }
+      if (mine(5)) {
 #pragma unroll
         for (int n = 0; n < NS; ++n) dma16c(tb + ok[n], B + SM::oTB + 512 * n);
+      }
+      if (mine(6)) {
         float* gate = reinterpret_cast<float*>(B + SM::nT);
         dma4c(w_g + ci * (2 * kC) + lane, gate);
         dma4c(w_g + ci * (2 * kC) + 64 + lane, gate + 64);
@@ -454,8 +478,8 @@ hipError_t launch_full_t(const PrefillArgs& p, int nch, hipStream_t s) {
 
 hipError_t launch_gdn_full(const PrefillArgs& p, int nch, hipStream_t s) {
   if (!p.bf16 || p.gla) return hipErrorInvalidValue;
-  if (p.D == 64) return launch_full_t<64, 4, 2>(p, nch, s);
-  if (p.D == 128) return launch_full_t<128, 4, 2>(p, nch, s);
+  if (p.D == 64) return launch_full_t<64, 4, 3>(p, nch, s);
+  if (p.D == 128) return launch_full_t<128, 4, 3>(p, nch, s);
   return hipErrorInvalidValue;
 }
 
