@@ -40,45 +40,45 @@ __device__ __forceinline__ void wave_lds_fence() {
   asm volatile("" ::: "memory");
 }
 
-// Global stores of the preparation's results.  DEV: every store is a
-// device-scope (agent) relaxed atomic store of 8 or 4 bytes, visible to every
-// compute unit once this wave's stores have completed, so that a consumer in
-// the same kernel can read the tiles coherently; else plain stores.
-template <bool DEV>
-__device__ __forceinline__ void put8(void* p, uint64_t x) {
+// Global stores of the preparation's results, at element offset `off` from
+// a wave-uniform base.  DEV: device-scope stores (cache policy sc1, through
+// a buffer resource on the base: written through to memory and visible to
+// every compute unit once complete), so that a consumer in the same kernel
+// can read the tiles coherently; else plain stores.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kCpolSc1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
+}
+template <bool DEV, class T, class V>
+__device__ __forceinline__ void put16(T* base, int off, const V& x) {      // one 16-byte piece
+  static_assert(sizeof(V) == 16, "16 bytes");
   if constexpr (DEV) {
-    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), dev_rsrc(base),
+                                           off * (int)sizeof(T), 0, kCpolSc1);
   } else {
-    *reinterpret_cast<uint64_t*>(p) = x;
+    *reinterpret_cast<V*>(base + off) = x;
   }
 }
 template <bool DEV, class T>
-__device__ __forceinline__ void put4v(T* p, const f32x4& x) {    // 4 values as T
-  if constexpr (DEV && sizeof(T) == 2) {
+__device__ __forceinline__ void put4v(T* base, int off, const f32x4& x) {  // 4 values as T
+  if constexpr (DEV) {
+    static_assert(sizeof(T) == 2, "device-scope stores for bf16 tiles only");
     const bf16x4 y = bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
                             static_cast<bf16>(x[3])};
-    put8<true>(p, __builtin_bit_cast(uint64_t, y));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, y), dev_rsrc(base), off * 2, 0, kCpolSc1);
   } else {
-    static_assert(!DEV || sizeof(T) == 2, "device-scope stores for bf16 tiles only");
-    store4(p, x);
-  }
-}
-template <bool DEV, class V>
-__device__ __forceinline__ void put16(void* p, const V& x) {     // one 16-byte piece
-  if constexpr (DEV) {
-    const uint4 u = __builtin_bit_cast(uint4, x);
-    put8<true>(p, (uint64_t)u.x | ((uint64_t)u.y << 32));
-    put8<true>(reinterpret_cast<char*>(p) + 8, (uint64_t)u.z | ((uint64_t)u.w << 32));
-  } else {
-    *reinterpret_cast<V*>(p) = x;
+    store4(base + off, x);
   }
 }
 template <bool DEV>
-__device__ __forceinline__ void put1f(float* p, float x) {
+__device__ __forceinline__ void put1f(float* base, int off, float x) {
   if constexpr (DEV) {
-    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, x), dev_rsrc(base), off * 4, 0,
+                                          kCpolSc1);
   } else {
-    *p = x;
+    base[off] = x;
   }
 }
 
@@ -197,10 +197,15 @@ template <class T, int D, bool FULL>
 struct PrepSmem {
   static constexpr int PAD = 16 / sizeof(T);
   static constexpr int SC = kC + PAD;       // [*][64] rows
-  static constexpr int oKT = 0;                             // K^T, tokens in acc order
-  static constexpr int oTBG = oKT + (FULL ? D * SC : 0);    // Tm diag(b gamma)
-  static constexpr int oA = oTBG + (FULL ? kC * SC : 0);    // scores
+  // full preparation: K^T (tokens in acc order); the scores A, whose area then
+  // holds TB = Tm diag(b) once A is written out; TBG = Tm diag(b gamma) and
+  // then the chunk's V rows reuse the solve buffer
+  static constexpr int oKT = 0;
+  static constexpr int oA = oKT + (FULL ? D * SC : 0);
   static constexpr int nT = oA + (FULL ? kC * SC : 0);
+  static constexpr int SV = D + PAD;                        // V rows, in the solve buffer
+  static_assert(!FULL || (kC * SV * (int)sizeof(T) <= 4 * kC * kSL && SC * (int)sizeof(T) <= 4 * kSL),
+                "TBG rows and V rows fit the solve buffer");
   static constexpr int bytesT = (nT * (int)sizeof(T) + 15) / 16 * 16;
   static constexpr int nL = kC * kSL;                       // solve buffer
   static constexpr int bytes = bytesT + 4 * (nL + 4 * kC);  // + g, gamma, b, K^T factors
@@ -214,10 +219,11 @@ struct PrepSmem {
 // workgroup barrier: the wave's own LDS operations complete in program order.
 template <class T, int D, bool FULL, bool DEV = false>
 __device__ __forceinline__ void gdn_prep_chunk(
-    const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ a,
-    const float* __restrict__ b, T* __restrict__ wtb, T* __restrict__ wtbg, T* __restrict__ wwm,
-    T* __restrict__ wktg, T* __restrict__ wa, float* __restrict__ wg, int T_, int H, int Hkv,
-    int n_sink, int window, int nch, int c, int h, int bi, unsigned char* smem_raw) {
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ a, const float* __restrict__ b, T* __restrict__ wtb,
+    T* __restrict__ wtbg, T* __restrict__ wwm, T* __restrict__ wktg, T* __restrict__ wa,
+    float* __restrict__ wut, float* __restrict__ wg, int T_, int H, int Hkv, int n_sink, int window,
+    int nch, int c, int h, int bi, unsigned char* smem_raw) {
   using SM = PrepSmem<T, D, FULL>;
   constexpr int EPC = 16 / (int)sizeof(T);     // elements per 16-byte piece
   constexpr int QV = 8 / EPC;                  // 16-byte pieces per fragment
@@ -227,9 +233,10 @@ __device__ __forceinline__ void gdn_prep_chunk(
 
   T* sT = reinterpret_cast<T*>(smem_raw);
   T* KTs = sT + SM::oKT;
-  T* TBGs = sT + SM::oTBG;
   T* As = sT + SM::oA;
+  T* TBs = As;                                 // after A is written out
   float* Lf = reinterpret_cast<float*>(smem_raw + SM::bytesT);
+  T* TBGs = reinterpret_cast<T*>(Lf);          // row r written after Lf row r is read
   float* lgs = Lf + SM::nL;
   float* gam = lgs + kC;
   float* bet = gam + kC;
@@ -343,10 +350,39 @@ __device__ __forceinline__ void gdn_prep_chunk(
           KTs[(32 * p + 8 * lg + i) * SC + acc_pos(16 * mt + l16)] = kr[mt][p][i / EPC][i % EPC];
   }
   wave_lds_fence();
+  if constexpr (FULL) {
+    // ---- A [64][64] out now, so that its area can take TB
+    T* aa = wa + ci * (kC * kC);
+#pragma unroll
+    for (int i = lane; i < kC * (kC / EPC); i += 64) {
+      const int r = i / (kC / EPC);
+      const int pc = (i % (kC / EPC)) * EPC;
+      put16<DEV>(aa, r * kC + pc, *reinterpret_cast<const V16*>(&As[r * SC + pc]));
+    }
+  }
   unit_lower_inverse_wave(Lf, lane);
 
+  // full preparation: the chunk's V rows (zero past the stream end), loaded
+  // now and staged once the solve buffer is free
+  constexpr int NPV = FULL ? kC * D / EPC / 64 : 1;
+  V16 vr[NPV];
+  if constexpr (FULL) {
+#pragma unroll
+    for (int n = 0; n < NPV; ++n) {
+      const int j = lane + 64 * n;
+      const int r = j / (D / EPC);
+      if (whole || i0 + r < iend) {
+        vr[n] = *reinterpret_cast<const V16*>(v + ((size_t)(bi * T_ + i0 + r) * Hkv + g) * D + (j % (D / EPC)) * EPC);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) vr[n][e] = from_f32<T>(0.f);
+      }
+    }
+  }
+
   // ---- TB = Tm diag(b) (and TBG = Tm diag(b gamma)): row r, columns
-  // s0..s0+3 at positions acc_pos(s0)..+3 of the row
+  // s0..s0+3 at positions acc_pos(s0)..+3 of the row; the full preparation
+  // keeps both in LDS
   T* tb = wtb + ci * (kC * kC);
 #pragma unroll 4
   for (int i = lane; i < kC * kC / 4; i += 64) {
@@ -356,12 +392,16 @@ __device__ __forceinline__ void gdn_prep_chunk(
     const f32x4 bb = *reinterpret_cast<const f32x4*>(&bet[s0]);
     const f32x4 gg = *reinterpret_cast<const f32x4*>(&gam[s0]);
     const f32x4 x = tm * bb;
-    put4v<DEV>(tb + r * kC + acc_pos(s0), x);
-    if (FULL) store4(&TBGs[r * SC + acc_pos(s0)], x * gg);
-    else put4v<DEV>(wtbg + ci * (kC * kC) + r * kC + acc_pos(s0), x * gg);
+    if constexpr (FULL) {
+      store4(&TBs[r * SC + acc_pos(s0)], x);
+      store4(&TBGs[r * SC + acc_pos(s0)], x * gg);
+    } else {
+      put4v<DEV>(tb, r * kC + acc_pos(s0), x);
+      put4v<DEV>(wtbg + ci * (kC * kC), r * kC + acc_pos(s0), x * gg);
+    }
   }
-  put1f<DEV>(&wg[ci * (2 * kC) + lane], lgs[lane]);
-  put1f<DEV>(&wg[ci * (2 * kC) + kC + lane], gam[lane]);
+  put1f<DEV>(wg + ci * (2 * kC), lane, lgs[lane]);
+  put1f<DEV>(wg + ci * (2 * kC), kC + lane, gam[lane]);
   if constexpr (FULL) {
     wave_lds_fence();
     // ---- -Wm = -(TBG K): per 16-row dk tile, Wm^T = K^T TBG^T on MFMA,
@@ -377,13 +417,12 @@ __device__ __forceinline__ void gdn_prep_chunk(
         f32x4 acc = zero4();
 #pragma unroll
         for (int p = 0; p < 2; ++p) acc = mfma(kf[p], lds_frag8(&TBGs[(16 * nt + l16) * SC + 32 * p + 8 * lg]), acc);
-        put4v<DEV>(wm + (16 * nt + l16) * D + 16 * mt + 4 * lg, -acc);
+        put4v<DEV>(wm, (16 * nt + l16) * D + 16 * mt + 4 * lg, -acc);
       }
     }
     // ---- K^T 2^{g_C - g} [D][64] (row r holds d_k index acc_pos(r), the
-    // state row order of the scan's accumulators) and A [64][64], 16-byte pieces
+    // state row order of the scan's accumulators), 16-byte pieces
     T* ktg = wktg + ci * (D * kC);
-    T* aa = wa + ci * (kC * kC);
 #pragma unroll 4
     for (int i = lane; i < D * (kC / EPC); i += 64) {
       const int r = i / (kC / EPC);
@@ -392,13 +431,43 @@ __device__ __forceinline__ void gdn_prep_chunk(
       V16 y;
 #pragma unroll
       for (int e = 0; e < EPC; ++e) y[e] = from_f32<T>(to_f32(x[e]) * fac[pc + e]);
-      put16<DEV>(ktg + r * kC + pc, y);
+      put16<DEV>(ktg, r * kC + pc, y);
     }
+    // ---- Ut = TB V [64][D] in fp32, written transposed as [D][64] (the
+    // scan reads each column's 4 consecutive tokens as one 16-byte piece):
+    // V rows staged in the solve buffer (TBG is no longer needed), V operands gathered
+    // column-wise (slot j of lane group lg is token 32 p + 16 (j / 4) + 4 lg + j % 4)
+    T* Vs = reinterpret_cast<T*>(Lf);
 #pragma unroll
-    for (int i = lane; i < kC * (kC / EPC); i += 64) {
-      const int r = i / (kC / EPC);
-      const int pc = (i % (kC / EPC)) * EPC;
-      put16<DEV>(aa + r * kC + pc, *reinterpret_cast<const V16*>(&As[r * SC + pc]));
+    for (int n = 0; n < NPV; ++n) {
+      const int j = lane + 64 * n;
+      *reinterpret_cast<V16*>(&Vs[(j / (D / EPC)) * SM::SV + (j % (D / EPC)) * EPC]) = vr[n];
+    }
+    wave_lds_fence();
+    Frag<T> tf[4][2];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) tf[rt][p] = lds_frag8(&TBs[(16 * rt + l16) * SC + 32 * p + 8 * lg]);
+    float* ut = wut + ci * (D * kC);
+#pragma unroll 2
+    for (int ct = 0; ct < D / 16; ++ct) {
+      Frag<T> vf[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        float x[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          x[jj] = to_f32(Vs[(32 * p + 16 * (jj / 4) + 4 * lg + jj % 4) * SM::SV + 16 * ct + l16]);
+        vf[p] = frag_from8<T>(x);
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int p = 0; p < 2; ++p) acc = mfma(tf[rt][p], vf[p], acc);
+        put16<DEV>(ut, (16 * ct + l16) * kC + 16 * rt + 4 * lg, acc);
+      }
     }
   }
 }

@@ -16,13 +16,14 @@ using prep::PrepSmem;
 
 template <class T, int D, bool FULL>
 __global__ __launch_bounds__(64) void gdn_prep_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ a,
-    const float* __restrict__ b, T* __restrict__ wtb, T* __restrict__ wtbg, T* __restrict__ wwm,
-    T* __restrict__ wktg, T* __restrict__ wa, float* __restrict__ wg, int T_, int H, int Hkv,
-    int n_sink, int window, int nch) {
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ a, const float* __restrict__ b, T* __restrict__ wtb,
+    T* __restrict__ wtbg, T* __restrict__ wwm, T* __restrict__ wktg, T* __restrict__ wa,
+    float* __restrict__ wut, float* __restrict__ wg, int T_, int H, int Hkv, int n_sink,
+    int window, int nch) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  prep::gdn_prep_chunk<T, D, FULL>(q, k, a, b, wtb, wtbg, wwm, wktg, wa, wg, T_, H, Hkv, n_sink,
-                                   window, nch, blockIdx.x, blockIdx.y, blockIdx.z, smem_raw);
+  prep::gdn_prep_chunk<T, D, FULL>(q, k, v, a, b, wtb, wtbg, wwm, wktg, wa, wut, wg, T_, H, Hkv,
+                                   n_sink, window, nch, blockIdx.x, blockIdx.y, blockIdx.z, smem_raw);
 }
 
 template <class T, int D, bool FULL>
@@ -33,8 +34,8 @@ hipError_t launch_prep_t(const PrefillArgs& p, int nch, hipStream_t s) {
   if (e != hipSuccess) return e;
   const GdnWorkspace w = gdn_workspace_layout(p.workspace, p.B, p.H, nch, D, sizeof(T), FULL);
   hipLaunchKernelGGL(kern, dim3(nch, p.H, p.B), dim3(64), SM::bytes, s, (const T*)p.q,
-                     (const T*)p.k, p.a, p.b, (T*)w.tb, (T*)w.tbg, (T*)w.wm, (T*)w.ktg, (T*)w.a, w.g,
-                     p.T, p.H, p.Hkv, p.n_sink, p.window, nch);
+                     (const T*)p.k, (const T*)p.v, p.a, p.b, (T*)w.tb, (T*)w.tbg, (T*)w.wm,
+                     (T*)w.ktg, (T*)w.a, w.ut, w.g, p.T, p.H, p.Hkv, p.n_sink, p.window, nch);
   return hipGetLastError();
 }
 
@@ -63,8 +64,8 @@ GdnWorkspace gdn_workspace_layout(void* base, int B, int H, int nch, int D, size
   const size_t n = (size_t)B * H * nch;
   unsigned char* p = static_cast<unsigned char*>(base);
   size_t off = 0;
-  w.tb = p + off;
-  off += n * kC * kC * elt;
+  w.tb = full ? nullptr : p + off;
+  off += full ? 0 : n * kC * kC * elt;
   w.tbg = full ? nullptr : p + off;
   off += full ? 0 : n * kC * kC * elt;
   w.wm = full ? p + off : nullptr;
@@ -73,6 +74,8 @@ GdnWorkspace gdn_workspace_layout(void* base, int B, int H, int nch, int D, size
   off += full ? n * D * kC * elt : 0;
   w.a = full ? p + off : nullptr;
   off += full ? n * kC * kC * elt : 0;
+  w.ut = full ? reinterpret_cast<float*>(p + off) : nullptr;
+  off += full ? n * D * kC * sizeof(float) : 0;
   w.g = reinterpret_cast<float*>(p + off);
   off += n * 2 * kC * sizeof(float);
   w.ready = full ? reinterpret_cast<uint64_t*>(p + off) : nullptr;

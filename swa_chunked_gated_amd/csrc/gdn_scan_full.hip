@@ -9,8 +9,8 @@
 // 填补近似缺口的实用设计 has the recurrence cover only evicted tokens, read
 // with lag `window`: o_lin[t] = S^(t-window)^T q_t.  Chunk form (64 stream
 // tokens, incoming state S; derived by unrolling the recurrence):
-//   U = TB V - Wm S,   O = diag(gamma) Q S + A U,   S <- gamma_C S + KTg U
-// with TB = Tm diag(b), Wm = Tm diag(b gamma) K, KTg = K^T diag(gamma_C /
+//   U = Ut - Wm S,   O = diag(gamma) Q S + A U,   S <- gamma_C S + KTg U
+// with Ut = Tm diag(b) V, Wm = Tm diag(b gamma) K, KTg = K^T diag(gamma_C /
 // gamma) and A the decayed causal scores, all read from the preparation.
 //
 // Work split: one workgroup per (sequence, head, 16 * NW state columns) with
@@ -38,7 +38,6 @@ namespace gdn {
 namespace {
 
 constexpr int kC = 64;   // chunk length
-typedef unsigned short ushort8 __attribute__((ext_vector_type(8)));
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(1))) void* gbl_void_ptr;
@@ -62,16 +61,16 @@ struct FullSmem {
   static constexpr int SK = D + 8;          // row stride of [64][D] tiles (elements)
   static constexpr int SC = kC + 8;         // row stride of [*][64] tiles
   static constexpr int DVS = 16 * NW;       // state columns per workgroup
-  static constexpr int SV = DVS + 8;        // row stride of the V slice
-  // one buffer: Q, -Wm, KTg, A, TB, V (bf16), then g (log2), gamma [64 each] fp32
+  static constexpr int SU = kC + 4;         // fp32 row stride of Ut^T
+  // one buffer: Q, -Wm, KTg, A (bf16), then Ut^T [DVS][SU], g (log2), gamma
+  // [64 each] fp32
   static constexpr int oQ = 0;
   static constexpr int oWm = oQ + kC * SK;
   static constexpr int oKT = oWm + kC * SK;
   static constexpr int oA = oKT + D * SC;
-  static constexpr int oTB = oA + kC * SC;
-  static constexpr int oV = oTB + kC * SC;
-  static constexpr int nT = oV + kC * SV;
-  static constexpr int buf_bytes = nT * 2 + 2 * kC * 4;
+  static constexpr int nT = oA + kC * SC;
+  static constexpr int nU = DVS * SU;
+  static constexpr int buf_bytes = nT * 2 + 4 * nU + 2 * kC * 4;
   static constexpr int bytes = 2 * buf_bytes;
   static_assert((nT * 2) % 16 == 0, "16-byte tiles");
 };
@@ -92,7 +91,16 @@ __device__ __forceinline__ void wait_ready(const uint64_t* f, uint64_t epoch) {
 }
 
 // Preparation waves per preparation workgroup (each needs its own PrepSmem).
-constexpr int kPrepWaves = 2;
+constexpr int kPrepWaves = 3;
+
+// Dynamic LDS of the fused kernel: the scan's two buffers, or the
+// preparation waves' work areas, whichever is larger.
+template <int D, int NW>
+constexpr int fused_lds_bytes() {
+  constexpr int scan = FullSmem<D, NW>::bytes;
+  constexpr int prep = kPrepWaves * prep::PrepSmem<bf16, D, true>::bytes;
+  return scan > prep ? scan : prep;
+}
 
 // Grid: n_prep preparation workgroups first, then one scan workgroup per
 // (sequence, head, column slice).  With n_prep = 0 the workspace is already
@@ -106,15 +114,15 @@ constexpr int kPrepWaves = 2;
 template <int D, int NW, int NL>
 __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const float* __restrict__ a, const float* __restrict__ b, bf16* __restrict__ w_tb,
-    bf16* __restrict__ w_wm, bf16* __restrict__ w_ktg, bf16* __restrict__ w_a,
+    const float* __restrict__ a, const float* __restrict__ b, bf16* __restrict__ w_wm,
+    bf16* __restrict__ w_ktg, bf16* __restrict__ w_a, float* __restrict__ w_ut,
     float* __restrict__ w_g, uint64_t* __restrict__ ready, uint64_t epoch, int n_prep,
     bf16* __restrict__ o, float* __restrict__ state_out, int B, int T_, int H, int Hkv,
     int n_sink, int window, int flags) {
   using SM = FullSmem<D, NW>;
   using PS = prep::PrepSmem<bf16, D, true>;
   static_assert(NL >= 1 && NL <= 4, "one to four loader waves");
-  static_assert(kPrepWaves * PS::bytes <= SM::bytes && PS::bytes % 16 == 0, "preparation LDS");
+  static_assert(PS::bytes % 16 == 0 && fused_lds_bytes<D, NW>() <= 160 * 1024, "LDS of one workgroup");
   constexpr int SK = SM::SK;
   constexpr int SC = SM::SC;
   constexpr int DVS = SM::DVS;
@@ -137,9 +145,9 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
     for (int it = blockIdx.x * kPrepWaves + wv; it < nch * BH; it += n_prep * kPrepWaves) {
       const int c = it / BH;
       const int bh = it % BH;
-      prep::gdn_prep_chunk<bf16, D, true, true>(q, k, a, b, w_tb, nullptr, w_wm, w_ktg, w_a, w_g, T_,
-                                                H, Hkv, n_sink, window, nch, c, bh % H, bh / H,
-                                                smem_raw + wv * PS::bytes);
+      prep::gdn_prep_chunk<bf16, D, true, true>(q, k, v, a, b, nullptr, nullptr, w_wm, w_ktg, w_a,
+                                                w_ut, w_g, T_, H, Hkv, n_sink, window, nch, c,
+                                                bh % H, bh / H, smem_raw + wv * PS::bytes);
       // every device-scope tile store of this wave has completed (vmcnt 0)
       // before the flag is stored
       asm volatile("" ::: "memory");
@@ -163,11 +171,11 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
 
   if (wv >= NW) {
     // ======================= loader waves: tile t of a chunk is loaded by
-    // loader kOwner[NL - 1][t] (tiles: Q, V, -Wm, KTg, A, TB, gates)
-    constexpr int kOwner[4][7] = {{0, 0, 0, 0, 0, 0, 0},
-                                  {0, 0, 1, 1, 0, 0, 0},
-                                  {0, 0, 1, 2, 1, 2, 2},
-                                  {0, 3, 1, 2, 3, 3, 0}};
+    // loader kOwner[NL - 1][t] (tiles: Q, Ut^T, -Wm, KTg, A, gates)
+    constexpr int kOwner[4][6] = {{0, 0, 0, 0, 0, 0},
+                                  {0, 0, 1, 1, 0, 0},
+                                  {0, 2, 1, 2, 0, 0},
+                                  {0, 3, 1, 2, 3, 0}};
     const int ld = wv - NW;
     auto mine = [&](int t) { return kOwner[NL - 1][t] == ld; };
     // Every LDS image is whole 1 KiB blocks of 16-byte slots; slot s = 64 n +
@@ -175,21 +183,19 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
     // piece of a row is padding and repeats piece 0).  The per-lane byte
     // offsets of the source pieces are the same for every chunk, so they are
     // formed once here and each load is a uniform base plus a lane offset.
-    constexpr int PV = DVS / 8;                      // pieces of a V slice row
     constexpr int NQ = kC * (P + 1) / 64;            // blocks of the Q and -Wm images
-    constexpr int NV = kC * (PV + 1) / 64;           // blocks of the V image
+    constexpr int NU = DVS * 17 / 64;                // blocks of the Ut^T image ([DVS][64] fp32)
     constexpr int NK = D * 9 / 64;                   // blocks of the KTg image ([D][64])
-    constexpr int NS = kC * 9 / 64;                  // blocks of the TB and A images
-    static_assert((kC * (PV + 1)) % 64 == 0 && (D * 9) % 64 == 0, "whole 1 KiB blocks");
+    constexpr int NS = kC * 9 / 64;                  // blocks of the A image
+    static_assert((DVS * 17) % 64 == 0 && (D * 9) % 64 == 0, "whole 1 KiB blocks");
     const size_t qrow = (size_t)H * D * 2;           // bytes between query rows
-    const size_t vrow = (size_t)Hkv * D * 2;         // bytes between V rows
     auto piece = [&](int n, int pp, int& r, int& p) {
       const int s = 64 * n + lane;
       r = s / (pp + 1);
       p = s % (pp + 1);
       if (p == pp) p = 0;
     };
-    uint32_t oq[NQ], ow[NQ], ov[NV], ok[NK];
+    uint32_t oq[NQ], ow[NQ], ou[NU], ok[NK];
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
       int r, p;
@@ -198,10 +204,10 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
       ow[n] = (uint32_t)((r * P + p) * 16);
     }
 #pragma unroll
-    for (int n = 0; n < NV; ++n) {
+    for (int n = 0; n < NU; ++n) {
       int r, p;
-      piece(n, PV, r, p);
-      ov[n] = (uint32_t)(r * vrow + p * 16);
+      piece(n, 16, r, p);
+      ou[n] = (uint32_t)(((c0 + r) * kC + 4 * p) * 4);    // column c0 + r of Ut^T
     }
 #pragma unroll
     for (int n = 0; n < NK; ++n) {
@@ -222,11 +228,9 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
         asm volatile("" ::: "memory");
         seen = c + 1 < nch ? __hip_atomic_load(ready + ci + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
       }
-      // query rows i0 + window + r and V rows i0 + r; in a partial chunk the
-      // rows past the stream repeat its last row (their outputs are never
-      // stored, and TB's columns for them are zero)
+      // query rows i0 + window + r; in a partial chunk the rows past the
+      // stream repeat its last row (their outputs are never stored)
       const char* qb = reinterpret_cast<const char*>(q + ((size_t)(bi * T_ + i0 + window) * H + h) * D);
-      const char* vb = reinterpret_cast<const char*>(v + ((size_t)(bi * T_ + i0) * Hkv + g) * D + c0);
       if (mine(0)) {
         if (Cc == kC) {
 #pragma unroll
@@ -241,22 +245,14 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
         }
       }
       if (mine(1)) {
-        if (Cc == kC) {
+        const char* ub = reinterpret_cast<const char*>(w_ut + ci * (D * kC));
+        float* U = reinterpret_cast<float*>(B + SM::nT);
 #pragma unroll
-          for (int n = 0; n < NV; ++n) dma16(vb + ov[n], B + SM::oV + 512 * n);
-        } else {
-#pragma unroll
-          for (int n = 0; n < NV; ++n) {
-            int r, p;
-            piece(n, PV, r, p);
-            dma16(vb + min(r, Cc - 1) * vrow + p * 16, B + SM::oV + 512 * n);
-          }
-        }
+        for (int n = 0; n < NU; ++n) dma16c(ub + ou[n], U + 256 * n);
       }
       const char* wb = reinterpret_cast<const char*>(w_wm + ci * (kC * D));
       const char* kb = reinterpret_cast<const char*>(w_ktg + ci * (D * kC));
       const char* ab = reinterpret_cast<const char*>(w_a + ci * (kC * kC));
-      const char* tb = reinterpret_cast<const char*>(w_tb + ci * (kC * kC));
       if (mine(2)) {
 #pragma unroll
         for (int n = 0; n < NQ; ++n) dma16c(wb + ow[n], B + SM::oWm + 512 * n);
@@ -270,11 +266,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
         for (int n = 0; n < NS; ++n) dma16c(ab + ok[n], B + SM::oA + 512 * n);
       }
       if (mine(5)) {
-#pragma unroll
-        for (int n = 0; n < NS; ++n) dma16c(tb + ok[n], B + SM::oTB + 512 * n);
-      }
-      if (mine(6)) {
-        float* gate = reinterpret_cast<float*>(B + SM::nT);
+        float* gate = reinterpret_cast<float*>(B + SM::nT) + SM::nU;
         dma4c(w_g + ci * (2 * kC) + lane, gate);
         dma4c(w_g + ci * (2 * kC) + 64 + lane, gate + 64);
       }
@@ -301,9 +293,8 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
     const bf16* Wms = B + SM::oWm;
     const bf16* KTs = B + SM::oKT;
     const bf16* Aqs = B + SM::oA;
-    const bf16* TBs = B + SM::oTB;
-    const bf16* Vs = B + SM::oV;
-    const float* gam = reinterpret_cast<const float*>(B + SM::nT) + kC;
+    const float* UTs = reinterpret_cast<const float*>(B + SM::nT);
+    const float* gam = UTs + SM::nU + kC;
     const int i0 = n_sink + c * kC;
     const int Cc = min(kC, iend - i0);
 
@@ -329,29 +320,11 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
         for (int rt = 0; rt < 4; ++rt) ot[rt] = mfma(sf[2 * ph + pp], qf[rt][pp], ot[rt]);
     }
 
-    // U = TB V - Wm S   (tokens x this wave's 16 columns)
+    // U = Ut - Wm S   (tokens x this wave's 16 columns): the accumulators
+    // start from Ut (rows 16 mt + 4 lg .. +3 of column cw + l16)
     f32x4 U[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) U[mt] = zero4();
-    {
-      // V operand of column cw + l16: tokens in acc order, gathered from the
-      // token-major V rows (slot j <-> token 32 p + 16 (j / 4) + 4 lg + j % 4)
-      Frag<bf16> vf[2], tf[4][2];
-      const unsigned short* vcol = reinterpret_cast<const unsigned short*>(Vs) + cw + l16;
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        ushort8 x;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = vcol[(32 * p + 16 * (j / 4) + 4 * lg + j % 4) * SM::SV];
-        vf[p].v = __builtin_bit_cast(bf16x8, x);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) tf[mt][p] = lds_frag8(&TBs[(16 * mt + l16) * SC + 32 * p + 8 * lg]);
-      }
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) U[mt] = mfma(tf[mt][p], vf[p], U[mt]);
-    }
+    for (int mt = 0; mt < 4; ++mt) U[mt] = *reinterpret_cast<const f32x4*>(&UTs[(cw + l16) * SM::SU + 16 * mt + 4 * lg]);
 #pragma unroll
     for (int ph = 0; ph < D / 64; ++ph) {
       Frag<bf16> wf[4][2];
@@ -449,8 +422,9 @@ uint64_t next_epoch() {
 template <int D, int NW, int NL>
 hipError_t launch_full_t(const PrefillArgs& p, int nch, hipStream_t s) {
   using SM = FullSmem<D, NW>;
+  constexpr int lds = fused_lds_bytes<D, NW>();
   auto kern = gdn_scan_full_kernel<D, NW, NL>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, SM::bytes);
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const GdnWorkspace w = gdn_workspace_layout(p.workspace, p.B, p.H, nch, D, sizeof(bf16), true);
   const int n_scan = p.B * p.H * (D / SM::DVS);
@@ -467,9 +441,9 @@ hipError_t launch_full_t(const PrefillArgs& p, int nch, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const uint64_t epoch = n_prep > 0 ? next_epoch() : 0;
-  hipLaunchKernelGGL(kern, dim3(n_prep + n_scan), dim3(64 * (NW + NL)), SM::bytes, s,
-                     (const bf16*)p.q, (const bf16*)p.k, (const bf16*)p.v, p.a, p.b, (bf16*)w.tb,
-                     (bf16*)w.wm, (bf16*)w.ktg, (bf16*)w.a, w.g, w.ready, epoch, n_prep,
+  hipLaunchKernelGGL(kern, dim3(n_prep + n_scan), dim3(64 * (NW + NL)), lds, s,
+                     (const bf16*)p.q, (const bf16*)p.k, (const bf16*)p.v, p.a, p.b, (bf16*)w.wm,
+                     (bf16*)w.ktg, (bf16*)w.a, w.ut, w.g, w.ready, epoch, n_prep,
                      (bf16*)p.o, p.state_out, p.B, p.T, p.H, p.Hkv, p.n_sink, p.window, p.flags);
   return hipGetLastError();
 }
@@ -478,8 +452,8 @@ hipError_t launch_full_t(const PrefillArgs& p, int nch, hipStream_t s) {
 
 hipError_t launch_gdn_full(const PrefillArgs& p, int nch, hipStream_t s) {
   if (!p.bf16 || p.gla) return hipErrorInvalidValue;
-  if (p.D == 64) return launch_full_t<64, 4, 3>(p, nch, s);
-  if (p.D == 128) return launch_full_t<128, 4, 3>(p, nch, s);
+  if (p.D == 64) return launch_full_t<64, 4, 4>(p, nch, s);
+  if (p.D == 128) return launch_full_t<128, 4, 4>(p, nch, s);
   return hipErrorInvalidValue;
 }
 

@@ -26,17 +26,19 @@ struct PrefillArgs {
 
 // Workspace of the gated delta rule prefill, per (sequence, head, chunk), as
 // consecutive arrays (I/O element type; token reduction index in acc order):
-//   TB = Tm diag(b) [64][64]; then either (light preparation) TBG =
-//   Tm diag(b gamma) [64][64], or (full preparation, bf16) -Wm [64][D] with
-//   d_k in natural order, K^T 2^{g_C - g} [D][64] whose row r holds d_k index
-//   acc_pos(r), and the scores A [64][64]; then g, gamma [2][64] fp32; the
-//   full preparation ends with one uint64 ready flag per chunk.
+//   light preparation: TB = Tm diag(b) [64][64], TBG = Tm diag(b gamma)
+//   [64][64], then g, gamma [2][64] fp32;
+//   full preparation (bf16): -Wm [64][D] with d_k in natural order,
+//   K^T 2^{g_C - g} [D][64] whose row r holds d_k index acc_pos(r), the
+//   scores A [64][64], (TB V)^T [D][64] fp32 (tokens in natural order),
+//   g, gamma [2][64] fp32, and one uint64 ready flag per chunk.
 struct GdnWorkspace {
   void* tb;
   void* tbg;
   void* wm;
   void* ktg;
   void* a;
+  float* ut;         // full preparation: (Tm diag(b) V)^T [D][64] fp32
   float* g;
   uint64_t* ready;   // full preparation: per-chunk ready flags
   size_t bytes;
