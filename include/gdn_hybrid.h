@@ -105,11 +105,15 @@ int gdn_hybrid_last_hip_error(void);
  * scan over chunks only does the state-dependent products.  With
  * nch = ceil((T - window - n_sink) / 64) and elt the size of `dtype`:
  *   GDN_DELTA, few chains (bf16 and B * H * dk / 64 < 256): B * H * nch *
- *     ((64 * 64 + 2 * 64 * dk) * elt + 64 * dk * 4 + 128 * 4 + 8) bytes
+ *     ((64 * 64 + 2 * 64 * dk) * elt + 64 * dk * 4 + 128 * 4 + 8 + dk / 2)
+ *     bytes
  *     (Wm, the decayed K^T, the decayed causal scores, the inverse of the
  *     chunk's unit lower-triangular system applied to b * V in fp32, the
- *     gate prefix sums: every state-independent chunk product, and a ready
- *     flag per chunk; about 150 MB for B=1, H=32, T=4096).  The flags need
+ *     gate prefix sums: every state-independent chunk product, and flags
+ *     that hand each chunk from the preparation to the scan and from the
+ *     scan to the softmax branch; about 150 MB for B=1, H=32, T=4096).  With
+ *     both branches, no GDN_ACCUMULATE and a multiple of 4 query heads per
+ *     KV head, the whole layer is one launch.  The flags need
  *     no initialisation; a workspace must not be shared by calls that may
  *     run concurrently;
  *   GDN_DELTA otherwise: B * H * nch * (2 * 64 * 64 * elt + 128 * 4) bytes

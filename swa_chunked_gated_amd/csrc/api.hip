@@ -117,11 +117,12 @@ int gdn_hybrid_prefill(const void* q, const void* k, const void* v, const float*
   // overwrite, zeroes rows t < N itself; the softmax kernel then adds what o
   // holds on rows t >= add_from.
   const bool run_linear = wst || (lin && T > N);
+  bool swa_done = false;
   if (run_linear) {
-    int rc = launched(gdn::launch_linear_prefill(p, s));
+    int rc = launched(gdn::launch_linear_prefill(p, s, &swa_done));
     if (rc) return rc;
   }
-  if (swa) {
+  if (swa && !swa_done) {
     const int add_from = acc ? 0 : ((lin && T > N) ? N : T);
     return launched(gdn::launch_swa_prefill(p, add_from, s));
   }

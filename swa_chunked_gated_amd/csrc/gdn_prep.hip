@@ -80,6 +80,8 @@ GdnWorkspace gdn_workspace_layout(void* base, int B, int H, int nch, int D, size
   off += n * 2 * kC * sizeof(float);
   w.ready = full ? reinterpret_cast<uint64_t*>(p + off) : nullptr;
   off += full ? n * sizeof(uint64_t) : 0;
+  w.done = full ? reinterpret_cast<uint64_t*>(p + off) : nullptr;
+  off += full ? n * (D / 16) * sizeof(uint64_t) : 0;
   w.bytes = off;
   return w;
 }

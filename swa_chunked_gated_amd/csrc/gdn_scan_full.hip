@@ -33,9 +33,12 @@
 #include "common.h"
 #include "gdn_prep.h"
 #include "launch.h"
+#include "swa_tile.h"
 
 namespace gdn {
 namespace {
+
+using swa::wait_ready;
 
 constexpr int kC = 64;   // chunk length
 
@@ -75,23 +78,10 @@ struct FullSmem {
   static_assert((nT * 2) % 16 == 0, "16-byte tiles");
 };
 
-// Waits until the preparation has published chunk `f` (flag == epoch).  The
-// flag is read at device scope and the chunk's tiles are then read with
-// device-scope loads issued after the flag was seen (the wave issues in
-// order; the asm keeps the compiler from moving loads above the loop).
-// Bounded: after about 0.1 s it gives up, so a missing producer can never
-// hang the GPU (the results would then be wrong, never the machine stuck).
-__device__ __forceinline__ void wait_ready(const uint64_t* f, uint64_t epoch) {
-  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();          // 100 MHz
-  while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
-    __builtin_amdgcn_s_sleep(1);
-    if (__builtin_amdgcn_s_memrealtime() - t0 > 10000000ull) break;
-  }
-  asm volatile("" ::: "memory");
-}
-
 // Preparation waves per preparation workgroup (each needs its own PrepSmem).
 constexpr int kPrepWaves = 3;
+// Query tiles per softmax workgroup (one continuous K/V prefetch pipeline).
+constexpr int kSwaTiles = 1;
 
 // Dynamic LDS of the fused kernel: the scan's two buffers, or the
 // preparation waves' work areas, whichever is larger.
@@ -102,23 +92,30 @@ constexpr int fused_lds_bytes() {
   return scan > prep ? scan : prep;
 }
 
-// Grid: n_prep preparation workgroups first, then one scan workgroup per
-// (sequence, head, column slice).  With n_prep = 0 the workspace is already
-// complete (the preparation kernel ran before) and nothing waits.  Otherwise
-// preparation waves take (chunk, head, sequence) items in chunk-major order,
-// write the chunk's tiles and then publish flags[(b H + h) nch + c] = epoch
-// (device-scope release); the scan's loader waves wait for that flag before
-// loading the chunk.  Preparation workgroups never wait and come first in the
-// grid, so they are all dispatched before any scan workgroup: the waits
-// always end.
+// Grid, in dispatch order: n_prep preparation workgroups, one scan workgroup
+// per (sequence, head, column slice), then n_swa softmax workgroups.
+//  * With n_prep = 0 the workspace is already complete (the preparation
+//    kernel ran before) and the scan waits for nothing.  Otherwise
+//    preparation waves take (chunk, head, sequence) items in chunk-major
+//    order, write the chunk's tiles with device-scope stores (written through
+//    to memory), wait for them to complete and publish
+//    ready[(b H + h) nch + c] = epoch; the scan's loader waves wait for that
+//    flag and then read the tiles with device-scope loads.
+//  * With n_swa > 0 the softmax branch is part of the kernel: the scan stores
+//    its rows at device scope and publishes them chunk by chunk (done flags);
+//    a softmax workgroup computes its tile and, before adding onto rows that
+//    hold the linear branch, waits for the flags of the chunks covering them.
+// Every wait is on work of an earlier part of the grid, which is dispatched
+// in full before the waiting workgroups (preparation workgroups wait for
+// nothing, scan workgroups only for preparation), so the waits always end.
 template <int D, int NW, int NL>
 __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ a, const float* __restrict__ b, bf16* __restrict__ w_wm,
     bf16* __restrict__ w_ktg, bf16* __restrict__ w_a, float* __restrict__ w_ut,
     float* __restrict__ w_g, uint64_t* __restrict__ ready, uint64_t epoch, int n_prep,
-    bf16* __restrict__ o, float* __restrict__ state_out, int B, int T_, int H, int Hkv,
-    int n_sink, int window, int flags) {
+    uint64_t* __restrict__ done, int n_swa, bf16* __restrict__ o, float* __restrict__ state_out,
+    int B, int T_, int H, int Hkv, int n_sink, int window, int flags) {
   using SM = FullSmem<D, NW>;
   using PS = prep::PrepSmem<bf16, D, true>;
   static_assert(NL >= 1 && NL <= 4, "one to four loader waves");
@@ -156,6 +153,23 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
       if (lane == 0)
         __hip_atomic_store(ready + (size_t)bh * nch + c, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    return;
+  }
+
+  const int n_scan = B * H * (D / DVS);
+  if ((int)blockIdx.x >= n_prep + n_scan) {
+    // ======================= softmax workgroup: kSwaTiles consecutive tiles
+    // of 64 query rows of the 4 query heads of a KV head (workgroups in row
+    // order), adding onto the linear output once the scan has published it.
+    // These come last in the grid and start as preparation workgroups finish.
+    const int wg = blockIdx.x - n_prep - n_scan;
+    const int groups = H / 4;
+    const int bx = wg / (groups * B);
+    const int rest = wg % (groups * B);
+    swa::swa_tiles<bf16, D, NW + NL, true>(q, k, v, o, T_, H, Hkv, 4, 64, kSwaTiles, n_sink, window,
+                                           n_sink + window, bx, rest % groups, rest / groups,
+                                           reinterpret_cast<bf16*>(smem_raw), done, epoch, nch,
+                                           (D / DVS) * NW);
     return;
   }
 
@@ -286,8 +300,24 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) S[mt] = zero4();
 
+  // linked softmax tiles read this wave's output rows of chunk c once
+  // done[((b H + h) nch + c) (D / DVS) NW + sp NW + wave] = epoch; it is set
+  // six chunks later, when the rows' device-scope stores have completed
+  // (vmcnt counts this wave's stores in order: waiting until at most the
+  // twenty row stores of the five previous chunks are outstanding)
+  const size_t done0 = chain * nch * (D / DVS) * NW + sp * NW + wv;
+  auto publish = [&](int c) {
+    if (lane == 0)
+      __hip_atomic_store(done + done0 + (size_t)c * (D / DVS) * NW, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
   for (int c = 0; c < nch; ++c) {
     lds_barrier();                     // chunk c's buffer is complete
+    if (n_swa > 0 && c >= 6) {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0x4F74);   // vmcnt(20)
+      asm volatile("" ::: "memory");
+      publish(c - 6);
+    }
     const bf16* B = buf(c & 1);
     const bf16* Qs = B + SM::oQ;
     const bf16* Wms = B + SM::oWm;
@@ -382,11 +412,29 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
         if (r < Cc) {
           bf16* orow = o + ((size_t)(bi * T_ + i0 + r + window) * H + h) * D + c0 + cw + 4 * lg;
           f32x4 val = ot[rt];
-          if (accumulate) val += load4(orow);
-          store4(orow, val);
+          if (n_swa > 0) {
+            // device-scope store (read by the linked softmax tiles)
+            const bf16x4 y = bf16x4{static_cast<bf16>(val[0]), static_cast<bf16>(val[1]),
+                                    static_cast<bf16>(val[2]), static_cast<bf16>(val[3])};
+            bf16* obase = o + ((size_t)(bi * T_ + i0 + window) * H + h) * D + c0 + cw;
+            typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, y),
+                                                  __builtin_amdgcn_make_buffer_rsrc(obase, 0, 0x7fffffff, 0x00020000),
+                                                  (r * H * D + 4 * lg) * 2, 0, prep::kCpolSc1);
+          } else {
+            if (accumulate) val += load4(orow);
+            store4(orow, val);
+          }
         }
       }
     }
+  }
+
+  if (n_swa > 0) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): every row store has completed
+    asm volatile("" ::: "memory");
+    for (int c = max(0, nch - 6); c < nch; ++c) publish(c);
   }
 
   // linear-only overwrite: rows t < n_sink + window carry no linear output
@@ -420,7 +468,7 @@ uint64_t next_epoch() {
 }
 
 template <int D, int NW, int NL>
-hipError_t launch_full_t(const PrefillArgs& p, int nch, hipStream_t s) {
+hipError_t launch_full_t(const PrefillArgs& p, int nch, hipStream_t s, bool* swa_done) {
   using SM = FullSmem<D, NW>;
   constexpr int lds = fused_lds_bytes<D, NW>();
   auto kern = gdn_scan_full_kernel<D, NW, NL>;
@@ -441,19 +489,27 @@ hipError_t launch_full_t(const PrefillArgs& p, int nch, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const uint64_t epoch = n_prep > 0 ? next_epoch() : 0;
-  hipLaunchKernelGGL(kern, dim3(n_prep + n_scan), dim3(64 * (NW + NL)), lds, s,
+  // The softmax branch joins the kernel (its tiles run on the preparation
+  // workgroups after their chunks, adding onto the scan's rows as they are
+  // published) when both branches are asked for without accumulation and a
+  // KV head serves a multiple of 4 query heads.
+  const bool link = n_prep > 0 && (p.flags & 2) && !(p.flags & 8) && (p.H / p.Hkv) % 4 == 0;
+  const int n_swa = link ? ((p.T + 63) / 64 + kSwaTiles - 1) / kSwaTiles * (p.H / 4) * p.B : 0;
+  if (swa_done) *swa_done = link;
+  hipLaunchKernelGGL(kern, dim3(n_prep + n_scan + n_swa), dim3(64 * (NW + NL)), lds, s,
                      (const bf16*)p.q, (const bf16*)p.k, (const bf16*)p.v, p.a, p.b, (bf16*)w.wm,
-                     (bf16*)w.ktg, (bf16*)w.a, w.ut, w.g, w.ready, epoch, n_prep,
+                     (bf16*)w.ktg, (bf16*)w.a, w.ut, w.g, w.ready, epoch, n_prep, w.done, n_swa,
                      (bf16*)p.o, p.state_out, p.B, p.T, p.H, p.Hkv, p.n_sink, p.window, p.flags);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gdn_full(const PrefillArgs& p, int nch, hipStream_t s) {
+hipError_t launch_gdn_full(const PrefillArgs& p, int nch, hipStream_t s, bool* swa_done) {
+  if (swa_done) *swa_done = false;
   if (!p.bf16 || p.gla) return hipErrorInvalidValue;
-  if (p.D == 64) return launch_full_t<64, 4, 4>(p, nch, s);
-  if (p.D == 128) return launch_full_t<128, 4, 4>(p, nch, s);
+  if (p.D == 64) return launch_full_t<64, 4, 4>(p, nch, s, swa_done);
+  if (p.D == 128) return launch_full_t<128, 4, 4>(p, nch, s, swa_done);
   return hipErrorInvalidValue;
 }
 

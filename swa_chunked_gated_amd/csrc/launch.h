@@ -31,7 +31,8 @@ struct PrefillArgs {
 //   full preparation (bf16): -Wm [64][D] with d_k in natural order,
 //   K^T 2^{g_C - g} [D][64] whose row r holds d_k index acc_pos(r), the
 //   scores A [64][64], (TB V)^T [D][64] fp32 (tokens in natural order),
-//   g, gamma [2][64] fp32, and one uint64 ready flag per chunk.
+//   g, gamma [2][64] fp32, one uint64 ready flag per chunk, and d / 16
+//   uint64 flags per chunk that publish the scan's output rows.
 struct GdnWorkspace {
   void* tb;
   void* tbg;
@@ -41,6 +42,7 @@ struct GdnWorkspace {
   float* ut;         // full preparation: (Tm diag(b) V)^T [D][64] fp32
   float* g;
   uint64_t* ready;   // full preparation: per-chunk ready flags
+  uint64_t* done;    // full preparation: per-chunk scan-output flags (d / 64 * 4 each)
   size_t bytes;
 };
 // Full preparation (everything state-independent precomputed) for bf16 when
@@ -50,7 +52,7 @@ GdnWorkspace gdn_workspace_layout(void* base, int B, int H, int nch, int D, size
 // Full preparation and state scan (bf16, d = 64 or 128): one kernel whose
 // preparation workgroups publish chunks to its scan workgroups when the scan
 // leaves half of the GPU free, else the preparation kernel then the scan.
-hipError_t launch_gdn_full(const PrefillArgs& p, int nch, hipStream_t s);
+hipError_t launch_gdn_full(const PrefillArgs& p, int nch, hipStream_t s, bool* swa_done);
 // Workspace of the GLA prefill: for each (sequence, head, chunk) Q 2^G
 // [64][D], (K 2^{G_C - G})^T [D][64], A [64][64] (I/O type, reduction index in
 // acc order) and 2^{G_C} [D] fp32, as four consecutive arrays.
@@ -119,7 +121,8 @@ struct ShortConvArgs {
 // t >= n_sink + window when the linear branch is selected, zeroes rows
 // t < n_sink + window for a linear-only overwrite, and writes the final
 // state when asked.
-hipError_t launch_linear_prefill(const PrefillArgs& a, hipStream_t s);
+// *swa_done is set when the softmax branch was computed in the same launch.
+hipError_t launch_linear_prefill(const PrefillArgs& a, hipStream_t s, bool* swa_done);
 // Chunk preparation of the gated delta rule / of GLA into a.workspace (nch chunks).
 hipError_t launch_gdn_prep(const PrefillArgs& a, int nch, hipStream_t s);
 hipError_t launch_gla_prep(const PrefillArgs& a, int nch, hipStream_t s);

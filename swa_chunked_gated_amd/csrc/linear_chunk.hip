@@ -612,9 +612,10 @@ hipError_t launch_linear_d(const PrefillArgs& p, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_linear_prefill(const PrefillArgs& p, hipStream_t s) {
+hipError_t launch_linear_prefill(const PrefillArgs& p, hipStream_t s, bool* swa_done) {
+  if (swa_done) *swa_done = false;
   const int nch = gdn_stream_chunks(p.T, p.n_sink, p.window);
-  if (!p.gla && gdn_full_prep(p.B, p.H, p.D, p.bf16)) return launch_gdn_full(p, nch, s);
+  if (!p.gla && gdn_full_prep(p.B, p.H, p.D, p.bf16)) return launch_gdn_full(p, nch, s, swa_done);
   if (nch > 0) {
     const hipError_t e = p.gla ? launch_gla_prep(p, nch, s) : launch_gdn_prep(p, nch, s);
     if (e != hipSuccess) return e;

@@ -1,5 +1,5 @@
 // Softmax branch of the hybrid layer over sinks + sliding window (prefill),
-// flash-style, for gfx950.
+// flash-style, for gfx950: the kernel over swa_tiles (swa_tile.h).
 //
 // Method (page "The Key to Going Linear: Analysis-Driven Transformer
 // Linearization", section 填补近似缺口的实用设计): query t attends with
@@ -29,413 +29,24 @@
 // (the linear branch, or the caller's values when accumulating), cast to the
 // output type.
 
-#include <type_traits>
-
 #include "common.h"
 #include "launch.h"
+#include "swa_tile.h"
 
 namespace gdn {
 namespace {
 
-constexpr int kNQ = 2;    // 16-query tiles per wave
-
-// Max over lanes l, l^16, l^32, l^48 (the four lane groups holding one
-// query's scores), with the row-swap permutes: VALU only, no LDS round trip.
-// Every lane of the group ends with the same value.
-__device__ __forceinline__ float max_lane_groups(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-// max of three floats in one instruction (the scores are never NaN, so the
-// NaN-quieting that fmaxf needs in IEEE mode is left out)
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
-// Keys per LDS block: 64 for bf16, 32 for fp32 (keeps the register prefetch
-// of a block small).
-template <class T> struct KeyBlock { static constexpr int n = sizeof(T) == 2 ? 64 : 32; };
+using swa::kNQ;
 
 template <class T, int D, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void swa_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                       const T* __restrict__ v, T* __restrict__ o,
                                                       int T_, int H, int Hkv, int HPW, int QT, int TPW,
                                                       int n_sink, int window, int add_from) {
-  constexpr int KB = KeyBlock<T>::n;
-  constexpr int NTH = 64 * NW;
-  constexpr int PAD = 16 / sizeof(T);
-  constexpr int SK = D + PAD;      // Ks row stride
-  constexpr int SV = KB + PAD;     // VTs row stride
-  // staging in 16-byte chunks: K row-major, one chunk per task; V as pieces
-  // of 4 consecutive keys x one chunk, transposed in registers into runs of
-  // 4 keys (contiguous in acc order) of EPC dims
-  constexpr int EPC = 16 / sizeof(T);
-  constexpr int CH = D / EPC;                      // chunks per row
-  constexpr int NPK = KB * CH / NTH;               // K chunks per thread
-  constexpr int NVP = (KB / 4) * CH;               // V pieces per block
-  constexpr int NPV = (NVP + NTH - 1) / NTH;       // V pieces per thread
-  static_assert(KB * CH % NTH == 0 && NPK >= 1, "staging shape");
-  typedef typename Vec16<T>::type V16;
-  __shared__ __attribute__((aligned(16))) T Ks[2][KB * SK];
-  __shared__ __attribute__((aligned(16))) T VTs[2][D * SV];
-
-  const int hgrp = blockIdx.y;
-  const int bi = blockIdx.z;
-  const int G = H / Hkv;
-  const int h0 = hgrp * HPW;
-  const int g = h0 / G;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = wave_id();
-  const int l16 = lane & 15;
-  const int lg = lane >> 4;
-  const int NWQ = QT / (16 * kNQ);
-  const int h = h0 + wv / NWQ;
-  const int tile0 = blockIdx.x * TPW;                 // first query tile of this workgroup
-  const int ntile = min(TPW, (T_ + QT - 1) / QT - tile0);
-  const float scale = kLog2e / sqrtf((float)D);
-
-  // Key blocks of query tile t0: sinks [0, min(n_sink, t_end)) then the
-  // window [max(n_sink, t0 - window + 1), t_end), KB keys per block.
-  struct Blk { int kb0, kend, sink; };
-  auto tile_blocks = [&](int t0, int& nbs, int& nbw, int& sink_end, int& win_lo, int& t_end) {
-    t_end = min(t0 + QT, T_);
-    sink_end = min(n_sink, t_end);
-    win_lo = max(n_sink, t0 - window + 1);
-    nbs = (sink_end + KB - 1) / KB;
-    nbw = t_end > win_lo ? (t_end - win_lo + KB - 1) / KB : 0;
-  };
-  // block blk of the workgroup's tile ti -> block description (every tile
-  // has at least one block)
-  auto block_of = [&](int ti, int blk, Blk& bl) {
-    int nbs, nbw, se, wl, te;
-    tile_blocks((tile0 + ti) * QT, nbs, nbw, se, wl, te);
-    const bool sk = blk < nbs;
-    bl.kb0 = sk ? blk * KB : wl + (blk - nbs) * KB;
-    bl.kend = sk ? se : te;
-    bl.sink = sk;
-  };
-
-  // query fragments (B operand of S^T = K Q^T, "linear" set over d) of tile
-  // ti: 16-byte loads, then converted and pre-multiplied by log2(e) / sqrt(d)
-  // so the scores come out of the MFMA already in exp2 units
-  constexpr int QV = 8 / EPC;                      // 16-byte pieces per fragment
-  typedef V16 QRaw[QV];
-  auto load_q = [&](int ti, QRaw (&qr)[kNQ][D / 32]) {
-    const int qb = (tile0 + ti) * QT + (wv % NWQ) * 16 * kNQ;
-#pragma unroll
-    for (int nq = 0; nq < kNQ; ++nq) {
-      const int t = qb + 16 * nq + l16;
-#pragma unroll
-      for (int p = 0; p < D / 32; ++p) {
-#pragma unroll
-        for (int u = 0; u < QV; ++u) {
-          if (t < T_) {
-            qr[nq][p][u] = *reinterpret_cast<const V16*>(q + ((size_t)(bi * T_ + t) * H + h) * D + 32 * p +
-                                                         8 * lg + u * EPC);
-          } else {
-#pragma unroll
-            for (int i = 0; i < EPC; ++i) qr[nq][p][u][i] = from_f32<T>(0.f);
-          }
-        }
-      }
-    }
-  };
-
-  // ---- register prefetch of a key block and its commit to an LDS buffer
-  V16 pk[NPK], pv[NPV][4];
-  const size_t kvstride = (size_t)Hkv * D;
-  auto prefetch = [&](const Blk& bl) {
-    const size_t off = ((size_t)(bi * T_ + bl.kb0) * Hkv + g) * D;
-    const T* kp = k + off;
-    const T* vp = v + off;
-    const int nkey = bl.kend - bl.kb0;             // keys of this block that exist
-    if (nkey >= KB) {                              // uniform: a whole block
-#pragma unroll
-      for (int j = 0; j < NPK; ++j) {
-        const int i = tid + j * NTH;
-        pk[j] = *reinterpret_cast<const V16*>(kp + (i / CH) * kvstride + (i % CH) * EPC);
-      }
-#pragma unroll
-      for (int j = 0; j < NPV; ++j) {
-        const int i = tid + j * NTH;
-        if (NVP % NTH == 0 || i < NVP) {
-          const T* src = vp + 4 * (i % (KB / 4)) * kvstride + (i / (KB / 4)) * EPC;
-#pragma unroll
-          for (int x = 0; x < 4; ++x) pv[j][x] = *reinterpret_cast<const V16*>(src + x * kvstride);
-        }
-      }
-    } else {
-      V16 z;
-#pragma unroll
-      for (int x = 0; x < EPC; ++x) z[x] = from_f32<T>(0.f);
-#pragma unroll
-      for (int j = 0; j < NPK; ++j) {
-        const int i = tid + j * NTH;
-        pk[j] = i / CH < nkey ? *reinterpret_cast<const V16*>(kp + (i / CH) * kvstride + (i % CH) * EPC) : z;
-      }
-#pragma unroll
-      for (int j = 0; j < NPV; ++j) {
-        const int i = tid + j * NTH;
-        if (NVP % NTH == 0 || i < NVP) {
-          const int key0 = 4 * (i % (KB / 4));
-          const T* src = vp + key0 * kvstride + (i / (KB / 4)) * EPC;
-#pragma unroll
-          for (int x = 0; x < 4; ++x)
-            pv[j][x] = key0 + x < nkey ? *reinterpret_cast<const V16*>(src + x * kvstride) : z;
-        }
-      }
-    }
-  };
-  auto commit = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < NPK; ++j) {
-      const int i = tid + j * NTH;
-      *reinterpret_cast<V16*>(&Ks[buf][(i / CH) * SK + (i % CH) * EPC]) = pk[j];
-    }
-#pragma unroll
-    for (int j = 0; j < NPV; ++j) {
-      const int i = tid + j * NTH;
-      if (NVP % NTH == 0 || i < NVP) {
-        T* col = &VTs[buf][(i / (KB / 4)) * EPC * SV + acc_pos(4 * (i % (KB / 4)))];
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          if constexpr (sizeof(T) == 2) {
-            *reinterpret_cast<bf16x4*>(col + e * SV) = bf16x4{pv[j][0][e], pv[j][1][e], pv[j][2][e], pv[j][3][e]};
-          } else {
-            *reinterpret_cast<f32x4*>(col + e * SV) = f32x4{pv[j][0][e], pv[j][1][e], pv[j][2][e], pv[j][3][e]};
-          }
-        }
-      }
-    }
-  };
-
-  Frag<T> ones;
-  {
-    float x1[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
-    ones = frag_from8<T>(x1);
-  }
-  int flat = 0;   // running block counter (selects the LDS buffer)
-  if (ntile > 0) {
-    Blk b0;
-    block_of(0, 0, b0);
-    prefetch(b0);
-    commit(0);
-  }
-  lds_barrier();
-
-  for (int ti = 0; ti < ntile; ++ti) {
-    const int t0 = (tile0 + ti) * QT;
-    const int qb = t0 + (wv % NWQ) * 16 * kNQ;      // first query row of this wave
-    const int qlast = qb + 16 * kNQ - 1;
-    int nbs, nbw, sink_end, win_lo, t_end;
-    tile_blocks(t0, nbs, nbw, sink_end, win_lo, t_end);
-    const int nblk = nbs + nbw;
-
-    QRaw qraw[kNQ][D / 32];
-    load_q(ti, qraw);
-    Frag<T> qf[kNQ][D / 32];
-#pragma unroll
-    for (int nq = 0; nq < kNQ; ++nq)
-#pragma unroll
-      for (int p = 0; p < D / 32; ++p) {
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = to_f32(qraw[nq][p][i / EPC][i % EPC]) * scale;
-        qf[nq][p] = frag_from8<T>(x);
-      }
-
-
-    f32x4 oacc[D / 16][kNQ];
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-      for (int nq = 0; nq < kNQ; ++nq) oacc[dt][nq] = zero4();
-    // running max (reference) per query and the row sums, the latter as an
-    // MFMA accumulator: a 16-row "ones" tile times P^T gives sum_k p in every
-    // row, so l is summed from the same rounded p that multiply V
-    float mrun[kNQ];
-    f32x4 lacc[kNQ];
-#pragma unroll
-    for (int nq = 0; nq < kNQ; ++nq) {
-      mrun[nq] = -INFINITY;
-      lacc[nq] = zero4();
-    }
-
-    for (int blk = 0; blk < nblk; ++blk, ++flat) {
-      const int buf = flat & 1;
-      const bool sinkph = blk < nbs;
-      const int kb0 = sinkph ? blk * KB : win_lo + (blk - nbs) * KB;
-      const int kend = sinkph ? sink_end : t_end;
-      const bool last = blk + 1 == nblk;
-      const bool has_next = !last || ti + 1 < ntile;
-      if (has_next) {
-        Blk nx;
-        block_of(last ? ti + 1 : ti, last ? 0 : blk + 1, nx);
-        prefetch(nx);
-      }
-      const T* Kb = Ks[buf];
-      const T* Vb = VTs[buf];
-
-      // ---- S^T tiles for this wave, computed relative to the running max:
-      // the accumulators start at -mbase, so the MFMAs return s - mbase
-      // (tiles no query of the wave sees are skipped; which ones is a scalar
-      // bit mask)
-      int onmask = 0;
-#pragma unroll
-      for (int kt = 0; kt < KB / 16; ++kt) {
-        const int k0 = kb0 + 16 * kt;
-        bool on = k0 < kend && k0 <= qlast && qb < T_;
-        if (!sinkph) on = on && (k0 + 15 > qb - window);
-        onmask |= on ? 1 << kt : 0;
-      }
-      onmask = __builtin_amdgcn_readfirstlane(onmask);
-      float mbase[kNQ];
-      f32x4 negm[kNQ];
-#pragma unroll
-      for (int nq = 0; nq < kNQ; ++nq) {
-        mbase[nq] = mrun[nq] == -INFINITY ? 0.f : mrun[nq];
-        negm[nq] = f32x4{-mbase[nq], -mbase[nq], -mbase[nq], -mbase[nq]};
-      }
-      f32x4 sacc[KB / 16][kNQ];
-#pragma unroll
-      for (int kt = 0; kt < KB / 16; ++kt) {
-#pragma unroll
-        for (int nq = 0; nq < kNQ; ++nq) sacc[kt][nq] = negm[nq];
-        if ((onmask >> kt) & 1) {
-          Frag<T> af[D / 32];
-#pragma unroll
-          for (int p = 0; p < D / 32; ++p) af[p] = lds_frag8(&Kb[(16 * kt + l16) * SK + 32 * p + 8 * lg]);
-#pragma unroll
-          for (int p = 0; p < D / 32; ++p)
-#pragma unroll
-            for (int nq = 0; nq < kNQ; ++nq) sacc[kt][nq] = mfma(af[p], qf[nq][p], sacc[kt][nq]);
-        }
-      }
-
-      // ---- mask and block max per query (per lane; 4 lane groups share a
-      // query).  A tile whose keys are all visible to all its queries skips
-      // the per-element mask.  Window phase: a key is visible iff
-      // 0 <= t - key < window (a key past the tile end is later than every
-      // real query of it); sink phase: iff key <= t and key < kend.
-      float mloc[kNQ];
-      auto mask_and_max = [&](auto sink_tag) {
-        constexpr bool SINK = decltype(sink_tag)::value;
-#pragma unroll
-        for (int nq = 0; nq < kNQ; ++nq) {
-          const int q0 = qb + 16 * nq;
-          const int t = q0 + l16;
-          float m = -INFINITY;
-#pragma unroll
-          for (int kt = 0; kt < KB / 16; ++kt) {
-            if (!((onmask >> kt) & 1)) continue;
-            const int k0 = kb0 + 16 * kt;
-            const bool full = SINK ? (k0 + 15 <= q0 && k0 + 15 < kend)
-                                   : (k0 + 15 <= q0 && k0 > q0 + 15 - window);
-            if (!full) {
-              const int key0 = k0 + 4 * lg;
-              const int d0 = t - key0;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const bool valid = SINK ? ((d0 - i >= 0) & (key0 + i < kend))
-                                        : (unsigned)(d0 - i) < (unsigned)window;
-                sacc[kt][nq][i] = valid ? sacc[kt][nq][i] : -INFINITY;
-              }
-            }
-            m = max3f(m, max3f(sacc[kt][nq][0], sacc[kt][nq][1], sacc[kt][nq][2]), sacc[kt][nq][3]);
-          }
-          mloc[nq] = m;
-        }
-      };
-      if (sinkph) mask_and_max(std::true_type{});
-      else mask_and_max(std::false_type{});
-
-      // ---- lazy rescale: the running max only moves (and O is rescaled)
-      // when the block raises it by more than 8 in log2 units, which keeps
-      // every exponent <= 2^8 while sparing most rescales.  Scores are held
-      // relative to mbase (the running max, or 0 before any key); a move
-      // shifts them to the new reference.
-#pragma unroll
-      for (int nq = 0; nq < kNQ; ++nq) {
-        const float mblk = mbase[nq] + max_lane_groups(mloc[nq]);
-        const float mref = mrun[nq];
-        if (__any(mblk > mref + 8.f)) {   // some query of the wave needs a new reference
-          const float mnew = fmaxf(mref, mblk);
-          const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mref - mnew);
-          lacc[nq] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt) oacc[dt][nq] *= alpha;
-          mrun[nq] = mnew;
-          // a lane that has seen no key yet keeps reference 0: its scores
-          // are all -inf and give p = 0 whatever the shift
-          const float shift = (mnew == -INFINITY ? 0.f : mnew) - mbase[nq];
-#pragma unroll
-          for (int kt = 0; kt < KB / 16; ++kt) sacc[kt][nq] -= shift;
-        }
-      }
-
-      // ---- p = exp2(s - m), row sums, O^T += V^T P^T, 32 keys at a time
-#pragma unroll
-      for (int pp = 0; pp < KB / 32; ++pp) {
-        const bool on0 = (onmask >> (2 * pp)) & 1;
-        const bool on1 = (onmask >> (2 * pp + 1)) & 1;
-        if (!(on0 || on1)) continue;
-        Frag<T> pf[kNQ];
-#pragma unroll
-        for (int nq = 0; nq < kNQ; ++nq) {
-          f32x4 p0 = zero4(), p1 = zero4();
-          if (on0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) p0[i] = __builtin_amdgcn_exp2f(sacc[2 * pp][nq][i]);
-          }
-          if (on1) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) p1[i] = __builtin_amdgcn_exp2f(sacc[2 * pp + 1][nq][i]);
-          }
-          pf[nq] = frag_from_acc<T>(p0, p1);
-          lacc[nq] = mfma(ones, pf[nq], lacc[nq]);
-        }
-        // V fragments in two halves to bound the live registers
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          Frag<T> vf[D / 32];
-#pragma unroll
-          for (int dd = 0; dd < D / 32; ++dd)
-            vf[dd] = lds_frag8(&Vb[(16 * (hf * D / 32 + dd) + l16) * SV + 32 * pp + 8 * lg]);
-#pragma unroll
-          for (int dd = 0; dd < D / 32; ++dd)
-#pragma unroll
-            for (int nq = 0; nq < kNQ; ++nq)
-              oacc[hf * D / 32 + dd][nq] = mfma(vf[dd], pf[nq], oacc[hf * D / 32 + dd][nq]);
-        }
-      }
-
-      if (has_next) commit(buf ^ 1);
-      lds_barrier();
-    }
-
-    // ---- epilogue of this query tile
-#pragma unroll
-    for (int nq = 0; nq < kNQ; ++nq) {
-      const float l = lacc[nq][0];
-      const int t = qb + 16 * nq + l16;
-      if (t >= T_) continue;
-      const float inv = 1.0f / l;
-      T* orow = o + ((size_t)(bi * T_ + t) * H + h) * D;
-      const bool addl = t >= add_from;
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        f32x4 val = oacc[dt][nq] * inv;
-        const int d0 = 16 * dt + 4 * lg;
-        if (addl) val += load4(orow + d0);
-        store4(orow + d0, val);
-      }
-    }
-  }
+  __shared__ __attribute__((aligned(16))) unsigned char lds[swa::SwaSmem<T, D>::bytes];
+  swa::swa_tiles<T, D, NW, false>(q, k, v, o, T_, H, Hkv, HPW, QT, TPW, n_sink, window, add_from,
+                                  blockIdx.x, blockIdx.y, blockIdx.z, reinterpret_cast<T*>(lds),
+                                  nullptr, 0, 0, 0);
 }
 
 template <class T>

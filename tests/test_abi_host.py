@@ -70,13 +70,13 @@ def test_workspace_query(lib):
     def gdn_bytes(B, T, H, d, elt, n=64):
         nch = -(-(T - n) // 64)
         full = elt == 2 and B * H * (2 if d == 128 else 1) < 256     # bf16, few chains
-        if full:    # -Wm, K^T, A in bf16; (TB V)^T in fp32; gates; a ready flag
-            per = (64 * d + d * 64 + 64 * 64) * elt + d * 64 * 4 + 512 + 8
+        if full:    # -Wm, K^T, A in bf16; (TB V)^T in fp32; gates; ready and done flags
+            per = (64 * d + d * 64 + 64 * 64) * elt + d * 64 * 4 + 512 + 8 + d // 16 * 8
         else:       # TB, TBG; gates
             per = 2 * 64 * 64 * elt + 512
         return B * H * nch * per
     assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 3) == (OK, gdn_bytes(1, 4096, 32, 128, 2))
-    assert gdn_bytes(1, 4096, 32, 128, 2) == 2016 * 74248
+    assert gdn_bytes(1, 4096, 32, 128, 2) == 2016 * 74312
     assert ws(lib, 2, 300, 4, 2, 64, 64, 8, 56, F32, DELTA, 5) == (OK, gdn_bytes(2, 300, 4, 64, 4))
     assert ws(lib, 8, 4096, 32, 8, 128, 128, 8, 120, BF16, DELTA, 5) == (OK, gdn_bytes(8, 4096, 32, 128, 2, 128))
     nch = (4096 - 64 + 63) // 64
