@@ -4,10 +4,12 @@
 Headline (the printed JSON line): prefill throughput of one layer with the
 LLaMA3.1-8B attention shape (B=1, 32 query / 8 KV heads, d=128, T=4096,
 budget 8 sinks + 56 window, bf16 inputs, fp32 state).  One step = one
-layer pass over the sequence: the linear branch (chunk preparation kernel,
-then the chunked GDN scan kernel), then the sink+SWA softmax kernel adding
-its branch; two ABI calls, so HIP events between them time each branch on
-the stream it runs on.  Inputs are resident in HBM before the timed region.
+layer pass over the sequence: one ABI call with both branches, which is one
+kernel launch (chunk preparation, chunked GDN state scan and the sink+SWA
+softmax tiles cooperating through per-chunk flags); HIP events around it on
+its stream time it.  The same layer as two calls (linear, then softmax
+adding its branch) is timed too, for reference.  Inputs are resident in HBM
+before the timed region.
 
 Secondary figures in "also": decode steps/s (B=256, 1000 consecutive steps),
 long-context prefill (B=8, T=32768, budget 128, final state out) and the
@@ -100,7 +102,7 @@ def timed(fn, steps, warmup):
 
 # ------------------------------------------------------------- headline
 
-def bench_main(steps, warmup):
+def bench_main(steps, warmup, split=True):
     import swa_chunked_gated_amd as gl
     from workloads import WORKLOADS, make_prefill_inputs
 
@@ -108,21 +110,21 @@ def bench_main(steps, warmup):
     inp = make_prefill_inputs(w, device="cuda")
     o = torch.empty(w.B, w.T, w.H, w.d, dtype=torch.bfloat16, device="cuda")
     q, k, v, a, b = (inp[x] for x in ("q", "k", "v", "a", "b"))
+    both = gl.BRANCH_LINEAR | gl.BRANCH_SOFTMAX
     ws = torch.empty(gl.prefill_workspace_bytes(w.B, w.T, w.H, w.Hkv, w.d, w.n_sink, w.window,
-                                                torch.bfloat16, flags=gl.BRANCH_LINEAR),
+                                                torch.bfloat16, flags=both),
                      dtype=torch.uint8, device="cuda")
+    f_lin, f_swa = gdn_flops(w), swa_flops(w)
+
+    # the layer: one call with both branches (one launch: preparation, state
+    # scan and softmax tiles in the same kernel), events around it on its stream
     n = steps + warmup
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
 
     def step(i):
-        e = ev[i]
-        e[0].record()
-        gl.hybrid_prefill(q, k, v, a, b, w.n_sink, w.window, flags=gl.BRANCH_LINEAR, o=o,
-                          workspace=ws)
-        e[1].record()
-        gl.hybrid_prefill(q, k, v, a, b, w.n_sink, w.window,
-                          flags=gl.BRANCH_SOFTMAX | gl.ACCUMULATE, o=o)
-        e[2].record()
+        ev[i][0].record()
+        gl.hybrid_prefill(q, k, v, a, b, w.n_sink, w.window, flags=both, o=o, workspace=ws)
+        ev[i][1].record()
 
     for i in range(warmup):
         step(i)
@@ -132,23 +134,34 @@ def bench_main(steps, warmup):
         step(i)
     torch.cuda.synchronize()
     sec = (time.perf_counter() - t0) / steps
-    lin_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(warmup, n)]))
-    swa_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(warmup, n)]))
-    f_lin, f_swa = gdn_flops(w), swa_flops(w)
-    if lin_ms >= swa_ms:
-        dom = (LINEAR_KERNELS, f_lin, lin_ms, LINEAR_SOURCES)
-    else:
-        dom = ("swa_kernel", f_swa, swa_ms, SWA_SOURCES)
-    achieved = dom[1] / (dom[2] * 1e-3)
+    layer_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(warmup, n)]))
+
+    # for reference, each branch alone: the linear call, then the softmax call
+    # adding its branch (the two-launch form of the same layer)
+    m_split = max(10, steps // 4)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(m_split + 3)]
+    for i in range(m_split + 3 if split else 0):
+        e = evs[i]
+        e[0].record()
+        gl.hybrid_prefill(q, k, v, a, b, w.n_sink, w.window, flags=gl.BRANCH_LINEAR, o=o, workspace=ws)
+        e[1].record()
+        gl.hybrid_prefill(q, k, v, a, b, w.n_sink, w.window, flags=gl.BRANCH_SOFTMAX | gl.ACCUMULATE, o=o)
+        e[2].record()
+    torch.cuda.synchronize()
+    lin_ms = float(np.mean([evs[i][0].elapsed_time(evs[i][1]) for i in range(3, m_split + 3)])) if split else None
+    swa_ms = float(np.mean([evs[i][1].elapsed_time(evs[i][2]) for i in range(3, m_split + 3)])) if split else None
+
+    achieved = (f_lin + f_swa) / (layer_ms * 1e-3)
     res = {
         "w": w, "sec": sec,
-        "kernels_ms": {LINEAR_KERNELS: lin_ms, "swa_kernel": swa_ms},
+        "kernels_ms": {LAYER_KERNEL: layer_ms,
+                       "two-launch reference": {LINEAR_KERNELS: lin_ms, "swa_kernel": swa_ms}},
         "roofline": {
-            "kernel": dom[0], "bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,
+            "kernel": LAYER_KERNEL, "bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,
             "unit": "TFLOP/s", "frac": achieved / PEAK_BF16,
-            "traffic": stored_traffic(dom[0], w.name, dom[3]),
+            "traffic": stored_traffic(LAYER_KERNEL, w.name, LAYER_SOURCES),
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-            "algorithmic_flops_per_launch": dom[1],
+            "algorithmic_flops_per_launch": f_lin + f_swa,
             "algorithmic_bytes_per_launch": prefill_bytes(w),
         },
         "layer_frac_mfma": (f_lin + f_swa) / sec / PEAK_BF16,
@@ -203,12 +216,17 @@ def kernel_sources_sha256(files):
     return h.hexdigest()
 
 
-LINEAR_SOURCES = ("swa_chunked_gated_amd/csrc/gdn_prep.hip", "swa_chunked_gated_amd/csrc/gdn_scan_full.hip",
-                  "swa_chunked_gated_amd/csrc/linear_chunk.hip", "swa_chunked_gated_amd/csrc/common.h")
-# the linear launch of the LLaMA-shaped layer (32 chains): chunk preparation,
-# then the loader-wave state scan
-LINEAR_KERNELS = "gdn_prep_kernel+gdn_scan_full_kernel"
-SWA_SOURCES = ("swa_chunked_gated_amd/csrc/swa.hip", "swa_chunked_gated_amd/csrc/common.h")
+LINEAR_SOURCES = ("swa_chunked_gated_amd/csrc/gdn_prep.h", "swa_chunked_gated_amd/csrc/gdn_prep.hip",
+                  "swa_chunked_gated_amd/csrc/gdn_scan_full.hip", "swa_chunked_gated_amd/csrc/linear_chunk.hip",
+                  "swa_chunked_gated_amd/csrc/common.h")
+# the linear launch of the LLaMA-shaped layer (32 chains): preparation and
+# state scan in one kernel; with both branches the softmax tiles join it
+LINEAR_KERNELS = "gdn_scan_full_kernel"
+LAYER_KERNEL = "gdn_scan_full_kernel"
+LAYER_SOURCES = ("swa_chunked_gated_amd/csrc/gdn_prep.h", "swa_chunked_gated_amd/csrc/gdn_scan_full.hip",
+                 "swa_chunked_gated_amd/csrc/swa_tile.h", "swa_chunked_gated_amd/csrc/common.h")
+SWA_SOURCES = ("swa_chunked_gated_amd/csrc/swa.hip", "swa_chunked_gated_amd/csrc/swa_tile.h",
+               "swa_chunked_gated_amd/csrc/common.h")
 DECODE_SOURCES = ("swa_chunked_gated_amd/csrc/decode.hip", "swa_chunked_gated_amd/csrc/common.h")
 # one decode step is three launches: softmax branch, state update, cache commit
 DECODE_KERNELS = "decode_swa_kernel+decode_state_kernel+decode_commit_kernel"
@@ -352,6 +370,8 @@ def main():
     ap.add_argument("--only", default="all",
                     choices=["all", "main", "decode", "longctx", "qwen32b", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-split", action="store_true",
+                    help="skip the two-launch reference timing of the headline layer (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -375,7 +395,7 @@ def main():
             print(json.dumps(bench_prefill_cfg(n, steps=args.steps, warmup=args.warmup)), flush=True)
         return
 
-    m = bench_main(args.steps, args.warmup)
+    m = bench_main(args.steps, args.warmup, split=not args.no_split)
     w = m["w"]
     also = {}
     if args.only == "all":
