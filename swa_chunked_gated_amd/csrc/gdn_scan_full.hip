@@ -92,6 +92,20 @@ constexpr int fused_lds_bytes() {
   return scan > prep ? scan : prep;
 }
 
+// Placement on the XCDs (workgroup i of a launch runs on XCD i % 8; each XCD
+// has its own L2): chains (sequence, head) are spread over the XCDs so that a
+// chain's preparation items and its scan workgroups share one XCD, and with
+// kXcdByGroup the query heads of one KV head share it too (their preparation
+// reads the same K and V rows).  A chain is named by its XCD x and its slot
+// among that XCD's chains.
+constexpr int kXcdNone = 0;
+constexpr int kXcdByGroup = 1;     // B Hkv divisible by 8
+constexpr int kXcdByChain = 2;     // B H divisible by 8
+__device__ __forceinline__ int xcd_chain(int mode, int G, int x, int slot) {
+  if (mode == kXcdByGroup) return ((slot / G) * 8 + x) * G + slot % G;
+  return slot * 8 + x;
+}
+
 // Grid, in dispatch order: n_prep preparation workgroups, one scan workgroup
 // per (sequence, head, column slice), then n_swa softmax workgroups.
 //  * With n_prep = 0 the workspace is already complete (the preparation
@@ -115,7 +129,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
     bf16* __restrict__ w_ktg, bf16* __restrict__ w_a, float* __restrict__ w_ut,
     float* __restrict__ w_g, uint64_t* __restrict__ ready, uint64_t epoch, int n_prep,
     uint64_t* __restrict__ done, int n_swa, bf16* __restrict__ o, float* __restrict__ state_out,
-    int B, int T_, int H, int Hkv, int n_sink, int window, int flags) {
+    int B, int T_, int H, int Hkv, int n_sink, int window, int flags, int xcd) {
   using SM = FullSmem<D, NW>;
   using PS = prep::PrepSmem<bf16, D, true>;
   static_assert(NL >= 1 && NL <= 4, "one to four loader waves");
@@ -139,9 +153,15 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
     // ======================= preparation workgroup
     if (wv >= kPrepWaves) return;
     const int BH = B * H;
-    for (int it = blockIdx.x * kPrepWaves + wv; it < nch * BH; it += n_prep * kPrepWaves) {
-      const int c = it / BH;
-      const int bh = it % BH;
+    // items in chunk-major order; with an XCD placement, this workgroup's
+    // XCD takes only the chains placed on it
+    const int x = xcd ? ((int)blockIdx.x - n_prep % 8 + 8) % 8 : 0;
+    const int per = xcd ? BH / 8 : BH;
+    const int first = xcd ? ((int)blockIdx.x / 8) * kPrepWaves + wv : (int)blockIdx.x * kPrepWaves + wv;
+    const int stride = xcd ? (n_prep / 8) * kPrepWaves : n_prep * kPrepWaves;
+    for (int it = first; it < nch * per; it += stride) {
+      const int c = it / per;
+      const int bh = xcd ? xcd_chain(xcd, H / Hkv, x, it % per) : it % per;
       prep::gdn_prep_chunk<bf16, D, true, true>(q, k, v, a, b, nullptr, nullptr, w_wm, w_ktg, w_a,
                                                 w_ut, w_g, T_, H, Hkv, n_sink, window, nch, c,
                                                 bh % H, bh / H, smem_raw + wv * PS::bytes);
@@ -174,9 +194,10 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
   }
 
   const int sw = blockIdx.x - n_prep;
-  const int sp = sw % (D / DVS);         // column slice
-  const int h = (sw / (D / DVS)) % H;
-  const int bi = sw / ((D / DVS) * H);
+  const int sp = xcd ? (sw / 8) % (D / DVS) : sw % (D / DVS);   // column slice
+  const int ch = xcd ? xcd_chain(xcd, H / Hkv, sw % 8, sw / 8 / (D / DVS)) : sw / (D / DVS);
+  const int h = ch % H;
+  const int bi = ch / H;
   const int g = h / (H / Hkv);
   const int l16 = lane & 15;
   const int lg = lane >> 4;
@@ -489,6 +510,9 @@ hipError_t launch_full_t(const PrefillArgs& p, int nch, hipStream_t s, bool* swa
     if (e != hipSuccess) return e;
   }
   const uint64_t epoch = n_prep > 0 ? next_epoch() : 0;
+  // XCD placement (the preparation's share needs whole rounds of 8 workgroups)
+  int xcd = kXcdNone;
+  if (n_prep % 8 == 0 && (p.B * p.H) % 8 == 0) xcd = (p.B * p.Hkv) % 8 == 0 ? kXcdByGroup : kXcdByChain;
   // The softmax branch joins the kernel (its tiles run on the preparation
   // workgroups after their chunks, adding onto the scan's rows as they are
   // published) when both branches are asked for without accumulation and a
@@ -499,7 +523,7 @@ hipError_t launch_full_t(const PrefillArgs& p, int nch, hipStream_t s, bool* swa
   hipLaunchKernelGGL(kern, dim3(n_prep + n_scan + n_swa), dim3(64 * (NW + NL)), lds, s,
                      (const bf16*)p.q, (const bf16*)p.k, (const bf16*)p.v, p.a, p.b, (bf16*)w.wm,
                      (bf16*)w.ktg, (bf16*)w.a, w.ut, w.g, w.ready, epoch, n_prep, w.done, n_swa,
-                     (bf16*)p.o, p.state_out, p.B, p.T, p.H, p.Hkv, p.n_sink, p.window, p.flags);
+                     (bf16*)p.o, p.state_out, p.B, p.T, p.H, p.Hkv, p.n_sink, p.window, p.flags, xcd);
   return hipGetLastError();
 }
 
