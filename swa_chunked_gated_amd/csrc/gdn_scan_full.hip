@@ -134,6 +134,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
   using PS = prep::PrepSmem<bf16, D, true>;
   static_assert(NL >= 1 && NL <= 4, "one to four loader waves");
   static_assert(PS::bytes % 16 == 0 && fused_lds_bytes<D, NW>() <= 160 * 1024, "LDS of one workgroup");
+  static_assert(swa::SwaSmem<bf16, D>::deep_bytes <= fused_lds_bytes<D, NW>(), "softmax tiles' LDS");
   constexpr int SK = SM::SK;
   constexpr int SC = SM::SC;
   constexpr int DVS = SM::DVS;

@@ -41,6 +41,9 @@ namespace swa {
 
 
 constexpr int kNQ = 2;    // 16-query tiles per wave
+// A linked tile with at most this many key blocks fetches them all at once
+// (one memory latency for the tile instead of one per block).
+constexpr int kDeepBlocks = 3;
 
 // Max over lanes l, l^16, l^32, l^48 (the four lane groups holding one
 // query's scores), with the row-swap permutes: VALU only, no LDS round trip.
@@ -79,18 +82,20 @@ __device__ __forceinline__ void wait_ready(const uint64_t* f, uint64_t epoch) {
   asm volatile("" ::: "memory");
 }
 
-// 4 bf16 at element offset `off` of a wave-uniform base, read at device
-// scope (cache policy sc1), as fp32.
-__device__ __forceinline__ f32x4 load4_dev(const bf16* base, int off) {
-  typedef unsigned int u2 __attribute__((ext_vector_type(2)));
-  const u2 raw = __builtin_amdgcn_raw_buffer_load_b64(
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), 0, 0x7fffffff, 0x00020000), off * 2, 0, 16);
-  const bf16x4 x = __builtin_bit_cast(bf16x4, raw);
-  return f32x4{static_cast<float>(x[0]), static_cast<float>(x[1]), static_cast<float>(x[2]),
-               static_cast<float>(x[3])};
-}
-__device__ __forceinline__ f32x4 load4_dev(const float* base, int off) {
-  return *reinterpret_cast<const f32x4*>(base + off);   // (bf16 only in linked use)
+// Waits until the n (<= 64) consecutive flags f[0..n) all equal epoch: lane
+// i reads flag i, every poll reads them all at once.  Bounded like
+// wait_ready.
+template <int SLEEP = 1>
+__device__ __forceinline__ void wait_ready_span(const uint64_t* f, int n, uint64_t epoch, int lane) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  const bool mine = lane < n;
+  while (true) {
+    const bool ok = !mine || __hip_atomic_load(f + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
+    if (__all(ok)) break;
+    __builtin_amdgcn_s_sleep(SLEEP);
+    if (__builtin_amdgcn_s_memrealtime() - t0 > 10000000ull) break;
+  }
+  asm volatile("" ::: "memory");
 }
 
 // LDS of swa_tiles: two K blocks (row-major) then two V^T blocks.
@@ -102,6 +107,8 @@ struct SwaSmem {
   static constexpr int nK = KB * SK;
   static constexpr int nV = D * SV;
   static constexpr int bytes = (2 * nK + 2 * nV) * (int)sizeof(T);
+  // linked tiles of few blocks: every block staged at once, K then V^T per block
+  static constexpr int deep_bytes = kDeepBlocks * (nK + nV) * (int)sizeof(T);
 };
 
 // The query tiles bx * TPW .. of (sequence bi, query heads hgrp * HPW ..
@@ -197,68 +204,65 @@ __device__ __forceinline__ void swa_tiles(const T* __restrict__ q, const T* __re
     }
   };
 
-  // ---- register prefetch of a key block and its commit to an LDS buffer
-  V16 pk[NPK], pv[NPV][4];
+  // ---- register prefetch of a key block and its commit to an LDS buffer.
+  // Every lane always loads (rows past the block's last key read that key
+  // again, so no address leaves the tensor); the rows past it are zeroed at
+  // commit.  One unconditional load sequence keeps the prefetch asynchronous:
+  // the loads are waited for only when the block is committed.
+  typedef V16 PK[NPK];
+  typedef V16 PV[NPV][4];
+  constexpr int NSET = LINKED ? kDeepBlocks : 1;   // register sets
+  PK pks[NSET];
+  PV pvs[NSET];
+  int nks[NSET];                                   // keys of each prefetched block that exist
   const size_t kvstride = (size_t)Hkv * D;
-  auto prefetch = [&](const Blk& bl) {
+  auto prefetch = [&](const Blk& bl, PK& pk, PV& pv, int& pf_nkey) {
     const size_t off = ((size_t)(bi * T_ + bl.kb0) * Hkv + g) * D;
     const T* kp = k + off;
     const T* vp = v + off;
-    const int nkey = bl.kend - bl.kb0;             // keys of this block that exist
-    if (nkey >= KB) {                              // uniform: a whole block
-#pragma unroll
-      for (int j = 0; j < NPK; ++j) {
-        const int i = tid + j * NTH;
-        pk[j] = *reinterpret_cast<const V16*>(kp + (i / CH) * kvstride + (i % CH) * EPC);
-      }
-#pragma unroll
-      for (int j = 0; j < NPV; ++j) {
-        const int i = tid + j * NTH;
-        if (NVP % NTH == 0 || i < NVP) {
-          const T* src = vp + 4 * (i % (KB / 4)) * kvstride + (i / (KB / 4)) * EPC;
-#pragma unroll
-          for (int x = 0; x < 4; ++x) pv[j][x] = *reinterpret_cast<const V16*>(src + x * kvstride);
-        }
-      }
-    } else {
-      V16 z;
-#pragma unroll
-      for (int x = 0; x < EPC; ++x) z[x] = from_f32<T>(0.f);
-#pragma unroll
-      for (int j = 0; j < NPK; ++j) {
-        const int i = tid + j * NTH;
-        pk[j] = i / CH < nkey ? *reinterpret_cast<const V16*>(kp + (i / CH) * kvstride + (i % CH) * EPC) : z;
-      }
-#pragma unroll
-      for (int j = 0; j < NPV; ++j) {
-        const int i = tid + j * NTH;
-        if (NVP % NTH == 0 || i < NVP) {
-          const int key0 = 4 * (i % (KB / 4));
-          const T* src = vp + key0 * kvstride + (i / (KB / 4)) * EPC;
-#pragma unroll
-          for (int x = 0; x < 4; ++x)
-            pv[j][x] = key0 + x < nkey ? *reinterpret_cast<const V16*>(src + x * kvstride) : z;
-        }
-      }
-    }
-  };
-  auto commit = [&](int buf) {
+    pf_nkey = bl.kend - bl.kb0;
+    const int last = pf_nkey - 1;
 #pragma unroll
     for (int j = 0; j < NPK; ++j) {
       const int i = tid + j * NTH;
-      *reinterpret_cast<V16*>(&Ks(buf)[(i / CH) * SK + (i % CH) * EPC]) = pk[j];
+      pk[j] = *reinterpret_cast<const V16*>(kp + min(i / CH, last) * kvstride + (i % CH) * EPC);
     }
 #pragma unroll
     for (int j = 0; j < NPV; ++j) {
       const int i = tid + j * NTH;
       if (NVP % NTH == 0 || i < NVP) {
-        T* col = &VTs(buf)[(i / (KB / 4)) * EPC * SV + acc_pos(4 * (i % (KB / 4)))];
+        const int key0 = 4 * (i % (KB / 4));
+        const T* src = vp + (i / (KB / 4)) * EPC;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) pv[j][x] = *reinterpret_cast<const V16*>(src + min(key0 + x, last) * kvstride);
+      }
+    }
+  };
+  auto commit = [&](T* Kd, T* Vd, const PK& pk, const PV& pv, int pf_nkey) {
+    const bool whole = pf_nkey >= KB;              // uniform
+    V16 z;
+#pragma unroll
+    for (int x = 0; x < EPC; ++x) z[x] = from_f32<T>(0.f);
+#pragma unroll
+    for (int j = 0; j < NPK; ++j) {
+      const int i = tid + j * NTH;
+      *reinterpret_cast<V16*>(&Kd[(i / CH) * SK + (i % CH) * EPC]) = whole || i / CH < pf_nkey ? pk[j] : z;
+    }
+#pragma unroll
+    for (int j = 0; j < NPV; ++j) {
+      const int i = tid + j * NTH;
+      if (NVP % NTH == 0 || i < NVP) {
+        const int key0 = 4 * (i % (KB / 4));
+        V16 pvv[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) pvv[x] = whole || key0 + x < pf_nkey ? pv[j][x] : z;
+        T* col = &Vd[(i / (KB / 4)) * EPC * SV + acc_pos(key0)];
 #pragma unroll
         for (int e = 0; e < EPC; ++e) {
           if constexpr (sizeof(T) == 2) {
-            *reinterpret_cast<bf16x4*>(col + e * SV) = bf16x4{pv[j][0][e], pv[j][1][e], pv[j][2][e], pv[j][3][e]};
+            *reinterpret_cast<bf16x4*>(col + e * SV) = bf16x4{pvv[0][e], pvv[1][e], pvv[2][e], pvv[3][e]};
           } else {
-            *reinterpret_cast<f32x4*>(col + e * SV) = f32x4{pv[j][0][e], pv[j][1][e], pv[j][2][e], pv[j][3][e]};
+            *reinterpret_cast<f32x4*>(col + e * SV) = f32x4{pvv[0][e], pvv[1][e], pvv[2][e], pvv[3][e]};
           }
         }
       }
@@ -270,12 +274,42 @@ __device__ __forceinline__ void swa_tiles(const T* __restrict__ q, const T* __re
     float x1[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
     ones = frag_from8<T>(x1);
   }
+  // Deep staging (linked, one tile of at most kDeepBlocks blocks): the
+  // loads of every block and of the queries are issued together, then every
+  // block is committed to its own LDS area.  Otherwise blocks go through two
+  // LDS buffers, the next one prefetched into registers while the current
+  // one is used.
+  auto DKs = [&](int blk) { return lds + blk * (KB * SK + D * SV); };
+  auto DVTs = [&](int blk) { return DKs(blk) + KB * SK; };
+  bool deep = false;
+  QRaw qraw[kNQ][D / 32];
+  if constexpr (LINKED) {
+    if (ntile == 1) {
+      int nbs, nbw, se, wl, te;
+      tile_blocks(tile0 * QT, nbs, nbw, se, wl, te);
+      const int nblk = nbs + nbw;
+      if (nblk <= kDeepBlocks) {
+        deep = true;
+#pragma unroll
+        for (int b2 = 0; b2 < kDeepBlocks; ++b2)
+          if (b2 < nblk) {
+            Blk bl;
+            block_of(0, b2, bl);
+            prefetch(bl, pks[b2], pvs[b2], nks[b2]);
+          }
+        load_q(0, qraw);
+#pragma unroll
+        for (int b2 = 0; b2 < kDeepBlocks; ++b2)
+          if (b2 < nblk) commit(DKs(b2), DVTs(b2), pks[b2], pvs[b2], nks[b2]);
+      }
+    }
+  }
   int flat = 0;   // running block counter (selects the LDS buffer)
-  if (ntile > 0) {
+  if (!deep && ntile > 0) {
     Blk b0;
     block_of(0, 0, b0);
-    prefetch(b0);
-    commit(0);
+    prefetch(b0, pks[0], pvs[0], nks[0]);
+    commit(Ks(0), VTs(0), pks[0], pvs[0], nks[0]);
   }
   lds_barrier();
 
@@ -287,8 +321,7 @@ __device__ __forceinline__ void swa_tiles(const T* __restrict__ q, const T* __re
     tile_blocks(t0, nbs, nbw, sink_end, win_lo, t_end);
     const int nblk = nbs + nbw;
 
-    QRaw qraw[kNQ][D / 32];
-    load_q(ti, qraw);
+    if (!deep) load_q(ti, qraw);
     Frag<T> qf[kNQ][D / 32];
 #pragma unroll
     for (int nq = 0; nq < kNQ; ++nq)
@@ -324,13 +357,13 @@ __device__ __forceinline__ void swa_tiles(const T* __restrict__ q, const T* __re
       const int kend = sinkph ? sink_end : t_end;
       const bool last = blk + 1 == nblk;
       const bool has_next = !last || ti + 1 < ntile;
-      if (has_next) {
+      if (!deep && has_next) {
         Blk nx;
         block_of(last ? ti + 1 : ti, last ? 0 : blk + 1, nx);
-        prefetch(nx);
+        prefetch(nx, pks[0], pvs[0], nks[0]);
       }
-      const T* Kb = Ks(buf);
-      const T* Vb = VTs(buf);
+      const T* Kb = deep ? DKs(blk) : Ks(buf);
+      const T* Vb = deep ? DVTs(blk) : VTs(buf);
 
       // ---- S^T tiles for this wave, computed relative to the running max:
       // the accumulators start at -mbase, so the MFMAs return s - mbase
@@ -465,17 +498,48 @@ __device__ __forceinline__ void swa_tiles(const T* __restrict__ q, const T* __re
         }
       }
 
-      if (has_next) commit(buf ^ 1);
-      lds_barrier();
+      if (!deep) {
+        if (has_next) commit(Ks(buf ^ 1), VTs(buf ^ 1), pks[0], pvs[0], nks[0]);
+        lds_barrier();
+      }
     }
 
     // ---- epilogue of this query tile
     if constexpr (LINKED) {
+      // the done flags of the scan chunks covering this wave's rows are
+      // consecutive: one flag per lane, polled together
       const int r_lo = max(qb, add_from);
       const int r_hi = min(qlast, T_ - 1);
       if (r_lo <= r_hi) {
-        for (int c = (r_lo - add_from) / 64; c <= (r_hi - add_from) / 64; ++c)
-          for (int f = 0; f < nflag; ++f) wait_ready<32>(done + ((size_t)(bi * H + h) * nch + c) * nflag + f, epoch);
+        const int c_lo = (r_lo - add_from) / 64;
+        const int nf = ((r_hi - add_from) / 64 - c_lo + 1) * nflag;
+        const uint64_t* f0 = done + ((size_t)(bi * H + h) * nch + c_lo) * nflag;
+        for (int s0 = 0; s0 < nf; s0 += 64) wait_ready_span<32>(f0 + s0, min(64, nf - s0), epoch, lane);
+      }
+    }
+    // what o holds on rows >= add_from, read before any row is written: every
+    // load is issued unconditionally (rows past the sequence read its last
+    // row) and the values are selected afterwards, so the loads overlap
+    typedef typename std::conditional<sizeof(T) == 2, bf16x4, f32x4>::type Raw4;
+    Raw4 raw[kNQ][D / 16];
+#pragma unroll
+    for (int nq = 0; nq < kNQ; ++nq) {
+      const int tr = min(qb + 16 * nq + l16, T_ - 1);
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const int d0 = 16 * dt + 4 * lg;
+        if constexpr (LINKED) {
+          // wave-uniform base, device-scope read of the scan's output
+          static_assert(sizeof(T) == 2, "linked tiles are bf16");
+          typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+          const T* obase = o + ((size_t)(bi * T_ + qb) * H + h) * D;
+          raw[nq][dt] = __builtin_bit_cast(
+              Raw4, __builtin_amdgcn_raw_buffer_load_b64(
+                        __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(obase), 0, 0x7fffffff, 0x00020000),
+                        ((tr - qb) * H * D + d0) * 2, 0, 16));
+        } else {
+          raw[nq][dt] = *reinterpret_cast<const Raw4*>(o + ((size_t)(bi * T_ + tr) * H + h) * D + d0);
+        }
       }
     }
 #pragma unroll
@@ -489,15 +553,9 @@ __device__ __forceinline__ void swa_tiles(const T* __restrict__ q, const T* __re
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
         f32x4 val = oacc[dt][nq] * inv;
-        const int d0 = 16 * dt + 4 * lg;
-        if constexpr (LINKED) {
-          // wave-uniform base, device-scope read of the scan's output
-          const T* obase = o + ((size_t)(bi * T_ + qb) * H + h) * D;
-          if (addl) val += load4_dev(obase, (16 * nq + l16) * H * D + d0);
-        } else {
-          if (addl) val += load4(orow + d0);
-        }
-        store4(orow + d0, val);
+        if (addl) val += f32x4{static_cast<float>(raw[nq][dt][0]), static_cast<float>(raw[nq][dt][1]),
+                               static_cast<float>(raw[nq][dt][2]), static_cast<float>(raw[nq][dt][3])};
+        store4(orow + 16 * dt + 4 * lg, val);
       }
     }
   }
