@@ -228,8 +228,8 @@ LAYER_SOURCES = ("swa_chunked_gated_amd/csrc/gdn_prep.h", "swa_chunked_gated_amd
 SWA_SOURCES = ("swa_chunked_gated_amd/csrc/swa.hip", "swa_chunked_gated_amd/csrc/swa_tile.h",
                "swa_chunked_gated_amd/csrc/common.h")
 DECODE_SOURCES = ("swa_chunked_gated_amd/csrc/decode.hip", "swa_chunked_gated_amd/csrc/common.h")
-# one decode step is three launches: softmax branch, state update, cache commit
-DECODE_KERNELS = "decode_swa_kernel+decode_state_kernel+decode_commit_kernel"
+# one decode step is two launches: both branches and the state update, then the cache commit
+DECODE_KERNELS = "decode_step_kernel+decode_commit_kernel"
 
 
 def stored_traffic(kernel, workload, sources):

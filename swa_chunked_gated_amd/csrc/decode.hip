@@ -8,13 +8,13 @@
 // e = t - window, is folded into the per-head recurrent state with its own
 // gates, and the state is read with q_t.  The two outputs are summed.
 //
-// Work split: the softmax branch runs first, one workgroup per (sequence,
-// KV head) for its G query heads, so every cached row is read once; the
-// linear branch then streams each head's d x d fp32 state through registers
-// exactly once (one read, one write), one workgroup per (sequence, query
-// head), and adds its output.  A third small kernel (one workgroup per
-// sequence) writes the new token into the freed slot and advances pos,
-// after every head has read the evicted entry.
+// Work split: one workgroup per (sequence, query head) runs both branches.
+// It streams the head's d x d fp32 state through registers exactly once (one
+// read, one write) and, while those loads are in flight, the softmax over
+// the cached rows; the G heads of a KV head share an XCD, so a cached row is
+// fetched from HBM once per group.  o is written once.  A second small kernel
+// (one workgroup per sequence) writes the new token into the freed slot and
+// advances pos, after every head has read the evicted entry.
 //
 // Gated delta rule in one pass over the old state S (a, b: evicted gates):
 //   c1 = S^T k_e, c2 = S^T q, u = b (v_e - a c1)
@@ -27,10 +27,7 @@
 namespace gdn {
 namespace {
 
-constexpr int kSwaThreads = 256;
-constexpr int kStateThreads = 512;
-constexpr int kMaxG = 16;
-constexpr int kSlotChunk = 64;   // cache rows staged in LDS at a time
+constexpr int kStepThreads = 512;
 
 // Slot state of cache slot j for the new token t: -1 not attended, 0 the
 // cached entry, 1 the new token (its slot is being overwritten this step).
@@ -42,190 +39,147 @@ __device__ __forceinline__ int slot_state_of(int j, int t, int n_sink, int windo
   return back == 0 ? 1 : (t - back >= n_sink ? 0 : -1);   // latest token of this ring slot
 }
 
-// Softmax branch of the decode step for the G query heads of one KV head:
-// each cached K and V row is staged through LDS once (both fetched together)
-// and used by all G heads.  Writes o (I/O type) = the softmax output of each
-// head.
-template <class T, int D>
-__global__ __launch_bounds__(kSwaThreads) void decode_swa_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const T* __restrict__ kc, const T* __restrict__ vc, const int* __restrict__ pos,
-    T* __restrict__ o, int B, int H, int Hkv, int n_sink, int window) {
-  constexpr int VEC = 16 / sizeof(T);
-  constexpr int SPH = kSwaThreads / D;      // slot phases of the P V sum
-  constexpr int SR = D + VEC;               // staged row stride
-  typedef typename Vec16<T>::type V16;
-  const int G = H / Hkv;
-  const int grp = blockIdx.x;               // (sequence, KV head)
-  const int bi = grp / Hkv;
-  const int g = grp % Hkv;
-  const int N = n_sink + window;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = wave_id();
-  const int t = pos[bi];
-  if (t < 0) return;   // outside the contract (pos >= 0); never index a negative slot
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* gbl_void_ptr;
 
-  extern __shared__ float sm[];
-  float* qs = sm;                           // [G][D]
-  float* kt = qs + G * D;                   // [D] new key
-  float* vt = kt + D;                       // [D] new value
-  float* lg = vt + D;                       // [G][N] logits, then probabilities
-  T* ks = reinterpret_cast<T*>((reinterpret_cast<uintptr_t>(lg + G * N) + 15) & ~(uintptr_t)15);
-  T* vs = ks + kSlotChunk * SR;             // [64][SR] staged K and V rows
-
-  const size_t kvbase = (size_t)grp * N * D;     // cache [B][Hkv][N][D]
-  const size_t tokkv = (size_t)grp * D;          // k, v  [B][Hkv][D]
-  // K and V rows of slots j0 .. j0 + nj - 1 (the new token's slot from k, v;
-  // slots not attended as zeros): fetched into registers, then stored to LDS
-  constexpr int PER = (kSlotChunk * (D / VEC) + kSwaThreads - 1) / kSwaThreads;
-  V16 kr[PER], vr[PER];
-  auto fetch = [&](int j0, int nj) {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int i = tid + u * kSwaThreads;
-      const int jj = i / (D / VEC);
-      const int c = (i % (D / VEC)) * VEC;
-      const int st = jj < nj ? slot_state_of(j0 + jj, t, n_sink, window) : -1;
-      if (st == 0) {
-        kr[u] = *reinterpret_cast<const V16*>(kc + kvbase + (size_t)(j0 + jj) * D + c);
-        vr[u] = *reinterpret_cast<const V16*>(vc + kvbase + (size_t)(j0 + jj) * D + c);
-      } else {
-#pragma unroll
-        for (int xx = 0; xx < VEC; ++xx) {
-          kr[u][xx] = from_f32<T>(0.f);
-          vr[u][xx] = from_f32<T>(0.f);
-        }
-      }
-    }
-  };
-  auto store = [&](int j0, int nj) {
-    lds_barrier();   // kt / vt are in place; the previous chunk's reads are done
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int i = tid + u * kSwaThreads;
-      const int jj = i / (D / VEC);
-      const int c = (i % (D / VEC)) * VEC;
-      if (jj < kSlotChunk) {
-        const int st = jj < nj ? slot_state_of(j0 + jj, t, n_sink, window) : -1;
-        if (st == 1) {
-#pragma unroll
-          for (int xx = 0; xx < VEC; ++xx) {
-            kr[u][xx] = from_f32<T>(kt[c + xx]);
-            vr[u][xx] = from_f32<T>(vt[c + xx]);
-          }
-        }
-        *reinterpret_cast<V16*>(&ks[jj * SR + c]) = kr[u];
-        *reinterpret_cast<V16*>(&vs[jj * SR + c]) = vr[u];
-      }
-    }
-    lds_barrier();
-  };
-  // the first chunk's rows are requested before the small per-step vectors
-  fetch(0, min(kSlotChunk, N));
-  for (int i = tid; i < G * D; i += kSwaThreads) qs[i] = to_f32(q[((size_t)bi * H + g * G) * D + i]);
-  for (int i = tid; i < D; i += kSwaThreads) {
-    kt[i] = to_f32(k[tokkv + i]);
-    vt[i] = to_f32(v[tokkv + i]);
-  }
-
-  // ---- logits: thread (slot, head) takes a whole dot product
-  const float scale = 1.0f / sqrtf((float)D);
-  for (int j0 = 0; j0 < N; j0 += kSlotChunk) {
-    const int nj = min(kSlotChunk, N - j0);
-    if (j0 > 0) fetch(j0, nj);
-    store(j0, nj);
-    for (int i = tid; i < nj * G; i += kSwaThreads) {
-      const int jj = i % nj;
-      const int hh = i / nj;
-      float acc = 0.f;
-#pragma unroll 4
-      for (int d = 0; d < D; d += VEC) {
-        const V16 kx = *reinterpret_cast<const V16*>(&ks[jj * SR + d]);
-#pragma unroll
-        for (int xx = 0; xx < VEC; ++xx) acc += to_f32(kx[xx]) * qs[hh * D + d + xx];
-      }
-      lg[hh * N + j0 + jj] = slot_state_of(j0 + jj, t, n_sink, window) >= 0 ? acc * scale : -INFINITY;
-    }
-  }
-  lds_barrier();
-  // ---- softmax per head (wave w takes heads w, w + 4, ...)
-  for (int hh = wv; hh < G; hh += kSwaThreads / 64) {
-    float* l = lg + hh * N;
-    float m = -INFINITY;
-    for (int j = lane; j < N; j += 64) m = fmaxf(m, l[j]);
-    m = wave_max(m);
-    float sum = 0.f;
-    for (int j = lane; j < N; j += 64) {
-      const float xv = l[j];
-      const float pr = xv == -INFINITY ? 0.f : __expf(xv - m);
-      l[j] = pr;
-      sum += pr;
-    }
-    sum = wave_sum(sum);
-    const float inv = 1.0f / sum;
-    for (int j = lane; j < N; j += 64) l[j] *= inv;
-  }
-  lds_barrier();
-  // ---- o = P V: thread (column c, head hh) sums over the slots; SPH heads
-  // per pass of the workgroup
-  const int c = tid % D;
-  for (int h0 = 0; h0 < G; h0 += SPH) {
-    const int hh = h0 + tid / D;
-    float acc = 0.f;
-    if (N > kSlotChunk) {
-      // several chunks: restage V chunk by chunk (all threads take part)
-      for (int j0 = 0; j0 < N; j0 += kSlotChunk) {
-        const int nj = min(kSlotChunk, N - j0);
-        fetch(j0, nj);
-        store(j0, nj);
-        if (hh < G)
-          for (int jj = 0; jj < nj; ++jj) acc += lg[hh * N + j0 + jj] * to_f32(vs[jj * SR + c]);
-      }
-    } else if (hh < G) {
-#pragma unroll 8
-      for (int jj = 0; jj < N; ++jj) acc += lg[hh * N + jj] * to_f32(vs[jj * SR + c]);
-    }
-    if (hh < G) o[((size_t)bi * H + g * G + hh) * D + c] = from_f32<T>(acc);
-  }
+// Lane L of the wave loads 16 bytes at g into LDS at base + 16 L; no
+// registers are involved.
+__device__ __forceinline__ void dma16(const void* g, void* base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_ptr)(void*)g, (lds_void_ptr)base, 16, 0, 0);
 }
 
-template <int D>
-struct StateMap {
+// Wait until at most n vector-memory operations of this wave are outstanding
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt at their
+// maxima).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+}
+
+template <class T, int D>
+struct StepMap {
   static constexpr int CG = D / 4;                 // column groups of 4 floats
-  static constexpr int RG = kStateThreads / CG;    // row groups
-  static constexpr int R = D / RG;                 // rows per thread
-  static constexpr int NWV = kStateThreads / 64;   // waves
+  static constexpr int RG = kStepThreads / CG;     // row groups
+  static constexpr int R = D / RG;                 // state rows per thread
+  static constexpr int NWV = kStepThreads / 64;    // waves
+  static constexpr int ROWS = 128 / sizeof(T);     // cache rows staged per pass
+  static constexpr int UPR = D * sizeof(T) / 16;   // 16-byte units per cache row
+  static constexpr int UPT = ROWS * UPR / kStepThreads;   // staged units per thread
+  static constexpr int LPS = kStepThreads / ROWS;  // lanes per row in the logits
+  static constexpr int VEC = 16 / sizeof(T);       // elements per unit
+  static constexpr int UPL = UPR / LPS;            // units per lane in the logits
+  static constexpr int VPT = ROWS / RG;            // V rows per thread in P V
+  static_assert(UPT >= 1 && UPL >= 1 && VPT >= 1, "tile shape");
 };
 
-// Linear branch of the decode step, one workgroup per (sequence, query
-// head): the head's d x d fp32 state is streamed through registers exactly
-// once (one read, one write), its loads issued before anything else.  With
-// the softmax branch, o already holds its output and the linear output is
-// added to it.
+// 4 consecutive elements of the I/O type (8 bytes of bf16, 16 of fp32).
+template <class T> struct Raw4;
+template <> struct Raw4<bf16> { typedef bf16x4 type; };
+template <> struct Raw4<float> { typedef f32x4 type; };
+__device__ __forceinline__ f32x4 raw4_f32(const bf16x4& x) {
+  return f32x4{static_cast<float>(x[0]), static_cast<float>(x[1]), static_cast<float>(x[2]),
+               static_cast<float>(x[3])};
+}
+__device__ __forceinline__ f32x4 raw4_f32(const f32x4& x) { return x; }
+
+// One decode step of one (sequence, query head), both branches in one
+// workgroup.  Issue order: the first pass of cached K and V rows goes
+// straight to LDS (no registers), then the small per-step vectors, then the
+// head's d x d fp32 state, which is streamed through registers exactly once
+// (one read, one write).  The softmax over the staged rows runs while the
+// state is still arriving.  Workgroups are placed so that the G query heads
+// of a KV head run together on one XCD: each cached row comes from HBM once
+// and from that XCD's L2 for the other heads.  o is written once.
 template <class T, bool GLA, int D>
-__global__ __launch_bounds__(kStateThreads) void decode_state_kernel(
-    const T* __restrict__ q, const float* __restrict__ a, const float* __restrict__ b,
-    float* __restrict__ state, const T* __restrict__ kc, const T* __restrict__ vc,
-    const float* __restrict__ ac, const float* __restrict__ bc, const int* __restrict__ pos,
-    T* __restrict__ o, int B, int H, int Hkv, int n_sink, int window, int flags) {
-  using M = StateMap<D>;
-  const int bh = blockIdx.x;
-  const int bi = bh / H;
-  const int h = bh % H;
-  const int g = h / (H / Hkv);
+__global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(6, 8))) void decode_step_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ a, const float* __restrict__ b, float* __restrict__ state,
+    const T* __restrict__ kc, const T* __restrict__ vc, const float* __restrict__ ac,
+    const float* __restrict__ bc, const int* __restrict__ pos, T* __restrict__ o, int B, int H,
+    int Hkv, int n_sink, int window, int flags) {
+  using M = StepMap<T, D>;
+  typedef typename Vec16<T>::type V16;
+  typedef typename Raw4<T>::type R4;
+  constexpr int VLOAD = 3 * M::UPR + (GLA ? D / 4 : 0);   // 16-byte units of the per-step vectors
+  constexpr int VUNITS = (VLOAD + 63) / 64 * 64;
+  static_assert(VUNITS <= 64 * M::NWV, "one load per wave");
+  const int G = H / Hkv;
+  int grp, member;
+  if (!xcd_grouped(blockIdx.x, G, B * Hkv, grp, member)) return;
+  const int bi = grp / Hkv;
+  const int h = (grp % Hkv) * G + member;
+  const int bh = bi * H + h;
   const int N = n_sink + window;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = wave_id();
   const int t = pos[bi];
   if (t < 0) return;   // outside the contract (pos >= 0); never index a negative slot
+  const bool lin = flags & 1;
+  const bool swa = flags & 2;
   const int e = t - window;
   const bool evict = e >= n_sink;
   const int slot = t < n_sink ? t : n_sink + (t - n_sink) % window;
   const int ring = t < n_sink ? -1 : (t - n_sink) % window;
 
-  // ---- the head's state is streamed once: issue its loads before anything else
+  __shared__ __align__(16) T ks[M::ROWS * D];
+  __shared__ __align__(16) T vs[M::ROWS * D];
+  __shared__ float lg[M::ROWS];   // logits of the staged rows, log2 domain
+  // per-step vectors as loaded: q, k_e, v_e (I/O type), then GLA's a_e (fp32)
+  __shared__ __align__(16) unsigned char vecs[VUNITS * 16];
+  __shared__ __align__(16) float gates[64];   // GDN: a_e, b_e
+  __shared__ float misc[4];
+  __shared__ float red[M::NWV * M::CG * 12];
+  __shared__ __align__(16) float fin[M::CG * 12];   // c1, c2, c3 per column group
+  const T* qv = reinterpret_cast<const T*>(vecs);
+  const T* kev = qv + D;
+  const T* vev = kev + D;
+  const float* aev = GLA ? reinterpret_cast<const float*>(vev + D) : gates;
+
+  // ---- cached K and V rows j0 .. j0 + ROWS - 1 into LDS, row-major; the
+  // new token's slot takes its row from k, v; rows past N repeat row N - 1
+  // (never used)
+  const size_t kvbase = (size_t)grp * N * D;   // cache [B][Hkv][N][D]
+  const size_t tokkv = (size_t)grp * D;        // k, v  [B][Hkv][D]
+  auto stage = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < M::UPT; ++u) {
+      const int w0 = (u * M::NWV + wv) * 64;   // first unit of this wave's load
+      const int P = w0 + lane;
+      const int j = min(j0 + P / M::UPR, N - 1);
+      const int c = (P % M::UPR) * M::VEC;
+      const T* kg = j == slot ? k + tokkv + c : kc + kvbase + (size_t)j * D + c;
+      const T* vg = j == slot ? v + tokkv + c : vc + kvbase + (size_t)j * D + c;
+      dma16(kg, ks + (size_t)w0 * M::VEC);
+      dma16(vg, vs + (size_t)w0 * M::VEC);
+    }
+  };
+  if (swa) stage(0);
+  asm volatile("" ::: "memory");
+
+  // ---- the small per-step vectors, also straight into LDS: wave w loads
+  // units 64 w .. 64 w + 63 of [q | k_e | v_e | a_e (GLA)]; units past the
+  // end repeat a valid address into padding
+  const size_t gb = evict ? ((size_t)bi * window + ring) * H + h : 0;   // gate cache [B][W][H](,D)
+  if (wv * 64 < VLOAD) {
+    const int P = min(wv * 64 + lane, VLOAD - 1);
+    const int vi = P / M::UPR;            // which vector
+    const int c = (P % M::UPR) * M::VEC;  // element offset (I/O-type vectors)
+    const void* src;
+    if (vi == 0) src = q + (size_t)bh * D + c;
+    else if (vi == 1) src = kc + kvbase + (size_t)slot * D + c;
+    else if (vi == 2) src = vc + kvbase + (size_t)slot * D + c;
+    else src = ac + gb * D + (P - 3 * M::UPR) * 4;   // GLA gates, fp32
+    dma16(src, vecs + wv * 64 * 16);
+  }
+  if (!GLA && wv == M::NWV - 1) {
+    const float* src = lane == 1 ? bc + gb : ac + gb;
+    __builtin_amdgcn_global_load_lds((gbl_void_ptr)(void*)src, (lds_void_ptr)(void*)gates, 4, 0, 0);
+  }
+  asm volatile("" ::: "memory");
+
+  // ---- the head's state, streamed once
   const int cg = tid % M::CG;
   const int rg = tid / M::CG;
   float* Sg = state + (size_t)bh * D * D;
@@ -234,31 +188,67 @@ __global__ __launch_bounds__(kStateThreads) void decode_state_kernel(
   for (int r = 0; r < M::R; ++r)
     s[r] = *reinterpret_cast<const f32x4*>(Sg + (size_t)(rg + M::RG * r) * D + 4 * cg);
 
-  __shared__ float qs[D], ke[D], ve[D], ae[D], misc[4];
-  __shared__ float red[M::NWV * M::CG * 8];
-  const size_t kvbase = ((size_t)bi * Hkv + g) * N * D;
-  for (int i = tid; i < D; i += kStateThreads) {
-    qs[i] = to_f32(q[(size_t)bh * D + i]);
-    if (evict) {
-      ke[i] = to_f32(kc[kvbase + (size_t)slot * D + i]);
-      ve[i] = to_f32(vc[kvbase + (size_t)slot * D + i]);
-    }
-  }
-  if (evict) {
-    const size_t gb = ((size_t)bi * window + ring) * H + h;   // gate cache [B][W][H](,D)
-    if (GLA) {
-      for (int i = tid; i < D; i += kStateThreads) ae[i] = ac[gb * D + i];
-    } else if (tid == 0) {
-      ae[0] = ac[gb];
-      misc[0] = bc[gb];
-    }
-  }
+  wait_vmcnt<M::R>();   // every load before the state's has landed (the staged rows)
   lds_barrier();
   if (evict && wv == 0) {
     float acc = 0.f;
-    for (int i = lane; i < D; i += 64) acc += ke[i] * qs[i];
+    for (int i = lane; i < D; i += 64) acc += to_f32(kev[i]) * to_f32(qv[i]);
     acc = wave_sum(acc);
     if (lane == 0) misc[1] = acc;   // k_e . q
+  }
+
+  // ---- softmax over the staged rows, online across passes of ROWS rows
+  float p3[4] = {0.f, 0.f, 0.f, 0.f};
+  float mx = -INFINITY, den = 0.f;
+  if (swa) {
+    const float lscale = 1.4426950408889634f / sqrtf((float)D);   // log2(e) / sqrt(d)
+    const int kj = tid / M::LPS;
+    const int kp = tid % M::LPS;
+    for (int j0 = 0; j0 < N; j0 += M::ROWS) {
+      if (j0 > 0) {
+        lds_barrier();   // every wave is done with the previous pass's rows
+        stage(j0);
+        wait_vmcnt<0>();
+        lds_barrier();
+      }
+      // logits: LPS lanes per row, units kp, kp + LPS, ... of the row
+      {
+        const int j = j0 + kj;
+        float acc = 0.f;
+#pragma unroll
+        for (int m = 0; m < M::UPL; ++m) {
+          const int c = (kp + M::LPS * m) * M::VEC;
+          const V16 kx = *reinterpret_cast<const V16*>(&ks[kj * D + c]);
+          const V16 qx = *reinterpret_cast<const V16*>(&qv[c]);
+#pragma unroll
+          for (int xx = 0; xx < M::VEC; ++xx) acc += to_f32(kx[xx]) * to_f32(qx[xx]);
+        }
+#pragma unroll
+        for (int m = 1; m < M::LPS; m <<= 1) acc += shfl_xor(acc, m);
+        if (kp == 0) {
+          const bool att = j < N && slot_state_of(j, t, n_sink, window) >= 0;
+          lg[kj] = att ? acc * lscale : -INFINITY;
+        }
+      }
+      lds_barrier();
+      // running maximum and denominator (every wave keeps its own copy)
+      const float lj = lane < M::ROWS ? lg[lane] : -INFINITY;
+      const float mn = fmaxf(mx, wave_max(lj));
+      const float sc = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - mn);
+      den = den * sc + wave_sum(lj == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lj - mn));
+      mx = mn;
+#pragma unroll
+      for (int xx = 0; xx < 4; ++xx) p3[xx] *= sc;
+#pragma unroll 1
+      for (int i = 0; i < M::VPT; ++i) {
+        const int jj = rg + M::RG * i;
+        const float l = lg[jj];
+        const f32x4 vv = raw4_f32(*reinterpret_cast<const R4*>(&vs[jj * D + 4 * cg]));
+        const float pj = l == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(l - mn);
+#pragma unroll
+        for (int xx = 0; xx < 4; ++xx) p3[xx] += l == -INFINITY ? 0.f : pj * vv[xx];
+      }
+    }
   }
 
   // ---- one pass over the state held in registers: c1 = S^T k_e, c2 = S^T q
@@ -267,12 +257,12 @@ __global__ __launch_bounds__(kStateThreads) void decode_state_kernel(
 #pragma unroll
   for (int r = 0; r < M::R; ++r) {
     const int row = rg + M::RG * r;
-    float qr = qs[row];
-    if (GLA && evict) qr *= ae[row];
-    const float kr = evict ? ke[row] : 0.f;
+    float qr = to_f32(qv[row]);
+    if (GLA && evict) qr *= aev[row];
+    const float kr2 = evict ? to_f32(kev[row]) : 0.f;
 #pragma unroll
     for (int xx = 0; xx < 4; ++xx) {
-      p1[xx] += s[r][xx] * kr;
+      p1[xx] += s[r][xx] * kr2;
       p2[xx] += s[r][xx] * qr;
     }
   }
@@ -283,55 +273,57 @@ __global__ __launch_bounds__(kStateThreads) void decode_state_kernel(
     for (int xx = 0; xx < 4; ++xx) {
       p1[xx] += shfl_xor(p1[xx], m);
       p2[xx] += shfl_xor(p2[xx], m);
+      p3[xx] += shfl_xor(p3[xx], m);
     }
   }
   if (lane < M::CG) {
 #pragma unroll
     for (int xx = 0; xx < 4; ++xx) {
-      red[(wv * M::CG + cg) * 8 + xx] = p1[xx];
-      red[(wv * M::CG + cg) * 8 + 4 + xx] = p2[xx];
+      red[(wv * M::CG + cg) * 12 + xx] = p1[xx];
+      red[(wv * M::CG + cg) * 12 + 4 + xx] = p2[xx];
+      red[(wv * M::CG + cg) * 12 + 8 + xx] = p3[xx];
     }
   }
   lds_barrier();
-  float c1[4], c2[4];
+  // across the waves: one thread per reduced value, so that few registers
+  // are live beside the state
+  if (tid < 12 * M::CG) {
+    float acc = 0.f;
 #pragma unroll
-  for (int xx = 0; xx < 4; ++xx) {
-    c1[xx] = 0.f;
-    c2[xx] = 0.f;
-#pragma unroll
-    for (int w = 0; w < M::NWV; ++w) {
-      c1[xx] += red[(w * M::CG + cg) * 8 + xx];
-      c2[xx] += red[(w * M::CG + cg) * 8 + 4 + xx];
-    }
+    for (int w = 0; w < M::NWV; ++w) acc += red[w * M::CG * 12 + tid];
+    fin[tid] = acc;
   }
+  lds_barrier();
+  const f32x4 c1 = *reinterpret_cast<const f32x4*>(&fin[cg * 12]);
   float olin[4];
+  const f32x4 c2 = *reinterpret_cast<const f32x4*>(&fin[cg * 12 + 4]);
   if (evict) {
     const float kqh = misc[1];
     if (GLA) {
 #pragma unroll
-      for (int xx = 0; xx < 4; ++xx) olin[xx] = c2[xx] + ve[4 * cg + xx] * kqh;
+      for (int xx = 0; xx < 4; ++xx) olin[xx] = c2[xx] + to_f32(vev[4 * cg + xx]) * kqh;
 #pragma unroll
       for (int r = 0; r < M::R; ++r) {
         const int row = rg + M::RG * r;
-        const float al = ae[row];
-        const float kr = ke[row];
+        const float al = aev[row];
+        const float kr2 = to_f32(kev[row]);
 #pragma unroll
-        for (int xx = 0; xx < 4; ++xx) s[r][xx] = al * s[r][xx] + kr * ve[4 * cg + xx];
+        for (int xx = 0; xx < 4; ++xx) s[r][xx] = al * s[r][xx] + kr2 * to_f32(vev[4 * cg + xx]);
       }
     } else {
-      const float al = ae[0];
-      const float bt = misc[0];
+      const float al = gates[0];
+      const float bt = gates[1];
       float u[4];
 #pragma unroll
       for (int xx = 0; xx < 4; ++xx) {
-        u[xx] = bt * (ve[4 * cg + xx] - al * c1[xx]);
+        u[xx] = bt * (to_f32(vev[4 * cg + xx]) - al * c1[xx]);
         olin[xx] = al * c2[xx] + u[xx] * kqh;
       }
 #pragma unroll
       for (int r = 0; r < M::R; ++r) {
-        const float kr = ke[rg + M::RG * r];
+        const float kr2 = to_f32(kev[rg + M::RG * r]);
 #pragma unroll
-        for (int xx = 0; xx < 4; ++xx) s[r][xx] = al * s[r][xx] + kr * u[xx];
+        for (int xx = 0; xx < 4; ++xx) s[r][xx] = al * s[r][xx] + kr2 * u[xx];
       }
     }
 #pragma unroll
@@ -341,13 +333,13 @@ __global__ __launch_bounds__(kStateThreads) void decode_state_kernel(
 #pragma unroll
     for (int xx = 0; xx < 4; ++xx) olin[xx] = c2[xx];
   }
-  if (rg == 0 && (flags & 1)) {
-    T* orow = o + (size_t)bh * D + 4 * cg;
+  if (rg == 0) {
+    const f32x4 c3 = *reinterpret_cast<const f32x4*>(&fin[cg * 12 + 8]);
+    const float inv = swa ? 1.0f / den : 0.f;
     f32x4 out;
 #pragma unroll
-    for (int xx = 0; xx < 4; ++xx) out[xx] = olin[xx];
-    if (flags & 2) out += load4(orow);
-    store4(orow, out);
+    for (int xx = 0; xx < 4; ++xx) out[xx] = (lin ? olin[xx] : 0.f) + (swa ? c3[xx] * inv : 0.f);
+    store4(o + (size_t)bh * D + 4 * cg, out);
   }
 }
 
@@ -440,23 +432,10 @@ __global__ __launch_bounds__(256) void cache_fill_kernel(
 template <class T, bool GLA, int D>
 hipError_t launch_decode_t(const DecodeArgs& p, hipStream_t s) {
   const int G = p.H / p.Hkv;
-  if (p.flags & 2) {
-    const size_t lds = decode_lds_bytes(G, p.n_sink + p.window, D, GLA, (int)sizeof(T));
-    if (lds > 64 * 1024) {
-      hipError_t e = hipFuncSetAttribute((const void*)decode_swa_kernel<T, D>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL((decode_swa_kernel<T, D>), dim3(p.B * p.Hkv), dim3(kSwaThreads), lds, s,
-                       (const T*)p.q, (const T*)p.k, (const T*)p.v, (const T*)p.k_cache,
-                       (const T*)p.v_cache, p.pos, (T*)p.o, p.B, p.H, p.Hkv, p.n_sink, p.window);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL((decode_state_kernel<T, GLA, D>), dim3(p.B * p.H), dim3(kStateThreads), 0, s,
-                     (const T*)p.q, p.a, p.b, p.state, (const T*)p.k_cache, (const T*)p.v_cache,
-                     p.a_cache, p.b_cache, p.pos, (T*)p.o, p.B, p.H, p.Hkv, p.n_sink, p.window,
-                     p.flags);
+  hipLaunchKernelGGL((decode_step_kernel<T, GLA, D>), dim3(xcd_grouped_grid((long long)p.B * p.Hkv, G)),
+                     dim3(kStepThreads), 0, s, (const T*)p.q, (const T*)p.k, (const T*)p.v, p.a,
+                     p.b, p.state, (const T*)p.k_cache, (const T*)p.v_cache, p.a_cache, p.b_cache,
+                     p.pos, (T*)p.o, p.B, p.H, p.Hkv, p.n_sink, p.window, p.flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_commit_kernel<T, GLA>), dim3(p.B), dim3(256), 0, s, (const T*)p.k,
@@ -474,11 +453,14 @@ hipError_t launch_decode_d(const DecodeArgs& p, hipStream_t s) {
 }  // namespace
 
 size_t decode_lds_bytes(int G, int N, int D, int gla, int elt) {
-  (void)gla;
-  const size_t floats = (size_t)G * D + 2 * (size_t)D + (size_t)G * N;
-  const size_t ints = 0;
-  const size_t staging = 2 * (size_t)kSlotChunk * (D + 16 / elt) * elt;   // K and V rows of the I/O type
-  return floats * sizeof(float) + ints * sizeof(int) + 16 + staging;
+  (void)G;
+  (void)N;
+  const size_t rows = 128 / (size_t)elt;                           // staged cache rows
+  const size_t tiles = 2 * rows * (size_t)D * (size_t)elt;          // K and V
+  const size_t vunits = 3 * (size_t)D * elt / 16 + (gla ? (size_t)D / 4 : 0);
+  const size_t vecs = (vunits + 63) / 64 * 64 * 16;                 // q, k_e, v_e (, a_e)
+  const size_t floats = rows + 64 + 4 + (kStepThreads / 64 + 1) * ((size_t)D / 4) * 12;
+  return tiles + vecs + floats * sizeof(float);
 }
 
 hipError_t launch_decode(const DecodeArgs& p, hipStream_t s) {
