@@ -179,14 +179,18 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(6,
   }
   asm volatile("" ::: "memory");
 
-  // ---- the head's state, streamed once
+  // ---- the head's state, streamed once; its loads and stores are marked
+  // non-temporal (a step's state is far larger than the caches and is not
+  // touched again within the step), which leaves the caches to the rows
+  // the heads of a group share
   const int cg = tid % M::CG;
   const int rg = tid / M::CG;
   float* Sg = state + (size_t)bh * D * D;
   f32x4 s[M::R];
 #pragma unroll
   for (int r = 0; r < M::R; ++r)
-    s[r] = *reinterpret_cast<const f32x4*>(Sg + (size_t)(rg + M::RG * r) * D + 4 * cg);
+    s[r] = __builtin_nontemporal_load(
+        reinterpret_cast<const f32x4*>(Sg + (size_t)(rg + M::RG * r) * D + 4 * cg));
 
   wait_vmcnt<M::R>();   // every load before the state's has landed (the staged rows)
   lds_barrier();
@@ -328,7 +332,7 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(6,
     }
 #pragma unroll
     for (int r = 0; r < M::R; ++r)
-      *reinterpret_cast<f32x4*>(Sg + (size_t)(rg + M::RG * r) * D + 4 * cg) = s[r];
+      __builtin_nontemporal_store(s[r], reinterpret_cast<f32x4*>(Sg + (size_t)(rg + M::RG * r) * D + 4 * cg));
   } else {
 #pragma unroll
     for (int xx = 0; xx < 4; ++xx) olin[xx] = c2[xx];
