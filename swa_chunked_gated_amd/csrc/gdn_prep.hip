@@ -22,8 +22,15 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(
     float* __restrict__ wut, float* __restrict__ wg, int T_, int H, int Hkv, int n_sink,
     int window, int nch) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  // the G query heads of one (chunk, KV head) run on one XCD and share the
+  // chunk's K rows through its L2; y is the sequence
+  const int G = H / Hkv;
+  int unit, member;
+  if (!xcd_grouped(blockIdx.x, G, nch * Hkv, unit, member)) return;
+  const int c = unit % nch;
+  const int h = (unit / nch) * G + member;
   prep::gdn_prep_chunk<T, D, FULL>(q, k, v, a, b, wtb, wtbg, wwm, wktg, wa, wut, wg, T_, H, Hkv,
-                                   n_sink, window, nch, blockIdx.x, blockIdx.y, blockIdx.z, smem_raw);
+                                   n_sink, window, nch, c, h, blockIdx.y, smem_raw);
 }
 
 template <class T, int D, bool FULL>
@@ -33,7 +40,8 @@ hipError_t launch_prep_t(const PrefillArgs& p, int nch, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, SM::bytes);
   if (e != hipSuccess) return e;
   const GdnWorkspace w = gdn_workspace_layout(p.workspace, p.B, p.H, nch, D, sizeof(T), FULL);
-  hipLaunchKernelGGL(kern, dim3(nch, p.H, p.B), dim3(64), SM::bytes, s, (const T*)p.q,
+  const dim3 grid(xcd_grouped_grid((long long)nch * p.Hkv, p.H / p.Hkv), p.B);
+  hipLaunchKernelGGL(kern, grid, dim3(64), SM::bytes, s, (const T*)p.q,
                      (const T*)p.k, (const T*)p.v, p.a, p.b, (T*)w.tb, (T*)w.tbg, (T*)w.wm,
                      (T*)w.ktg, (T*)w.a, w.ut, w.g, p.T, p.H, p.Hkv, p.n_sink, p.window, nch);
   return hipGetLastError();

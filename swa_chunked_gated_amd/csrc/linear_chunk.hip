@@ -120,11 +120,16 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
   T* TBGs = sT + SM::oTBG;
   float* gate = reinterpret_cast<float*>(smem_raw + SM::bytesT);   // GDN: g[64], gam[64]; GLA: 2^{G_C}[D]
 
-  const int sp = blockIdx.x;          // column slice
-  const int h = blockIdx.y;
-  const int bi = blockIdx.z;
+  // the G query heads of a KV head and their column slices run on one XCD,
+  // so the K and V rows they all read come from HBM once per group
+  constexpr int NSP = D / DVS;        // column slices per chain
   const int G = H / Hkv;
-  const int g = h / G;
+  int unit, member;
+  if (!xcd_grouped(blockIdx.x, G * NSP, Hkv, unit, member)) return;
+  const int sp = member % NSP;        // column slice
+  const int g = unit;
+  const int bi = blockIdx.y;
+  const int h = g * G + member / NSP;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = wave_id();
@@ -571,7 +576,10 @@ hipError_t launch_linear_t(const PrefillArgs& p, hipStream_t s) {
   auto kern = linear_chunk_kernel<T, D, NW, DW, GLA>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, SM::bytes);
   if (e != hipSuccess) return e;
-  const dim3 grid(D / SM::DVS, p.H, p.B);
+  // x: the (column slice, query head) members of each KV head, placed by
+  // xcd_grouped (a multiple of 8 wide, so the XCD of a workgroup is x mod 8
+  // in every row); y: the sequence
+  const dim3 grid(xcd_grouped_grid(p.Hkv, (D / SM::DVS) * (p.H / p.Hkv)), p.B);
   const int nch = gdn_stream_chunks(p.T, p.n_sink, p.window);
   const T* w0;
   const T* w1;
