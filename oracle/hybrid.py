@@ -56,7 +56,8 @@ exact retrieval with orthonormal keys; equality with full causal softmax
 (torch SDPA, fp64) when T <= budget; an fp64 chunked (WY/UT) form for several
 chunk sizes; the GLA diagonal-product form; prefill + decode == longer
 prefill; GQA == explicitly repeated K/V; torch conv1d for the short conv;
-RoPE closed forms and invariants.  No function here is "parity unpinned"
+RoPE closed forms and invariants; short-conv decode steps from a prefill's
+history == the longer prefill's rows.  No function here is "parity unpinned"
 against the mathematics; none is pinned by printed values, since the pages
 print no worked example.
 """
@@ -80,6 +81,8 @@ __all__ = [
     "causal_depthwise_conv",
     "l2norm",
     "shortconv_qkv",
+    "shortconv_state_from_prefill",
+    "shortconv_decode_step",
 ]
 
 BRANCH_LINEAR = 1
@@ -432,3 +435,74 @@ def shortconv_qkv(q, k, v, wq, wk, wv, rope_theta: float, pos0: int = 0,
         q = l2norm(q)
         k = l2norm(k)
     return q, k, v
+
+
+# --------------------------------------------------------------------------
+# Q/K/V preparation in decode (the same operation as shortconv_qkv, taken one
+# token at a time): each sequence keeps the inputs of its last ks - 1 tokens
+# after RoPE and before the convolution; token i sits at ring index
+# i mod (ks - 1).  Tokens before the sequence start count as zero.
+# --------------------------------------------------------------------------
+
+def _rope_row(x, pos: int, theta: float):
+    """Rotate-half RoPE of one token's heads x [heads, d] at position pos."""
+    x = np.asarray(x, np.float64)
+    half = x.shape[-1] // 2
+    ang = pos * theta ** (-2.0 * np.arange(half) / x.shape[-1])
+    c, s = np.cos(ang), np.sin(ang)
+    return np.concatenate([x[:, :half] * c - x[:, half:] * s, x[:, half:] * c + x[:, :half] * s], axis=-1)
+
+
+def shortconv_state_from_prefill(q, k, v, ksize: int, rope_theta: float, pos0: int = 0,
+                                 flags: int = 3):
+    """History after a prefill of T tokens (positions pos0 .. pos0+T-1), so that
+    decoding continues with token T: for q, k, v the inputs of tokens
+    T-ks+1 .. T-1 (rotated for q and k when flags & 1), each at ring index
+    i mod (ks-1).  Returns three fp64 arrays [B, ks-1, heads*d]."""
+    out = []
+    for x, rot in ((q, True), (k, True), (v, False)):
+        x = np.asarray(x, np.float64)
+        B, T, nh, d = x.shape
+        hist = np.zeros((B, max(ksize - 1, 0), nh * d))
+        for i in range(T - (ksize - 1), T):
+            if i < 0:
+                continue
+            for b in range(B):
+                xi = _rope_row(x[b, i], pos0 + i, rope_theta) if (rot and flags & 1) else x[b, i]
+                hist[b, i % (ksize - 1)] = xi.reshape(-1)
+        out.append(hist)
+    return tuple(out)
+
+
+def shortconv_decode_step(q, k, v, wq, wk, wv, hist_q, hist_k, hist_v, pos, rope_theta: float,
+                          pos0: int = 0, flags: int = 3):
+    """One new token per sequence: q [B,H,d], k, v [B,Hkv,d] (raw projections),
+    pos [B] the token's index in its sequence.  RoPE at position pos0 + pos
+    (flags & 1, q and k), causal depthwise conv over the token and its ks-1
+    predecessors from the history (y = sum_j w[c, ks-1-j] x[t-j]), L2 norm
+    (flags & 2, q and k).  The histories [B, ks-1, C] are updated in place
+    (the new input replaces token t-ks+1 at ring index t mod (ks-1)).
+    Returns (q_out, k_out, v_out) in fp64."""
+    outs = []
+    for x, w, hist, rot in ((q, wq, hist_q, True), (k, wk, hist_k, True), (v, wv, hist_v, False)):
+        x = np.asarray(x, np.float64)
+        w = np.asarray(w, np.float64)
+        B, nh, d = x.shape
+        ks = w.shape[1]
+        y = np.zeros((B, nh * d))
+        for b in range(B):
+            t = int(pos[b])
+            xt = _rope_row(x[b], pos0 + t, rope_theta) if (rot and flags & 1) else x[b]
+            xt = xt.reshape(-1)
+            acc = w[:, ks - 1] * xt
+            for j in range(1, ks):
+                if t - j >= 0:
+                    acc = acc + w[:, ks - 1 - j] * hist[b, (t - j) % (ks - 1)]
+            if ks > 1:
+                hist[b, t % (ks - 1)] = xt
+            y[b] = acc
+        y = y.reshape(B, nh, d)
+        if rot and flags & 2:
+            y = l2norm(y)
+        outs.append(y)
+    return tuple(outs)

@@ -422,3 +422,41 @@ def test_shortconv_pipeline_order_and_norm():
     w_delay[:, 6] = 1.0
     qo, _, _ = O.shortconv_qkv(q, k, v, w_delay, wk, wv, 100.0, 0, flags=1)
     np.testing.assert_allclose(qo[:, 1:], O.rope(q, 100.0)[:, :-1], atol=1e-14)
+
+
+@pytest.mark.parametrize("ks", [1, 2, 8])
+@pytest.mark.parametrize("T0", [0, 1, 6, 7, 8, 13])
+def test_shortconv_decode_steps_equal_prefill_rows(ks, T0):
+    # Decode keeps the last ks-1 rotated inputs in a ring; stepping tokens
+    # T0 .. T-1 from the history of a T0-token prefill must give the rows of
+    # the T-token prefill (itself pinned to torch conv1d), including the zero
+    # history before the sequence start and the RoPE position offset pos0.
+    B, T, H, Hkv, d, pos0 = 2, 20, 4, 2, 8, 5
+    q = RNG.standard_normal((B, T, H, d))
+    k = RNG.standard_normal((B, T, Hkv, d))
+    v = RNG.standard_normal((B, T, Hkv, d))
+    wq = RNG.standard_normal((H * d, ks))
+    wk = RNG.standard_normal((Hkv * d, ks))
+    wv = RNG.standard_normal((Hkv * d, ks))
+    for flags in (0, 1, 3):
+        ref = O.shortconv_qkv(q, k, v, wq, wk, wv, 1e4, pos0, flags=flags)
+        hq, hk, hv = O.shortconv_state_from_prefill(q[:, :T0], k[:, :T0], v[:, :T0], ks, 1e4, pos0, flags)
+        assert hq.shape == (B, ks - 1, H * d) and hk.shape == (B, ks - 1, Hkv * d)
+        for t in range(T0, T):
+            out = O.shortconv_decode_step(q[:, t], k[:, t], v[:, t], wq, wk, wv, hq, hk, hv,
+                                          np.full(B, t), 1e4, pos0, flags)
+            for x, r in zip(out, ref):
+                np.testing.assert_allclose(x, r[:, t], rtol=0, atol=1e-12)
+
+
+def test_shortconv_history_holds_rotated_inputs_at_ring_slots():
+    # The history after a prefill is the rotated (pre-conv) input of the last
+    # ks-1 tokens, token i at ring index i mod (ks-1): check against RoPE of the
+    # whole sequence, and that earlier tokens leave no trace.
+    B, T, H, d, ks, pos0 = 1, 11, 2, 8, 8, 3
+    x = RNG.standard_normal((B, T, H, d))
+    hq, _, hv = O.shortconv_state_from_prefill(x, x, x, ks, 50.0, pos0, flags=1)
+    rot = O.rope(x, 50.0, pos0)
+    for i in range(T - ks + 1, T):
+        np.testing.assert_allclose(hq[0, i % (ks - 1)], rot[0, i].reshape(-1), atol=1e-14)
+        np.testing.assert_array_equal(hv[0, i % (ks - 1)], x[0, i].reshape(-1))
