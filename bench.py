@@ -12,8 +12,9 @@ adding its branch) is timed too, for reference.  Inputs are resident in HBM
 before the timed region.
 
 Secondary figures in "also": decode steps/s (B=256, 1000 consecutive steps),
-long-context prefill (B=8, T=32768, budget 128, final state out) and the
-Qwen3-32B-shaped full stack (short conv + GDN, short conv + GLA, budget 896).
+long-context prefill (B=8, T=32768, budget 128, final state out), the
+Qwen3-32B-shaped full stack (short conv + GDN, short conv + GLA, budget 896)
+and its serving step (short-conv decode feeding the layer's decode step).
 
 Roofline: algorithmic FLOPs (or bytes) per launch of the dominant kernel
 divided by its mean event-timed duration, against the MI355X peaks (bf16
@@ -302,6 +303,61 @@ def bench_decode(steps=1000, warmup=10):
     }
 
 
+def shortconv_decode_bytes(w, elt=2):
+    """One short-conv decode step: raw q, k, v in and prepared out, the conv
+    weights, the ks-1 history rows read and one row written (fp32)."""
+    C = (w.H + 2 * w.Hkv) * w.d
+    ks = w.conv_ks
+    return w.B * C * elt * 2 + C * ks * 4 + w.B * C * 4 * ks
+
+
+def bench_qwen_decode(steps=200, warmup=10):
+    """Serving step of the Qwen-shaped stack after its T=8192 prefill: the
+    short-conv decode of the new raw q, k, v feeding the layer's decode step
+    (budget 896), both on one stream; timed over consecutive steps."""
+    import swa_chunked_gated_amd as gl
+    from workloads import WORKLOADS, make_decode_inputs
+
+    w = WORKLOADS["qwen32b_decode"]
+    inp = make_decode_inputs(w, device="cuda", steps=steps)
+    keys = ("state", "k_cache", "v_cache", "a_cache", "b_cache", "pos", "hist_q", "hist_k", "hist_v")
+    o = torch.empty(w.B, w.H, w.d, dtype=torch.bfloat16, device="cuda")
+    conv = tuple(torch.empty_like(inp[x][0]) for x in ("q", "k", "v"))
+
+    def run(st, s):
+        qc, kc, vc = gl.shortconv_decode(inp["q"][s], inp["k"][s], inp["v"][s], inp["wq"], inp["wk"],
+                                         inp["wv"], st["hist_q"], st["hist_k"], st["hist_v"], st["pos"],
+                                         w.rope_theta, 0, gl.ROPE | gl.L2NORM, out=conv)
+        gl.hybrid_decode(qc, kc, vc, inp["a"][s], inp["b"][s], st["state"], st["k_cache"],
+                         st["v_cache"], st["a_cache"], st["b_cache"], st["pos"], w.n_sink, w.window,
+                         o=o)
+
+    scratch = {x: inp[x].clone() for x in keys}
+    for s in range(warmup):
+        run(scratch, s)
+    del scratch
+    st = {x: inp[x].clone() for x in keys}
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for s in range(steps):
+        run(st, s)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    ev_ms = e0.elapsed_time(e1) / steps
+    byts = decode_bytes(w) + shortconv_decode_bytes(w)
+    return {
+        "workload": "qwen32b_decode (B=2, H=64, Hkv=8, d=128, cache 8+888, short conv k=8, t=8192..)",
+        "steps": steps, "ms_per_step": sec * 1e3, "steps_per_s": 1.0 / sec,
+        "tokens_per_s": w.B / sec, "event_ms_per_step": ev_ms,
+        "kernels": "shortconv_decode_kernel + decode_step_kernel + decode_commit_kernel",
+        "bound": "launch latency (8.4 MB of state per step)",
+        "hbm_frac": byts / (ev_ms * 1e-3) / PEAK_HBM, "algorithmic_bytes_per_step": byts,
+    }
+
+
 def bench_copy(mib=1024, reps=3):
     """A plain device copy of known size: the reference the HBM byte counters
     (FETCH_SIZE, WRITE_SIZE) are scaled by, and the practical read+write roof."""
@@ -368,7 +424,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default="all",
-                    choices=["all", "main", "decode", "longctx", "qwen32b", "copy"])
+                    choices=["all", "main", "decode", "longctx", "qwen32b", "qwen32b_decode", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-split", action="store_true",
                     help="skip the two-launch reference timing of the headline layer (profiling runs)")
@@ -384,6 +440,9 @@ def main():
 
     if args.only == "decode":
         print(json.dumps(bench_decode(steps=args.steps, warmup=args.warmup)), flush=True)
+        return
+    if args.only == "qwen32b_decode":
+        print(json.dumps(bench_qwen_decode(steps=args.steps, warmup=args.warmup)), flush=True)
         return
     if args.only == "copy":
         print(json.dumps(bench_copy()), flush=True)
@@ -403,6 +462,7 @@ def main():
         also["longctx_b8_t32768"] = bench_prefill_cfg("longctx_b8_t32768")
         also["qwen32b_t8192_gdn"] = bench_prefill_cfg("qwen32b_t8192_gdn")
         also["qwen32b_t8192_gla"] = bench_prefill_cfg("qwen32b_t8192_gla")
+        also["qwen32b_decode"] = bench_qwen_decode()
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(m["inputs"], w)

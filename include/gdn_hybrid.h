@@ -239,6 +239,57 @@ int shortconv_qkv(const void* q, const void* k, const void* v,
                   float rope_theta, int pos0, int flags, int dtype,
                   void* stream);
 
+/*
+ * Short-conv history for decoding after a prefill ([P1] 实践建议 item 3: the
+ * short convolution of shortconv_qkv, continued one token at a time).  For
+ * q, k and v it holds the inputs of the last ksize - 1 tokens after RoPE
+ * (q and k, flags & GDN_ROPE) and before the convolution, in fp32; token i
+ * sits at ring index i mod (ksize - 1).  This call writes the history after
+ * a prefill of T tokens at positions pos0 .. pos0 + T - 1, so that decoding
+ * continues with token T; ring slots of tokens before 0 are zeroed.
+ *
+ *   q [B, T, H, d], k, v [B, T, Hkv, d]   dtype: the raw projections that
+ *              were given to shortconv_qkv (may be NULL when T = 0)
+ *   hist_q [B, ksize-1, H*d], hist_k, hist_v [B, ksize-1, Hkv*d] fp32, out
+ *              (caller-owned; channel c = h * d + i)
+ * ksize = 1 keeps no history: nothing is written and the history pointers
+ * may be NULL.  Supported: d in {64, 128}; 1 <= ksize <= 8; B <= 65535;
+ * rope_theta > 0 when RoPE is on; pos0 >= 0.
+ */
+int shortconv_history_from_prefill(const void* q, const void* k, const void* v,
+                                   float* hist_q, float* hist_k, float* hist_v,
+                                   int B, int T, int H, int Hkv, int d, int ksize,
+                                   float rope_theta, int pos0, int flags, int dtype,
+                                   void* stream);
+
+/*
+ * One decode step of the Q/K/V preparation: shortconv_qkv evaluated at one
+ * new token per sequence.  Sequence b's token has index t = pos[b] in its
+ * sequence and RoPE position pos0 + t.  pos is only read: call this before
+ * gdn_hybrid_decode of the same step (which advances pos) and feed it the
+ * outputs.  The token's input after RoPE is convolved with the history of
+ * its ksize - 1 predecessors (zero before the sequence start), q and k are
+ * L2-normalised (flags & GDN_L2NORM), and the input replaces token
+ * t - ksize + 1 at ring index t mod (ksize - 1) of the history.
+ *
+ *   q, q_out   [B, H, d]      dtype (raw projection in, prepared out)
+ *   k, v, k_out, v_out [B, Hkv, d] dtype
+ *   wq, wk, wv as in shortconv_qkv
+ *   hist_q, hist_k, hist_v  as in shortconv_history_from_prefill, in/out
+ *              (a fresh sequence starts from zeros; may be NULL for ksize 1)
+ *   pos        [B] int32 >= 0, read only
+ * Supported: d in {64, 128}; 1 <= ksize <= 8; B <= 65535; rope_theta > 0
+ * when RoPE is on; 0 <= pos0 < 2^30.
+ */
+int shortconv_qkv_decode(const void* q, const void* k, const void* v,
+                         const float* wq, const float* wk, const float* wv,
+                         float* hist_q, float* hist_k, float* hist_v,
+                         const int* pos,
+                         void* q_out, void* k_out, void* v_out,
+                         int B, int H, int Hkv, int d, int ksize,
+                         float rope_theta, int pos0, int flags, int dtype,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

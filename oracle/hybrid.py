@@ -81,7 +81,7 @@ __all__ = [
     "causal_depthwise_conv",
     "l2norm",
     "shortconv_qkv",
-    "shortconv_state_from_prefill",
+    "shortconv_history_from_prefill",
     "shortconv_decode_step",
 ]
 
@@ -453,7 +453,7 @@ def _rope_row(x, pos: int, theta: float):
     return np.concatenate([x[:, :half] * c - x[:, half:] * s, x[:, half:] * c + x[:, :half] * s], axis=-1)
 
 
-def shortconv_state_from_prefill(q, k, v, ksize: int, rope_theta: float, pos0: int = 0,
+def shortconv_history_from_prefill(q, k, v, ksize: int, rope_theta: float, pos0: int = 0,
                                  flags: int = 3):
     """History after a prefill of T tokens (positions pos0 .. pos0+T-1), so that
     decoding continues with token T: for q, k, v the inputs of tokens

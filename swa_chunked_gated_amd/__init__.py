@@ -188,3 +188,47 @@ def shortconv_qkv(q, k, v, wq, wk, wv, rope_theta: float = 1e6, pos0: int = 0,
                            B, T, H, Hkv, d, ks, float(rope_theta), pos0, flags, dt, _stream(q))
     _lib.check("shortconv_qkv", rc)
     return qo, ko, vo
+
+
+def shortconv_history_from_prefill(q, k, v, ksize: int, rope_theta: float = 1e6, pos0: int = 0,
+                                   flags: int = ROPE | L2NORM):
+    """History of the short conv after a prefill of the raw q [B,T,H,d],
+    k/v [B,T,Hkv,d]: fp32 [B, ksize-1, heads*d] for q, k, v (rotated inputs of
+    the last ksize-1 tokens at ring index i mod (ksize-1))."""
+    B, T, H, d = q.shape
+    Hkv = k.shape[2]
+    dt = _io_dtype(q, k, v)
+    m = max(ksize - 1, 0)
+    hist = (torch.empty(B, m, H * d, dtype=torch.float32, device=q.device),
+            torch.empty(B, m, Hkv * d, dtype=torch.float32, device=q.device),
+            torch.empty(B, m, Hkv * d, dtype=torch.float32, device=q.device))
+    lib = _lib.load()
+    rc = lib.shortconv_history_from_prefill(_p(q), _p(k), _p(v), _p(hist[0]), _p(hist[1]), _p(hist[2]),
+                                            B, T, H, Hkv, d, ksize, float(rope_theta), pos0, flags, dt,
+                                            _stream(q))
+    _lib.check("shortconv_history_from_prefill", rc)
+    return hist
+
+
+def shortconv_decode(q, k, v, wq, wk, wv, hist_q, hist_k, hist_v, pos, rope_theta: float = 1e6,
+                     pos0: int = 0, flags: int = ROPE | L2NORM, out=None):
+    """One short-conv decode step: q [B,H,d], k/v [B,Hkv,d] raw projections of
+    the new tokens at sequence indices pos [B] (int32, read only); updates the
+    histories in place; returns (q_out, k_out, v_out)."""
+    B, H, d = q.shape
+    Hkv = k.shape[1]
+    ks = wq.shape[1]
+    dt = _io_dtype(q, k, v)
+    _f32(wq, wk, wv, hist_q, hist_k, hist_v)
+    if pos.dtype != torch.int32 or not pos.is_contiguous():
+        raise TypeError("pos must be a contiguous int32 tensor")
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    qo, ko, vo = out
+    lib = _lib.load()
+    rc = lib.shortconv_qkv_decode(_p(q), _p(k), _p(v), _p(wq), _p(wk), _p(wv), _p(hist_q), _p(hist_k),
+                                  _p(hist_v), _p(pos), _p(qo), _p(ko), _p(vo), B, H, Hkv, d, ks,
+                                  float(rope_theta), pos0, flags, dt, _stream(q))
+    _lib.check("shortconv_qkv_decode", rc)
+    return qo, ko, vo
+

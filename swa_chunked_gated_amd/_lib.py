@@ -29,6 +29,10 @@ SIGNATURES = {
         _c_int, [_ptr] * 8 + [_c_int] * 10 + [_ptr]),
     "shortconv_qkv": (
         _c_int, [_ptr] * 9 + [_c_int] * 6 + [ctypes.c_float, _c_int, _c_int, _c_int, _ptr]),
+    "shortconv_history_from_prefill": (
+        _c_int, [_ptr] * 6 + [_c_int] * 6 + [ctypes.c_float, _c_int, _c_int, _c_int, _ptr]),
+    "shortconv_qkv_decode": (
+        _c_int, [_ptr] * 13 + [_c_int] * 5 + [ctypes.c_float, _c_int, _c_int, _c_int, _ptr]),
 }
 
 _lib = None

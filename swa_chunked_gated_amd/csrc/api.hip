@@ -182,4 +182,45 @@ int shortconv_qkv(const void* q, const void* k, const void* v, const float* wq, 
   return launched(gdn::launch_shortconv(p, (hipStream_t)stream));
 }
 
+int shortconv_history_from_prefill(const void* q, const void* k, const void* v, float* hist_q,
+                                   float* hist_k, float* hist_v, int B, int T, int H, int Hkv, int d,
+                                   int ksize, float rope_theta, int pos0, int flags, int dtype,
+                                   void* stream) {
+  if (!dims_ok(B, T, H, Hkv, d, d, 0, 1, dtype, GDN_DELTA)) return GDN_EINVAL;
+  if (ksize < 1 || ksize > 8) return GDN_EUNSUPPORTED;
+  if (flags < 0 || flags > 3) return GDN_EINVAL;
+  if ((flags & GDN_ROPE) && !(rope_theta > 0.f)) return GDN_EINVAL;
+  if (pos0 < 0 || (int64_t)pos0 + T >= (int64_t)1 << 30) return GDN_EINVAL;
+  if (B > 65535) return GDN_EUNSUPPORTED;   // the sequence is a grid dimension
+  if (ksize == 1) return GDN_OK;   // no history to keep
+  if (!hist_q || !hist_k || !hist_v) return GDN_EINVAL;
+  if (T > 0 && (!q || !k || !v)) return GDN_EINVAL;
+  if (!aligned16({q, k, v, hist_q, hist_k, hist_v})) return GDN_EINVAL;
+  gdn::ShortConvArgs p{q, k, v, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, B, T, H, Hkv,
+                       d, ksize, rope_theta, pos0, flags, dtype == GDN_BF16};
+  float* const hist[3] = {hist_q, hist_k, hist_v};
+  return launched(gdn::launch_shortconv_history(p, hist, (hipStream_t)stream));
+}
+
+int shortconv_qkv_decode(const void* q, const void* k, const void* v, const float* wq,
+                         const float* wk, const float* wv, float* hist_q, float* hist_k,
+                         float* hist_v, const int* pos, void* q_out, void* k_out, void* v_out, int B,
+                         int H, int Hkv, int d, int ksize, float rope_theta, int pos0, int flags,
+                         int dtype, void* stream) {
+  if (!dims_ok(B, 1, H, Hkv, d, d, 0, 1, dtype, GDN_DELTA)) return GDN_EINVAL;
+  if (!q || !k || !v || !wq || !wk || !wv || !pos || !q_out || !k_out || !v_out) return GDN_EINVAL;
+  if (ksize < 1 || ksize > 8) return GDN_EUNSUPPORTED;
+  if (ksize > 1 && (!hist_q || !hist_k || !hist_v)) return GDN_EINVAL;
+  if (B > 65535) return GDN_EUNSUPPORTED;   // the sequence is a grid dimension
+  if (flags < 0 || flags > 3) return GDN_EINVAL;
+  if ((flags & GDN_ROPE) && !(rope_theta > 0.f)) return GDN_EINVAL;
+  if (pos0 < 0 || pos0 >= 1 << 30) return GDN_EINVAL;
+  if (!aligned16({q, k, v, wq, wk, wv, hist_q, hist_k, hist_v, pos, q_out, k_out, v_out}))
+    return GDN_EINVAL;
+  gdn::ShortConvArgs p{q, k, v, wq, wk, wv, q_out, k_out, v_out, B, 1, H, Hkv, d, ksize,
+                       rope_theta, pos0, flags, dtype == GDN_BF16};
+  float* const hist[3] = {hist_q, hist_k, hist_v};
+  return launched(gdn::launch_shortconv_decode(p, hist, pos, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -135,6 +135,11 @@ hipError_t launch_zero_head_rows(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_cache_from_prefill(const CacheArgs& a, hipStream_t s);
 hipError_t launch_shortconv(const ShortConvArgs& a, hipStream_t s);
+// Short-conv decode step (a.T unused; pos [B] on the device) and the history
+// after a prefill of a.T tokens; hist = {q, k, v} histories [B][ks-1][C] fp32.
+hipError_t launch_shortconv_decode(const ShortConvArgs& a, float* const hist[3], const int* pos,
+                                   hipStream_t s);
+hipError_t launch_shortconv_history(const ShortConvArgs& a, float* const hist[3], hipStream_t s);
 
 // Dynamic LDS bytes the decode kernel needs (the front end checks the limit).
 size_t decode_lds_bytes(int G, int N, int D, int gla, int elt);

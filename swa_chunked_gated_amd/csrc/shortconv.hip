@@ -15,6 +15,9 @@
 // leave registers; the tile re-reads a 7-token causal halo.  The rotation
 // angle is set in fp64 at the tile start and then advanced one token at a
 // time by a fixed complex rotation (error grows ~1e-7 per token).
+//
+// Decode (one new token per sequence) keeps a short history per sequence;
+// see the decode section below.
 
 #include <math.h>
 
@@ -135,7 +138,176 @@ hipError_t launch_all(const ShortConvArgs& p, hipStream_t s) {
   return launch_one<T, D>(p.v, p.wv, p.v_out, p, p.Hkv, 0, 0, s);
 }
 
+// ------------------------------------------------------------------ decode
+//
+// Decode keeps, per sequence and tensor, the inputs of the last ks - 1 tokens
+// after RoPE and before the convolution (fp32, so a decode step convolves the
+// same values the prefill kernel keeps in registers); token i sits at ring
+// index i mod (ks - 1) of hist [B][ks-1][channels].
+
+// RoPE factors of pair j at absolute position `apos`: the angle in fp64,
+// reduced to [-pi, pi] before the fp32 cos / sin.
+template <int D>
+__device__ __forceinline__ void rope_cs(int j, long long apos, float theta, float& cs, float& sn) {
+  const double f = exp(-(2.0 * j / D) * log((double)theta));
+  const double ang = (double)apos * f;
+  const double twopi = 6.283185307179586476925;
+  const double red = ang - twopi * rint(ang / twopi);
+  cs = (float)cos(red);
+  sn = (float)sin(red);
+}
+
+// The three tensors of one call (q, k, v), selected by blockIdx.z.
+struct ConvTensor {
+  const void* x;      // raw inputs
+  const float* w;     // [nh * D, ks]
+  float* hist;        // [B][ks-1][nh * D]
+  void* y;            // decode outputs
+  int nh, rope, norm;
+};
+struct ConvSet {
+  ConvTensor t[3];
+};
+
+// One decode step: one wave per (sequence, 64 / (D/2) heads), lane j owning
+// the RoPE pair (j, j + D/2) of its head as in the prefill kernel.  Each
+// thread reads and then rewrites only its own two channels of the history.
+template <class T, int D>
+__global__ __launch_bounds__(256) void shortconv_decode_kernel(ConvSet set, const int* __restrict__ pos,
+                                                               int ks, float theta, int pos0) {
+  constexpr int LPH = D / 2;
+  constexpr int HW = 64 / LPH;
+  const ConvTensor tt = set.t[blockIdx.z];
+  const int lane = threadIdx.x & 63;
+  const int h = (blockIdx.x * 4 + (threadIdx.x >> 6)) * HW + lane / LPH;
+  if (h >= tt.nh) return;              // whole head groups leave together
+  const int j = lane % LPH;
+  const int bi = blockIdx.y;
+  const int t = pos[bi];
+  if (t < 0) return;                   // outside the contract (pos >= 0)
+  const int C = tt.nh * D;
+  const int c1 = h * D + j;
+  const int c2 = c1 + LPH;
+  const T* x = reinterpret_cast<const T*>(tt.x) + (size_t)bi * C;
+  float x1 = to_f32(x[c1]);
+  float x2 = to_f32(x[c2]);
+  if (tt.rope) {
+    float cs, sn;
+    rope_cs<D>(j, (long long)pos0 + t, theta, cs, sn);
+    const float r1 = x1 * cs - x2 * sn;
+    const float r2 = x2 * cs + x1 * sn;
+    x1 = r1;
+    x2 = r2;
+  }
+  const float* w = tt.w;
+  float y1 = w[(size_t)c1 * ks + ks - 1] * x1;
+  float y2 = w[(size_t)c2 * ks + ks - 1] * x2;
+  if (ks > 1) {
+    const int m = ks - 1;
+    float* hb = tt.hist + (size_t)bi * m * C;
+    for (int jj = 1; jj < ks; ++jj) {
+      if (t - jj < 0) break;           // zero history before the sequence start
+      const float* hr = hb + (size_t)((t - jj) % m) * C;
+      y1 += w[(size_t)c1 * ks + ks - 1 - jj] * hr[c1];
+      y2 += w[(size_t)c2 * ks + ks - 1 - jj] * hr[c2];
+    }
+    float* hw = hb + (size_t)(t % m) * C;   // token t - ks + 1 leaves the ring
+    hw[c1] = x1;
+    hw[c2] = x2;
+  }
+  if (tt.norm) {
+    float ss = y1 * y1 + y2 * y2;
+#pragma unroll
+    for (int mm = 1; mm < LPH; mm <<= 1) ss += shfl_xor(ss, mm);
+    const float inv = 1.0f / sqrtf(ss + 1e-6f);
+    y1 *= inv;
+    y2 *= inv;
+  }
+  T* y = reinterpret_cast<T*>(tt.y) + (size_t)bi * C;
+  y[c1] = from_f32<T>(y1);
+  y[c2] = from_f32<T>(y2);
+}
+
+// History after a prefill of T_ tokens: ring slot r holds token
+// i = T_ - 1 - ((T_ - 1 - r) mod (ks - 1)), rotated at position pos0 + i, or
+// zero when i < 0.  One thread per (pair, head); grid x = 3 * pair blocks
+// (the tensor is blockIdx.x mod 3), y = ring slot, z = sequence.
+template <class T, int D>
+__global__ __launch_bounds__(256) void shortconv_history_kernel(ConvSet set, int T_, int ks, float theta,
+                                                                int pos0) {
+  constexpr int LPH = D / 2;
+  const ConvTensor tt = set.t[blockIdx.x % 3];
+  const int idx = (blockIdx.x / 3) * 256 + threadIdx.x;
+  if (idx >= tt.nh * LPH) return;
+  const int h = idx / LPH;
+  const int j = idx % LPH;
+  const int r = blockIdx.y;
+  const int bi = blockIdx.z;
+  const int m = ks - 1;
+  const int C = tt.nh * D;
+  const int c1 = h * D + j;
+  const int c2 = c1 + LPH;
+  const int i = T_ - 1 - (((T_ - 1 - r) % m) + m) % m;
+  float x1 = 0.f, x2 = 0.f;
+  if (i >= 0) {
+    const T* x = reinterpret_cast<const T*>(tt.x) + ((size_t)bi * T_ + i) * C;
+    x1 = to_f32(x[c1]);
+    x2 = to_f32(x[c2]);
+    if (tt.rope) {
+      float cs, sn;
+      rope_cs<D>(j, (long long)pos0 + i, theta, cs, sn);
+      const float r1 = x1 * cs - x2 * sn;
+      const float r2 = x2 * cs + x1 * sn;
+      x1 = r1;
+      x2 = r2;
+    }
+  }
+  float* hr = tt.hist + ((size_t)bi * m + r) * C;
+  hr[c1] = x1;
+  hr[c2] = x2;
+}
+
+ConvSet conv_set(const ShortConvArgs& p, float* const hist[3]) {
+  const int rope = p.flags & 1;
+  const int norm = (p.flags >> 1) & 1;
+  ConvSet set;
+  set.t[0] = ConvTensor{p.q, p.wq, hist[0], p.q_out, p.H, rope, norm};
+  set.t[1] = ConvTensor{p.k, p.wk, hist[1], p.k_out, p.Hkv, rope, norm};
+  set.t[2] = ConvTensor{p.v, p.wv, hist[2], p.v_out, p.Hkv, 0, 0};
+  return set;
+}
+
+template <class T, int D>
+hipError_t launch_decode_t(const ShortConvArgs& p, float* const hist[3], const int* pos, hipStream_t s) {
+  constexpr int HW = 128 / D;
+  const int units = (p.H + HW - 1) / HW;   // q has the most heads
+  const dim3 grid((units + 3) / 4, p.B, 3);
+  hipLaunchKernelGGL((shortconv_decode_kernel<T, D>), grid, dim3(256), 0, s, conv_set(p, hist), pos,
+                     p.ksize, p.rope_theta, p.pos0);
+  return hipGetLastError();
+}
+
+template <class T, int D>
+hipError_t launch_history_t(const ShortConvArgs& p, float* const hist[3], hipStream_t s) {
+  const int pairs = p.H * (D / 2);   // q has the most heads
+  const dim3 grid(3 * ((pairs + 255) / 256), p.ksize - 1, p.B);
+  hipLaunchKernelGGL((shortconv_history_kernel<T, D>), grid, dim3(256), 0, s, conv_set(p, hist), p.T,
+                     p.ksize, p.rope_theta, p.pos0);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_shortconv_decode(const ShortConvArgs& p, float* const hist[3], const int* pos,
+                                   hipStream_t s) {
+  if (p.bf16) return p.D == 64 ? launch_decode_t<bf16, 64>(p, hist, pos, s) : launch_decode_t<bf16, 128>(p, hist, pos, s);
+  return p.D == 64 ? launch_decode_t<float, 64>(p, hist, pos, s) : launch_decode_t<float, 128>(p, hist, pos, s);
+}
+
+hipError_t launch_shortconv_history(const ShortConvArgs& p, float* const hist[3], hipStream_t s) {
+  if (p.bf16) return p.D == 64 ? launch_history_t<bf16, 64>(p, hist, s) : launch_history_t<bf16, 128>(p, hist, s);
+  return p.D == 64 ? launch_history_t<float, 64>(p, hist, s) : launch_history_t<float, 128>(p, hist, s);
+}
 
 hipError_t launch_shortconv(const ShortConvArgs& p, hipStream_t s) {
   if (p.bf16) return p.D == 64 ? launch_all<bf16, 64>(p, s) : launch_all<bf16, 128>(p, s);

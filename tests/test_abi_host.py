@@ -36,7 +36,8 @@ def lib():
 
 def test_header_declares_expected_entry_points():
     names = declared_functions()
-    for n in ("gdn_hybrid_prefill", "gdn_hybrid_decode", "shortconv_qkv",
+    for n in ("gdn_hybrid_prefill", "gdn_hybrid_decode", "shortconv_qkv", "shortconv_qkv_decode",
+              "shortconv_history_from_prefill",
               "gdn_hybrid_cache_from_prefill", "gdn_hybrid_prefill_workspace"):
         assert n in names
 
@@ -211,3 +212,49 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError, match="not built"):
         _lib.load()
+
+
+def test_shortconv_decode_validation(lib):
+    f = lib.shortconv_qkv_decode
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, wq=FAKE, wk=FAKE, wv=FAKE, hq=FAKE, hk=FAKE, hv=FAKE,
+                 pos=FAKE, qo=FAKE, ko=FAKE, vo=FAKE, B=1, H=4, Hkv=2, d=64, ks=8, theta=1e6,
+                 pos0=0, flags=3, dt=BF16)
+        a.update(kw)
+        return f(a["q"], a["k"], a["v"], a["wq"], a["wk"], a["wv"], a["hq"], a["hk"], a["hv"],
+                 a["pos"], a["qo"], a["ko"], a["vo"], a["B"], a["H"], a["Hkv"], a["d"], a["ks"],
+                 a["theta"], a["pos0"], a["flags"], a["dt"], None)
+
+    for name in ("q", "k", "v", "wq", "wk", "wv", "pos", "qo", "ko", "vo", "hq", "hk", "hv"):
+        assert call(**{name: None}) == EINVAL, name
+    assert call(ks=0) == EUNSUP
+    assert call(ks=9) == EUNSUP
+    assert call(d=96) == EINVAL
+    assert call(H=3) == EINVAL
+    assert call(theta=0.0) == EINVAL
+    assert call(flags=4) == EINVAL
+    assert call(pos0=-1) == EINVAL
+    assert call(B=65536) == EUNSUP
+    assert call(q=ctypes.c_void_p(0x1004)) == EINVAL                # not 16-byte aligned
+
+
+def test_shortconv_history_validation(lib):
+    f = lib.shortconv_history_from_prefill
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, hq=FAKE, hk=FAKE, hv=FAKE, B=1, T=16, H=4, Hkv=2, d=64,
+                 ks=8, theta=1e6, pos0=0, flags=3, dt=BF16)
+        a.update(kw)
+        return f(a["q"], a["k"], a["v"], a["hq"], a["hk"], a["hv"], a["B"], a["T"], a["H"],
+                 a["Hkv"], a["d"], a["ks"], a["theta"], a["pos0"], a["flags"], a["dt"], None)
+
+    assert call(ks=1, hq=None, hk=None, hv=None) == OK             # no history: nothing launched
+    assert call(ks=9) == EUNSUP
+    for name in ("hq", "hk", "hv", "q", "k", "v"):
+        assert call(**{name: None}) == EINVAL, name
+    assert call(T=-1) == EINVAL
+    assert call(theta=-1.0) == EINVAL
+    assert call(pos0=-1) == EINVAL
+    assert call(B=65536) == EUNSUP
+    assert call(hq=ctypes.c_void_p(0x1008)) == EINVAL

@@ -271,6 +271,128 @@ def test_qwen32b_full_stack_sampled():
             assert heads[0] // G == g
 
 
+# -------------------------------------------------------- short-conv decode
+
+def assert_hist_close(got, ref, what):
+    # histories are fp32 copies of rotated inputs: fp32 rounding of RoPE only
+    got = f64(got)
+    err = np.max(np.abs(got - ref)) if got.size else 0.0
+    assert err <= 1e-5 * max(np.max(np.abs(ref)) if ref.size else 0.0, 1.0), f"{what}: {err:.3e}"
+
+
+@pytest.mark.parametrize("dtype,d,ks,T0,flags,pos0", [
+    ("bf16", 128, 8, 0, 3, 0), ("bf16", 128, 8, 5, 3, 0), ("bf16", 128, 8, 100, 3, 7),
+    ("f32", 64, 8, 7, 3, 0), ("f32", 64, 4, 2, 1, 3), ("f32", 128, 1, 10, 3, 0),
+    ("bf16", 64, 2, 9, 0, 0), ("f32", 128, 8, 300, 2, 1000)])
+def test_shortconv_decode_steps(dtype, d, ks, T0, flags, pos0):
+    """History after a prefill, then decode steps, for sequences at different
+    positions: against the oracle's decode stepper, the oracle's prefill rows
+    and the GPU prefill kernel's rows."""
+    n = 10
+    T0s = [T0, T0 + 3, max(T0 - 2, 0)]
+    w = small(T=max(T0s) + n, d=d, dtype=dtype, shortconv=True, conv_ks=ks, H=4, Hkv=2, B=3)
+    inp = to_dev(make_prefill_inputs(w, seed=11 + T0))
+    theta = 1e4
+    fp32 = dtype == "f32"
+    m = ks - 1
+    hist = [torch.zeros(w.B, m, nh * d, dtype=torch.float32, device=DEV) for nh in (w.H, w.Hkv, w.Hkv)]
+    ref_hist = [np.zeros((w.B, m, nh * d)) for nh in (w.H, w.Hkv, w.Hkv)]
+    for bi, t0 in enumerate(T0s):
+        sl = slice(bi, bi + 1)
+        hb = gl.shortconv_history_from_prefill(*(inp[x][sl, :t0].contiguous() for x in "qkv"), ks,
+                                               theta, pos0, flags)
+        rb = O.shortconv_history_from_prefill(*(f64(inp[x][sl, :t0]) for x in "qkv"), ks, theta,
+                                              pos0, flags)
+        for j in range(3):
+            hist[j][sl] = hb[j]
+            ref_hist[j][sl] = rb[j]
+    torch.cuda.synchronize()
+    for j, name in enumerate("qkv"):
+        assert_hist_close(hist[j], ref_hist[j], f"history {name}")
+    ref_pre = O.shortconv_qkv(*(f64(inp[x]) for x in ("q", "k", "v", "wq", "wk", "wv")), theta,
+                              pos0, flags=flags)
+    gpu_pre = gl.shortconv_qkv(inp["q"], inp["k"], inp["v"], inp["wq"], inp["wk"], inp["wv"],
+                               rope_theta=theta, pos0=pos0, flags=flags)
+    pos = torch.tensor(T0s, dtype=torch.int32, device=DEV)
+    for s in range(n):
+        ts = [t0 + s for t0 in T0s]
+        idx = torch.tensor(ts, device=DEV)
+        bsel = torch.arange(w.B, device=DEV)
+        step = {x: inp[x][bsel, idx].contiguous() for x in "qkv"}
+        out = gl.shortconv_decode(step["q"], step["k"], step["v"], inp["wq"], inp["wk"], inp["wv"],
+                                  *hist, pos, theta, pos0, flags)
+        torch.cuda.synchronize()
+        ro = O.shortconv_decode_step(*(f64(step[x]) for x in "qkv"),
+                                     *(f64(inp[x]) for x in ("wq", "wk", "wv")), *ref_hist,
+                                     pos.cpu().numpy(), theta, pos0, flags)
+        for j, name in enumerate("qkv"):
+            rows_ref = ref_pre[j][np.arange(w.B), ts]
+            assert_close(f64(out[j]), ro[j], fp32, f"{name} step {s} vs oracle step")
+            assert_close(f64(out[j]), rows_ref, fp32, f"{name} step {s} vs oracle prefill")
+            assert_close(f64(out[j]), f64(gpu_pre[j][bsel, idx]), fp32, f"{name} step {s} vs GPU prefill")
+        pos += 1
+    for j, name in enumerate("qkv"):
+        assert_hist_close(hist[j], ref_hist[j], f"history {name} after the steps")
+
+
+@pytest.mark.parametrize("name", ["qwen32b_t8192_gdn", "qwen32b_t8192_gla"])
+def test_qwen32b_full_stack_decode(name):
+    """Serving path of the Qwen-shaped stack: short-conv + layer prefill of T0
+    tokens, then steps of short-conv decode feeding the layer's decode step
+    (budget 896).  Each stage is checked against the oracle on sampled heads:
+    the decode conv rows against the oracle conv of the raw inputs, the layer
+    rows against the oracle layer on the GPU's conv outputs."""
+    base = WORKLOADS[name]
+    T0, n = 900, 4
+    w = Workload(name, B=2, H=base.H, Hkv=base.Hkv, d=base.d, n_sink=base.n_sink,
+                 window=base.window, T=T0 + n, sigma=base.sigma, update=base.update,
+                 shortconv=True, rope_theta=base.rope_theta)
+    raw = to_dev(make_prefill_inputs(w, seed=5))
+    pre = {x: raw[x][:, :T0].contiguous() for x in ("q", "k", "v", "a", "b")}
+    qc, kc, vc = gl.shortconv_qkv(pre["q"], pre["k"], pre["v"], raw["wq"], raw["wk"], raw["wv"],
+                                  rope_theta=w.rope_theta, pos0=0, flags=gl.ROPE | gl.L2NORM)
+    _, state = gl.hybrid_prefill(qc, kc, vc, pre["a"], pre["b"], w.n_sink, w.window,
+                                 update=w.update, flags=gl.WRITE_STATE)
+    kca, vca, aca, bca = gl.cache_from_prefill(kc, vc, pre["a"], pre["b"], w.H, w.n_sink, w.window,
+                                               update=w.update)
+    hist = gl.shortconv_history_from_prefill(pre["q"], pre["k"], pre["v"], w.conv_ks, w.rope_theta,
+                                             0, gl.ROPE | gl.L2NORM)
+    pos = torch.full((w.B,), T0, dtype=torch.int32, device=DEV)
+    conv_rows = {x: [] for x in "qkv"}
+    outs = []
+    for t in range(T0, T0 + n):
+        step = {x: raw[x][:, t].contiguous() for x in ("q", "k", "v", "a", "b")}
+        sq, sk, sv = gl.shortconv_decode(step["q"], step["k"], step["v"], raw["wq"], raw["wk"],
+                                         raw["wv"], *hist, pos, w.rope_theta, 0, gl.ROPE | gl.L2NORM)
+        o = gl.hybrid_decode(sq, sk, sv, step["a"], step["b"], state, kca, vca, aca, bca, pos,
+                             w.n_sink, w.window, update=w.update)
+        for x, y in zip("qkv", (sq, sk, sv)):
+            conv_rows[x].append(y)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.all(pos == T0 + n)
+    G = w.H // w.Hkv
+    full = {x: torch.cat([c, torch.stack(conv_rows[x], dim=1)], dim=1)
+            for x, c in zip("qkv", (qc, kc, vc))}
+    full.update(a=raw["a"], b=raw["b"])
+    o_dec = torch.stack(outs, dim=1)                     # [B, n, H, d]
+    rows = list(range(T0, T0 + n))
+    for bsel, heads, g in (([0], [0, 3], 0), ([1], [61], 7)):
+        cq = slice(heads[0], heads[-1] + 1)
+        rq, rk, rv = O.shortconv_qkv(
+            f64(raw["q"][bsel][:, :, cq]), f64(raw["k"][bsel][:, :, g:g + 1]),
+            f64(raw["v"][bsel][:, :, g:g + 1]),
+            f64(raw["wq"].view(w.H, w.d, -1)[cq].reshape(-1, w.conv_ks)),
+            f64(raw["wk"].view(w.Hkv, w.d, -1)[g]), f64(raw["wv"].view(w.Hkv, w.d, -1)[g]),
+            w.rope_theta, 0, flags=3)
+        assert_close(f64(full["q"][bsel][:, rows][:, :, cq]), rq[:, rows], False, "decode conv q")
+        assert_close(f64(full["k"][bsel][:, rows][:, :, g:g + 1]), rk[:, rows], False, "decode conv k")
+        assert_close(f64(full["v"][bsel][:, rows][:, :, g:g + 1]), rv[:, rows], False, "decode conv v")
+        ref, _ = oracle_subset(full, w, bsel, heads, rows=rows)
+        assert_close(f64(o_dec[bsel][:, :, heads]), ref[:, rows], False, f"{name} decode o")
+        assert heads[-1] // G == g
+
+
 # ------------------------------------------------------------------ decode
 
 def run_decode(step_inp, st, w, flags=ALL):

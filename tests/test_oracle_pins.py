@@ -440,7 +440,7 @@ def test_shortconv_decode_steps_equal_prefill_rows(ks, T0):
     wv = RNG.standard_normal((Hkv * d, ks))
     for flags in (0, 1, 3):
         ref = O.shortconv_qkv(q, k, v, wq, wk, wv, 1e4, pos0, flags=flags)
-        hq, hk, hv = O.shortconv_state_from_prefill(q[:, :T0], k[:, :T0], v[:, :T0], ks, 1e4, pos0, flags)
+        hq, hk, hv = O.shortconv_history_from_prefill(q[:, :T0], k[:, :T0], v[:, :T0], ks, 1e4, pos0, flags)
         assert hq.shape == (B, ks - 1, H * d) and hk.shape == (B, ks - 1, Hkv * d)
         for t in range(T0, T):
             out = O.shortconv_decode_step(q[:, t], k[:, t], v[:, t], wq, wk, wv, hq, hk, hv,
@@ -455,7 +455,7 @@ def test_shortconv_history_holds_rotated_inputs_at_ring_slots():
     # whole sequence, and that earlier tokens leave no trace.
     B, T, H, d, ks, pos0 = 1, 11, 2, 8, 8, 3
     x = RNG.standard_normal((B, T, H, d))
-    hq, _, hv = O.shortconv_state_from_prefill(x, x, x, ks, 50.0, pos0, flags=1)
+    hq, _, hv = O.shortconv_history_from_prefill(x, x, x, ks, 50.0, pos0, flags=1)
     rot = O.rope(x, 50.0, pos0)
     for i in range(T - ks + 1, T):
         np.testing.assert_allclose(hq[0, i % (ks - 1)], rot[0, i].reshape(-1), atol=1e-14)

@@ -81,6 +81,10 @@ WORKLOADS = {
     "qwen32b_t8192_gla": Workload("qwen32b_t8192_gla", B=2, H=64, Hkv=8, d=128,
                                   n_sink=8, window=888, T=8192, sigma=0.5,
                                   shortconv=True, update="gla"),
+    # Serving the Qwen-shaped stack: decode steps after the T=8192 prefill
+    # (short-conv decode feeding the layer's decode step), budget 896.
+    "qwen32b_decode": Workload("qwen32b_decode", B=2, H=64, Hkv=8, d=128, n_sink=8,
+                               window=888, sigma=0.5, shortconv=True, pos0=8192, steps=200),
 }
 
 
@@ -144,7 +148,10 @@ def make_decode_inputs(w: Workload, device="cpu", seed: int = 0, steps: int | No
     Returns state [B,H,d,d] fp32 ~ N(0, state_var); k_cache/v_cache
     [B,Hkv,N,d]; a_cache/b_cache [B,W,H] (GLA a: [B,W,H,d]); pos [B] int32;
     and per-step q [S,B,H,d], k/v [S,B,Hkv,d], a [S,B,H] (GLA [S,B,H,d]),
-    b [S,B,H].
+    b [S,B,H].  For the short-conv stack the per-step q, k are the raw
+    (un-normalised) projections, and conv weights wq [H*d,ks], wk/wv
+    [Hkv*d,ks] ~ N(0, 1/ks) and fp32 histories hist_q [B,ks-1,H*d],
+    hist_k/hist_v [B,ks-1,Hkv*d] ~ N(0, 1) are added (drawn last).
     """
     steps = w.steps if steps is None else steps
     B = w.B if B is None else B
@@ -155,24 +162,37 @@ def make_decode_inputs(w: Workload, device="cpu", seed: int = 0, steps: int | No
     mu = _unit(torch.randn(Hkv, d, **f32))
 
     def keys(*lead):
-        return _unit(mu.view(*([1] * len(lead[:-1])), Hkv, d)
-                     + w.sigma * torch.randn(*lead, d, **f32))
+        x = mu.view(*([1] * len(lead[:-1])), Hkv, d) + w.sigma * torch.randn(*lead, d, **f32)
+        return x if raw else _unit(x)
 
     def gate_a(*shape):
         return torch.exp(-torch.nn.functional.softplus(torch.randn(*shape, **f32) + w.gate_mean))
 
+    raw = False
     state = torch.randn(B, H, d, d, **f32) * math.sqrt(w.state_var)
     k_cache = keys(B, N, Hkv).permute(0, 2, 1, 3).to(dt).contiguous()
+    raw = w.shortconv          # the cache holds prepared keys; new tokens arrive raw
     v_cache = torch.randn(B, Hkv, N, d, **f32).to(dt).contiguous()
     a_shape = (B, W, H, d) if w.update == "gla" else (B, W, H)
     a_cache = gate_a(*a_shape).contiguous()
     b_cache = torch.sigmoid(torch.randn(B, W, H, **f32)).contiguous()
     pos = torch.full((B,), w.pos0, dtype=torch.int32, device=device)
-    q = _unit(torch.randn(steps, B, H, d, **f32)).to(dt).contiguous()
+    q = torch.randn(steps, B, H, d, **f32)
+    q = (q if raw else _unit(q)).to(dt).contiguous()
     k = keys(steps, B, Hkv).to(dt).contiguous()
     v = torch.randn(steps, B, Hkv, d, **f32).to(dt).contiguous()
     a_step_shape = (steps, B, H, d) if w.update == "gla" else (steps, B, H)
     a = gate_a(*a_step_shape).contiguous()
     b = torch.sigmoid(torch.randn(steps, B, H, **f32)).contiguous()
-    return dict(state=state, k_cache=k_cache, v_cache=v_cache, a_cache=a_cache,
-                b_cache=b_cache, pos=pos, q=q, k=k, v=v, a=a, b=b)
+    out = dict(state=state, k_cache=k_cache, v_cache=v_cache, a_cache=a_cache,
+               b_cache=b_cache, pos=pos, q=q, k=k, v=v, a=a, b=b)
+    if w.shortconv:
+        ks = w.conv_ks
+        std = 1.0 / math.sqrt(ks)
+        out["wq"] = torch.randn(H * d, ks, **f32) * std
+        out["wk"] = torch.randn(Hkv * d, ks, **f32) * std
+        out["wv"] = torch.randn(Hkv * d, ks, **f32) * std
+        out["hist_q"] = torch.randn(B, ks - 1, H * d, **f32)
+        out["hist_k"] = torch.randn(B, ks - 1, Hkv * d, **f32)
+        out["hist_v"] = torch.randn(B, ks - 1, Hkv * d, **f32)
+    return out
