@@ -57,13 +57,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
 }
 
-template <class T, int D>
+template <class T, int D, int MR>
 struct StepMap {
   static constexpr int CG = D / 4;                 // column groups of 4 floats
   static constexpr int RG = kStepThreads / CG;     // row groups
   static constexpr int R = D / RG;                 // state rows per thread
   static constexpr int NWV = kStepThreads / 64;    // waves
-  static constexpr int ROWS = 128 / sizeof(T);     // cache rows staged per pass
+  static constexpr int ROWS = MR * 128 / sizeof(T);   // cache rows staged per pass
   static constexpr int UPR = D * sizeof(T) / 16;   // 16-byte units per cache row
   static constexpr int UPT = ROWS * UPR / kStepThreads;   // staged units per thread
   static constexpr int LPS = kStepThreads / ROWS;  // lanes per row in the logits
@@ -90,15 +90,18 @@ __device__ __forceinline__ f32x4 raw4_f32(const f32x4& x) { return x; }
 // (one read, one write).  The softmax over the staged rows runs while the
 // state is still arriving.  Workgroups are placed so that the G query heads
 // of a KV head run together on one XCD: each cached row comes from HBM once
-// and from that XCD's L2 for the other heads.  o is written once.
-template <class T, bool GLA, int D>
-__global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(6, 8))) void decode_step_kernel(
+// and from that XCD's L2 for the other heads.  o is written once.  MR scales
+// the rows staged per pass (MR * 128 bytes of each of K and V per head
+// dimension): 1 for budgets that fit one pass, 4 for long budgets, whose
+// serial passes (one staging round trip each) would otherwise dominate.
+template <class T, bool GLA, int D, int MR>
+__device__ __forceinline__ void decode_step_body(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ a, const float* __restrict__ b, float* __restrict__ state,
     const T* __restrict__ kc, const T* __restrict__ vc, const float* __restrict__ ac,
     const float* __restrict__ bc, const int* __restrict__ pos, T* __restrict__ o, int B, int H,
     int Hkv, int n_sink, int window, int flags) {
-  using M = StepMap<T, D>;
+  using M = StepMap<T, D, MR>;
   typedef typename Vec16<T>::type V16;
   typedef typename Raw4<T>::type R4;
   constexpr int VLOAD = 3 * M::UPR + (GLA ? D / 4 : 0);   // 16-byte units of the per-step vectors
@@ -236,10 +239,16 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(6,
       }
       lds_barrier();
       // running maximum and denominator (every wave keeps its own copy)
-      const float lj = lane < M::ROWS ? lg[lane] : -INFINITY;
-      const float mn = fmaxf(mx, wave_max(lj));
+      float cm = -INFINITY;
+      for (int r = lane; r < M::ROWS; r += 64) cm = fmaxf(cm, lg[r]);
+      const float mn = fmaxf(mx, wave_max(cm));
       const float sc = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - mn);
-      den = den * sc + wave_sum(lj == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lj - mn));
+      float ps = 0.f;
+      for (int r = lane; r < M::ROWS; r += 64) {
+        const float l = lg[r];
+        ps += l == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(l - mn);
+      }
+      den = den * sc + wave_sum(ps);
       mx = mn;
 #pragma unroll
       for (int xx = 0; xx < 4; ++xx) p3[xx] *= sc;
@@ -347,6 +356,32 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(6,
   }
 }
 
+#define GDN_DECODE_STEP_PARAMS                                                                  \
+  const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,                       \
+      const float *__restrict__ a, const float *__restrict__ b, float *__restrict__ state,         \
+      const T *__restrict__ kc, const T *__restrict__ vc, const float *__restrict__ ac,             \
+      const float *__restrict__ bc, const int *__restrict__ pos, T *__restrict__ o, int B, int H,   \
+      int Hkv, int n_sink, int window, int flags
+#define GDN_DECODE_STEP_ARGS q, k, v, a, b, state, kc, vc, ac, bc, pos, o, B, H, Hkv, n_sink, window, flags
+
+// One staged pass (48 KB of LDS): three workgroups per CU, so at most 80
+// VGPRs.
+template <class T, bool GLA, int D>
+__global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(6, 8))) void decode_step_kernel(
+    GDN_DECODE_STEP_PARAMS) {
+  decode_step_body<T, GLA, D, 1>(GDN_DECODE_STEP_ARGS);
+}
+
+// Long budgets: four times the rows per pass (145 KB of LDS, one workgroup
+// per CU).
+template <class T, bool GLA, int D>
+__global__ __launch_bounds__(kStepThreads) void decode_step_wide_kernel(GDN_DECODE_STEP_PARAMS) {
+  decode_step_body<T, GLA, D, 4>(GDN_DECODE_STEP_ARGS);
+}
+
+#undef GDN_DECODE_STEP_PARAMS
+#undef GDN_DECODE_STEP_ARGS
+
 // After every head has read the evicted entry: store the new token in its
 // slot (and its gates at its ring index) and advance pos.  One workgroup per
 // sequence.
@@ -436,10 +471,14 @@ __global__ __launch_bounds__(256) void cache_fill_kernel(
 template <class T, bool GLA, int D>
 hipError_t launch_decode_t(const DecodeArgs& p, hipStream_t s) {
   const int G = p.H / p.Hkv;
-  hipLaunchKernelGGL((decode_step_kernel<T, GLA, D>), dim3(xcd_grouped_grid((long long)p.B * p.Hkv, G)),
-                     dim3(kStepThreads), 0, s, (const T*)p.q, (const T*)p.k, (const T*)p.v, p.a,
-                     p.b, p.state, (const T*)p.k_cache, (const T*)p.v_cache, p.a_cache, p.b_cache,
-                     p.pos, (T*)p.o, p.B, p.H, p.Hkv, p.n_sink, p.window, p.flags);
+  const dim3 grid(xcd_grouped_grid((long long)p.B * p.Hkv, G));
+  // one pass of 128 / sizeof(T) rows holds the whole budget: the narrow kernel
+  auto kern = p.n_sink + p.window <= (int)(128 / sizeof(T)) ? decode_step_kernel<T, GLA, D>
+                                                             : decode_step_wide_kernel<T, GLA, D>;
+  hipLaunchKernelGGL(kern, grid, dim3(kStepThreads), 0, s, (const T*)p.q, (const T*)p.k,
+                     (const T*)p.v, p.a, p.b, p.state, (const T*)p.k_cache, (const T*)p.v_cache,
+                     p.a_cache, p.b_cache, p.pos, (T*)p.o, p.B, p.H, p.Hkv, p.n_sink, p.window,
+                     p.flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_commit_kernel<T, GLA>), dim3(p.B), dim3(256), 0, s, (const T*)p.k,
@@ -458,8 +497,7 @@ hipError_t launch_decode_d(const DecodeArgs& p, hipStream_t s) {
 
 size_t decode_lds_bytes(int G, int N, int D, int gla, int elt) {
   (void)G;
-  (void)N;
-  const size_t rows = 128 / (size_t)elt;                           // staged cache rows
+  const size_t rows = (N <= 128 / elt ? 1 : 4) * 128 / (size_t)elt;   // staged cache rows
   const size_t tiles = 2 * rows * (size_t)D * (size_t)elt;          // K and V
   const size_t vunits = 3 * (size_t)D * elt / 16 + (gla ? (size_t)D / 4 : 0);
   const size_t vecs = (vunits + 63) / 64 * 64 * 16;                 // q, k_e, v_e (, a_e)

@@ -432,6 +432,33 @@ def test_decode_steps_small(update, pos0):
             assert np.array_equal(f64(st["b_cache"]), ref["b_cache"])
 
 
+@pytest.mark.parametrize("dtype,n_sink,window,pos0,update", [
+    ("f32", 3, 61, 62, "gdn"), ("bf16", 8, 592, 5, "gdn"), ("bf16", 8, 592, 598, "gla"),
+    ("bf16", 0, 300, 1000, "gdn"), ("f32", 8, 120, 130, "gla"), ("bf16", 8, 888, 4000, "gdn")])
+def test_decode_long_budgets(dtype, n_sink, window, pos0, update):
+    """Budgets that take several staged passes of cached rows (online softmax
+    across passes, a partial last pass), against the oracle's decode step."""
+    w = Workload("decl", B=2, H=8, Hkv=2, d=128 if dtype == "bf16" else 64, n_sink=n_sink,
+                 window=window, update=update, pos0=pos0, steps=3, dtype=dtype)
+    inp = make_decode_inputs(w, device=DEV, seed=pos0 + window)
+    st = {k: inp[k].clone() for k in ("state", "k_cache", "v_cache", "a_cache", "b_cache", "pos")}
+    ref = {k: f64(st[k]) for k in st}
+    ref["pos"] = st["pos"].cpu().numpy().astype(np.int64)
+    fp32 = dtype == "f32"
+    for s in range(w.steps):
+        step = {k: inp[k][s] for k in ("q", "k", "v", "a", "b")}
+        o = run_decode(step, st, w)
+        ro, ref["state"], ref["k_cache"], ref["v_cache"], ref["a_cache"], ref["b_cache"], ref["pos"] = \
+            O.decode_step(f64(step["q"]), f64(step["k"]), f64(step["v"]), f64(step["a"]),
+                          f64(step["b"]), ref["state"], ref["k_cache"], ref["v_cache"],
+                          ref["a_cache"], ref["b_cache"], ref["pos"], w.n_sink, w.window,
+                          update=update)
+        assert_close(f64(o), ro, fp32, f"o step {s}")
+        assert_close(f64(st["state"]), ref["state"], fp32, f"state step {s}")
+        assert np.array_equal(f64(st["k_cache"]), ref["k_cache"])
+        assert np.array_equal(f64(st["v_cache"]), ref["v_cache"])
+
+
 def test_decode_b256_sampled_sequences():
     w = WORKLOADS["decode_b256"]
     inp = make_decode_inputs(w, device=DEV, steps=3)
