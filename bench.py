@@ -352,7 +352,7 @@ def bench_qwen_decode(steps=200, warmup=10):
         "workload": "qwen32b_decode (B=2, H=64, Hkv=8, d=128, cache 8+888, short conv k=8, t=8192..)",
         "steps": steps, "ms_per_step": sec * 1e3, "steps_per_s": 1.0 / sec,
         "tokens_per_s": w.B / sec, "event_ms_per_step": ev_ms,
-        "kernels": "shortconv_decode_kernel + decode_step_kernel + decode_commit_kernel",
+        "kernels": "shortconv_decode_kernel + decode_step_wide_kernel + decode_commit_kernel",
         "bound": "launch latency (8.4 MB of state per step)",
         "hbm_frac": byts / (ev_ms * 1e-3) / PEAK_HBM, "algorithmic_bytes_per_step": byts,
     }
