@@ -205,6 +205,34 @@ int gdn_hybrid_decode(const void* q, const void* k, const void* v,
                       void* stream);
 
 /*
+ * Inference-time hybridisation ([P3] 关键设计 (1): the two branches' weights
+ * set their contributions at inference): gdn_hybrid_prefill and
+ * gdn_hybrid_decode with o = w_lin * o_lin + w_swa * o_swa on the selected
+ * branches (GDN_ACCUMULATE: o += that).  Weights (1, 1) are the plain sum the
+ * calls above compute; (1, 0) and (0, 1) give what the single-branch flags
+ * give.  Arguments, layouts and return codes as in those calls; non-finite
+ * weights are GDN_EINVAL.
+ */
+int gdn_hybrid_prefill_weighted(const void* q, const void* k, const void* v,
+                                const float* a, const float* b,
+                                void* o, float* state_out,
+                                int B, int T, int H, int Hkv, int dk, int dv,
+                                int n_sink, int window, int dtype, int update, int flags,
+                                float w_lin, float w_swa,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+int gdn_hybrid_decode_weighted(const void* q, const void* k, const void* v,
+                               const float* a, const float* b,
+                               float* state,
+                               void* k_cache, void* v_cache,
+                               float* a_cache, float* b_cache,
+                               int* pos, void* o,
+                               int B, int H, int Hkv, int dk, int dv,
+                               int n_sink, int window, int dtype, int update, int flags,
+                               float w_lin, float w_swa,
+                               void* stream);
+
+/*
  * Fill the decode cache after a prefill of T tokens, so decoding resumes at
  * position T: sinks 0..min(n_sink,T)-1 and window tokens
  * max(n_sink, T-window)..T-1 go to their slots (layouts as in

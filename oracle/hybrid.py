@@ -42,7 +42,8 @@ the design notes of the repository):
 * Linear set of query t:   L(t) = { i : n_sink <= i <= t - window }, i.e. the
   recurrence runs over evicted non-sink tokens and is queried with lag
   ``window``: o_lin,t = S^(t-window)^T q_t, and 0 while t - window < n_sink.
-* Layer output: o = o_lin + o_swa (plain sum).
+* Layer output: o = o_lin + o_swa (plain sum); with branch weights
+  (inference-time hybridisation, P3 关键设计 (1)) o = w_lin o_lin + w_swa o_swa.
 * Grouped-query attention: query head h uses KV head h // (H // Hkv); gates
   and the state are per query head.
 * Short conv: causal, depthwise, zero history, no bias, no activation; tap
@@ -215,8 +216,11 @@ def swa_branch(q, k, v, n_sink: int, window: int, rows=None):
 # --------------------------------------------------------------------------
 
 def hybrid_prefill(q, k, v, a, b, n_sink: int, window: int, update: str = "gdn",
-                   flags: int = BRANCH_LINEAR | BRANCH_SOFTMAX | WRITE_STATE):
-    """o = o_lin + o_swa for a whole sequence starting at position 0.
+                   flags: int = BRANCH_LINEAR | BRANCH_SOFTMAX | WRITE_STATE,
+                   w_lin: float = 1.0, w_swa: float = 1.0):
+    """o = w_lin o_lin + w_swa o_swa for a whole sequence starting at
+    position 0; the weights (P3, 关键设计 (1): inference-time hybridisation
+    sets the branches' contributions by weights) default to the plain sum.
 
     ``update`` is "gdn" (a, b: [B,T,H]) or "gla" (a: [B,T,H,dk], b unused).
     Returns (o [B,T,H,dv], final state [B,H,dk,dv] or None).
@@ -234,9 +238,9 @@ def hybrid_prefill(q, k, v, a, b, n_sink: int, window: int, update: str = "gdn",
         else:
             raise ValueError(update)
         if flags & BRANCH_LINEAR:
-            o = o + o_lin
+            o = o + w_lin * o_lin
     if flags & BRANCH_SOFTMAX:
-        o = o + swa_branch(q, k, v, n_sink, window)
+        o = o + w_swa * swa_branch(q, k, v, n_sink, window)
     return o, (S if flags & WRITE_STATE else None)
 
 
@@ -284,8 +288,10 @@ def cache_from_prefill(k, v, a, b, n_sink: int, window: int, update: str = "gdn"
 
 def decode_step(q, k, v, a, b, state, k_cache, v_cache, a_cache, b_cache, pos,
                 n_sink: int, window: int, update: str = "gdn",
-                flags: int = BRANCH_LINEAR | BRANCH_SOFTMAX):
+                flags: int = BRANCH_LINEAR | BRANCH_SOFTMAX, w_lin: float = 1.0,
+                w_swa: float = 1.0):
     """One decode step for every sequence; returns new copies of everything.
+    The output is w_lin o_lin + w_swa o_swa (weights as in hybrid_prefill).
 
     q [B,H,dk]; k [B,Hkv,dk]; v [B,Hkv,dv]; a [B,H] (GLA: [B,H,dk]); b [B,H];
     state [B,H,dk,dv]; caches as in ``cache_from_prefill``; pos [B] = index t
@@ -357,9 +363,9 @@ def decode_step(q, k, v, a, b, state, k_cache, v_cache, a_cache, b_cache, pos,
         o_swa = np.einsum("hn,nhd->hd", p, vals)
         out = np.zeros((H, dv))
         if flags & BRANCH_LINEAR:
-            out = out + o_lin
+            out = out + w_lin * o_lin
         if flags & BRANCH_SOFTMAX:
-            out = out + o_swa
+            out = out + w_swa * o_swa
         o[bi] = out
         # 4. store the new token
         s_t = cache_slot(t, n_sink, window)

@@ -81,8 +81,11 @@ def prefill_workspace_bytes(B: int, T: int, H: int, Hkv: int, d: int, n_sink: in
 
 def hybrid_prefill(q, k, v, a, b, n_sink: int, window: int, update: str = "gdn",
                    flags: int = BRANCH_LINEAR | BRANCH_SOFTMAX, o=None, state_out=None,
-                   workspace=None):
+                   workspace=None, weights=None):
     """Layer output for whole sequences starting at position 0.
+
+    ``weights=(w_lin, w_swa)`` gives o = w_lin o_lin + w_swa o_swa (the
+    weighted entry point); omitted, the plain sum.
 
     q [B,T,H,d], k/v [B,T,Hkv,d] (fp32 or bf16); a [B,T,H] (GLA: [B,T,H,d])
     and b [B,T,H] fp32.  Returns (o [B,T,H,d], state [B,H,d,d] fp32 or None).
@@ -111,17 +114,27 @@ def hybrid_prefill(q, k, v, a, b, n_sink: int, window: int, update: str = "gdn",
     if need.value > 0 and workspace is None:
         workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = lib.gdn_hybrid_prefill(_p(q), _p(k), _p(v), _p(a), _p(b), _p(o), _p(state_out),
-                                B, T, H, Hkv, dk, dv, n_sink, window, dt, _UPDATES[update],
-                                flags, _p(workspace), ws_bytes, _stream(q))
-    _lib.check("gdn_hybrid_prefill", rc)
+    if weights is None:
+        rc = lib.gdn_hybrid_prefill(_p(q), _p(k), _p(v), _p(a), _p(b), _p(o), _p(state_out),
+                                    B, T, H, Hkv, dk, dv, n_sink, window, dt, _UPDATES[update],
+                                    flags, _p(workspace), ws_bytes, _stream(q))
+        _lib.check("gdn_hybrid_prefill", rc)
+    else:
+        rc = lib.gdn_hybrid_prefill_weighted(_p(q), _p(k), _p(v), _p(a), _p(b), _p(o),
+                                             _p(state_out), B, T, H, Hkv, dk, dv, n_sink, window,
+                                             dt, _UPDATES[update], flags, float(weights[0]),
+                                             float(weights[1]), _p(workspace), ws_bytes, _stream(q))
+        _lib.check("gdn_hybrid_prefill_weighted", rc)
     return o, state_out
 
 
 def hybrid_decode(q, k, v, a, b, state, k_cache, v_cache, a_cache, b_cache, pos,
                   n_sink: int, window: int, update: str = "gdn",
-                  flags: int = BRANCH_LINEAR | BRANCH_SOFTMAX, o=None):
+                  flags: int = BRANCH_LINEAR | BRANCH_SOFTMAX, o=None, weights=None):
     """One decode step for every sequence (state, caches and pos in place).
+
+    ``weights=(w_lin, w_swa)``: o = w_lin o_lin + w_swa o_swa; omitted, the
+    plain sum.
 
     q [B,H,d]; k/v [B,Hkv,d]; a [B,H] (GLA [B,H,d]); b [B,H]; state
     [B,H,d,d] fp32; k/v_cache [B,Hkv,n_sink+window,d]; a/b_cache
@@ -136,11 +149,17 @@ def hybrid_decode(q, k, v, a, b, state, k_cache, v_cache, a_cache, b_cache, pos,
     if o is None:
         o = torch.empty(B, H, dv, dtype=q.dtype, device=q.device)
     lib = _lib.load()
-    rc = lib.gdn_hybrid_decode(_p(q), _p(k), _p(v), _p(a), _p(b), _p(state), _p(k_cache),
-                               _p(v_cache), _p(a_cache), _p(b_cache), _p(pos), _p(o),
-                               B, H, Hkv, dk, dv, n_sink, window, dt, _UPDATES[update], flags,
-                               _stream(q))
-    _lib.check("gdn_hybrid_decode", rc)
+    ptrs = (_p(q), _p(k), _p(v), _p(a), _p(b), _p(state), _p(k_cache), _p(v_cache),
+            _p(a_cache), _p(b_cache), _p(pos), _p(o))
+    if weights is None:
+        rc = lib.gdn_hybrid_decode(*ptrs, B, H, Hkv, dk, dv, n_sink, window, dt, _UPDATES[update],
+                                   flags, _stream(q))
+        _lib.check("gdn_hybrid_decode", rc)
+    else:
+        rc = lib.gdn_hybrid_decode_weighted(*ptrs, B, H, Hkv, dk, dv, n_sink, window, dt,
+                                            _UPDATES[update], flags, float(weights[0]),
+                                            float(weights[1]), _stream(q))
+        _lib.check("gdn_hybrid_decode_weighted", rc)
     return o
 
 

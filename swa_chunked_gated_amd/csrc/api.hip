@@ -1,6 +1,8 @@
 // C-ABI front end of the hybrid layer library: host-side validation, then the
 // launches on the caller's stream.  See include/gdn_hybrid.h for the contract.
 
+#include <cmath>
+
 #include "gdn_hybrid.h"
 
 #include <stdint.h>
@@ -90,7 +92,18 @@ int gdn_hybrid_prefill(const void* q, const void* k, const void* v, const float*
                        const float* b, void* o, float* state_out, int B, int T, int H, int Hkv,
                        int dk, int dv, int n_sink, int window, int dtype, int update, int flags,
                        void* workspace, size_t workspace_bytes, void* stream) {
+  return gdn_hybrid_prefill_weighted(q, k, v, a, b, o, state_out, B, T, H, Hkv, dk, dv, n_sink,
+                                     window, dtype, update, flags, 1.f, 1.f, workspace,
+                                     workspace_bytes, stream);
+}
+
+int gdn_hybrid_prefill_weighted(const void* q, const void* k, const void* v, const float* a,
+                                const float* b, void* o, float* state_out, int B, int T, int H,
+                                int Hkv, int dk, int dv, int n_sink, int window, int dtype,
+                                int update, int flags, float w_lin, float w_swa, void* workspace,
+                                size_t workspace_bytes, void* stream) {
   if (!dims_ok(B, T, H, Hkv, dk, dv, n_sink, window, dtype, update)) return GDN_EINVAL;
+  if (!std::isfinite(w_lin) || !std::isfinite(w_swa)) return GDN_EINVAL;
   if (flags < 1 || flags > 15 || (flags & 7) == 0) return GDN_EINVAL;
   const bool lin = flags & GDN_BRANCH_LINEAR;
   const bool swa = flags & GDN_BRANCH_SOFTMAX;
@@ -110,7 +123,7 @@ int gdn_hybrid_prefill(const void* q, const void* k, const void* v, const float*
   if (T == 0 && !wst) return GDN_OK;
 
   gdn::PrefillArgs p{q, k, v, a, b, o, state_out, B, T, H, Hkv, dk, n_sink, window,
-                     dtype == GDN_BF16, update == GDN_GLA, flags, workspace};
+                     dtype == GDN_BF16, update == GDN_GLA, flags, workspace, w_lin, w_swa};
   hipStream_t s = (hipStream_t)stream;
   const int N = n_sink + window;
   // The linear kernel writes (or adds) rows t >= N and, for a linear-only
@@ -134,7 +147,18 @@ int gdn_hybrid_decode(const void* q, const void* k, const void* v, const float* 
                       float* state, void* k_cache, void* v_cache, float* a_cache, float* b_cache,
                       int* pos, void* o, int B, int H, int Hkv, int dk, int dv, int n_sink,
                       int window, int dtype, int update, int flags, void* stream) {
+  return gdn_hybrid_decode_weighted(q, k, v, a, b, state, k_cache, v_cache, a_cache, b_cache, pos,
+                                    o, B, H, Hkv, dk, dv, n_sink, window, dtype, update, flags, 1.f,
+                                    1.f, stream);
+}
+
+int gdn_hybrid_decode_weighted(const void* q, const void* k, const void* v, const float* a,
+                               const float* b, float* state, void* k_cache, void* v_cache,
+                               float* a_cache, float* b_cache, int* pos, void* o, int B, int H,
+                               int Hkv, int dk, int dv, int n_sink, int window, int dtype,
+                               int update, int flags, float w_lin, float w_swa, void* stream) {
   if (!dims_ok(B, 1, H, Hkv, dk, dv, n_sink, window, dtype, update)) return GDN_EINVAL;
+  if (!std::isfinite(w_lin) || !std::isfinite(w_swa)) return GDN_EINVAL;
   if (flags < 1 || flags > 3) return GDN_EINVAL;
   if (!q || !k || !v || !a || !state || !k_cache || !v_cache || !a_cache || !pos || !o)
     return GDN_EINVAL;
@@ -146,7 +170,8 @@ int gdn_hybrid_decode(const void* q, const void* k, const void* v, const float* 
   if (gdn::decode_lds_bytes(G, n_sink + window, dk, update == GDN_GLA, dtype == GDN_BF16 ? 2 : 4) > 160 * 1024)
     return GDN_EUNSUPPORTED;
   gdn::DecodeArgs p{q, k, v, a, b, state, k_cache, v_cache, a_cache, b_cache, pos, o,
-                    B, H, Hkv, dk, n_sink, window, dtype == GDN_BF16, update == GDN_GLA, flags};
+                    B, H, Hkv, dk, n_sink, window, dtype == GDN_BF16, update == GDN_GLA, flags,
+                    w_lin, w_swa};
   return launched(gdn::launch_decode(p, (hipStream_t)stream));
 }
 

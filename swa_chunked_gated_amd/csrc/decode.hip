@@ -90,7 +90,8 @@ __device__ __forceinline__ f32x4 raw4_f32(const f32x4& x) { return x; }
 // (one read, one write).  The softmax over the staged rows runs while the
 // state is still arriving.  Workgroups are placed so that the G query heads
 // of a KV head run together on one XCD: each cached row comes from HBM once
-// and from that XCD's L2 for the other heads.  o is written once.  MR scales
+// and from that XCD's L2 for the other heads.  o is written once, as
+// w_lin o_lin + w_swa o_swa (1, 1 for the plain sum).  MR scales
 // the rows staged per pass (MR * 128 bytes of each of K and V per head
 // dimension): 1 for budgets that fit one pass, 4 for long budgets, whose
 // serial passes (one staging round trip each) would otherwise dominate.
@@ -100,7 +101,7 @@ __device__ __forceinline__ void decode_step_body(
     const float* __restrict__ a, const float* __restrict__ b, float* __restrict__ state,
     const T* __restrict__ kc, const T* __restrict__ vc, const float* __restrict__ ac,
     const float* __restrict__ bc, const int* __restrict__ pos, T* __restrict__ o, int B, int H,
-    int Hkv, int n_sink, int window, int flags) {
+    int Hkv, int n_sink, int window, int flags, float w_lin, float w_swa) {
   using M = StepMap<T, D, MR>;
   typedef typename Vec16<T>::type V16;
   typedef typename Raw4<T>::type R4;
@@ -348,10 +349,10 @@ __device__ __forceinline__ void decode_step_body(
   }
   if (rg == 0) {
     const f32x4 c3 = *reinterpret_cast<const f32x4*>(&fin[cg * 12 + 8]);
-    const float inv = swa ? 1.0f / den : 0.f;
+    const float inv = swa ? w_swa / den : 0.f;
     f32x4 out;
 #pragma unroll
-    for (int xx = 0; xx < 4; ++xx) out[xx] = (lin ? olin[xx] : 0.f) + (swa ? c3[xx] * inv : 0.f);
+    for (int xx = 0; xx < 4; ++xx) out[xx] = (lin ? olin[xx] * w_lin : 0.f) + (swa ? c3[xx] * inv : 0.f);
     store4(o + (size_t)bh * D + 4 * cg, out);
   }
 }
@@ -361,8 +362,9 @@ __device__ __forceinline__ void decode_step_body(
       const float *__restrict__ a, const float *__restrict__ b, float *__restrict__ state,         \
       const T *__restrict__ kc, const T *__restrict__ vc, const float *__restrict__ ac,             \
       const float *__restrict__ bc, const int *__restrict__ pos, T *__restrict__ o, int B, int H,   \
-      int Hkv, int n_sink, int window, int flags
-#define GDN_DECODE_STEP_ARGS q, k, v, a, b, state, kc, vc, ac, bc, pos, o, B, H, Hkv, n_sink, window, flags
+      int Hkv, int n_sink, int window, int flags, float w_lin, float w_swa
+#define GDN_DECODE_STEP_ARGS \
+  q, k, v, a, b, state, kc, vc, ac, bc, pos, o, B, H, Hkv, n_sink, window, flags, w_lin, w_swa
 
 // One staged pass (48 KB of LDS): three workgroups per CU, so at most 80
 // VGPRs.
@@ -478,7 +480,7 @@ hipError_t launch_decode_t(const DecodeArgs& p, hipStream_t s) {
   hipLaunchKernelGGL(kern, grid, dim3(kStepThreads), 0, s, (const T*)p.q, (const T*)p.k,
                      (const T*)p.v, p.a, p.b, p.state, (const T*)p.k_cache, (const T*)p.v_cache,
                      p.a_cache, p.b_cache, p.pos, (T*)p.o, p.B, p.H, p.Hkv, p.n_sink, p.window,
-                     p.flags);
+                     p.flags, p.w_lin, p.w_swa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_commit_kernel<T, GLA>), dim3(p.B), dim3(256), 0, s, (const T*)p.k,

@@ -129,7 +129,8 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
     bf16* __restrict__ w_ktg, bf16* __restrict__ w_a, float* __restrict__ w_ut,
     float* __restrict__ w_g, uint64_t* __restrict__ ready, uint64_t epoch, int n_prep,
     uint64_t* __restrict__ done, int n_swa, bf16* __restrict__ o, float* __restrict__ state_out,
-    int B, int T_, int H, int Hkv, int n_sink, int window, int flags, int xcd) {
+    int B, int T_, int H, int Hkv, int n_sink, int window, int flags, int xcd, float w_lin,
+    float w_swa) {
   using SM = FullSmem<D, NW>;
   using PS = prep::PrepSmem<bf16, D, true>;
   static_assert(NL >= 1 && NL <= 4, "one to four loader waves");
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
     swa::swa_tiles<bf16, D, NW + NL, true>(q, k, v, o, T_, H, Hkv, 4, 64, kSwaTiles, n_sink, window,
                                            n_sink + window, bx, rest % groups, rest / groups,
                                            reinterpret_cast<bf16*>(smem_raw), done, epoch, nch,
-                                           (D / DVS) * NW);
+                                           (D / DVS) * NW, w_swa);
     return;
   }
 
@@ -433,7 +434,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
         const int r = 16 * rt + l16;
         if (r < Cc) {
           bf16* orow = o + ((size_t)(bi * T_ + i0 + r + window) * H + h) * D + c0 + cw + 4 * lg;
-          f32x4 val = ot[rt];
+          f32x4 val = ot[rt] * w_lin;
           if (n_swa > 0) {
             // device-scope store (read by the linked softmax tiles)
             const bf16x4 y = bf16x4{static_cast<bf16>(val[0]), static_cast<bf16>(val[1]),
@@ -524,7 +525,8 @@ hipError_t launch_full_t(const PrefillArgs& p, int nch, hipStream_t s, bool* swa
   hipLaunchKernelGGL(kern, dim3(n_prep + n_scan + n_swa), dim3(64 * (NW + NL)), lds, s,
                      (const bf16*)p.q, (const bf16*)p.k, (const bf16*)p.v, p.a, p.b, (bf16*)w.wm,
                      (bf16*)w.ktg, (bf16*)w.a, w.ut, w.g, w.ready, epoch, n_prep, w.done, n_swa,
-                     (bf16*)p.o, p.state_out, p.B, p.T, p.H, p.Hkv, p.n_sink, p.window, p.flags, xcd);
+                     (bf16*)p.o, p.state_out, p.B, p.T, p.H, p.Hkv, p.n_sink, p.window, p.flags, xcd,
+                     p.w_lin, p.w_swa);
   return hipGetLastError();
 }
 

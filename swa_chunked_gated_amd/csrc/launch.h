@@ -22,6 +22,8 @@ struct PrefillArgs {
   int gla;      // 1: GLA diagonal-gate update, 0: gated delta rule
   int flags;    // GDN_BRANCH_LINEAR | GDN_BRANCH_SOFTMAX | GDN_WRITE_STATE
   void* workspace;   // chunk preparation results (gated delta rule), see GdnWorkspace
+  float w_lin = 1.f;   // branch weights: o = w_lin o_lin + w_swa o_swa
+  float w_swa = 1.f;
 };
 
 // Workspace of the gated delta rule prefill, per (sequence, head, chunk), as
@@ -86,6 +88,8 @@ struct DecodeArgs {
   int B, H, Hkv, D;
   int n_sink, window;
   int bf16, gla, flags;
+  float w_lin = 1.f;   // branch weights: o = w_lin o_lin + w_swa o_swa
+  float w_swa = 1.f;
 };
 
 struct CacheArgs {

@@ -79,7 +79,9 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ w0, const T* __restrict__ w1, const T* __restrict__ w2,
     const float* __restrict__ wf, T* __restrict__ o,
-    float* __restrict__ state_out, int T_, int H, int Hkv, int n_sink, int window, int flags) {
+    float* __restrict__ state_out, int T_, int H, int Hkv, int n_sink, int window, int flags,
+    float w_lin) {
+  // w_lin weighs the linear branch in o (1 for the plain sum).
   // chunk preparation results (workspace), per (sequence, head, chunk):
   //   GDN, light: w0 = Tm diag(b), w1 = Tm diag(b gamma), wf = g (log2), gamma
   //   GLA:        w0 = Q 2^G, w1 = (K 2^{G_C - G})^T, w2 = A, wf = 2^{G_C}
@@ -539,7 +541,7 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
           T* orow = o + ((size_t)(bi * T_ + i0 + r + window) * H + h) * D + c0 + cw;
 #pragma unroll
           for (int dt = 0; dt < NT; ++dt) {
-            f32x4 val = ot[dt][rt];
+            f32x4 val = ot[dt][rt] * w_lin;
             if (accumulate) val += load4(orow + 16 * dt + 4 * lg);
             store4(orow + 16 * dt + 4 * lg, val);
           }
@@ -599,7 +601,7 @@ hipError_t launch_linear_t(const PrefillArgs& p, hipStream_t s) {
   }
   hipLaunchKernelGGL(kern, grid, dim3(64 * NW), SM::bytes, s, (const T*)p.q, (const T*)p.k,
                      (const T*)p.v, w0, w1, w2, wf, (T*)p.o, p.state_out, p.T, p.H, p.Hkv,
-                     p.n_sink, p.window, p.flags);
+                     p.n_sink, p.window, p.flags, p.w_lin);
   return hipGetLastError();
 }
 

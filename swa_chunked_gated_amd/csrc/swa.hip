@@ -42,11 +42,12 @@ template <class T, int D, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void swa_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                       const T* __restrict__ v, T* __restrict__ o,
                                                       int T_, int H, int Hkv, int HPW, int QT, int TPW,
-                                                      int n_sink, int window, int add_from) {
+                                                      int n_sink, int window, int add_from,
+                                                      float w_swa) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[swa::SwaSmem<T, D>::bytes];
   swa::swa_tiles<T, D, NW, false>(q, k, v, o, T_, H, Hkv, HPW, QT, TPW, n_sink, window, add_from,
                                   blockIdx.x, blockIdx.y, blockIdx.z, reinterpret_cast<T*>(lds),
-                                  nullptr, 0, 0, 0);
+                                  nullptr, 0, 0, 0, w_swa);
 }
 
 template <class T>
@@ -78,7 +79,7 @@ hipError_t launch_swa_t(const PrefillArgs& p, int add_from, hipStream_t s) {
 #define GDN_SWA_LAUNCH(NWV)                                                                         \
   hipLaunchKernelGGL((swa_kernel<T, D, NWV>), grid, dim3(64 * NWV), 0, s, (const T*)p.q,           \
                      (const T*)p.k, (const T*)p.v, (T*)p.o, p.T, p.H, p.Hkv, HPW, QT, TPW,         \
-                     p.n_sink, p.window, add_from)
+                     p.n_sink, p.window, add_from, p.w_swa)
   if (waves == 2) GDN_SWA_LAUNCH(2);
   else GDN_SWA_LAUNCH(4);
 #undef GDN_SWA_LAUNCH

@@ -26,9 +26,10 @@
 // Exponentials use exp2 with log2(e) folded into the scale.  A 16-key tile
 // that no query of the wave can see is skipped.
 //
-// Epilogue: o = O / l, plus the value o already holds on rows t >= add_from
-// (the linear branch, or the caller's values when accumulating), cast to the
-// output type.
+// Epilogue: o = w_swa O / l, plus the value o already holds on rows
+// t >= add_from (the linear branch, or the caller's values when
+// accumulating), cast to the output type.  w_swa weighs the softmax branch
+// (inference-time hybridisation; 1 for the plain sum).
 
 #pragma once
 
@@ -124,7 +125,8 @@ __device__ __forceinline__ void swa_tiles(const T* __restrict__ q, const T* __re
                                           const T* __restrict__ v, T* __restrict__ o, int T_, int H,
                                           int Hkv, int HPW, int QT, int TPW, int n_sink, int window,
                                           int add_from, int bx, int hgrp, int bi, T* lds,
-                                          const uint64_t* done, uint64_t epoch, int nch, int nflag) {
+                                          const uint64_t* done, uint64_t epoch, int nch, int nflag,
+                                          float w_swa) {
   constexpr int KB = KeyBlock<T>::n;
   constexpr int NTH = 64 * NW;
   constexpr int PAD = 16 / sizeof(T);
@@ -547,7 +549,7 @@ __device__ __forceinline__ void swa_tiles(const T* __restrict__ q, const T* __re
       const float l = lacc[nq][0];
       const int t = qb + 16 * nq + l16;
       if (t >= T_) continue;
-      const float inv = 1.0f / l;
+      const float inv = w_swa / l;
       T* orow = o + ((size_t)(bi * T_ + t) * H + h) * D;
       const bool addl = t >= add_from;
 #pragma unroll

@@ -258,3 +258,13 @@ def test_shortconv_history_validation(lib):
     assert call(pos0=-1) == EINVAL
     assert call(B=65536) == EUNSUP
     assert call(hq=ctypes.c_void_p(0x1008)) == EINVAL
+
+
+def test_weighted_calls_reject_non_finite_weights(lib):
+    import math
+    for wl, ws in ((math.nan, 1.0), (1.0, math.inf)):
+        assert lib.gdn_hybrid_prefill_weighted(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 8, 2, 2, 64,
+                                               64, 8, 56, BF16, DELTA, 3, wl, ws, None, 0, None) == EINVAL
+        assert lib.gdn_hybrid_decode_weighted(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                              FAKE, FAKE, 1, 2, 2, 64, 64, 8, 56, BF16, DELTA, 3, wl, ws,
+                                              None) == EINVAL

@@ -271,6 +271,73 @@ def test_qwen32b_full_stack_sampled():
             assert heads[0] // G == g
 
 
+# ------------------------------------------- weighted branches (hybridisation)
+
+@pytest.mark.parametrize("B,H,Hkv,d,T,dtype,update", [
+    (1, 4, 1, 128, 300, "bf16", "gdn"),     # few chains: one launch, linked softmax tiles
+    (4, 32, 8, 128, 200, "bf16", "gdn"),    # many chains: preparation + scan, then softmax
+    (2, 4, 2, 128, 260, "bf16", "gla"),
+    (1, 2, 2, 64, 150, "f32", "gdn")])
+def test_weighted_prefill(B, H, Hkv, d, T, dtype, update):
+    w = small(B=B, H=H, Hkv=Hkv, d=d, T=T, dtype=dtype, update=update)
+    inp = to_dev(make_prefill_inputs(w, seed=B * 100 + T))
+    fp32 = dtype == "f32"
+    plain, _ = run_prefill(inp, w, flags=ALL)
+    same, _ = gl.hybrid_prefill(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], w.n_sink, w.window,
+                                update=update, flags=ALL, weights=(1.0, 1.0))
+    torch.cuda.synchronize()
+    assert torch.equal(plain, same), "weights (1, 1) must equal the plain sum bitwise"
+    wl, ws = 0.3, 1.7
+    o, _ = gl.hybrid_prefill(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], w.n_sink, w.window,
+                             update=update, flags=ALL, weights=(wl, ws))
+    prior = torch.randn_like(o)
+    acc = prior.clone()
+    gl.hybrid_prefill(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], w.n_sink, w.window,
+                      update=update, flags=ALL | gl.ACCUMULATE, o=acc, weights=(wl, ws))
+    torch.cuda.synchronize()
+    G = H // Hkv
+    for bsel, heads in (([0], [0]), ([B - 1], [H - 1])):
+        g = heads[0] // G
+        qq = f64(inp["q"][bsel][:, :, heads])
+        kk, vv = f64(inp["k"][bsel][:, :, g:g + 1]), f64(inp["v"][bsel][:, :, g:g + 1])
+        aa, bb = f64(inp["a"][bsel][:, :, heads]), f64(inp["b"][bsel][:, :, heads])
+        ref, _ = O.hybrid_prefill(qq, kk, vv, aa, bb, w.n_sink, w.window, update, ALL, wl, ws)
+        assert_close(f64(o[bsel][:, :, heads]), ref, fp32, "weighted o")
+        assert_close(f64(acc[bsel][:, :, heads]) - f64(prior[bsel][:, :, heads]), ref, fp32,
+                     "weighted accumulate")
+
+
+@pytest.mark.parametrize("dtype,n_sink,window,pos0", [("bf16", 3, 61, 70), ("bf16", 8, 300, 400),
+                                                      ("f32", 3, 29, 40)])
+def test_weighted_decode(dtype, n_sink, window, pos0):
+    w = Workload("decw", B=2, H=8, Hkv=2, d=128 if dtype == "bf16" else 64, n_sink=n_sink,
+                 window=window, pos0=pos0, steps=2, dtype=dtype)
+    inp = make_decode_inputs(w, device=DEV, seed=pos0)
+    fp32 = dtype == "f32"
+    keys = ("state", "k_cache", "v_cache", "a_cache", "b_cache", "pos")
+    st = {k: inp[k].clone() for k in keys}
+    st1 = {k: inp[k].clone() for k in keys}
+    ref = {k: f64(st[k]) for k in keys}
+    ref["pos"] = st["pos"].cpu().numpy().astype(np.int64)
+    for s_ in range(w.steps):
+        step = {k: inp[k][s_] for k in ("q", "k", "v", "a", "b")}
+        args = (step["q"], step["k"], step["v"], step["a"], step["b"])
+        o = gl.hybrid_decode(*args, st["state"], st["k_cache"], st["v_cache"], st["a_cache"],
+                             st["b_cache"], st["pos"], w.n_sink, w.window, weights=(-0.5, 2.0))
+        o1 = gl.hybrid_decode(*args, st1["state"], st1["k_cache"], st1["v_cache"], st1["a_cache"],
+                              st1["b_cache"], st1["pos"], w.n_sink, w.window, weights=(1.0, 1.0))
+        if s_ == 0:   # the plain call from the same initial state
+            o_plain = run_decode(step, {k: inp[k].clone() for k in keys}, w)
+            assert torch.equal(o1, o_plain), "weights (1, 1) must equal the plain sum bitwise"
+        torch.cuda.synchronize()
+        ro, ref["state"], ref["k_cache"], ref["v_cache"], ref["a_cache"], ref["b_cache"], ref["pos"] = \
+            O.decode_step(*(f64(x) for x in args), ref["state"], ref["k_cache"], ref["v_cache"],
+                          ref["a_cache"], ref["b_cache"], ref["pos"], w.n_sink, w.window,
+                          w_lin=-0.5, w_swa=2.0)
+        assert_close(f64(o), ro, fp32, f"weighted decode step {s_}")
+        assert_close(f64(st["state"]), ref["state"], fp32, f"state step {s_}")
+
+
 # -------------------------------------------------------- short-conv decode
 
 def assert_hist_close(got, ref, what):

@@ -460,3 +460,32 @@ def test_shortconv_history_holds_rotated_inputs_at_ring_slots():
     for i in range(T - ks + 1, T):
         np.testing.assert_allclose(hq[0, i % (ks - 1)], rot[0, i].reshape(-1), atol=1e-14)
         np.testing.assert_array_equal(hv[0, i % (ks - 1)], x[0, i].reshape(-1))
+
+
+@pytest.mark.parametrize("update", ["gdn", "gla"])
+def test_branch_weights_reduce_to_single_branch_flags(update):
+    # Weights (1, 0) and (0, 1) give the single-branch outputs (the softmax
+    # branch is pinned to SDPA, the linear branch to closed forms); general
+    # weights give their combination, in prefill and in decode.
+    B, T, H, Hkv, d, ns, win = 1, 40, 4, 2, 8, 2, 9
+    q = unit(RNG.standard_normal((B, T, H, d)))
+    k = unit(RNG.standard_normal((B, T, Hkv, d)))
+    v = RNG.standard_normal((B, T, Hkv, d))
+    a = RNG.uniform(0.8, 1.0, (B, T, H, d) if update == "gla" else (B, T, H))
+    b = RNG.uniform(0.0, 1.0, (B, T, H))
+    lin, _ = O.hybrid_prefill(q, k, v, a, b, ns, win, update, flags=O.BRANCH_LINEAR)
+    sm, _ = O.hybrid_prefill(q, k, v, a, b, ns, win, update, flags=O.BRANCH_SOFTMAX)
+    both = O.BRANCH_LINEAR | O.BRANCH_SOFTMAX
+    np.testing.assert_array_equal(O.hybrid_prefill(q, k, v, a, b, ns, win, update, both, 1.0, 0.0)[0], lin)
+    np.testing.assert_array_equal(O.hybrid_prefill(q, k, v, a, b, ns, win, update, both, 0.0, 1.0)[0], sm)
+    got, _ = O.hybrid_prefill(q, k, v, a, b, ns, win, update, both, 0.25, 1.5)
+    np.testing.assert_allclose(got, 0.25 * lin + 1.5 * sm, atol=1e-13)
+    # decode: the next token's output with weights from the same caches
+    T0 = T - 1
+    pre = [x[:, :T0] for x in (q, k, v, a, b)]
+    _, S = O.hybrid_prefill(*pre, ns, win, update, flags=O.WRITE_STATE)
+    caches = O.cache_from_prefill(pre[1], pre[2], pre[3], pre[4], ns, win, update)
+    step = [x[:, T0] for x in (q, k, v, a, b)]
+    pos = np.full(B, T0)
+    o_w = O.decode_step(*step, S, *caches, pos, ns, win, update, both, 0.25, 1.5)[0]
+    np.testing.assert_allclose(o_w, got[:, T0], atol=1e-12)
