@@ -158,6 +158,29 @@ __device__ __forceinline__ Frag<float> lds_frag8_scaled(const float* p, const fl
                 b[0] * s1[0], b[1] * s1[1], b[2] * s1[2], b[3] * s1[3]};
   return frag_from8<float>(x);
 }
+// 8 contiguous LDS elements; elements 0..3 multiplied by s0[0..3] and 4..7
+// by s1[0..3] (fp32, 16-byte aligned) before the fragment is formed.
+__device__ __forceinline__ Frag<bf16> lds_frag8_scaled(const bf16* p, const float* s0p, const float* s1p) {
+  const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+  const f32x4 s0 = *reinterpret_cast<const f32x4*>(s0p);
+  const f32x4 s1 = *reinterpret_cast<const f32x4*>(s1p);
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = static_cast<float>(v[i]) * s0[i];
+    x[4 + i] = static_cast<float>(v[4 + i]) * s1[i];
+  }
+  return frag_from8<bf16>(x);
+}
+__device__ __forceinline__ Frag<float> lds_frag8_scaled(const float* p, const float* s0p, const float* s1p) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  const f32x4 s0 = *reinterpret_cast<const f32x4*>(s0p);
+  const f32x4 s1 = *reinterpret_cast<const f32x4*>(s1p);
+  float x[8] = {a[0] * s0[0], a[1] * s0[1], a[2] * s0[2], a[3] * s0[3],
+                b[0] * s1[0], b[1] * s1[1], b[2] * s1[2], b[3] * s1[3]};
+  return frag_from8<float>(x);
+}
 
 // 8 contiguous global elements converted to a fragment (q rows etc.).
 __device__ __forceinline__ Frag<bf16> gbl_frag8(const bf16* p) {

@@ -380,9 +380,10 @@ __device__ __forceinline__ void gdn_prep_chunk(
     }
   }
 
-  // ---- TB = Tm diag(b) (and TBG = Tm diag(b gamma)): row r, columns
-  // s0..s0+3 at positions acc_pos(s0)..+3 of the row; the full preparation
-  // keeps both in LDS
+  // ---- TB = Tm diag(b) (and, for the full preparation, TBG = Tm diag(b
+  // gamma)): row r, columns s0..s0+3 at positions acc_pos(s0)..+3 of the row;
+  // the full preparation keeps both in LDS, the light one writes TB (the scan
+  // scales it by gamma where it needs TBG)
   T* tb = wtb + ci * (kC * kC);
 #pragma unroll 4
   for (int i = lane; i < kC * kC / 4; i += 64) {
@@ -396,8 +397,8 @@ __device__ __forceinline__ void gdn_prep_chunk(
       store4(&TBs[r * SC + acc_pos(s0)], x);
       store4(&TBGs[r * SC + acc_pos(s0)], x * gg);
     } else {
+      (void)gg;
       put4v<DEV>(tb, r * kC + acc_pos(s0), x);
-      put4v<DEV>(wtbg + ci * (kC * kC), r * kC + acc_pos(s0), x * gg);
     }
   }
   put1f<DEV>(wg + ci * (2 * kC), lane, lgs[lane]);

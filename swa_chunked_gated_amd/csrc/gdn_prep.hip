@@ -74,8 +74,7 @@ GdnWorkspace gdn_workspace_layout(void* base, int B, int H, int nch, int D, size
   size_t off = 0;
   w.tb = full ? nullptr : p + off;
   off += full ? 0 : n * kC * kC * elt;
-  w.tbg = full ? nullptr : p + off;
-  off += full ? 0 : n * kC * kC * elt;
+  w.tbg = nullptr;   // the scan forms Tm diag(b gamma) from TB and gamma
   w.wm = full ? p + off : nullptr;
   off += full ? n * kC * D * elt : 0;
   w.ktg = full ? p + off : nullptr;

@@ -28,8 +28,8 @@ struct PrefillArgs {
 
 // Workspace of the gated delta rule prefill, per (sequence, head, chunk), as
 // consecutive arrays (I/O element type; token reduction index in acc order):
-//   light preparation: TB = Tm diag(b) [64][64], TBG = Tm diag(b gamma)
-//   [64][64], then g, gamma [2][64] fp32;
+//   light preparation: TB = Tm diag(b) [64][64], then g, gamma [2][64] fp32
+//   (the scan forms Tm diag(b gamma) from TB and gamma);
 //   full preparation (bf16): -Wm [64][D] with d_k in natural order,
 //   K^T 2^{g_C - g} [D][64] whose row r holds d_k index acc_pos(r), the
 //   scores A [64][64], (TB V)^T [D][64] fp32 (tokens in natural order),

@@ -27,9 +27,10 @@
 // wave owns 16 columns of S as fp32 MFMA accumulators in registers for the
 // whole sequence, and every S-dependent product of a chunk is wave-local.
 // The chunk preparation kernels (gdn_prep.hip, gla_prep.hip) have already
-// produced the triangular solve (TB, TBG) and the gates (GDN) or every
-// state-independent tile (GLA); the GDN chunk's Q K^T scores and Wm are
-// formed here on MFMA and shared through LDS.  (bf16 GDN with too few chains
+// produced the triangular solve (TB = Tm diag(b)) and the gates (GDN) or
+// every state-independent tile (GLA); the GDN chunk's Q K^T scores and
+// Wm = Tm diag(b gamma) K are formed here on MFMA (TB scaled by gamma as its
+// fragments are read) and shared through LDS.  (bf16 GDN with too few chains
 // to fill the GPU runs gdn_scan_full.hip instead.)
 // Chunk c+1's inputs are loaded into registers while chunk c is computed.
 // Every LDS tile keeps its reduction dimension in acc order (see common.h),
@@ -66,8 +67,7 @@ struct Smem {
   static constexpr int oAq = oVT + nVT;
   static constexpr int oWm = oAq + nA;
   static constexpr int oTB = oWm + (GLA ? 0 : nK);
-  static constexpr int oTBG = oTB + (GLA ? 0 : nA);
-  static constexpr int nT = oTBG + (GLA ? 0 : nA);
+  static constexpr int nT = oTB + (GLA ? 0 : nA);
   static constexpr int bytesT = ((nT * (int)sizeof(T)) + 15) / 16 * 16;
   // fp32 part: GDN g (log2), gamma [64 each]; GLA 2^{G_C} [D]
   static constexpr int nGate = GLA ? D : 2 * kC;
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
     float w_lin) {
   // w_lin weighs the linear branch in o (1 for the plain sum).
   // chunk preparation results (workspace), per (sequence, head, chunk):
-  //   GDN, light: w0 = Tm diag(b), w1 = Tm diag(b gamma), wf = g (log2), gamma
+  //   GDN, light: w0 = Tm diag(b), wf = g (log2), gamma (w1 unused)
   //   GLA:        w0 = Q 2^G, w1 = (K 2^{G_C - G})^T, w2 = A, wf = 2^{G_C}
   using SM = Smem<T, D, NW, DW, GLA>;
   constexpr int kThreads = 64 * NW;
@@ -119,7 +119,6 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
   T* Aqs = sT + SM::oAq;
   T* Wms = sT + SM::oWm;
   T* TBs = sT + SM::oTB;
-  T* TBGs = sT + SM::oTBG;
   float* gate = reinterpret_cast<float*>(smem_raw + SM::bytesT);   // GDN: g[64], gam[64]; GLA: 2^{G_C}[D]
 
   // the G query heads of a KV head and their column slices run on one XCD,
@@ -159,13 +158,13 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
   // ---------------- register prefetch of one chunk's inputs
   typedef typename Vec16<T>::type V16;
   // V (dword columns, both updates); GDN: K (dword columns), Q (16-byte row
-  // pieces), TB / TBG and g, gamma from the workspace; GLA: Q 2^G, K^T 2^{G_C-G},
+  // pieces), TB and g, gamma from the workspace; GLA: Q 2^G, K^T 2^{G_C-G},
   // A and 2^{G_C} from the workspace
   uint32_t pk[GLA ? 1 : TPT], pv[TPTV];
   V16 pq[NPQ];
   constexpr int NPT = GLA ? 1 : kC * kC / VEC / kThreads;
   static_assert(GLA || (kC * kC / VEC) % kThreads == 0, "TB staging");
-  V16 ptb[GLA ? NPK : NPT], ptbg[GLA ? NPA : NPT];
+  V16 ptb[GLA ? NPK : NPT], ptbg[GLA ? NPA : 1];
   f32x4 pgm = zero4();
   const size_t chain = (size_t)bi * H + h;
 
@@ -221,9 +220,6 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
       const V16* tb = reinterpret_cast<const V16*>(w0 + ci * (kC * kC));
 #pragma unroll
       for (int n = 0; n < NPT; ++n) ptb[n] = tb[tid + n * kThreads];
-      const V16* tbg = reinterpret_cast<const V16*>(w1 + ci * (kC * kC));
-#pragma unroll
-      for (int n = 0; n < NPT; ++n) ptbg[n] = tbg[tid + n * kThreads];
       if (tid < 2 * kC / 4) pgm = reinterpret_cast<const f32x4*>(wf + ci * (2 * kC))[tid];
     }
   };
@@ -280,7 +276,6 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
         const int r = j / (kC / VEC);
         const int pc = (j % (kC / VEC)) * VEC;      // already in acc order
         *reinterpret_cast<V16*>(&TBs[r * SC + pc]) = ptb[n];
-        *reinterpret_cast<V16*>(&TBGs[r * SC + pc]) = ptbg[n];
       }
       if (tid < 2 * kC / 4) *reinterpret_cast<f32x4*>(&gate[4 * tid]) = pgm;
     }
@@ -300,7 +295,7 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
       const float* lgs = gate;
       // ---- Q K^T -> A (decayed, masked s <= r) on the 10 lower 16x16 tiles;
       // the rest of the chunk's state-independent work comes from the chunk
-      // preparation (TB, TBG, g, gamma)
+      // preparation (TB, g, gamma)
       for (int job = wv; job < 10; job += NW) {
         const int mt = kTileM[job];
         const int nt = kTileN[job];
@@ -325,13 +320,18 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
         }
       }
       // ---- Wm^T = K^T (Tm diag(b gamma))^T, stored as -Wm [token][dk];
-      // each wave owns MT/NW dk tiles and reuses the TBG fragments
+      // each wave owns MT/NW dk tiles and reuses the TBG fragments, formed
+      // from TB: the 8 acc-order positions 32p + 8lg .. +7 of a row are
+      // tokens 32p + 4lg + 0..3 and 32p + 16 + 4lg + 0..3, scaled by gamma
       if (wv < MT) {
+        const float* gmv = lgs + kC;
         Frag<T> tbg[4][2];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-          for (int p = 0; p < 2; ++p) tbg[nt][p] = lds_frag8(&TBGs[(16 * nt + l16) * SC + 32 * p + 8 * lg]);
+          for (int p = 0; p < 2; ++p)
+            tbg[nt][p] = lds_frag8_scaled(&TBs[(16 * nt + l16) * SC + 32 * p + 8 * lg],
+                                          gmv + 32 * p + 4 * lg, gmv + 32 * p + 16 + 4 * lg);
         constexpr int MPW = MT >= NW ? MT / NW : 1;
 #pragma unroll
         for (int mi = 0; mi < MPW; ++mi) {

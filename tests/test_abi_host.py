@@ -66,15 +66,15 @@ def ws(lib, *args):
 def test_workspace_query(lib):
     # gated delta rule, per (sequence, head, 64-token chunk of the linear
     # stream): with few chains (B*H*(d/64) < 256) the full preparation,
-    # Tm diag(b), -Wm, K^T 2^{g_C-g} and A; else Tm diag(b), Tm diag(b gamma);
-    # plus 128 fp32 gate values
+    # Tm diag(b), -Wm, K^T 2^{g_C-g} and A; else Tm diag(b); plus 128 fp32
+    # gate values
     def gdn_bytes(B, T, H, d, elt, n=64):
         nch = -(-(T - n) // 64)
         full = elt == 2 and B * H * (2 if d == 128 else 1) < 256     # bf16, few chains
         if full:    # -Wm, K^T, A in bf16; (TB V)^T in fp32; gates; ready and done flags
             per = (64 * d + d * 64 + 64 * 64) * elt + d * 64 * 4 + 512 + 8 + d // 16 * 8
-        else:       # TB, TBG; gates
-            per = 2 * 64 * 64 * elt + 512
+        else:       # TB; gates
+            per = 64 * 64 * elt + 512
         return B * H * nch * per
     assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 3) == (OK, gdn_bytes(1, 4096, 32, 128, 2))
     assert gdn_bytes(1, 4096, 32, 128, 2) == 2016 * 74312
