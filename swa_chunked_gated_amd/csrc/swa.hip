@@ -72,9 +72,13 @@ hipError_t launch_swa_t(const PrefillArgs& p, int add_from, hipStream_t s) {
   const int waves = HPW * (QT / (16 * kNQ));
   const int ntiles = (p.T + QT - 1) / QT;
   const int groups = p.H / HPW;
-  // keep at least ~4 workgroups per CU of work before batching tiles
+  // keep at least ~4 workgroups per CU of work before batching tiles; long
+  // budgets do not batch (each tile's key loop is long enough to amortise
+  // its pipeline start, and more workgroups run at once: budget 896 is
+  // fastest with one tile per workgroup, budget 128 with eight)
   int TPW = 1;
-  while (TPW < 8 && (size_t)((ntiles + 2 * TPW - 1) / (2 * TPW)) * groups * p.B >= 2048) TPW *= 2;
+  if (p.n_sink + p.window < 512)
+    while (TPW < 8 && (size_t)((ntiles + 2 * TPW - 1) / (2 * TPW)) * groups * p.B >= 2048) TPW *= 2;
   const dim3 grid((ntiles + TPW - 1) / TPW, groups, p.B);
 #define GDN_SWA_LAUNCH(NWV)                                                                         \
   hipLaunchKernelGGL((swa_kernel<T, D, NWV>), grid, dim3(64 * NWV), 0, s, (const T*)p.q,           \
