@@ -29,6 +29,7 @@ namespace {
 
 constexpr int kTT = 64;      // tokens per wave
 constexpr int kMaxKs = 8;
+constexpr int kLB = 16;      // tokens whose loads are issued together
 
 template <class T, int D>
 __global__ __launch_bounds__(256) void shortconv_kernel(const T* __restrict__ x, const float* __restrict__ w,
@@ -77,42 +78,57 @@ __global__ __launch_bounds__(256) void shortconv_kernel(const T* __restrict__ x,
   const size_t row = (size_t)nh * D;
   const T* xb = x + (size_t)bi * T_ * row;
   T* yb = y + (size_t)bi * T_ * row;
-  for (int t = ts; t < t1; ++t) {
-    float x1 = to_f32(xb[(size_t)t * row + c1]);
-    float x2 = to_f32(xb[(size_t)t * row + c2]);
-    if (rope) {
-      const float r1 = x1 * cs - x2 * sn;
-      const float r2 = x2 * cs + x1 * sn;
-      x1 = r1;
-      x2 = r2;
-      const float cn = cs * cf - sn * sf;
-      sn = sn * cf + cs * sf;
-      cs = cn;
+  // the tile's tokens in blocks of kLB: a block's loads are issued together
+  // (indices clamped into the tile), so the wave waits for memory once per
+  // block instead of once per token
+  for (int tb = ts; tb < t1; tb += kLB) {
+    T xr1[kLB], xr2[kLB];
+#pragma unroll
+    for (int u = 0; u < kLB; ++u) {
+      const size_t tt = (size_t)min(tb + u, t1 - 1);
+      xr1[u] = xb[tt * row + c1];
+      xr2[u] = xb[tt * row + c2];
     }
 #pragma unroll
-    for (int jj = kMaxKs - 1; jj > 0; --jj) {
-      win1[jj] = win1[jj - 1];
-      win2[jj] = win2[jj - 1];
-    }
-    win1[0] = x1;
-    win2[0] = x2;
-    if (t < t0) continue;
-    float y1 = 0.f, y2 = 0.f;
+    for (int u = 0; u < kLB; ++u) {
+      const int t = tb + u;
+      if (t >= t1) break;
+      float x1 = to_f32(xr1[u]);
+      float x2 = to_f32(xr2[u]);
+      if (rope) {
+        const float r1 = x1 * cs - x2 * sn;
+        const float r2 = x2 * cs + x1 * sn;
+        x1 = r1;
+        x2 = r2;
+        const float cn = cs * cf - sn * sf;
+        sn = sn * cf + cs * sf;
+        cs = cn;
+      }
 #pragma unroll
-    for (int jj = 0; jj < kMaxKs; ++jj) {
-      y1 += w1[jj] * win1[jj];
-      y2 += w2[jj] * win2[jj];
-    }
-    if (norm) {
-      float ss = y1 * y1 + y2 * y2;
+      for (int jj = kMaxKs - 1; jj > 0; --jj) {
+        win1[jj] = win1[jj - 1];
+        win2[jj] = win2[jj - 1];
+      }
+      win1[0] = x1;
+      win2[0] = x2;
+      if (t < t0) continue;
+      float y1 = 0.f, y2 = 0.f;
 #pragma unroll
-      for (int m = 1; m < LPH; m <<= 1) ss += shfl_xor(ss, m);
-      const float inv = 1.0f / sqrtf(ss + 1e-6f);
-      y1 *= inv;
-      y2 *= inv;
+      for (int jj = 0; jj < kMaxKs; ++jj) {
+        y1 += w1[jj] * win1[jj];
+        y2 += w2[jj] * win2[jj];
+      }
+      if (norm) {
+        float ss = y1 * y1 + y2 * y2;
+#pragma unroll
+        for (int m = 1; m < LPH; m <<= 1) ss += shfl_xor(ss, m);
+        const float inv = 1.0f / sqrtf(ss + 1e-6f);
+        y1 *= inv;
+        y2 *= inv;
+      }
+      yb[(size_t)t * row + c1] = from_f32<T>(y1);
+      yb[(size_t)t * row + c2] = from_f32<T>(y2);
     }
-    yb[(size_t)t * row + c1] = from_f32<T>(y1);
-    yb[(size_t)t * row + c2] = from_f32<T>(y2);
   }
 }
 
