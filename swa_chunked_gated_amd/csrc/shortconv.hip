@@ -11,8 +11,8 @@
 //
 // Work split: one wave per (sequence, head, 64-token tile).  Lane j owns the
 // RoPE pair (j, j + d/2) of its head, so rotation, the 8-tap sliding window
-// over time and the per-head norm (a butterfly over the head's lanes) never
-// leave registers; the tile re-reads a 7-token causal halo.  The rotation
+// over time and the per-head norm (a register-only reduction over the head's
+// lanes) never leave registers; the tile re-reads a 7-token causal halo.  The rotation
 // angle is set in fp64 at the tile start and then advanced one token at a
 // time by a fixed complex rotation (error grows ~1e-7 per token).
 //
@@ -26,6 +26,30 @@
 
 namespace gdn {
 namespace {
+
+// Sum over the N (32 or 64) lanes holding one head, in registers: within
+// each row of 16 lanes by DPP (lane ^ 1, lane ^ 2, then the half-row and row
+// mirrors, each step adding the other half of the group so far), then across
+// rows with the row-swap permutes.  Every lane of the group ends with the sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ float head_sum(float x) {
+  static_assert(N == 32 || N == 64, "a head spans half or all of the wave");
+  x += dpp_f<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+  x += dpp_f<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+  x += dpp_f<0x141>(x);   // row_half_mirror
+  x += dpp_f<0x140>(x);   // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  if constexpr (N == 64) {
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  }
+  return x;
+}
 
 constexpr int kTT = 64;      // tokens per wave
 constexpr int kMaxKs = 8;
@@ -119,9 +143,7 @@ __global__ __launch_bounds__(256) void shortconv_kernel(const T* __restrict__ x,
         y2 += w2[jj] * win2[jj];
       }
       if (norm) {
-        float ss = y1 * y1 + y2 * y2;
-#pragma unroll
-        for (int m = 1; m < LPH; m <<= 1) ss += shfl_xor(ss, m);
+        const float ss = head_sum<LPH>(y1 * y1 + y2 * y2);
         const float inv = 1.0f / sqrtf(ss + 1e-6f);
         y1 *= inv;
         y2 *= inv;
@@ -232,9 +254,7 @@ __global__ __launch_bounds__(256) void shortconv_decode_kernel(ConvSet set, cons
     hw[c2] = x2;
   }
   if (tt.norm) {
-    float ss = y1 * y1 + y2 * y2;
-#pragma unroll
-    for (int mm = 1; mm < LPH; mm <<= 1) ss += shfl_xor(ss, mm);
+    const float ss = head_sum<LPH>(y1 * y1 + y2 * y2);
     const float inv = 1.0f / sqrtf(ss + 1e-6f);
     y1 *= inv;
     y2 *= inv;
