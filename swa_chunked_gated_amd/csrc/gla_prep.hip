@@ -41,13 +41,19 @@ struct GlaPrepSmem {
   static constexpr int SC = kC + PAD;     // stride of [*][64] tiles
   static constexpr int oQD = 0;                       // q 2^{G - M}
   static constexpr int oKD = oQD + kC * SK;           // k 2^{M - G}
-  static constexpr int oKT = oKD + kC * SK;           // K^T 2^{G_C - G}
-  static constexpr int oA = oKT + D * SC;             // A
-  static constexpr int nT = oA + kC * SC;
-  static constexpr int bytesT = (nT * (int)sizeof(T) + 15) / 16 * 16;
-  static constexpr int nG = kC * D;                   // cumulative log2 gates
+  // one region, first the cumulative log2 gates (fp32 [64][D]), then, once
+  // they are no longer read, K^T 2^{G_C - G} [D][SC] and A [64][SC]
+  static constexpr int oU = oKD + kC * SK;
+  static constexpr int nG = kC * D;
+  static constexpr int nGT = nG * 4 / (int)sizeof(T);   // the gates in T elements
+  static constexpr int nKA = D * SC + kC * SC;
+  static constexpr int nU = nGT > nKA ? nGT : nKA;
+  static constexpr int oKT = oU;
+  static constexpr int oA = oU + D * SC;
+  static constexpr int bytesT = ((oU + nU) * (int)sizeof(T) + 15) / 16 * 16;
   static constexpr int nMf = 6 * D;                   // tile-pair factors
-  static constexpr int bytes = bytesT + 4 * (nG + nMf);
+  static constexpr int bytes = bytesT + 4 * nMf;
+  static_assert((oU * (int)sizeof(T)) % 16 == 0, "gate region alignment");
 };
 
 template <class T, int D>
@@ -68,8 +74,8 @@ __global__ __launch_bounds__(512) void gla_prep_kernel(
   T* KDs = sT + SM::oKD;
   T* KTs = sT + SM::oKT;
   T* As = sT + SM::oA;
-  float* Gl = reinterpret_cast<float*>(smem_raw + SM::bytesT);   // [64][D]
-  float* Mf = Gl + SM::nG;                                        // [6][D], acc order
+  float* Gl = reinterpret_cast<float*>(sT + SM::oU);              // [64][D], aliases K^T and A
+  float* Mf = reinterpret_cast<float*>(smem_raw + SM::bytesT);    // [6][D], acc order
 
   // the query heads of one KV head run back to back on one XCD (shared K)
   const int G = H / Hkv;
@@ -164,9 +170,11 @@ __global__ __launch_bounds__(512) void gla_prep_kernel(
   __syncthreads();
 
   // ---- scaled operands: Q 2^G (to the workspace), q 2^{G - M}, k 2^{M - G}
-  // (LDS, for A) and K^T 2^{G_C - G} (LDS, copied out below); VEC channels of
-  // one row per piece, written as runs of 4 (contiguous in acc order)
+  // (LDS, for A) and K^T 2^{G_C - G} (kept in registers until the gates'
+  // LDS region is free, then LDS, copied out below); VEC channels of one row
+  // per piece, written as runs of 4 (contiguous in acc order)
   T* qg = wqg + ci * (kC * D);
+  T ktr[NPC][VEC];
 #pragma unroll
   for (int j = 0; j < NPC; ++j) {
     const int idx = tid + j * NTH;
@@ -193,7 +201,7 @@ __global__ __launch_bounds__(512) void gla_prep_kernel(
       store4(&QDs[r * SK + pc], qd);
       store4(&KDs[r * SK + pc], kd);
 #pragma unroll
-      for (int x = 0; x < 4; ++x) KTs[(cc + x) * SC + acc_pos(r)] = from_f32<T>(kt[x]);
+      for (int x = 0; x < 4; ++x) ktr[j][4 * m + x] = from_f32<T>(kt[x]);
     }
   }
   // tile-pair factors 2^{M_mt - M_nt}, pair index mt (mt - 1) / 2 + nt
@@ -205,7 +213,15 @@ __global__ __launch_bounds__(512) void gla_prep_kernel(
     Mf[pr * D + acc_pos(cc)] = __builtin_amdgcn_exp2f(Gl[(16 * mt + 7) * D + cc] - Gl[(16 * nt + 7) * D + cc]);
   }
   if (tid < D) wegc[ci * D + tid] = __builtin_amdgcn_exp2f(Gl[(kC - 1) * D + tid]);
-  __syncthreads();
+  __syncthreads();   // the gates are no longer read: their region takes K^T and A
+#pragma unroll
+  for (int j = 0; j < NPC; ++j) {
+    const int idx = tid + j * NTH;
+    const int r = idx / (D / VEC);
+    const int cb = (idx % (D / VEC)) * VEC;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) KTs[(cb + e) * SC + acc_pos(r)] = ktr[j][e];
+  }
 
   // ---- A = [s <= r] 2^{G_r - G_s} o (Q K^T) on the 10 lower tiles
   for (int job = wv; job < 10; job += NTH / 64) {
