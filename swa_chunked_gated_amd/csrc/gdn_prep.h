@@ -221,7 +221,7 @@ template <class T, int D, bool FULL, bool DEV = false>
 __device__ __forceinline__ void gdn_prep_chunk(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ a, const float* __restrict__ b, T* __restrict__ wtb,
-    T* __restrict__ wtbg, T* __restrict__ wwm, T* __restrict__ wktg, T* __restrict__ wa,
+    T* __restrict__ wwm, T* __restrict__ wktg, T* __restrict__ wa,
     float* __restrict__ wut, float* __restrict__ wg, int T_, int H, int Hkv, int n_sink, int window,
     int nch, int c, int h, int bi, unsigned char* smem_raw) {
   using SM = PrepSmem<T, D, FULL>;

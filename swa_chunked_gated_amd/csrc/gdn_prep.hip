@@ -18,7 +18,7 @@ template <class T, int D, bool FULL>
 __global__ __launch_bounds__(64) void gdn_prep_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ a, const float* __restrict__ b, T* __restrict__ wtb,
-    T* __restrict__ wtbg, T* __restrict__ wwm, T* __restrict__ wktg, T* __restrict__ wa,
+    T* __restrict__ wwm, T* __restrict__ wktg, T* __restrict__ wa,
     float* __restrict__ wut, float* __restrict__ wg, int T_, int H, int Hkv, int n_sink,
     int window, int nch) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -29,7 +29,7 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(
   if (!xcd_grouped(blockIdx.x, G, nch * Hkv, unit, member)) return;
   const int c = unit % nch;
   const int h = (unit / nch) * G + member;
-  prep::gdn_prep_chunk<T, D, FULL>(q, k, v, a, b, wtb, wtbg, wwm, wktg, wa, wut, wg, T_, H, Hkv,
+  prep::gdn_prep_chunk<T, D, FULL>(q, k, v, a, b, wtb, wwm, wktg, wa, wut, wg, T_, H, Hkv,
                                    n_sink, window, nch, c, h, blockIdx.y, smem_raw);
 }
 
@@ -42,7 +42,7 @@ hipError_t launch_prep_t(const PrefillArgs& p, int nch, hipStream_t s) {
   const GdnWorkspace w = gdn_workspace_layout(p.workspace, p.B, p.H, nch, D, sizeof(T), FULL);
   const dim3 grid(xcd_grouped_grid((long long)nch * p.Hkv, p.H / p.Hkv), p.B);
   hipLaunchKernelGGL(kern, grid, dim3(64), SM::bytes, s, (const T*)p.q,
-                     (const T*)p.k, (const T*)p.v, p.a, p.b, (T*)w.tb, (T*)w.tbg, (T*)w.wm,
+                     (const T*)p.k, (const T*)p.v, p.a, p.b, (T*)w.tb, (T*)w.wm,
                      (T*)w.ktg, (T*)w.a, w.ut, w.g, p.T, p.H, p.Hkv, p.n_sink, p.window, nch);
   return hipGetLastError();
 }
@@ -74,7 +74,6 @@ GdnWorkspace gdn_workspace_layout(void* base, int B, int H, int nch, int D, size
   size_t off = 0;
   w.tb = full ? nullptr : p + off;
   off += full ? 0 : n * kC * kC * elt;
-  w.tbg = nullptr;   // the scan forms Tm diag(b gamma) from TB and gamma
   w.wm = full ? p + off : nullptr;
   off += full ? n * kC * D * elt : 0;
   w.ktg = full ? p + off : nullptr;

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
     for (int it = first; it < nch * per; it += stride) {
       const int c = it / per;
       const int bh = xcd ? xcd_chain(xcd, H / Hkv, x, it % per) : it % per;
-      prep::gdn_prep_chunk<bf16, D, true, true>(q, k, v, a, b, nullptr, nullptr, w_wm, w_ktg, w_a,
+      prep::gdn_prep_chunk<bf16, D, true, true>(q, k, v, a, b, nullptr, w_wm, w_ktg, w_a,
                                                 w_ut, w_g, T_, H, Hkv, n_sink, window, nch, c,
                                                 bh % H, bh / H, smem_raw + wv * PS::bytes);
       // every device-scope tile store of this wave has completed (vmcnt 0)

@@ -37,7 +37,6 @@ struct PrefillArgs {
 //   uint64 flags per chunk that publish the scan's output rows.
 struct GdnWorkspace {
   void* tb;
-  void* tbg;
   void* wm;
   void* ktg;
   void* a;

@@ -596,7 +596,7 @@ hipError_t launch_linear_t(const PrefillArgs& p, hipStream_t s) {
   } else {
     const GdnWorkspace w = gdn_workspace_layout(p.workspace, p.B, p.H, nch, D, sizeof(T), false);
     w0 = (const T*)w.tb;
-    w1 = (const T*)w.tbg;
+    w1 = nullptr;   // Tm diag(b gamma) is formed from TB and gamma
     wf = w.g;
   }
   hipLaunchKernelGGL(kern, grid, dim3(64 * NW), SM::bytes, s, (const T*)p.q, (const T*)p.k,
