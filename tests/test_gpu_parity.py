@@ -271,6 +271,52 @@ def test_qwen32b_full_stack_sampled():
             assert heads[0] // G == g
 
 
+# ---------------------------------------------------------- edge shapes
+
+def test_many_chain_full_wave_scan():
+    """B*H >= 256: one 8-wave scan workgroup per chain (light preparation),
+    then the softmax launch; sampled chains against the oracle."""
+    w = small(B=8, H=32, Hkv=8, d=128, T=300, sigma=1.0)
+    inp = to_dev(make_prefill_inputs(w, seed=21))
+    o, st = run_prefill(inp, w)
+    for bsel, heads in (([0], [0, 1]), ([5], [17]), ([7], [31])):
+        ref, S = oracle_subset(inp, w, bsel, heads)
+        assert_close(f64(o[bsel][:, :, heads]), ref, False, "o")
+        assert_close(f64(st[bsel][:, heads]), S, False, "state")
+
+
+@pytest.mark.parametrize("dtype,d,n_sink,window,T", [("bf16", 128, 0, 1, 100), ("bf16", 128, 8, 1, 150),
+                                                     ("f32", 64, 0, 1, 90), ("bf16", 64, 0, 64, 64)])
+def test_degenerate_budgets(dtype, d, n_sink, window, T):
+    """Window of one token, no sinks, and T equal to the budget."""
+    w = small(B=1, H=4, Hkv=1, d=d, T=T, n_sink=n_sink, window=window, dtype=dtype)
+    inp = to_dev(make_prefill_inputs(w, seed=T + window))
+    o, st = run_prefill(inp, w)
+    ref, S = O.hybrid_prefill(*(f64(inp[x]) for x in ("q", "k", "v", "a", "b")), n_sink, window)
+    assert_close(f64(o), ref, dtype == "f32", "o")
+    assert_close(f64(st), S, dtype == "f32", "state")
+
+
+@pytest.mark.parametrize("n_sink,window,pos0", [(8, 56, 100), (8, 192, 300), (0, 1, 5), (2, 1, 1)])
+def test_decode_largest_group_and_window_one(n_sink, window, pos0):
+    """16 query heads per KV head (the largest group), narrow and wide cache
+    passes; a one-token window, with and without sinks."""
+    w = Workload("decg", B=3, H=16, Hkv=1, d=128, n_sink=n_sink, window=window, pos0=pos0, steps=3)
+    inp = make_decode_inputs(w, device=DEV, seed=pos0 + window)
+    st = {k: inp[k].clone() for k in ("state", "k_cache", "v_cache", "a_cache", "b_cache", "pos")}
+    ref = {k: f64(st[k]) for k in st}
+    ref["pos"] = st["pos"].cpu().numpy().astype(np.int64)
+    for s_ in range(w.steps):
+        step = {k: inp[k][s_] for k in ("q", "k", "v", "a", "b")}
+        o = run_decode(step, st, w)
+        ro, ref["state"], ref["k_cache"], ref["v_cache"], ref["a_cache"], ref["b_cache"], ref["pos"] = \
+            O.decode_step(*(f64(step[x]) for x in ("q", "k", "v", "a", "b")), ref["state"], ref["k_cache"],
+                          ref["v_cache"], ref["a_cache"], ref["b_cache"], ref["pos"], w.n_sink, w.window)
+        assert_close(f64(o), ro, False, f"o step {s_}")
+        assert_close(f64(st["state"]), ref["state"], False, f"state step {s_}")
+        assert np.array_equal(f64(st["k_cache"]), ref["k_cache"])
+
+
 # ------------------------------------------- weighted branches (hybridisation)
 
 @pytest.mark.parametrize("B,H,Hkv,d,T,dtype,update", [
