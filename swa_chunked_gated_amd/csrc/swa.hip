@@ -37,6 +37,8 @@ namespace gdn {
 namespace {
 
 using swa::kNQ;
+// most consecutive 64-row tiles per workgroup of the resident-block kernel
+constexpr int kRingTiles = 16;
 
 template <class T, int D, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void swa_kernel(const T* __restrict__ q, const T* __restrict__ k,
@@ -48,6 +50,21 @@ __global__ __launch_bounds__(64 * NW, 2) void swa_kernel(const T* __restrict__ q
   swa::swa_tiles<T, D, NW, false>(q, k, v, o, T_, H, Hkv, HPW, QT, TPW, n_sink, window, add_from,
                                   blockIdx.x, blockIdx.y, blockIdx.z, reinterpret_cast<T*>(lds),
                                   nullptr, 0, 0, 0, w_swa);
+}
+
+// Four query heads of one KV head, 64-row tiles (two waves per head), key
+// blocks resident in LDS across the workgroup's TPW consecutive tiles (short
+// budgets, many tiles per workgroup; bf16 only, whose key blocks are 64 keys).
+template <class T, int D>
+__global__ __launch_bounds__(512) void swa_ring_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                       const T* __restrict__ v, T* __restrict__ o,
+                                                       int T_, int H, int Hkv, int TPW, int n_sink,
+                                                       int window, int add_from, float w_swa) {
+  static_assert(swa::KeyBlock<T>::n == 64, "64-row tiles advance by one key block");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[swa::SwaSmem<T, D>::ring_bytes];
+  swa::swa_tiles<T, D, 8, false, true>(q, k, v, o, T_, H, Hkv, 4, 64, TPW, n_sink, window, add_from,
+                                       blockIdx.x, blockIdx.y, blockIdx.z, reinterpret_cast<T*>(lds),
+                                       nullptr, 0, 0, 0, w_swa);
 }
 
 template <class T>
@@ -68,6 +85,24 @@ hipError_t launch_swa_t(const PrefillArgs& p, int add_from, hipStream_t s) {
   const int G = p.H / p.Hkv;
   int HPW = 1;
   while (HPW < 4 && G % (2 * HPW) == 0) HPW *= 2;
+  if constexpr (sizeof(T) == 2) {
+    // resident key blocks: a 64-row tile's window must fit in three aligned
+    // 64-key blocks (window <= 129) and the sinks in one; worth it when every
+    // workgroup walks at least four tiles
+    if (HPW == 4 && p.n_sink <= 64 && p.window <= 129) {
+      const int nt64 = (p.T + 63) / 64;
+      const int groups4 = p.H / 4;
+      int TPW = 1;
+      while (TPW < kRingTiles && (size_t)((nt64 + 2 * TPW - 1) / (2 * TPW)) * groups4 * p.B >= 1024) TPW *= 2;
+      if (TPW >= 4) {
+        const dim3 grid((nt64 + TPW - 1) / TPW, groups4, p.B);
+        hipLaunchKernelGGL((swa_ring_kernel<T, D>), grid, dim3(512), 0, s, (const T*)p.q, (const T*)p.k,
+                           (const T*)p.v, (T*)p.o, p.T, p.H, p.Hkv, TPW, p.n_sink, p.window, add_from,
+                           p.w_swa);
+        return hipGetLastError();
+      }
+    }
+  }
   const int QT = HPW == 1 ? 64 : 32;
   const int waves = HPW * (QT / (16 * kNQ));
   const int ntiles = (p.T + QT - 1) / QT;

@@ -110,6 +110,8 @@ struct SwaSmem {
   static constexpr int bytes = (2 * nK + 2 * nV) * (int)sizeof(T);
   // linked tiles of few blocks: every block staged at once, K then V^T per block
   static constexpr int deep_bytes = kDeepBlocks * (nK + nV) * (int)sizeof(T);
+  // resident key blocks: three window blocks (a ring) and the sink block
+  static constexpr int ring_bytes = 4 * (nK + nV) * (int)sizeof(T);
 };
 
 // The query tiles bx * TPW .. of (sequence bi, query heads hgrp * HPW ..
@@ -120,7 +122,13 @@ struct SwaSmem {
 // done flags of the scan chunks (64 rows from add_from each) that cover its
 // rows, nflag flags per (sequence, head, chunk), and reads them at device
 // scope.
-template <class T, int D, int NW, bool LINKED>
+// RING (not linked; QT = KB, n_sink <= KB, window <= 2 KB + 1; SwaSmem
+// ring_bytes of LDS): key blocks are aligned to multiples of KB and stay
+// resident while the workgroup walks its consecutive tiles.  A tile's window
+// spans at most three such blocks, held in slots (block index mod 3); the
+// sink keys sit in a fourth slot staged once.  Each tile stages only the one
+// block the next tile adds, into the slot of the block it no longer needs.
+template <class T, int D, int NW, bool LINKED, bool RING = false>
 __device__ __forceinline__ void swa_tiles(const T* __restrict__ q, const T* __restrict__ k,
                                           const T* __restrict__ v, T* __restrict__ o, int T_, int H,
                                           int Hkv, int HPW, int QT, int TPW, int n_sink, int window,
@@ -141,6 +149,7 @@ __device__ __forceinline__ void swa_tiles(const T* __restrict__ q, const T* __re
   constexpr int NVP = (KB / 4) * CH;               // V pieces per block
   constexpr int NPV = (NVP + NTH - 1) / NTH;       // V pieces per thread
   static_assert(KB * CH % NTH == 0 && NPK >= 1, "staging shape");
+  static_assert(!(LINKED && RING), "resident blocks are for the unlinked kernel");
   typedef typename Vec16<T>::type V16;
   auto Ks = [&](int buf) { return lds + buf * (KB * SK); };
   auto VTs = [&](int buf) { return lds + 2 * (KB * SK) + buf * (D * SV); };
@@ -168,6 +177,16 @@ __device__ __forceinline__ void swa_tiles(const T* __restrict__ q, const T* __re
     win_lo = max(n_sink, t0 - window + 1);
     nbs = (sink_end + KB - 1) / KB;
     nbw = t_end > win_lo ? (t_end - win_lo + KB - 1) / KB : 0;
+  };
+  // RING: tile t0's sink block (if any) and its window blocks blo..bhi
+  // (KB-aligned; empty when bhi < blo)
+  auto ring_range = [&](int t0, int& nbs, int& blo, int& bhi, int& sink_end, int& t_end) {
+    t_end = min(t0 + QT, T_);
+    sink_end = min(n_sink, t_end);
+    nbs = sink_end > 0 ? 1 : 0;
+    const int lo = max(n_sink, t0 - window + 1);
+    blo = lo / KB;
+    bhi = t_end > lo ? (t_end - 1) / KB : blo - 1;
   };
   // block blk of the workgroup's tile ti -> block description (every tile
   // has at least one block)
@@ -307,7 +326,24 @@ __device__ __forceinline__ void swa_tiles(const T* __restrict__ q, const T* __re
     }
   }
   int flat = 0;   // running block counter (selects the LDS buffer)
-  if (!deep && ntile > 0) {
+  if constexpr (RING) {
+    // the first tile's blocks: the sinks into slot 3, window block b into
+    // slot b mod 3 (each staged whole, up to the sequence end)
+    if (ntile > 0) {
+      int nbs0, blo0, bhi0, se0, te0;
+      ring_range(tile0 * QT, nbs0, blo0, bhi0, se0, te0);
+      if (nbs0) {
+        const Blk bl{0, min(n_sink, T_), 1};
+        prefetch(bl, pks[0], pvs[0], nks[0]);
+        commit(DKs(3), DVTs(3), pks[0], pvs[0], nks[0]);
+      }
+      for (int b2 = blo0; b2 <= bhi0; ++b2) {
+        const Blk bl{b2 * KB, min(b2 * KB + KB, T_), 0};
+        prefetch(bl, pks[0], pvs[0], nks[0]);
+        commit(DKs(b2 % 3), DVTs(b2 % 3), pks[0], pvs[0], nks[0]);
+      }
+    }
+  } else if (!deep && ntile > 0) {
     Blk b0;
     block_of(0, 0, b0);
     prefetch(b0, pks[0], pvs[0], nks[0]);
@@ -320,7 +356,26 @@ __device__ __forceinline__ void swa_tiles(const T* __restrict__ q, const T* __re
     const int qb = t0 + (wv % NWQ) * 16 * kNQ;      // first query row of this wave
     const int qlast = qb + 16 * kNQ - 1;
     int nbs, nbw, sink_end, win_lo, t_end;
-    tile_blocks(t0, nbs, nbw, sink_end, win_lo, t_end);
+    int blo = 0, nb = 0;            // RING: first window block; block staged for the next tile
+    bool newblk = false;
+    if constexpr (RING) {
+      int bhi;
+      ring_range(t0, nbs, blo, bhi, sink_end, t_end);
+      nbw = bhi - blo + 1;
+      win_lo = 0;
+      if (ti + 1 < ntile) {
+        int nbs2, blo2, bhi2, se2, te2;
+        ring_range(t0 + QT, nbs2, blo2, bhi2, se2, te2);
+        nb = bhi2;
+        newblk = bhi2 > bhi;
+        if (newblk) {
+          const Blk bl{nb * KB, min(nb * KB + KB, T_), 0};
+          prefetch(bl, pks[0], pvs[0], nks[0]);
+        }
+      }
+    } else {
+      tile_blocks(t0, nbs, nbw, sink_end, win_lo, t_end);
+    }
     const int nblk = nbs + nbw;
 
     if (!deep) load_q(ti, qraw);
@@ -355,17 +410,19 @@ __device__ __forceinline__ void swa_tiles(const T* __restrict__ q, const T* __re
     for (int blk = 0; blk < nblk; ++blk, ++flat) {
       const int buf = flat & 1;
       const bool sinkph = blk < nbs;
-      const int kb0 = sinkph ? blk * KB : win_lo + (blk - nbs) * KB;
+      const int kb0 = RING ? (sinkph ? 0 : (blo + blk - nbs) * KB)
+                           : (sinkph ? blk * KB : win_lo + (blk - nbs) * KB);
       const int kend = sinkph ? sink_end : t_end;
       const bool last = blk + 1 == nblk;
       const bool has_next = !last || ti + 1 < ntile;
-      if (!deep && has_next) {
+      if (!RING && !deep && has_next) {
         Blk nx;
         block_of(last ? ti + 1 : ti, last ? 0 : blk + 1, nx);
         prefetch(nx, pks[0], pvs[0], nks[0]);
       }
-      const T* Kb = deep ? DKs(blk) : Ks(buf);
-      const T* Vb = deep ? DVTs(blk) : VTs(buf);
+      const int slot = sinkph ? 3 : (blo + blk - nbs) % 3;   // RING
+      const T* Kb = RING ? DKs(slot) : deep ? DKs(blk) : Ks(buf);
+      const T* Vb = RING ? DVTs(slot) : deep ? DVTs(blk) : VTs(buf);
 
       // ---- S^T tiles for this wave, computed relative to the running max:
       // the accumulators start at -mbase, so the MFMAs return s - mbase
@@ -376,7 +433,7 @@ __device__ __forceinline__ void swa_tiles(const T* __restrict__ q, const T* __re
       for (int kt = 0; kt < KB / 16; ++kt) {
         const int k0 = kb0 + 16 * kt;
         bool on = k0 < kend && k0 <= qlast && qb < T_;
-        if (!sinkph) on = on && (k0 + 15 > qb - window);
+        if (!sinkph) on = on && (k0 + 15 > qb - window) && (!RING || k0 + 15 >= n_sink);
         onmask |= on ? 1 << kt : 0;
       }
       onmask = __builtin_amdgcn_readfirstlane(onmask);
@@ -420,15 +477,17 @@ __device__ __forceinline__ void swa_tiles(const T* __restrict__ q, const T* __re
           for (int kt = 0; kt < KB / 16; ++kt) {
             if (!((onmask >> kt) & 1)) continue;
             const int k0 = kb0 + 16 * kt;
+            // (RING window blocks may start below n_sink: those keys belong
+            // to the sink phase)
             const bool full = SINK ? (k0 + 15 <= q0 && k0 + 15 < kend)
-                                   : (k0 + 15 <= q0 && k0 > q0 + 15 - window);
+                                   : (k0 + 15 <= q0 && k0 > q0 + 15 - window && (!RING || k0 >= n_sink));
             if (!full) {
               const int key0 = k0 + 4 * lg;
               const int d0 = t - key0;
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const bool valid = SINK ? ((d0 - i >= 0) & (key0 + i < kend))
-                                        : (unsigned)(d0 - i) < (unsigned)window;
+                                        : ((unsigned)(d0 - i) < (unsigned)window) & (!RING || key0 + i >= n_sink);
                 sacc[kt][nq][i] = valid ? sacc[kt][nq][i] : -INFINITY;
               }
             }
@@ -500,7 +559,7 @@ __device__ __forceinline__ void swa_tiles(const T* __restrict__ q, const T* __re
         }
       }
 
-      if (!deep) {
+      if (!deep && !RING) {
         if (has_next) commit(Ks(buf ^ 1), VTs(buf ^ 1), pks[0], pvs[0], nks[0]);
         lds_barrier();
       }
@@ -558,6 +617,14 @@ __device__ __forceinline__ void swa_tiles(const T* __restrict__ q, const T* __re
         if (addl) val += f32x4{static_cast<float>(raw[nq][dt][0]), static_cast<float>(raw[nq][dt][1]),
                                static_cast<float>(raw[nq][dt][2]), static_cast<float>(raw[nq][dt][3])};
         store4(orow + 16 * dt + 4 * lg, val);
+      }
+    }
+    if constexpr (RING) {
+      // the next tile's new block replaces the one only this tile needed
+      if (newblk) {
+        lds_barrier();
+        commit(DKs(nb % 3), DVTs(nb % 3), pks[0], pvs[0], nks[0]);
+        lds_barrier();
       }
     }
   }
