@@ -94,7 +94,7 @@ hipError_t launch_swa_t(const PrefillArgs& p, int add_from, hipStream_t s) {
       const int groups4 = p.H / 4;
       int TPW = 1;
       while (TPW < kRingTiles && (size_t)((nt64 + 2 * TPW - 1) / (2 * TPW)) * groups4 * p.B >= 1024) TPW *= 2;
-      if (TPW >= 4) {
+      if (std::min(TPW, nt64) >= 4) {
         const dim3 grid((nt64 + TPW - 1) / TPW, groups4, p.B);
         hipLaunchKernelGGL((swa_ring_kernel<T, D>), grid, dim3(512), 0, s, (const T*)p.q, (const T*)p.k,
                            (const T*)p.v, (T*)p.o, p.T, p.H, p.Hkv, TPW, p.n_sink, p.window, add_from,

@@ -285,14 +285,15 @@ def test_many_chain_full_wave_scan():
         assert_close(f64(st[bsel][:, heads]), S, False, "state")
 
 
-@pytest.mark.parametrize("n_sink,window,flags", [(8, 120, ALL | gl.WRITE_STATE), (0, 129, ALL),
-                                                  (64, 64, ALL), (3, 20, gl.BRANCH_SOFTMAX)])
-def test_resident_key_blocks(n_sink, window, flags):
+@pytest.mark.parametrize("n_sink,window,flags,T", [(8, 120, ALL | gl.WRITE_STATE, 520), (0, 129, ALL, 520),
+                                                    (64, 64, ALL, 520), (3, 20, gl.BRANCH_SOFTMAX, 520),
+                                                    (0, 1, ALL, 257), (64, 65, ALL | gl.WRITE_STATE, 300)])
+def test_resident_key_blocks(n_sink, window, flags, T):
     """Many sequences and groups of four query heads per KV head: the softmax
     launch keeps its key blocks resident across a workgroup's consecutive
-    64-row tiles (here nine per workgroup, the last one ragged); sampled
+    64-row tiles (nine, or five, per workgroup, the last one ragged); sampled
     (sequence, head) chains against the oracle."""
-    w = small(B=256, H=16, Hkv=4, d=128, T=520, n_sink=n_sink, window=window, sigma=1.0)
+    w = small(B=256, H=16, Hkv=4, d=128, T=T, n_sink=n_sink, window=window, sigma=1.0)
     inp = to_dev(make_prefill_inputs(w, seed=window))
     o, st = run_prefill(inp, w, flags=flags)
     for bsel, heads in (([0], [0, 3]), ([77], [5, 6]), ([255], [12, 15])):
