@@ -12,7 +12,9 @@
 // KV head, run of TPW consecutive tiles of QT query rows); each wave owns 32
 // query rows of one head.  The next key block is fetched into registers
 // (16-byte loads; unguarded when the block is whole) while the current one
-// is used from LDS (two LDS buffers), across tiles.
+// is used from LDS (two LDS buffers), across tiles.  At short budgets with
+// many tiles per workgroup (swa_ring_kernel) the key blocks instead stay
+// resident in LDS across 64-row tiles and each tile stages one new block.
 // Keys are visited in two phases, the sinks [0, n_sink) and then the window
 // [max(n_sink, t0 - window + 1), t_end), so a key in both ranges is counted
 // once.  64-key blocks of K (row-major) and V (transposed) are staged in LDS
