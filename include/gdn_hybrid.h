@@ -258,7 +258,8 @@ int gdn_hybrid_cache_from_prefill(const void* k, const void* v,
  *   q, q_out   [B, T, H, d]    dtype      channel c = h * d + i
  *   k, v, k_out, v_out [B, T, Hkv, d] dtype
  *   wq [H*d, ksize], wk [Hkv*d, ksize], wv [Hkv*d, ksize] fp32
- * Supported: d in {64, 128}; 1 <= ksize <= 8; rope_theta > 0; pos0 >= 0.
+ * Supported: d in {64, 128}; 1 <= ksize <= 8; rope_theta > 0; pos0 >= 0;
+ * B <= 65535 and T <= 65535 * 64 (grid dimensions), else GDN_EUNSUPPORTED.
  */
 int shortconv_qkv(const void* q, const void* k, const void* v,
                   const float* wq, const float* wk, const float* wv,

@@ -201,6 +201,8 @@ int shortconv_qkv(const void* q, const void* k, const void* v, const float* wq, 
   if (flags < 0 || flags > 3) return GDN_EINVAL;
   if ((flags & GDN_ROPE) && !(rope_theta > 0.f)) return GDN_EINVAL;
   if (pos0 < 0 || (int64_t)pos0 + T >= (int64_t)1 << 30) return GDN_EINVAL;
+  // the sequence and the 64-token tile are grid dimensions
+  if (B > 65535 || (T + 63) / 64 > 65535) return GDN_EUNSUPPORTED;
   if (T == 0) return GDN_OK;
   gdn::ShortConvArgs p{q, k, v, wq, wk, wv, q_out, k_out, v_out, B, T, H, Hkv, d, ksize,
                        rope_theta, pos0, flags, dtype == GDN_BF16};

@@ -9,7 +9,8 @@
 // token; rotate-half RoPE with inv_freq_j = theta^(-2j/d) at position pos0 + t
 // on q and k; L2 norm x / sqrt(sum x^2 + 1e-6) on q and k.
 //
-// Work split: one wave per (sequence, head, 64-token tile).  Lane j owns the
+// Work split: one wave per (sequence, head, 64-token tile); consecutive
+// workgroups take consecutive heads of the same tile.  Lane j owns the
 // RoPE pair (j, j + d/2) of its head, so rotation, the 8-tap sliding window
 // over time and the per-head norm (a register-only reduction over the head's
 // lanes) never leave registers; the tile re-reads a 7-token causal halo.  The rotation
@@ -55,20 +56,21 @@ constexpr int kTT = 64;      // tokens per wave
 constexpr int kMaxKs = 8;
 constexpr int kLB = 16;      // tokens whose loads are issued together
 
-template <class T, int D>
+template <class T, int D, bool ROPE, bool NORM>
 __global__ __launch_bounds__(256) void shortconv_kernel(const T* __restrict__ x, const float* __restrict__ w,
                                                         T* __restrict__ y, int T_, int nh, int ks,
-                                                        float theta, int pos0, int rope, int norm) {
+                                                        float theta, int pos0) {
   constexpr int LPH = D / 2;        // lanes per head
   constexpr int HW = 64 / LPH;      // heads per wave
+  constexpr int NH = kMaxKs - 1;    // most halo tokens
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  const int unit = blockIdx.y * 4 + wv;
+  const int unit = blockIdx.x * 4 + wv;
   const int h = unit * HW + lane / LPH;
   if (h >= nh) return;              // whole head groups leave together
   const int j = lane % LPH;
   const int bi = blockIdx.z;
-  const int t0 = blockIdx.x * kTT;
+  const int t0 = blockIdx.y * kTT;
   const int t1 = min(t0 + kTT, T_);
   const int c1 = h * D + j;
   const int c2 = c1 + LPH;
@@ -86,9 +88,9 @@ __global__ __launch_bounds__(256) void shortconv_kernel(const T* __restrict__ x,
     win2[jj] = 0.f;
   }
 
-  const int ts = max(0, t0 - (ks - 1));
+  const int ts = max(0, t0 - (ks - 1));   // first halo token
   float cs = 1.f, sn = 0.f, cf = 1.f, sf = 0.f;
-  if (rope) {
+  if constexpr (ROPE) {
     const double f = exp(-(2.0 * j / D) * log((double)theta));
     const double ang = (double)(pos0 + ts) * f;
     const double twopi = 6.283185307179586476925;
@@ -102,54 +104,86 @@ __global__ __launch_bounds__(256) void shortconv_kernel(const T* __restrict__ x,
   const size_t row = (size_t)nh * D;
   const T* xb = x + (size_t)bi * T_ * row;
   T* yb = y + (size_t)bi * T_ * row;
-  // the tile's tokens in blocks of kLB: a block's loads are issued together
-  // (indices clamped into the tile), so the wave waits for memory once per
-  // block instead of once per token
-  for (int tb = ts; tb < t1; tb += kLB) {
-    T xr1[kLB], xr2[kLB];
+  // one token into the window: RoPE at the running angle, then the shift
+  auto push = [&](float x1, float x2) {
+    if constexpr (ROPE) {
+      const float r1 = x1 * cs - x2 * sn;
+      const float r2 = x2 * cs + x1 * sn;
+      x1 = r1;
+      x2 = r2;
+      const float cn = cs * cf - sn * sf;
+      sn = sn * cf + cs * sf;
+      cs = cn;
+    }
+#pragma unroll
+    for (int jj = kMaxKs - 1; jj > 0; --jj) {
+      win1[jj] = win1[jj - 1];
+      win2[jj] = win2[jj - 1];
+    }
+    win1[0] = x1;
+    win2[0] = x2;
+  };
+  // the convolution at the newest token (and the per-head norm), stored
+  auto emit = [&](int t) {
+    float y1 = 0.f, y2 = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < kMaxKs; ++jj) {
+      y1 += w1[jj] * win1[jj];
+      y2 += w2[jj] * win2[jj];
+    }
+    if constexpr (NORM) {
+      const float ss = head_sum<LPH>(y1 * y1 + y2 * y2);
+      const float inv = 1.0f / sqrtf(ss + 1e-6f);
+      y1 *= inv;
+      y2 *= inv;
+    }
+    yb[(size_t)t * row + c1] = from_f32<T>(y1);
+    yb[(size_t)t * row + c2] = from_f32<T>(y2);
+  };
+
+  // halo tokens ts .. t0-1 and the first block are loaded together; loads
+  // are clamped into [ts, t1) (the extra values are never pushed)
+  T hr1[NH], hr2[NH];
+#pragma unroll
+  for (int u = 0; u < NH; ++u) {
+    const size_t tt = (size_t)min(ts + u, t1 - 1);
+    hr1[u] = xb[tt * row + c1];
+    hr2[u] = xb[tt * row + c2];
+  }
+  // the tile's tokens in blocks of kLB with straight-line bodies (every
+  // token of a full block is stored), so that the tokens' reductions overlap;
+  // the loads of a block are issued together
+  int t = t0;
+  T xr1[kLB], xr2[kLB];
+  auto load_block = [&](int tb) {
 #pragma unroll
     for (int u = 0; u < kLB; ++u) {
       const size_t tt = (size_t)min(tb + u, t1 - 1);
       xr1[u] = xb[tt * row + c1];
       xr2[u] = xb[tt * row + c2];
     }
+  };
+  load_block(t0);
+#pragma unroll
+  for (int u = 0; u < NH; ++u)
+    if (u < t0 - ts) push(to_f32(hr1[u]), to_f32(hr2[u]));
+  for (; t + kLB <= t1; t += kLB) {
+    if (t > t0) load_block(t);
 #pragma unroll
     for (int u = 0; u < kLB; ++u) {
-      const int t = tb + u;
-      if (t >= t1) break;
-      float x1 = to_f32(xr1[u]);
-      float x2 = to_f32(xr2[u]);
-      if (rope) {
-        const float r1 = x1 * cs - x2 * sn;
-        const float r2 = x2 * cs + x1 * sn;
-        x1 = r1;
-        x2 = r2;
-        const float cn = cs * cf - sn * sf;
-        sn = sn * cf + cs * sf;
-        cs = cn;
-      }
+      push(to_f32(xr1[u]), to_f32(xr2[u]));
+      emit(t + u);
+    }
+  }
+  // ragged end of the sequence: the remaining tokens one by one
+  if (t < t1) {
+    if (t > t0) load_block(t);
 #pragma unroll
-      for (int jj = kMaxKs - 1; jj > 0; --jj) {
-        win1[jj] = win1[jj - 1];
-        win2[jj] = win2[jj - 1];
+    for (int u = 0; u < kLB; ++u) {
+      if (t + u < t1) {
+        push(to_f32(xr1[u]), to_f32(xr2[u]));
+        emit(t + u);
       }
-      win1[0] = x1;
-      win2[0] = x2;
-      if (t < t0) continue;
-      float y1 = 0.f, y2 = 0.f;
-#pragma unroll
-      for (int jj = 0; jj < kMaxKs; ++jj) {
-        y1 += w1[jj] * win1[jj];
-        y2 += w2[jj] * win2[jj];
-      }
-      if (norm) {
-        const float ss = head_sum<LPH>(y1 * y1 + y2 * y2);
-        const float inv = 1.0f / sqrtf(ss + 1e-6f);
-        y1 *= inv;
-        y2 *= inv;
-      }
-      yb[(size_t)t * row + c1] = from_f32<T>(y1);
-      yb[(size_t)t * row + c2] = from_f32<T>(y2);
     }
   }
 }
@@ -159,9 +193,18 @@ hipError_t launch_one(const void* x, const float* w, void* y, const ShortConvArg
                       int rope, int norm, hipStream_t s) {
   constexpr int HW = 128 / D;
   const int units = (nh + HW - 1) / HW;
-  const dim3 grid((p.T + kTT - 1) / kTT, (units + 3) / 4, p.B);
-  hipLaunchKernelGGL((shortconv_kernel<T, D>), grid, dim3(256), 0, s, (const T*)x, w, (T*)y, p.T,
-                     nh, p.ksize, p.rope_theta, p.pos0, rope, norm);
+  // head groups vary fastest, so the workgroups in flight cover whole token
+  // rows (every head of the same 64 tokens) rather than one head's column
+  const dim3 grid((units + 3) / 4, (p.T + kTT - 1) / kTT, p.B);
+#define GDN_SC_LAUNCH(R, N)                                                                        \
+  hipLaunchKernelGGL((shortconv_kernel<T, D, R, N>), grid, dim3(256), 0, s, (const T*)x, w, (T*)y, p.T, \
+                     nh, p.ksize, p.rope_theta, p.pos0)
+  if (rope) {
+    if (norm) GDN_SC_LAUNCH(true, true); else GDN_SC_LAUNCH(true, false);
+  } else {
+    if (norm) GDN_SC_LAUNCH(false, true); else GDN_SC_LAUNCH(false, false);
+  }
+#undef GDN_SC_LAUNCH
   return hipGetLastError();
 }
 

@@ -197,6 +197,8 @@ def test_shortconv_validation(lib):
     assert shortconv(lib, flags=4) == EINVAL
     assert shortconv(lib, pos0=-1) == EINVAL
     assert shortconv(lib, T=0) == OK
+    assert shortconv(lib, T=65535 * 64 + 1, H=1, Hkv=1) == EUNSUP   # 64-token tiles: a grid dimension
+    assert shortconv(lib, B=65536, T=1, H=1, Hkv=1) == EUNSUP
 
 
 def test_cache_fill_validation(lib):
