@@ -344,7 +344,8 @@ def test_decode_largest_group_and_window_one(n_sink, window, pos0):
     (1, 4, 1, 128, 300, "bf16", "gdn"),     # few chains: one launch, linked softmax tiles
     (4, 32, 8, 128, 200, "bf16", "gdn"),    # many chains: preparation + scan, then softmax
     (2, 4, 2, 128, 260, "bf16", "gla"),
-    (1, 2, 2, 64, 150, "f32", "gdn")])
+    (1, 2, 2, 64, 150, "f32", "gdn"),
+    (256, 16, 4, 128, 520, "bf16", "gdn")])  # softmax with resident key blocks
 def test_weighted_prefill(B, H, Hkv, d, T, dtype, update):
     w = small(B=B, H=H, Hkv=Hkv, d=d, T=T, dtype=dtype, update=update)
     inp = to_dev(make_prefill_inputs(w, seed=B * 100 + T))
