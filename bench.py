@@ -1,42 +1,47 @@
 #!/usr/bin/env python3
 """Benchmark of the hybrid GDN + sink/SWA layer on one MI355X.
 
-Headline (the printed JSON line): prefill throughput of one layer with the
-LLaMA3.1-8B attention shape (B=1, 32 query / 8 KV heads, d=128, T=4096,
-budget 8 sinks + 56 window, bf16 inputs, fp32 state).  One step = one
-layer pass over the sequence: one ABI call with both branches, which is one
-kernel launch (chunk preparation, chunked GDN state scan and the sink+SWA
-softmax tiles cooperating through per-chunk flags); HIP events around it on
-its stream time it.  The same layer as two calls (linear, then softmax
-adding its branch) is timed too, for reference.  Inputs are resident in HBM
-before the timed region.
+Headline (the printed JSON line): prefill throughput of one layer on the
+long-context workload, the largest one that fits one GPU: B=8 sequences of
+T=32768 tokens, 32 query / 8 KV heads, d=128, budget 8 sinks + 120 window,
+bf16 q/k/v/o, fp32 gates and state, final states written.  One step = one
+layer pass over the batch: one ABI call with both branches and the state
+output.  K steps are timed between device synchronisations (ms_per_step,
+value = B*T / that time); each step is also bracketed by HIP events on its
+stream (median reported).  Inputs are resident in HBM before timing.
 
-Secondary figures in "also": decode steps/s (B=256, 1000 consecutive steps),
-long-context prefill (B=8, T=32768, budget 128, final state out), the
-Qwen3-32B-shaped full stack (short conv + GDN, short conv + GLA, budget 896)
-and its serving step (short-conv decode feeding the layer's decode step).
+Roofline: the layer's call is split into its branch calls (the linear branch
+with the state, then the softmax branch adding onto it), each timed with
+HIP events on the stream the kernels run on; the slowest is the dominant
+kernel launch, whose algorithmic FLOPs divided by its median duration is
+compared with the bf16 dense MFMA peak (2.5 PFLOP/s).  HBM traffic comes
+from the committed rocprofv3 counter readings (profiles/hbm_traffic.txt)
+while the kernel sources are the ones measured, else null.
 
-Roofline: algorithmic FLOPs (or bytes) per launch of the dominant kernel
-divided by its mean event-timed duration, against the MI355X peaks (bf16
-dense MFMA 2.5 PFLOP/s, HBM 8 TB/s); traffic from the committed rocprofv3
-counter reading when it was taken on the current kernel sources.
-cpu_baseline: the fp64 NumPy oracle timed on this host over the whole layer,
-one thread, repeated to at least 10 s.
+cpu_baseline: the fp64 NumPy oracle, timed on this host before the GPU is
+touched, on a bounded sample of the same workload, with its (sequence,
+query head) chains spread over a pool of worker processes (one per allowed
+core, at most 16).
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--only main|decode|...]
+"also" carries the other workloads, each with its own roofline and oracle
+baseline: the tiny fp32 layer, the LLaMA3.1-8B-shaped layer (T=4096), decode
+(B=256, 1000 consecutive steps, HBM roofline), the Qwen3-32B-shaped stack
+(short conv + GDN, short conv + GLA, budget 896) and its serving step.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--only headline|...]
 """
 
 from __future__ import annotations
 
 import argparse
 import json
+import multiprocessing as mp
 import os
 import platform
 import sys
 import time
 
 import numpy as np
-import torch
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -44,38 +49,53 @@ sys.path.insert(0, ROOT)
 PEAK_BF16 = 2.5e15      # dense bf16 MFMA FLOP/s
 PEAK_HBM = 8.0e12       # bytes/s
 CHUNK = 64
+HEADLINE = "longctx_b8_t32768"
 
+
+# ------------------------------------------------------- algorithmic work
 
 def gdn_flops(w, T=None):
-    """Algorithmic FLOPs of the chunked GDN linear branch (one layer)."""
+    """Algorithmic FLOPs of the chunked GDN linear branch (one layer):
+    6 dk dv + 2C(3dk + 2dv) per stream token and query head."""
     T = w.T if T is None else T
     stream = max(0, T - w.budget)
     d = w.d
-    per = 6 * d * d + 2 * CHUNK * (3 * d + 2 * d)
-    return w.B * w.H * stream * per
+    return w.B * w.H * stream * (6 * d * d + 2 * CHUNK * (3 * d + 2 * d))
 
 
 def gla_flops(w, T=None):
+    """GLA linear branch: 4 dk dv + 2C(dk + dv) per stream token and query head."""
     T = w.T if T is None else T
     stream = max(0, T - w.budget)
     d = w.d
-    per = 4 * d * d + 2 * CHUNK * (d + d)
-    return w.B * w.H * stream * per
+    return w.B * w.H * stream * (4 * d * d + 2 * CHUNK * (d + d))
+
+
+def linear_flops(w):
+    return gdn_flops(w) if w.update == "gdn" else gla_flops(w)
 
 
 def swa_flops(w, T=None):
+    """Softmax branch: 4 min(t+1, N) d per query row and head."""
     T = w.T if T is None else T
     t = np.arange(T)
     return w.B * w.H * int(np.sum(4 * np.minimum(t + 1, w.budget))) * w.d
 
 
-def prefill_bytes(w, elt=2, state=False):
+def prefill_bytes(w):
+    """One read of q, k, v, a, b and one write of o (and the state)."""
+    elt = 4 if w.dtype == "f32" else 2
     d = w.d
     b = w.B * w.T * (w.H * d * elt * 2 + 2 * w.Hkv * d * elt)      # q, o, k, v
     b += w.B * w.T * w.H * 4 * (d if w.update == "gla" else 2)     # gates
-    if state:
+    if w.write_state:
         b += w.B * w.H * d * d * 4
     return b
+
+
+def shortconv_bytes(w):
+    """Short conv: raw q, k, v read once, prepared q, k, v written once."""
+    return 2 * 2 * w.B * w.T * (w.H + 2 * w.Hkv) * w.d
 
 
 def decode_bytes(w, elt=2):
@@ -90,157 +110,64 @@ def decode_bytes(w, elt=2):
     return b
 
 
-def timed(fn, steps, warmup):
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        fn()
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
+def shortconv_decode_bytes(w, elt=2):
+    """One short-conv decode step: raw q, k, v in and prepared out, the conv
+    weights, the ks-1 history rows read and one row written (fp32)."""
+    C = (w.H + 2 * w.Hkv) * w.d
+    ks = w.conv_ks
+    return w.B * C * elt * 2 + C * ks * 4 + w.B * C * 4 * ks
 
 
-# ------------------------------------------------------------- headline
+# ------------------------------------------------------------- kernels
 
-def bench_main(steps, warmup, split=True):
-    import swa_chunked_gated_amd as gl
-    from workloads import WORKLOADS, make_prefill_inputs
-
-    w = WORKLOADS["llama8b_t4096"]
-    inp = make_prefill_inputs(w, device="cuda")
-    o = torch.empty(w.B, w.T, w.H, w.d, dtype=torch.bfloat16, device="cuda")
-    q, k, v, a, b = (inp[x] for x in ("q", "k", "v", "a", "b"))
-    both = gl.BRANCH_LINEAR | gl.BRANCH_SOFTMAX
-    ws = torch.empty(gl.prefill_workspace_bytes(w.B, w.T, w.H, w.Hkv, w.d, w.n_sink, w.window,
-                                                torch.bfloat16, flags=both),
-                     dtype=torch.uint8, device="cuda")
-    f_lin, f_swa = gdn_flops(w), swa_flops(w)
-
-    # the layer: one call with both branches (one launch: preparation, state
-    # scan and softmax tiles in the same kernel), events around it on its stream
-    n = steps + warmup
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
-
-    def step(i):
-        ev[i][0].record()
-        gl.hybrid_prefill(q, k, v, a, b, w.n_sink, w.window, flags=both, o=o, workspace=ws)
-        ev[i][1].record()
-
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(warmup, n):
-        step(i)
-    torch.cuda.synchronize()
-    sec = (time.perf_counter() - t0) / steps
-    layer_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(warmup, n)]))
-
-    # for reference, each branch alone: the linear call, then the softmax call
-    # adding its branch (the two-launch form of the same layer)
-    m_split = max(10, steps // 4)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(m_split + 3)]
-    for i in range(m_split + 3 if split else 0):
-        e = evs[i]
-        e[0].record()
-        gl.hybrid_prefill(q, k, v, a, b, w.n_sink, w.window, flags=gl.BRANCH_LINEAR, o=o, workspace=ws)
-        e[1].record()
-        gl.hybrid_prefill(q, k, v, a, b, w.n_sink, w.window, flags=gl.BRANCH_SOFTMAX | gl.ACCUMULATE, o=o)
-        e[2].record()
-    torch.cuda.synchronize()
-    lin_ms = float(np.mean([evs[i][0].elapsed_time(evs[i][1]) for i in range(3, m_split + 3)])) if split else None
-    swa_ms = float(np.mean([evs[i][1].elapsed_time(evs[i][2]) for i in range(3, m_split + 3)])) if split else None
-
-    achieved = (f_lin + f_swa) / (layer_ms * 1e-3)
-    res = {
-        "w": w, "sec": sec,
-        "kernels_ms": {LAYER_KERNEL: layer_ms,
-                       "two-launch reference": {LINEAR_KERNELS: lin_ms, "swa_kernel": swa_ms}},
-        "roofline": {
-            "kernel": LAYER_KERNEL, "bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,
-            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16,
-            "traffic": stored_traffic(LAYER_KERNEL, w.name, LAYER_SOURCES),
-            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-            "algorithmic_flops_per_launch": f_lin + f_swa,
-            "algorithmic_bytes_per_launch": prefill_bytes(w),
-        },
-        "layer_frac_mfma": (f_lin + f_swa) / sec / PEAK_BF16,
-        "inputs": inp,
-    }
-    return res
+# Kernels each call launches, by workload (the library's launch choice:
+# bf16 GDN with B*H*d/64 < 256 runs preparation, scan and, with both
+# branches, the softmax tiles as one launch; otherwise the light
+# preparation, then the many-chain scan; the softmax branch keeps its key
+# blocks resident when every workgroup walks at least four 64-row tiles).
+CALL_KERNELS = {
+    "longctx_b8_t32768": {"linear": "gdn_prep_kernel+linear_chunk_kernel",
+                          "softmax": "swa_ring_kernel"},
+    "llama8b_t4096": {"layer": "gdn_scan_full_kernel", "linear": "gdn_scan_full_kernel",
+                      "softmax": "swa_kernel"},
+    "tiny_fp32": {"linear": "gdn_prep_kernel+linear_chunk_kernel", "softmax": "swa_kernel"},
+    "qwen32b_t8192_gdn": {"shortconv": "shortconv_kernel",
+                          "linear": "gdn_prep_kernel+linear_chunk_kernel", "softmax": "swa_kernel"},
+    "qwen32b_t8192_gla": {"shortconv": "shortconv_kernel",
+                          "linear": "gla_prep_kernel+linear_chunk_kernel", "softmax": "swa_kernel"},
+}
+CSRC = "swa_chunked_gated_amd/csrc/"
+KERNEL_SOURCES = {
+    "gdn_prep_kernel+linear_chunk_kernel": ("gdn_prep.h", "gdn_prep.hip", "gdn_scan_full.hip",
+                                            "linear_chunk.hip", "common.h"),
+    "gla_prep_kernel+linear_chunk_kernel": ("gla_prep.hip", "linear_chunk.hip", "common.h"),
+    "gdn_scan_full_kernel": ("gdn_prep.h", "gdn_scan_full.hip", "swa_tile.h", "common.h"),
+    "swa_ring_kernel": ("swa.hip", "swa_tile.h", "common.h"),
+    "swa_kernel": ("swa.hip", "swa_tile.h", "common.h"),
+    "shortconv_kernel": ("shortconv.hip", "common.h"),
+    "decode_step_kernel+decode_commit_kernel": ("decode.hip", "common.h"),
+}
 
 
-def cpu_baseline(inp, w, min_seconds=10.0, max_reps=6):
-    """fp64 oracle over the whole layer (all heads, whole T), one thread,
-    repeated until at least `min_seconds` of CPU work; mean time per layer."""
-    from threadpoolctl import threadpool_limits
-    from oracle import hybrid as O
-
-    f = {x: inp[x].double().cpu().numpy() for x in ("q", "k", "v", "a", "b")}
-    times = []
-    with threadpool_limits(1):
-        while sum(times) < min_seconds and len(times) < max_reps:
-            t0 = time.perf_counter()
-            O.hybrid_prefill(f["q"], f["k"], f["v"], f["a"], f["b"], w.n_sink, w.window, flags=3)
-            times.append(time.perf_counter() - t0)
-    per = sum(times) / len(times)
-    return {
-        "value": w.B * w.T / per, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-        "sample": f"whole layer prefill (B={w.B}, T={w.T}, {w.H} query / {w.Hkv} KV heads, "
-                  f"both branches), fp64 NumPy oracle on one thread, {len(times)} repetitions, "
-                  f"{sum(times):.1f} s total, {per:.2f} s per layer",
-        "cpu": _cpu_model(),
-        "host_cores_allowed": len(os.sched_getaffinity(0)),
-    }
-
-
-def _cpu_model():
-    try:
-        with open("/proc/cpuinfo") as fh:
-            for line in fh:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
-    except OSError:
-        pass
-    return platform.processor() or platform.machine()
-
-
-def kernel_sources_sha256(files):
+def kernel_sources_sha256(kernel):
     """Digest of the sources a kernel is compiled from; a stored counter
     reading only applies while this digest is unchanged."""
     import hashlib
     h = hashlib.sha256()
-    for f in files:
-        with open(os.path.join(ROOT, f), "rb") as fh:
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, CSRC + f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-LINEAR_SOURCES = ("swa_chunked_gated_amd/csrc/gdn_prep.h", "swa_chunked_gated_amd/csrc/gdn_prep.hip",
-                  "swa_chunked_gated_amd/csrc/gdn_scan_full.hip", "swa_chunked_gated_amd/csrc/linear_chunk.hip",
-                  "swa_chunked_gated_amd/csrc/common.h")
-# the linear launch of the LLaMA-shaped layer (32 chains): preparation and
-# state scan in one kernel; with both branches the softmax tiles join it
-LINEAR_KERNELS = "gdn_scan_full_kernel"
-LAYER_KERNEL = "gdn_scan_full_kernel"
-LAYER_SOURCES = ("swa_chunked_gated_amd/csrc/gdn_prep.h", "swa_chunked_gated_amd/csrc/gdn_scan_full.hip",
-                 "swa_chunked_gated_amd/csrc/swa_tile.h", "swa_chunked_gated_amd/csrc/common.h")
-SWA_SOURCES = ("swa_chunked_gated_amd/csrc/swa.hip", "swa_chunked_gated_amd/csrc/swa_tile.h",
-               "swa_chunked_gated_amd/csrc/common.h")
-DECODE_SOURCES = ("swa_chunked_gated_amd/csrc/decode.hip", "swa_chunked_gated_amd/csrc/common.h")
-# one decode step is two launches: both branches and the state update, then the cache commit
-DECODE_KERNELS = "decode_step_kernel+decode_commit_kernel"
-
-
-def stored_traffic(kernel, workload, sources):
+def stored_traffic(kernel, workload):
     """HBM bytes per launch from profiles/hbm_traffic.txt: rocprofv3 FETCH_SIZE
     and WRITE_SIZE (KiB per dispatch) times the factors a plain device copy of
     known size gives.  None when no reading exists for the current sources."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
-    if not os.path.exists(path):
+    if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
         return None
-    digest = kernel_sources_sha256(sources)
+    digest = kernel_sources_sha256(kernel)
     fac = {}
     rows = []
     with open(path) as fh:
@@ -259,9 +186,247 @@ def stored_traffic(kernel, workload, sources):
     return None
 
 
-# ------------------------------------------------------------ secondary
+# ----------------------------------------------------- oracle (CPU) leg
+
+_CPU = {}   # inputs of the oracle sample, inherited by the forked workers
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def _oracle_prefill_head(h):
+    """Oracle layer (both branches, state) of query head h of the sample."""
+    from oracle import hybrid as O
+    w, f = _CPU["w"], _CPU["f"]
+    G = w.H // w.Hkv
+    g = h // G
+    if w.shortconv:
+        q, k, v = O.shortconv_qkv(f["q"][:, :, h:h + 1], f["k"][:, :, g:g + 1], f["v"][:, :, g:g + 1],
+                                  f["wq"].reshape(w.H, w.d, -1)[h], f["wk"].reshape(w.Hkv, w.d, -1)[g],
+                                  f["wv"].reshape(w.Hkv, w.d, -1)[g], w.rope_theta, 0, flags=3)
+    else:
+        q, k, v = f["q"][:, :, h:h + 1], f["k"][:, :, g:g + 1], f["v"][:, :, g:g + 1]
+    b = f["b"][:, :, h:h + 1] if w.update == "gdn" else None
+    O.hybrid_prefill(q, k, v, f["a"][:, :, h:h + 1], b, w.n_sink, w.window, update=w.update)
+    return h
+
+
+def _oracle_decode_seqs(sl):
+    """Oracle decode steps of the sample's sequences sl[0]:sl[1]."""
+    from oracle import hybrid as O
+    w, f = _CPU["w"], _CPU["f"]
+    s0, s1 = sl
+    st = [f[x][s0:s1] for x in ("state", "k_cache", "v_cache", "a_cache", "b_cache", "pos")]
+    for s in range(_CPU["steps"]):
+        res = O.decode_step(*(f[x][s, s0:s1] for x in ("q", "k", "v", "a", "b")), *st,
+                            w.n_sink, w.window, update=w.update)
+        st = list(res[1:])
+    return s1 - s0
+
+
+def cpu_baseline(name, cores, T_sample=None, heads=None, steps=None):
+    """The oracle on a bounded sample of workload `name`: prefill runs
+    sequence 0 (first T_sample tokens, the listed query heads), one task per
+    head; decode runs `steps` steps of every sequence, one task per slice of
+    sequences.  Rate in the workload's unit (tokens/s; steps/s)."""
+    import torch
+    from workloads import WORKLOADS, make_decode_inputs, make_prefill_inputs
+
+    w = WORKLOADS[name]
+    _CPU.clear()
+    _CPU["w"] = w
+    decode = w.T == 0
+    if decode:
+        inp = make_decode_inputs(w, steps=steps)
+        _CPU["steps"] = steps
+    else:
+        inp = make_prefill_inputs(w, T=T_sample, B=1)
+    _CPU["f"] = {x: (t.to(torch.float64).numpy() if t.is_floating_point() else t.numpy())
+                 for x, t in inp.items()}
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores) as pool:
+        pool.map(abs, range(cores))          # workers started before timing
+        t0 = time.perf_counter()
+        if decode:
+            per = max(1, w.B // (4 * cores))
+            tasks = [(s, min(s + per, w.B)) for s in range(0, w.B, per)]
+            pool.map(_oracle_decode_seqs, tasks, chunksize=1)
+        else:
+            pool.map(_oracle_prefill_head, list(heads), chunksize=1)
+        wall = time.perf_counter() - t0
+    _CPU.clear()
+    res = {"kind": "oracle", "cores": cores, "cpu": _cpu_model(),
+           "host_cores_allowed": len(os.sched_getaffinity(0)), "seconds": wall}
+    if decode:
+        res.update(value=steps / wall, unit="steps/s",
+                   sample=f"{steps} consecutive decode steps of all {w.B} sequences x {w.H} heads "
+                          f"(fp64 NumPy oracle, {len(tasks)} tasks of sequences over {cores} worker "
+                          f"processes), {wall:.2f} s wall")
+    else:
+        conv = "short conv + " if w.shortconv else ""
+        res.update(value=T_sample / wall, unit="tokens/s",
+                   sample=f"sequence 0, tokens 0..{T_sample - 1}, {len(heads)} of {w.H} query heads"
+                          f"{'' if len(heads) == w.H else ' (rate scaled to all heads)'}: {conv}both "
+                          f"branches and the final state, fp64 NumPy oracle, one task per head over "
+                          f"{cores} worker processes, {wall:.2f} s wall")
+        if len(heads) != w.H:
+            res["value"] *= len(heads) / w.H
+    return res
+
+
+CPU_SAMPLES = {
+    # prefill: (tokens of sequence 0, query heads); decode: steps of the whole batch
+    "longctx_b8_t32768": dict(T_sample=8192, heads=range(32)),
+    "tiny_fp32": dict(T_sample=256, heads=range(2)),
+    "llama8b_t4096": dict(T_sample=4096, heads=range(32)),
+    "qwen32b_t8192_gdn": dict(T_sample=4096, heads=range(32)),
+    "qwen32b_t8192_gla": dict(T_sample=4096, heads=range(32)),
+    "decode_b256": dict(steps=20),
+}
+
+
+# ------------------------------------------------------------- GPU legs
+
+def _events(n):
+    import torch
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+
+def time_call(fn, reps, warmup):
+    """Median and mean event-timed duration (ms) of fn on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    ev = _events(reps)
+    for e in ev:
+        e[0].record()
+        fn()
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    return float(np.median(ms)), float(np.mean(ms))
+
+
+def bench_prefill(name, steps, warmup, parts=True):
+    """One workload's layer: K timed steps (wall clock between
+    synchronisations, and per-step events), then each call of the split
+    layer event-timed on its own for the roofline."""
+    import torch
+    import swa_chunked_gated_amd as gl
+    from workloads import WORKLOADS, make_prefill_inputs
+
+    w = WORKLOADS[name]
+    inp = make_prefill_inputs(w, device="cuda")
+    dt = w.torch_dtype
+    st_flag = gl.WRITE_STATE if w.write_state else 0
+    both = gl.BRANCH_LINEAR | gl.BRANCH_SOFTMAX | st_flag
+    o = torch.empty(w.B, w.T, w.H, w.d, dtype=dt, device="cuda")
+    st = torch.empty(w.B, w.H, w.d, w.d, dtype=torch.float32, device="cuda") if w.write_state else None
+    if w.shortconv:
+        qc, kc, vc = (torch.empty_like(inp[x]) for x in ("q", "k", "v"))
+    nws = gl.prefill_workspace_bytes(w.B, w.T, w.H, w.Hkv, w.d, w.n_sink, w.window, dt,
+                                     update=w.update, flags=both)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+
+    def conv():
+        gl.shortconv_qkv(inp["q"], inp["k"], inp["v"], inp["wq"], inp["wk"], inp["wv"],
+                         rope_theta=w.rope_theta, flags=gl.ROPE | gl.L2NORM, out=(qc, kc, vc))
+
+    def qkv():
+        return (qc, kc, vc) if w.shortconv else (inp["q"], inp["k"], inp["v"])
+
+    def layer():
+        if w.shortconv:
+            conv()
+        gl.hybrid_prefill(*qkv(), inp["a"], inp["b"], w.n_sink, w.window, update=w.update,
+                          flags=both, o=o, state_out=st, workspace=ws)
+
+    for _ in range(warmup):
+        layer()
+    ev = _events(steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record()
+        layer()
+        e[1].record()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    ev_ms = [a.elapsed_time(b) for a, b in ev]
+    f_lin, f_swa = linear_flops(w), swa_flops(w)
+    res = {"workload": name, "B": w.B, "T": w.T, "H": w.H, "Hkv": w.Hkv, "d": w.d,
+           "n_sink": w.n_sink, "window": w.window, "update": w.update, "dtype": w.dtype,
+           "state_out": w.write_state, "shortconv": w.shortconv,
+           "steps": steps, "ms_per_step": sec * 1e3, "tokens_per_s": w.B * w.T / sec,
+           "event_ms_median": float(np.median(ev_ms)), "event_ms_mean": float(np.mean(ev_ms)),
+           "algorithmic_gflop": (f_lin + f_swa) / 1e9,
+           "layer_frac_mfma": (f_lin + f_swa) / sec / PEAK_BF16}
+    if not parts:
+        return res
+
+    # the layer's calls one by one, each event-timed (median of >= 20)
+    reps = max(20, steps)
+    calls = {}
+    names = CALL_KERNELS[name]
+    if w.shortconv:
+        med, mean = time_call(conv, reps, 2)
+        calls["shortconv"] = {"kernel": names["shortconv"], "ms_median": med, "ms_mean": mean,
+                              "algorithmic_bytes": shortconv_bytes(w)}
+    if w.shortconv:
+        conv()
+    q, k, v = qkv()
+    lin_flags = gl.BRANCH_LINEAR | st_flag
+    med, mean = time_call(lambda: gl.hybrid_prefill(q, k, v, inp["a"], inp["b"], w.n_sink, w.window,
+                                                    update=w.update, flags=lin_flags, o=o,
+                                                    state_out=st, workspace=ws), reps, 2)
+    calls["linear"] = {"kernel": names["linear"], "ms_median": med, "ms_mean": mean,
+                       "algorithmic_flops": f_lin}
+    med, mean = time_call(lambda: gl.hybrid_prefill(q, k, v, inp["a"], inp["b"], w.n_sink, w.window,
+                                                    update=w.update,
+                                                    flags=gl.BRANCH_SOFTMAX | gl.ACCUMULATE, o=o),
+                          reps, 2)
+    calls["softmax"] = {"kernel": names["softmax"], "ms_median": med, "ms_mean": mean,
+                        "algorithmic_flops": f_swa}
+    res["calls"] = calls
+
+    # dominant kernel launch: the whole layer when it is one launch, else the
+    # slowest of the split calls' MFMA-bound launches
+    if "layer" in names:
+        kern, ms, flops = names["layer"], res["event_ms_median"], f_lin + f_swa
+        byts = prefill_bytes(w)
+    else:
+        key = max(("linear", "softmax"), key=lambda c: calls[c]["ms_median"])
+        kern, ms, flops = calls[key]["kernel"], calls[key]["ms_median"], calls[key]["algorithmic_flops"]
+        byts = None
+    achieved = flops / (ms * 1e-3)
+    res["roofline"] = {
+        "kernel": kern, "bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,
+        "unit": "TFLOP/s", "frac": achieved / PEAK_BF16,
+        "traffic": stored_traffic(kern, name),
+        "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+        "algorithmic_flops_per_launch": flops, "launch_ms_median": ms,
+    }
+    if byts is not None:
+        res["roofline"]["algorithmic_bytes_per_launch"] = byts
+    if w.shortconv:
+        c = calls["shortconv"]
+        gbs = c["algorithmic_bytes"] / (c["ms_median"] * 1e-3)
+        res["shortconv_roofline"] = {"kernel": c["kernel"], "bound": "hbm", "achieved": gbs / 1e9,
+                                     "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": gbs / PEAK_HBM,
+                                     "traffic": None}
+    return res
+
 
 def bench_decode(steps=1000, warmup=10):
+    import torch
     import swa_chunked_gated_amd as gl
     from workloads import WORKLOADS, make_decode_inputs
 
@@ -291,30 +456,24 @@ def bench_decode(steps=1000, warmup=10):
     sec = (time.perf_counter() - t0) / steps
     ev_ms = e0.elapsed_time(e1) / steps
     byts = decode_bytes(w)
+    kern = "decode_step_kernel+decode_commit_kernel"
     return {
         "workload": "decode_b256 (B=256, H=32, Hkv=8, d=128, cache 8+56, t=4096..5095)",
         "steps": steps, "ms_per_step": sec * 1e3, "steps_per_s": 1.0 / sec,
         "tokens_per_s": w.B / sec, "event_ms_per_step": ev_ms,
-        "roofline": {"kernel": DECODE_KERNELS, "bound": "hbm",
+        "roofline": {"kernel": kern, "bound": "hbm",
                      "achieved": byts / (ev_ms * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9,
                      "unit": "GB/s", "frac": byts / (ev_ms * 1e-3) / PEAK_HBM,
                      "algorithmic_bytes_per_step": byts,
-                     "traffic": stored_traffic(DECODE_KERNELS, w.name, DECODE_SOURCES)},
+                     "traffic": stored_traffic(kern, w.name)},
     }
-
-
-def shortconv_decode_bytes(w, elt=2):
-    """One short-conv decode step: raw q, k, v in and prepared out, the conv
-    weights, the ks-1 history rows read and one row written (fp32)."""
-    C = (w.H + 2 * w.Hkv) * w.d
-    ks = w.conv_ks
-    return w.B * C * elt * 2 + C * ks * 4 + w.B * C * 4 * ks
 
 
 def bench_qwen_decode(steps=200, warmup=10):
     """Serving step of the Qwen-shaped stack after its T=8192 prefill: the
     short-conv decode of the new raw q, k, v feeding the layer's decode step
     (budget 896), both on one stream; timed over consecutive steps."""
+    import torch
     import swa_chunked_gated_amd as gl
     from workloads import WORKLOADS, make_decode_inputs
 
@@ -361,6 +520,7 @@ def bench_qwen_decode(steps=200, warmup=10):
 def bench_copy(mib=1024, reps=3):
     """A plain device copy of known size: the reference the HBM byte counters
     (FETCH_SIZE, WRITE_SIZE) are scaled by, and the practical read+write roof."""
+    import torch
     n = mib * 2**20 // 4
     x = torch.randn(n, device="cuda")
     y = torch.empty_like(x)
@@ -377,115 +537,100 @@ def bench_copy(mib=1024, reps=3):
             "us_per_copy": ms * 1e3, "read_plus_write_GBps": 8 * n / (ms * 1e-3) / 1e9}
 
 
-def bench_prefill_cfg(name, steps=5, warmup=2):
-    import swa_chunked_gated_amd as gl
-    from workloads import WORKLOADS, make_prefill_inputs
-
-    w = WORKLOADS[name]
-    inp = make_prefill_inputs(w, device="cuda")
-    flags = gl.BRANCH_LINEAR | gl.BRANCH_SOFTMAX | (gl.WRITE_STATE if w.write_state else 0)
-    o = torch.empty(w.B, w.T, w.H, w.d, dtype=torch.bfloat16, device="cuda")
-    st = torch.empty(w.B, w.H, w.d, w.d, dtype=torch.float32, device="cuda") if w.write_state else None
-    if w.shortconv:
-        qc, kc, vc = (torch.empty_like(inp[x]) for x in ("q", "k", "v"))
-    nws = gl.prefill_workspace_bytes(w.B, w.T, w.H, w.Hkv, w.d, w.n_sink, w.window,
-                                     torch.bfloat16, update=w.update, flags=flags)
-    ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
-
-    def layer():
-        if w.shortconv:
-            gl.shortconv_qkv(inp["q"], inp["k"], inp["v"], inp["wq"], inp["wk"], inp["wv"],
-                             rope_theta=w.rope_theta, flags=gl.ROPE | gl.L2NORM, out=(qc, kc, vc))
-            q, k, v = qc, kc, vc
-        else:
-            q, k, v = inp["q"], inp["k"], inp["v"]
-        gl.hybrid_prefill(q, k, v, inp["a"], inp["b"], w.n_sink, w.window, update=w.update,
-                          flags=flags, o=o, state_out=st, workspace=ws)
-
-    sec = timed(layer, steps, warmup)
-    f = (gdn_flops(w) if w.update == "gdn" else gla_flops(w)) + swa_flops(w)
-    res = {"workload": name, "B": w.B, "T": w.T, "H": w.H, "Hkv": w.Hkv, "budget": w.budget,
-           "update": w.update, "ms_per_step": sec * 1e3, "tokens_per_s": w.B * w.T / sec,
-           "algorithmic_gflop": f / 1e9, "layer_frac_mfma": f / sec / PEAK_BF16}
-    if w.shortconv:
-        def conv():
-            gl.shortconv_qkv(inp["q"], inp["k"], inp["v"], inp["wq"], inp["wk"], inp["wv"],
-                             rope_theta=w.rope_theta, flags=gl.ROPE | gl.L2NORM, out=(qc, kc, vc))
-        csec = timed(conv, steps, warmup)
-        cbytes = 2 * sum(inp[x].numel() * inp[x].element_size() for x in ("q", "k", "v"))
-        res["shortconv_ms"] = csec * 1e3
-        res["shortconv_frac_hbm"] = cbytes / csec / PEAK_HBM
-    return res
-
+# ------------------------------------------------------------------ main
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default="all",
-                    choices=["all", "main", "decode", "longctx", "qwen32b", "qwen32b_decode", "copy"])
+                    choices=["all", "headline", "longctx", "llama", "tiny", "decode", "qwen32b",
+                             "qwen32b_decode", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-split", action="store_true",
-                    help="skip the two-launch reference timing of the headline layer (profiling runs)")
+    ap.add_argument("--no-parts", action="store_true",
+                    help="time the layer only, not its calls one by one (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    parts = not args.no_parts
+
+    # single-workload legs (profiling and counter runs)
+    single = {"longctx": HEADLINE, "llama": "llama8b_t4096", "tiny": "tiny_fp32"}
+    if args.only in single or args.only in ("decode", "qwen32b", "qwen32b_decode", "copy"):
+        import torch
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            sys.exit(2)
+        torch.cuda.set_device(0)
+        if args.only in single:
+            out = bench_prefill(single[args.only], args.steps, args.warmup, parts=parts)
+        elif args.only == "decode":
+            out = bench_decode(steps=args.steps, warmup=args.warmup)
+        elif args.only == "qwen32b_decode":
+            out = bench_qwen_decode(steps=args.steps, warmup=args.warmup)
+        elif args.only == "copy":
+            out = bench_copy()
+        else:
+            for n in ("qwen32b_t8192_gdn", "qwen32b_t8192_gla"):
+                print(json.dumps(bench_prefill(n, args.steps, args.warmup, parts=parts)), flush=True)
+            return
+        print(json.dumps(out), flush=True)
+        return
+
+    # the oracle first, before anything touches the GPU (its workers fork)
+    cpu = {}
+    if not args.no_cpu_baseline:
+        todo = [HEADLINE] + ([] if args.only == "headline" else
+                             ["tiny_fp32", "llama8b_t4096", "decode_b256", "qwen32b_t8192_gdn",
+                              "qwen32b_t8192_gla"])
+        for n in todo:
+            cpu[n] = cpu_baseline(n, cores, **CPU_SAMPLES[n])
+            print(f"# cpu_baseline {n}: {cpu[n]['value']:.1f} {cpu[n]['unit']} "
+                  f"({cpu[n]['seconds']:.1f} s)", file=sys.stderr, flush=True)
+
+    import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
 
-    if args.only == "decode":
-        print(json.dumps(bench_decode(steps=args.steps, warmup=args.warmup)), flush=True)
-        return
-    if args.only == "qwen32b_decode":
-        print(json.dumps(bench_qwen_decode(steps=args.steps, warmup=args.warmup)), flush=True)
-        return
-    if args.only == "copy":
-        print(json.dumps(bench_copy()), flush=True)
-        return
-    if args.only in ("longctx", "qwen32b"):
-        names = ["longctx_b8_t32768"] if args.only == "longctx" else \
-            ["qwen32b_t8192_gdn", "qwen32b_t8192_gla"]
-        for n in names:
-            print(json.dumps(bench_prefill_cfg(n, steps=args.steps, warmup=args.warmup)), flush=True)
-        return
-
-    m = bench_main(args.steps, args.warmup, split=not args.no_split)
-    w = m["w"]
+    m = bench_prefill(HEADLINE, args.steps, args.warmup, parts=True)
+    print(f"# headline done: {m['ms_per_step']:.3f} ms per step", file=sys.stderr, flush=True)
     also = {}
     if args.only == "all":
-        also["decode"] = bench_decode()
-        also["longctx_b8_t32768"] = bench_prefill_cfg("longctx_b8_t32768")
-        also["qwen32b_t8192_gdn"] = bench_prefill_cfg("qwen32b_t8192_gdn")
-        also["qwen32b_t8192_gla"] = bench_prefill_cfg("qwen32b_t8192_gla")
+        for n in ("tiny_fp32", "llama8b_t4096", "qwen32b_t8192_gdn", "qwen32b_t8192_gla"):
+            also[n] = bench_prefill(n, args.steps, args.warmup, parts=True)
+            also[n]["cpu_baseline"] = cpu.get(n)
+            print(f"# {n} done", file=sys.stderr, flush=True)
+        also["decode_b256"] = bench_decode()
+        also["decode_b256"]["cpu_baseline"] = cpu.get("decode_b256")
         also["qwen32b_decode"] = bench_qwen_decode()
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(m["inputs"], w)
+        also["copy"] = bench_copy()
+    roof = dict(m.pop("roofline"))
     line = {
-        "metric": "hybrid GDN+sink/SWA layer prefill tokens/s (LLaMA3.1-8B attention shape)",
-        "value": w.B * w.T / m["sec"],
+        "metric": "hybrid GDN+sink/SWA layer prefill tokens/s (long-context: B=8, T=32768, "
+                  "32 query / 8 KV heads, d=128, budget 8+120, final state out)",
+        "value": m["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": m["sec"] * 1e3,
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; shapes and distributions of the workload, no weights)",
-        "config": {"workload": "llama8b_t4096 prefill", "B": w.B, "T": w.T, "H": w.H,
-                   "Hkv": w.Hkv, "d": w.d, "n_sink": w.n_sink, "window": w.window,
-                   "update": "gdn", "state": "fp32"},
-        "roofline": m["roofline"],
-        "cpu_baseline": cpu,
-        "kernels_ms": m["kernels_ms"],
-        "layer_frac_mfma": m["layer_frac_mfma"],
+        "config": {"workload": "longctx_b8_t32768 prefill", "B": m["B"], "T": m["T"], "H": m["H"],
+                   "Hkv": m["Hkv"], "d": m["d"], "n_sink": m["n_sink"], "window": m["window"],
+                   "update": "gdn", "state": "fp32, written"},
+        "roofline": roof,
+        "cpu_baseline": cpu.get(HEADLINE),
+        "layer": m,
         "also": also,
     }
     print(json.dumps(line), flush=True)

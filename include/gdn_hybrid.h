@@ -53,8 +53,18 @@
  *     the GDN path are L2-normalised (or come from shortconv_qkv); a in (0,1],
  *     b in [0,1]; decode positions pos[b] >= 0 and the cache/state hold the
  *     sequence's prefix up to pos[b] - 1.
- *   - No global mutable state besides the last HIP error code: calls are
- *     thread-safe as far as HIP launches are.
+ *   - No global mutable state besides the last HIP error code and the
+ *     test-only fault setting below: calls are thread-safe as far as HIP
+ *     launches are.
+ *   - Waits inside a launch: the one-launch few-chain prefill (see
+ *     gdn_hybrid_prefill_workspace) hands each chunk from preparation
+ *     workgroups to scan workgroups, and the scan's rows to softmax
+ *     workgroups, through flags in the workspace.  Every such wait is on
+ *     workgroups earlier in the grid (dispatched in order, so already
+ *     resident) and is bounded in time (0.1 s by default).  If a bound ever
+ *     expires (e.g. another workload starves the producers), the rows and
+ *     states computed from the missing data are written as NaN, never as
+ *     silently wrong values.
  */
 #ifndef GDN_HYBRID_H
 #define GDN_HYBRID_H
@@ -96,6 +106,19 @@ const char* gdn_hybrid_strerror(int code);
 
 /* hipError_t of the last failed launch in this process (0 if none). */
 int gdn_hybrid_last_hip_error(void);
+
+/*
+ * Test-only fault injection for the bounded waits described above
+ * (process-wide; affects launches issued after the call).  faults: bit 0 =
+ * the preparation publishes no chunk-ready flags, bit 1 = the scan publishes
+ * no row-done flags, so every wait on them runs into its bound and the
+ * affected rows / states come out as NaN while every kernel still exits.
+ * wait_us: the bound of each wait in microseconds (default 100000).
+ * faults = 0, wait_us = 100000 restores normal operation.
+ * Errors: GDN_EINVAL if faults is outside 0..3 or wait_us outside
+ * 1..1000000.
+ */
+int gdn_hybrid_set_test_faults(int faults, int wait_us);
 
 /*
  * Workspace bytes gdn_hybrid_prefill needs for these arguments (written to

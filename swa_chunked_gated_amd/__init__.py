@@ -37,6 +37,14 @@ def version() -> int:
     return _lib.load().gdn_hybrid_version()
 
 
+def set_test_faults(faults: int = 0, wait_us: int = 100000) -> None:
+    """Test-only: inject faults into the one-launch prefill's flag hand-offs
+    (bit 0: no chunk-ready flags, bit 1: no row-done flags) with each bounded
+    wait limited to ``wait_us``; the affected rows and states come out NaN.
+    ``set_test_faults()`` restores normal operation."""
+    _lib.check("gdn_hybrid_set_test_faults", _lib.load().gdn_hybrid_set_test_faults(faults, wait_us))
+
+
 def _p(t):
     if t is None:
         return None

@@ -19,6 +19,7 @@ SIGNATURES = {
     "gdn_hybrid_version": (_c_int, []),
     "gdn_hybrid_strerror": (ctypes.c_char_p, [_c_int]),
     "gdn_hybrid_last_hip_error": (_c_int, []),
+    "gdn_hybrid_set_test_faults": (_c_int, [_c_int, _c_int]),
     "gdn_hybrid_prefill_workspace": (
         _c_int, [_c_int] * 11 + [ctypes.POINTER(ctypes.c_size_t)]),
     "gdn_hybrid_prefill": (

@@ -15,6 +15,8 @@
 namespace {
 
 std::atomic<int> g_last_hip_error{0};
+std::atomic<int> g_faults{0};
+std::atomic<int> g_wait_us{100000};   // 0.1 s
 
 int launched(hipError_t e) {
   if (e == hipSuccess) return GDN_OK;
@@ -47,7 +49,20 @@ bool aligned16(std::initializer_list<const void*> ptrs) {
 
 }  // namespace
 
+namespace gdn {
+TestFaults test_faults() {
+  return TestFaults{g_faults.load(), (uint64_t)g_wait_us.load() * 100u};
+}
+}  // namespace gdn
+
 extern "C" {
+
+int gdn_hybrid_set_test_faults(int faults, int wait_us) {
+  if (faults < 0 || faults > 3 || wait_us < 1 || wait_us > 1000000) return GDN_EINVAL;
+  g_faults.store(faults);
+  g_wait_us.store(wait_us);
+  return GDN_OK;
+}
 
 int gdn_hybrid_version(void) { return 10000; }
 

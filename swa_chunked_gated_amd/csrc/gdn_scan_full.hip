@@ -82,6 +82,11 @@ struct FullSmem {
 constexpr int kPrepWaves = 3;
 // Query tiles per softmax workgroup (one continuous K/V prefetch pipeline).
 constexpr int kSwaTiles = 1;
+// Injected faults (set only by tests, see gdn_hybrid_set_test_faults): the
+// preparation does not publish its ready flags / the scan does not publish
+// its done flags, so that every wait on them runs into its time bound.
+constexpr int kFaultNoReady = 1;
+constexpr int kFaultNoDone = 2;
 
 // Dynamic LDS of the fused kernel: the scan's two buffers, or the
 // preparation waves' work areas, whichever is larger.
@@ -130,7 +135,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
     float* __restrict__ w_g, uint64_t* __restrict__ ready, uint64_t epoch, int n_prep,
     uint64_t* __restrict__ done, int n_swa, bf16* __restrict__ o, float* __restrict__ state_out,
     int B, int T_, int H, int Hkv, int n_sink, int window, int flags, int xcd, float w_lin,
-    float w_swa) {
+    float w_swa, uint64_t wait_ticks, int faults) {
   using SM = FullSmem<D, NW>;
   using PS = prep::PrepSmem<bf16, D, true>;
   static_assert(NL >= 1 && NL <= 4, "one to four loader waves");
@@ -172,7 +177,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_waitcnt(0x0F70);
       asm volatile("" ::: "memory");
-      if (lane == 0)
+      if (lane == 0 && !(faults & kFaultNoReady))
         __hip_atomic_store(ready + (size_t)bh * nch + c, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     return;
@@ -191,7 +196,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
     swa::swa_tiles<bf16, D, NW + NL, true>(q, k, v, o, T_, H, Hkv, 4, 64, kSwaTiles, n_sink, window,
                                            n_sink + window, bx, rest % groups, rest / groups,
                                            reinterpret_cast<bf16*>(smem_raw), done, epoch, nch,
-                                           (D / DVS) * NW, w_swa);
+                                           (D / DVS) * NW, w_swa, wait_ticks);
     return;
   }
 
@@ -205,6 +210,9 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
   const int lg = lane >> 4;
   const int c0 = sp * DVS;
   const size_t chain = (size_t)bi * H + h;
+  // lost[b][l]: loader wave l gave up waiting for a chunk it staged into
+  // buffer b (or an earlier one); the compute waves then poison the state
+  __shared__ int lost[2][NL];
 
   if (wv >= NW) {
     // ======================= loader waves: tile t of a chunk is loaded by
@@ -255,13 +263,14 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
     // ready flag of the next chunk to stage, read one chunk ahead so that its
     // latency hides behind the current chunk's loads
     uint64_t seen = 0;
+    bool gave_up = false;    // sticky: once a wait gave up, later chunks are not waited for
     auto stage = [&](int c, int b) {
       bf16* B = buf(b);
       const int i0 = n_sink + c * kC;
       const int Cc = min(kC, iend - i0);
       const size_t ci = chain * nch + c;
       if (n_prep > 0) {
-        if (seen != epoch) wait_ready(ready + ci, epoch);
+        if (!gave_up && seen != epoch) gave_up = !wait_ready(ready + ci, epoch, wait_ticks);
         asm volatile("" ::: "memory");
         seen = c + 1 < nch ? __hip_atomic_load(ready + ci + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
       }
@@ -307,6 +316,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
         dma4c(w_g + ci * (2 * kC) + lane, gate);
         dma4c(w_g + ci * (2 * kC) + 64 + lane, gate + 64);
       }
+      if (lane == 0) lost[b][ld] = gave_up ? 1 : 0;
       __builtin_amdgcn_s_waitcnt(0);   // this buffer is complete in LDS
     };
     if (nch > 0) stage(0, 0);
@@ -330,7 +340,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
   // twenty row stores of the five previous chunks are outstanding)
   const size_t done0 = chain * nch * (D / DVS) * NW + sp * NW + wv;
   auto publish = [&](int c) {
-    if (lane == 0)
+    if (lane == 0 && !(faults & kFaultNoDone))
       __hip_atomic_store(done + done0 + (size_t)c * (D / DVS) * NW, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   for (int c = 0; c < nch; ++c) {
@@ -340,6 +350,16 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gdn_scan_full_kernel(
       __builtin_amdgcn_s_waitcnt(0x4F74);   // vmcnt(20)
       asm volatile("" ::: "memory");
       publish(c - 6);
+    }
+    bool stale = false;
+#pragma unroll
+    for (int l = 0; l < NL; ++l) stale |= lost[c & 1][l] != 0;
+    if (stale) {
+      // the chunk's tiles were not published in time: the state and every
+      // output from this chunk on become NaN instead of silently wrong
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) S[mt] = f32x4{__builtin_nanf(""), __builtin_nanf(""),
+                                                    __builtin_nanf(""), __builtin_nanf("")};
     }
     const bf16* B = buf(c & 1);
     const bf16* Qs = B + SM::oQ;
@@ -512,21 +532,25 @@ hipError_t launch_full_t(const PrefillArgs& p, int nch, hipStream_t s, bool* swa
     if (e != hipSuccess) return e;
   }
   const uint64_t epoch = n_prep > 0 ? next_epoch() : 0;
+  const TestFaults tf = test_faults();
   // XCD placement (the preparation's share needs whole rounds of 8 workgroups)
   int xcd = kXcdNone;
   if (n_prep % 8 == 0 && (p.B * p.H) % 8 == 0) xcd = (p.B * p.Hkv) % 8 == 0 ? kXcdByGroup : kXcdByChain;
   // The softmax branch joins the kernel (its tiles run on the preparation
   // workgroups after their chunks, adding onto the scan's rows as they are
   // published) when both branches are asked for without accumulation and a
-  // KV head serves a multiple of 4 query heads.
-  const bool link = n_prep > 0 && (p.flags & 2) && !(p.flags & 8) && (p.H / p.Hkv) % 4 == 0;
+  // KV head serves a multiple of 4 query heads.  Without the linear branch
+  // the scan writes no rows for the tiles to add onto, so the softmax branch
+  // then runs as its own launch (which writes every row).
+  const bool link = n_prep > 0 && (p.flags & 1) && (p.flags & 2) && !(p.flags & 8) &&
+                    (p.H / p.Hkv) % 4 == 0;
   const int n_swa = link ? ((p.T + 63) / 64 + kSwaTiles - 1) / kSwaTiles * (p.H / 4) * p.B : 0;
   if (swa_done) *swa_done = link;
   hipLaunchKernelGGL(kern, dim3(n_prep + n_scan + n_swa), dim3(64 * (NW + NL)), lds, s,
                      (const bf16*)p.q, (const bf16*)p.k, (const bf16*)p.v, p.a, p.b, (bf16*)w.wm,
                      (bf16*)w.ktg, (bf16*)w.a, w.ut, w.g, w.ready, epoch, n_prep, w.done, n_swa,
                      (bf16*)p.o, p.state_out, p.B, p.T, p.H, p.Hkv, p.n_sink, p.window, p.flags, xcd,
-                     p.w_lin, p.w_swa);
+                     p.w_lin, p.w_swa, tf.wait_ticks, tf.faults);
   return hipGetLastError();
 }
 

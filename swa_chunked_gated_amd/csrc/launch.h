@@ -144,6 +144,16 @@ hipError_t launch_shortconv_decode(const ShortConvArgs& a, float* const hist[3],
                                    hipStream_t s);
 hipError_t launch_shortconv_history(const ShortConvArgs& a, float* const hist[3], hipStream_t s);
 
+// Time bound of the in-kernel waits on flags published by other workgroups
+// of the same launch (100 MHz real-time counter ticks), and faults injected
+// by tests (bit 0: the preparation publishes no ready flags; bit 1: the scan
+// publishes no done flags).  Process-wide; set by gdn_hybrid_set_test_faults.
+struct TestFaults {
+  int faults;
+  uint64_t wait_ticks;
+};
+TestFaults test_faults();
+
 // Dynamic LDS bytes the decode kernel needs (the front end checks the limit).
 size_t decode_lds_bytes(int G, int N, int D, int gla, int elt);
 

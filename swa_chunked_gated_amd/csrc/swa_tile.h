@@ -71,32 +71,44 @@ template <class T> struct KeyBlock { static constexpr int n = sizeof(T) == 2 ? 6
 // are issued only after that (in-order issue; the asm keeps the compiler from
 // moving them above the loop).  SLEEP (units of 64 clocks) spaces the polls,
 // so that many waiting waves do not load the memory system.  Bounded: after
-// about 0.1 s it gives up, so a missing producer can never hang the GPU (the
-// results would then be wrong, never the machine stuck).
+// `ticks` of the 100 MHz real-time counter it gives up and returns false, so
+// a missing producer can never hang the GPU; the caller then poisons what it
+// computes from the data it waited for (NaN), so a give-up is never silent.
 template <int SLEEP = 1>
-__device__ __forceinline__ void wait_ready(const uint64_t* f, uint64_t epoch) {
+__device__ __forceinline__ bool wait_ready(const uint64_t* f, uint64_t epoch, uint64_t ticks) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();          // 100 MHz
+  bool ok = true;
   while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
     __builtin_amdgcn_s_sleep(SLEEP);
-    if (__builtin_amdgcn_s_memrealtime() - t0 > 10000000ull) break;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > ticks) {
+      ok = false;
+      break;
+    }
   }
   asm volatile("" ::: "memory");
+  return ok;
 }
 
 // Waits until the n (<= 64) consecutive flags f[0..n) all equal epoch: lane
 // i reads flag i, every poll reads them all at once.  Bounded like
-// wait_ready.
+// wait_ready; the result is the same in every lane.
 template <int SLEEP = 1>
-__device__ __forceinline__ void wait_ready_span(const uint64_t* f, int n, uint64_t epoch, int lane) {
+__device__ __forceinline__ bool wait_ready_span(const uint64_t* f, int n, uint64_t epoch, int lane,
+                                                uint64_t ticks) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   const bool mine = lane < n;
+  bool done = false;
   while (true) {
     const bool ok = !mine || __hip_atomic_load(f + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
-    if (__all(ok)) break;
+    if (__all(ok)) {
+      done = true;
+      break;
+    }
     __builtin_amdgcn_s_sleep(SLEEP);
-    if (__builtin_amdgcn_s_memrealtime() - t0 > 10000000ull) break;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > ticks) break;
   }
   asm volatile("" ::: "memory");
+  return done;
 }
 
 // LDS of swa_tiles: two K blocks (row-major) then two V^T blocks.
@@ -134,7 +146,7 @@ __device__ __forceinline__ void swa_tiles(const T* __restrict__ q, const T* __re
                                           int Hkv, int HPW, int QT, int TPW, int n_sink, int window,
                                           int add_from, int bx, int hgrp, int bi, T* lds,
                                           const uint64_t* done, uint64_t epoch, int nch, int nflag,
-                                          float w_swa) {
+                                          float w_swa, uint64_t wait_ticks = 0) {
   constexpr int KB = KeyBlock<T>::n;
   constexpr int NTH = 64 * NW;
   constexpr int PAD = 16 / sizeof(T);
@@ -566,6 +578,7 @@ __device__ __forceinline__ void swa_tiles(const T* __restrict__ q, const T* __re
     }
 
     // ---- epilogue of this query tile
+    bool linked_ok = true;   // LINKED: the scan published every row this wave adds onto
     if constexpr (LINKED) {
       // the done flags of the scan chunks covering this wave's rows are
       // consecutive: one flag per lane, polled together
@@ -575,7 +588,8 @@ __device__ __forceinline__ void swa_tiles(const T* __restrict__ q, const T* __re
         const int c_lo = (r_lo - add_from) / 64;
         const int nf = ((r_hi - add_from) / 64 - c_lo + 1) * nflag;
         const uint64_t* f0 = done + ((size_t)(bi * H + h) * nch + c_lo) * nflag;
-        for (int s0 = 0; s0 < nf; s0 += 64) wait_ready_span<32>(f0 + s0, min(64, nf - s0), epoch, lane);
+        for (int s0 = 0; s0 < nf && linked_ok; s0 += 64)
+          linked_ok = wait_ready_span<32>(f0 + s0, min(64, nf - s0), epoch, lane, wait_ticks);
       }
     }
     // what o holds on rows >= add_from, read before any row is written: every
@@ -616,6 +630,9 @@ __device__ __forceinline__ void swa_tiles(const T* __restrict__ q, const T* __re
         f32x4 val = oacc[dt][nq] * inv;
         if (addl) val += f32x4{static_cast<float>(raw[nq][dt][0]), static_cast<float>(raw[nq][dt][1]),
                                static_cast<float>(raw[nq][dt][2]), static_cast<float>(raw[nq][dt][3])};
+        // a row whose linear part was never published is poisoned, not guessed
+        if (LINKED && addl && !linked_ok) val = f32x4{__builtin_nanf(""), __builtin_nanf(""),
+                                                      __builtin_nanf(""), __builtin_nanf("")};
         store4(orow + 16 * dt + 4 * lg, val);
       }
     }

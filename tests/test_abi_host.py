@@ -270,3 +270,12 @@ def test_weighted_calls_reject_non_finite_weights(lib):
         assert lib.gdn_hybrid_decode_weighted(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                               FAKE, FAKE, 1, 2, 2, 64, 64, 8, 56, BF16, DELTA, 3, wl, ws,
                                               None) == EINVAL
+
+
+def test_test_fault_setting_validation(lib):
+    assert lib.gdn_hybrid_set_test_faults(-1, 100) == EINVAL
+    assert lib.gdn_hybrid_set_test_faults(4, 100) == EINVAL
+    assert lib.gdn_hybrid_set_test_faults(0, 0) == EINVAL
+    assert lib.gdn_hybrid_set_test_faults(0, 1000001) == EINVAL
+    assert lib.gdn_hybrid_set_test_faults(3, 50) == OK
+    assert lib.gdn_hybrid_set_test_faults(0, 100000) == OK   # normal operation restored
