@@ -256,6 +256,33 @@ int gdn_hybrid_decode_weighted(const void* q, const void* k, const void* v,
                                void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * gdn_hybrid_prefill without a workspace argument.  Arguments, layouts,
+ * flags and results are those of gdn_hybrid_prefill; the kernels are the
+ * same.  The chunk workspace is a library-owned device array of
+ * gdn_hybrid_noalloc_max_workspace() bytes (256 MiB) per GPU, created when
+ * the library's device code is loaded on that GPU and held until the
+ * process ends; the call itself allocates and frees nothing.  Its address
+ * is looked up on the first call on each device (the current device at the
+ * time of the call; the stream must belong to it).  Nothing in the array
+ * needs clearing between calls (the workspace's hand-off flags carry a
+ * per-call value).  Every call on one GPU shares that GPU's array, so calls
+ * whose work may overlap on one GPU (other streams, other host threads)
+ * race: serialise them.
+ * Errors: as gdn_hybrid_prefill, and GDN_EWORKSPACE when the workspace
+ * these arguments need (gdn_hybrid_prefill_workspace) exceeds the array.
+ */
+int gdn_hybrid_prefill_noalloc(const void* q, const void* k, const void* v,
+                               const float* a, const float* b,
+                               void* o, float* state_out,
+                               int B, int T, int H, int Hkv, int dk, int dv,
+                               int n_sink, int window, int dtype, int update, int flags,
+                               void* stream);
+/* Bytes of the per-GPU array gdn_hybrid_prefill_noalloc uses. */
+size_t gdn_hybrid_noalloc_max_workspace(void);
+
+/*
  * Fill the decode cache after a prefill of T tokens, so decoding resumes at
  * position T: sinks 0..min(n_sink,T)-1 and window tokens
  * max(n_sink, T-window)..T-1 go to their slots (layouts as in

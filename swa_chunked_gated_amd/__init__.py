@@ -136,6 +136,37 @@ def hybrid_prefill(q, k, v, a, b, n_sink: int, window: int, update: str = "gdn",
     return o, state_out
 
 
+def hybrid_prefill_noalloc(q, k, v, a, b, n_sink: int, window: int, update: str = "gdn",
+                           flags: int = BRANCH_LINEAR | BRANCH_SOFTMAX, o=None, state_out=None):
+    """``hybrid_prefill`` through the entry point that allocates nothing: its
+    chunk workspace is the library's per-GPU array (see
+    ``noalloc_max_workspace``); calls that may overlap on one GPU race.
+    Outputs are allocated here with torch when not given."""
+    if flags & ACCUMULATE and o is None:
+        raise ValueError("ACCUMULATE needs an initialised output tensor o")
+    B, T, H, dk = q.shape
+    Hkv, dv = k.shape[2], v.shape[3]
+    dt = _io_dtype(q, k, v)
+    _f32(a, b)
+    if o is None and flags & (BRANCH_LINEAR | BRANCH_SOFTMAX):
+        o = torch.empty(B, T, H, dv, dtype=q.dtype, device=q.device)
+    if state_out is None and flags & WRITE_STATE:
+        state_out = torch.empty(B, H, dk, dv, dtype=torch.float32, device=q.device)
+    if o is not None:
+        _io_dtype(q, o)
+    _f32(state_out)
+    rc = _lib.load().gdn_hybrid_prefill_noalloc(_p(q), _p(k), _p(v), _p(a), _p(b), _p(o),
+                                                _p(state_out), B, T, H, Hkv, dk, dv, n_sink,
+                                                window, dt, _UPDATES[update], flags, _stream(q))
+    _lib.check("gdn_hybrid_prefill_noalloc", rc)
+    return o, state_out
+
+
+def noalloc_max_workspace() -> int:
+    """Bytes of the per-GPU workspace array of ``hybrid_prefill_noalloc``."""
+    return int(_lib.load().gdn_hybrid_noalloc_max_workspace())
+
+
 def hybrid_decode(q, k, v, a, b, state, k_cache, v_cache, a_cache, b_cache, pos,
                   n_sink: int, window: int, update: str = "gdn",
                   flags: int = BRANCH_LINEAR | BRANCH_SOFTMAX, o=None, weights=None):

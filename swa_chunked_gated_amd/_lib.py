@@ -28,6 +28,9 @@ SIGNATURES = {
         _c_int, [_ptr] * 12 + [_c_int] * 10 + [_ptr]),
     "gdn_hybrid_prefill_weighted": (
         _c_int, [_ptr] * 7 + [_c_int] * 11 + [ctypes.c_float] * 2 + [_ptr, ctypes.c_size_t, _ptr]),
+    "gdn_hybrid_prefill_noalloc": (
+        _c_int, [_ptr] * 7 + [_c_int] * 11 + [_ptr]),
+    "gdn_hybrid_noalloc_max_workspace": (ctypes.c_size_t, []),
     "gdn_hybrid_decode_weighted": (
         _c_int, [_ptr] * 12 + [_c_int] * 10 + [ctypes.c_float] * 2 + [_ptr]),
     "gdn_hybrid_cache_from_prefill": (

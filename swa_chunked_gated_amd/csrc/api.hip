@@ -9,6 +9,7 @@
 
 #include <atomic>
 #include <initializer_list>
+#include <mutex>
 
 #include "launch.h"
 
@@ -45,6 +46,46 @@ bool aligned16(std::initializer_list<const void*> ptrs) {
   for (const void* p : ptrs)
     if (((uintptr_t)p & 15u) != 0) return false;
   return true;
+}
+
+}  // namespace
+
+// Device-resident prefill workspace of the allocation-free entry point
+// (gdn_hybrid_prefill_noalloc): one copy per GPU, alive until the process
+// ends.  Host code never passes `scratch` itself to a kernel (in host code
+// the name is a host-side stand-in, not a device address): it uses the
+// address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = size_t(256) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of the current device's scratch array, looked up once per device
+// (with that device current) and kept.
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_last_hip_error.store((int)e);
+    return GDN_ELAUNCH;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return GDN_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      g_last_hip_error.store((int)(e != hipSuccess ? e : hipErrorInvalidSymbol));
+      return GDN_ELAUNCH;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GDN_OK;
 }
 
 }  // namespace
@@ -112,11 +153,14 @@ int gdn_hybrid_prefill(const void* q, const void* k, const void* v, const float*
                                      workspace_bytes, stream);
 }
 
-int gdn_hybrid_prefill_weighted(const void* q, const void* k, const void* v, const float* a,
-                                const float* b, void* o, float* state_out, int B, int T, int H,
-                                int Hkv, int dk, int dv, int n_sink, int window, int dtype,
-                                int update, int flags, float w_lin, float w_swa, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+namespace {
+// Validation and launch of a prefill; with use_scratch the workspace is the
+// device's scratch array (workspace / workspace_bytes are ignored).
+int prefill_impl(const void* q, const void* k, const void* v, const float* a, const float* b,
+                 void* o, float* state_out, int B, int T, int H, int Hkv, int dk, int dv,
+                 int n_sink, int window, int dtype, int update, int flags, float w_lin,
+                 float w_swa, void* workspace, size_t workspace_bytes, bool use_scratch,
+                 void* stream) {
   if (!dims_ok(B, T, H, Hkv, dk, dv, n_sink, window, dtype, update)) return GDN_EINVAL;
   if (!std::isfinite(w_lin) || !std::isfinite(w_swa)) return GDN_EINVAL;
   if (flags < 1 || flags > 15 || (flags & 7) == 0) return GDN_EINVAL;
@@ -133,6 +177,16 @@ int gdn_hybrid_prefill_weighted(const void* q, const void* k, const void* v, con
   if (!aligned16({q, k, v, a, b, o, state_out})) return GDN_EINVAL;
   if (needs_rec && dtype == GDN_F32 && dk != 64) return GDN_EUNSUPPORTED;
   const size_t need = prefill_workspace_bytes(B, T, H, dk, n_sink, window, dtype, update, flags);
+  if (use_scratch) {
+    if (need > kScratchBytes) return GDN_EWORKSPACE;
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (need > 0) {
+      const int rc = scratch_of_current_device(&workspace);
+      if (rc) return rc;
+      workspace_bytes = kScratchBytes;
+    }
+  }
   if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_EWORKSPACE;
   if (need > 0 && ((uintptr_t)workspace & 255u) != 0) return GDN_EINVAL;
   if (T == 0 && !wst) return GDN_OK;
@@ -156,6 +210,26 @@ int gdn_hybrid_prefill_weighted(const void* q, const void* k, const void* v, con
   }
   if (lin && !acc && !run_linear) return launched(gdn::launch_zero_head_rows(p, s));
   return GDN_OK;
+}
+}  // namespace
+
+int gdn_hybrid_prefill_weighted(const void* q, const void* k, const void* v, const float* a,
+                                const float* b, void* o, float* state_out, int B, int T, int H,
+                                int Hkv, int dk, int dv, int n_sink, int window, int dtype,
+                                int update, int flags, float w_lin, float w_swa, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return prefill_impl(q, k, v, a, b, o, state_out, B, T, H, Hkv, dk, dv, n_sink, window, dtype,
+                      update, flags, w_lin, w_swa, workspace, workspace_bytes, false, stream);
+}
+
+size_t gdn_hybrid_noalloc_max_workspace(void) { return kScratchBytes; }
+
+int gdn_hybrid_prefill_noalloc(const void* q, const void* k, const void* v, const float* a,
+                               const float* b, void* o, float* state_out, int B, int T, int H,
+                               int Hkv, int dk, int dv, int n_sink, int window, int dtype,
+                               int update, int flags, void* stream) {
+  return prefill_impl(q, k, v, a, b, o, state_out, B, T, H, Hkv, dk, dv, n_sink, window, dtype,
+                      update, flags, 1.f, 1.f, nullptr, 0, true, stream);
 }
 
 int gdn_hybrid_decode(const void* q, const void* k, const void* v, const float* a, const float* b,

@@ -279,3 +279,26 @@ def test_test_fault_setting_validation(lib):
     assert lib.gdn_hybrid_set_test_faults(0, 1000001) == EINVAL
     assert lib.gdn_hybrid_set_test_faults(3, 50) == OK
     assert lib.gdn_hybrid_set_test_faults(0, 100000) == OK   # normal operation restored
+
+
+def test_noalloc_prefill_validation(lib):
+    """Rejected on the host before the device array is looked up."""
+    cap = lib.gdn_hybrid_noalloc_max_workspace()
+    assert cap == 256 << 20
+    p = [FAKE] * 7
+    # workspace beyond the array: B=64, H=32, T=8192 (light preparation, ~2.2 GB)
+    ws = ctypes.c_size_t(0)
+    assert lib.gdn_hybrid_prefill_workspace(64, 8192, 32, 8, 128, 128, 8, 56, BF16, DELTA, 3,
+                                            ctypes.byref(ws)) == OK
+    assert ws.value > cap
+    assert lib.gdn_hybrid_prefill_noalloc(*p, 64, 8192, 32, 8, 128, 128, 8, 56, BF16, DELTA, 3,
+                                          None) == EWS
+    # the usual argument checks
+    assert lib.gdn_hybrid_prefill_noalloc(*p, 1, 100, 3, 2, 128, 128, 8, 56, BF16, DELTA, 3,
+                                          None) == EINVAL          # H % Hkv != 0
+    assert lib.gdn_hybrid_prefill_noalloc(*p, 1, 100, 4, 2, 128, 128, 8, 56, BF16, DELTA, 0,
+                                          None) == EINVAL          # no flag
+    assert lib.gdn_hybrid_prefill_noalloc(None, *p[1:], 1, 100, 4, 2, 128, 128, 8, 56, BF16, DELTA,
+                                          3, None) == EINVAL       # q NULL
+    assert lib.gdn_hybrid_prefill_noalloc(*p, 1, 100, 4, 2, 128, 128, 8, 56, F32, DELTA, 1,
+                                          None) == EUNSUP          # fp32 linear branch at d = 128
