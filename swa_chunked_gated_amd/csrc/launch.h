@@ -126,6 +126,12 @@ struct ShortConvArgs {
 // state when asked.
 // *swa_done is set when the softmax branch was computed in the same launch.
 hipError_t launch_linear_prefill(const PrefillArgs& a, hipStream_t s, bool* swa_done);
+// The whole layer in one pass over q, k, v (light preparation, then one
+// kernel running the state scan and the softmax rows of each chunk): bf16
+// GDN at d = 128 with both branches and no accumulation, many chains,
+// window <= 128 and n_sink <= 16.
+bool gdn_layer_applies(const PrefillArgs& p);
+hipError_t launch_gdn_layer(const PrefillArgs& p, hipStream_t s);
 // Chunk preparation of the gated delta rule / of GLA into a.workspace (nch chunks).
 hipError_t launch_gdn_prep(const PrefillArgs& a, int nch, hipStream_t s);
 hipError_t launch_gla_prep(const PrefillArgs& a, int nch, hipStream_t s);

@@ -626,6 +626,10 @@ hipError_t launch_linear_prefill(const PrefillArgs& p, hipStream_t s, bool* swa_
   if (swa_done) *swa_done = false;
   const int nch = gdn_stream_chunks(p.T, p.n_sink, p.window);
   if (!p.gla && gdn_full_prep(p.B, p.H, p.D, p.bf16)) return launch_gdn_full(p, nch, s, swa_done);
+  if (gdn_layer_applies(p)) {
+    if (swa_done) *swa_done = true;
+    return launch_gdn_layer(p, s);
+  }
   if (nch > 0) {
     const hipError_t e = p.gla ? launch_gla_prep(p, nch, s) : launch_gdn_prep(p, nch, s);
     if (e != hipSuccess) return e;

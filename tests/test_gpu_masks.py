@@ -241,3 +241,18 @@ def test_decode_b256_1000_steps_sampled():
     assert np.array_equal(f64(st["b_cache"][bsel]), ref["b_cache"])
     assert np.all(st["pos"].cpu().numpy() == w.pos0 + w.steps)
     print(f"worst relative error over 1000 steps: {worst:.3e}")
+
+
+@pytest.mark.parametrize("B,H,Hkv,T,n_sink,window", [(32, 8, 2, 300, 8, 56), (16, 16, 4, 517, 8, 120),
+                                                     (32, 8, 2, 400, 16, 128), (32, 8, 8, 250, 0, 1),
+                                                     (64, 4, 1, 129, 3, 64), (32, 8, 2, 700, 0, 100),
+                                                     (16, 16, 2, 137, 8, 120)])
+def test_mask_probe_one_pass_layer(B, H, Hkv, T, n_sink, window):
+    """Both branches on many chains (B*H >= 128, window <= 128, n_sink <= 16):
+    the layer runs as the one-pass kernel whose softmax rows read keys from a
+    ring of three chunks; q = 0 makes the linear branch exactly 0."""
+    q, k, v, a, b = probe_inputs(B, T, H, Hkv, 128, torch.bfloat16, seed=T + window, gates=True)
+    o, st = gl.hybrid_prefill(q, k, v, a, b, n_sink, window, flags=ALL | gl.WRITE_STATE)
+    torch.cuda.synchronize()
+    check_counts(o, n_sink, window)
+    assert bool(torch.isfinite(st).all())

@@ -288,6 +288,25 @@ def test_many_chain_full_wave_scan():
         assert_close(f64(st[bsel][:, heads]), S, False, "state")
 
 
+@pytest.mark.parametrize("B,H,Hkv,T,n_sink,window", [(8, 32, 8, 300, 8, 56), (16, 16, 4, 517, 8, 120),
+                                                     (32, 8, 2, 400, 16, 128), (32, 8, 8, 250, 0, 1),
+                                                     (64, 4, 1, 129, 3, 64), (16, 8, 2, 700, 0, 100),
+                                                     (16, 16, 2, 200, 8, 120), (16, 8, 4, 193, 8, 120)])
+def test_one_pass_layer(B, H, Hkv, T, n_sink, window):
+    """Both branches on many chains: the one-pass kernel (state scan and the
+    softmax rows of each chunk in one workgroup per chain, o written once);
+    ragged lengths, one-chunk streams, windows 1..128, 0..16 sinks; sampled
+    chains against the oracle, output rows and final state."""
+    w = small(B=B, H=H, Hkv=Hkv, d=128, T=T, n_sink=n_sink, window=window, sigma=1.0)
+    inp = to_dev(make_prefill_inputs(w, seed=T * 7 + window))
+    o, st = run_prefill(inp, w)
+    G = H // Hkv
+    for bsel, heads in (([0], [0]), ([B // 2], list(range(G * (Hkv - 1), G * Hkv))), ([B - 1], [H - 1])):
+        ref, S = oracle_subset(inp, w, bsel, heads)
+        assert_close(f64(o[bsel][:, :, heads]), ref, False, f"o b{bsel} h{heads}")
+        assert_close(f64(st[bsel][:, heads]), S, False, f"state b{bsel} h{heads}")
+
+
 @pytest.mark.parametrize("n_sink,window,flags,T", [(8, 120, ALL | gl.WRITE_STATE, 520), (0, 129, ALL, 520),
                                                     (64, 64, ALL, 520), (3, 20, gl.BRANCH_SOFTMAX, 520),
                                                     (0, 1, ALL, 257), (64, 65, ALL | gl.WRITE_STATE, 300)])
