@@ -53,35 +53,71 @@ namespace {
 
 constexpr int kC = 64;           // chunk length
 constexpr int kD = 128;          // head dimension
-constexpr int kSR = kD + 8;      // row stride (elements) of [rows][128] tiles
+// Row stride (elements) of every [rows][128] tile (K, V, queries): 288
+// bytes.  Measured on gfx950, it keeps the transposing reads and the 16-byte
+// row reads free of bank conflicts; the 8-byte row reads it does not suit
+// (two-way) are few.
+constexpr int kSR = kD + 16;
+constexpr int kSV = kSR;
 constexpr int kSC = kC + 8;      // row stride of [64][64] tiles
 constexpr int kSinkRows = 16;    // sink keys held in LDS (n_sink <= 16)
 constexpr int kThreads = 512;
 
 // LDS layout (bf16 elements, then fp32 gates)
 constexpr int oKR = 0;                             // K ring [3][64][kSR]
-constexpr int oVR = oKR + 3 * kC * kSR;            // V ring [3][64][kSR]
-constexpr int oKS = oVR + 3 * kC * kSR;            // sink K [16][kSR]
-constexpr int oVS = oKS + kSinkRows * kSR;         // sink V [16][kSR]
-constexpr int oQ = oVS + kSinkRows * kSR;          // lagged queries [64][kSR] (acc order); then the hand-over rows
+constexpr int oVR = oKR + 3 * kC * kSR;            // V ring [3][64][kSV]
+constexpr int oKS = oVR + 3 * kC * kSV;            // sink K [16][kSR]
+constexpr int oVS = oKS + kSinkRows * kSR;         // sink V [16][kSV]
+constexpr int oQ = oVS + kSinkRows * kSV;          // lagged queries [64][kSR]; then the hand-over rows
 constexpr int oTB = oQ + kC * kSR;                 // TB [64][kSC] (acc order)
 constexpr int oA = oTB + kC * kSC;                 // A [64][kSC] (acc order)
 constexpr int nLdsT = oA + kC * kSC;
-constexpr int kLdsBytes = nLdsT * 2 + 2 * kC * 4;  // + g (log2), gamma
+// + fp32 per-token gate values of the chunk: g (log2 prefix), gamma = 2^g,
+//   -gamma, and 2^(g_C - g) (the decay from each token to the chunk's end)
+constexpr int kLdsBytes = nLdsT * 2 + 4 * kC * 4;
 static_assert(kLdsBytes <= 160 * 1024, "one workgroup per compute unit");
 
 typedef __attribute__((address_space(3))) bf16x4* lds_bf16x4_ptr;
 
 // Two transposing 8-byte LDS reads: lane (g, j) receives X[r0 + 4g + i][c0 + j]
 // and X[r0 + 16 + 4g + i][c0 + j], i = 0..3, of the row-major bf16 tile X
-// (row stride kSR): the operand X^T[c0 + j][K_g] (A side) or X[K_g][c0 + j]
+// (row stride SX): the operand X^T[c0 + j][K_g] (A side) or X[K_g][c0 + j]
 // (B side).  Within each 16-lane group, lane 4 r + c1 addresses row
 // r0 + 4g + r at columns c0 + 4 c1 .. + 3, and the hardware hands column
-// c0 + j of the group's four rows to lane j.
+// c0 + j of the group's four rows to lane j.  The V tiles, read only this
+// way, use a 288-byte row stride, which spreads a read's 16 rows x 32
+// bytes over distinct banks; the K tiles, mostly read as rows (row_frag),
+// use 272 bytes, which does the same for the row reads.
+template <int SX = kSR>
 __device__ __forceinline__ Frag<bf16> tr_frag(const bf16* X, int r0, int c0, int lane) {
   const int g = lane >> 4;
   const int j = lane & 15;
-  const bf16* p0 = X + (r0 + 4 * g + (j >> 2)) * kSR + c0 + 4 * (j & 3);
+  const bf16* p0 = X + (r0 + 4 * g + (j >> 2)) * SX + c0 + 4 * (j & 3);
+  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(p0));
+  const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(p0 + 16 * SX));
+  Frag<bf16> f;
+  f.v = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return f;
+}
+
+// Row `row` of a natural-order [rows][128] tile as an operand reduced over
+// d on the set 32 p + 8 g .. + 7 (one 16-byte read).  Every product over d
+// uses that set: the state's accumulator rows are ordered so that two
+// stacked state tiles provide it (see tr_frag_k).
+__device__ __forceinline__ Frag<bf16> row_frag8(const bf16* X, int row, int p, int g) {
+  return lds_frag8(X + row * kSR + 32 * p + 8 * g);
+}
+
+// K^T as the A operand of the state update, producing state tile
+// mt = 2 p + hh whose accumulator row 4 g + i holds d_k = 32 p + 8 g + 4 hh + i
+// (so that state tiles 2p and 2p+1 stacked as an operand hold d_k
+// 32 p + 8 g .. + 7 in order): a transposing read whose 16-lane group
+// addresses the rows (tokens) r0 + 4g + r and, in lane 4 r + c1, the columns
+// 32 p + 8 c1 + 4 hh .. + 3, which the hardware hands to lanes 4 c1 .. + 3.
+__device__ __forceinline__ Frag<bf16> tr_frag_k(const bf16* X, int r0, int p, int hh, int lane) {
+  const int g = lane >> 4;
+  const int j = lane & 15;
+  const bf16* p0 = X + (r0 + 4 * g + (j >> 2)) * kSR + 32 * p + 8 * (j & 3) + 4 * hh;
   const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(p0));
   const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(p0 + 16 * kSR));
   Frag<bf16> f;
@@ -89,10 +125,19 @@ __device__ __forceinline__ Frag<bf16> tr_frag(const bf16* X, int r0, int c0, int
   return f;
 }
 
-// Natural-order row `row` of a [rows][128] tile as an operand reduced over d
-// on the set 32 p + K_g (two 8-byte reads).
-__device__ __forceinline__ Frag<bf16> row_frag(const bf16* X, int row, int p, int g) {
-  return lds_frag44(X + row * kSR + 32 * p + 4 * g, X + row * kSR + 32 * p + 16 + 4 * g);
+// A transposing read pair at Xl + off and 16 rows below, Xl holding the
+// lane's part of the address (row 4 g + j / 4, column 4 (j % 4) of a
+// [rows][kSR] tile; see tr_frag).  The loops pass the lane parts of their
+// addresses through an empty asm once per chunk: the compiler then adds a
+// tile's uniform base to one lane register and folds the remaining
+// constant into each instruction's offset, instead of keeping every
+// distinct lane offset in a register of its own across the loop.
+__device__ __forceinline__ Frag<bf16> tr_at(const bf16* Xl, int off) {
+  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(Xl + off));
+  const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(Xl + off + 16 * kSR));
+  Frag<bf16> f;
+  f.v = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return f;
 }
 
 // Sum over lanes l, l^16, l^32, l^48 (the four lane groups of one column).
@@ -121,63 +166,58 @@ struct KeyPair {
   bool half;
 };
 
-// Softmax over up to NP key pairs for the queries t = t0 + j (lane column
-// j), in two phases.  Phase 1 (sm_scores): the scores of the pairs not
-// given (have[pair]) from the query fragments qf (S^T tiles: key 4g + i of
-// each 16-key half, query j), masked keys set to -inf, and the row maximum.
-// Phase 2 (sm_values): weights 2^((s - m) log2(e) / sqrt(d)), their sum (on
-// the matrix cores, against a ones operand) and the O^T tiles (d = 16 dt +
-// 4g + i, query j).  A pair every row attends in full needs no mask.
-template <int NP>
-__device__ __forceinline__ float sm_scores(const KeyPair (&kp)[NP], const bool (&use)[NP],
-                                           f32x4 (&st)[NP][2], const bool (&have)[NP],
+// Softmax over NP key pairs for the queries t = t0 + j (lane column j), in
+// two phases and without branches: every pair is processed, keys outside a
+// row's window (or past its sinks) weigh exactly 0.  Phase 1 (sm_scores):
+// the scores of pairs NG.. from the query fragments qf (the first NG pairs'
+// scores are given; S^T tiles: key 4g + i of each 16-key half, query j),
+// masked keys set to -inf, and the row maximum.  Phase 2 (sm_values):
+// weights 2^((s - m) log2(e) / sqrt(d)), their sum (on the matrix cores,
+// against a ones operand) and the O^T tiles (d = 16 dt + 4g + i, query j).
+template <int NP, int NG>
+__device__ __forceinline__ float sm_scores(const KeyPair (&kp)[NP], f32x4 (&st)[NP][2],
                                            const Frag<bf16> (&qf)[4], int t0, int n_sink,
-                                           int window, int T_, int lane) {
+                                           int window, int lane) {
   const int g = lane >> 4;
   const int j = lane & 15;
   const int t = t0 + j;
 #pragma unroll
-  for (int pi = 0; pi < NP; ++pi) {
-    if (!use[pi] || have[pi]) continue;
+  for (int pi = NG; pi < NP; ++pi) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       st[pi][hf] = zero4();
       if (hf == 1 && kp[pi].half) continue;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) st[pi][hf] = mfma(row_frag(kp[pi].K, kp[pi].r0 + 16 * hf + j, p, g), qf[p], st[pi][hf]);
+      for (int p = 0; p < 4; ++p) st[pi][hf] = mfma(row_frag8(kp[pi].K, kp[pi].r0 + 16 * hf + j, p, g), qf[p], st[pi][hf]);
     }
   }
   float m = -INFINITY;
 #pragma unroll
   for (int pi = 0; pi < NP; ++pi) {
-    if (!use[pi]) continue;
-    const int kk0 = kp[pi].kk0;
-    // every key of a ring pair inside every row's window (t - window, t]
-    const bool full = !kp[pi].half && kk0 > t0 + 15 - window && kk0 + 31 <= t0 && kk0 + 31 < T_;
+    // ring keys (>= n_sink): attended inside the window, kk - t in (-window, 0];
+    // the sink pair holds keys 0 .. 15, of which those below n_sink (and <= t)
+    // are sinks (the others, if any, are window keys held in the ring)
+    const int d0 = kp[pi].kk0 + 4 * g - t + window - 1;      // (kk - t) + window - 1 at i = 0
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (!full) {
-          const int kk = kk0 + 16 * hf + 4 * g + i;
-          // the sink pair holds keys 0 .. 15, of which only kk < n_sink are
-          // sinks (the others, if any, are window keys held in the ring);
-          // ring pairs hold keys >= n_sink, attended inside the window
-          const bool on = kp[pi].half ? hf == 0 && kk < n_sink && kk <= t
-                                      : kk <= t && kk < T_ && kk > t - window;
-          if (!on) st[pi][hf][i] = -INFINITY;
-        }
-        m = fmaxf(m, st[pi][hf][i]);
+        const int kk = kp[pi].kk0 + 16 * hf + 4 * g + i;
+        const bool on = kp[pi].half ? hf == 0 && kk < n_sink && kk <= t
+                                    : (unsigned)(d0 + 16 * hf + i) < (unsigned)window;
+        st[pi][hf][i] = on ? st[pi][hf][i] : -INFINITY;
       }
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+      m = fmaxf(fmaxf(m, fmaxf(st[pi][hf][0], st[pi][hf][1])), fmaxf(st[pi][hf][2], st[pi][hf][3]));
   }
   m = max_lane_groups(m);
   return m == -INFINITY ? 0.f : m;   // a row with no key (past the sequence): weights 0
 }
 
 template <int NP>
-__device__ __forceinline__ void sm_values(const KeyPair (&kp)[NP], const bool (&use)[NP],
-                                          const f32x4 (&st)[NP][2], float m, int lane,
-                                          f32x4 (&oacc)[8], float& inv_l) {
+__device__ __forceinline__ void sm_values(const KeyPair (&kp)[NP], const f32x4 (&st)[NP][2], float m,
+                                          int lane, f32x4 (&oacc)[8], float& inv_l) {
   const float scale = kLog2e / sqrtf((float)kD);
   const float mb = -m * scale;
   Frag<bf16> ones;
@@ -188,7 +228,6 @@ __device__ __forceinline__ void sm_values(const KeyPair (&kp)[NP], const bool (&
   for (int dt = 0; dt < 8; ++dt) oacc[dt] = zero4();
 #pragma unroll
   for (int pi = 0; pi < NP; ++pi) {
-    if (!use[pi]) continue;
     f32x4 p0, p1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -205,11 +244,11 @@ __device__ __forceinline__ void sm_values(const KeyPair (&kp)[NP], const bool (&
         // 16 rows twice
         const int g = lane >> 4;
         const int j = lane & 15;
-        const bf16* p0p = kp[pi].V + (kp[pi].r0 + 4 * g + (j >> 2)) * kSR + 16 * dt + 4 * (j & 3);
+        const bf16* p0p = kp[pi].V + (kp[pi].r0 + 4 * g + (j >> 2)) * kSV + 16 * dt + 4 * (j & 3);
         const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(p0p));
         vf.v = bf16x8{x[0], x[1], x[2], x[3], x[0], x[1], x[2], x[3]};
       } else {
-        vf = tr_frag(kp[pi].V, kp[pi].r0, 16 * dt, lane);
+        vf = tr_frag<kSV>(kp[pi].V, kp[pi].r0, 16 * dt, lane);
       }
       oacc[dt] = mfma(vf, pf, oacc[dt]);
     }
@@ -218,9 +257,12 @@ __device__ __forceinline__ void sm_values(const KeyPair (&kp)[NP], const bool (&
   inv_l = lacc[0] > 0.f ? 1.f / lacc[0] : 0.f;
 }
 
+// q, k, v, w_tb and w_g are read through plain (not restrict) pointers on
+// purpose: the prefetch loads must stay where they are issued, ahead of the
+// chunk's barriers, rather than be moved next to their use.
 __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const bf16* __restrict__ w_tb, const float* __restrict__ w_g, bf16* __restrict__ o,
+    const bf16* q, const bf16* k, const bf16* v, const bf16* w_tb, const float* w_g,
+    bf16* __restrict__ o,
     float* __restrict__ state_out, int B, int T_, int H, int Hkv, int n_sink, int window,
     int nch, int write_state, float w_lin, float w_swa) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -233,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
   bf16* Xs = sm + oQ;             // hand-over rows (after the queries are read)
   bf16* TBs = sm + oTB;
   bf16* As = sm + oA;
-  float* Gs = reinterpret_cast<float*>(smem_raw + nLdsT * 2);   // g[64], gamma[64]
+  float* Gs = reinterpret_cast<float*>(smem_raw + nLdsT * 2);   // g, gamma, -gamma, 2^(g_C - g) [64 each]
 
   // the G query heads of a KV head are consecutive workgroups on one XCD
   // and share the K and V rows through its L2
@@ -276,16 +318,46 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
     const int cp = (n & 15) * 8;
     return *reinterpret_cast<const V16*>(base + (size_t)r * stride + cp);
   };
-  auto put_row = [&](bf16* tile, int n, const V16& x) {
+  // The prefetch's 4 pieces m of 64 rows from row0, for the thread with
+  // piece index n0 (rows n0 / 16 + 16 m): a uniform row base plus a per-lane
+  // offset when all 64 rows exist, the clamped form near the end.
+  auto load_tile4 = [&](const bf16* base, size_t stride, int row0, int n0, V16 (&x)[4]) {
+    if (row0 + kC <= T_) {
+      const bf16* rb = base + (size_t)row0 * stride;
+      const int off = (n0 >> 4) * (int)stride + (n0 & 15) * 8;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) x[m] = *reinterpret_cast<const V16*>(rb + off + 16 * m * (int)stride);
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) x[m] = load_rows(base, stride, row0, n0 + 256 * m);
+    }
+  };
+  auto put_row = [&](bf16* tile, int n, const V16& x) {      // K tiles
     *reinterpret_cast<V16*>(tile + (n >> 4) * kSR + (n & 15) * 8) = x;
   };
-  auto put_q = [&](int n, const V16& x) {      // query columns in acc order (runs of 4)
-    const int r = n >> 4;
-    const int cp = (n & 15) * 8;
-    *reinterpret_cast<bf16x4*>(Qs + r * kSR + acc_pos(cp)) = bf16x4{x[0], x[1], x[2], x[3]};
-    *reinterpret_cast<bf16x4*>(Qs + r * kSR + acc_pos(cp + 4)) = bf16x4{x[4], x[5], x[6], x[7]};
+  auto put_vrow = [&](bf16* tile, int n, const V16& x) {     // V tiles
+    *reinterpret_cast<V16*>(tile + (n >> 4) * kSV + (n & 15) * 8) = x;
   };
+  auto put_q = [&](int n, const V16& x) { put_row(Qs, n, x); };
   auto tb_of = [&](int c) { return w_tb + (chain * nch + c) * (kC * kC); };
+  // the gate block of a chunk from the 32 f32x4 pieces of (g, gamma): lane
+  // l < 32 of one wave holds piece l (g for l < 16, gamma after); g_C is
+  // g[63], piece 15's last value
+  // (called by a whole wave, l = its lane; lanes 32.. only take part in the
+  // shuffle)
+  auto put_gates = [&](int l, const f32x4& x) {
+    const float gC = __shfl(x[3], 15, 64);
+    if (l >= 32) return;
+    *reinterpret_cast<f32x4*>(Gs + 4 * l) = x;
+    if (l < 16) {
+      f32x4 f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[i] = __builtin_amdgcn_exp2f(fminf(gC - x[i], 0.f));
+      *reinterpret_cast<f32x4*>(Gs + 3 * kC + 4 * l) = f;
+    } else {
+      *reinterpret_cast<f32x4*>(Gs + kC + 4 * l) = -x;     // -gamma at 2 kC + 4 (l - 16)
+    }
+  };
   auto g_of = [&](int c) { return w_g + (chain * nch + c) * (2 * kC); };
   auto q_row0 = [&](int c) { return n_sink + c * kC + window; };
   auto kv_row0 = [&](int c) { return n_sink + c * kC; };
@@ -295,17 +367,17 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
     const int r = n >> 4;
     const bool in = r < n_sink && r < T_;
     put_row(KSk, n, in ? *reinterpret_cast<const V16*>(kb + (size_t)r * kvrow + (n & 15) * 8) : zero8);
-    put_row(VSk, n, in ? *reinterpret_cast<const V16*>(vb + (size_t)r * kvrow + (n & 15) * 8) : zero8);
+    put_vrow(VSk, n, in ? *reinterpret_cast<const V16*>(vb + (size_t)r * kvrow + (n & 15) * 8) : zero8);
   }
   for (int n = tid; n < 3 * 1024; n += kThreads) {
     const int sl = n >> 10;
     put_row(KR + sl * kC * kSR, n & 1023, load_rows(kb, kvrow, kv_row0(sl), n & 1023));
-    put_row(VR + sl * kC * kSR, n & 1023, load_rows(vb, kvrow, kv_row0(sl), n & 1023));
+    put_vrow(VR + sl * kC * kSV, n & 1023, load_rows(vb, kvrow, kv_row0(sl), n & 1023));
   }
   for (int n = tid; n < 1024; n += kThreads) put_q(n, load_rows(qb, qrow, q_row0(0), n));
   *reinterpret_cast<V16*>(TBs + (tid >> 3) * kSC + (tid & 7) * 8) =
       *reinterpret_cast<const V16*>(tb_of(0) + (tid >> 3) * kC + (tid & 7) * 8);
-  if (tid < 32) *reinterpret_cast<f32x4*>(Gs + 4 * tid) = *reinterpret_cast<const f32x4*>(g_of(0) + 4 * tid);
+  if (tid < 64) put_gates(tid, *reinterpret_cast<const f32x4*>(g_of(0) + 4 * (tid & 31)));
   __syncthreads();
 
   // ---------------------------------------------------------- chunks
@@ -319,86 +391,96 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
   // the prefetched TB and gates of chunk c+1 and K, V of chunk c+3; after
   // B3 they commit chunk c+1's queries.
   if (scan_wave) {
-    // state columns 32 wv .. + 31; natural d_k rows 16 mt + 4 g + i
+    // state columns 32 wv .. + 31; tile mt's accumulator row 4 g + i holds
+    // d_k = 32 (mt / 2) + 8 g + 4 (mt % 2) + i (see tr_frag_k)
     const int cw = 32 * wv;
+
     f32x4 S[8][2];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) S[mt][nt] = zero4();
+    V16 pq[4];
     for (int c = 0; c < nch; ++c) {
       const int i0 = n_sink + c * kC;
-      const bf16* Kc = KR + (c % 3) * kC * kSR;
-      const bf16* Vc = VR + (c % 3) * kC * kSR;
-      const float* gl = Gs;
+      const bf16* Kc = KR + ((unsigned)c % 3u) * kC * kSR;
+      const bf16* Vc = VR + ((unsigned)c % 3u) * kC * kSV;
       const float* gam = Gs + kC;
+      // lane parts of the LDS addresses: row reads, V^T and K^T reads,
+      // [64][64] tiles, hand-over rows
+      int l_row = j * kSR + 8 * g, l_tv = (4 * g + (j >> 2)) * kSR + 4 * (j & 3);
+      int l_tk = (4 * g + (j >> 2)) * kSR + 8 * (j & 3), l_acc = j * kSC + 8 * g, l_x = j * kSR + 4 * g;
+      asm volatile("" : "+v"(l_row), "+v"(l_tv), "+v"(l_tk), "+v"(l_acc), "+v"(l_x));
       lds_barrier();                     // B0
-      // ---- O^T = S^T Q^T   [dv tile nt][query tile rt]
-      Frag<bf16> sf[4][2];
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) sf[p][nt] = frag_from_acc<bf16>(S[2 * p][nt], S[2 * p + 1][nt]);
-      f32x4 ot[2][4];
+      // ---- prefetch the queries of chunk c + 1, committed after B3.
+      // Always issued (past the last chunk they reread valid rows and are
+      // not committed), so that the memory counters the compiler waits on
+      // are exact.
+      load_tile4(qb, qrow, q_row0(min(c + 1, nch - 1)), tid, pq);
+      asm volatile("" ::: "memory");     // issue them here, ahead of the products
+      // ---- O^T = S^T Q^T [dv tile nt][query tile rt] and KS = K S [token
+      // tile mt][dv tile nt], one d-step at a time (the state's operand
+      // fragments of a step are formed from its accumulators when needed)
+      f32x4 ot[2][4], KS[4][2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) ot[nt][rt] = zero4();
+        for (int rt = 0; rt < 4; ++rt) {
+          ot[nt][rt] = zero4();
+          KS[rt][nt] = zero4();
+        }
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        Frag<bf16> qf[4];
+        Frag<bf16> sf[2], qf[4], kf[4];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) qf[rt] = lds_frag8(Qs + (16 * rt + j) * kSR + 32 * p + 8 * g);
+        for (int nt = 0; nt < 2; ++nt) sf[nt] = frag_from_acc<bf16>(S[2 * p][nt], S[2 * p + 1][nt]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) qf[rt] = lds_frag8(Qs + l_row + 16 * rt * kSR + 32 * p);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) ot[nt][rt] = mfma(sf[p][nt], qf[rt], ot[nt][rt]);
-      }
-      // ---- KS = K S   [token tile mt][dv tile nt]
-      f32x4 KS[4][2];
+          for (int nt = 0; nt < 2; ++nt) ot[nt][rt] = mfma(sf[nt], qf[rt], ot[nt][rt]);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) KS[mt][nt] = zero4();
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        Frag<bf16> kf[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) kf[mt] = row_frag(Kc, 16 * mt + j, p, g);
+        for (int mt = 0; mt < 4; ++mt) kf[mt] = lds_frag8(Kc + l_row + 16 * mt * kSR + 32 * p);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) KS[mt][nt] = mfma(kf[mt], sf[p][nt], KS[mt][nt]);
+          for (int nt = 0; nt < 2; ++nt) KS[mt][nt] = mfma(kf[mt], sf[nt], KS[mt][nt]);
       }
-      // ---- U = TB V - TB diag(gamma) KS   [token tile mt][dv tile nt]
+      // ---- U = TB V - TB diag(gamma) KS   [token tile mt][dv tile nt];
+      // diag(-gamma) is applied to KS's token rows as its fragments form
+      Frag<bf16> ksf[2][2];
+      {
+        const float* ngam = Gs + 2 * kC;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const f32x4 n0 = *reinterpret_cast<const f32x4*>(ngam + 32 * pp + 4 * g);
+          const f32x4 n1 = *reinterpret_cast<const f32x4*>(ngam + 32 * pp + 16 + 4 * g);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+            ksf[pp][nt] = frag_from_acc_scaled<bf16>(KS[2 * pp][nt], KS[2 * pp + 1][nt], n0, n1);
+        }
+      }
       f32x4 U[4][2];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) U[mt][nt] = zero4();
-      const f32x4 neg = f32x4{-1.f, -1.f, -1.f, -1.f};
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
-        Frag<bf16> tf[4], vf[2], kf[2];
+        Frag<bf16> tf[4], vf[2];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) tf[mt] = lds_frag8(TBs + (16 * mt + j) * kSC + 32 * pp + 8 * g);
+        for (int mt = 0; mt < 4; ++mt) tf[mt] = lds_frag8(TBs + l_acc + 16 * mt * kSC + 32 * pp);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) vf[nt] = tr_frag(Vc, 32 * pp, cw + 16 * nt, lane);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          kf[nt] = frag_from_acc_scaled<bf16>(KS[2 * pp][nt], KS[2 * pp + 1][nt], neg, neg);
+        for (int nt = 0; nt < 2; ++nt) vf[nt] = tr_at(Vc + cw + l_tv, 32 * pp * kSR + 16 * nt);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) U[mt][nt] = mfma(tf[mt], vf[nt], U[mt][nt]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-          tf[mt] = lds_frag8_scaled(TBs + (16 * mt + j) * kSC + 32 * pp + 8 * g, gam + 32 * pp + 4 * g,
-                                    gam + 32 * pp + 16 + 4 * g);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) U[mt][nt] = mfma(tf[mt], kf[nt], U[mt][nt]);
+          for (int nt = 0; nt < 2; ++nt) U[mt][nt] = mfma(tf[mt], ksf[pp][nt], U[mt][nt]);
       }
 
       lds_barrier();                     // B1: A is in LDS
@@ -410,17 +492,13 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) ot[nt][rt] *= gq;
       }
-      const float lgC = gl[kC - 1];
       const float gC = gam[kC - 1];
+      const float* dec = Gs + 3 * kC;    // 2^(g_C - g_s)
       Frag<bf16> uf[2][2], us[2][2];
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
-        f32x4 s0, s1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          s0[i] = __builtin_amdgcn_exp2f(fminf(lgC - gl[32 * pp + 4 * g + i], 0.f));
-          s1[i] = __builtin_amdgcn_exp2f(fminf(lgC - gl[32 * pp + 16 + 4 * g + i], 0.f));
-        }
+        const f32x4 s0 = *reinterpret_cast<const f32x4*>(dec + 32 * pp + 4 * g);
+        const f32x4 s1 = *reinterpret_cast<const f32x4*>(dec + 32 * pp + 16 + 4 * g);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           uf[pp][nt] = frag_from_acc<bf16>(U[2 * pp][nt], U[2 * pp + 1][nt]);
@@ -431,7 +509,7 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
       for (int pp = 0; pp < 2; ++pp) {
         Frag<bf16> af[4];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) af[rt] = lds_frag8(As + (16 * rt + j) * kSC + 32 * pp + 8 * g);
+        for (int rt = 0; rt < 4; ++rt) af[rt] = lds_frag8(As + l_acc + 16 * rt * kSC + 32 * pp);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -446,7 +524,8 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
       for (int mt = 0; mt < 8; ++mt) {
         Frag<bf16> kt[2];
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) kt[pp] = tr_frag(Kc, 32 * pp, 16 * mt, lane);
+        for (int pp = 0; pp < 2; ++pp)
+          kt[pp] = tr_at(Kc + l_tk, 32 * pp * kSR + 32 * (mt >> 1) + 4 * (mt & 1));
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
@@ -466,7 +545,7 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
           for (int nt = 0; nt < 2; ++nt) {
             const int r = 16 * rt + j;
             const int col = cw + 16 * nt + 4 * g;
-            const f32x4 x = ot[nt][rt] * w_lin + load4(Xs + r * kSR + col);
+            const f32x4 x = ot[nt][rt] * w_lin + load4(Xs + cw + l_x + 16 * rt * kSR + 16 * nt);
             const bf16x4 y = bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
                                     static_cast<bf16>(x[3])};
             typedef unsigned int u2 __attribute__((ext_vector_type(2)));
@@ -474,6 +553,10 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
           }
       }
       lds_barrier();                     // B3: the softmax rows are read
+      if (c + 1 < nch) {
+#pragma unroll
+        for (int m2 = 0; m2 < 4; ++m2) put_q(tid + 256 * m2, pq[m2]);
+      }
     }
     if (write_state) {
       float* Sg = state_out + chain * kD * kD;
@@ -482,7 +565,8 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Sg[(size_t)(16 * mt + 4 * g + i) * kD + cw + 16 * nt + j] = S[mt][nt][i];
+          for (int i = 0; i < 4; ++i)
+            Sg[(size_t)(32 * (mt >> 1) + 8 * g + 4 * (mt & 1) + i) * kD + cw + 16 * nt + j] = S[mt][nt][i];
     }
     return;
   }
@@ -499,27 +583,17 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
       const int tq = t0 + j;
       const int tl = min(tq, nrow - 1);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(qb + (size_t)tl * qrow + 32 * p + 4 * g);
-        const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(qb + (size_t)tl * qrow + 32 * p + 16 + 4 * g);
-        qf[p].v = bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-      }
+      for (int p = 0; p < 4; ++p) qf[p].v = *reinterpret_cast<const bf16x8*>(qb + (size_t)tl * qrow + 32 * p + 8 * g);
       const KeyPair kp[5] = {{KSk, VSk, 0, 0, true},
                              {KR, VR, 0, n_sink, false},
                              {KR, VR, 32, n_sink + 32, false},
-                             {KR + kC * kSR, VR + kC * kSR, 0, n_sink + 64, false},
-                             {KR + kC * kSR, VR + kC * kSR, 32, n_sink + 96, false}};
-      bool use[5], have[5];
+                             {KR + kC * kSR, VR + kC * kSV, 0, n_sink + 64, false},
+                             {KR + kC * kSR, VR + kC * kSV, 32, n_sink + 96, false}};
       f32x4 st[5][2];
-#pragma unroll
-      for (int pi = 0; pi < 5; ++pi) {
-        use[pi] = pi == 0 ? n_sink > 0 : kp[pi].kk0 <= t0 + 15 && kp[pi].kk0 < T_;
-        have[pi] = false;
-      }
-      const float m = sm_scores<5>(kp, use, st, have, qf, t0, n_sink, window, T_, lane);
+      const float m = sm_scores<5, 0>(kp, st, qf, t0, n_sink, window, lane);
       f32x4 oacc[8];
       float inv_l;
-      sm_values<5>(kp, use, st, m, lane, oacc, inv_l);
+      sm_values<5>(kp, st, m, lane, oacc, inv_l);
       if (tq < nrow) {
         const float f = w_swa * inv_l;
 #pragma unroll
@@ -528,120 +602,251 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
     }
   }
 
-  V16 pq[4], pt[2], pk[4], pv[4];
+  // Rows r = 16 jq + j of chunk c are the times t = i0 + window + r.  They
+  // attend to the ring keys at offsets (from i0) 16 jq + 1 + j .. 16 jq +
+  // window + j, all inside the five 32-key blocks pb .. pb + 4, pb = jq / 2
+  // (window <= 128); block b holds offsets 32 b .. + 31, rows 32 (b % 2) ..
+  // of ring chunk c + b / 2.  Slot 0 is block pb, whose scores the chunk's
+  // own score tiles give (blocks 0 and 1 are chunk c); slots 1-3 are blocks
+  // 2, 3, 4; slot 4 is block 5 (pb = 1) or block 1 (pb = 0, recomputed so
+  // that every wave runs the same code); slot 5 is the sink block.
+  const int pb = jq >> 1;
+  const int bX = pb ? 5 : 1;
+  // A block needs the window mask iff some of its keys lie outside some
+  // row's window; the other blocks are attended by all 16 rows.
+  auto partial = [&](int b) { return !(32 * b >= 16 * jq + 16 && 32 * b + 31 <= 16 * jq + window); };
+  const bool mk0 = partial(pb), mk1 = partial(2), mk2 = partial(3), mk3 = partial(4), mk4 = partial(bX);
+  // key 16 hf + 4 g + i of block b is in row j's window iff
+  // e0 + 32 b + 16 hf + i lies in [0, window)
+  const int e0 = 4 * g - 16 * jq - j - 1;
+  auto mask_block = [&](f32x4 (&x)[2], int b, int e) {
+    const int d0 = e + 32 * b;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        x[hf][i] = (unsigned)(d0 + 16 * hf + i) < (unsigned)window ? x[hf][i] : -INFINITY;
+  };
+  // the sink scores accumulate onto 0 (key 4 g + i < n_sink) or -inf; loop
+  // rows are later than every sink, and keys 16 .. 31 of the block are none
+  f32x4 sbias;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sbias[i] = 4 * g + i < n_sink ? 0.f : -INFINITY;
+  const float scale = kLog2e / sqrtf((float)kD);
+  Frag<bf16> ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones.v[e] = static_cast<bf16>(1.f);
+
+  V16 pk[4], pv[4], pt[2];
   f32x4 pg;
   for (int c = 0; c < nch; ++c) {
     const int i0 = n_sink + c * kC;
-    const bf16* Kc = KR + (c % 3) * kC * kSR;
-    const bf16* Vc = VR + (c % 3) * kC * kSR;
+    const bf16* Kc = KR + ((unsigned)c % 3u) * kC * kSR;
+    const bf16* Vc = VR + ((unsigned)c % 3u) * kC * kSV;
+    const bf16* K1 = KR + ((unsigned)(c + 1) % 3u) * kC * kSR;
+    const bf16* V1 = VR + ((unsigned)(c + 1) % 3u) * kC * kSV;
+    const bf16* K2 = KR + ((unsigned)(c + 2) % 3u) * kC * kSR;
+    const bf16* V2 = VR + ((unsigned)(c + 2) % 3u) * kC * kSV;
+    const bf16* KX = KR + ((unsigned)(c + 2 * pb) % 3u) * kC * kSR;
+    const bf16* VX = VR + ((unsigned)(c + 2 * pb) % 3u) * kC * kSV;
     const float* gl = Gs;
+    // lane parts of the LDS addresses: row reads, V^T reads, A rows
+    int l_row = j * kSR + 8 * g, l_tv = (4 * g + (j >> 2)) * kSR + 4 * (j & 3), l_acc = j * kSC + 8 * g;
+    asm volatile("" : "+v"(l_row), "+v"(l_tv), "+v"(l_acc));
     lds_barrier();                       // B0: chunk c is in LDS
-    // ---- prefetch, committed after the chunk: queries, TB, gates of c + 1
-    // and K, V of chunk c + 3.  Always issued (past the last chunk they
-    // reread valid rows and are not committed), so that the memory
-    // counters the compiler waits on are exact.
+    // ---- prefetch TB and the gates of chunk c + 1, committed after B2
+    // (always issued, as the other prefetches)
     {
       const int cn = min(c + 1, nch - 1);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) pq[m] = load_rows(qb, qrow, q_row0(cn), ptid + 256 * m);
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const int n = ptid + 256 * m;
         pt[m] = *reinterpret_cast<const V16*>(tb_of(cn) + (n >> 3) * kC + (n & 7) * 8);
       }
       pg = *reinterpret_cast<const f32x4*>(g_of(cn) + 4 * (ptid & 31));
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        pk[m] = load_rows(kb, kvrow, kv_row0(c + 3), ptid + 256 * m);
-        pv[m] = load_rows(vb, kvrow, kv_row0(c + 3), ptid + 256 * m);
-      }
+      asm volatile("" ::: "memory");     // issue them here, ahead of the scores
     }
-    // ---- query-key scores of rows r = 16 jq + j (lane column) against the
-    // window (ring chunks c, c+1, c+2) and the sinks; the chunk's own keys
-    // also give A
+    // ---- scores (S^T tiles: key 4 g + i of each 16-key half, query j), in
+    // batches of two 16-key tiles whose K reads are issued one batch ahead
+    // of their products (the scheduling barriers keep that order)
+    const int r = 16 * jq + j;
     Frag<bf16> qf[4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) qf[p] = lds_frag8(Qs + (16 * jq + j) * kSR + 32 * p + 8 * g);
-    f32x4 st[7][2];
+    for (int p = 0; p < 4; ++p) qf[p] = lds_frag8(Qs + l_row + 16 * jq * kSR + 32 * p);
+    const float lr = gl[r];
+    f32x4 ls[4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      f32x4 acc = zero4();
+    for (int kt = 0; kt < 4; ++kt) ls[kt] = *reinterpret_cast<const f32x4*>(gl + 16 * kt + 4 * g);
+    auto kfr = [&](const bf16* X, int row0, Frag<bf16> (&f)[4]) {
 #pragma unroll
-      for (int p = 0; p < 4; ++p) acc = mfma(row_frag(Kc, 16 * kt + j, p, g), qf[p], acc);
-      st[kt >> 1][kt & 1] = acc;
-    }
-    // A rows: [s <= r] 2^{g_r - g_s} q_r.k_s, columns in acc order
+      for (int p = 0; p < 4; ++p) f[p] = lds_frag8(X + l_row + row0 * kSR + 32 * p);
+    };
+    auto kmma = [&](const Frag<bf16> (&f)[4], f32x4 acc) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) acc = mfma(f[p], qf[p], acc);
+      return acc;
+    };
+    Frag<bf16> ka[4], kb2[4], kc[4], kd[4];
+    f32x4 sa[4], st[6][2];
+    kfr(Kc, 0, ka);
+    kfr(Kc, 16, kb2);
+    __builtin_amdgcn_sched_barrier(0);
+    kfr(Kc, 32, kc);
+    kfr(Kc, 48, kd);
+    sa[0] = kmma(ka, zero4());
+    sa[1] = kmma(kb2, zero4());
+    __builtin_amdgcn_sched_barrier(0);
+    kfr(K1, 0, ka);
+    kfr(K1, 16, kb2);
+    sa[2] = kmma(kc, zero4());
+    sa[3] = kmma(kd, zero4());
+    __builtin_amdgcn_sched_barrier(0);
+    kfr(K1, 32, kc);
+    kfr(K1, 48, kd);
+    st[1][0] = kmma(ka, zero4());
+    st[1][1] = kmma(kb2, zero4());
+    // A rows: [s <= r] 2^{g_r - g_s} q_r.k_s, columns in acc order; tile
+    // kt is below the diagonal (kt < jq), on it, or above (zero)
     {
-      const int r = 16 * jq + j;
-      const float lr = gl[r];
+      int jj = j;
+      asm volatile("" : "+v"(jj));
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const f32x4 ls = *reinterpret_cast<const f32x4*>(gl + 16 * kt + 4 * g);
         f32x4 x;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int s_ = 16 * kt + 4 * g + i;
-          x[i] = s_ <= r ? __builtin_amdgcn_exp2f(fminf(lr - ls[i], 0.f)) * st[kt >> 1][kt & 1][i] : 0.f;
+          const float dec = __builtin_amdgcn_exp2f(fminf(lr - ls[kt][i], 0.f));
+          x[i] = kt < jq || (kt == jq && 4 * g + i <= jj) ? dec * sa[kt][i] : 0.f;
         }
-        store4(As + r * kSC + acc_pos(16 * kt + 4 * g), x);
+        store4(As + l_acc + 16 * jq * kSC + 32 * (kt >> 1) + 4 * (kt & 1), x);
       }
     }
-    const int t0 = i0 + window + 16 * jq;
-    const bf16* K1 = KR + ((c + 1) % 3) * kC * kSR;
-    const bf16* V1 = VR + ((c + 1) % 3) * kC * kSR;
-    const bf16* K2 = KR + ((c + 2) % 3) * kC * kSR;
-    const bf16* V2 = VR + ((c + 2) % 3) * kC * kSR;
-    const KeyPair kp[7] = {{Kc, Vc, 0, i0, false},       {Kc, Vc, 32, i0 + 32, false},
-                           {K1, V1, 0, i0 + 64, false},  {K1, V1, 32, i0 + 96, false},
-                           {K2, V2, 0, i0 + 128, false}, {K2, V2, 32, i0 + 160, false},
-                           {KSk, VSk, 0, 0, true}};
-    bool use[7], have[7];
+    __builtin_amdgcn_sched_barrier(0);
+    kfr(K2, 0, ka);
+    kfr(K2, 16, kb2);
+    st[2][0] = kmma(kc, zero4());
+    st[2][1] = kmma(kd, zero4());
+    __builtin_amdgcn_sched_barrier(0);
+    kfr(KX, 32, kc);
+    kfr(KX, 48, kd);
+    st[3][0] = kmma(ka, zero4());
+    st[3][1] = kmma(kb2, zero4());
+    __builtin_amdgcn_sched_barrier(0);
+    kfr(KSk, 0, ka);
+    st[4][0] = kmma(kc, zero4());
+    st[4][1] = kmma(kd, zero4());
+    __builtin_amdgcn_sched_barrier(0);
+    st[5][0] = kmma(ka, sbias);
+    st[5][1] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-    for (int pi = 0; pi < 6; ++pi) {
-      // some key of the pair may be in some row's window (t - window, t]
-      const int kk0 = kp[pi].kk0;
-      use[pi] = kk0 + 31 > t0 - window && kk0 <= t0 + 15 && kk0 < T_;
-      have[pi] = pi < 2;
-    }
-    use[6] = n_sink > 0;
-    have[6] = false;
-    const float m = sm_scores<7>(kp, use, st, have, qf, t0, n_sink, window, T_, lane);
+    for (int hf = 0; hf < 2; ++hf) st[0][hf] = pb ? sa[2 + hf] : sa[hf];
+    // ---- window masks (blocks with keys outside some row's window) and the
+    // row maximum
+    // (e0 passes through an empty asm so that the compares stay in the loop:
+    // hoisted, their lane masks would not fit the scalar registers)
+    int e = e0;
+    asm volatile("" : "+v"(e));
+    if (mk0) mask_block(st[0], pb, e);
+    if (mk1) mask_block(st[1], 2, e);
+    if (mk2) mask_block(st[2], 3, e);
+    if (mk3) mask_block(st[3], 4, e);
+    if (mk4) mask_block(st[4], bX, e);
+    float m = -INFINITY;
+#pragma unroll
+    for (int sl = 0; sl < 6; ++sl)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        m = fmaxf(fmaxf(m, fmaxf(st[sl][hf][0], st[sl][hf][1])), fmaxf(st[sl][hf][2], st[sl][hf][3]));
+    m = max_lane_groups(m);
+    m = m == -INFINITY ? 0.f : m;      // a row with no key (past the sequence): weights 0
     lds_barrier();                       // B1
-    f32x4 oacc[8];
-    float inv_l;
-    sm_values<7>(kp, use, st, m, lane, oacc, inv_l);
+    // ---- prefetch K, V of chunk c + 3 (committed after B2; always issued,
+    // rows past the sequence clamped)
+    load_tile4(kb, kvrow, kv_row0(c + 3), ptid, pk);
+    load_tile4(vb, kvrow, kv_row0(c + 3), ptid, pv);
+    asm volatile("" ::: "memory");       // issue them here, ahead of the softmax
+    // ---- weights 2^((s - m) log2(e) / sqrt(d)), their sum (on the matrix
+    // cores, against a ones operand) and O^T tiles (d = 16 dt + 4 g + i,
+    // query j); the V^T reads of a slot are issued one slot ahead
+    const float mb = -m * scale;
+    auto vfr = [&](const bf16* X, int r0, Frag<bf16> (&f)[8]) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) f[dt] = tr_at(X + l_tv, r0 * kSR + 16 * dt);
+    };
+    auto pfr = [&](const f32x4 (&x)[2]) {
+      f32x4 p0, p1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[0][i], scale, mb));
+        p1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[1][i], scale, mb));
+      }
+      return frag_from_acc<bf16>(p0, p1);
+    };
+    f32x4 lacc = zero4(), oacc[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) oacc[dt] = zero4();
+    auto vmma = [&](const Frag<bf16> (&f)[8], const Frag<bf16>& pf) {
+      lacc = mfma(ones, pf, lacc);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) oacc[dt] = mfma(f[dt], pf, oacc[dt]);
+    };
+    Frag<bf16> va[8], vb2[8], pa, pb2;
+    vfr(Vc, 32 * pb, va);
+    pa = pfr(st[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    vfr(V1, 0, vb2);
+    pb2 = pfr(st[1]);
+    vmma(va, pa);
+    __builtin_amdgcn_sched_barrier(0);
+    vfr(V1, 32, va);
+    pa = pfr(st[2]);
+    vmma(vb2, pb2);
+    __builtin_amdgcn_sched_barrier(0);
+    vfr(V2, 0, vb2);
+    pb2 = pfr(st[3]);
+    vmma(va, pa);
+    __builtin_amdgcn_sched_barrier(0);
+    vfr(VX, 32, va);
+    pa = pfr(st[4]);
+    vmma(vb2, pb2);
+    __builtin_amdgcn_sched_barrier(0);
+    // the sink block: 16 keys, read once and used for both halves (the
+    // second half weighs 0)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(VSk + l_tv + 16 * dt));
+      vb2[dt].v = bf16x8{x[0], x[1], x[2], x[3], x[0], x[1], x[2], x[3]};
+    }
+    pb2 = pfr(st[5]);
+    vmma(va, pa);
+    __builtin_amdgcn_sched_barrier(0);
+    vmma(vb2, pb2);
+    // the bf16 weights summed (the same rounding as the weights P V uses)
+    const float inv_l = lacc[0] > 0.f ? 1.f / lacc[0] : 0.f;
     // ---- the softmax rows, w_swa-weighted, into the query tile ([row][d])
     {
-      const int r = 16 * jq + j;
       const float f = w_swa * inv_l;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) store4(Xs + r * kSR + 16 * dt + 4 * g, oacc[dt] * f);
+      for (int dt = 0; dt < 8; ++dt) store4(Xs + l_row - 4 * g + 16 * jq * kSR + 16 * dt, oacc[dt] * f);
     }
     lds_barrier();                       // B2
-    // ---- commit TB and gates of chunk c + 1, K and V of chunk c + 3 (into
-    // the ring slot chunk c leaves)
+    // ---- commit K, V of chunk c + 3 into the ring slot chunk c leaves (past
+    // the sequence: its clamped last row, a key no row attends), then TB
+    // and the gates of chunk c + 1 (their last reads were before B2)
+#pragma unroll
+    for (int m2 = 0; m2 < 4; ++m2) {
+      put_row(KR + ((unsigned)c % 3u) * kC * kSR, ptid + 256 * m2, pk[m2]);
+      put_vrow(VR + ((unsigned)c % 3u) * kC * kSV, ptid + 256 * m2, pv[m2]);
+    }
     if (c + 1 < nch) {
 #pragma unroll
       for (int m2 = 0; m2 < 2; ++m2) {
         const int n = ptid + 256 * m2;
         *reinterpret_cast<V16*>(TBs + (n >> 3) * kSC + (n & 7) * 8) = pt[m2];
       }
-      if (ptid < 32) *reinterpret_cast<f32x4*>(Gs + 4 * ptid) = pg;
-    }
-    if (kv_row0(c + 3) < T_) {
-      bf16* Ks3 = KR + (c % 3) * kC * kSR;
-      bf16* Vs3 = VR + (c % 3) * kC * kSR;
-#pragma unroll
-      for (int m2 = 0; m2 < 4; ++m2) {
-        put_row(Ks3, ptid + 256 * m2, pk[m2]);
-        put_row(Vs3, ptid + 256 * m2, pv[m2]);
-      }
+      if (ptid < 64) put_gates(ptid, pg);
     }
     lds_barrier();                       // B3: the softmax rows are read
-    if (c + 1 < nch) {
-#pragma unroll
-      for (int m2 = 0; m2 < 4; ++m2) put_q(ptid + 256 * m2, pq[m2]);
-    }
   }
 }
 
