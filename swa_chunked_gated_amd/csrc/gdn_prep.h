@@ -32,6 +32,30 @@ namespace prep {
 constexpr int kC = 64;          // chunk length
 constexpr int kSL = 68;         // fp32 stride of the 64x64 solve buffer
 
+// Layouts of the fp32 solve buffer, by 16-row block rows R = 0..3.  Square:
+// the whole 64 x 64 matrix, row stride kSL.  Packed: only the blocks on and
+// below the diagonal, block row R holding 16 (R + 1) columns at row stride
+// 16 (R + 1) + 4 (each stride spreads a 16-lane column read over distinct
+// banks): 11 KiB instead of 17, so that more preparation waves fit a
+// compute unit.
+struct SquareL {
+  static constexpr int size = kC * kSL;
+  __host__ __device__ static constexpr int stride(int) { return kSL; }
+  __host__ __device__ static constexpr int row0(int R) { return 16 * R * kSL; }
+};
+struct PackedL {
+  static constexpr int size = 16 * (20 + 36 + 52 + 68);
+  __host__ __device__ static constexpr int stride(int R) { return 16 * (R + 1) + 4; }
+  __host__ __device__ static constexpr int row0(int R) {
+    return R == 0 ? 0 : R == 1 ? 16 * 20 : R == 2 ? 16 * (20 + 36) : 16 * (20 + 36 + 52);
+  }
+};
+// block (R, C) of the solve buffer; element (r, s) of the matrix
+template <class LL>
+__device__ __forceinline__ float* lblk(float* Lf, int R, int C) { return Lf + LL::row0(R) + 16 * C; }
+template <class LL>
+__device__ __forceinline__ int lidx(int r, int s) { return LL::row0(r >> 4) + (r & 15) * LL::stride(r >> 4) + s; }
+
 // Orders this wave's LDS accesses: every earlier LDS operation has completed
 // before any later one is issued (no workgroup barrier).
 __device__ __forceinline__ void wave_lds_fence() {
@@ -86,21 +110,24 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// C += A(16x16) B(16x16), both fp32 row-major in LDS.
+// C += A(16x16) B(16x16), both fp32 row-major in LDS (row strides SA, SB).
+template <int SA, int SB>
 __device__ __forceinline__ f32x4 mm16(const float* A, const float* B, f32x4 c, int l16, int lg) {
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) c = mfma4(A[l16 * kSL + 4 * kk + lg], B[(4 * kk + lg) * kSL + l16], c);
+  for (int kk = 0; kk < 4; ++kk) c = mfma4(A[l16 * SA + 4 * kk + lg], B[(4 * kk + lg) * SB + l16], c);
   return c;
 }
-// C += A(16x16, LDS) Y(16x16, accumulator registers of this wave).
+// C += A(16x16, LDS, row stride SA) Y(16x16, accumulator registers of this wave).
+template <int SA>
 __device__ __forceinline__ f32x4 mm16_acc(const float* A, const f32x4& Y, f32x4 c, int l16, int lg) {
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) c = mfma4(A[l16 * kSL + 4 * lg + kk], Y[kk], c);
+  for (int kk = 0; kk < 4; ++kk) c = mfma4(A[l16 * SA + 4 * lg + kk], Y[kk], c);
   return c;
 }
+template <int S>
 __device__ __forceinline__ void st16(float* blk, const f32x4& x, int l16, int lg) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) blk[(4 * lg + i) * kSL + l16] = x[i];
+  for (int i = 0; i < 4; ++i) blk[(4 * lg + i) * S + l16] = x[i];
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts inside
@@ -122,27 +149,31 @@ __device__ __forceinline__ float wave_prefix_sum(float x, int lane) {
   return x + off;
 }
 
-// (I + L)^-1 in place for the strictly lower 64 x 64 L in Lf (fp32, unit
-// diagonal implied, upper part zero), by one wave: 16x16 diagonal blocks by
-// forward substitution (lane = block x column j; row r of the block's inverse
-// column is e_j[r] - sum_{s<r} L[r][s] x[s], with L's rows read as 16-byte
-// pieces), then the off-diagonal blocks by block recursion on fp32 MFMA
-// (exact fp32 products).  A wave's LDS operations complete in program order;
-// wave_lds_fence marks the phases.
+// (I + L)^-1 in place for the strictly lower 64 x 64 L in Lf (fp32, layout
+// LL, unit diagonal implied, zero on and above the diagonal of the diagonal
+// blocks), by one wave: 16x16 diagonal blocks by forward substitution (lane
+// = block x column j; row r of the block's inverse column is e_j[r] -
+// sum_{s<r} L[r][s] x[s], with L's rows read as 16-byte pieces), then the
+// off-diagonal blocks by block recursion on fp32 MFMA (exact fp32 products).
+// A wave's LDS operations complete in program order; wave_lds_fence marks
+// the phases.
+template <class LL>
 __device__ __forceinline__ void unit_lower_inverse_wave(float* Lf, int lane) {
   const int l16 = lane & 15;
   const int lg = lane >> 4;
+  constexpr int S0 = LL::stride(0), S1 = LL::stride(1), S2 = LL::stride(2), S3 = LL::stride(3);
   {
     const int blk = lane >> 4;
     const int j = l16;
-    float* Lb = Lf + 16 * blk * kSL + 16 * blk;
+    const int SB = LL::stride(blk);
+    float* Lb = Lf + LL::row0(blk) + 16 * blk;
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float lr[16];
 #pragma unroll
       for (int q4 = 0; q4 < (r + 3) / 4; ++q4) {
-        const f32x4 t = *reinterpret_cast<const f32x4*>(&Lb[r * kSL + 4 * q4]);
+        const f32x4 t = *reinterpret_cast<const f32x4*>(&Lb[r * SB + 4 * q4]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) lr[4 * q4 + e] = t[e];
       }
@@ -152,44 +183,47 @@ __device__ __forceinline__ void unit_lower_inverse_wave(float* Lf, int lane) {
       x[r] = acc;
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) Lb[r * kSL + j] = x[r];
+    for (int r = 0; r < 16; ++r) Lb[r * SB + j] = x[r];
   }
   wave_lds_fence();
   // level 1: X10 = -X11 L10 X00, X32 = -X33 L32 X22
-  f32x4 x10[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int o0 = 32 * u;
-    const f32x4 y = mm16(Lf + (o0 + 16) * kSL + o0, Lf + o0 * kSL + o0, zero4(), l16, lg);
-    x10[u] = -mm16_acc(Lf + (o0 + 16) * kSL + o0 + 16, y, zero4(), l16, lg);
+  {
+    const f32x4 y0 = mm16<S1, S0>(lblk<LL>(Lf, 1, 0), lblk<LL>(Lf, 0, 0), zero4(), l16, lg);
+    const f32x4 x10 = -mm16_acc<S1>(lblk<LL>(Lf, 1, 1), y0, zero4(), l16, lg);
+    const f32x4 y1 = mm16<S3, S2>(lblk<LL>(Lf, 3, 2), lblk<LL>(Lf, 2, 2), zero4(), l16, lg);
+    const f32x4 x32 = -mm16_acc<S3>(lblk<LL>(Lf, 3, 3), y1, zero4(), l16, lg);
+    st16<S1>(lblk<LL>(Lf, 1, 0), x10, l16, lg);
+    st16<S3>(lblk<LL>(Lf, 3, 2), x32, l16, lg);
   }
-#pragma unroll
-  for (int u = 0; u < 2; ++u) st16(Lf + (32 * u + 16) * kSL + 32 * u, x10[u], l16, lg);
   wave_lds_fence();
   // level 2: bottom-left 32x32 block = -X_BR (L_BL X_TL); every product is
-  // read before any of the four 16x16 blocks is overwritten
+  // read before any of the four 16x16 blocks is overwritten.  Block (R, C),
+  // R = 2, 3, C = 0, 1: first Y = sum_{K = C..1} L(R, K) X(K, C), then
+  // -sum_{K = 2..R} X(R, K) Y(K, C).
   f32x4 y[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int br = 32 + 16 * (u >> 1);
-    const int bc = 16 * (u & 1);
-    y[u] = zero4();
-    for (int kb = bc; kb < 32; kb += 16) y[u] = mm16(Lf + br * kSL + kb, Lf + kb * kSL + bc, y[u], l16, lg);
-  }
+  y[0] = mm16<S2, S0>(lblk<LL>(Lf, 2, 0), lblk<LL>(Lf, 0, 0), zero4(), l16, lg);
+  y[0] = mm16<S2, S1>(lblk<LL>(Lf, 2, 1), lblk<LL>(Lf, 1, 0), y[0], l16, lg);
+  y[1] = mm16<S2, S1>(lblk<LL>(Lf, 2, 1), lblk<LL>(Lf, 1, 1), zero4(), l16, lg);
+  y[2] = mm16<S3, S0>(lblk<LL>(Lf, 3, 0), lblk<LL>(Lf, 0, 0), zero4(), l16, lg);
+  y[2] = mm16<S3, S1>(lblk<LL>(Lf, 3, 1), lblk<LL>(Lf, 1, 0), y[2], l16, lg);
+  y[3] = mm16<S3, S1>(lblk<LL>(Lf, 3, 1), lblk<LL>(Lf, 1, 1), zero4(), l16, lg);
   wave_lds_fence();
-#pragma unroll
-  for (int u = 0; u < 4; ++u) st16(Lf + (32 + 16 * (u >> 1)) * kSL + 16 * (u & 1), y[u], l16, lg);
+  st16<S2>(lblk<LL>(Lf, 2, 0), y[0], l16, lg);
+  st16<S2>(lblk<LL>(Lf, 2, 1), y[1], l16, lg);
+  st16<S3>(lblk<LL>(Lf, 3, 0), y[2], l16, lg);
+  st16<S3>(lblk<LL>(Lf, 3, 1), y[3], l16, lg);
   wave_lds_fence();
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int br = 32 + 16 * (u >> 1);
-    const int bc = 16 * (u & 1);
-    y[u] = zero4();
-    for (int kb = 32; kb <= br; kb += 16) y[u] = mm16(Lf + br * kSL + kb, Lf + kb * kSL + bc, y[u], l16, lg);
-  }
+  y[0] = mm16<S2, S2>(lblk<LL>(Lf, 2, 2), lblk<LL>(Lf, 2, 0), zero4(), l16, lg);
+  y[1] = mm16<S2, S2>(lblk<LL>(Lf, 2, 2), lblk<LL>(Lf, 2, 1), zero4(), l16, lg);
+  y[2] = mm16<S3, S2>(lblk<LL>(Lf, 3, 2), lblk<LL>(Lf, 2, 0), zero4(), l16, lg);
+  y[2] = mm16<S3, S3>(lblk<LL>(Lf, 3, 3), lblk<LL>(Lf, 3, 0), y[2], l16, lg);
+  y[3] = mm16<S3, S2>(lblk<LL>(Lf, 3, 2), lblk<LL>(Lf, 2, 1), zero4(), l16, lg);
+  y[3] = mm16<S3, S3>(lblk<LL>(Lf, 3, 3), lblk<LL>(Lf, 3, 1), y[3], l16, lg);
   wave_lds_fence();
-#pragma unroll
-  for (int u = 0; u < 4; ++u) st16(Lf + (32 + 16 * (u >> 1)) * kSL + 16 * (u & 1), -y[u], l16, lg);
+  st16<S2>(lblk<LL>(Lf, 2, 0), -y[0], l16, lg);
+  st16<S2>(lblk<LL>(Lf, 2, 1), -y[1], l16, lg);
+  st16<S3>(lblk<LL>(Lf, 3, 0), -y[2], l16, lg);
+  st16<S3>(lblk<LL>(Lf, 3, 1), -y[3], l16, lg);
   wave_lds_fence();
 }
 
@@ -207,7 +241,8 @@ struct PrepSmem {
   static_assert(!FULL || (kC * SV * (int)sizeof(T) <= 4 * kC * kSL && SC * (int)sizeof(T) <= 4 * kSL),
                 "TBG rows and V rows fit the solve buffer");
   static constexpr int bytesT = (nT * (int)sizeof(T) + 15) / 16 * 16;
-  static constexpr int nL = kC * kSL;                       // solve buffer
+  using LL = typename std::conditional<FULL, SquareL, PackedL>::type;
+  static constexpr int nL = LL::size;                       // solve buffer
   static constexpr int bytes = bytesT + 4 * (nL + 4 * kC);  // + g, gamma, b, K^T factors
 };
 
@@ -225,6 +260,7 @@ __device__ __forceinline__ void gdn_prep_chunk(
     float* __restrict__ wut, float* __restrict__ wg, int T_, int H, int Hkv, int n_sink, int window,
     int nch, int c, int h, int bi, unsigned char* smem_raw) {
   using SM = PrepSmem<T, D, FULL>;
+  using LL = typename SM::LL;
   constexpr int EPC = 16 / (int)sizeof(T);     // elements per 16-byte piece
   constexpr int QV = 8 / EPC;                  // 16-byte pieces per fragment
   constexpr int KS = D / 32;                   // 32-wide k-steps over d
@@ -292,9 +328,9 @@ __device__ __forceinline__ void gdn_prep_chunk(
   // ---- zero the solve buffer (and the score tile, whose strictly upper
   // 16x16 tiles stay zero); gates: g = inclusive cumsum of log2 a, gamma =
   // 2^g, b
-#pragma unroll
-  for (int i = lane; i < SM::nL / 4; i += 64) reinterpret_cast<f32x4*>(Lf)[i] = zero4();
   if constexpr (FULL) {
+#pragma unroll
+    for (int i = lane; i < SM::nL / 4; i += 64) reinterpret_cast<f32x4*>(Lf)[i] = zero4();
 #pragma unroll
     for (int i = lane; i < kC * SC / EPC; i += 64) {
       V16 z;
@@ -334,7 +370,7 @@ __device__ __forceinline__ void gdn_prep_chunk(
       for (int i = 0; i < 4; ++i) {
         const int r = r0 + i;
         const float dec = __builtin_amdgcn_exp2f(fminf(lr[i] - ls, 0.f));
-        Lf[r * kSL + s] = s < r ? br[i] * dec * acc[i] : 0.f;
+        Lf[lidx<LL>(r, s)] = s < r ? br[i] * dec * acc[i] : 0.f;
         if constexpr (FULL) As[r * SC + acc_pos(s)] = from_f32<T>(s <= r ? dec * accq[i] : 0.f);
       }
     }
@@ -360,7 +396,7 @@ __device__ __forceinline__ void gdn_prep_chunk(
       put16<DEV>(aa, r * kC + pc, *reinterpret_cast<const V16*>(&As[r * SC + pc]));
     }
   }
-  unit_lower_inverse_wave(Lf, lane);
+  unit_lower_inverse_wave<LL>(Lf, lane);
 
   // full preparation: the chunk's V rows (zero past the stream end), loaded
   // now and staged once the solve buffer is free
@@ -389,7 +425,8 @@ __device__ __forceinline__ void gdn_prep_chunk(
   for (int i = lane; i < kC * kC / 4; i += 64) {
     const int r = i >> 4;
     const int s0 = (i & 15) * 4;
-    const f32x4 tm = *reinterpret_cast<const f32x4*>(&Lf[r * kSL + s0]);
+    // (the packed layout holds no blocks above the diagonal: zero there)
+    const f32x4 tm = (s0 >> 4) <= (r >> 4) ? *reinterpret_cast<const f32x4*>(&Lf[lidx<LL>(r, s0)]) : zero4();
     const f32x4 bb = *reinterpret_cast<const f32x4*>(&bet[s0]);
     const f32x4 gg = *reinterpret_cast<const f32x4*>(&gam[s0]);
     const f32x4 x = tm * bb;
