@@ -75,6 +75,13 @@ def linear_flops(w):
     return gdn_flops(w) if w.update == "gdn" else gla_flops(w)
 
 
+def gdn_prep_flops(w):
+    """The part of gdn_flops the chunk preparation runs: the K K^T tiles of
+    each chunk, 2 C dk per stream token and query head."""
+    stream = max(0, w.T - w.budget)
+    return w.B * w.H * stream * 2 * CHUNK * w.d
+
+
 def swa_flops(w, T=None):
     """Softmax branch: 4 min(t+1, N) d per query row and head."""
     T = w.T if T is None else T
@@ -91,6 +98,15 @@ def prefill_bytes(w):
     if w.write_state:
         b += w.B * w.H * d * d * 4
     return b
+
+
+def tb_bytes(w):
+    """The chunk preparation's per-chunk results the layer reads back: TB
+    [64][64] in the I/O type and g, gamma [2][64] fp32, per chunk and query
+    head."""
+    elt = 4 if w.dtype == "f32" else 2
+    nch = -(-max(0, w.T - w.budget) // CHUNK)
+    return w.B * w.H * nch * (CHUNK * CHUNK * elt + 2 * CHUNK * 4)
 
 
 def shortconv_bytes(w):
@@ -122,12 +138,13 @@ def shortconv_decode_bytes(w, elt=2):
 
 # Kernels each call launches, by workload (the library's launch choice:
 # bf16 GDN with B*H*d/64 < 256 runs preparation, scan and, with both
-# branches, the softmax tiles as one launch; otherwise the light
-# preparation, then the many-chain scan; the softmax branch keeps its key
-# blocks resident when every workgroup walks at least four 64-row tiles).
+# branches, the softmax tiles as one launch; bf16 GDN at d = 128 with both
+# branches, window <= 128 and at most 16 sinks otherwise runs the light
+# preparation, then the one-pass layer ("prepare" and "layer2": two
+# launches, timed one by one through the two-phase flags); otherwise the
+# light preparation, then the many-chain scan, and the softmax kernel).
 CALL_KERNELS = {
-    "longctx_b8_t32768": {"linear": "gdn_prep_kernel+linear_chunk_kernel",
-                          "softmax": "swa_ring_kernel"},
+    "longctx_b8_t32768": {"prepare": "gdn_prep_kernel", "layer2": "gdn_layer_kernel"},
     "llama8b_t4096": {"layer": "gdn_scan_full_kernel", "linear": "gdn_scan_full_kernel",
                       "softmax": "swa_kernel"},
     "tiny_fp32": {"linear": "gdn_prep_kernel+linear_chunk_kernel", "softmax": "swa_kernel"},
@@ -138,6 +155,8 @@ CALL_KERNELS = {
 }
 CSRC = "swa_chunked_gated_amd/csrc/"
 KERNEL_SOURCES = {
+    "gdn_layer_kernel": ("gdn_layer.hip", "common.h"),
+    "gdn_prep_kernel": ("gdn_prep.h", "gdn_prep.hip", "common.h"),
     "gdn_prep_kernel+linear_chunk_kernel": ("gdn_prep.h", "gdn_prep.hip", "gdn_scan_full.hip",
                                             "linear_chunk.hip", "common.h"),
     "gla_prep_kernel+linear_chunk_kernel": ("gla_prep.hip", "linear_chunk.hip", "common.h"),
@@ -383,29 +402,44 @@ def bench_prefill(name, steps, warmup, parts=True):
     if w.shortconv:
         conv()
     q, k, v = qkv()
-    lin_flags = gl.BRANCH_LINEAR | st_flag
-    med, mean = time_call(lambda: gl.hybrid_prefill(q, k, v, inp["a"], inp["b"], w.n_sink, w.window,
-                                                    update=w.update, flags=lin_flags, o=o,
-                                                    state_out=st, workspace=ws), reps, 2)
-    calls["linear"] = {"kernel": names["linear"], "ms_median": med, "ms_mean": mean,
-                       "algorithmic_flops": f_lin}
-    med, mean = time_call(lambda: gl.hybrid_prefill(q, k, v, inp["a"], inp["b"], w.n_sink, w.window,
-                                                    update=w.update,
-                                                    flags=gl.BRANCH_SOFTMAX | gl.ACCUMULATE, o=o),
-                          reps, 2)
-    calls["softmax"] = {"kernel": names["softmax"], "ms_median": med, "ms_mean": mean,
-                        "algorithmic_flops": f_swa}
+
+    def call(flags):
+        return lambda: gl.hybrid_prefill(q, k, v, inp["a"], inp["b"], w.n_sink, w.window,
+                                         update=w.update, flags=flags, o=o, state_out=st,
+                                         workspace=ws)
+
+    if "layer2" in names:
+        # preparation alone, then the one-pass layer kernel alone (its
+        # workspace filled by the first)
+        med, mean = time_call(call(both | gl.PREPARE_ONLY), reps, 2)
+        f_prep = gdn_prep_flops(w)
+        calls["prepare"] = {"kernel": names["prepare"], "ms_median": med, "ms_mean": mean,
+                            "algorithmic_flops": f_prep}
+        med, mean = time_call(call(both | gl.PREPARED), reps, 2)
+        calls["layer"] = {"kernel": names["layer2"], "ms_median": med, "ms_mean": mean,
+                          "algorithmic_flops": f_lin + f_swa - f_prep}
+    else:
+        lin_flags = gl.BRANCH_LINEAR | st_flag
+        med, mean = time_call(call(lin_flags), reps, 2)
+        calls["linear"] = {"kernel": names["linear"], "ms_median": med, "ms_mean": mean,
+                           "algorithmic_flops": f_lin}
+        med, mean = time_call(call(gl.BRANCH_SOFTMAX | gl.ACCUMULATE), reps, 2)
+        calls["softmax"] = {"kernel": names["softmax"], "ms_median": med, "ms_mean": mean,
+                            "algorithmic_flops": f_swa}
     res["calls"] = calls
 
-    # dominant kernel launch: the whole layer when it is one launch, else the
-    # slowest of the split calls' MFMA-bound launches
-    if "layer" in names:
+    # dominant kernel launch: the one-pass layer kernel; the whole layer when
+    # it is one launch; else the slowest of the split calls' launches
+    byts = None
+    if "layer2" in names:
+        kern, ms, flops = names["layer2"], calls["layer"]["ms_median"], calls["layer"]["algorithmic_flops"]
+        byts = prefill_bytes(w) + tb_bytes(w)
+    elif "layer" in names:
         kern, ms, flops = names["layer"], res["event_ms_median"], f_lin + f_swa
         byts = prefill_bytes(w)
     else:
         key = max(("linear", "softmax"), key=lambda c: calls[c]["ms_median"])
         kern, ms, flops = calls[key]["kernel"], calls[key]["ms_median"], calls[key]["algorithmic_flops"]
-        byts = None
     achieved = flops / (ms * 1e-3)
     res["roofline"] = {
         "kernel": kern, "bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16 / 1e12,
@@ -416,6 +450,8 @@ def bench_prefill(name, steps, warmup, parts=True):
     }
     if byts is not None:
         res["roofline"]["algorithmic_bytes_per_launch"] = byts
+        res["roofline"]["hbm_view"] = {"achieved_GBps": byts / (ms * 1e-3) / 1e9,
+                                       "frac": byts / (ms * 1e-3) / PEAK_HBM}
     if w.shortconv:
         c = calls["shortconv"]
         gbs = c["algorithmic_bytes"] / (c["ms_median"] * 1e-3)

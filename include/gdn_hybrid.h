@@ -83,8 +83,19 @@ enum {
   GDN_BRANCH_LINEAR = 1,   /* add o_lin to o                                   */
   GDN_BRANCH_SOFTMAX = 2,  /* add o_swa to o                                   */
   GDN_WRITE_STATE = 4,     /* prefill only: write the final state to state_out */
-  GDN_ACCUMULATE = 8       /* prefill only: add the selected branches to the
+  GDN_ACCUMULATE = 8,      /* prefill only: add the selected branches to the
                               values o already holds instead of overwriting */
+  /* Two-phase prefill (gated delta rule or GLA, linear branch or state
+     selected, at least one stream chunk, and a launch plan with a separate
+     chunk-preparation launch: every plan except the bf16 one-launch path
+     for fewer chains than compute units, which returns GDN_EUNSUPPORTED
+     for either flag).  GDN_PREPARE_ONLY runs only the state-independent
+     chunk preparation into the workspace (o and state_out untouched);
+     GDN_PREPARED skips it, the workspace holding what a GDN_PREPARE_ONLY
+     call with the same arguments (other flags equal) wrote, with k, a and b
+     unchanged since.  Setting both is GDN_EINVAL. */
+  GDN_PREPARE_ONLY = 16,
+  GDN_PREPARED = 32
 };
 
 /* flags of shortconv_qkv */

@@ -19,6 +19,10 @@ BRANCH_LINEAR = 1
 BRANCH_SOFTMAX = 2
 WRITE_STATE = 4
 ACCUMULATE = 8
+# two-phase prefill: the state-independent chunk preparation alone, then the
+# rest from a workspace that holds it (same arguments, k, a, b unchanged)
+PREPARE_ONLY = 16
+PREPARED = 32
 ROPE = 1
 L2NORM = 2
 
@@ -29,7 +33,7 @@ __all__ = [
     "hybrid_prefill", "hybrid_decode", "cache_from_prefill", "shortconv_qkv",
     "prefill_workspace_bytes",
     "version", "GdnError", "BRANCH_LINEAR", "BRANCH_SOFTMAX", "WRITE_STATE", "ACCUMULATE",
-    "ROPE", "L2NORM",
+    "PREPARE_ONLY", "PREPARED", "ROPE", "L2NORM",
 ]
 
 
@@ -100,9 +104,13 @@ def hybrid_prefill(q, k, v, a, b, n_sink: int, window: int, update: str = "gdn",
     With ACCUMULATE in flags, ``o`` must be given and receives o += branches.
     ``workspace``: a uint8 device tensor of at least
     ``prefill_workspace_bytes(...)`` bytes; allocated here when omitted.
+    PREPARE_ONLY fills the workspace with the chunk preparation alone;
+    PREPARED (with that workspace) runs the rest of the same call.
     """
     if flags & ACCUMULATE and o is None:
         raise ValueError("ACCUMULATE needs an initialised output tensor o")
+    if flags & PREPARED and workspace is None:
+        raise ValueError("PREPARED needs the workspace a PREPARE_ONLY call filled")
     B, T, H, dk = q.shape
     Hkv, dv = k.shape[2], v.shape[3]
     dt = _io_dtype(q, k, v)

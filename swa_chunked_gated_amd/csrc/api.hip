@@ -121,6 +121,11 @@ const char* gdn_hybrid_strerror(int code) {
 int gdn_hybrid_last_hip_error(void) { return g_last_hip_error.load(); }
 
 namespace {
+bool prefill_flags_ok(int flags) {
+  if (flags < 1 || flags > 63 || (flags & 7) == 0) return false;
+  return (flags & (GDN_PREPARE_ONLY | GDN_PREPARED)) != (GDN_PREPARE_ONLY | GDN_PREPARED);
+}
+
 // Workspace the linear branch of this call needs (0 unless the gated delta
 // rule recurrence runs over at least one chunk).
 size_t prefill_workspace_bytes(int B, int T, int H, int dk, int n_sink, int window, int dtype,
@@ -139,7 +144,7 @@ int gdn_hybrid_prefill_workspace(int B, int T, int H, int Hkv, int dk, int dv, i
                                  int window, int dtype, int update, int flags, size_t* bytes) {
   if (!bytes) return GDN_EINVAL;
   if (!dims_ok(B, T, H, Hkv, dk, dv, n_sink, window, dtype, update)) return GDN_EINVAL;
-  if (flags < 1 || flags > 15 || (flags & 7) == 0) return GDN_EINVAL;
+  if (!prefill_flags_ok(flags)) return GDN_EINVAL;
   *bytes = prefill_workspace_bytes(B, T, H, dk, n_sink, window, dtype, update, flags);
   return GDN_OK;
 }
@@ -163,7 +168,10 @@ int prefill_impl(const void* q, const void* k, const void* v, const float* a, co
                  void* stream) {
   if (!dims_ok(B, T, H, Hkv, dk, dv, n_sink, window, dtype, update)) return GDN_EINVAL;
   if (!std::isfinite(w_lin) || !std::isfinite(w_swa)) return GDN_EINVAL;
-  if (flags < 1 || flags > 15 || (flags & 7) == 0) return GDN_EINVAL;
+  if (!prefill_flags_ok(flags)) return GDN_EINVAL;
+  const bool prep_only = flags & GDN_PREPARE_ONLY;
+  const bool prepared = flags & GDN_PREPARED;
+  flags &= 15;
   const bool lin = flags & GDN_BRANCH_LINEAR;
   const bool swa = flags & GDN_BRANCH_SOFTMAX;
   const bool wst = flags & GDN_WRITE_STATE;
@@ -194,6 +202,11 @@ int prefill_impl(const void* q, const void* k, const void* v, const float* a, co
   gdn::PrefillArgs p{q, k, v, a, b, o, state_out, B, T, H, Hkv, dk, n_sink, window,
                      dtype == GDN_BF16, update == GDN_GLA, flags, workspace, w_lin, w_swa};
   hipStream_t s = (hipStream_t)stream;
+  if (prep_only || prepared) {
+    if (!needs_rec || !gdn::separate_preparation(p)) return GDN_EUNSUPPORTED;
+    if (prep_only) return launched(gdn::launch_preparation(p, s));
+    p.prepared = true;
+  }
   const int N = n_sink + window;
   // The linear kernel writes (or adds) rows t >= N and, for a linear-only
   // overwrite, zeroes rows t < N itself; the softmax kernel then adds what o

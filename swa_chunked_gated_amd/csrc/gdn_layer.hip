@@ -860,7 +860,7 @@ bool gdn_layer_applies(const PrefillArgs& p) {
 
 hipError_t launch_gdn_layer(const PrefillArgs& p, hipStream_t s) {
   const int nch = gdn_stream_chunks(p.T, p.n_sink, p.window);
-  hipError_t e = launch_gdn_prep(p, nch, s);
+  hipError_t e = p.prepared ? hipSuccess : launch_gdn_prep(p, nch, s);
   if (e != hipSuccess) return e;
   e = hipFuncSetAttribute((const void*)gdn_layer_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
   if (e != hipSuccess) return e;

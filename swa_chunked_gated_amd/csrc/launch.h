@@ -24,6 +24,7 @@ struct PrefillArgs {
   void* workspace;   // chunk preparation results (gated delta rule), see GdnWorkspace
   float w_lin = 1.f;   // branch weights: o = w_lin o_lin + w_swa o_swa
   float w_swa = 1.f;
+  bool prepared = false;   // the workspace already holds the chunk preparation
 };
 
 // Workspace of the gated delta rule prefill, per (sequence, head, chunk), as
@@ -130,6 +131,11 @@ hipError_t launch_linear_prefill(const PrefillArgs& a, hipStream_t s, bool* swa_
 // kernel running the state scan and the softmax rows of each chunk): bf16
 // GDN at d = 128 with both branches and no accumulation, many chains,
 // window <= 128 and n_sink <= 16.
+// Whether the linear branch of p runs a separate chunk-preparation launch
+// (false when there is no stream chunk or the one-launch path applies), and
+// that launch alone.
+bool separate_preparation(const PrefillArgs& p);
+hipError_t launch_preparation(const PrefillArgs& p, hipStream_t s);
 bool gdn_layer_applies(const PrefillArgs& p);
 hipError_t launch_gdn_layer(const PrefillArgs& p, hipStream_t s);
 // Chunk preparation of the gated delta rule / of GLA into a.workspace (nch chunks).

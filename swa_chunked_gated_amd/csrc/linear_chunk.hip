@@ -622,6 +622,15 @@ hipError_t launch_linear_d(const PrefillArgs& p, hipStream_t s) {
 
 }  // namespace
 
+bool separate_preparation(const PrefillArgs& p) {
+  return gdn_stream_chunks(p.T, p.n_sink, p.window) > 0 && (p.gla || !gdn_full_prep(p.B, p.H, p.D, p.bf16));
+}
+
+hipError_t launch_preparation(const PrefillArgs& p, hipStream_t s) {
+  const int nch = gdn_stream_chunks(p.T, p.n_sink, p.window);
+  return p.gla ? launch_gla_prep(p, nch, s) : launch_gdn_prep(p, nch, s);
+}
+
 hipError_t launch_linear_prefill(const PrefillArgs& p, hipStream_t s, bool* swa_done) {
   if (swa_done) *swa_done = false;
   const int nch = gdn_stream_chunks(p.T, p.n_sink, p.window);
@@ -630,7 +639,7 @@ hipError_t launch_linear_prefill(const PrefillArgs& p, hipStream_t s, bool* swa_
     if (swa_done) *swa_done = true;
     return launch_gdn_layer(p, s);
   }
-  if (nch > 0) {
+  if (nch > 0 && !p.prepared) {
     const hipError_t e = p.gla ? launch_gla_prep(p, nch, s) : launch_gdn_prep(p, nch, s);
     if (e != hipSuccess) return e;
   }

@@ -130,6 +130,26 @@ def test_prefill_validation(lib):
     assert prefill(lib, B=1 << 16, T=1 << 16) == EINVAL          # B*T overflows int
 
 
+def test_two_phase_flags(lib):
+    # both phases at once, unknown bits, or no branch: invalid
+    assert prefill(lib, flags=3 | 16 | 32) == EINVAL
+    assert prefill(lib, flags=3 | 64) == EINVAL
+    assert prefill(lib, flags=16) == EINVAL
+    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 3 | 16 | 32)[0] == EINVAL
+    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 3 | 16)[0] == OK
+    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 3 | 32)[0] == OK
+    # no stream chunk (T = n_sink + window): nothing to prepare
+    assert prefill(lib, flags=3 | 16) == EUNSUP
+    assert prefill(lib, flags=3 | 32) == EUNSUP
+    # softmax only: no recurrence to prepare
+    assert prefill(lib, T=200, flags=2 | 16) == EUNSUP
+    # bf16, 2 chains: the one-launch path, whose preparation runs inside it
+    big = ctypes.c_void_p(0x100000)
+    for f in (3 | 16, 3 | 32):
+        assert lib.gdn_hybrid_prefill(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 200, 2, 2, 64, 64,
+                                      8, 56, BF16, DELTA, f, big, 1 << 30, None) == EUNSUP
+
+
 def test_prefill_workspace_checks(lib):
     # T = 200 > budget: the gated delta rule needs its chunk workspace
     assert prefill(lib, T=200) == EWS
