@@ -35,7 +35,9 @@ the design notes of the repository):
 
 * Column vectors; S is d_k x d_v; the linear output is S^T q.
 * GDN gate is one scalar a_t per (token, query head); a_t (I - b k k^T) S is
-  the same as (I - b k k^T) a_t S for a scalar gate.
+  the same as (I - b k k^T) a_t S for a scalar gate.  The diagonal-gate
+  variant ("dgd") keeps the page's order for a per-channel gate: the gate
+  first, then the delta projection, (I - b k k^T) Diag(alpha) S.
 * Softmax set of query t:  A(t) = { i <= t : i < n_sink or i > t - window }
   (window includes the current token; sinks are absolute positions 0..n_sink-1;
   the union counts each key once).
@@ -55,7 +57,10 @@ Pins (in ``tests/test_oracle_pins.py``): brute-force partition of the index
 sets; the materialised effective-attention product form on tiny inputs;
 exact retrieval with orthonormal keys; equality with full causal softmax
 (torch SDPA, fp64) when T <= budget; an fp64 chunked (WY/UT) form for several
-chunk sizes; the GLA diagonal-product form; prefill + decode == longer
+chunk sizes; the GLA diagonal-product form; for the diagonal-gate delta
+rule: a channel-uniform gate == the scalar-gate rule, the per-channel
+closed form with one-hot keys, and an fp64 chunked form with per-channel
+decays; prefill + decode == longer
 prefill; GQA == explicitly repeated K/V; torch conv1d for the short conv;
 RoPE closed forms and invariants; short-conv decode steps from a prefill's
 history == the longer prefill's rows.  No function here is "parity unpinned"
@@ -74,6 +79,7 @@ __all__ = [
     "linear_index_set",
     "gdn_linear_branch",
     "gla_linear_branch",
+    "dgd_linear_branch",
     "swa_branch",
     "hybrid_prefill",
     "cache_from_prefill",
@@ -184,6 +190,37 @@ def gla_linear_branch(q, k, v, alpha, n_sink: int, window: int):
     return o, S
 
 
+def dgd_linear_branch(q, k, v, alpha, b, n_sink: int, window: int):
+    """Lagged delta rule with a diagonal gate (P1, 线性注意力替换机制: the GDN
+    update with G_t = Diag(alpha_t), one forget value per d_k channel).
+
+    For i = n_sink .. T-1-window:
+        S <- (I - b_i k_i k_i^T) Diag(alpha_i) S + b_i k_i v_i^T
+        o_lin[i + window] = S^T q[i + window]
+    ``alpha`` is [B,T,H,dk], ``b`` [B,T,H].  Returns (o_lin, S_final).
+    """
+    q = np.asarray(q, np.float64)
+    B, T, H, dk = q.shape
+    kh = _expand_kv(np.asarray(k, np.float64), H)
+    vh = _expand_kv(np.asarray(v, np.float64), H)
+    alpha = np.asarray(alpha, np.float64)
+    b = np.asarray(b, np.float64)
+    dv = vh.shape[-1]
+    S = np.zeros((B, H, dk, dv))
+    o = np.zeros((B, T, H, dv))
+    for i in range(n_sink, T - window):
+        ki = kh[:, i]                                   # [B,H,dk]
+        vi = vh[:, i]
+        bi = b[:, i][:, :, None, None]
+        GS = alpha[:, i][:, :, :, None] * S             # Diag(alpha_i) S
+        kGS = np.einsum("bhk,bhkv->bhv", ki, GS)        # k^T Diag(alpha) S
+        S = GS - bi * (ki[:, :, :, None] * kGS[:, :, None, :]) \
+            + bi * (ki[:, :, :, None] * vi[:, :, None, :])
+        t = i + window
+        o[:, t] = np.einsum("bhkv,bhk->bhv", S, q[:, t])
+    return o, S
+
+
 # --------------------------------------------------------------------------
 # Softmax branch over sinks + sliding window (P1, 填补近似缺口的实用设计;
 # scale 1/sqrt(d_k) from the first-order-approximation section)
@@ -222,7 +259,8 @@ def hybrid_prefill(q, k, v, a, b, n_sink: int, window: int, update: str = "gdn",
     position 0; the weights (P3, 关键设计 (1): inference-time hybridisation
     sets the branches' contributions by weights) default to the plain sum.
 
-    ``update`` is "gdn" (a, b: [B,T,H]) or "gla" (a: [B,T,H,dk], b unused).
+    ``update`` is "gdn" (a, b: [B,T,H]), "gla" (a: [B,T,H,dk], b unused) or
+    "dgd" (the delta rule with a diagonal gate: a [B,T,H,dk], b [B,T,H]).
     Returns (o [B,T,H,dv], final state [B,H,dk,dv] or None).
     """
     q = np.asarray(q, np.float64)
@@ -235,6 +273,8 @@ def hybrid_prefill(q, k, v, a, b, n_sink: int, window: int, update: str = "gdn",
             o_lin, S = gdn_linear_branch(q, k, v, a, b, n_sink, window)
         elif update == "gla":
             o_lin, S = gla_linear_branch(q, k, v, a, n_sink, window)
+        elif update == "dgd":
+            o_lin, S = dgd_linear_branch(q, k, v, a, b, n_sink, window)
         else:
             raise ValueError(update)
         if flags & BRANCH_LINEAR:
@@ -271,7 +311,7 @@ def cache_from_prefill(k, v, a, b, n_sink: int, window: int, update: str = "gdn"
     N = n_sink + window
     kc = np.zeros((B, Hkv, N, dk))
     vc = np.zeros((B, Hkv, N, dv))
-    ac = np.zeros((B, window, H) + ((dk,) if update == "gla" else ()))
+    ac = np.zeros((B, window, H) + ((dk,) if update in ("gla", "dgd") else ()))
     bc = np.zeros((B, window, H))
     toks = list(range(min(n_sink, T))) + list(range(max(n_sink, T - window), T))
     for i in toks:
@@ -293,7 +333,7 @@ def decode_step(q, k, v, a, b, state, k_cache, v_cache, a_cache, b_cache, pos,
     """One decode step for every sequence; returns new copies of everything.
     The output is w_lin o_lin + w_swa o_swa (weights as in hybrid_prefill).
 
-    q [B,H,dk]; k [B,Hkv,dk]; v [B,Hkv,dv]; a [B,H] (GLA: [B,H,dk]); b [B,H];
+    q [B,H,dk]; k [B,Hkv,dk]; v [B,Hkv,dv]; a [B,H] (GLA, DGD: [B,H,dk]); b [B,H];
     state [B,H,dk,dv]; caches as in ``cache_from_prefill``; pos [B] = index t
     of the new token.  Per sequence:
       1. e = t - window; if e >= n_sink, fold token e (read from its slot,
@@ -339,6 +379,12 @@ def decode_step(q, k, v, a, b, state, k_cache, v_cache, a_cache, b_cache, pos,
                 kS = np.einsum("hk,hkv->hv", ke, S[bi])  # k_e^T S
                 proj_S = S[bi] - be * (ke[:, :, None] * kS[:, None, :])
                 S[bi] = ae * proj_S + be * (ke[:, :, None] * ve[:, None, :])
+            elif update == "dgd":
+                be = bc[bi, r_e][:, None, None]
+                GS = ac[bi, r_e][:, :, None] * S[bi]    # Diag(alpha_e) S
+                kGS = np.einsum("hk,hkv->hv", ke, GS)
+                S[bi] = GS - be * (ke[:, :, None] * kGS[:, None, :]) \
+                    + be * (ke[:, :, None] * ve[:, None, :])
             else:
                 S[bi] = ac[bi, r_e][:, :, None] * S[bi] \
                     + ke[:, :, None] * ve[:, None, :]

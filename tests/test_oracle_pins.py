@@ -286,6 +286,90 @@ def test_chunked_form_matches_stepwise(C):
     np.testing.assert_allclose(Sc, S, atol=1e-12, rtol=0)
 
 
+# ------------------------- delta rule with a diagonal (per-channel) gate
+
+def test_dgd_channel_uniform_gate_equals_scalar_gate_gdn():
+    """alpha_i = a_i in every channel: Diag(alpha_i) = a_i I, so the
+    diagonal-gate delta rule is the scalar-gate one."""
+    n_sink, window, T, B, H, Hkv, d = 3, 4, 41, 2, 4, 2, 8
+    q, k, v, a, b = rand_layer(B, T, H, Hkv, d)
+    alpha = np.repeat(a[..., None], d, axis=-1)
+    o1, S1 = O.dgd_linear_branch(q, k, v, alpha, b, n_sink, window)
+    o2, S2 = O.gdn_linear_branch(q, k, v, a, b, n_sink, window)
+    np.testing.assert_allclose(o1, o2, atol=1e-13, rtol=0)
+    np.testing.assert_allclose(S1, S2, atol=1e-13, rtol=0)
+
+
+def test_dgd_one_hot_keys_closed_form():
+    """k_i = e_{c_i} (channels may repeat): the projection touches row c_i
+    only, so each row of S follows its own scalar recursion:
+    every row decays by its channel's gate, then row c_i <- (1 - b_i) row +
+    b_i v_i.  The readout is S^T q at lag ``window``."""
+    n_sink, window, T, d, dv = 2, 3, 30, 6, 5
+    rng = np.random.default_rng(11)
+    ch = rng.integers(0, d, T)
+    k = np.eye(d)[ch][None, :, None, :]
+    v = rng.standard_normal((1, T, 1, dv))
+    q = rng.standard_normal((1, T, 1, d))
+    alpha = rng.uniform(0.3, 1.0, (1, T, 1, d))
+    b = rng.uniform(0.0, 1.0, (1, T, 1))
+    o, S = O.dgd_linear_branch(q, k, v, alpha, b, n_sink, window)
+    R = np.zeros((d, dv))
+    o_ref = np.zeros((T, dv))
+    for i in range(n_sink, T - window):
+        R = alpha[0, i, 0][:, None] * R
+        c = ch[i]
+        R[c] = (1 - b[0, i, 0]) * R[c] + b[0, i, 0] * v[0, i, 0]
+        o_ref[i + window] = R.T @ q[0, i + window, 0]
+    np.testing.assert_allclose(S[0, 0], R, atol=1e-14, rtol=0)
+    np.testing.assert_allclose(o[0, :, 0], o_ref, atol=1e-14, rtol=0)
+
+
+def chunked_dgd(q, k, v, alpha, b, n_sink, window, C):
+    """fp64 chunked form with per-channel decays: in a chunk with incoming
+    state S0 and Gam_r = prod_{s <= r} alpha_s (per channel),
+    (I + L) U = diag(b) (V - (K o Gam) S0), L_rs = b_r (k_r o Gam_r).(k_s / Gam_s) (s < r),
+    O = (Q o Gam) S0 + ([s <= r] (Q o Gam)(K / Gam)^T) U,
+    S_C = Diag(Gam_C) S0 + (K o Gam_C / Gam)^T U."""
+    B, T, H, dk = q.shape
+    G = H // k.shape[2]
+    dv = v.shape[-1]
+    o = np.zeros((B, T, H, dv))
+    Sf = np.zeros((B, H, dk, dv))
+    for bi in range(B):
+        for h in range(H):
+            g = h // G
+            S = np.zeros((dk, dv))
+            for c0 in range(n_sink, T - window, C):
+                c1 = min(c0 + C, T - window)
+                K = k[bi, c0:c1, g]
+                V = v[bi, c0:c1, g]
+                Q = q[bi, c0 + window:c1 + window, h]
+                bb = b[bi, c0:c1, h]
+                Gam = np.cumprod(alpha[bi, c0:c1, h], axis=0)       # [C, dk]
+                Kg, Kd = K * Gam, K / Gam
+                L = np.tril(bb[:, None] * (Kg @ Kd.T), -1)
+                Tm = np.linalg.inv(np.eye(len(bb)) + L)
+                Wm = Tm @ (bb[:, None] * Kg)
+                Ut = Tm @ (bb[:, None] * V)
+                U = Ut - Wm @ S
+                Qg = Q * Gam
+                o[bi, c0 + window:c1 + window, h] = Qg @ S + np.tril(Qg @ Kd.T) @ U
+                S = Gam[-1][:, None] * S + (K * (Gam[-1] / Gam)).T @ U
+            Sf[bi, h] = S
+    return o, Sf
+
+
+@pytest.mark.parametrize("C", [64, 16, 7])
+def test_dgd_chunked_form_matches_stepwise(C):
+    n_sink, window, T, B, H, Hkv, d = 4, 12, 173, 1, 4, 2, 8
+    q, k, v, a, b = rand_layer(B, T, H, Hkv, d, gla=True)
+    o, S = O.dgd_linear_branch(q, k, v, a, b, n_sink, window)
+    oc, Sc = chunked_dgd(q, k, v, a, b, n_sink, window, C)
+    np.testing.assert_allclose(oc, o, atol=1e-11, rtol=0)
+    np.testing.assert_allclose(Sc, S, atol=1e-11, rtol=0)
+
+
 def test_gla_alpha1_equals_gdn_a1_b1_on_fresh_orthonormal_keys():
     """With orthonormal keys that never repeat, the delta projection removes
     nothing, so GLA (alpha = 1) and GDN (a = b = 1) coincide."""
@@ -326,14 +410,14 @@ def test_linear_in_v():
 
 # ------------------------------------------- decode: lag and ring cache
 
-@pytest.mark.parametrize("update", ["gdn", "gla"])
+@pytest.mark.parametrize("update", ["gdn", "gla", "dgd"])
 @pytest.mark.parametrize("T0", [1, 3, 7, 8, 9, 10, 29])
 def test_prefill_then_decode_equals_longer_prefill(update, T0):
     """prefill(T0) + n decode steps reproduces prefill(T0 + n): outputs, final
     state and cache contents (budget 8 = 3 sinks + 5 window)."""
     n_sink, window, n, B, H, Hkv, d = 3, 5, 14, 2, 4, 2, 6
     T = T0 + n
-    q, k, v, a, b = rand_layer(B, T, H, Hkv, d, gla=(update == "gla"))
+    q, k, v, a, b = rand_layer(B, T, H, Hkv, d, gla=(update != "gdn"))
     o_full, S_full = O.hybrid_prefill(q, k, v, a, b, n_sink, window, update=update)
     _, S = O.hybrid_prefill(q[:, :T0], k[:, :T0], v[:, :T0], a[:, :T0], b[:, :T0],
                             n_sink, window, update=update)
@@ -462,7 +546,7 @@ def test_shortconv_history_holds_rotated_inputs_at_ring_slots():
         np.testing.assert_array_equal(hv[0, i % (ks - 1)], x[0, i].reshape(-1))
 
 
-@pytest.mark.parametrize("update", ["gdn", "gla"])
+@pytest.mark.parametrize("update", ["gdn", "gla", "dgd"])
 def test_branch_weights_reduce_to_single_branch_flags(update):
     # Weights (1, 0) and (0, 1) give the single-branch outputs (the softmax
     # branch is pinned to SDPA, the linear branch to closed forms); general
@@ -471,7 +555,7 @@ def test_branch_weights_reduce_to_single_branch_flags(update):
     q = unit(RNG.standard_normal((B, T, H, d)))
     k = unit(RNG.standard_normal((B, T, Hkv, d)))
     v = RNG.standard_normal((B, T, Hkv, d))
-    a = RNG.uniform(0.8, 1.0, (B, T, H, d) if update == "gla" else (B, T, H))
+    a = RNG.uniform(0.8, 1.0, (B, T, H, d) if update != "gdn" else (B, T, H))
     b = RNG.uniform(0.0, 1.0, (B, T, H))
     lin, _ = O.hybrid_prefill(q, k, v, a, b, ns, win, update, flags=O.BRANCH_LINEAR)
     sm, _ = O.hybrid_prefill(q, k, v, a, b, ns, win, update, flags=O.BRANCH_SOFTMAX)
