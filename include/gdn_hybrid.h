@@ -76,7 +76,13 @@ extern "C" {
 #endif
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
-typedef enum { GDN_DELTA = 0, GDN_GLA = 1 } gdn_update;
+/* recurrence of the linear branch (page "The Key to Going Linear", section
+   线性注意力替换机制): GDN_DELTA the gated delta rule with one scalar gate
+   a_t per token and head; GDN_GLA the diagonal-gate linear update; and
+   GDN_DELTA_DIAG the delta rule with the diagonal gate,
+   S_t = (I - b_t k_t k_t^T) Diag(alpha_t) S_{t-1} + b_t k_t v_t^T, whose
+   gates are per channel (a [.., dk], as GLA) and b per token and head */
+typedef enum { GDN_DELTA = 0, GDN_GLA = 1, GDN_DELTA_DIAG = 2 } gdn_update;
 
 /* flags of gdn_hybrid_prefill / gdn_hybrid_decode */
 enum {
@@ -153,7 +159,10 @@ int gdn_hybrid_set_test_faults(int faults, int wait_us);
  *   GDN_DELTA otherwise: B * H * nch * (2 * 64 * 64 * elt + 128 * 4) bytes
  *     (the inverse scaled by b and by b * gamma, the gate prefix sums);
  *   GDN_GLA: B * H * nch * ((2 * 64 * dk + 64 * 64) * elt + dk * 4) bytes
- *     (gate-scaled Q and K^T, the intra-chunk scores, the chunk decay).
+ *     (gate-scaled Q and K^T, the intra-chunk scores, the chunk decay);
+ *   GDN_DELTA_DIAG: B * H * nch * ((3 * 64 * dk + 2 * 64 * 64) * elt +
+ *     dk * 4) bytes (as GDN_GLA, plus the inverse scaled by b and its
+ *     product with the gate-scaled K).
  * Errors: GDN_EINVAL if bytes is NULL or the shape arguments are invalid.
  */
 int gdn_hybrid_prefill_workspace(int B, int T, int H, int Hkv, int dk, int dv,
@@ -167,8 +176,9 @@ int gdn_hybrid_prefill_workspace(int B, int T, int H, int Hkv, int dk, int dv,
  *   q          [B, T, H, dk]    dtype
  *   k          [B, T, Hkv, dk]  dtype
  *   v          [B, T, Hkv, dv]  dtype
- *   a          GDN: [B, T, H] fp32 (scalar gate); GLA: [B, T, H, dk] fp32
- *   b          GDN: [B, T, H] fp32; GLA: ignored (may be NULL)
+ *   a          GDN: [B, T, H] fp32 (scalar gate); GLA, GDN_DELTA_DIAG:
+ *              [B, T, H, dk] fp32 (one gate per channel)
+ *   b          GDN, GDN_DELTA_DIAG: [B, T, H] fp32; GLA: ignored (may be NULL)
  *   o          [B, T, H, dv]    dtype, written (every row) unless flags has
  *              neither branch bit (then it may be NULL)
  *   state_out  [B, H, dk, dv] fp32: S after token T-1-window (zero if none),
@@ -188,10 +198,10 @@ int gdn_hybrid_prefill_workspace(int B, int T, int H, int Hkv, int dk, int dv,
  * Supported: d in {64, 128} for bf16; the linear branch (or the state) in
  * fp32 only at d = 64 (GDN_EUNSUPPORTED otherwise).
  * Preconditions (not checked): gates a in (0, 1], b in [0, 1].  GDN gates
- * may decay at any rate.  GLA operands are formed relative to a reference
- * token every 16 tokens, so results are exact (to rounding) while the
- * product of any 8 consecutive gates of one channel stays above e^-80
- * (a mean gate above about 5e-5).
+ * may decay at any rate.  GLA and GDN_DELTA_DIAG operands are formed
+ * relative to a reference token every 16 tokens, so results are exact (to
+ * rounding) while the product of any 8 consecutive gates of one channel
+ * stays above e^-80 (a mean gate above about 5e-5).
  */
 int gdn_hybrid_prefill(const void* q, const void* k, const void* v,
                        const float* a, const float* b,
@@ -212,14 +222,16 @@ int gdn_hybrid_prefill(const void* q, const void* k, const void* v,
  *
  *   q          [B, H, dk]        dtype
  *   k, v       [B, Hkv, dk|dv]   dtype    (the new token)
- *   a          GDN [B, H] fp32; GLA [B, H, dk] fp32
- *   b          GDN [B, H] fp32; GLA: ignored (may be NULL)
+ *   a          GDN [B, H] fp32; GLA, GDN_DELTA_DIAG [B, H, dk] fp32
+ *   b          GDN, GDN_DELTA_DIAG [B, H] fp32; GLA: ignored (may be NULL)
  *   state      [B, H, dk, dv] fp32, in/out
  *   k_cache, v_cache [B, Hkv, n_sink + window, d] dtype, in/out.  Token i
  *              lives in slot i if i < n_sink, else in slot
  *              n_sink + (i - n_sink) mod window.
- *   a_cache    GDN [B, window, H] fp32; GLA [B, window, H, dk] fp32, in/out
- *   b_cache    GDN [B, window, H] fp32 (GLA: ignored, may be NULL), in/out.
+ *   a_cache    GDN [B, window, H] fp32; GLA, GDN_DELTA_DIAG [B, window, H, dk]
+ *              fp32, in/out
+ *   b_cache    GDN, GDN_DELTA_DIAG [B, window, H] fp32 (GLA: ignored, may be
+ *              NULL), in/out.
  *              Gates of token i >= n_sink live at ring index
  *              (i - n_sink) mod window.
  *   pos        [B] int32, in/out: position of the new token; incremented.

@@ -27,7 +27,8 @@ ROPE = 1
 L2NORM = 2
 
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
-_UPDATES = {"gdn": 0, "gla": 1}
+# "dgd": the delta rule with a diagonal (per-channel) gate
+_UPDATES = {"gdn": 0, "gla": 1, "dgd": 2}
 
 __all__ = [
     "hybrid_prefill", "hybrid_decode", "cache_from_prefill", "shortconv_qkv",
@@ -223,7 +224,7 @@ def cache_from_prefill(k, v, a, b, H: int, n_sink: int, window: int, update: str
     dev = k.device
     kc = torch.empty(B, Hkv, N, dk, dtype=k.dtype, device=dev)
     vc = torch.empty(B, Hkv, N, dv, dtype=k.dtype, device=dev)
-    ac = torch.empty((B, window, H, dk) if update == "gla" else (B, window, H),
+    ac = torch.empty((B, window, H, dk) if update in ("gla", "dgd") else (B, window, H),
                      dtype=torch.float32, device=dev)
     bc = torch.empty(B, window, H, dtype=torch.float32, device=dev)
     lib = _lib.load()

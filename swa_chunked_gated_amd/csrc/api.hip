@@ -31,7 +31,7 @@ bool dims_ok(int B, int T, int H, int Hkv, int dk, int dv, int n_sink, int windo
   if (dk != dv || (dk != 64 && dk != 128)) return false;
   if (n_sink < 0 || window < 1) return false;
   if (dtype != GDN_F32 && dtype != GDN_BF16) return false;
-  if (update != GDN_DELTA && update != GDN_GLA) return false;
+  if (update != GDN_DELTA && update != GDN_GLA && update != GDN_DELTA_DIAG) return false;
   // index arithmetic: (b*T + t) fits int, element counts fit 2^40
   if ((int64_t)B * T >= (int64_t)1 << 31) return false;
   if ((int64_t)B * T * H * dk >= (int64_t)1 << 40) return false;
@@ -135,7 +135,8 @@ size_t prefill_workspace_bytes(int B, int T, int H, int dk, int n_sink, int wind
   const int nch = gdn::gdn_stream_chunks(T, n_sink, window);
   if (nch == 0) return 0;
   const size_t elt = dtype == GDN_BF16 ? 2 : 4;
-  if (update == GDN_GLA) return gdn::gla_workspace_layout(nullptr, B, H, nch, dk, elt).bytes;
+  if (update != GDN_DELTA)
+    return gdn::gla_workspace_layout(nullptr, B, H, nch, dk, elt, update == GDN_DELTA_DIAG).bytes;
   return gdn::gdn_workspace_layout(nullptr, B, H, nch, dk, elt, gdn::gdn_full_prep(B, H, dk, elt == 2)).bytes;
 }
 }  // namespace
@@ -180,7 +181,7 @@ int prefill_impl(const void* q, const void* k, const void* v, const float* a, co
   if (!q || !k || !v) return GDN_EINVAL;
   if ((lin || swa) && !o) return GDN_EINVAL;
   if (needs_rec && !a) return GDN_EINVAL;
-  if (needs_rec && update == GDN_DELTA && !b) return GDN_EINVAL;
+  if (needs_rec && update != GDN_GLA && !b) return GDN_EINVAL;
   if (wst && !state_out) return GDN_EINVAL;
   if (!aligned16({q, k, v, a, b, o, state_out})) return GDN_EINVAL;
   if (needs_rec && dtype == GDN_F32 && dk != 64) return GDN_EUNSUPPORTED;
@@ -200,7 +201,8 @@ int prefill_impl(const void* q, const void* k, const void* v, const float* a, co
   if (T == 0 && !wst) return GDN_OK;
 
   gdn::PrefillArgs p{q, k, v, a, b, o, state_out, B, T, H, Hkv, dk, n_sink, window,
-                     dtype == GDN_BF16, update == GDN_GLA, flags, workspace, w_lin, w_swa};
+                     dtype == GDN_BF16, update != GDN_DELTA, flags, workspace, w_lin, w_swa};
+  p.dgd = update == GDN_DELTA_DIAG;
   hipStream_t s = (hipStream_t)stream;
   if (prep_only || prepared) {
     if (!needs_rec || !gdn::separate_preparation(p)) return GDN_EUNSUPPORTED;
@@ -264,16 +266,17 @@ int gdn_hybrid_decode_weighted(const void* q, const void* k, const void* v, cons
   if (flags < 1 || flags > 3) return GDN_EINVAL;
   if (!q || !k || !v || !a || !state || !k_cache || !v_cache || !a_cache || !pos || !o)
     return GDN_EINVAL;
-  if (update == GDN_DELTA && (!b || !b_cache)) return GDN_EINVAL;
+  if (update != GDN_GLA && (!b || !b_cache)) return GDN_EINVAL;
   if (!aligned16({q, k, v, a, b, state, k_cache, v_cache, a_cache, b_cache, pos, o})) return GDN_EINVAL;
   const int G = H / Hkv;
   if (G > 16) return GDN_EUNSUPPORTED;
   if ((int64_t)G * (n_sink + window) > 12288) return GDN_EUNSUPPORTED;
-  if (gdn::decode_lds_bytes(G, n_sink + window, dk, update == GDN_GLA, dtype == GDN_BF16 ? 2 : 4) > 160 * 1024)
+  if (gdn::decode_lds_bytes(G, n_sink + window, dk, update != GDN_DELTA, dtype == GDN_BF16 ? 2 : 4) > 160 * 1024)
     return GDN_EUNSUPPORTED;
   gdn::DecodeArgs p{q, k, v, a, b, state, k_cache, v_cache, a_cache, b_cache, pos, o,
-                    B, H, Hkv, dk, n_sink, window, dtype == GDN_BF16, update == GDN_GLA, flags,
+                    B, H, Hkv, dk, n_sink, window, dtype == GDN_BF16, update != GDN_DELTA, flags,
                     w_lin, w_swa};
+  p.dgd = update == GDN_DELTA_DIAG;
   return launched(gdn::launch_decode(p, (hipStream_t)stream));
 }
 
@@ -283,12 +286,13 @@ int gdn_hybrid_cache_from_prefill(const void* k, const void* v, const float* a, 
                                   int window, int dtype, int update, void* stream) {
   if (!dims_ok(B, T, H, Hkv, dk, dv, n_sink, window, dtype, update)) return GDN_EINVAL;
   if (!k_cache || !v_cache || !a_cache) return GDN_EINVAL;
-  if (update == GDN_DELTA && !b_cache) return GDN_EINVAL;
+  if (update != GDN_GLA && !b_cache) return GDN_EINVAL;
   if (T > 0 && (!k || !v || !a)) return GDN_EINVAL;
-  if (T > 0 && update == GDN_DELTA && !b) return GDN_EINVAL;
+  if (T > 0 && update != GDN_GLA && !b) return GDN_EINVAL;
   if (!aligned16({k, v, a, b, k_cache, v_cache, a_cache, b_cache})) return GDN_EINVAL;
   gdn::CacheArgs p{k, v, a, b, k_cache, v_cache, a_cache, b_cache, B, T, H, Hkv, dk,
-                   n_sink, window, dtype == GDN_BF16, update == GDN_GLA};
+                   n_sink, window, dtype == GDN_BF16, update != GDN_DELTA};
+  p.dgd = update == GDN_DELTA_DIAG;
   return launched(gdn::launch_cache_from_prefill(p, (hipStream_t)stream));
 }
 

@@ -20,6 +20,10 @@
 //   c1 = S^T k_e, c2 = S^T q, u = b (v_e - a c1)
 //   S' = a S + k_e u^T,  o_lin = S'^T q = a c2 + u (k_e . q)
 // GLA: S' = Diag(alpha) S + k_e v_e^T, o_lin = S^T (alpha * q) + v_e (k_e . q).
+// Delta rule with the diagonal gate (mode 2): c1 = S^T (alpha * k_e),
+// c2 = S^T (alpha * q), u = b (v_e - c1), S' = Diag(alpha) S + k_e u^T,
+// o_lin = c2 + u (k_e . q).
+// MODE: 0 the gated delta rule, 1 GLA, 2 the delta rule with the diagonal gate.
 
 #include "common.h"
 #include "launch.h"
@@ -95,7 +99,7 @@ __device__ __forceinline__ f32x4 raw4_f32(const f32x4& x) { return x; }
 // the rows staged per pass (MR * 128 bytes of each of K and V per head
 // dimension): 1 for budgets that fit one pass, 4 for long budgets, whose
 // serial passes (one staging round trip each) would otherwise dominate.
-template <class T, bool GLA, int D, int MR>
+template <class T, int MODE, int D, int MR>
 __device__ __forceinline__ void decode_step_body(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ a, const float* __restrict__ b, float* __restrict__ state,
@@ -105,6 +109,8 @@ __device__ __forceinline__ void decode_step_body(
   using M = StepMap<T, D, MR>;
   typedef typename Vec16<T>::type V16;
   typedef typename Raw4<T>::type R4;
+  constexpr bool GLA = MODE != 0;    // per-channel gate a_e
+  constexpr bool DGD = MODE == 2;
   constexpr int VLOAD = 3 * M::UPR + (GLA ? D / 4 : 0);   // 16-byte units of the per-step vectors
   constexpr int VUNITS = (VLOAD + 63) / 64 * 64;
   static_assert(VUNITS <= 64 * M::NWV, "one load per wave");
@@ -177,8 +183,9 @@ __device__ __forceinline__ void decode_step_body(
     else src = ac + gb * D + (P - 3 * M::UPR) * 4;   // GLA gates, fp32
     dma16(src, vecs + wv * 64 * 16);
   }
-  if (!GLA && wv == M::NWV - 1) {
-    const float* src = lane == 1 ? bc + gb : ac + gb;
+  if ((!GLA || DGD) && wv == M::NWV - 1) {
+    // gates[0] = a_e (scalar gate), gates[1] = b_e
+    const float* src = (lane == 1 || DGD) ? bc + gb : ac + gb;
     __builtin_amdgcn_global_load_lds((gbl_void_ptr)(void*)src, (lds_void_ptr)(void*)gates, 4, 0, 0);
   }
   asm volatile("" ::: "memory");
@@ -273,7 +280,7 @@ __device__ __forceinline__ void decode_step_body(
     const int row = rg + M::RG * r;
     float qr = to_f32(qv[row]);
     if (GLA && evict) qr *= aev[row];
-    const float kr2 = evict ? to_f32(kev[row]) : 0.f;
+    const float kr2 = evict ? to_f32(kev[row]) * (DGD ? aev[row] : 1.f) : 0.f;
 #pragma unroll
     for (int xx = 0; xx < 4; ++xx) {
       p1[xx] += s[r][xx] * kr2;
@@ -313,7 +320,23 @@ __device__ __forceinline__ void decode_step_body(
   const f32x4 c2 = *reinterpret_cast<const f32x4*>(&fin[cg * 12 + 4]);
   if (evict) {
     const float kqh = misc[1];
-    if (GLA) {
+    if constexpr (DGD) {
+      const float bt = gates[1];
+      float u[4];
+#pragma unroll
+      for (int xx = 0; xx < 4; ++xx) {
+        u[xx] = bt * (to_f32(vev[4 * cg + xx]) - c1[xx]);
+        olin[xx] = c2[xx] + u[xx] * kqh;
+      }
+#pragma unroll
+      for (int r = 0; r < M::R; ++r) {
+        const int row = rg + M::RG * r;
+        const float al = aev[row];
+        const float kr2 = to_f32(kev[row]);
+#pragma unroll
+        for (int xx = 0; xx < 4; ++xx) s[r][xx] = al * s[r][xx] + kr2 * u[xx];
+      }
+    } else if (GLA) {
 #pragma unroll
       for (int xx = 0; xx < 4; ++xx) olin[xx] = c2[xx] + to_f32(vev[4 * cg + xx]) * kqh;
 #pragma unroll
@@ -368,17 +391,17 @@ __device__ __forceinline__ void decode_step_body(
 
 // One staged pass (48 KB of LDS): three workgroups per CU, so at most 80
 // VGPRs.
-template <class T, bool GLA, int D>
+template <class T, int MODE, int D>
 __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(6, 8))) void decode_step_kernel(
     GDN_DECODE_STEP_PARAMS) {
-  decode_step_body<T, GLA, D, 1>(GDN_DECODE_STEP_ARGS);
+  decode_step_body<T, MODE, D, 1>(GDN_DECODE_STEP_ARGS);
 }
 
 // Long budgets: four times the rows per pass (145 KB of LDS, one workgroup
 // per CU).
-template <class T, bool GLA, int D>
+template <class T, int MODE, int D>
 __global__ __launch_bounds__(kStepThreads) void decode_step_wide_kernel(GDN_DECODE_STEP_PARAMS) {
-  decode_step_body<T, GLA, D, 4>(GDN_DECODE_STEP_ARGS);
+  decode_step_body<T, MODE, D, 4>(GDN_DECODE_STEP_ARGS);
 }
 
 #undef GDN_DECODE_STEP_PARAMS
@@ -387,7 +410,7 @@ __global__ __launch_bounds__(kStepThreads) void decode_step_wide_kernel(GDN_DECO
 // After every head has read the evicted entry: store the new token in its
 // slot (and its gates at its ring index) and advance pos.  One workgroup per
 // sequence.
-template <class T, bool GLA>
+template <class T, int MODE>
 __global__ __launch_bounds__(256) void decode_commit_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ a,
     const float* __restrict__ b, T* __restrict__ kc, T* __restrict__ vc, float* __restrict__ ac,
@@ -407,8 +430,10 @@ __global__ __launch_bounds__(256) void decode_commit_kernel(
   if (t >= n_sink) {
     const int ring = (t - n_sink) % window;
     const size_t gb = ((size_t)bi * window + ring) * H;
-    if (GLA) {
+    if (MODE != 0) {
       for (int i = threadIdx.x; i < H * D; i += blockDim.x) ac[gb * D + i] = a[(size_t)bi * H * D + i];
+      if (MODE == 2)
+        for (int i = threadIdx.x; i < H; i += blockDim.x) bc[gb + i] = b[(size_t)bi * H + i];
     } else {
       for (int i = threadIdx.x; i < H; i += blockDim.x) {
         ac[gb + i] = a[(size_t)bi * H + i];
@@ -423,7 +448,7 @@ __global__ __launch_bounds__(256) void decode_commit_kernel(
 // Cache contents after a prefill of T tokens: sinks 0..min(n_sink,T)-1 in
 // their slots, window tokens max(n_sink, T-window)..T-1 in ring slots, their
 // gates at ring index (i - n_sink) mod window; unwritten slots are zeroed.
-template <class T, bool GLA>
+template <class T, int MODE>
 __global__ __launch_bounds__(256) void cache_fill_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ a,
     const float* __restrict__ b, T* __restrict__ kc, T* __restrict__ vc,
@@ -458,9 +483,11 @@ __global__ __launch_bounds__(256) void cache_fill_kernel(
   if (ring >= 0) {
     const size_t gb = ((size_t)bi * window + ring) * H;
     const size_t src = ((size_t)bi * T_ + (tok >= 0 ? tok : 0)) * H;
-    if (GLA) {
+    if (MODE != 0) {
       for (int i = threadIdx.x; i < H * D; i += blockDim.x)
         ac[gb * D + i] = tok >= 0 ? a[src * D + i] : 0.f;
+      if (MODE == 2)
+        for (int i = threadIdx.x; i < H; i += blockDim.x) bc[gb + i] = tok >= 0 ? b[src + i] : 0.f;
     } else {
       for (int i = threadIdx.x; i < H; i += blockDim.x) {
         ac[gb + i] = tok >= 0 ? a[src + i] : 0.f;
@@ -470,20 +497,20 @@ __global__ __launch_bounds__(256) void cache_fill_kernel(
   }
 }
 
-template <class T, bool GLA, int D>
+template <class T, int MODE, int D>
 hipError_t launch_decode_t(const DecodeArgs& p, hipStream_t s) {
   const int G = p.H / p.Hkv;
   const dim3 grid(xcd_grouped_grid((long long)p.B * p.Hkv, G));
   // one pass of 128 / sizeof(T) rows holds the whole budget: the narrow kernel
-  auto kern = p.n_sink + p.window <= (int)(128 / sizeof(T)) ? decode_step_kernel<T, GLA, D>
-                                                             : decode_step_wide_kernel<T, GLA, D>;
+  auto kern = p.n_sink + p.window <= (int)(128 / sizeof(T)) ? decode_step_kernel<T, MODE, D>
+                                                             : decode_step_wide_kernel<T, MODE, D>;
   hipLaunchKernelGGL(kern, grid, dim3(kStepThreads), 0, s, (const T*)p.q, (const T*)p.k,
                      (const T*)p.v, p.a, p.b, p.state, (const T*)p.k_cache, (const T*)p.v_cache,
                      p.a_cache, p.b_cache, p.pos, (T*)p.o, p.B, p.H, p.Hkv, p.n_sink, p.window,
                      p.flags, p.w_lin, p.w_swa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_commit_kernel<T, GLA>), dim3(p.B), dim3(256), 0, s, (const T*)p.k,
+  hipLaunchKernelGGL((decode_commit_kernel<T, MODE>), dim3(p.B), dim3(256), 0, s, (const T*)p.k,
                      (const T*)p.v, p.a, p.b, (T*)p.k_cache, (T*)p.v_cache, p.a_cache, p.b_cache,
                      p.pos, p.H, p.Hkv, D, p.n_sink, p.window);
   return hipGetLastError();
@@ -491,8 +518,9 @@ hipError_t launch_decode_t(const DecodeArgs& p, hipStream_t s) {
 
 template <class T>
 hipError_t launch_decode_d(const DecodeArgs& p, hipStream_t s) {
-  if (p.gla) return p.D == 64 ? launch_decode_t<T, true, 64>(p, s) : launch_decode_t<T, true, 128>(p, s);
-  return p.D == 64 ? launch_decode_t<T, false, 64>(p, s) : launch_decode_t<T, false, 128>(p, s);
+  if (p.gla && p.dgd) return p.D == 64 ? launch_decode_t<T, 2, 64>(p, s) : launch_decode_t<T, 2, 128>(p, s);
+  if (p.gla) return p.D == 64 ? launch_decode_t<T, 1, 64>(p, s) : launch_decode_t<T, 1, 128>(p, s);
+  return p.D == 64 ? launch_decode_t<T, 0, 64>(p, s) : launch_decode_t<T, 0, 128>(p, s);
 }
 
 }  // namespace
@@ -513,14 +541,15 @@ hipError_t launch_decode(const DecodeArgs& p, hipStream_t s) {
 
 hipError_t launch_cache_from_prefill(const CacheArgs& p, hipStream_t s) {
   const dim3 grid(p.n_sink + p.window, p.B);
-#define GDN_CACHE_LAUNCH(ET, GLA)                                                                  \
-  hipLaunchKernelGGL((cache_fill_kernel<ET, GLA>), grid, dim3(256), 0, s, (const ET*)p.k,          \
+#define GDN_CACHE_LAUNCH(ET, MODE)                                                                 \
+  hipLaunchKernelGGL((cache_fill_kernel<ET, MODE>), grid, dim3(256), 0, s, (const ET*)p.k,         \
                      (const ET*)p.v, p.a, p.b, (ET*)p.k_cache, (ET*)p.v_cache, p.a_cache,         \
                      p.b_cache, p.T, p.H, p.Hkv, p.D, p.n_sink, p.window)
+  const int mode = p.gla ? (p.dgd ? 2 : 1) : 0;
   if (p.bf16) {
-    if (p.gla) GDN_CACHE_LAUNCH(bf16, true); else GDN_CACHE_LAUNCH(bf16, false);
+    if (mode == 2) GDN_CACHE_LAUNCH(bf16, 2); else if (mode == 1) GDN_CACHE_LAUNCH(bf16, 1); else GDN_CACHE_LAUNCH(bf16, 0);
   } else {
-    if (p.gla) GDN_CACHE_LAUNCH(float, true); else GDN_CACHE_LAUNCH(float, false);
+    if (mode == 2) GDN_CACHE_LAUNCH(float, 2); else if (mode == 1) GDN_CACHE_LAUNCH(float, 1); else GDN_CACHE_LAUNCH(float, 0);
   }
 #undef GDN_CACHE_LAUNCH
   return hipGetLastError();

@@ -25,6 +25,7 @@ struct PrefillArgs {
   float w_lin = 1.f;   // branch weights: o = w_lin o_lin + w_swa o_swa
   float w_swa = 1.f;
   bool prepared = false;   // the workspace already holds the chunk preparation
+  int dgd = 0;   // with gla = 1: the delta rule with a diagonal gate (b used)
 };
 
 // Workspace of the gated delta rule prefill, per (sequence, head, chunk), as
@@ -58,14 +59,20 @@ hipError_t launch_gdn_full(const PrefillArgs& p, int nch, hipStream_t s, bool* s
 // Workspace of the GLA prefill: for each (sequence, head, chunk) Q 2^G
 // [64][D], (K 2^{G_C - G})^T [D][64], A [64][64] (I/O type, reduction index in
 // acc order) and 2^{G_C} [D] fp32, as four consecutive arrays.
+// Workspace of the per-channel-gate prefill, per (sequence, head, chunk):
+// Q 2^G [64][D], (K 2^{G_C - G})^T [D][64], A [64][64], 2^{G_C} [D] fp32;
+// the diagonal-gate delta rule adds TB = Tm diag(b) [64][64] and
+// -Wm = -TB (K 2^G) [64][D] (d_k in acc order).
 struct GlaWorkspace {
   void* qg;
   void* ktg;
   void* a;
   float* egc;
+  void* tb;    // delta only
+  void* wm;    // delta only
   size_t bytes;
 };
-GlaWorkspace gla_workspace_layout(void* base, int B, int H, int nch, int D, size_t elt);
+GlaWorkspace gla_workspace_layout(void* base, int B, int H, int nch, int D, size_t elt, bool delta);
 // Chunks of the linear stream of a sequence of length T.
 inline int gdn_stream_chunks(int T, int n_sink, int window) {
   const long long n = (long long)T - window - n_sink;
@@ -87,9 +94,10 @@ struct DecodeArgs {
   void* o;
   int B, H, Hkv, D;
   int n_sink, window;
-  int bf16, gla, flags;
+  int bf16, gla, flags;   // gla: per-channel gates (GLA, or the diagonal-gate delta rule)
   float w_lin = 1.f;   // branch weights: o = w_lin o_lin + w_swa o_swa
   float w_swa = 1.f;
+  int dgd = 0;   // with gla = 1: the delta rule with a diagonal gate (b used)
 };
 
 struct CacheArgs {
@@ -103,7 +111,8 @@ struct CacheArgs {
   float* b_cache;
   int B, T, H, Hkv, D;
   int n_sink, window;
-  int bf16, gla;
+  int bf16, gla;   // gla: per-channel gates (GLA, or the diagonal-gate delta rule)
+  int dgd = 0;     // the diagonal-gate delta rule: b cached too
 };
 
 struct ShortConvArgs {

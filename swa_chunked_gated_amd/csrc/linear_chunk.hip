@@ -21,6 +21,9 @@
 // per-channel cumulative log-gates G:
 //   A = [s <= r] o (Q e^G)(K e^-G)^T,  O = (Q e^G) S0 + A V,
 //   S = e^{G_C} o_rows S0 + (K e^{G_C - G})^T V.
+// The delta rule with that diagonal gate (mode 2) replaces V by
+// U = TB V - Wm S0 (TB = (I + L)^-1 diag(b), Wm = TB (K e^G), both from its
+// preparation): O = (Q e^G) S0 + A U, S = e^{G_C} o_rows S0 + (K e^{G_C - G})^T U.
 //
 // Work split: one workgroup per (sequence, query head, column slice of the
 // state).  The state's d_v columns are independent in both updates, so each
@@ -49,8 +52,12 @@ constexpr int kC = 64;          // chunk length
 __constant__ const int kTileM[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
 __constant__ const int kTileN[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 
-template <class T, int D, int NW, int DW, bool GLA>
+// MODE: 0 the gated delta rule, 1 GLA, 2 the delta rule with a diagonal
+// gate (the per-channel-gate tiles of GLA, plus TB and Wm).
+template <class T, int D, int NW, int DW, int MODE>
 struct Smem {
+  static constexpr bool GLA = MODE != 0;    // per-channel gate tiles from the workspace
+  static constexpr bool DELTA = MODE != 1;  // U = TB V - Wm S
   static constexpr int PAD = 16 / sizeof(T);
   static constexpr int SK = D + PAD;        // stride of [64][D] arrays
   static constexpr int SC = kC + PAD;       // stride of [*][64] arrays
@@ -66,26 +73,29 @@ struct Smem {
   static constexpr int oVT = oQ + nK;
   static constexpr int oAq = oVT + nVT;
   static constexpr int oWm = oAq + nA;
-  static constexpr int oTB = oWm + (GLA ? 0 : nK);
-  static constexpr int nT = oTB + (GLA ? 0 : nA);
+  static constexpr int oTB = oWm + (DELTA ? nK : 0);
+  static constexpr int nT = oTB + (DELTA ? nA : 0);
   static constexpr int bytesT = ((nT * (int)sizeof(T)) + 15) / 16 * 16;
   // fp32 part: GDN g (log2), gamma [64 each]; GLA 2^{G_C} [D]
   static constexpr int nGate = GLA ? D : 2 * kC;
   static constexpr int bytes = bytesT + 4 * nGate;
 };
 
-template <class T, int D, int NW, int DW, bool GLA>
+template <class T, int D, int NW, int DW, int MODE>
 __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ w0, const T* __restrict__ w1, const T* __restrict__ w2,
-    const float* __restrict__ wf, T* __restrict__ o,
+    const T* __restrict__ w3, const T* __restrict__ w4, const float* __restrict__ wf, T* __restrict__ o,
     float* __restrict__ state_out, int T_, int H, int Hkv, int n_sink, int window, int flags,
     float w_lin) {
   // w_lin weighs the linear branch in o (1 for the plain sum).
   // chunk preparation results (workspace), per (sequence, head, chunk):
   //   GDN, light: w0 = Tm diag(b), wf = g (log2), gamma (w1 unused)
   //   GLA:        w0 = Q 2^G, w1 = (K 2^{G_C - G})^T, w2 = A, wf = 2^{G_C}
-  using SM = Smem<T, D, NW, DW, GLA>;
+  //   diagonal-gate delta rule: as GLA, plus w3 = TB, w4 = -Wm
+  using SM = Smem<T, D, NW, DW, MODE>;
+  constexpr bool GLA = SM::GLA;
+  constexpr bool DGD = MODE == 2;
   constexpr int kThreads = 64 * NW;
   constexpr int SK = SM::SK;
   constexpr int SC = SM::SC;
@@ -165,6 +175,8 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
   constexpr int NPT = GLA ? 1 : kC * kC / VEC / kThreads;
   static_assert(GLA || (kC * kC / VEC) % kThreads == 0, "TB staging");
   V16 ptb[GLA ? NPK : NPT], ptbg[GLA ? NPA : 1];
+  constexpr int NPT2 = kC * kC / VEC / kThreads;   // diagonal-gate delta: TB pieces
+  V16 pt2[DGD ? NPT2 : 1], pwm[DGD ? NPQ : 1];
   f32x4 pgm = zero4();
   const size_t chain = (size_t)bi * H + h;
 
@@ -194,6 +206,14 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
 #pragma unroll
       for (int n = 0; n < NPA; ++n) ptbg[n] = aa[tid + n * kThreads];
       if (tid < D / 4) pgm = reinterpret_cast<const f32x4*>(wf + ci * D)[tid];
+      if constexpr (DGD) {
+        const V16* tb = reinterpret_cast<const V16*>(w3 + ci * (kC * kC));
+        const V16* wm = reinterpret_cast<const V16*>(w4 + ci * (kC * D));
+#pragma unroll
+        for (int n = 0; n < NPT2; ++n) pt2[n] = tb[tid + n * kThreads];
+#pragma unroll
+        for (int n = 0; n < NPQ; ++n) pwm[n] = wm[tid + n * kThreads];
+      }
     } else {
       const T* kp = k + ((size_t)(bi * T_ + i0 + kr0) * Hkv + g) * D + kdc * EPD;
       if (full) {
@@ -246,6 +266,18 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
         *reinterpret_cast<V16*>(&Aqs[(j / (kC / VEC)) * SC + (j % (kC / VEC)) * VEC]) = ptbg[n];
       }
       if (tid < D / 4) *reinterpret_cast<f32x4*>(&gate[4 * tid]) = pgm;
+      if constexpr (DGD) {
+#pragma unroll
+        for (int n = 0; n < NPT2; ++n) {
+          const int j = tid + n * kThreads;
+          *reinterpret_cast<V16*>(&TBs[(j / (kC / VEC)) * SC + (j % (kC / VEC)) * VEC]) = pt2[n];
+        }
+#pragma unroll
+        for (int n = 0; n < NPQ; ++n) {
+          const int j = tid + n * kThreads;
+          *reinterpret_cast<V16*>(&Wms[(j / (D / VEC)) * SK + (j % (D / VEC)) * VEC]) = pwm[n];
+        }
+      }
     } else {
       // K row-major (one dword per token, columns in acc order) and
       // transposed (tokens in acc order, runs of 4)
@@ -291,7 +323,7 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
     lds_barrier();
     if (c + 1 < nch) prefetch(c + 1);
 
-    if constexpr (!GLA) {
+    if constexpr (MODE == 0) {
       const float* lgs = gate;
       // ---- Q K^T -> A (decayed, masked s <= r) on the 10 lower 16x16 tiles;
       // the rest of the chunk's state-independent work comes from the chunk
@@ -384,7 +416,7 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
           for (int dt = 0; dt < NT; ++dt) ot[dt][rt] = mfma(sf[2 * ph + pp][dt], qf[rt][pp], ot[dt][rt]);
     }
 
-    if (GLA) {
+    if constexpr (MODE == 1) {
       // ... + V^T A^T
       {
         Frag<T> vf[NT][2], af[4][2];
@@ -430,7 +462,7 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
       }
     } else {
       const float* gam = gate + kC;
-      // U = Tm diag(b) V - Wm S   (tokens x columns)
+      // U = Tm diag(b) V - Wm S   (tokens x columns); the same in both delta modes
       f32x4 U[4][NT];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -468,28 +500,33 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) U[mt][nt] = mfma(wf[mt][pp], sf[2 * ph + pp][nt], U[mt][nt]);
       }
-      // O^T: scale the S^T Q^T part by gamma of each query column, then + U^T A^T
+      // O^T: (scalar gate) scale the S^T Q^T part by gamma of each query
+      // column, then + U^T A^T
+      if constexpr (!DGD) {
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const float gq = gam[16 * rt + l16];
+        for (int rt = 0; rt < 4; ++rt) {
+          const float gq = gam[16 * rt + l16];
 #pragma unroll
-        for (int dt = 0; dt < NT; ++dt) ot[dt][rt] *= gq;
+          for (int dt = 0; dt < NT; ++dt) ot[dt][rt] *= gq;
+        }
       }
-      const float gC = gam[kC - 1];
-      const float lgC = gate[kC - 1];
-      Frag<T> uf[2][NT], us[2][NT];   // U as operand: plain, and scaled by gamma_C / gamma_s
+      // U as operand: plain, and (scalar gate) scaled by gamma_C / gamma_s
+      Frag<T> uf[2][NT], us[2][NT];
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
         f32x4 s0, s1;
+        if constexpr (!DGD) {
+          const float lgC = gate[kC - 1];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          s0[i] = __builtin_amdgcn_exp2f(fminf(lgC - gate[32 * pp + 4 * lg + i], 0.f));
-          s1[i] = __builtin_amdgcn_exp2f(fminf(lgC - gate[32 * pp + 16 + 4 * lg + i], 0.f));
+          for (int i = 0; i < 4; ++i) {
+            s0[i] = __builtin_amdgcn_exp2f(fminf(lgC - gate[32 * pp + 4 * lg + i], 0.f));
+            s1[i] = __builtin_amdgcn_exp2f(fminf(lgC - gate[32 * pp + 16 + 4 * lg + i], 0.f));
+          }
         }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           uf[pp][nt] = frag_from_acc<T>(U[2 * pp][nt], U[2 * pp + 1][nt]);
-          us[pp][nt] = frag_from_acc_scaled<T>(U[2 * pp][nt], U[2 * pp + 1][nt], s0, s1);
+          us[pp][nt] = DGD ? uf[pp][nt] : frag_from_acc_scaled<T>(U[2 * pp][nt], U[2 * pp + 1][nt], s0, s1);
         }
       }
       {
@@ -507,11 +544,22 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
 #pragma unroll
             for (int dt = 0; dt < NT; ++dt) ot[dt][rt] = mfma(uf[pp][dt], af[rt][pp], ot[dt][rt]);
       }
-      // S = gamma_C S + K^T diag(gamma_C / gamma) U
+      // S = gamma_C S + K^T diag(gamma_C / gamma) U; diagonal gate:
+      // S = 2^{G_C} o_rows S + (K 2^{G_C - G})^T U
+      if constexpr (DGD) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt) {
+          const f32x4 dec = *reinterpret_cast<const f32x4*>(&gate[16 * mt + 4 * lg]);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) S[mt][nt] *= gC;
+          for (int nt = 0; nt < NT; ++nt) S[mt][nt] *= dec;
+        }
+      } else {
+        const float gC = gam[kC - 1];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) S[mt][nt] *= gC;
+      }
 #pragma unroll
       for (int m4 = 0; m4 < MT / 4; ++m4) {
         Frag<T> kf[4][2];
@@ -572,10 +620,10 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
   }
 }
 
-template <class T, int D, int NW, int DW, bool GLA>
+template <class T, int D, int NW, int DW, int MODE>
 hipError_t launch_linear_t(const PrefillArgs& p, hipStream_t s) {
-  using SM = Smem<T, D, NW, DW, GLA>;
-  auto kern = linear_chunk_kernel<T, D, NW, DW, GLA>;
+  using SM = Smem<T, D, NW, DW, MODE>;
+  auto kern = linear_chunk_kernel<T, D, NW, DW, MODE>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, SM::bytes);
   if (e != hipSuccess) return e;
   // x: the (column slice, query head) members of each KV head, placed by
@@ -586,12 +634,16 @@ hipError_t launch_linear_t(const PrefillArgs& p, hipStream_t s) {
   const T* w0;
   const T* w1;
   const T* w2 = nullptr;
+  const T* w3 = nullptr;
+  const T* w4 = nullptr;
   const float* wf;
-  if (GLA) {
-    const GlaWorkspace w = gla_workspace_layout(p.workspace, p.B, p.H, nch, D, sizeof(T));
+  if (MODE != 0) {
+    const GlaWorkspace w = gla_workspace_layout(p.workspace, p.B, p.H, nch, D, sizeof(T), MODE == 2);
     w0 = (const T*)w.qg;
     w1 = (const T*)w.ktg;
     w2 = (const T*)w.a;
+    w3 = (const T*)w.tb;
+    w4 = (const T*)w.wm;
     wf = w.egc;
   } else {
     const GdnWorkspace w = gdn_workspace_layout(p.workspace, p.B, p.H, nch, D, sizeof(T), false);
@@ -600,24 +652,37 @@ hipError_t launch_linear_t(const PrefillArgs& p, hipStream_t s) {
     wf = w.g;
   }
   hipLaunchKernelGGL(kern, grid, dim3(64 * NW), SM::bytes, s, (const T*)p.q, (const T*)p.k,
-                     (const T*)p.v, w0, w1, w2, wf, (T*)p.o, p.state_out, p.T, p.H, p.Hkv,
+                     (const T*)p.v, w0, w1, w2, w3, w4, wf, (T*)p.o, p.state_out, p.T, p.H, p.Hkv,
                      p.n_sink, p.window, p.flags, p.w_lin);
   return hipGetLastError();
 }
 
-template <class T, int D, int NW, bool GLA>
+template <class T, int D, int NW, int MODE>
 hipError_t launch_linear_f(const PrefillArgs& p, hipStream_t s) {
-  return launch_linear_t<T, D, NW, 16, GLA>(p, s);
+  return launch_linear_t<T, D, NW, 16, MODE>(p, s);
 }
 
 // 16 state columns per wave.  d = 128: one workgroup of 8 waves per chain
 // when there are enough chains to fill the GPU, else two workgroups of 4
 // waves per chain.  d = 64: one workgroup of 4 waves.
-template <class T, bool GLA>
+template <class T, int MODE>
 hipError_t launch_linear_d(const PrefillArgs& p, hipStream_t s) {
-  if (p.D == 64) return launch_linear_f<T, 64, 4, GLA>(p, s);
-  if ((size_t)p.B * p.H >= 256) return launch_linear_f<T, 128, 8, GLA>(p, s);
-  return launch_linear_f<T, 128, 4, GLA>(p, s);
+  if (p.D == 64) return launch_linear_f<T, 64, 4, MODE>(p, s);
+  if ((size_t)p.B * p.H >= 256) return launch_linear_f<T, 128, 8, MODE>(p, s);
+  return launch_linear_f<T, 128, 4, MODE>(p, s);
+}
+
+// bf16: d = 64 or 128; fp32: d = 64 only (its state tiles fit LDS only there)
+template <class T, int MODE>
+hipError_t launch_linear_dt(const PrefillArgs& p, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) return launch_linear_d<T, MODE>(p, s);
+  else return launch_linear_f<T, 64, 4, MODE>(p, s);
+}
+
+template <class T>
+hipError_t launch_linear_m(const PrefillArgs& p, hipStream_t s) {
+  if (!p.gla) return launch_linear_dt<T, 0>(p, s);
+  return p.dgd ? launch_linear_dt<T, 2>(p, s) : launch_linear_dt<T, 1>(p, s);
 }
 
 }  // namespace
@@ -643,9 +708,9 @@ hipError_t launch_linear_prefill(const PrefillArgs& p, hipStream_t s, bool* swa_
     const hipError_t e = p.gla ? launch_gla_prep(p, nch, s) : launch_gdn_prep(p, nch, s);
     if (e != hipSuccess) return e;
   }
-  if (p.bf16) return p.gla ? launch_linear_d<bf16, true>(p, s) : launch_linear_d<bf16, false>(p, s);
+  if (p.bf16) return launch_linear_m<bf16>(p, s);
   if (p.D != 64) return hipErrorInvalidValue;   // fp32 state tiles fit LDS only at d = 64
-  return p.gla ? launch_linear_f<float, 64, 4, true>(p, s) : launch_linear_f<float, 64, 4, false>(p, s);
+  return launch_linear_m<float>(p, s);
 }
 
 }  // namespace gdn

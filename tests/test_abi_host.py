@@ -93,7 +93,11 @@ def test_workspace_query(lib):
     assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 0, BF16, DELTA, 3)[0] == EINVAL    # window
     assert ws(lib, 1, 4096, 32, 8, 128, 128, -1, 56, BF16, DELTA, 3)[0] == EINVAL  # n_sink
     assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, 2, DELTA, 3)[0] == EINVAL      # dtype
-    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, 2, 3)[0] == EINVAL       # update
+    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, 3, 3)[0] == EINVAL       # update
+    # the diagonal-gate delta rule: the per-channel-gate tiles plus TB and Wm
+    rc, n = ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, 2, 3)
+    nch = (4096 - 64 + 63) // 64
+    assert rc == OK and n >= 32 * nch * ((3 * 64 * 128 + 2 * 64 * 64) * 2 + 128 * 4)
     assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 0)[0] == EINVAL   # flags
     assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 8)[0] == EINVAL
     assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 16)[0] == EINVAL
@@ -113,6 +117,7 @@ def test_prefill_validation(lib):
     assert prefill(lib, o=None) == EINVAL
     assert prefill(lib, a=None) == EINVAL                       # linear branch needs a
     assert prefill(lib, b=None) == EINVAL                       # GDN needs b
+    assert prefill(lib, b=None, up=2) == EINVAL                 # so does the diagonal-gate delta rule
     assert prefill(lib, st=None, flags=7) == EINVAL             # state requested
     assert prefill(lib, B=0) == EINVAL
     assert prefill(lib, T=-1) == EINVAL

@@ -558,7 +558,7 @@ def run_decode(step_inp, st, w, flags=ALL):
     return o
 
 
-@pytest.mark.parametrize("update", ["gdn", "gla"])
+@pytest.mark.parametrize("update", ["gdn", "gla", "dgd"])
 @pytest.mark.parametrize("pos0", [0, 2, 6, 60, 63, 64, 65, 500])
 def test_decode_steps_small(update, pos0):
     w = Workload("dec", B=3, H=4, Hkv=2, d=128, n_sink=3, window=61, update=update, pos0=pos0,
@@ -582,13 +582,14 @@ def test_decode_steps_small(update, pos0):
         assert np.array_equal(f64(st["k_cache"]), ref["k_cache"])
         assert np.array_equal(f64(st["v_cache"]), ref["v_cache"])
         assert np.array_equal(f64(st["a_cache"]), ref["a_cache"])
-        if update == "gdn":
+        if update != "gla":
             assert np.array_equal(f64(st["b_cache"]), ref["b_cache"])
 
 
 @pytest.mark.parametrize("dtype,n_sink,window,pos0,update", [
     ("f32", 3, 61, 62, "gdn"), ("bf16", 8, 592, 5, "gdn"), ("bf16", 8, 592, 598, "gla"),
-    ("bf16", 0, 300, 1000, "gdn"), ("f32", 8, 120, 130, "gla"), ("bf16", 8, 888, 4000, "gdn")])
+    ("bf16", 0, 300, 1000, "gdn"), ("f32", 8, 120, 130, "gla"), ("bf16", 8, 888, 4000, "gdn"),
+    ("bf16", 8, 592, 598, "dgd"), ("f32", 3, 61, 62, "dgd")])
 def test_decode_long_budgets(dtype, n_sink, window, pos0, update):
     """Budgets that take several staged passes of cached rows (online softmax
     across passes, a partial last pass), against the oracle's decode step."""

@@ -41,7 +41,7 @@ class Workload:
     T: int = 0                 # prefill length (0 for decode-only workloads)
     sigma: float = 0.5         # key noise scale around the head direction
     dtype: str = "bf16"        # q/k/v/o/cache element type: "f32" or "bf16"
-    update: str = "gdn"        # "gdn" or "gla"
+    update: str = "gdn"        # "gdn", "gla" or "dgd" (delta rule, per-channel gate)
     write_state: bool = False
     shortconv: bool = False    # raw q/k/v go through RoPE -> conv -> L2 norm
     conv_ks: int = 8
@@ -119,7 +119,7 @@ def make_prefill_inputs(w: Workload, device="cpu", seed: int = 0, T: int | None 
     a_logit = torch.randn(B, T, w.H, **f32) + w.gate_mean
     k = mu[None, None] + w.sigma * knoise
     out = {}
-    if w.update == "gla":
+    if w.update in ("gla", "dgd"):
         a_logit = torch.randn(B, T, w.H, d, **f32) + w.gate_mean
     if w.shortconv:
         ks = w.conv_ks
@@ -173,7 +173,7 @@ def make_decode_inputs(w: Workload, device="cpu", seed: int = 0, steps: int | No
     k_cache = keys(B, N, Hkv).permute(0, 2, 1, 3).to(dt).contiguous()
     raw = w.shortconv          # the cache holds prepared keys; new tokens arrive raw
     v_cache = torch.randn(B, Hkv, N, d, **f32).to(dt).contiguous()
-    a_shape = (B, W, H, d) if w.update == "gla" else (B, W, H)
+    a_shape = (B, W, H, d) if w.update in ("gla", "dgd") else (B, W, H)
     a_cache = gate_a(*a_shape).contiguous()
     b_cache = torch.sigmoid(torch.randn(B, W, H, **f32)).contiguous()
     pos = torch.full((B,), w.pos0, dtype=torch.int32, device=device)
@@ -181,7 +181,7 @@ def make_decode_inputs(w: Workload, device="cpu", seed: int = 0, steps: int | No
     q = (q if raw else _unit(q)).to(dt).contiguous()
     k = keys(steps, B, Hkv).to(dt).contiguous()
     v = torch.randn(steps, B, Hkv, d, **f32).to(dt).contiguous()
-    a_step_shape = (steps, B, H, d) if w.update == "gla" else (steps, B, H)
+    a_step_shape = (steps, B, H, d) if w.update in ("gla", "dgd") else (steps, B, H)
     a = gate_a(*a_step_shape).contiguous()
     b = torch.sigmoid(torch.randn(steps, B, H, **f32)).contiguous()
     out = dict(state=state, k_cache=k_cache, v_cache=v_cache, a_cache=a_cache,
