@@ -72,7 +72,9 @@ def gla_flops(w, T=None):
 
 
 def linear_flops(w):
-    return gdn_flops(w) if w.update == "gdn" else gla_flops(w)
+    """The delta rule with the diagonal gate does the scalar-gate rule's
+    products (its gates scale operands instead of rows)."""
+    return gla_flops(w) if w.update == "gla" else gdn_flops(w)
 
 
 def gdn_prep_flops(w):
@@ -152,6 +154,7 @@ CALL_KERNELS = {
                           "linear": "gdn_prep_kernel+linear_chunk_kernel", "softmax": "swa_kernel"},
     "qwen32b_t8192_gla": {"shortconv": "shortconv_kernel",
                           "linear": "gla_prep_kernel+linear_chunk_kernel", "softmax": "swa_kernel"},
+    "dgd_b8_t8192": {"linear": "gla_prep_kernel+linear_chunk_kernel", "softmax": "swa_ring_kernel"},
 }
 CSRC = "swa_chunked_gated_amd/csrc/"
 KERNEL_SOURCES = {
@@ -233,7 +236,7 @@ def _oracle_prefill_head(h):
                                   f["wv"].reshape(w.Hkv, w.d, -1)[g], w.rope_theta, 0, flags=3)
     else:
         q, k, v = f["q"][:, :, h:h + 1], f["k"][:, :, g:g + 1], f["v"][:, :, g:g + 1]
-    b = f["b"][:, :, h:h + 1] if w.update == "gdn" else None
+    b = f["b"][:, :, h:h + 1] if w.update != "gla" else None
     O.hybrid_prefill(q, k, v, f["a"][:, :, h:h + 1], b, w.n_sink, w.window, update=w.update)
     return h
 
@@ -308,6 +311,7 @@ CPU_SAMPLES = {
     "llama8b_t4096": dict(T_sample=4096, heads=range(32)),
     "qwen32b_t8192_gdn": dict(T_sample=4096, heads=range(32)),
     "qwen32b_t8192_gla": dict(T_sample=4096, heads=range(32)),
+    "dgd_b8_t8192": dict(T_sample=4096, heads=range(32)),
     "decode_b256": dict(steps=20),
 }
 
@@ -581,7 +585,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default="all",
-                    choices=["all", "headline", "longctx", "llama", "tiny", "decode", "qwen32b",
+                    choices=["all", "headline", "longctx", "llama", "tiny", "dgd", "decode", "qwen32b",
                              "qwen32b_decode", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parts", action="store_true",
@@ -595,7 +599,7 @@ def main():
     parts = not args.no_parts
 
     # single-workload legs (profiling and counter runs)
-    single = {"longctx": HEADLINE, "llama": "llama8b_t4096", "tiny": "tiny_fp32"}
+    single = {"longctx": HEADLINE, "llama": "llama8b_t4096", "tiny": "tiny_fp32", "dgd": "dgd_b8_t8192"}
     if args.only in single or args.only in ("decode", "qwen32b", "qwen32b_decode", "copy"):
         import torch
         if not torch.cuda.is_available():
@@ -622,7 +626,7 @@ def main():
     if not args.no_cpu_baseline:
         todo = [HEADLINE] + ([] if args.only == "headline" else
                              ["tiny_fp32", "llama8b_t4096", "decode_b256", "qwen32b_t8192_gdn",
-                              "qwen32b_t8192_gla"])
+                              "qwen32b_t8192_gla", "dgd_b8_t8192"])
         for n in todo:
             cpu[n] = cpu_baseline(n, cores, **CPU_SAMPLES[n])
             print(f"# cpu_baseline {n}: {cpu[n]['value']:.1f} {cpu[n]['unit']} "
@@ -638,7 +642,7 @@ def main():
     print(f"# headline done: {m['ms_per_step']:.3f} ms per step", file=sys.stderr, flush=True)
     also = {}
     if args.only == "all":
-        for n in ("tiny_fp32", "llama8b_t4096", "qwen32b_t8192_gdn", "qwen32b_t8192_gla"):
+        for n in ("tiny_fp32", "llama8b_t4096", "qwen32b_t8192_gdn", "qwen32b_t8192_gla", "dgd_b8_t8192"):
             also[n] = bench_prefill(n, args.steps, args.warmup, parts=True)
             also[n]["cpu_baseline"] = cpu.get(n)
             print(f"# {n} done", file=sys.stderr, flush=True)

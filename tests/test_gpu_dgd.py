@@ -86,3 +86,21 @@ def test_dgd_prefill_cache_then_decode_equals_longer_prefill():
         torch.cuda.synchronize()
         assert_close(f64(o), ref[:, t], False, f"o t={t}")
     assert bool((pos == T0 + n).all())
+
+
+def test_dgd_b8_t8192_sampled():
+    """The benchmarked shape (B = 8, T = 8192, 32 / 8 heads, budget 8 + 120,
+    state out) in the launch configuration the bench times; sequence 0's
+    first KV group against the oracle on every row and the final state."""
+    from workloads import WORKLOADS
+    w = WORKLOADS["dgd_b8_t8192"]
+    inp = make_prefill_inputs(w, device=DEV)
+    o, st = gl.hybrid_prefill(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], w.n_sink, w.window,
+                              update="dgd", flags=ALL | gl.WRITE_STATE)
+    torch.cuda.synchronize()
+    heads = [0, 3]
+    ref, S = O.hybrid_prefill(f64(inp["q"][:1][:, :, heads]), f64(inp["k"][:1][:, :, :1]),
+                              f64(inp["v"][:1][:, :, :1]), f64(inp["a"][:1][:, :, heads]),
+                              f64(inp["b"][:1][:, :, heads]), w.n_sink, w.window, update="dgd")
+    assert_close(f64(o[:1][:, :, heads]), ref, False, "o")
+    assert_close(f64(st[:1][:, heads]), S, False, "state")

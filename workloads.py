@@ -71,6 +71,10 @@ WORKLOADS = {
     "longctx_b8_t32768": Workload("longctx_b8_t32768", B=8, H=32, Hkv=8, d=128,
                                   n_sink=8, window=120, T=32768, sigma=1.0,
                                   write_state=True),
+    # The delta rule with a diagonal (per-channel) gate at the long-context
+    # head shape: 8 sequences of 8192 tokens, budget 8 + 120, final state out.
+    "dgd_b8_t8192": Workload("dgd_b8_t8192", B=8, H=32, Hkv=8, d=128, n_sink=8, window=120,
+                             T=8192, sigma=1.0, write_state=True, update="dgd"),
     # Decode: 256 sequences, 32 query / 8 KV heads, cache 8 + 56, t = 4096+.
     "decode_b256": Workload("decode_b256", B=256, H=32, Hkv=8, d=128, n_sink=8,
                             window=56, sigma=0.5, pos0=4096, steps=1000),
