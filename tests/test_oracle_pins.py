@@ -276,6 +276,74 @@ def chunked_gdn(q, k, v, a, b, n_sink, window, C):
     return o, Sf
 
 
+def segmented_gdn(q, k, v, a, b, n_sink, window, C, P):
+    """fp64 segmented chunk scan: the stream's chunks split into P segments.
+    Phase 1 (independent per segment): run the chunk form from a zero state
+    on V, giving local outputs and the segment's end state N_s, and on the
+    augmented value columns [0 | I] (initial state I, V = 0), giving the
+    segment's state map M_s = prod M_c and, as outputs, every row's
+    q_hat = P_t^T q_t (P_t: the map from the segment's start to the row's
+    state).  Phase 2: S_in(s+1) = M_s S_in(s) + N_s.  Phase 3:
+    o_t = o_local_t + S_in(s)^T q_hat_t."""
+    B, T, H, dk = q.shape
+    G = H // k.shape[2]
+    dv = v.shape[-1]
+    o = np.zeros((B, T, H, dv))
+    Sf = np.zeros((B, H, dk, dv))
+    starts = list(range(n_sink, T - window, C))
+    per = -(-len(starts) // P) if starts else 0
+    for bi in range(B):
+        for h in range(H):
+            g = h // G
+            segs = []
+            for s0 in range(0, len(starts), per):
+                S = np.zeros((dk, dv))
+                Pm = np.eye(dk)
+                rows = []
+                for c0 in starts[s0:s0 + per]:
+                    c1 = min(c0 + C, T - window)
+                    K = k[bi, c0:c1, g]
+                    V = v[bi, c0:c1, g]
+                    Q = q[bi, c0 + window:c1 + window, h]
+                    bb = b[bi, c0:c1, h]
+                    gam = np.exp(np.cumsum(np.log(a[bi, c0:c1, h])))
+                    ratio = gam[:, None] / gam[None, :]
+                    L = np.tril(bb[:, None] * ratio * (K @ K.T), -1)
+                    Tm = np.linalg.inv(np.eye(len(bb)) + L)
+                    Wm = Tm @ ((bb * gam)[:, None] * K)
+                    Ut = Tm @ (bb[:, None] * V)
+                    Aq = np.tril(ratio) * (Q @ K.T)
+                    Kt = (gam[-1] / gam)[:, None] * K
+                    U = Ut - Wm @ S
+                    UP = -Wm @ Pm
+                    rows.append((c0 + window, c1 + window,
+                                 gam[:, None] * (Q @ S) + Aq @ U,        # o_local
+                                 gam[:, None] * (Q @ Pm) + Aq @ UP))     # q_hat rows
+                    S = gam[-1] * S + Kt.T @ U
+                    Pm = gam[-1] * Pm + Kt.T @ UP
+                segs.append((S, Pm, rows))
+            S_in = np.zeros((dk, dv))
+            for N_s, M_s, rows in segs:
+                for r0, r1, o_loc, q_hat in rows:
+                    o[bi, r0:r1, h] = o_loc + q_hat @ S_in
+                S_in = M_s @ S_in + N_s
+            Sf[bi, h] = S_in
+    return o, Sf
+
+
+@pytest.mark.parametrize("C,P", [(16, 1), (16, 3), (16, 8), (7, 5), (64, 2)])
+def test_segmented_chunk_scan_matches_stepwise(C, P):
+    """Segment composition (affine maps M_s, N_s per segment, a P-step carry
+    and a per-row fix-up through q_hat) reproduces the stepwise outputs and
+    final state."""
+    n_sink, window, T, B, H, Hkv, d = 4, 12, 190, 1, 2, 1, 8
+    q, k, v, a, b = rand_layer(B, T, H, Hkv, d)
+    o, S = O.gdn_linear_branch(q, k, v, a, b, n_sink, window)
+    os_, Ss = segmented_gdn(q, k, v, a, b, n_sink, window, C, P)
+    np.testing.assert_allclose(os_, o, atol=1e-11, rtol=0)
+    np.testing.assert_allclose(Ss, S, atol=1e-11, rtol=0)
+
+
 @pytest.mark.parametrize("C", [64, 16, 7])
 def test_chunked_form_matches_stepwise(C):
     n_sink, window, T, B, H, Hkv, d = 4, 12, 173, 1, 4, 2, 8
