@@ -288,10 +288,15 @@ __device__ __forceinline__ void gdn_prep_chunk(
   const T* kbase = k + ((size_t)(bi * T_ + i0) * Hkv + g) * D;
   const T* qbase = q + ((size_t)(bi * T_ + i0 + window) * H + h) * D;
 
-  // ---- this chunk's gates first (a = 1, b = 0 past the stream end)
+  // ---- this chunk's gates first (a = 1, b = 0 past the stream end).  Every
+  // load is unconditional (rows past the stream read its last row), so the
+  // memory counters the compiler waits on stay exact and the gate math
+  // waits for the gates only.
   const int tok = i0 + lane;
-  const float av = tok < iend ? a[(size_t)(bi * T_ + tok) * H + h] : 1.f;
-  const float bv = tok < iend ? b[(size_t)(bi * T_ + tok) * H + h] : 0.f;
+  const size_t tokc = (size_t)(bi * T_ + min(tok, iend - 1)) * H + h;
+  const float ar = a[tokc];
+  const float br0 = b[tokc];
+  asm volatile("" ::: "memory");   // the gates' loads go out first
 
   // ---- operand pieces: lane holds rows 16 mt + l16, dims 32 p + 8 lg .. +7
   V16 kr[4][KS][QV];
@@ -299,25 +304,23 @@ __device__ __forceinline__ void gdn_prep_chunk(
   const bool whole = i0 + kC <= iend;          // uniform: no row past the stream
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
-    const int r = 16 * mt + l16;
-    const bool live = whole || i0 + r < iend;
+    const int r = min(16 * mt + l16, iend - 1 - i0);
 #pragma unroll
     for (int p = 0; p < KS; ++p)
 #pragma unroll
       for (int u = 0; u < QV; ++u) {
         const int col = 32 * p + 8 * lg + u * EPC;
-        if (live) {
-          kr[mt][p][u] = *reinterpret_cast<const V16*>(kbase + (size_t)r * Hkv * D + col);
-          if constexpr (FULL) qr[mt][p][u] = *reinterpret_cast<const V16*>(qbase + (size_t)r * H * D + col);
-        } else {
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) {
-            kr[mt][p][u][e] = from_f32<T>(0.f);
-            if constexpr (FULL) qr[mt][p][u][e] = from_f32<T>(0.f);
-          }
-        }
+        kr[mt][p][u] = *reinterpret_cast<const V16*>(kbase + (size_t)r * Hkv * D + col);
+        if constexpr (FULL) qr[mt][p][u] = *reinterpret_cast<const V16*>(qbase + (size_t)r * H * D + col);
       }
   }
+  // Rows past the stream keep their duplicated values: with a = 1 and b = 0
+  // there, they add nothing.  Their L rows are b_r (...) = 0, so their TB
+  // (and TBG) rows and columns are zero, which zeroes their Wm and U rows and
+  // the products of their K^T columns; their query rows are never stored.
+  const float av = tok < iend ? ar : 1.f;
+  const float bv = tok < iend ? br0 : 0.f;
+  (void)whole;
   auto frag_of = [&](const V16 (&pc)[QV]) {
     float x[8];
 #pragma unroll
@@ -421,22 +424,40 @@ __device__ __forceinline__ void gdn_prep_chunk(
   // the full preparation keeps both in LDS, the light one writes TB (the scan
   // scales it by gamma where it needs TBG)
   T* tb = wtb + ci * (kC * kC);
+  if constexpr (FULL) {
 #pragma unroll 4
-  for (int i = lane; i < kC * kC / 4; i += 64) {
-    const int r = i >> 4;
-    const int s0 = (i & 15) * 4;
-    // (the packed layout holds no blocks above the diagonal: zero there)
-    const f32x4 tm = (s0 >> 4) <= (r >> 4) ? *reinterpret_cast<const f32x4*>(&Lf[lidx<LL>(r, s0)]) : zero4();
-    const f32x4 bb = *reinterpret_cast<const f32x4*>(&bet[s0]);
-    const f32x4 gg = *reinterpret_cast<const f32x4*>(&gam[s0]);
-    const f32x4 x = tm * bb;
-    if constexpr (FULL) {
+    for (int i = lane; i < kC * kC / 4; i += 64) {
+      const int r = i >> 4;
+      const int s0 = (i & 15) * 4;
+      const f32x4 tm = *reinterpret_cast<const f32x4*>(&Lf[lidx<LL>(r, s0)]);
+      const f32x4 bb = *reinterpret_cast<const f32x4*>(&bet[s0]);
+      const f32x4 gg = *reinterpret_cast<const f32x4*>(&gam[s0]);
+      const f32x4 x = tm * bb;
       store4(&TBs[r * SC + acc_pos(s0)], x);
       store4(&TBGs[r * SC + acc_pos(s0)], x * gg);
-    } else {
-      (void)gg;
-      put4v<DEV>(tb, r * kC + acc_pos(s0), x);
     }
+  } else {
+    // lane: columns s0 .. s0 + 3 of rows 16 R + 4 m + (lane / 16); every
+    // row's block row R is known at compile time, and the reads (all issued
+    // before the stores) stay inside the packed buffer: a column block above
+    // the diagonal reads some other row's values, which the select zeroes
+    const int s0 = (lane & 15) * 4;
+    const int rr = lane >> 4;
+    const f32x4 bb = *reinterpret_cast<const f32x4*>(&bet[s0]);
+    f32x4 tm[4][4];
+#pragma unroll
+    for (int R = 0; R < 4; ++R)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        tm[R][m] = *reinterpret_cast<const f32x4*>(&Lf[LL::row0(R) + (4 * m + rr) * LL::stride(R) + s0]);
+#pragma unroll
+    for (int R = 0; R < 4; ++R)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int r = 16 * R + 4 * m + rr;
+        const f32x4 x = (s0 >> 4) <= R ? tm[R][m] * bb : zero4();
+        put4v<DEV>(tb, r * kC + acc_pos(s0), x);
+      }
   }
   put1f<DEV>(wg + ci * (2 * kC), lane, lgs[lane]);
   put1f<DEV>(wg + ci * (2 * kC), kC + lane, gam[lane]);
