@@ -392,7 +392,9 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
   // B3 they commit chunk c+1's queries.
   if (scan_wave) {
     // state columns 32 wv .. + 31; tile mt's accumulator row 4 g + i holds
-    // d_k = 32 (mt / 2) + 8 g + 4 (mt % 2) + i (see tr_frag_k)
+    // d_k = 32 (mt / 2) + 8 g + 4 (mt % 2) + i (see tr_frag_k), and column j
+    // of tile nt is d_v = 32 wv + 8 (j / 4) + 4 nt + j % 4, so that a lane's
+    // two output tiles hold 8 adjacent columns of a row (one 16-byte store)
     const int cw = 32 * wv;
 
     f32x4 S[8][2];
@@ -409,7 +411,7 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
       // lane parts of the LDS addresses: row reads, V^T and K^T reads,
       // [64][64] tiles, hand-over rows
       int l_row = j * kSR + 8 * g, l_tv = (4 * g + (j >> 2)) * kSR + 4 * (j & 3);
-      int l_tk = (4 * g + (j >> 2)) * kSR + 8 * (j & 3), l_acc = j * kSC + 8 * g, l_x = j * kSR + 4 * g;
+      int l_tk = (4 * g + (j >> 2)) * kSR + 8 * (j & 3), l_acc = j * kSC + 8 * g, l_x = j * kSR + 8 * g;
       asm volatile("" : "+v"(l_row), "+v"(l_tv), "+v"(l_tk), "+v"(l_acc), "+v"(l_x));
       lds_barrier();                     // B0
       // ---- prefetch the queries of chunk c + 1, committed after B3.
@@ -472,7 +474,7 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) tf[mt] = lds_frag8(TBs + l_acc + 16 * mt * kSC + 32 * pp);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) vf[nt] = tr_at(Vc + cw + l_tv, 32 * pp * kSR + 16 * nt);
+        for (int nt = 0; nt < 2; ++nt) vf[nt] = tr_at(Vc + cw + l_tk, 32 * pp * kSR + 4 * nt);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -540,17 +542,19 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             ob + (size_t)(i0 + window) * qrow, 0, (int)min(left, 0x7fffffffLL), 0x00020000);
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
+        for (int rt = 0; rt < 4; ++rt) {
+          // lane: row 16 rt + j, columns cw + 8 g .. + 7 (tile 0 then tile 1)
+          const int r = 16 * rt + j;
+          const bf16x8 xs = *reinterpret_cast<const bf16x8*>(Xs + cw + l_x + 16 * rt * kSR);
+          bf16x8 y;
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            const int r = 16 * rt + j;
-            const int col = cw + 16 * nt + 4 * g;
-            const f32x4 x = ot[nt][rt] * w_lin + load4(Xs + cw + l_x + 16 * rt * kSR + 16 * nt);
-            const bf16x4 y = bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
-                                    static_cast<bf16>(x[3])};
-            typedef unsigned int u2 __attribute__((ext_vector_type(2)));
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, y), rs, (r * (int)qrow + col) * 2, 0, 0);
-          }
+          for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              y[4 * nt + i] = static_cast<bf16>(__builtin_fmaf(ot[nt][rt][i], w_lin, static_cast<float>(xs[4 * nt + i])));
+          typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, y), rs, (r * (int)qrow + cw + 8 * g) * 2, 0, 0);
+        }
       }
       lds_barrier();                     // B3: the softmax rows are read
       if (c + 1 < nch) {
@@ -566,7 +570,8 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            Sg[(size_t)(32 * (mt >> 1) + 8 * g + 4 * (mt & 1) + i) * kD + cw + 16 * nt + j] = S[mt][nt][i];
+            Sg[(size_t)(32 * (mt >> 1) + 8 * g + 4 * (mt & 1) + i) * kD + cw + 8 * (j >> 2) + 4 * nt + (j & 3)] =
+                S[mt][nt][i];
     }
     return;
   }
