@@ -311,7 +311,7 @@ CPU_SAMPLES = {
     "llama8b_t4096": dict(T_sample=4096, heads=range(32)),
     "qwen32b_t8192_gdn": dict(T_sample=4096, heads=range(32)),
     "qwen32b_t8192_gla": dict(T_sample=4096, heads=range(32)),
-    "dgd_b8_t8192": dict(T_sample=4096, heads=range(32)),
+    "dgd_b8_t8192": dict(T_sample=8192, heads=range(32)),
     "decode_b256": dict(steps=20),
 }
 
