@@ -139,16 +139,18 @@ def shortconv_decode_bytes(w, elt=2):
 # ------------------------------------------------------------- kernels
 
 # Kernels each call launches, by workload (the library's launch choice:
+# bf16 GDN at d = 128 with both branches, window <= 128 and at most 16
+# sinks runs the light preparation, then the one-pass layer: one launch
+# when the chains fill the GPU, and with at most 64 chains the segmented
+# scan (segment maps, carry, then the layer kernel per segment); "prepare"
+# and "layer2" are timed one by one through the two-phase flags.  Other
 # bf16 GDN with B*H*d/64 < 256 runs preparation, scan and, with both
-# branches, the softmax tiles as one launch; bf16 GDN at d = 128 with both
-# branches, window <= 128 and at most 16 sinks otherwise runs the light
-# preparation, then the one-pass layer ("prepare" and "layer2": two
-# launches, timed one by one through the two-phase flags); otherwise the
-# light preparation, then the many-chain scan, and the softmax kernel).
+# branches, the softmax tiles as one launch; otherwise the light
+# preparation, then the many-chain scan, and the softmax kernel).
+SEGMENTED = "gdn_segmap_kernel+gdn_carry_kernel+gdn_layer_kernel"
 CALL_KERNELS = {
     "longctx_b8_t32768": {"prepare": "gdn_prep_kernel", "layer2": "gdn_layer_kernel"},
-    "llama8b_t4096": {"layer": "gdn_scan_full_kernel", "linear": "gdn_scan_full_kernel",
-                      "softmax": "swa_kernel"},
+    "llama8b_t4096": {"prepare": "gdn_prep_kernel", "layer2": SEGMENTED},
     "tiny_fp32": {"linear": "gdn_prep_kernel+linear_chunk_kernel", "softmax": "swa_kernel"},
     "qwen32b_t8192_gdn": {"shortconv": "shortconv_kernel",
                           "linear": "gdn_prep_kernel+linear_chunk_kernel", "softmax": "swa_kernel"},
@@ -159,6 +161,7 @@ CALL_KERNELS = {
 CSRC = "swa_chunked_gated_amd/csrc/"
 KERNEL_SOURCES = {
     "gdn_layer_kernel": ("gdn_layer.hip", "common.h"),
+    SEGMENTED: ("gdn_layer.hip", "common.h"),
     "gdn_prep_kernel": ("gdn_prep.h", "gdn_prep.hip", "common.h"),
     "gdn_prep_kernel+linear_chunk_kernel": ("gdn_prep.h", "gdn_prep.hip", "gdn_scan_full.hip",
                                             "linear_chunk.hip", "common.h"),

@@ -135,6 +135,8 @@ size_t prefill_workspace_bytes(int B, int T, int H, int dk, int n_sink, int wind
   const int nch = gdn::gdn_stream_chunks(T, n_sink, window);
   if (nch == 0) return 0;
   const size_t elt = dtype == GDN_BF16 ? 2 : 4;
+  if (update == GDN_DELTA && gdn::gdn_segmented(B, T, H, dk, n_sink, window, elt == 2, 0, flags & 15))
+    return gdn::gdn_seg_layout(nullptr, B, H, nch).bytes;
   if (update != GDN_DELTA)
     return gdn::gla_workspace_layout(nullptr, B, H, nch, dk, elt, update == GDN_DELTA_DIAG).bytes;
   return gdn::gdn_workspace_layout(nullptr, B, H, nch, dk, elt, gdn::gdn_full_prep(B, H, dk, elt == 2)).bytes;

@@ -45,6 +45,8 @@
 // natural-order rows are read as two 8-byte pieces (K as an operand reduced
 // over d) or through the transposing reads (K^T, V^T, V).
 
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
     const bf16* q, const bf16* k, const bf16* v, const bf16* w_tb, const float* w_g,
     bf16* __restrict__ o,
     float* __restrict__ state_out, int B, int T_, int H, int Hkv, int n_sink, int window,
-    int nch, int write_state, float w_lin, float w_swa) {
+    int nch, int write_state, float w_lin, float w_swa, int seg_len, const float* s_in) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   bf16* sm = reinterpret_cast<bf16*>(smem_raw);
   bf16* KR = sm + oKR;
@@ -286,6 +288,11 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
   const int gk = unit % Hkv;
   const int h = gk * G + member;
   const size_t chain = (size_t)bi * H + h;
+  // segment y of the chain: chunks cb .. ce - 1, entered with the state
+  // s_in holds for it (segment 0, or no s_in: the zero state)
+  const int sg = blockIdx.y;
+  const int cb = sg * seg_len;
+  const int ce = min(nch, cb + seg_len);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -362,7 +369,8 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
   auto q_row0 = [&](int c) { return n_sink + c * kC + window; };
   auto kv_row0 = [&](int c) { return n_sink + c * kC; };
 
-  // initial fill: sinks, ring chunks 0..2, chunk 0's queries, TB and gates
+  // initial fill: sinks, ring chunks cb .. cb + 2, chunk cb's queries, TB
+  // and gates
   for (int n = tid; n < kSinkRows * 16; n += kThreads) {
     const int r = n >> 4;
     const bool in = r < n_sink && r < T_;
@@ -370,14 +378,15 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
     put_vrow(VSk, n, in ? *reinterpret_cast<const V16*>(vb + (size_t)r * kvrow + (n & 15) * 8) : zero8);
   }
   for (int n = tid; n < 3 * 1024; n += kThreads) {
-    const int sl = n >> 10;
-    put_row(KR + sl * kC * kSR, n & 1023, load_rows(kb, kvrow, kv_row0(sl), n & 1023));
-    put_vrow(VR + sl * kC * kSV, n & 1023, load_rows(vb, kvrow, kv_row0(sl), n & 1023));
+    const int cs = cb + (n >> 10);
+    const unsigned sl = (unsigned)cs % 3u;
+    put_row(KR + sl * kC * kSR, n & 1023, load_rows(kb, kvrow, kv_row0(cs), n & 1023));
+    put_vrow(VR + sl * kC * kSV, n & 1023, load_rows(vb, kvrow, kv_row0(cs), n & 1023));
   }
-  for (int n = tid; n < 1024; n += kThreads) put_q(n, load_rows(qb, qrow, q_row0(0), n));
+  for (int n = tid; n < 1024; n += kThreads) put_q(n, load_rows(qb, qrow, q_row0(cb), n));
   *reinterpret_cast<V16*>(TBs + (tid >> 3) * kSC + (tid & 7) * 8) =
-      *reinterpret_cast<const V16*>(tb_of(0) + (tid >> 3) * kC + (tid & 7) * 8);
-  if (tid < 64) put_gates(tid, *reinterpret_cast<const f32x4*>(g_of(0) + 4 * (tid & 31)));
+      *reinterpret_cast<const V16*>(tb_of(cb) + (tid >> 3) * kC + (tid & 7) * 8);
+  if (tid < 64) put_gates(tid, *reinterpret_cast<const f32x4*>(g_of(cb) + 4 * (tid & 31)));
   __syncthreads();
 
   // ---------------------------------------------------------- chunks
@@ -398,12 +407,23 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
     const int cw = 32 * wv;
 
     f32x4 S[8][2];
+    if (s_in && sg > 0) {
+      const float* Si = s_in + ((size_t)sg * B * H + chain) * kD * kD;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+      for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) S[mt][nt] = zero4();
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            S[mt][nt][i] = Si[(32 * (mt >> 1) + 8 * g + 4 * (mt & 1) + i) * kD + cw + 8 * (j >> 2) + 4 * nt + (j & 3)];
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) S[mt][nt] = zero4();
+    }
     V16 pq[4];
-    for (int c = 0; c < nch; ++c) {
+    for (int c = cb; c < ce; ++c) {
       const int i0 = n_sink + c * kC;
       const bf16* Kc = KR + ((unsigned)c % 3u) * kC * kSR;
       const bf16* Vc = VR + ((unsigned)c % 3u) * kC * kSV;
@@ -418,7 +438,7 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
       // Always issued (past the last chunk they reread valid rows and are
       // not committed), so that the memory counters the compiler waits on
       // are exact.
-      load_tile4(qb, qrow, q_row0(min(c + 1, nch - 1)), tid, pq);
+      load_tile4(qb, qrow, q_row0(min(c + 1, ce - 1)), tid, pq);
       asm volatile("" ::: "memory");     // issue them here, ahead of the products
       // ---- O^T = S^T Q^T [dv tile nt][query tile rt] and KS = K S [token
       // tile mt][dv tile nt], one d-step at a time (the state's operand
@@ -557,7 +577,7 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
         }
       }
       lds_barrier();                     // B3: the softmax rows are read
-      if (c + 1 < nch) {
+      if (c + 1 < ce) {
 #pragma unroll
         for (int m2 = 0; m2 < 4; ++m2) put_q(tid + 256 * m2, pq[m2]);
       }
@@ -579,10 +599,11 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
   // ---------------------------------------------------------- softmax waves
   const int jq = wv - 4;              // rows 16 jq .. + 15 of each chunk
   const int ptid = tid - 256;         // prefetch pieces n = ptid + 256 m
-  // prologue: rows t < n_sink + window carry no linear branch and attend to
-  // every key t' <= t: the sinks and ring chunks 0 and 1 hold them all
+  // prologue (first segment): rows t < n_sink + window carry no linear
+  // branch and attend to every key t' <= t: the sinks and ring chunks 0 and
+  // 1 hold them all
   {
-    const int nrow = min(n_sink + window, T_);
+    const int nrow = sg == 0 ? min(n_sink + window, T_) : 0;
     for (int t0 = 16 * jq; t0 < nrow; t0 += 64) {
       Frag<bf16> qf[4];
       const int tq = t0 + j;
@@ -644,7 +665,7 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
 
   V16 pk[4], pv[4], pt[2];
   f32x4 pg;
-  for (int c = 0; c < nch; ++c) {
+  for (int c = cb; c < ce; ++c) {
     const int i0 = n_sink + c * kC;
     const bf16* Kc = KR + ((unsigned)c % 3u) * kC * kSR;
     const bf16* Vc = VR + ((unsigned)c % 3u) * kC * kSV;
@@ -662,7 +683,7 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
     // ---- prefetch TB and the gates of chunk c + 1, committed after B2
     // (always issued, as the other prefetches)
     {
-      const int cn = min(c + 1, nch - 1);
+      const int cn = min(c + 1, ce - 1);
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const int n = ptid + 256 * m;
@@ -843,7 +864,7 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
       put_row(KR + ((unsigned)c % 3u) * kC * kSR, ptid + 256 * m2, pk[m2]);
       put_vrow(VR + ((unsigned)c % 3u) * kC * kSV, ptid + 256 * m2, pv[m2]);
     }
-    if (c + 1 < nch) {
+    if (c + 1 < ce) {
 #pragma unroll
       for (int m2 = 0; m2 < 2; ++m2) {
         const int n = ptid + 256 * m2;
@@ -853,6 +874,334 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
     }
     lds_barrier();                       // B3: the softmax rows are read
   }
+}
+
+// ---------------------------------------------------------------------------
+// Segmented scan for few chains.  When the chains cannot fill the GPU, each
+// chain's stream chunks are cut into P segments of L chunks.  Over a segment
+// the state update is affine in the incoming state, S_end = M S_start + N
+// (the recurrence is linear in S with the gates, keys and values fixed): N is
+// the state the segment's chunks produce from S_start = 0, and M what they
+// make of S_start = I with the values set to zero (column k of M is the
+// image of the unit state e_k).  After the chunk preparation three launches
+// run: the maps of all segments at once (gdn_segmap_kernel), the carry
+// S_{s+1} = M_s S_s + N_s from S_0 = 0 (gdn_carry_kernel), and the layer
+// kernel on every segment at once from its incoming state S_s.
+
+// LDS of the map kernel: two slots of K [64][kSR], V [64][kSV] (natural
+// order), TB [64][kSC] (acc order), then the fp32 gate blocks of the slots.
+constexpr int mK = 0;
+constexpr int mV = mK + kC * kSR;
+constexpr int mTB = mV + kC * kSV;
+constexpr int mSlot = mTB + kC * kSC;
+constexpr int kMapBytes = 2 * mSlot * 2 + 2 * 4 * kC * 4;
+static_assert(kMapBytes <= 160 * 1024, "one workgroup per compute unit");
+
+// The gate block (g, gamma, -gamma, 2^(g_C - g)) of one chunk from the 32
+// f32x4 pieces of (g, gamma): lane l < 32 holds piece l.  Called by a whole
+// wave (lanes 32.. take part in the shuffle only).
+__device__ __forceinline__ void put_gate_block(float* gs, int l, const f32x4& x) {
+  const float gC = __shfl(x[3], 15, 64);
+  if (l >= 32) return;
+  *reinterpret_cast<f32x4*>(gs + 4 * l) = x;
+  if (l < 16) {
+    f32x4 f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __builtin_amdgcn_exp2f(fminf(gC - x[i], 0.f));
+    *reinterpret_cast<f32x4*>(gs + 3 * kC + 4 * l) = f;
+  } else {
+    *reinterpret_cast<f32x4*>(gs + kC + 4 * l) = -x;
+  }
+}
+
+// Maps of segment y of each chain.  Waves 0-3 run the recurrence from the
+// zero state on the values (32 columns of N each), waves 4-7 from the
+// identity without values (32 columns of M each); the products are those of
+// the layer kernel's state waves (KS = K S, U = TB V - TB diag(gamma) KS,
+// S <- gamma_C S + K^T diag(gamma_C / gamma) U) with the same register
+// layouts.  One barrier per chunk: chunk c + 1 is fetched into registers
+// while chunk c is computed and written into the other slot after it.
+// Out: N fp32 and M bf16, [d_k][column] row-major, per (segment, chain).
+__global__ __launch_bounds__(kThreads) void gdn_segmap_kernel(
+    const bf16* k, const bf16* v, const bf16* w_tb, const float* w_g, bf16* __restrict__ seg_m,
+    float* __restrict__ seg_n, int B, int T_, int H, int Hkv, int n_sink, int nch, int seg_len) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  bf16* sm = reinterpret_cast<bf16*>(smem_raw);
+  float* Gb = reinterpret_cast<float*>(smem_raw + 2 * mSlot * 2);
+  const int G = H / Hkv;
+  int unit, member;
+  if (!xcd_grouped(blockIdx.x, G, B * Hkv, unit, member)) return;
+  const int bi = unit / Hkv;
+  const int gk = unit % Hkv;
+  const int h = gk * G + member;
+  const size_t chain = (size_t)bi * H + h;
+  const int sg = blockIdx.y;
+  const int cb = sg * seg_len;
+  const int ce = min(nch, cb + seg_len);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = wave_id();
+  const int g = lane >> 4;
+  const int j = lane & 15;
+  const bool mw = wv >= 4;              // the map M: identity start, no values
+  const int cw = 32 * (wv & 3);
+  typedef bf16x8 V16;
+  const size_t kvrow = (size_t)Hkv * kD;
+  const bf16* kb = k + ((size_t)bi * T_ * Hkv + gk) * kD;
+  const bf16* vb = v + ((size_t)bi * T_ * Hkv + gk) * kD;
+
+  // staging of one chunk: K and V pieces tid and tid + 512 (16-byte piece n:
+  // row n / 16, columns 8 (n % 16) ..; rows past the sequence repeat its
+  // last row and meet zero rows and columns of TB), TB piece tid, and the
+  // gate pieces (wave 0)
+  V16 pk[2], pv[2], pt;
+  f32x4 pg = zero4();
+  auto fetch = [&](int c) {
+    const int row0 = n_sink + c * kC;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int n = tid + 512 * m;
+      const size_t r = (size_t)min(row0 + (n >> 4), T_ - 1);
+      pk[m] = *reinterpret_cast<const V16*>(kb + r * kvrow + (n & 15) * 8);
+      pv[m] = *reinterpret_cast<const V16*>(vb + r * kvrow + (n & 15) * 8);
+    }
+    const size_t ci = chain * nch + c;
+    pt = *reinterpret_cast<const V16*>(w_tb + ci * (kC * kC) + (tid >> 3) * kC + (tid & 7) * 8);
+    if (wv == 0) pg = *reinterpret_cast<const f32x4*>(w_g + ci * (2 * kC) + 4 * (lane & 31));
+  };
+  auto commit = [&](int sl) {
+    bf16* base = sm + sl * mSlot;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int n = tid + 512 * m;
+      *reinterpret_cast<V16*>(base + mK + (n >> 4) * kSR + (n & 15) * 8) = pk[m];
+      *reinterpret_cast<V16*>(base + mV + (n >> 4) * kSV + (n & 15) * 8) = pv[m];
+    }
+    *reinterpret_cast<V16*>(base + mTB + (tid >> 3) * kSC + (tid & 7) * 8) = pt;
+    if (wv == 0) put_gate_block(Gb + sl * 4 * kC, lane, pg);
+  };
+
+  // state tile mt's accumulator row 4 g + i is d_k = 32 (mt / 2) + 8 g +
+  // 4 (mt % 2) + i; column j of tile nt is 32 (wv % 4) + 8 (j / 4) + 4 nt + j % 4
+  auto row_of = [&](int mt, int i) { return 32 * (mt >> 1) + 8 * g + 4 * (mt & 1) + i; };
+  auto col_of = [&](int nt) { return cw + 8 * (j >> 2) + 4 * nt + (j & 3); };
+  f32x4 S[8][2];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[mt][nt][i] = mw && row_of(mt, i) == col_of(nt) ? 1.f : 0.f;
+
+  fetch(cb);
+  commit(0);
+  for (int c = cb; c < ce; ++c) {
+    const int sl = (c - cb) & 1;
+    const bf16* Kc = sm + sl * mSlot + mK;
+    const bf16* Vc = sm + sl * mSlot + mV;
+    const bf16* TBc = sm + sl * mSlot + mTB;
+    const float* Gc = Gb + sl * 4 * kC;
+    int l_row = j * kSR + 8 * g, l_tk = (4 * g + (j >> 2)) * kSR + 8 * (j & 3), l_acc = j * kSC + 8 * g;
+    asm volatile("" : "+v"(l_row), "+v"(l_tk), "+v"(l_acc));
+    lds_barrier();                       // chunk c is in slot sl; slot sl ^ 1 is free
+    if (c + 1 < ce) fetch(c + 1);
+    asm volatile("" ::: "memory");       // issue the loads here, ahead of the products
+    // ---- KS = K S [token tile mt][column tile nt]
+    f32x4 KS[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) KS[mt][nt] = zero4();
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      Frag<bf16> sf[2], kf[4];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) sf[nt] = frag_from_acc<bf16>(S[2 * p][nt], S[2 * p + 1][nt]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) kf[mt] = lds_frag8(Kc + l_row + 16 * mt * kSR + 32 * p);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) KS[mt][nt] = mfma(kf[mt], sf[nt], KS[mt][nt]);
+    }
+    // ---- U = TB V - TB diag(gamma) KS (the map waves: no values)
+    Frag<bf16> ksf[2][2];
+    {
+      const float* ngam = Gc + 2 * kC;
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const f32x4 n0 = *reinterpret_cast<const f32x4*>(ngam + 32 * pp + 4 * g);
+        const f32x4 n1 = *reinterpret_cast<const f32x4*>(ngam + 32 * pp + 16 + 4 * g);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          ksf[pp][nt] = frag_from_acc_scaled<bf16>(KS[2 * pp][nt], KS[2 * pp + 1][nt], n0, n1);
+      }
+    }
+    f32x4 U[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) U[mt][nt] = zero4();
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      Frag<bf16> tf[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) tf[mt] = lds_frag8(TBc + l_acc + 16 * mt * kSC + 32 * pp);
+      if (!mw) {
+        Frag<bf16> vf[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) vf[nt] = tr_at(Vc + cw + l_tk, 32 * pp * kSR + 4 * nt);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) U[mt][nt] = mfma(tf[mt], vf[nt], U[mt][nt]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) U[mt][nt] = mfma(tf[mt], ksf[pp][nt], U[mt][nt]);
+    }
+    // ---- S = gamma_C S + K^T diag(gamma_C / gamma) U
+    const float gC = Gc[2 * kC - 1];
+    const float* dec = Gc + 3 * kC;
+    Frag<bf16> us[2][2];
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      const f32x4 s0 = *reinterpret_cast<const f32x4*>(dec + 32 * pp + 4 * g);
+      const f32x4 s1 = *reinterpret_cast<const f32x4*>(dec + 32 * pp + 16 + 4 * g);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) us[pp][nt] = frag_from_acc_scaled<bf16>(U[2 * pp][nt], U[2 * pp + 1][nt], s0, s1);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) S[mt][nt] *= gC;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      Frag<bf16> kt[2];
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) kt[pp] = tr_at(Kc + l_tk, 32 * pp * kSR + 32 * (mt >> 1) + 4 * (mt & 1));
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) S[mt][nt] = mfma(kt[pp], us[pp][nt], S[mt][nt]);
+    }
+    if (c + 1 < ce) commit(sl ^ 1);
+  }
+
+  const size_t off = ((size_t)sg * B * H + chain) * kD * kD;
+  if (mw) {
+    // segment 0 starts from the zero state: its M is never used
+    if (sg == 0) return;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) seg_m[off + row_of(mt, i) * kD + col_of(nt)] = static_cast<bf16>(S[mt][nt][i]);
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) seg_n[off + row_of(mt, i) * kD + col_of(nt)] = S[mt][nt][i];
+  }
+}
+
+// The carry over the segments of one chain, for 32 state columns c0 .. c0 +
+// 31 (the columns of S are independent): S_1 = N_0, S_{s+1} = M_s S_s + N_s.
+// Writes S_1 .. S_{P-1} (the incoming states of segments 1 .. P-1) and, with
+// write_state, S_P (the final state).  Wave w computes rows 32 w .. + 31;
+// the state passes between steps through LDS as bf16 S^T [column][d_k]; the
+// maps' operands of the next step are loaded while a step runs.
+constexpr int kCarryST = kD + 8;    // row stride of S^T in LDS
+__global__ __launch_bounds__(256) void gdn_carry_kernel(const bf16* __restrict__ seg_m,
+                                                        const float* __restrict__ seg_n,
+                                                        float* __restrict__ seg_s,
+                                                        float* __restrict__ state_out, int C,
+                                                        int P, int write_state) {
+  __shared__ __attribute__((aligned(16))) bf16 ST[32 * kCarryST];
+  const int chain = blockIdx.x >> 2;
+  const int c0 = 32 * (blockIdx.x & 3);
+  const int lane = threadIdx.x & 63;
+  const int wv = wave_id();
+  const int g = lane >> 4;
+  const int j = lane & 15;
+  // accumulator tile (t, u): rows 32 wv + 16 t + 4 g + i, column c0 + 16 u + j
+  auto at = [&](int t, int u, int i) { return (32 * wv + 16 * t + 4 * g + i) * kD + c0 + 16 * u + j; };
+  auto mat = [&](int s) { return ((size_t)s * C + chain) * kD * kD; };
+  f32x4 acc[2][2];
+  const float* N0 = seg_n + mat(0);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[t][u][i] = N0[at(t, u, i)];
+  const int last = write_state ? P : P - 1;   // the last state needed
+  // operands of step s (S_{s+1} = M_s S_s + N_s): A fragments of M_s rows
+  // 32 wv + 16 t + j, d_k 32 p + 8 g .. + 7, and N_s
+  Frag<bf16> ma[2][4];
+  f32x4 na[2][2];
+  auto load_step = [&](int s) {
+    const bf16* M = seg_m + mat(s);
+    const float* N = seg_n + mat(s);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        ma[t][p].v = *reinterpret_cast<const bf16x8*>(M + (32 * wv + 16 * t + j) * kD + 32 * p + 8 * g);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) na[t][u][i] = N[at(t, u, i)];
+  };
+  if (last >= 2) load_step(1);
+  for (int s = 1; s < last; ++s) {
+    // acc holds S_s: out to the segment's incoming state, and as bf16 S^T
+    float* So = seg_s + mat(s);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) So[at(t, u, i)] = acc[t][u][i];
+        bf16x4 x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = static_cast<bf16>(acc[t][u][i]);
+        *reinterpret_cast<bf16x4*>(ST + (16 * u + j) * kCarryST + 32 * wv + 16 * t + 4 * g) = x;
+      }
+    lds_barrier();
+    Frag<bf16> sb[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) sb[u][p] = lds_frag8(ST + (16 * u + j) * kCarryST + 32 * p + 8 * g);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) acc[t][u] = na[t][u];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) acc[t][u] = mfma(ma[t][p], sb[u][p], acc[t][u]);
+    if (s + 1 < last) load_step(s + 1);
+    lds_barrier();                       // S^T is read before the next step overwrites it
+  }
+  // acc holds S_last: the final state, or the last segment's incoming state
+  float* So = last == P ? state_out + (size_t)chain * kD * kD : seg_s + mat(last);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) So[at(t, u, i)] = acc[t][u][i];
 }
 
 }  // namespace
@@ -874,7 +1223,77 @@ hipError_t launch_gdn_layer(const PrefillArgs& p, hipStream_t s) {
   hipLaunchKernelGGL(gdn_layer_kernel, grid, dim3(kThreads), kLdsBytes, s, (const bf16*)p.q,
                      (const bf16*)p.k, (const bf16*)p.v, (const bf16*)w.tb, w.g, (bf16*)p.o,
                      p.state_out, p.B, p.T, p.H, p.Hkv, p.n_sink, p.window, nch,
-                     (p.flags & 4) ? 1 : 0, p.w_lin, p.w_swa);
+                     (p.flags & 4) ? 1 : 0, p.w_lin, p.w_swa, nch, (const float*)nullptr);
+  return hipGetLastError();
+}
+
+SegPlan gdn_seg_plan(int B, int H, int nch) {
+  const long long C = (long long)B * H;
+  // one workgroup per compute unit in the map and layer launches
+  const long long want = C > 0 ? 256 / C : 0;
+  SegPlan pl{1, nch};
+  if (want < 4 || nch < 4) return pl;
+  pl.P = (int)std::min<long long>(want, nch);
+  pl.L = (nch + pl.P - 1) / pl.P;
+  pl.P = (nch + pl.L - 1) / pl.L;
+  return pl;
+}
+
+bool gdn_segmented(int B, int T, int H, int D, int n_sink, int window, int bf16, int gla, int flags) {
+  const int nch = gdn_stream_chunks(T, n_sink, window);
+  return bf16 && !gla && D == kD && (flags & 3) == 3 && !(flags & 8) && window <= 128 &&
+         n_sink <= kSinkRows && gdn_seg_plan(B, H, nch).P >= 4;
+}
+bool gdn_segmented(const PrefillArgs& p) {
+  return gdn_segmented(p.B, p.T, p.H, p.D, p.n_sink, p.window, p.bf16, p.gla, p.flags);
+}
+
+SegWorkspace gdn_seg_layout(void* base, int B, int H, int nch) {
+  const GdnWorkspace w = gdn_workspace_layout(base, B, H, nch, kD, sizeof(bf16), false);
+  const SegPlan pl = gdn_seg_plan(B, H, nch);
+  const size_t mats = (size_t)pl.P * B * H * kD * kD;
+  const size_t al = 256;
+  size_t off = (w.bytes + al - 1) / al * al;
+  SegWorkspace s;
+  s.light = w;
+  unsigned char* b = static_cast<unsigned char*>(base);
+  s.m = b + off;
+  off += (mats * 2 + al - 1) / al * al;
+  s.n = reinterpret_cast<float*>(b + off);
+  off += mats * 4;
+  s.s = reinterpret_cast<float*>(b + off);
+  off += mats * 4;
+  s.bytes = off;
+  return s;
+}
+
+hipError_t launch_gdn_segmented(const PrefillArgs& p, hipStream_t s) {
+  const int nch = gdn_stream_chunks(p.T, p.n_sink, p.window);
+  const SegPlan pl = gdn_seg_plan(p.B, p.H, nch);
+  const int C = p.B * p.H;
+  const bool wst = (p.flags & 4) != 0;
+  const int need = wst ? pl.P : pl.P - 1;      // segments whose maps the carry uses
+  hipError_t e = p.prepared ? hipSuccess : launch_gdn_prep(p, nch, s);
+  if (e != hipSuccess) return e;
+  const SegWorkspace w = gdn_seg_layout(p.workspace, p.B, p.H, nch);
+  const unsigned gx = xcd_grouped_grid((long long)p.B * p.Hkv, p.H / p.Hkv);
+  e = hipFuncSetAttribute((const void*)gdn_segmap_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMapBytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gdn_segmap_kernel, dim3(gx, need), dim3(kThreads), kMapBytes, s, (const bf16*)p.k,
+                     (const bf16*)p.v, (const bf16*)w.light.tb, w.light.g, (bf16*)w.m, w.n, p.B, p.T, p.H,
+                     p.Hkv, p.n_sink, nch, pl.L);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gdn_carry_kernel, dim3(4 * C), dim3(256), 0, s, (const bf16*)w.m,
+                     (const float*)w.n, w.s, p.state_out, C, pl.P, wst ? 1 : 0);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)gdn_layer_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gdn_layer_kernel, dim3(gx, pl.P), dim3(kThreads), kLdsBytes, s, (const bf16*)p.q,
+                     (const bf16*)p.k, (const bf16*)p.v, (const bf16*)w.light.tb, w.light.g, (bf16*)p.o,
+                     p.state_out, p.B, p.T, p.H, p.Hkv, p.n_sink, p.window, nch, 0, p.w_lin, p.w_swa,
+                     pl.L, (const float*)w.s);
   return hipGetLastError();
 }
 

@@ -53,7 +53,7 @@ hipError_t launch_prep_d(const PrefillArgs& p, int nch, hipStream_t s) {
     return hipErrorInvalidValue;   // fp32 linear branch runs at d = 64 only
   } else {
     if constexpr (sizeof(T) == 2) {
-      if (gdn_full_prep(p.B, p.H, p.D, 1)) return launch_prep_t<T, D, true>(p, nch, s);
+      if (gdn_full_prep(p.B, p.H, p.D, 1) && !gdn_segmented(p)) return launch_prep_t<T, D, true>(p, nch, s);
     }
     return launch_prep_t<T, D, false>(p, nch, s);
   }

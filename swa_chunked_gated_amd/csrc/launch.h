@@ -147,6 +147,28 @@ bool separate_preparation(const PrefillArgs& p);
 hipError_t launch_preparation(const PrefillArgs& p, hipStream_t s);
 bool gdn_layer_applies(const PrefillArgs& p);
 hipError_t launch_gdn_layer(const PrefillArgs& p, hipStream_t s);
+// Segmented scan (bf16 GDN at d = 128, both branches, no accumulation,
+// window <= 128, n_sink <= 16, too few chains to fill the GPU): each chain's
+// P segments of L chunks each; P = 1 when the chains fill the GPU.
+struct SegPlan {
+  int P, L;
+};
+SegPlan gdn_seg_plan(int B, int H, int nch);
+bool gdn_segmented(int B, int T, int H, int D, int n_sink, int window, int bf16, int gla, int flags);
+bool gdn_segmented(const PrefillArgs& p);
+// Its workspace: the light preparation's, then per (segment, chain) the
+// map M (bf16), the state N (fp32) and the incoming state S (fp32), each
+// [128][128] row-major.
+struct SegWorkspace {
+  GdnWorkspace light;
+  void* m;
+  float* n;
+  float* s;
+  size_t bytes;
+};
+SegWorkspace gdn_seg_layout(void* base, int B, int H, int nch);
+// Preparation (unless prepared), maps, carry, and the layer kernel per segment.
+hipError_t launch_gdn_segmented(const PrefillArgs& p, hipStream_t s);
 // Chunk preparation of the gated delta rule / of GLA into a.workspace (nch chunks).
 hipError_t launch_gdn_prep(const PrefillArgs& a, int nch, hipStream_t s);
 hipError_t launch_gla_prep(const PrefillArgs& a, int nch, hipStream_t s);

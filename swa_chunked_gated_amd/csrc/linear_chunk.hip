@@ -688,7 +688,8 @@ hipError_t launch_linear_m(const PrefillArgs& p, hipStream_t s) {
 }  // namespace
 
 bool separate_preparation(const PrefillArgs& p) {
-  return gdn_stream_chunks(p.T, p.n_sink, p.window) > 0 && (p.gla || !gdn_full_prep(p.B, p.H, p.D, p.bf16));
+  return gdn_stream_chunks(p.T, p.n_sink, p.window) > 0 &&
+         (p.gla || !gdn_full_prep(p.B, p.H, p.D, p.bf16) || gdn_segmented(p));
 }
 
 hipError_t launch_preparation(const PrefillArgs& p, hipStream_t s) {
@@ -699,6 +700,10 @@ hipError_t launch_preparation(const PrefillArgs& p, hipStream_t s) {
 hipError_t launch_linear_prefill(const PrefillArgs& p, hipStream_t s, bool* swa_done) {
   if (swa_done) *swa_done = false;
   const int nch = gdn_stream_chunks(p.T, p.n_sink, p.window);
+  if (gdn_segmented(p)) {
+    if (swa_done) *swa_done = true;
+    return launch_gdn_segmented(p, s);
+  }
   if (!p.gla && gdn_full_prep(p.B, p.H, p.D, p.bf16)) return launch_gdn_full(p, nch, s, swa_done);
   if (gdn_layer_applies(p)) {
     if (swa_done) *swa_done = true;

@@ -76,7 +76,15 @@ def test_workspace_query(lib):
         else:       # TB; gates
             per = 64 * 64 * elt + 512
         return B * H * nch * per
-    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 3) == (OK, gdn_bytes(1, 4096, 32, 128, 2))
+    # few chains, bf16 d = 128, both branches, window <= 128, <= 16 sinks:
+    # the segmented scan's light preparation (TB, gates), then per (segment,
+    # chain) M bf16, N and the incoming state fp32, [128][128] each; 32
+    # chains over 63 chunks: 8 segments
+    light = 2016 * (64 * 64 * 2 + 512)
+    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 3) == (OK, light + 8 * 32 * 128 * 128 * (2 + 4 + 4))
+    # the same shape, linear branch and state only: the one-launch path's
+    # full preparation
+    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 5) == (OK, gdn_bytes(1, 4096, 32, 128, 2))
     assert gdn_bytes(1, 4096, 32, 128, 2) == 2016 * 74312
     assert ws(lib, 2, 300, 4, 2, 64, 64, 8, 56, F32, DELTA, 5) == (OK, gdn_bytes(2, 300, 4, 64, 4))
     assert ws(lib, 8, 4096, 32, 8, 128, 128, 8, 120, BF16, DELTA, 5) == (OK, gdn_bytes(8, 4096, 32, 128, 2, 128))

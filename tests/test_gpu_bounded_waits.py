@@ -31,8 +31,9 @@ def close(got, ref, what):
 
 @pytest.mark.parametrize("faults", [1, 2])
 def test_wait_give_up_poisons_dependent_rows(faults):
-    # few chains, four query heads per KV head, both branches: one launch
-    w = Workload("waits", B=1, H=8, Hkv=2, d=128, n_sink=8, window=56, T=520, sigma=0.5)
+    # few chains, four query heads per KV head, both branches, a window
+    # longer than 128 (no segmented scan): one launch
+    w = Workload("waits", B=1, H=8, Hkv=2, d=128, n_sink=8, window=130, T=600, sigma=0.5)
     inp = {x: t.to(DEV) for x, t in make_prefill_inputs(w, seed=3).items()}
     args = (inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], w.n_sink, w.window)
     ref, S = O.hybrid_prefill(*(f64(inp[x]) for x in ("q", "k", "v", "a", "b")), w.n_sink, w.window)

@@ -15,7 +15,9 @@ The prefill probes are placed on the shapes that reach each kernel path:
     with few sequences), bf16 and fp32 key blocks;
   * swa_ring_kernel (resident key blocks: bf16, four query heads per KV head,
     at least four 64-row tiles per workgroup, many sequences);
-  * the softmax tiles linked into the one-launch few-chain layer kernel
+  * the softmax tiles linked into the one-launch few-chain layer kernel,
+    and the softmax waves of the one-pass layer kernel run per segment by
+    the segmented scan
     (bf16, few chains, both branches, G a multiple of 4);
 and the decode probe crosses the sink boundary, the full budget and several
 wraps of the ring.
@@ -112,12 +114,15 @@ def test_mask_probe_swa_kernel(G, dtype, d, n_sink, window):
 
 @pytest.mark.parametrize("B,H,Hkv,T,n_sink,window", [(1, 32, 8, 4096, 8, 56), (1, 8, 2, 1000, 8, 56),
                                                      (2, 8, 2, 700, 0, 64), (1, 16, 4, 900, 8, 120),
-                                                     (1, 4, 1, 650, 3, 130), (1, 8, 1, 333, 8, 1)])
+                                                     (1, 8, 1, 333, 8, 1), (1, 4, 1, 650, 3, 130),
+                                                     (1, 8, 2, 1000, 20, 56), (2, 8, 2, 700, 17, 200)])
 def test_mask_probe_linked_tiles(B, H, Hkv, T, n_sink, window):
-    """Both branches on a few-chain bf16 shape with G a multiple of 4: the
-    softmax tiles run inside the one-launch layer kernel and add onto the
-    scan's rows.  q = 0 makes the linear branch exactly 0, so o is the
-    softmax branch alone."""
+    """Both branches on a few-chain bf16 shape with G a multiple of 4.  With
+    window <= 128 and n_sink <= 16 (the first five cases) the segmented scan
+    runs the one-pass layer kernel per segment, whose softmax waves form the
+    rows; with a longer window or more sinks the softmax tiles run inside the
+    one-launch layer kernel and add onto the scan's rows.  q = 0 makes the
+    linear branch exactly 0, so o is the softmax branch alone."""
     q, k, v, a, b = probe_inputs(B, T, H, Hkv, 128, torch.bfloat16, seed=T, gates=True)
     o, st = gl.hybrid_prefill(q, k, v, a, b, n_sink, window, flags=ALL | gl.WRITE_STATE)
     torch.cuda.synchronize()

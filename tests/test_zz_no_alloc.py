@@ -34,8 +34,10 @@ def _equal(ref, got, flags):
         assert torch.equal(ref[1], got[1]), "state differs from the regular entry point"
 
 
-# (first call, second smaller call): few-chain one-launch path (flags and
-# hand-off epochs in the array), many-chain light preparation, GLA, fp32
+# (first call, second smaller call): few chains (both branches: the
+# segmented scan's maps and states in the array; linear only: the one-launch
+# path, flags and hand-off epochs in the array), many-chain light
+# preparation, GLA, fp32
 CASES = [
     (dict(B=1, H=32, Hkv=8, d=128, T=2000), dict(B=1, H=8, Hkv=2, d=128, T=700)),
     (dict(B=8, H=32, Hkv=8, d=128, T=900), dict(B=4, H=32, Hkv=8, d=128, T=333)),
