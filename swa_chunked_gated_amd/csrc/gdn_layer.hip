@@ -142,6 +142,14 @@ __device__ __forceinline__ Frag<bf16> tr_at(const bf16* Xl, int off) {
   return f;
 }
 
+// The segment states N and S_s in the workspace are fp32 [128][128] in the
+// carry's accumulator order: 16 x 16 tiles (row tile, column tile), and in a
+// tile lane 16 (r % 16 / 4) + c % 16 holds its 4 rows r % 4 = 0..3, so that
+// the carry moves a tile with one 16-byte access per lane.
+__device__ __forceinline__ int tile_off(int r, int c) {
+  return ((r >> 4) * 8 + (c >> 4)) * 256 + (16 * ((r & 15) >> 2) + (c & 15)) * 4 + (r & 3);
+}
+
 // Sum over lanes l, l^16, l^32, l^48 (the four lane groups of one column).
 __device__ __forceinline__ float sum_lane_groups(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -371,22 +379,45 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
 
   // initial fill: sinks, ring chunks cb .. cb + 2, chunk cb's queries, TB
   // and gates
-  for (int n = tid; n < kSinkRows * 16; n += kThreads) {
-    const int r = n >> 4;
-    const bool in = r < n_sink && r < T_;
-    put_row(KSk, n, in ? *reinterpret_cast<const V16*>(kb + (size_t)r * kvrow + (n & 15) * 8) : zero8);
-    put_vrow(VSk, n, in ? *reinterpret_cast<const V16*>(vb + (size_t)r * kvrow + (n & 15) * 8) : zero8);
+  // (every load is issued before the first LDS store, so that their
+  // latencies overlap)
+  {
+    static_assert(kSinkRows * 16 <= kThreads, "one sink piece per thread");
+    V16 fk[6], fv[6], fq[2], fsk = zero8, fsv = zero8, ftb;
+    f32x4 fg = zero4();
+    const int rs = tid >> 4;
+    const bool sin = tid < kSinkRows * 16 && rs < n_sink && rs < T_;
+    if (sin) {
+      fsk = *reinterpret_cast<const V16*>(kb + (size_t)rs * kvrow + (tid & 15) * 8);
+      fsv = *reinterpret_cast<const V16*>(vb + (size_t)rs * kvrow + (tid & 15) * 8);
+    }
+#pragma unroll
+    for (int m = 0; m < 6; ++m) {
+      const int n = tid + kThreads * m;
+      fk[m] = load_rows(kb, kvrow, kv_row0(cb + (n >> 10)), n & 1023);
+      fv[m] = load_rows(vb, kvrow, kv_row0(cb + (n >> 10)), n & 1023);
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) fq[m] = load_rows(qb, qrow, q_row0(cb), tid + kThreads * m);
+    ftb = *reinterpret_cast<const V16*>(tb_of(cb) + (tid >> 3) * kC + (tid & 7) * 8);
+    if (tid < 64) fg = *reinterpret_cast<const f32x4*>(g_of(cb) + 4 * (tid & 31));
+    asm volatile("" ::: "memory");
+    if (tid < kSinkRows * 16) {
+      put_row(KSk, tid, fsk);
+      put_vrow(VSk, tid, fsv);
+    }
+#pragma unroll
+    for (int m = 0; m < 6; ++m) {
+      const int n = tid + kThreads * m;
+      const unsigned sl = (unsigned)(cb + (n >> 10)) % 3u;
+      put_row(KR + sl * kC * kSR, n & 1023, fk[m]);
+      put_vrow(VR + sl * kC * kSV, n & 1023, fv[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) put_q(tid + kThreads * m, fq[m]);
+    *reinterpret_cast<V16*>(TBs + (tid >> 3) * kSC + (tid & 7) * 8) = ftb;
+    if (tid < 64) put_gates(tid, fg);
   }
-  for (int n = tid; n < 3 * 1024; n += kThreads) {
-    const int cs = cb + (n >> 10);
-    const unsigned sl = (unsigned)cs % 3u;
-    put_row(KR + sl * kC * kSR, n & 1023, load_rows(kb, kvrow, kv_row0(cs), n & 1023));
-    put_vrow(VR + sl * kC * kSV, n & 1023, load_rows(vb, kvrow, kv_row0(cs), n & 1023));
-  }
-  for (int n = tid; n < 1024; n += kThreads) put_q(n, load_rows(qb, qrow, q_row0(cb), n));
-  *reinterpret_cast<V16*>(TBs + (tid >> 3) * kSC + (tid & 7) * 8) =
-      *reinterpret_cast<const V16*>(tb_of(cb) + (tid >> 3) * kC + (tid & 7) * 8);
-  if (tid < 64) put_gates(tid, *reinterpret_cast<const f32x4*>(g_of(cb) + 4 * (tid & 31)));
   __syncthreads();
 
   // ---------------------------------------------------------- chunks
@@ -415,7 +446,7 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            S[mt][nt][i] = Si[(32 * (mt >> 1) + 8 * g + 4 * (mt & 1) + i) * kD + cw + 8 * (j >> 2) + 4 * nt + (j & 3)];
+            S[mt][nt][i] = Si[tile_off(32 * (mt >> 1) + 8 * g + 4 * (mt & 1) + i, cw + 8 * (j >> 2) + 4 * nt + (j & 3))];
     } else {
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
@@ -888,46 +919,49 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
 // S_{s+1} = M_s S_s + N_s from S_0 = 0 (gdn_carry_kernel), and the layer
 // kernel on every segment at once from its incoming state S_s.
 
-// LDS of the map kernel: two slots of K [64][kSR], V [64][kSV] (natural
-// order), TB [64][kSC] (acc order), then the fp32 gate blocks of the slots.
-constexpr int mK = 0;
-constexpr int mV = mK + kC * kSR;
-constexpr int mTB = mV + kC * kSV;
-constexpr int mSlot = mTB + kC * kSC;
-constexpr int kMapBytes = 2 * mSlot * 2 + 2 * 4 * kC * 4;
+// The map kernel's chunk inputs reach LDS by direct loads (global_load_lds:
+// lane L of a wave writes 16 bytes at base + 16 L, 1 KB per instruction),
+// two chunks ahead, into a ring of three slots: K [64][kSR] and V [64][kSV]
+// (natural order), TB [64][kSC] (acc order), then g and gamma [64 each]
+// fp32 (in a 1 KB block).  A lane whose 16 bytes fall in a row's padding
+// (or past the gates) loads the row's first piece again (never read).  46
+// instructions per chunk, 6 per wave (the last one three times).
+constexpr int oMK = 0;
+constexpr int oMV = oMK + kC * kSR * 2;
+constexpr int oMTB = oMV + kC * kSV * 2;
+constexpr int oMG = oMTB + kC * kSC * 2;
+constexpr int kMapSlot = oMG + 1024;
+constexpr int kMapBytes = 3 * kMapSlot;
+constexpr int kMapDma = 6;              // direct loads per wave per chunk
 static_assert(kMapBytes <= 160 * 1024, "one workgroup per compute unit");
+static_assert((kC * kSR * 2) % 1024 == 0 && (kC * kSC * 2) % 1024 == 0, "whole 1 KB loads");
 
-// The gate block (g, gamma, -gamma, 2^(g_C - g)) of one chunk from the 32
-// f32x4 pieces of (g, gamma): lane l < 32 holds piece l.  Called by a whole
-// wave (lanes 32.. take part in the shuffle only).
-__device__ __forceinline__ void put_gate_block(float* gs, int l, const f32x4& x) {
-  const float gC = __shfl(x[3], 15, 64);
-  if (l >= 32) return;
-  *reinterpret_cast<f32x4*>(gs + 4 * l) = x;
-  if (l < 16) {
-    f32x4 f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = __builtin_amdgcn_exp2f(fminf(gC - x[i], 0.f));
-    *reinterpret_cast<f32x4*>(gs + 3 * kC + 4 * l) = f;
-  } else {
-    *reinterpret_cast<f32x4*>(gs + kC + 4 * l) = -x;
-  }
+// One direct load (16 bytes per lane into LDS at lds + 16 lane).  Written
+// as asm so that the compiler, which cannot tell which LDS bytes such a load
+// writes, does not wait for it before every transposing LDS read: the
+// kernel itself waits (vmcnt) before the barrier that hands a slot over.
+// It has no register result; m0 holds the wave-uniform LDS address.
+__device__ __forceinline__ void dma16(const void* g, const void* lds) {
+  const unsigned la = __builtin_amdgcn_readfirstlane(
+      (unsigned)(size_t)(const __attribute__((address_space(3))) void*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(la), "v"(g)
+               : "memory", "m0");
 }
 
 // Maps of segment y of each chain.  Waves 0-3 run the recurrence from the
 // zero state on the values (32 columns of N each), waves 4-7 from the
 // identity without values (32 columns of M each); the products are those of
-// the layer kernel's state waves (KS = K S, U = TB V - TB diag(gamma) KS,
+// the layer kernel's state waves (KS = K S, U = TB (V - diag(gamma) KS),
 // S <- gamma_C S + K^T diag(gamma_C / gamma) U) with the same register
-// layouts.  One barrier per chunk: chunk c + 1 is fetched into registers
-// while chunk c is computed and written into the other slot after it.
-// Out: N fp32 and M bf16, [d_k][column] row-major, per (segment, chain).
+// layouts.  One barrier per chunk.
+// Out: N fp32 (tile order, tile_off) and M bf16 ([d_k][column] row-major),
+// per (segment, chain).
 __global__ __launch_bounds__(kThreads) void gdn_segmap_kernel(
     const bf16* k, const bf16* v, const bf16* w_tb, const float* w_g, bf16* __restrict__ seg_m,
     float* __restrict__ seg_n, int B, int T_, int H, int Hkv, int n_sink, int nch, int seg_len) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  bf16* sm = reinterpret_cast<bf16*>(smem_raw);
-  float* Gb = reinterpret_cast<float*>(smem_raw + 2 * mSlot * 2);
   const int G = H / Hkv;
   int unit, member;
   if (!xcd_grouped(blockIdx.x, G, B * Hkv, unit, member)) return;
@@ -946,40 +980,43 @@ __global__ __launch_bounds__(kThreads) void gdn_segmap_kernel(
   const int j = lane & 15;
   const bool mw = wv >= 4;              // the map M: identity start, no values
   const int cw = 32 * (wv & 3);
-  typedef bf16x8 V16;
   const size_t kvrow = (size_t)Hkv * kD;
   const bf16* kb = k + ((size_t)bi * T_ * Hkv + gk) * kD;
   const bf16* vb = v + ((size_t)bi * T_ * Hkv + gk) * kD;
 
-  // staging of one chunk: K and V pieces tid and tid + 512 (16-byte piece n:
-  // row n / 16, columns 8 (n % 16) ..; rows past the sequence repeat its
-  // last row and meet zero rows and columns of TB), TB piece tid, and the
-  // gate pieces (wave 0)
-  V16 pk[2], pv[2], pt;
-  f32x4 pg = zero4();
-  auto fetch = [&](int c) {
+  // this wave's direct loads of chunk c into slot sl: list entries wv + 8 m
+  // (K pieces 0..17, V 18..35, TB 36..44, the gates 45); rows past the
+  // sequence repeat its last row (they meet zero rows and columns of TB)
+  auto issue = [&](int c, int sl) {
     const int row0 = n_sink + c * kC;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int n = tid + 512 * m;
-      const size_t r = (size_t)min(row0 + (n >> 4), T_ - 1);
-      pk[m] = *reinterpret_cast<const V16*>(kb + r * kvrow + (n & 15) * 8);
-      pv[m] = *reinterpret_cast<const V16*>(vb + r * kvrow + (n & 15) * 8);
-    }
     const size_t ci = chain * nch + c;
-    pt = *reinterpret_cast<const V16*>(w_tb + ci * (kC * kC) + (tid >> 3) * kC + (tid & 7) * 8);
-    if (wv == 0) pg = *reinterpret_cast<const f32x4*>(w_g + ci * (2 * kC) + 4 * (lane & 31));
-  };
-  auto commit = [&](int sl) {
-    bf16* base = sm + sl * mSlot;
+    const unsigned char* base = smem_raw + sl * kMapSlot;
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int n = tid + 512 * m;
-      *reinterpret_cast<V16*>(base + mK + (n >> 4) * kSR + (n & 15) * 8) = pk[m];
-      *reinterpret_cast<V16*>(base + mV + (n >> 4) * kSV + (n & 15) * 8) = pv[m];
+    for (int m = 0; m < kMapDma; ++m) {
+      const int i = min(wv + 8 * m, 45);
+      const void* src;
+      int dst;
+      if (i < 36) {
+        const int n = i < 18 ? i : i - 18;
+        const int off = 1024 * n + 16 * lane;
+        const int r = off / (kSR * 2);
+        const int pc = (off % (kSR * 2)) >> 4;
+        const size_t row = (size_t)min(row0 + r, T_ - 1);
+        src = (i < 18 ? kb : vb) + row * kvrow + (pc < 16 ? 8 * pc : 0);
+        dst = (i < 18 ? oMK : oMV) + 1024 * n;
+      } else if (i < 45) {
+        const int n = i - 36;
+        const int off = 1024 * n + 16 * lane;
+        const int r = off / (kSC * 2);
+        const int pc = (off % (kSC * 2)) >> 4;
+        src = w_tb + ci * (kC * kC) + r * kC + (pc < 8 ? 8 * pc : 0);
+        dst = oMTB + 1024 * n;
+      } else {
+        src = w_g + ci * (2 * kC) + 4 * (lane & 31);
+        dst = oMG;
+      }
+      dma16(src, base + dst);
     }
-    *reinterpret_cast<V16*>(base + mTB + (tid >> 3) * kSC + (tid & 7) * 8) = pt;
-    if (wv == 0) put_gate_block(Gb + sl * 4 * kC, lane, pg);
   };
 
   // state tile mt's accumulator row 4 g + i is d_k = 32 (mt / 2) + 8 g +
@@ -994,19 +1031,24 @@ __global__ __launch_bounds__(kThreads) void gdn_segmap_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) S[mt][nt][i] = mw && row_of(mt, i) == col_of(nt) ? 1.f : 0.f;
 
-  fetch(cb);
-  commit(0);
+  // chunks cb and cb + 1 (every issue is made, the chunk index clamped, so
+  // that each wave always has exactly kMapDma loads per chunk in flight)
+  issue(cb, 0);
+  issue(min(cb + 1, ce - 1), 1);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | kMapDma);   // vmcnt(6): chunk cb has landed
+  unsigned sl = 0;
   for (int c = cb; c < ce; ++c) {
-    const int sl = (c - cb) & 1;
-    const bf16* Kc = sm + sl * mSlot + mK;
-    const bf16* Vc = sm + sl * mSlot + mV;
-    const bf16* TBc = sm + sl * mSlot + mTB;
-    const float* Gc = Gb + sl * 4 * kC;
+    const bf16* Kc = reinterpret_cast<const bf16*>(smem_raw + sl * kMapSlot + oMK);
+    const bf16* Vc = reinterpret_cast<const bf16*>(smem_raw + sl * kMapSlot + oMV);
+    const bf16* TBc = reinterpret_cast<const bf16*>(smem_raw + sl * kMapSlot + oMTB);
+    const float* Gc = reinterpret_cast<const float*>(smem_raw + sl * kMapSlot + oMG);
+    const unsigned sl2 = sl == 0 ? 2u : sl - 1;      // (sl + 2) % 3: chunk c - 1's slot
     int l_row = j * kSR + 8 * g, l_tk = (4 * g + (j >> 2)) * kSR + 8 * (j & 3), l_acc = j * kSC + 8 * g;
     asm volatile("" : "+v"(l_row), "+v"(l_tk), "+v"(l_acc));
-    lds_barrier();                       // chunk c is in slot sl; slot sl ^ 1 is free
-    if (c + 1 < ce) fetch(c + 1);
-    asm volatile("" ::: "memory");       // issue the loads here, ahead of the products
+    lds_barrier();                       // chunk c is in slot sl; chunk c - 1's slot is free
+    issue(min(c + 2, ce - 1), sl2);
+    asm volatile("" ::: "memory");
     // ---- KS = K S [token tile mt][column tile nt]
     f32x4 KS[4][2];
 #pragma unroll
@@ -1025,17 +1067,29 @@ __global__ __launch_bounds__(kThreads) void gdn_segmap_kernel(
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) KS[mt][nt] = mfma(kf[mt], sf[nt], KS[mt][nt]);
     }
-    // ---- U = TB V - TB diag(gamma) KS (the map waves: no values)
-    Frag<bf16> ksf[2][2];
-    {
-      const float* ngam = Gc + 2 * kC;
+    // ---- U = TB (V - diag(gamma) KS) (the map waves: no values); the
+    // operand X = V - diag(gamma) KS is formed in fp32 and rounded once
+    const float* gam = Gc + kC;
+    Frag<bf16> xf[2][2];
 #pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        const f32x4 n0 = *reinterpret_cast<const f32x4*>(ngam + 32 * pp + 4 * g);
-        const f32x4 n1 = *reinterpret_cast<const f32x4*>(ngam + 32 * pp + 16 + 4 * g);
+    for (int pp = 0; pp < 2; ++pp) {
+      const f32x4 n0 = -*reinterpret_cast<const f32x4*>(gam + 32 * pp + 4 * g);
+      const f32x4 n1 = -*reinterpret_cast<const f32x4*>(gam + 32 * pp + 16 + 4 * g);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          ksf[pp][nt] = frag_from_acc_scaled<bf16>(KS[2 * pp][nt], KS[2 * pp + 1][nt], n0, n1);
+      for (int nt = 0; nt < 2; ++nt) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = n0[i] * KS[2 * pp][nt][i];
+          x[4 + i] = n1[i] * KS[2 * pp + 1][nt][i];
+        }
+        if (!mw) {
+          // V^T fragment with the same (token, column) per element as KS's
+          const Frag<bf16> vf = tr_at(Vc + cw + l_tk, 32 * pp * kSR + 4 * nt);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] += static_cast<float>(vf.v[e]);
+        }
+        xf[pp][nt] = frag_from8<bf16>(x);
       }
     }
     f32x4 U[4][2];
@@ -1048,28 +1102,25 @@ __global__ __launch_bounds__(kThreads) void gdn_segmap_kernel(
       Frag<bf16> tf[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) tf[mt] = lds_frag8(TBc + l_acc + 16 * mt * kSC + 32 * pp);
-      if (!mw) {
-        Frag<bf16> vf[2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) vf[nt] = tr_at(Vc + cw + l_tk, 32 * pp * kSR + 4 * nt);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) U[mt][nt] = mfma(tf[mt], vf[nt], U[mt][nt]);
-      }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) U[mt][nt] = mfma(tf[mt], ksf[pp][nt], U[mt][nt]);
+        for (int nt = 0; nt < 2; ++nt) U[mt][nt] = mfma(tf[mt], xf[pp][nt], U[mt][nt]);
     }
     // ---- S = gamma_C S + K^T diag(gamma_C / gamma) U
-    const float gC = Gc[2 * kC - 1];
-    const float* dec = Gc + 3 * kC;
+    const float gC = gam[kC - 1];
+    const float lgC = Gc[kC - 1];
     Frag<bf16> us[2][2];
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
-      const f32x4 s0 = *reinterpret_cast<const f32x4*>(dec + 32 * pp + 4 * g);
-      const f32x4 s1 = *reinterpret_cast<const f32x4*>(dec + 32 * pp + 16 + 4 * g);
+      const f32x4 l0 = *reinterpret_cast<const f32x4*>(Gc + 32 * pp + 4 * g);
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(Gc + 32 * pp + 16 + 4 * g);
+      f32x4 s0, s1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s0[i] = __builtin_amdgcn_exp2f(fminf(lgC - l0[i], 0.f));
+        s1[i] = __builtin_amdgcn_exp2f(fminf(lgC - l1[i], 0.f));
+      }
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) us[pp][nt] = frag_from_acc_scaled<bf16>(U[2 * pp][nt], U[2 * pp + 1][nt], s0, s1);
     }
@@ -1087,8 +1138,11 @@ __global__ __launch_bounds__(kThreads) void gdn_segmap_kernel(
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) S[mt][nt] = mfma(kt[pp], us[pp][nt], S[mt][nt]);
     }
-    if (c + 1 < ce) commit(sl ^ 1);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kMapDma);   // vmcnt(6): chunk c + 1 has landed
+    sl = sl == 2 ? 0u : sl + 1;
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // no direct load outlives the workgroup
 
   const size_t off = ((size_t)sg * B * H + chain) * kD * kD;
   if (mw) {
@@ -1106,18 +1160,21 @@ __global__ __launch_bounds__(kThreads) void gdn_segmap_kernel(
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) seg_n[off + row_of(mt, i) * kD + col_of(nt)] = S[mt][nt][i];
+        for (int i = 0; i < 4; ++i) seg_n[off + tile_off(row_of(mt, i), col_of(nt))] = S[mt][nt][i];
   }
 }
 
 // The carry over the segments of one chain, for 32 state columns c0 .. c0 +
 // 31 (the columns of S are independent): S_1 = N_0, S_{s+1} = M_s S_s + N_s.
-// Writes S_1 .. S_{P-1} (the incoming states of segments 1 .. P-1) and, with
-// write_state, S_P (the final state).  Wave w computes rows 32 w .. + 31;
+// Writes S_1 .. S_{P-1} (the incoming states of segments 1 .. P-1, tile
+// order) and, with write_state, S_P (the final state).  Wave w computes rows
+// 16 w .. + 15;
 // the state passes between steps through LDS as bf16 S^T [column][d_k]; the
-// maps' operands of the next step are loaded while a step runs.
+// operands of M_s and N_s are loaded kCarryDepth steps ahead (they do not
+// depend on the carry), so a step waits only on its own products.
 constexpr int kCarryST = kD + 8;    // row stride of S^T in LDS
-__global__ __launch_bounds__(256) void gdn_carry_kernel(const bf16* __restrict__ seg_m,
+constexpr int kCarryDepth = 4;
+__global__ __launch_bounds__(512) void gdn_carry_kernel(const bf16* __restrict__ seg_m,
                                                         const float* __restrict__ seg_n,
                                                         float* __restrict__ seg_s,
                                                         float* __restrict__ state_out, int C,
@@ -1129,79 +1186,89 @@ __global__ __launch_bounds__(256) void gdn_carry_kernel(const bf16* __restrict__
   const int wv = wave_id();
   const int g = lane >> 4;
   const int j = lane & 15;
-  // accumulator tile (t, u): rows 32 wv + 16 t + 4 g + i, column c0 + 16 u + j
-  auto at = [&](int t, int u, int i) { return (32 * wv + 16 * t + 4 * g + i) * kD + c0 + 16 * u + j; };
+  // accumulator tile u: rows 16 wv + 4 g + i, column c0 + 16 u + j; at(u)
+  // is its 4 values' offset in tile order
+  auto at = [&](int u) { return (wv * 8 + (c0 >> 4) + u) * 256 + 4 * lane; };
   auto mat = [&](int s) { return ((size_t)s * C + chain) * kD * kD; };
-  f32x4 acc[2][2];
-  const float* N0 = seg_n + mat(0);
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[t][u][i] = N0[at(t, u, i)];
   const int last = write_state ? P : P - 1;   // the last state needed
   // operands of step s (S_{s+1} = M_s S_s + N_s): A fragments of M_s rows
-  // 32 wv + 16 t + j, d_k 32 p + 8 g .. + 7, and N_s
-  Frag<bf16> ma[2][4];
-  f32x4 na[2][2];
-  auto load_step = [&](int s) {
+  // 16 wv + j, d_k 32 p + 8 g .. + 7, and N_s
+  Frag<bf16> ma[kCarryDepth][4];
+  f32x4 na[kCarryDepth][2];
+  // (every step loads and stores unconditionally, so that the compiler's
+  // memory-counter waits stay exact: loads past the last map reread map
+  // P - 1, and the states of steps past the last go to the workspace's
+  // spare slot P)
+  auto load_step = [&](int q, int s) {
+    s = min(s, P - 1);
     const bf16* M = seg_m + mat(s);
     const float* N = seg_n + mat(s);
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int p = 0; p < 4; ++p)
+      ma[q][p].v = *reinterpret_cast<const bf16x8*>(M + (16 * wv + j) * kD + 32 * p + 8 * g);
 #pragma unroll
-      for (int p = 0; p < 4; ++p)
-        ma[t][p].v = *reinterpret_cast<const bf16x8*>(M + (32 * wv + 16 * t + j) * kD + 32 * p + 8 * g);
+    for (int u = 0; u < 2; ++u) na[q][u] = *reinterpret_cast<const f32x4*>(N + at(u));
+  };
+  f32x4 acc[2];
+  const float* N0 = seg_n + mat(0);
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+  for (int u = 0; u < 2; ++u) acc[u] = *reinterpret_cast<const f32x4*>(N0 + at(u));
+  // (the empty asm statements keep the loads in step order, so that a
+  // step's wait covers only its own operands)
+#pragma unroll
+  for (int q = 0; q < kCarryDepth; ++q) {
+    load_step(q, 1 + q);
+    asm volatile("" ::: "memory");
+  }
+  for (int s0 = 1; s0 < last; s0 += kCarryDepth) {
+#pragma unroll
+    for (int q = 0; q < kCarryDepth; ++q) {
+      const int s = s0 + q;
+      const bool live = s < last;
+      // acc holds S_s (past the last step: S_last): out to the segment's
+      // incoming state, and as bf16 S^T
+      float* So = seg_s + mat(min(s, P));
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        *reinterpret_cast<f32x4*>(So + at(u)) = acc[u];
+        bf16x4 x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = static_cast<bf16>(acc[u][i]);
+        *reinterpret_cast<bf16x4*>(ST + (16 * u + j) * kCarryST + 16 * wv + 4 * g) = x;
+      }
+      lds_barrier();
+      Frag<bf16> sb[2][4];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) na[t][u][i] = N[at(t, u, i)];
-  };
-  if (last >= 2) load_step(1);
-  for (int s = 1; s < last; ++s) {
-    // acc holds S_s: out to the segment's incoming state, and as bf16 S^T
-    float* So = seg_s + mat(s);
+        for (int p = 0; p < 4; ++p) sb[u][p] = lds_frag8(ST + (16 * u + j) * kCarryST + 32 * p + 8 * g);
+      f32x4 nx[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int u = 0; u < 2; ++u) nx[u] = na[q][u];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int p = 0; p < 4; ++p)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) So[at(t, u, i)] = acc[t][u][i];
-        bf16x4 x;
+        for (int u = 0; u < 2; ++u) nx[u] = mfma(ma[q][p], sb[u][p], nx[u]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = static_cast<bf16>(acc[t][u][i]);
-        *reinterpret_cast<bf16x4*>(ST + (16 * u + j) * kCarryST + 32 * wv + 16 * t + 4 * g) = x;
-      }
-    lds_barrier();
-    Frag<bf16> sb[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int p = 0; p < 4; ++p) sb[u][p] = lds_frag8(ST + (16 * u + j) * kCarryST + 32 * p + 8 * g);
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) acc[t][u] = na[t][u];
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) acc[t][u] = mfma(ma[t][p], sb[u][p], acc[t][u]);
-    if (s + 1 < last) load_step(s + 1);
-    lds_barrier();                       // S^T is read before the next step overwrites it
+      for (int u = 0; u < 2; ++u) acc[u] = live ? nx[u] : acc[u];
+      asm volatile("" ::: "memory");
+      load_step(q, s + kCarryDepth);
+      lds_barrier();                     // S^T is read before the next step overwrites it
+    }
   }
-  // acc holds S_last: the final state, or the last segment's incoming state
-  float* So = last == P ? state_out + (size_t)chain * kD * kD : seg_s + mat(last);
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
+  // acc holds S_last: the final state ([d_k][d_v] row-major), or the last
+  // segment's incoming state
+  if (last == P) {
+    float* So = state_out + (size_t)chain * kD * kD;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) So[at(t, u, i)] = acc[t][u][i];
+      for (int i = 0; i < 4; ++i) So[(16 * wv + 4 * g + i) * kD + c0 + 16 * u + j] = acc[u][i];
+  } else {
+    float* So = seg_s + mat(last);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) *reinterpret_cast<f32x4*>(So + at(u)) = acc[u];
+  }
 }
 
 }  // namespace
@@ -1262,7 +1329,7 @@ SegWorkspace gdn_seg_layout(void* base, int B, int H, int nch) {
   s.n = reinterpret_cast<float*>(b + off);
   off += mats * 4;
   s.s = reinterpret_cast<float*>(b + off);
-  off += mats * 4;
+  off += mats * 4 + (size_t)B * H * kD * kD * 4;   // + the carry's spare slot P
   s.bytes = off;
   return s;
 }
@@ -1284,7 +1351,7 @@ hipError_t launch_gdn_segmented(const PrefillArgs& p, hipStream_t s) {
                      p.Hkv, p.n_sink, nch, pl.L);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gdn_carry_kernel, dim3(4 * C), dim3(256), 0, s, (const bf16*)w.m,
+  hipLaunchKernelGGL(gdn_carry_kernel, dim3(4 * C), dim3(512), 0, s, (const bf16*)w.m,
                      (const float*)w.n, w.s, p.state_out, C, pl.P, wst ? 1 : 0);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

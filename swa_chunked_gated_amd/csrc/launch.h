@@ -157,8 +157,8 @@ SegPlan gdn_seg_plan(int B, int H, int nch);
 bool gdn_segmented(int B, int T, int H, int D, int n_sink, int window, int bf16, int gla, int flags);
 bool gdn_segmented(const PrefillArgs& p);
 // Its workspace: the light preparation's, then per (segment, chain) the
-// map M (bf16), the state N (fp32) and the incoming state S (fp32), each
-// [128][128] row-major.
+// map M (bf16), the state N (fp32) and the incoming state S (fp32, one
+// more spare segment), each [128][128] row-major.
 struct SegWorkspace {
   GdnWorkspace light;
   void* m;
