@@ -306,6 +306,44 @@ int gdn_hybrid_prefill_noalloc(const void* q, const void* k, const void* v,
 size_t gdn_hybrid_noalloc_max_workspace(void);
 
 /*
+ * Backward pass of the prefill (the training path; [P1] 实践建议 item 4
+ * trains the linearised layers, [P1] 线性注意力替换机制 gives the recurrence
+ * differentiated): the gradients of
+ *     L = sum(d_o * o) + sum(d_state * S_final),
+ *     o = w_lin o_lin + w_swa o_swa   (both branches, no cache),
+ * for o and S_final as gdn_hybrid_prefill_weighted computes them from q, k,
+ * v, a, b (state starting at zero).
+ *   d_o      [B,T,H,d]     upstream gradient of o (dtype of q)
+ *   d_state  [B,H,d,d]     upstream gradient of the final state, fp32; NULL
+ *                          means zero
+ *   dq       [B,T,H,d]     fp32, dL/dq
+ *   dk, dv   [B,T,Hkv,d]   fp32, dL/dk, dL/dv (summed over the G query heads
+ *                          of each KV head)
+ *   da, db   [B,T,H]       fp32, dL/da, dL/db (zero where the recurrence
+ *                          does not read them)
+ * Every output is overwritten.  Supported: update = GDN_DELTA, dtype =
+ * GDN_BF16, d_k = d_v = 128 (GDN_EUNSUPPORTED otherwise); any B, T, H, Hkv,
+ * n_sink >= 0, window >= 1.  The workspace (device, 256-byte aligned, size
+ * from gdn_hybrid_prefill_backward_workspace; its contents on entry do not
+ * matter) holds the chunk preparation, the state entering every 64-token
+ * chunk and the gradient of the state leaving it (bf16), and the softmax
+ * row statistics.  fp32 gradients are accumulated from bf16 MFMA products
+ * with fp32 accumulation.
+ * Errors: as gdn_hybrid_prefill.
+ */
+int gdn_hybrid_prefill_backward_workspace(int B, int T, int H, int Hkv, int dk, int dv,
+                                          int n_sink, int window, int dtype, int update,
+                                          size_t* bytes);
+int gdn_hybrid_prefill_backward(const void* q, const void* k, const void* v,
+                                const float* a, const float* b,
+                                const void* d_o, const float* d_state,
+                                float* dq, float* dk, float* dv, float* da, float* db,
+                                int B, int T, int H, int Hkv, int dk_, int dv_,
+                                int n_sink, int window, int dtype, int update,
+                                float w_lin, float w_swa,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Fill the decode cache after a prefill of T tokens, so decoding resumes at
  * position T: sinks 0..min(n_sink,T)-1 and window tokens
  * max(n_sink, T-window)..T-1 go to their slots (layouts as in

@@ -32,7 +32,7 @@ _UPDATES = {"gdn": 0, "gla": 1, "dgd": 2}
 
 __all__ = [
     "hybrid_prefill", "hybrid_decode", "cache_from_prefill", "shortconv_qkv",
-    "prefill_workspace_bytes",
+    "prefill_workspace_bytes", "hybrid_prefill_backward", "prefill_backward_workspace_bytes",
     "version", "GdnError", "BRANCH_LINEAR", "BRANCH_SOFTMAX", "WRITE_STATE", "ACCUMULATE",
     "PREPARE_ONLY", "PREPARED", "ROPE", "L2NORM",
 ]
@@ -174,6 +174,54 @@ def hybrid_prefill_noalloc(q, k, v, a, b, n_sink: int, window: int, update: str 
 def noalloc_max_workspace() -> int:
     """Bytes of the per-GPU workspace array of ``hybrid_prefill_noalloc``."""
     return int(_lib.load().gdn_hybrid_noalloc_max_workspace())
+
+
+def prefill_backward_workspace_bytes(B: int, T: int, H: int, Hkv: int, d: int, n_sink: int,
+                                     window: int) -> int:
+    """Device workspace (bytes) ``hybrid_prefill_backward`` needs."""
+    n = ctypes.c_size_t(0)
+    rc = _lib.load().gdn_hybrid_prefill_backward_workspace(B, T, H, Hkv, d, d, n_sink, window,
+                                                           _DTYPES[torch.bfloat16],
+                                                           _UPDATES["gdn"], ctypes.byref(n))
+    _lib.check("gdn_hybrid_prefill_backward_workspace", rc)
+    return n.value
+
+
+def hybrid_prefill_backward(q, k, v, a, b, n_sink: int, window: int, d_o, d_state=None,
+                            weights=(1.0, 1.0), workspace=None):
+    """Gradients of sum(d_o * o) + sum(d_state * S_final) for the prefill
+    o = w_lin o_lin + w_swa o_swa (gated delta rule, bf16, d = 128).
+
+    q, d_o [B,T,H,d] and k, v [B,T,Hkv,d] bf16; a, b [B,T,H] fp32; d_state
+    [B,H,d,d] fp32 or None.  Returns fp32 (dq, dk, dv, da, db) with the
+    shapes of q, k, v, a, b.
+    """
+    B, T, H, d = q.shape
+    Hkv = k.shape[2]
+    dt = _io_dtype(q, k, v, d_o)
+    _f32(a, b, d_state)
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq = torch.empty(B, T, H, d, **f32)
+    dk = torch.empty(B, T, Hkv, d, **f32)
+    dv = torch.empty(B, T, Hkv, d, **f32)
+    da = torch.empty(B, T, H, **f32)
+    db = torch.empty(B, T, H, **f32)
+    lib = _lib.load()
+    need = ctypes.c_size_t(0)
+    rc = lib.gdn_hybrid_prefill_backward_workspace(B, T, H, Hkv, d, d, n_sink, window, dt,
+                                                   _UPDATES["gdn"], ctypes.byref(need))
+    _lib.check("gdn_hybrid_prefill_backward_workspace", rc)
+    if workspace is None:
+        workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    rc = lib.gdn_hybrid_prefill_backward(_p(q), _p(k), _p(v), _p(a), _p(b), _p(d_o), _p(d_state),
+                                         _p(dq), _p(dk), _p(dv), _p(da), _p(db), B, T, H, Hkv, d, d,
+                                         n_sink, window, dt, _UPDATES["gdn"],
+                                         float(weights[0]), float(weights[1]), _p(workspace),
+                                         ws_bytes, _stream(q))
+    _lib.check("gdn_hybrid_prefill_backward", rc)
+    return dq, dk, dv, da, db
 
 
 def hybrid_decode(q, k, v, a, b, state, k_cache, v_cache, a_cache, b_cache, pos,

@@ -31,6 +31,10 @@ SIGNATURES = {
     "gdn_hybrid_prefill_noalloc": (
         _c_int, [_ptr] * 7 + [_c_int] * 11 + [_ptr]),
     "gdn_hybrid_noalloc_max_workspace": (ctypes.c_size_t, []),
+    "gdn_hybrid_prefill_backward_workspace": (
+        _c_int, [_c_int] * 10 + [ctypes.POINTER(ctypes.c_size_t)]),
+    "gdn_hybrid_prefill_backward": (
+        _c_int, [_ptr] * 12 + [_c_int] * 10 + [ctypes.c_float] * 2 + [_ptr, ctypes.c_size_t, _ptr]),
     "gdn_hybrid_decode_weighted": (
         _c_int, [_ptr] * 12 + [_c_int] * 10 + [ctypes.c_float] * 2 + [_ptr]),
     "gdn_hybrid_cache_from_prefill": (

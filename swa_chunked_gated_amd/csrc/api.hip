@@ -39,6 +39,16 @@ bool dims_ok(int B, int T, int H, int Hkv, int dk, int dv, int n_sink, int windo
   return true;
 }
 
+// The backward pass: bf16 GDN at d = 128 (the query tile, head and sequence
+// are grid dimensions).
+int backward_supported(int B, int T, int H, int Hkv, int dk, int dv, int n_sink, int window,
+                       int dtype, int update) {
+  if (!dims_ok(B, T, H, Hkv, dk, dv, n_sink, window, dtype, update)) return GDN_EINVAL;
+  if (update != GDN_DELTA || dtype != GDN_BF16 || dk != 128) return GDN_EUNSUPPORTED;
+  if ((T + 63) / 64 > 65535 || H > 65535 || B > 65535) return GDN_EUNSUPPORTED;
+  return GDN_OK;
+}
+
 // Tensor arguments are read and written with 16-byte vector accesses: every
 // pointer must be 16-byte aligned (NULL passes; whether a NULL is allowed is
 // checked separately).
@@ -247,6 +257,35 @@ int gdn_hybrid_prefill_noalloc(const void* q, const void* k, const void* v, cons
                                int update, int flags, void* stream) {
   return prefill_impl(q, k, v, a, b, o, state_out, B, T, H, Hkv, dk, dv, n_sink, window, dtype,
                       update, flags, 1.f, 1.f, nullptr, 0, true, stream);
+}
+
+int gdn_hybrid_prefill_backward_workspace(int B, int T, int H, int Hkv, int dk, int dv, int n_sink,
+                                          int window, int dtype, int update, size_t* bytes) {
+  if (!bytes) return GDN_EINVAL;
+  const int rc = backward_supported(B, T, H, Hkv, dk, dv, n_sink, window, dtype, update);
+  if (rc) return rc;
+  *bytes = gdn::gdn_bwd_layout(nullptr, B, T, H, n_sink, window).bytes;
+  return GDN_OK;
+}
+
+int gdn_hybrid_prefill_backward(const void* q, const void* k, const void* v, const float* a,
+                                const float* b, const void* d_o, const float* d_state, float* dq,
+                                float* dk, float* dv, float* da, float* db, int B, int T, int H,
+                                int Hkv, int dk_, int dv_, int n_sink, int window, int dtype,
+                                int update, float w_lin, float w_swa, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  const int rc = backward_supported(B, T, H, Hkv, dk_, dv_, n_sink, window, dtype, update);
+  if (rc) return rc;
+  if (!std::isfinite(w_lin) || !std::isfinite(w_swa)) return GDN_EINVAL;
+  if (!q || !k || !v || !a || !b || !d_o || !dq || !dk || !dv || !da || !db) return GDN_EINVAL;
+  if (!aligned16({q, k, v, a, b, d_o, d_state, dq, dk, dv, da, db})) return GDN_EINVAL;
+  const size_t need = gdn::gdn_bwd_layout(nullptr, B, T, H, n_sink, window).bytes;
+  if (!workspace || workspace_bytes < need) return GDN_EWORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return GDN_EINVAL;
+  if (T == 0) return GDN_OK;
+  gdn::BwdArgs p{q, k, v, a, b, d_o, d_state, dq, dk, dv, da, db, B, T, H, Hkv, n_sink, window,
+                 w_lin, w_swa, workspace};
+  return launched(gdn::launch_gdn_backward(p, (hipStream_t)stream));
 }
 
 int gdn_hybrid_decode(const void* q, const void* k, const void* v, const float* a, const float* b,

@@ -1,0 +1,1125 @@
+// Backward pass of the hybrid layer (prefill, bf16 GDN at d = 128): the
+// gradients of L = sum(do * o) + sum(dS * S_final) with respect to q, k, v
+// and the gates a, b, for o = w_lin o_lin + w_swa o_swa.
+//
+// Method (page "The Key to Going Linear: Analysis-Driven Transformer
+// Linearization"): section 线性注意力替换机制 gives the gated delta rule
+// S_i = a_i (I - b_i k_i k_i^T) S_{i-1} + b_i k_i v_i^T, and section 实践建议
+// item 4 trains the linearised layers, which needs its gradients; section
+// 填补近似缺口的实用设计 fixes the sink + window budget and the lag of the
+// linear read-out (o_lin[t] = S_{t-window}^T q_t).
+//
+// Chunk form (64 stream tokens, incoming state S0; g the prefix sum of log a
+// inside the chunk, gamma = e^g, D_rs = e^{g_r - g_s} (s <= r), L the strictly
+// lower b_r D_rs k_r.k_s, T = (I + L)^-1, TB = T diag(b)):
+//   U = TB (V - diag(gamma) K S0),  A = D o Q K^T (s <= r),
+//   O = diag(gamma) Q S0 + A U,  S1 = gamma_C S0 + (diag(gamma_C / gamma) K)^T U.
+// Its reverse mode, for dO and the gradient dS1 of the chunk's final state:
+//   dU = A^T dO + diag(gamma_C / gamma) K dS1
+//   dS0 = gamma_C dS1 + (diag(gamma) Q)^T dO - (TB diag(gamma) K)^T dU
+//   dA = dO U^T (s <= r);  dQ = diag(gamma) dO S0^T + (dA o D) K
+//   dK = (dA o D)^T Q + diag(gamma_C / gamma) U dS1^T + diag(b gamma) Y + (M + M^T) K
+//   Z = T^T dU,  Y = -Z S0^T,  dV = diag(b) Z
+//   dL = -(Z V^T + Y K^T diag(gamma)) TB^T (s < r),  M = dL o (b_r D_rs)
+// with the gate terms collected per token (db from Z.v, Y.k and dL o D o K K^T;
+// the log-decay gradient from the gamma and D dependences, summed backwards
+// over the chunk into d log a).
+//
+// Launches: the light chunk preparation (also writing T), the forward sweep
+// (the state entering every chunk, bf16), the reverse sweep (the gradient of
+// every chunk's final state, bf16), the per-chunk gradient kernel (one
+// workgroup per chunk and KV head, looping over the KV head's query heads so
+// that dK and dV are summed in registers), then the softmax branch: dq per
+// 64-row query tile (which also saves each row's log-sum-exp and D = do.o,
+// and the sink keys' partial dK, dV), dk and dv per 64-key tile, and the sum
+// of the sink partials.
+//
+// Operand fragments (v_mfma_f32_16x16x32_bf16, lane l = 16 g + j): lane (g, j)
+// supplies operand row m0 + j at the reduction positions k0 + {4g..4g+3,
+// 16+4g..16+4g+3} (the set two stacked accumulator tiles provide).  From a
+// row-major bf16 LDS tile X: fr_row reads them along row m0 + j (two 8-byte
+// reads), fr_col down column m0 + j (two transposing reads), fr_acc along a
+// row stored in acc order (one 16-byte read).  D[4g + i][j] = sum over the
+// reduction of (A-operand row 4g + i) . (B-operand row j).
+
+#include <algorithm>
+
+#include "common.h"
+#include "launch.h"
+
+namespace gdn {
+namespace {
+
+constexpr int bC = 64;            // chunk length
+constexpr int bD = 128;           // head dimension
+constexpr int bSR = bD + 8;       // row stride of [*][128] bf16 tiles
+constexpr int bSC = bC + 8;       // row stride of [*][64] bf16 tiles
+
+typedef __attribute__((address_space(3))) bf16x4* lds4_ptr;
+
+__device__ __forceinline__ Frag<bf16> fr_row(const bf16* X, int S, int m0, int k0, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const bf16* p = X + (m0 + j) * S + k0 + 4 * g;
+  return lds_frag44(p, p + 16);
+}
+__device__ __forceinline__ Frag<bf16> fr_col(const bf16* X, int S, int k0, int m0, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const bf16* p = X + (k0 + 4 * g + (j >> 2)) * S + m0 + 4 * (j & 3);
+  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4_ptr)(p));
+  const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4_ptr)(p + 16 * S));
+  Frag<bf16> f;
+  f.v = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return f;
+}
+__device__ __forceinline__ Frag<bf16> fr_acc(const bf16* X, int S, int m0, int k0, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  return lds_frag8(X + (m0 + j) * S + k0 + 8 * g);
+}
+__device__ __forceinline__ Frag<bf16> neg(Frag<bf16> f) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = static_cast<bf16>(-static_cast<float>(f.v[e]));
+  return f;
+}
+// Sum over the 16 lanes j of each lane group (xor within 16).
+__device__ __forceinline__ float sum16(float x) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+// 4 bf16 values at p (8-byte aligned)
+__device__ __forceinline__ void put4(bf16* p, const f32x4& x) {
+  *reinterpret_cast<bf16x4*>(p) = bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]),
+                                         static_cast<bf16>(x[2]), static_cast<bf16>(x[3])};
+}
+__device__ __forceinline__ float bf(bf16 x) { return static_cast<float>(x); }
+
+// A [64][128] tile of token rows row0 .. row0 + 63 (row stride `stride`
+// elements) into LDS [64][bSR] by nth threads; rows at or past `valid` are
+// zero when `zero_past`, else they repeat row valid - 1 (valid >= 1).
+__device__ __forceinline__ void load_rows128(bf16* dst, const bf16* src, size_t stride, int valid,
+                                             bool zero_past, float scale, int tid, int nth) {
+  typedef bf16x8 V16;
+  for (int n = tid; n < bC * 16; n += nth) {
+    const int r = n >> 4;
+    const int c = (n & 15) * 8;
+    V16 x;
+    if (r < valid || !zero_past) {
+      x = *reinterpret_cast<const V16*>(src + (size_t)min(r, valid - 1) * stride + c);
+      if (scale != 1.f) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = static_cast<bf16>(bf(x[e]) * scale);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = static_cast<bf16>(0.f);
+    }
+    *reinterpret_cast<V16*>(dst + r * bSR + c) = x;
+  }
+}
+
+// ------------------------------------------------------------------------
+// Reverse sweep: one workgroup of 8 waves per (sequence, query head); wave w
+// owns the columns 16 w .. + 15 of dS as fp32 accumulators (rows d_k = 16 mt
+// + 4 g + i).  For chunk c = nch - 1 .. 0 it stores dS (the gradient of the
+// state after chunk c) to ds1 and steps dS back over the chunk.
+constexpr int rK = 0;                      // bf16 element offsets
+constexpr int rQ = rK + bC * bSR;
+constexpr int rKG = rQ + bC * bSR;         // diag(gamma) K
+constexpr int rO = rKG + bC * bSR;         // w_lin dO (zero past the stream)
+constexpr int rTB = rO + bC * bSR;         // TB (acc order)
+constexpr int rA = rTB + bC * bSC;         // A (natural)
+constexpr int rWt = rA + bC * bSC;         // W^T [128][bSC]
+constexpr int rEnd = rWt + bD * bSC;
+constexpr int kRevBytes = rEnd * 2 + 2 * bC * 4;
+static_assert(kRevBytes <= 160 * 1024, "LDS");
+
+__global__ __launch_bounds__(512) void gdn_bwd_rev_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ d_o,
+    const bf16* __restrict__ w_tb, const float* __restrict__ w_g, const float* __restrict__ d_state,
+    bf16* __restrict__ ds1, int B, int T_, int H, int Hkv, int n_sink, int window, int nch,
+    float w_lin) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  bf16* sm = reinterpret_cast<bf16*>(smem_raw);
+  bf16* Ks = sm + rK;
+  bf16* Qs = sm + rQ;
+  bf16* KGs = sm + rKG;
+  bf16* Os = sm + rO;
+  bf16* TBs = sm + rTB;
+  bf16* As = sm + rA;
+  bf16* Wt = sm + rWt;
+  float* lg = reinterpret_cast<float*>(smem_raw + rEnd * 2);   // g (log2), then gamma
+  float* gm = lg + bC;
+
+  const int G = H / Hkv;
+  int unit, member;
+  if (!xcd_grouped(blockIdx.x, G, B * Hkv, unit, member)) return;
+  const int bi = unit / Hkv;
+  const int gk = unit % Hkv;
+  const int h = gk * G + member;
+  const size_t chain = (size_t)bi * H + h;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = wave_id();
+  const int g = lane >> 4;
+  const int j = lane & 15;
+  const int v0 = 16 * wv;
+  const int iend = T_ - window;
+
+  f32x4 dS[8];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dS[mt][i] = d_state ? d_state[(chain * bD + 16 * mt + 4 * g + i) * bD + v0 + j] : 0.f;
+
+  for (int c = nch - 1; c >= 0; --c) {
+    const int i0 = n_sink + c * bC;
+    const int Cc = min(bC, iend - i0);
+    const size_t ci = chain * nch + c;
+    // the gradient of the state after chunk c
+    bf16* dst = ds1 + ci * (bD * bD);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(16 * mt + 4 * g + i) * bD + v0 + j] = static_cast<bf16>(dS[mt][i]);
+    __syncthreads();                       // the previous chunk's LDS reads are done
+    load_rows128(Ks, k + ((size_t)(bi * T_ + i0) * Hkv + gk) * bD, (size_t)Hkv * bD, T_ - i0, false, 1.f, tid, 512);
+    load_rows128(Qs, q + ((size_t)(bi * T_ + i0 + window) * H + h) * bD, (size_t)H * bD, Cc, false, 1.f, tid, 512);
+    load_rows128(Os, d_o + ((size_t)(bi * T_ + i0 + window) * H + h) * bD, (size_t)H * bD, Cc, true, w_lin, tid, 512);
+    {
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(w_tb + ci * (bC * bC) + (tid >> 3) * bC + (tid & 7) * 8);
+      *reinterpret_cast<bf16x8*>(TBs + (tid >> 3) * bSC + (tid & 7) * 8) = x;
+    }
+    if (tid < 2 * bC) lg[tid] = w_g[ci * (2 * bC) + tid];
+    __syncthreads();
+    // diag(gamma) K
+    for (int n = tid; n < bC * 16; n += 512) {
+      const int r = n >> 4;
+      const int cc = (n & 15) * 8;
+      bf16x8 x = *reinterpret_cast<const bf16x8*>(Ks + r * bSR + cc);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = static_cast<bf16>(bf(x[e]) * gm[r]);
+      *reinterpret_cast<bf16x8*>(KGs + r * bSR + cc) = x;
+    }
+    // A = D o Q K^T (s <= r): tiles (r tile, s tile), two per wave
+#pragma unroll
+    for (int w2 = 0; w2 < 2; ++w2) {
+      const int t2 = wv + 8 * w2;
+      const int mt = t2 >> 2, nt = t2 & 3;
+      f32x4 acc = zero4();
+      if (nt <= mt) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) acc = mfma(fr_row(Qs, bSR, 16 * mt, 32 * p, lane), fr_row(Ks, bSR, 16 * nt, 32 * p, lane), acc);
+      }
+      const int s = 16 * nt + j;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mt + 4 * g + i;
+        As[r * bSC + s] = static_cast<bf16>(s <= r ? __builtin_amdgcn_exp2f(fminf(lg[r] - lg[s], 0.f)) * acc[i] : 0.f);
+      }
+    }
+    __syncthreads();
+    // W^T [k][s] = sum_t TB[s][t] gamma_t K[t][k]: 32 tiles, four per wave
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t4 = wv + 8 * u;
+      const int mt = t4 >> 2, nt = t4 & 3;    // k tile, s tile
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int p = 0; p < 2; ++p) acc = mfma(fr_col(KGs, bSR, 32 * p, 16 * mt, lane), fr_acc(TBs, bSC, 16 * nt, 32 * p, lane), acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Wt[(16 * mt + 4 * g + i) * bSC + 16 * nt + j] = static_cast<bf16>(acc[i]);
+    }
+    __syncthreads();
+
+    // ---- dU [s][v] (4 s tiles) = A^T dO + diag(gamma_C / gamma) K dS
+    const float gC = gm[bC - 1];
+    f32x4 dU[4];
+    {
+      Frag<bf16> sf[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) sf[p] = frag_from_acc<bf16>(dS[2 * p], dS[2 * p + 1]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4 kd = zero4(), ad = zero4();
+#pragma unroll
+        for (int p = 0; p < 4; ++p) kd = mfma(fr_row(Ks, bSR, 16 * mt, 32 * p, lane), sf[p], kd);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) ad = mfma(fr_col(As, bSC, 32 * p, 16 * mt, lane), fr_col(Os, bSR, 32 * p, v0, lane), ad);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dU[mt][i] = ad[i] + gC / gm[16 * mt + 4 * g + i] * kd[i];
+      }
+    }
+    // ---- dS <- gamma_C dS + (diag(gamma) Q)^T dO - W^T dU
+    {
+      Frag<bf16> uf[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) uf[p] = neg(frag_from_acc<bf16>(dU[2 * p], dU[2 * p + 1]));
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        f32x4 acc = dS[mt] * gC;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          // (diag(gamma) Q)^T as A operand: rows k, reduction r, scaled by gamma_r
+          Frag<bf16> qf = fr_col(Qs, bSR, 32 * p, 16 * mt, lane);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 32 * p + 4 * g + (e & 3) + 16 * (e >> 2);
+            qf.v[e] = static_cast<bf16>(bf(qf.v[e]) * gm[r]);
+          }
+          acc = mfma(qf, fr_col(Os, bSR, 32 * p, v0, lane), acc);
+        }
+#pragma unroll
+        for (int p = 0; p < 2; ++p) acc = mfma(fr_row(Wt, bSC, 16 * mt, 32 * p, lane), uf[p], acc);
+        dS[mt] = acc;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// Per-chunk gradients: one workgroup of 8 waves per (chunk, KV head,
+// sequence), looping over the KV head's query heads.  S0 and dS1 (bf16
+// [128][128]) pass through LDS in blocks of 32 rows.  [64][128] results are
+// split over the waves as tiles (row tile wv / 2, column tiles 2 u + wv % 2),
+// so that dQ, dK and dV stay in the same registers across the stages.
+constexpr int cK = 0;                       // byte offsets
+constexpr int cV = cK + bC * bSR * 2;
+constexpr int cQ = cV + bC * bSR * 2;
+constexpr int cO = cQ + bC * bSR * 2;       // w_lin dO, later Y^T [128][bSC]
+constexpr int cTB = cO + bD * bSC * 2;
+constexpr int cTm = cTB + bC * bSC * 2;
+constexpr int cBlk = cTm + bC * bSC * 2;    // two [32][bSR] blocks; later dA o D, then M + M^T
+constexpr int cX = cBlk + 2 * 32 * bSR * 2; // X^T, then U^T, then Z^T [128][bSC]
+constexpr int cA = cX + bD * bSC * 2;       // A, then R [64][bSC]
+constexpr int cdU = cA + bC * bSC * 2;      // dU^T [128][bSC]
+constexpr int cF = cdU + bD * bSC * 2;      // fp32: g, gamma, b, dgam, e, rk, db, ddr, ddc, sdot
+constexpr int kChunkBytes = cF + (9 * bC + 4) * 4;
+static_assert(bC * bSR * 2 <= bD * bSC * 2, "Y^T fits the dO slot");
+static_assert(bC * bSC * 2 <= 2 * 32 * bSR * 2, "dA o D fits the block slot");
+static_assert(kChunkBytes <= 160 * 1024, "LDS");
+
+__global__ __launch_bounds__(512) void gdn_bwd_chunk_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ a, const bf16* __restrict__ d_o, const bf16* __restrict__ w_tb,
+    const bf16* __restrict__ w_tm, const float* __restrict__ w_g, const float* __restrict__ bgate,
+    const bf16* __restrict__ s0, const bf16* __restrict__ ds1, float* __restrict__ dq,
+    float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ da, float* __restrict__ db,
+    int B, int T_, int H, int Hkv, int n_sink, int window, int nch, float w_lin) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  bf16* Ks = reinterpret_cast<bf16*>(smem_raw + cK);
+  bf16* Vs = reinterpret_cast<bf16*>(smem_raw + cV);
+  bf16* Qs = reinterpret_cast<bf16*>(smem_raw + cQ);
+  bf16* Os = reinterpret_cast<bf16*>(smem_raw + cO);
+  bf16* Yt = Os;
+  bf16* TBs = reinterpret_cast<bf16*>(smem_raw + cTB);
+  bf16* Tms = reinterpret_cast<bf16*>(smem_raw + cTm);
+  bf16* blkA = reinterpret_cast<bf16*>(smem_raw + cBlk);
+  bf16* blkB = blkA + 32 * bSR;
+  bf16* DAs = blkA;                           // dA o D [64][bSC]
+  bf16* Ms = blkA;                            // M + M^T [64][bSC]
+  bf16* Xt = reinterpret_cast<bf16*>(smem_raw + cX);
+  bf16* As = reinterpret_cast<bf16*>(smem_raw + cA);
+  bf16* Rs = As;
+  bf16* dUt = reinterpret_cast<bf16*>(smem_raw + cdU);
+  float* lgs = reinterpret_cast<float*>(smem_raw + cF);   // g (log2)
+  float* gm = lgs + bC;
+  float* bb = gm + bC;
+  float* dgam = bb + bC;
+  float* ee = dgam + bC;
+  float* rk = ee + bC;
+  float* dbs = rk + bC;
+  float* ddr = dbs + bC;
+  float* ddc = ddr + bC;
+  float* sdot = ddc + bC;
+
+  const int c = blockIdx.x;
+  const int gk = blockIdx.y;
+  const int bi = blockIdx.z;
+  const int G = H / Hkv;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = wave_id();
+  const int g = lane >> 4;
+  const int j = lane & 15;
+  const int iend = T_ - window;
+  const int i0 = n_sink + c * bC;
+  const int Cc = min(bC, iend - i0);
+  const int om = wv >> 1;                     // owned row tile
+  auto on = [&](int u) { return 2 * u + (wv & 1); };   // owned column tiles
+
+  load_rows128(Ks, k + ((size_t)(bi * T_ + i0) * Hkv + gk) * bD, (size_t)Hkv * bD, T_ - i0, false, 1.f, tid, 512);
+  load_rows128(Vs, v + ((size_t)(bi * T_ + i0) * Hkv + gk) * bD, (size_t)Hkv * bD, T_ - i0, false, 1.f, tid, 512);
+
+  f32x4 dK[4], dV[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) dK[u] = dV[u] = zero4();
+
+  for (int m = 0; m < G; ++m) {
+    const int h = gk * G + m;
+    const size_t chain = (size_t)bi * H + h;
+    const size_t ci = chain * nch + c;
+    const bf16* S0g = s0 + ci * (bD * bD);
+    const bf16* dS1g = ds1 + ci * (bD * bD);
+    __syncthreads();                         // the previous head's LDS reads are done
+    load_rows128(Qs, q + ((size_t)(bi * T_ + i0 + window) * H + h) * bD, (size_t)H * bD, Cc, false, 1.f, tid, 512);
+    load_rows128(Os, d_o + ((size_t)(bi * T_ + i0 + window) * H + h) * bD, (size_t)H * bD, Cc, true, w_lin, tid, 512);
+    {
+      const int r = tid >> 3, cc = (tid & 7) * 8;
+      *reinterpret_cast<bf16x8*>(TBs + r * bSC + cc) = *reinterpret_cast<const bf16x8*>(w_tb + ci * (bC * bC) + r * bC + cc);
+      *reinterpret_cast<bf16x8*>(Tms + r * bSC + cc) = *reinterpret_cast<const bf16x8*>(w_tm + ci * (bC * bC) + r * bC + cc);
+    }
+    if (tid < 2 * bC) lgs[tid] = w_g[ci * (2 * bC) + tid];
+    if (tid < bC) {
+      const int t = i0 + tid;
+      bb[tid] = t < iend ? bgate[((size_t)bi * T_ + t) * H + h] : 0.f;
+    }
+    if (tid < 6 * bC + 1) dgam[tid] = 0.f;   // dgam, ee, rk, dbs, ddr, ddc, sdot
+    auto load_blk = [&](bf16* dst, const bf16* src, int kb) {
+      const int r = tid >> 4, cc = (tid & 15) * 8;
+      *reinterpret_cast<bf16x8*>(dst + r * bSR + cc) = *reinterpret_cast<const bf16x8*>(src + (32 * kb + r) * bD + cc);
+    };
+
+    // ---- S0 pass: KS = K S0 (owned tiles), P1 = dO S0^T -> dQ = diag(gamma) P1
+    f32x4 KS[4], dQ[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) KS[u] = dQ[u] = zero4();
+    for (int kb = 0; kb < 4; ++kb) {
+      __syncthreads();
+      load_blk(blkA, S0g, kb);
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < 4; ++u) KS[u] = mfma(fr_row(Ks, bSR, 16 * om, 32 * kb, lane), fr_col(blkA, bSR, 0, 16 * on(u), lane), KS[u]);
+      f32x4 p1 = zero4();
+#pragma unroll
+      for (int p = 0; p < 4; ++p) p1 = mfma(fr_row(Os, bSR, 16 * om, 32 * p, lane), fr_row(blkA, bSR, 16 * (wv & 1), 32 * p, lane), p1);
+      const int kcol = 32 * kb + 16 * (wv & 1) + j;       // owned dQ tile u = kb
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * om + 4 * g + i;
+        dQ[kb][i] = gm[r] * p1[i];
+        const float x = sum16(p1[i] * bf(Qs[r * bSR + kcol]));
+        if (j == 0) atomicAdd(&dgam[r], x);
+      }
+    }
+    __syncthreads();
+    // X = V - diag(gamma) KS, stored as X^T [v][t]
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int vv = 16 * on(u) + j;
+      f32x4 x;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * om + 4 * g + i;
+        x[i] = bf(Vs[t * bSR + vv]) - gm[t] * KS[u][i];
+      }
+      put4(Xt + vv * bSC + 16 * om + 4 * g, x);
+    }
+    __syncthreads();
+    // U = TB X (owned tiles), then U^T over X^T
+    f32x4 Ur[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int p = 0; p < 2; ++p) acc = mfma(fr_acc(TBs, bSC, 16 * om, 32 * p, lane), fr_row(Xt, bSC, 16 * on(u), 32 * p, lane), acc);
+      Ur[u] = acc;
+    }
+    // A = D o Q K^T (s <= r), two tiles per wave
+#pragma unroll
+    for (int w2 = 0; w2 < 2; ++w2) {
+      const int t2 = wv + 8 * w2;
+      const int mt = t2 >> 2, nt = t2 & 3;
+      f32x4 acc = zero4();
+      if (nt <= mt) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) acc = mfma(fr_row(Qs, bSR, 16 * mt, 32 * p, lane), fr_row(Ks, bSR, 16 * nt, 32 * p, lane), acc);
+      }
+      const int s = 16 * nt + j;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mt + 4 * g + i;
+        As[r * bSC + s] = static_cast<bf16>(s <= r ? __builtin_amdgcn_exp2f(fminf(lgs[r] - lgs[s], 0.f)) * acc[i] : 0.f);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) put4(Xt + (16 * on(u) + j) * bSC + 16 * om + 4 * g, Ur[u]);   // U^T
+    const float gCv = gm[bC - 1];
+
+    // ---- dS1 pass: KdS = K dS1 (owned tiles); dKt = U dS1^T -> dK; <dS1, S0>
+    f32x4 KdS[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) KdS[u] = zero4();
+    for (int kb = 0; kb < 4; ++kb) {
+      __syncthreads();
+      load_blk(blkA, dS1g, kb);
+      load_blk(blkB, S0g, kb);
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < 4; ++u) KdS[u] = mfma(fr_row(Ks, bSR, 16 * om, 32 * kb, lane), fr_col(blkA, bSR, 0, 16 * on(u), lane), KdS[u]);
+      f32x4 kt = zero4();
+#pragma unroll
+      for (int p = 0; p < 4; ++p) kt = mfma(fr_col(Xt, bSC, 32 * p, 16 * om, lane), fr_row(blkA, bSR, 16 * (wv & 1), 32 * p, lane), kt);
+      const int kcol = 32 * kb + 16 * (wv & 1) + j;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = 16 * om + 4 * g + i;
+        dK[kb][i] += gCv / gm[s] * kt[i];
+        const float x = sum16(kt[i] * bf(Ks[s * bSR + kcol]));
+        if (j == 0) atomicAdd(&ee[s], x);
+      }
+      {
+        const int r = tid >> 4, cc = (tid & 15) * 8;
+        float x = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x += bf(blkA[r * bSR + cc + e]) * bf(blkB[r * bSR + cc + e]);
+        x = wave_sum(x);
+        if (lane == 0) atomicAdd(sdot, x);
+      }
+    }
+    // dU = A^T dO + diag(gamma_C / gamma) KdS -> dU^T
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      f32x4 ad = zero4();
+#pragma unroll
+      for (int p = 0; p < 2; ++p) ad = mfma(fr_col(As, bSC, 32 * p, 16 * om, lane), fr_col(Os, bSR, 32 * p, 16 * on(u), lane), ad);
+      f32x4 x;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = ad[i] + gCv / gm[16 * om + 4 * g + i] * KdS[u][i];
+      put4(dUt + (16 * on(u) + j) * bSC + 16 * om + 4 * g, x);
+    }
+    __syncthreads();
+
+    // ---- dA = dO U^T (s <= r): D D terms, dA o D
+#pragma unroll
+    for (int w2 = 0; w2 < 2; ++w2) {
+      const int t2 = wv + 8 * w2;
+      const int mt = t2 >> 2, nt = t2 & 3;
+      f32x4 acc = zero4();
+      if (nt <= mt) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) acc = mfma(fr_row(Os, bSR, 16 * mt, 32 * p, lane), fr_col(Xt, bSC, 32 * p, 16 * nt, lane), acc);
+      }
+      const int s = 16 * nt + j;
+      float csum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mt + 4 * g + i;
+        const bool in = s <= r;
+        const float dA = in ? acc[i] : 0.f;
+        const float dd = dA * bf(As[r * bSC + s]);
+        const float rsum = sum16(dd);
+        if (j == 0 && nt <= mt) atomicAdd(&ddr[r], rsum);
+        csum += dd;
+        DAs[r * bSC + s] = static_cast<bf16>(in ? dA * __builtin_amdgcn_exp2f(fminf(lgs[r] - lgs[s], 0.f)) : 0.f);
+      }
+      csum += __shfl_xor(csum, 16, 64);
+      csum += __shfl_xor(csum, 32, 64);
+      if (g == 0 && nt <= mt) atomicAdd(&ddc[s], csum);
+    }
+    __syncthreads();
+    // dQ += (dA o D) K ; dK += (dA o D)^T Q
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        dQ[u] = mfma(fr_row(DAs, bSC, 16 * om, 32 * p, lane), fr_col(Ks, bSR, 32 * p, 16 * on(u), lane), dQ[u]);
+        dK[u] = mfma(fr_col(DAs, bSC, 32 * p, 16 * om, lane), fr_col(Qs, bSR, 32 * p, 16 * on(u), lane), dK[u]);
+      }
+    }
+    // dQ out (rows past the stream are not written)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * om + 4 * g + i;
+        if (r < Cc) dq[((size_t)(bi * T_ + i0 + window + r) * H + h) * bD + 16 * on(u) + j] = dQ[u][i];
+      }
+    __syncthreads();
+
+    // ---- Z = T^T dU: dV += diag(b) Z, db += Z.v; Z^T over U^T
+    f32x4 Zr[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int p = 0; p < 2; ++p) acc = mfma(fr_col(Tms, bSC, 32 * p, 16 * om, lane), fr_row(dUt, bSC, 16 * on(u), 32 * p, lane), acc);
+      Zr[u] = acc;
+      const int vv = 16 * on(u) + j;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * om + 4 * g + i;
+        dV[u][i] += bb[t] * acc[i];
+        const float x = sum16(acc[i] * bf(Vs[t * bSR + vv]));
+        if (j == 0) atomicAdd(&dbs[t], x);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) put4(Xt + (16 * on(u) + j) * bSC + 16 * om + 4 * g, Zr[u]);   // Z^T
+
+    // ---- S0 pass 2: Y = -Z S0^T -> dK += diag(b gamma) Y, rk = Y.k; Y^T
+    for (int kb = 0; kb < 4; ++kb) {
+      __syncthreads();
+      load_blk(blkA, S0g, kb);
+      __syncthreads();
+      f32x4 y = zero4();
+#pragma unroll
+      for (int p = 0; p < 4; ++p) y = mfma(fr_col(Xt, bSC, 32 * p, 16 * om, lane), fr_row(blkA, bSR, 16 * (wv & 1), 32 * p, lane), y);
+      y = -y;
+      const int kcol = 32 * kb + 16 * (wv & 1) + j;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * om + 4 * g + i;
+        dK[kb][i] += bb[t] * gm[t] * y[i];
+        const float x = sum16(y[i] * bf(Ks[t * bSR + kcol]));
+        if (j == 0) atomicAdd(&rk[t], x);
+      }
+      put4(Yt + kcol * bSC + 16 * om + 4 * g, y);
+    }
+    __syncthreads();
+    // ---- R = Z V^T + (Y K^T) diag(gamma), all 16 tiles
+#pragma unroll
+    for (int w2 = 0; w2 < 2; ++w2) {
+      const int t2 = wv + 8 * w2;
+      const int mt = t2 >> 2, nt = t2 & 3;
+      f32x4 zv = zero4(), yk = zero4();
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        zv = mfma(fr_col(Xt, bSC, 32 * p, 16 * mt, lane), fr_row(Vs, bSR, 16 * nt, 32 * p, lane), zv);
+        yk = mfma(fr_col(Yt, bSC, 32 * p, 16 * mt, lane), fr_row(Ks, bSR, 16 * nt, 32 * p, lane), yk);
+      }
+      const int s = 16 * nt + j;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Rs[(16 * mt + 4 * g + i) * bSC + s] = static_cast<bf16>(zv[i] + gm[s] * yk[i]);
+    }
+    __syncthreads();
+    // ---- dL = -R TB^T (s < r): D D, db, M + M^T
+#pragma unroll
+    for (int w2 = 0; w2 < 2; ++w2) {
+      const int t2 = wv + 8 * w2;
+      const int mt = t2 >> 2, nt = t2 & 3;
+      if (nt > mt) continue;
+      f32x4 dl = zero4(), kk = zero4();
+#pragma unroll
+      for (int p = 0; p < 2; ++p) dl = mfma(fr_row(Rs, bSC, 16 * mt, 32 * p, lane), fr_acc(TBs, bSC, 16 * nt, 32 * p, lane), dl);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) kk = mfma(fr_row(Ks, bSR, 16 * mt, 32 * p, lane), fr_row(Ks, bSR, 16 * nt, 32 * p, lane), kk);
+      const int s = 16 * nt + j;
+      float csum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mt + 4 * g + i;
+        const bool in = s < r;
+        const float dL = in ? -dl[i] : 0.f;
+        const float Dv = __builtin_amdgcn_exp2f(fminf(lgs[r] - lgs[s], 0.f));
+        const float dd = dL * bb[r] * Dv * kk[i];
+        const float rsum = sum16(dd);
+        const float dbx = sum16(dL * Dv * kk[i]);
+        if (j == 0) {
+          atomicAdd(&ddr[r], rsum);
+          atomicAdd(&dbs[r], dbx);
+        }
+        csum += dd;
+        const float mv = dL * bb[r] * Dv;
+        if (s <= r) {
+          Ms[r * bSC + s] = static_cast<bf16>(mv);
+          Ms[s * bSC + r] = static_cast<bf16>(mv);
+        }
+      }
+      csum += __shfl_xor(csum, 16, 64);
+      csum += __shfl_xor(csum, 32, 64);
+      if (g == 0) atomicAdd(&ddc[s], csum);
+    }
+    __syncthreads();
+    // ---- dK += (M + M^T) K
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) dK[u] = mfma(fr_row(Ms, bSC, 16 * om, 32 * p, lane), fr_col(Ks, bSR, 32 * p, 16 * on(u), lane), dK[u]);
+
+    // ---- gates (wave 0, lane r): d log a and db of this head's chunk rows
+    if (wv == 0) {
+      const int r = lane;
+      const float gr = gm[r];
+      const float e_over = ee[r] / gr;
+      float dg = dgam[r] + bb[r] * rk[r] - ee[r] * gCv / (gr * gr);
+      const float se = wave_sum(e_over);
+      if (r == bC - 1) dg += se + *sdot;
+      dg = dg * gr + ddr[r] - ddc[r];
+      // d log a_s = sum over r >= s of dg_r (suffix sum)
+      float x = dg;
+#pragma unroll
+      for (int m2 = 1; m2 < 64; m2 <<= 1) {
+        const float y = __shfl_down(x, m2, 64);
+        if (r + m2 < 64) x += y;
+      }
+      if (r < Cc) {
+        const size_t o = ((size_t)bi * T_ + i0 + r) * H + h;
+        da[o] = x / a[o];
+        db[o] = dbs[r] + gr * rk[r];
+      }
+    }
+  }
+  // dK, dV of the chunk's rows (summed over the query heads)
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * om + 4 * g + i;
+      if (t < Cc) {
+        const size_t o = ((size_t)(bi * T_ + i0 + t) * Hkv + gk) * bD + 16 * on(u) + j;
+        dk[o] = dK[u][i];
+        dv[o] = dV[u][i];
+      }
+    }
+}
+
+// ------------------------------------------------------------------------
+// Softmax branch, dq: one workgroup of 4 waves per (64-row query tile, query
+// head, sequence); wave w owns rows t0 + 16 w + j.  Keys come in blocks of
+// 32: the sink blocks (keys < n_sink, attended by rows t >= key) first, then
+// the window blocks from max(n_sink, t0 - window + 1) to t0 + 63.  Three
+// sweeps over the blocks: the row maxima, the sums and o (for D = do.o), then
+// dS = P (dP - D) into dq (and, on the sink blocks, the sinks' partial dK
+// and dV of the tile).  Scores s = q.k / sqrt(d); tiles S^T [key][row].
+constexpr int sQ = 0;                       // bf16 element offsets
+constexpr int sO = sQ + bC * bSR;           // w_swa do
+constexpr int sK = sO + bC * bSR;           // key block [32][bSR]
+constexpr int sV = sK + 32 * bSR;
+constexpr int sPT = sV + 32 * bSR;          // P^T [32][bSC] (sink blocks)
+constexpr int sST = sPT + 32 * bSC;         // dS^T [32][bSC]
+constexpr int sEnd = sST + 32 * bSC;
+constexpr int kSwaDqBytes = sEnd * 2;
+
+__device__ __forceinline__ float max_groups(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+__device__ __forceinline__ float sum_groups(float x) {
+  x += __shfl_xor(x, 16, 64);
+  return x + __shfl_xor(x, 32, 64);
+}
+
+__global__ __launch_bounds__(256) void swa_bwd_dq_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ d_o, float* __restrict__ dq, float* __restrict__ stats,
+    float* __restrict__ pk, float* __restrict__ pv, int T_, int H, int Hkv, int n_sink, int window,
+    float w_swa) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  bf16* sm = reinterpret_cast<bf16*>(smem_raw);
+  bf16* Qs = sm + sQ;
+  bf16* Os = sm + sO;
+  bf16* Kb = sm + sK;
+  bf16* Vb = sm + sV;
+  bf16* PT = sm + sPT;
+  bf16* ST = sm + sST;
+  const int tile = blockIdx.x;
+  const int h = blockIdx.y;
+  const int bi = blockIdx.z;
+  const int ntile = gridDim.x;
+  const int gk = h / (H / Hkv);
+  const int t0 = 64 * tile;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = wave_id();
+  const int g = lane >> 4;
+  const int j = lane & 15;
+  const int t = t0 + 16 * wv + j;            // this lane's query row
+  const float cs = kLog2e / sqrtf((float)bD);
+  const size_t kvrow = (size_t)Hkv * bD;
+  const bf16* kb = k + ((size_t)bi * T_ * Hkv + gk) * bD;
+  const bf16* vb = v + ((size_t)bi * T_ * Hkv + gk) * bD;
+
+  load_rows128(Qs, q + ((size_t)(bi * T_ + t0) * H + h) * bD, (size_t)H * bD, T_ - t0, false, 1.f, tid, 256);
+  load_rows128(Os, d_o + ((size_t)(bi * T_ + t0) * H + h) * bD, (size_t)H * bD, T_ - t0, true, w_swa, tid, 256);
+  const int nsb = (n_sink + 31) / 32;                       // sink blocks
+  const int wlo = max(n_sink, t0 - window + 1);
+  const int whi = min(t0 + 63, T_ - 1);
+  const int nwb = whi >= wlo ? (whi - wlo) / 32 + 1 : 0;    // window blocks
+  auto block_base = [&](int bidx) { return bidx < nsb ? 32 * bidx : wlo + 32 * (bidx - nsb); };
+  auto load_block = [&](int base) {
+    for (int n = tid; n < 32 * 16; n += 256) {
+      const int r = n >> 4, cc = (n & 15) * 8;
+      const size_t row = (size_t)min(base + r, T_ - 1);
+      *reinterpret_cast<bf16x8*>(Kb + r * bSR + cc) = *reinterpret_cast<const bf16x8*>(kb + row * kvrow + cc);
+      *reinterpret_cast<bf16x8*>(Vb + r * bSR + cc) = *reinterpret_cast<const bf16x8*>(vb + row * kvrow + cc);
+    }
+  };
+  auto attended = [&](int bidx, int kk) {
+    if (bidx < nsb) return kk < n_sink && kk <= t;
+    return kk >= max(n_sink, t - window + 1) && kk <= t;
+  };
+  auto scores = [&](f32x4 (&st)[2]) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      st[hf] = zero4();
+#pragma unroll
+      for (int p = 0; p < 4; ++p) st[hf] = mfma(fr_row(Kb, bSR, 16 * hf, 32 * p, lane), fr_row(Qs, bSR, 16 * wv, 32 * p, lane), st[hf]);
+    }
+  };
+  const int nb = nsb + nwb;
+  // ---- sweep 1: row maxima
+  float m = -INFINITY;
+  for (int bidx = 0; bidx < nb; ++bidx) {
+    const int base = block_base(bidx);
+    __syncthreads();
+    load_block(base);
+    __syncthreads();
+    f32x4 st[2];
+    scores(st);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (attended(bidx, base + 16 * hf + 4 * g + i)) m = fmaxf(m, st[hf][i]);
+  }
+  m = max_groups(m);
+  // ---- sweep 2: sums and o^T
+  float l = 0.f;
+  f32x4 ot[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) ot[dt] = zero4();
+  for (int bidx = 0; bidx < nb; ++bidx) {
+    const int base = block_base(bidx);
+    __syncthreads();
+    load_block(base);
+    __syncthreads();
+    f32x4 st[2];
+    scores(st);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool on = attended(bidx, base + 16 * hf + 4 * g + i);
+        st[hf][i] = on ? __builtin_amdgcn_exp2f((st[hf][i] - m) * cs) : 0.f;
+        l += st[hf][i];
+      }
+    const Frag<bf16> pf = frag_from_acc<bf16>(st[0], st[1]);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) ot[dt] = mfma(fr_col(Vb, bSR, 0, 16 * dt, lane), pf, ot[dt]);
+  }
+  l = sum_groups(l);
+  const float inv_l = l > 0.f ? 1.f / l : 0.f;
+  float Dr = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Dr += ot[dt][i] * bf(Os[(16 * wv + j) * bSR + 16 * dt + 4 * g + i]);
+  Dr = sum_groups(Dr) * inv_l;
+  const float lse = m * cs + __builtin_amdgcn_logf(l) * 1.f;   // log2 of the sum, m in score units
+  if (g == 0 && t < T_) {
+    float* sp = stats + (((size_t)bi * H + h) * T_ + t) * 2;
+    sp[0] = lse;
+    sp[1] = Dr;
+  }
+  // ---- sweep 3: dS = P (dP - D): dq, and the sinks' partial dK, dV
+  f32x4 dqt[8];
+#pragma unroll
+  for (int kt = 0; kt < 8; ++kt) dqt[kt] = zero4();
+  for (int bidx = 0; bidx < nb; ++bidx) {
+    const int base = block_base(bidx);
+    __syncthreads();
+    load_block(base);
+    __syncthreads();
+    f32x4 st[2], dp[2];
+    scores(st);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      dp[hf] = zero4();
+#pragma unroll
+      for (int p = 0; p < 4; ++p) dp[hf] = mfma(fr_row(Vb, bSR, 16 * hf, 32 * p, lane), fr_row(Os, bSR, 16 * wv, 32 * p, lane), dp[hf]);
+    }
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool on = attended(bidx, base + 16 * hf + 4 * g + i);
+        const float p = on ? __builtin_amdgcn_exp2f(st[hf][i] * cs - lse) : 0.f;
+        st[hf][i] = p;
+        dp[hf][i] = p * (dp[hf][i] - Dr);
+      }
+    const Frag<bf16> sf = frag_from_acc<bf16>(dp[0], dp[1]);
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) dqt[kt] = mfma(fr_col(Kb, bSR, 0, 16 * kt, lane), sf, dqt[kt]);
+    if (bidx < nsb) {
+      // the sink keys' partial dV = P^T do and dK = dS^T q over the tile's rows
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          PT[(16 * hf + 4 * g + i) * bSC + 16 * wv + j] = static_cast<bf16>(st[hf][i]);
+          ST[(16 * hf + 4 * g + i) * bSC + 16 * wv + j] = static_cast<bf16>(dp[hf][i]);
+        }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int id = wv + 4 * u;             // 32 tiles: (dV | dK, key tile, d tile)
+        const int which = id >> 4, kt2 = (id >> 3) & 1, dt = id & 7;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+          acc = mfma(fr_row(which ? ST : PT, bSC, 16 * kt2, 32 * p, lane),
+                     fr_col(which ? Qs : Os, bSR, 32 * p, 16 * dt, lane), acc);
+        float* dst = which ? pk : pv;
+        const float f = which ? cs / kLog2e : 1.f;   // dK carries 1 / sqrt(d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kk = base + 16 * kt2 + 4 * g + i;
+          if (kk < n_sink)
+            dst[((((size_t)bi * H + h) * ntile + tile) * n_sink + kk) * bD + 16 * dt + j] = acc[i] * f;
+        }
+      }
+    }
+  }
+  if (t < T_) {
+    const float f = cs / kLog2e;
+    float* dst = dq + ((size_t)(bi * T_ + t) * H + h) * bD;
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) {
+      f32x4 x = *reinterpret_cast<const f32x4*>(dst + 16 * kt + 4 * g);
+      x += dqt[kt] * f;
+      *reinterpret_cast<f32x4*>(dst + 16 * kt + 4 * g) = x;
+    }
+  }
+}
+
+// Softmax branch, dk and dv of the window keys (key >= n_sink): one
+// workgroup of 4 waves per (64-key tile, KV head, sequence); wave w owns
+// keys j0 + 16 w + (4 g + i).  Loops over the KV head's query heads and the
+// 32-row query blocks that attend the tile (rows key .. key + window - 1),
+// recomputing P from each row's saved log-sum-exp and D.
+constexpr int dKs = 0;
+constexpr int dVs = dKs + bC * bSR;
+constexpr int dQb = dVs + bC * bSR;
+constexpr int dOb = dQb + 32 * bSR;
+constexpr int dPT = dOb + 32 * bSR;          // per wave: P^T, dS^T [16][40] each
+constexpr int kPTS = 40;
+constexpr int dEnd = dPT + 4 * 2 * 16 * kPTS;
+constexpr int kSwaDkvBytes = dEnd * 2 + 2 * 32 * 4;
+
+__global__ __launch_bounds__(256) void swa_bwd_dkdv_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ d_o, const float* __restrict__ stats, float* __restrict__ dk,
+    float* __restrict__ dv, int T_, int H, int Hkv, int n_sink, int window, float w_swa) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  bf16* sm = reinterpret_cast<bf16*>(smem_raw);
+  bf16* Ks = sm + dKs;
+  bf16* Vs = sm + dVs;
+  bf16* Qb = sm + dQb;
+  bf16* Ob = sm + dOb;
+  float* lse_s = reinterpret_cast<float*>(smem_raw + dEnd * 2);
+  float* dr_s = lse_s + 32;
+  const int j0 = n_sink + 64 * blockIdx.x;
+  const int gk = blockIdx.y;
+  const int bi = blockIdx.z;
+  const int G = H / Hkv;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = wave_id();
+  const int g = lane >> 4;
+  const int j = lane & 15;
+  bf16* PTw = sm + dPT + wv * 2 * 16 * kPTS;
+  bf16* STw = PTw + 16 * kPTS;
+  const float cs = kLog2e / sqrtf((float)bD);
+  const size_t kvrow = (size_t)Hkv * bD;
+
+  load_rows128(Ks, k + ((size_t)(bi * T_ + j0) * Hkv + gk) * bD, kvrow, T_ - j0, false, 1.f, tid, 256);
+  load_rows128(Vs, v + ((size_t)(bi * T_ + j0) * Hkv + gk) * bD, kvrow, T_ - j0, false, 1.f, tid, 256);
+  const int qhi = min(T_ - 1, j0 + 63 + window - 1);
+  f32x4 dka[8], dva[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) dka[dt] = dva[dt] = zero4();
+  for (int m = 0; m < G; ++m) {
+    const int h = gk * G + m;
+    for (int qb0 = j0; qb0 <= qhi; qb0 += 32) {
+      __syncthreads();
+      for (int n = tid; n < 32 * 16; n += 256) {
+        const int r = n >> 4, cc = (n & 15) * 8;
+        const size_t row = (size_t)min(qb0 + r, T_ - 1);
+        bf16x8 x = *reinterpret_cast<const bf16x8*>(q + ((size_t)(bi * T_) + row) * H * bD + (size_t)h * bD + cc);
+        *reinterpret_cast<bf16x8*>(Qb + r * bSR + cc) = x;
+        bf16x8 y = *reinterpret_cast<const bf16x8*>(d_o + ((size_t)(bi * T_) + row) * H * bD + (size_t)h * bD + cc);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = static_cast<bf16>(bf(y[e]) * w_swa);
+        *reinterpret_cast<bf16x8*>(Ob + r * bSR + cc) = y;
+      }
+      if (tid < 32) {
+        const int tt = min(qb0 + tid, T_ - 1);
+        const float* sp = stats + (((size_t)bi * H + h) * T_ + tt) * 2;
+        lse_s[tid] = sp[0];
+        dr_s[tid] = sp[1];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh) {
+        f32x4 st = zero4(), dp = zero4();
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          st = mfma(fr_row(Ks, bSR, 16 * wv, 32 * p, lane), fr_row(Qb, bSR, 16 * qh, 32 * p, lane), st);
+          dp = mfma(fr_row(Vs, bSR, 16 * wv, 32 * p, lane), fr_row(Ob, bSR, 16 * qh, 32 * p, lane), dp);
+        }
+        const int rr = 16 * qh + j;
+        const int tq = qb0 + rr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kk = j0 + 16 * wv + 4 * g + i;
+          const bool on = kk < T_ && tq < T_ && kk <= tq && tq - window < kk;
+          const float p = on ? __builtin_amdgcn_exp2f(st[i] * cs - lse_s[rr]) : 0.f;
+          PTw[(4 * g + i) * kPTS + rr] = static_cast<bf16>(p);
+          STw[(4 * g + i) * kPTS + rr] = static_cast<bf16>(p * (dp[i] - dr_s[rr]));
+        }
+      }
+      // dV += P^T dO, dK += dS^T Q over the block's 32 rows (wave-local)
+      const Frag<bf16> pf = fr_row(PTw, kPTS, 0, 0, lane);
+      const Frag<bf16> sf = fr_row(STw, kPTS, 0, 0, lane);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        dva[dt] = mfma(pf, fr_col(Ob, bSR, 0, 16 * dt, lane), dva[dt]);
+        dka[dt] = mfma(sf, fr_col(Qb, bSR, 0, 16 * dt, lane), dka[dt]);
+      }
+    }
+  }
+  const float f = cs / kLog2e;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int kk = j0 + 16 * wv + 4 * g + i;
+    if (kk < T_) {
+      const size_t o = ((size_t)(bi * T_ + kk) * Hkv + gk) * bD;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        dk[o + 16 * dt + j] += dka[dt][i] * f;
+        dv[o + 16 * dt + j] += dva[dt][i];
+      }
+    }
+  }
+}
+
+// The sink keys' dK, dV: the partials of every query tile and query head.
+__global__ __launch_bounds__(128) void swa_bwd_sink_kernel(const float* __restrict__ pk,
+                                                           const float* __restrict__ pv,
+                                                           float* __restrict__ dk, float* __restrict__ dv,
+                                                           int T_, int H, int Hkv, int n_sink, int ntile) {
+  const int kk = blockIdx.x;
+  const int gk = blockIdx.y;
+  const int bi = blockIdx.z;
+  const int d = threadIdx.x;
+  if (kk >= T_) return;
+  const int G = H / Hkv;
+  float sk = 0.f, sv = 0.f;
+  for (int m = 0; m < G; ++m) {
+    const int h = gk * G + m;
+    for (int tl = 0; tl < ntile; ++tl) {
+      const size_t o = ((((size_t)bi * H + h) * ntile + tl) * n_sink + kk) * bD + d;
+      sk += pk[o];
+      sv += pv[o];
+    }
+  }
+  const size_t o = ((size_t)(bi * T_ + kk) * Hkv + gk) * bD + d;
+  dk[o] += sk;
+  dv[o] += sv;
+}
+
+__global__ void zero_kernel(float* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0.f;
+}
+
+hipError_t zero(float* p, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 8192);
+  hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+BwdWorkspace gdn_bwd_layout(void* base, int B, int T, int H, int n_sink, int window) {
+  const int nch = gdn_stream_chunks(T, n_sink, window);
+  const size_t items = (size_t)B * H * nch;
+  const size_t al = 256;
+  auto up = [&](size_t x) { return (x + al - 1) / al * al; };
+  BwdWorkspace w;
+  unsigned char* p = static_cast<unsigned char*>(base);
+  w.light = gdn_workspace_layout(base, B, H, nch, bD, sizeof(bf16), false);
+  size_t off = up(w.light.bytes);
+  w.tm = p + off;
+  off += up(items * bC * bC * 2);
+  w.s0 = p + off;
+  off += up(items * bD * bD * 2);
+  w.ds1 = p + off;
+  off += up(items * bD * bD * 2);
+  w.stats = reinterpret_cast<float*>(p + off);
+  off += up((size_t)B * H * T * 2 * 4);
+  const int ntile = (T + 63) / 64;
+  const size_t np = (size_t)B * H * ntile * n_sink * bD;
+  w.pk = reinterpret_cast<float*>(p + off);
+  off += up(np * 4);
+  w.pv = reinterpret_cast<float*>(p + off);
+  off += up(np * 4);
+  w.bytes = off;
+  return w;
+}
+
+hipError_t launch_gdn_backward(const BwdArgs& a, hipStream_t s) {
+  const int nch = gdn_stream_chunks(a.T, a.n_sink, a.window);
+  const BwdWorkspace w = gdn_bwd_layout(a.workspace, a.B, a.T, a.H, a.n_sink, a.window);
+  const size_t nq = (size_t)a.B * a.T * a.H * bD;
+  const size_t nkv = (size_t)a.B * a.T * a.Hkv * bD;
+  const size_t ng = (size_t)a.B * a.T * a.H;
+  hipError_t e;
+  if ((e = zero(a.dq, nq, s)) != hipSuccess) return e;
+  if ((e = zero(a.dk, nkv, s)) != hipSuccess) return e;
+  if ((e = zero(a.dv, nkv, s)) != hipSuccess) return e;
+  if ((e = zero(a.da, ng, s)) != hipSuccess) return e;
+  if ((e = zero(a.db, ng, s)) != hipSuccess) return e;
+  if (nch > 0) {
+    PrefillArgs p{a.q, a.k, a.v, a.a, a.b, nullptr, nullptr, a.B, a.T, a.H, a.Hkv, bD, a.n_sink,
+                  a.window, 1, 0, 0, a.workspace};
+    if ((e = launch_gdn_prep_tm(p, nch, w.tm, s)) != hipSuccess) return e;
+    p.ckpt = w.s0;
+    p.prepared = true;
+    if ((e = launch_linear_ckpt(p, s)) != hipSuccess) return e;
+    const int G = a.H / a.Hkv;
+    e = hipFuncSetAttribute((const void*)gdn_bwd_rev_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kRevBytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gdn_bwd_rev_kernel, dim3(xcd_grouped_grid((long long)a.B * a.Hkv, G)), dim3(512), kRevBytes, s,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.d_o, (const bf16*)w.light.tb,
+                       w.light.g, a.d_state, (bf16*)w.ds1, a.B, a.T, a.H, a.Hkv, a.n_sink, a.window, nch,
+                       a.w_lin);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)gdn_bwd_chunk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kChunkBytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gdn_bwd_chunk_kernel, dim3(nch, a.Hkv, a.B), dim3(512), kChunkBytes, s,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.a, (const bf16*)a.d_o,
+                       (const bf16*)w.light.tb, (const bf16*)w.tm, w.light.g, a.b, (const bf16*)w.s0,
+                       (const bf16*)w.ds1, a.dq, a.dk, a.dv, a.da, a.db, a.B, a.T, a.H, a.Hkv, a.n_sink,
+                       a.window, nch, a.w_lin);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (a.T > 0) {
+    const int ntile = (a.T + 63) / 64;
+    e = hipFuncSetAttribute((const void*)swa_bwd_dq_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kSwaDqBytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(swa_bwd_dq_kernel, dim3(ntile, a.H, a.B), dim3(256), kSwaDqBytes, s, (const bf16*)a.q,
+                       (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.d_o, a.dq, w.stats, w.pk, w.pv,
+                       a.T, a.H, a.Hkv, a.n_sink, a.window, a.w_swa);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.T > a.n_sink) {
+      e = hipFuncSetAttribute((const void*)swa_bwd_dkdv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kSwaDkvBytes);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(swa_bwd_dkdv_kernel, dim3((a.T - a.n_sink + 63) / 64, a.Hkv, a.B), dim3(256), kSwaDkvBytes, s,
+                         (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.d_o, w.stats,
+                         a.dk, a.dv, a.T, a.H, a.Hkv, a.n_sink, a.window, a.w_swa);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (a.n_sink > 0) {
+      hipLaunchKernelGGL(swa_bwd_sink_kernel, dim3(std::min(a.n_sink, a.T), a.Hkv, a.B), dim3(128), 0, s,
+                         (const float*)w.pk, (const float*)w.pv, a.dk, a.dv, a.T, a.H, a.Hkv, a.n_sink, ntile);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace gdn

@@ -252,13 +252,16 @@ struct PrepSmem {
 // into registers, so the only LDS a chunk needs is the 64 x 64 fp32 solve
 // buffer (plus, for the full preparation, K^T, TBG and A staging).  No
 // workgroup barrier: the wave's own LDS operations complete in program order.
-template <class T, int D, bool FULL, bool DEV = false>
+// TM (light preparation only): also write Tm itself, [64][64] in natural
+// column order, to wtm (the backward pass needs Tm^T products).
+template <class T, int D, bool FULL, bool DEV = false, bool TM = false>
 __device__ __forceinline__ void gdn_prep_chunk(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ a, const float* __restrict__ b, T* __restrict__ wtb,
     T* __restrict__ wwm, T* __restrict__ wktg, T* __restrict__ wa,
     float* __restrict__ wut, float* __restrict__ wg, int T_, int H, int Hkv, int n_sink, int window,
-    int nch, int c, int h, int bi, unsigned char* smem_raw) {
+    int nch, int c, int h, int bi, unsigned char* smem_raw, T* __restrict__ wtm = nullptr) {
+  static_assert(!(TM && FULL), "Tm is written by the light preparation");
   using SM = PrepSmem<T, D, FULL>;
   using LL = typename SM::LL;
   constexpr int EPC = 16 / (int)sizeof(T);     // elements per 16-byte piece
@@ -457,6 +460,7 @@ __device__ __forceinline__ void gdn_prep_chunk(
         const int r = 16 * R + 4 * m + rr;
         const f32x4 x = (s0 >> 4) <= R ? tm[R][m] * bb : zero4();
         put4v<DEV>(tb, r * kC + acc_pos(s0), x);
+        if constexpr (TM) put4v<DEV>(wtm + ci * (kC * kC), r * kC + s0, (s0 >> 4) <= R ? tm[R][m] : zero4());
       }
   }
   put1f<DEV>(wg + ci * (2 * kC), lane, lgs[lane]);

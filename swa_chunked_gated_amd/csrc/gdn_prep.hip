@@ -14,13 +14,13 @@ namespace {
 using prep::kC;
 using prep::PrepSmem;
 
-template <class T, int D, bool FULL>
+template <class T, int D, bool FULL, bool TM = false>
 __global__ __launch_bounds__(64) void gdn_prep_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ a, const float* __restrict__ b, T* __restrict__ wtb,
     T* __restrict__ wwm, T* __restrict__ wktg, T* __restrict__ wa,
     float* __restrict__ wut, float* __restrict__ wg, int T_, int H, int Hkv, int n_sink,
-    int window, int nch) {
+    int window, int nch, T* __restrict__ wtm) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   // the G query heads of one (chunk, KV head) run on one XCD and share the
   // chunk's K rows through its L2; y is the sequence
@@ -29,8 +29,8 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(
   if (!xcd_grouped(blockIdx.x, G, nch * Hkv, unit, member)) return;
   const int c = unit % nch;
   const int h = (unit / nch) * G + member;
-  prep::gdn_prep_chunk<T, D, FULL>(q, k, v, a, b, wtb, wwm, wktg, wa, wut, wg, T_, H, Hkv,
-                                   n_sink, window, nch, c, h, blockIdx.y, smem_raw);
+  prep::gdn_prep_chunk<T, D, FULL, false, TM>(q, k, v, a, b, wtb, wwm, wktg, wa, wut, wg, T_, H, Hkv,
+                                              n_sink, window, nch, c, h, blockIdx.y, smem_raw, wtm);
 }
 
 template <class T, int D, bool FULL>
@@ -43,7 +43,7 @@ hipError_t launch_prep_t(const PrefillArgs& p, int nch, hipStream_t s) {
   const dim3 grid(xcd_grouped_grid((long long)nch * p.Hkv, p.H / p.Hkv), p.B);
   hipLaunchKernelGGL(kern, grid, dim3(64), SM::bytes, s, (const T*)p.q,
                      (const T*)p.k, (const T*)p.v, p.a, p.b, (T*)w.tb, (T*)w.wm,
-                     (T*)w.ktg, (T*)w.a, w.ut, w.g, p.T, p.H, p.Hkv, p.n_sink, p.window, nch);
+                     (T*)w.ktg, (T*)w.a, w.ut, w.g, p.T, p.H, p.Hkv, p.n_sink, p.window, nch, (T*)nullptr);
   return hipGetLastError();
 }
 
@@ -90,6 +90,21 @@ GdnWorkspace gdn_workspace_layout(void* base, int B, int H, int nch, int D, size
   off += full ? n * (D / 16) * sizeof(uint64_t) : 0;
   w.bytes = off;
   return w;
+}
+
+hipError_t launch_gdn_prep_tm(const PrefillArgs& p, int nch, void* tm, hipStream_t s) {
+  if (!p.bf16 || p.D != 128) return hipErrorInvalidValue;
+  using SM = PrepSmem<bf16, 128, false>;
+  auto kern = gdn_prep_kernel<bf16, 128, false, true>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, SM::bytes);
+  if (e != hipSuccess) return e;
+  const GdnWorkspace w = gdn_workspace_layout(p.workspace, p.B, p.H, nch, 128, sizeof(bf16), false);
+  const dim3 grid(xcd_grouped_grid((long long)nch * p.Hkv, p.H / p.Hkv), p.B);
+  hipLaunchKernelGGL(kern, grid, dim3(64), SM::bytes, s, (const bf16*)p.q, (const bf16*)p.k,
+                     (const bf16*)p.v, p.a, p.b, (bf16*)w.tb, (bf16*)nullptr, (bf16*)nullptr,
+                     (bf16*)nullptr, (float*)nullptr, w.g, p.T, p.H, p.Hkv, p.n_sink, p.window, nch,
+                     (bf16*)tm);
+  return hipGetLastError();
 }
 
 hipError_t launch_gdn_prep(const PrefillArgs& p, int nch, hipStream_t s) {

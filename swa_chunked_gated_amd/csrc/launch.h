@@ -26,6 +26,7 @@ struct PrefillArgs {
   float w_swa = 1.f;
   bool prepared = false;   // the workspace already holds the chunk preparation
   int dgd = 0;   // with gla = 1: the delta rule with a diagonal gate (b used)
+  void* ckpt = nullptr;    // backward pass: states entering each chunk (bf16 [d][d])
 };
 
 // Workspace of the gated delta rule prefill, per (sequence, head, chunk), as
@@ -171,6 +172,12 @@ SegWorkspace gdn_seg_layout(void* base, int B, int H, int nch);
 hipError_t launch_gdn_segmented(const PrefillArgs& p, hipStream_t s);
 // Chunk preparation of the gated delta rule / of GLA into a.workspace (nch chunks).
 hipError_t launch_gdn_prep(const PrefillArgs& a, int nch, hipStream_t s);
+// The backward pass's preparation (bf16, d = 128): the light preparation
+// into a.workspace, plus Tm [64][64] (natural order) per chunk into tm.
+hipError_t launch_gdn_prep_tm(const PrefillArgs& a, int nch, void* tm, hipStream_t s);
+// The backward pass's forward sweep (bf16 GDN, d = 128, light preparation
+// in a.workspace): writes the state entering every chunk to a.ckpt.
+hipError_t launch_linear_ckpt(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_gla_prep(const PrefillArgs& a, int nch, hipStream_t s);
 // Softmax branch: writes every row of o, adding the value o already holds
 // on rows t >= add_from.
@@ -186,6 +193,45 @@ hipError_t launch_shortconv(const ShortConvArgs& a, hipStream_t s);
 hipError_t launch_shortconv_decode(const ShortConvArgs& a, float* const hist[3], const int* pos,
                                    hipStream_t s);
 hipError_t launch_shortconv_history(const ShortConvArgs& a, float* const hist[3], hipStream_t s);
+
+// Backward pass (bf16 GDN at d = 128): gradients of sum(do * o) +
+// sum(d_state * S_final) into fp32 dq [B,T,H,d], dk, dv [B,T,Hkv,d], da, db
+// [B,T,H] (overwritten).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* a;
+  const float* b;
+  const void* d_o;
+  const float* d_state;     // may be null (zero)
+  float* dq;
+  float* dk;
+  float* dv;
+  float* da;
+  float* db;
+  int B, T, H, Hkv;
+  int n_sink, window;
+  float w_lin, w_swa;
+  void* workspace;
+};
+// Its workspace: the light preparation's, then per (sequence, head, chunk)
+// Tm (bf16 [64][64]), the state entering the chunk and the gradient of the
+// state leaving it (bf16 [128][128] each), then per (sequence, head, row) the
+// softmax log-sum-exp and D = do.o, and the sink keys' partial dK, dV per
+// 64-row query tile (fp32).
+struct BwdWorkspace {
+  GdnWorkspace light;
+  void* tm;
+  void* s0;
+  void* ds1;
+  float* stats;
+  float* pk;
+  float* pv;
+  size_t bytes;
+};
+BwdWorkspace gdn_bwd_layout(void* base, int B, int T, int H, int n_sink, int window);
+hipError_t launch_gdn_backward(const BwdArgs& a, hipStream_t s);
 
 // Time bound of the in-kernel waits on flags published by other workgroups
 // of the same launch (100 MHz real-time counter ticks), and faults injected

@@ -87,8 +87,10 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
     const T* __restrict__ w0, const T* __restrict__ w1, const T* __restrict__ w2,
     const T* __restrict__ w3, const T* __restrict__ w4, const float* __restrict__ wf, T* __restrict__ o,
     float* __restrict__ state_out, int T_, int H, int Hkv, int n_sink, int window, int flags,
-    float w_lin) {
-  // w_lin weighs the linear branch in o (1 for the plain sum).
+    float w_lin, T* __restrict__ ckpt) {
+  // w_lin weighs the linear branch in o (1 for the plain sum).  ckpt (the
+  // backward pass's forward sweep): the state entering each chunk, in T,
+  // [d_k][d_v] row-major per (sequence, head, chunk).
   // chunk preparation results (workspace), per (sequence, head, chunk):
   //   GDN, light: w0 = Tm diag(b), wf = g (log2), gamma (w1 unused)
   //   GLA:        w0 = Q 2^G, w1 = (K 2^{G_C - G})^T, w2 = A, wf = 2^{G_C}
@@ -318,6 +320,16 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
   for (int c = 0; c < nch; ++c) {
     const int i0 = n_sink + c * kC;
     const int Cc = min(kC, iend - i0);
+    if (ckpt) {
+      T* Sc = ckpt + (chain * nch + c) * (size_t)(D * D);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            Sc[(16 * mt + 4 * lg + i) * D + c0 + cw + 16 * nt + l16] = from_f32<T>(S[mt][nt][i]);
+    }
     lds_barrier();          // previous chunk's LDS reads are done
     commit();
     lds_barrier();
@@ -653,7 +665,7 @@ hipError_t launch_linear_t(const PrefillArgs& p, hipStream_t s) {
   }
   hipLaunchKernelGGL(kern, grid, dim3(64 * NW), SM::bytes, s, (const T*)p.q, (const T*)p.k,
                      (const T*)p.v, w0, w1, w2, w3, w4, wf, (T*)p.o, p.state_out, p.T, p.H, p.Hkv,
-                     p.n_sink, p.window, p.flags, p.w_lin);
+                     p.n_sink, p.window, p.flags, p.w_lin, (T*)p.ckpt);
   return hipGetLastError();
 }
 
@@ -686,6 +698,11 @@ hipError_t launch_linear_m(const PrefillArgs& p, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_linear_ckpt(const PrefillArgs& p, hipStream_t s) {
+  if (!p.bf16 || p.gla || p.D != 128 || !p.ckpt) return hipErrorInvalidValue;
+  return launch_linear_d<bf16, 0>(p, s);
+}
 
 bool separate_preparation(const PrefillArgs& p) {
   return gdn_stream_chunks(p.T, p.n_sink, p.window) > 0 &&

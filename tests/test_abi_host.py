@@ -78,10 +78,11 @@ def test_workspace_query(lib):
         return B * H * nch * per
     # few chains, bf16 d = 128, both branches, window <= 128, <= 16 sinks:
     # the segmented scan's light preparation (TB, gates), then per (segment,
-    # chain) M bf16, N and the incoming state fp32, [128][128] each; 32
-    # chains over 63 chunks: 8 segments
+    # chain) M bf16, N and the incoming state fp32, [128][128] each (the
+    # states with one spare segment); 32 chains over 63 chunks: 8 segments
     light = 2016 * (64 * 64 * 2 + 512)
-    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 3) == (OK, light + 8 * 32 * 128 * 128 * (2 + 4 + 4))
+    seg = 8 * 32 * 128 * 128 * (2 + 4 + 4) + 32 * 128 * 128 * 4
+    assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 3) == (OK, light + seg)
     # the same shape, linear branch and state only: the one-launch path's
     # full preparation
     assert ws(lib, 1, 4096, 32, 8, 128, 128, 8, 56, BF16, DELTA, 5) == (OK, gdn_bytes(1, 4096, 32, 128, 2))
@@ -335,3 +336,59 @@ def test_noalloc_prefill_validation(lib):
                                           3, None) == EINVAL       # q NULL
     assert lib.gdn_hybrid_prefill_noalloc(*p, 1, 100, 4, 2, 128, 128, 8, 56, F32, DELTA, 1,
                                           None) == EUNSUP          # fp32 linear branch at d = 128
+
+
+# ------------------------------------------------------------- backward pass
+
+def bws(lib, B=1, T=300, H=4, Hkv=1, d=128, n_sink=8, window=56, dtype=BF16, update=DELTA):
+    n = ctypes.c_size_t(99)
+    rc = lib.gdn_hybrid_prefill_backward_workspace(B, T, H, Hkv, d, d, n_sink, window, dtype,
+                                                   update, ctypes.byref(n))
+    return rc, n.value
+
+
+def bwd(lib, B=1, T=300, H=4, Hkv=1, d=128, n_sink=8, window=56, dtype=BF16, update=DELTA,
+        ptrs=None, dstate=None, ws_ptr=None, ws_bytes=1 << 40, w=(1.0, 1.0)):
+    p = ptrs if ptrs is not None else [FAKE] * 11
+    q, k, v, a, b, do, dq, dk, dv, da, db = p
+    return lib.gdn_hybrid_prefill_backward(q, k, v, a, b, do, dstate, dq, dk, dv, da, db, B, T, H,
+                                           Hkv, d, d, n_sink, window, dtype, update, w[0], w[1],
+                                           ws_ptr if ws_ptr is not None else ctypes.c_void_p(0x100000),
+                                           ws_bytes, None)
+
+
+def test_backward_workspace_query(lib):
+    rc, n = bws(lib)
+    assert rc == OK
+    # light preparation (TB bf16 + 128 gate floats), Tm (bf16 64 x 64), the
+    # states entering and the gradients leaving each chunk (bf16 128 x 128),
+    # per-row softmax statistics (2 floats), sink partials (2 x n_sink x 128
+    # floats per 64-row query tile), each part 256-byte aligned
+    items = 1 * 4 * 4                      # T = 300, budget 64: 4 chunks
+    up = lambda x: (x + 255) // 256 * 256
+    want = up(items * (64 * 64 * 2 + 512)) + up(items * 64 * 64 * 2) + 2 * up(items * 128 * 128 * 2) \
+        + up(4 * 300 * 2 * 4) + 2 * up(4 * 5 * 8 * 128 * 4)
+    assert n == want
+    assert bws(lib, dtype=F32)[0] == EUNSUP
+    assert bws(lib, d=64)[0] == EUNSUP
+    assert bws(lib, update=GLA)[0] == EUNSUP
+    assert bws(lib, update=2)[0] == EUNSUP
+    assert bws(lib, H=4, Hkv=3)[0] == EINVAL
+    assert bws(lib, window=0)[0] == EINVAL
+    assert lib.gdn_hybrid_prefill_backward_workspace(1, 300, 4, 1, 128, 128, 8, 56, BF16, DELTA, None) == EINVAL
+
+
+def test_backward_validation(lib):
+    assert bwd(lib, dtype=F32) == EUNSUP
+    assert bwd(lib, d=64) == EUNSUP
+    for i in range(11):
+        p = [FAKE] * 11
+        p[i] = None
+        assert bwd(lib, ptrs=p) == EINVAL, i
+    p = [FAKE] * 11
+    p[3] = ctypes.c_void_p(0x1008)          # a misaligned
+    assert bwd(lib, ptrs=p) == EINVAL
+    assert bwd(lib, dstate=ctypes.c_void_p(0x1004)) == EINVAL
+    assert bwd(lib, w=(float("nan"), 1.0)) == EINVAL
+    assert bwd(lib, ws_bytes=16) == EWS
+    assert bwd(lib, ws_ptr=ctypes.c_void_p(0x100008)) == EINVAL    # workspace not 256-aligned
