@@ -26,7 +26,9 @@ core, at most 16).
 "also" carries the other workloads, each with its own roofline and oracle
 baseline: the tiny fp32 layer, the LLaMA3.1-8B-shaped layer (T=4096), decode
 (B=256, 1000 consecutive steps, HBM roofline), the Qwen3-32B-shaped stack
-(short conv + GDN, short conv + GLA, budget 896) and its serving step.
+(short conv + GDN, short conv + GLA, budget 896) and its serving step, and
+the backward pass (the training path) at the LLaMA-shaped and long-context
+shapes.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--only headline|...]
 """
@@ -89,6 +91,19 @@ def swa_flops(w, T=None):
     T = w.T if T is None else T
     t = np.arange(T)
     return w.B * w.H * int(np.sum(4 * np.minimum(t + 1, w.budget))) * w.d
+
+
+def backward_flops(w):
+    """The backward pass's algorithmic work (gated delta rule): per chunk
+    and query head the gradient products of the chunk form, 6 C d^2 + 9 C^2 d
+    + C^3 multiply-adds (dU, dS, dQ, dK^T terms over d^2; the score-shaped
+    and UT-transform terms over C^2 d; the C^3 one for dL), twice the
+    forward's chunk work; the softmax branch 10 min(t+1, N) d per query row
+    and head (scores, dP, dQ, dK, dV: 2.5 times its forward)."""
+    stream = max(0, w.T - w.budget)
+    nch = -(-stream // CHUNK)
+    lin = w.B * w.H * nch * 2 * (6 * CHUNK * w.d ** 2 + 9 * CHUNK ** 2 * w.d + CHUNK ** 3)
+    return lin + 2.5 * swa_flops(w)
 
 
 def prefill_bytes(w):
@@ -244,6 +259,18 @@ def _oracle_prefill_head(h):
     return h
 
 
+def _oracle_backward_head(h):
+    """Oracle backward (both branches, final-state gradient) of query head h
+    of the sample."""
+    from oracle import backward as OB
+    w, f = _CPU["w"], _CPU["f"]
+    g = h // (w.H // w.Hkv)
+    OB.hybrid_prefill_backward(f["q"][:, :, h:h + 1], f["k"][:, :, g:g + 1], f["v"][:, :, g:g + 1],
+                               f["a"][:, :, h:h + 1], f["b"][:, :, h:h + 1], w.n_sink, w.window,
+                               f["d_o"][:, :, h:h + 1], f["d_state"][:, h:h + 1])
+    return h
+
+
 def _oracle_decode_seqs(sl):
     """Oracle decode steps of the sample's sequences sl[0]:sl[1]."""
     from oracle import hybrid as O
@@ -257,11 +284,12 @@ def _oracle_decode_seqs(sl):
     return s1 - s0
 
 
-def cpu_baseline(name, cores, T_sample=None, heads=None, steps=None):
+def cpu_baseline(name, cores, T_sample=None, heads=None, steps=None, backward=False):
     """The oracle on a bounded sample of workload `name`: prefill runs
     sequence 0 (first T_sample tokens, the listed query heads), one task per
-    head; decode runs `steps` steps of every sequence, one task per slice of
-    sequences.  Rate in the workload's unit (tokens/s; steps/s)."""
+    head (with backward, the backward pass instead); decode runs `steps`
+    steps of every sequence, one task per slice of sequences.  Rate in the
+    workload's unit (tokens/s; steps/s)."""
     import torch
     from workloads import WORKLOADS, make_decode_inputs, make_prefill_inputs
 
@@ -274,6 +302,8 @@ def cpu_baseline(name, cores, T_sample=None, heads=None, steps=None):
         _CPU["steps"] = steps
     else:
         inp = make_prefill_inputs(w, T=T_sample, B=1)
+        if backward:
+            inp.update(backward_grads(w, T_sample, 1))
     _CPU["f"] = {x: (t.to(torch.float64).numpy() if t.is_floating_point() else t.numpy())
                  for x, t in inp.items()}
     ctx = mp.get_context("fork")
@@ -285,7 +315,8 @@ def cpu_baseline(name, cores, T_sample=None, heads=None, steps=None):
             tasks = [(s, min(s + per, w.B)) for s in range(0, w.B, per)]
             pool.map(_oracle_decode_seqs, tasks, chunksize=1)
         else:
-            pool.map(_oracle_prefill_head, list(heads), chunksize=1)
+            pool.map(_oracle_backward_head if backward else _oracle_prefill_head, list(heads),
+                     chunksize=1)
         wall = time.perf_counter() - t0
     _CPU.clear()
     res = {"kind": "oracle", "cores": cores, "cpu": _cpu_model(),
@@ -297,6 +328,8 @@ def cpu_baseline(name, cores, T_sample=None, heads=None, steps=None):
                           f"processes), {wall:.2f} s wall")
     else:
         conv = "short conv + " if w.shortconv else ""
+        if backward:
+            conv = "the backward pass (gradients of q, k, v, a, b) of "
         res.update(value=T_sample / wall, unit="tokens/s",
                    sample=f"sequence 0, tokens 0..{T_sample - 1}, {len(heads)} of {w.H} query heads"
                           f"{'' if len(heads) == w.H else ' (rate scaled to all heads)'}: {conv}both "
@@ -305,6 +338,18 @@ def cpu_baseline(name, cores, T_sample=None, heads=None, steps=None):
         if len(heads) != w.H:
             res["value"] *= len(heads) / w.H
     return res
+
+
+def backward_grads(w, T=None, B=None, device="cpu"):
+    """Seeded upstream gradients of the backward workloads: d_o ~ N(0, 0.5^2)
+    in the I/O type and the final state's gradient ~ N(0, 0.05^2) fp32."""
+    import torch
+    T = w.T if T is None else T
+    B = w.B if B is None else B
+    g = torch.Generator(device="cpu").manual_seed(1234)
+    d_o = (torch.randn(B, T, w.H, w.d, generator=g) * 0.5).to(w.torch_dtype)
+    d_state = torch.randn(B, w.H, w.d, w.d, generator=g) * 0.05
+    return {"d_o": d_o.to(device), "d_state": d_state.to(device)}
 
 
 CPU_SAMPLES = {
@@ -317,6 +362,13 @@ CPU_SAMPLES = {
     "dgd_b8_t8192": dict(T_sample=8192, heads=range(32)),
     "decode_b256": dict(steps=20),
 }
+# backward pass: (tokens of sequence 0, query heads)
+CPU_BWD_SAMPLES = {
+    "llama8b_t4096": dict(T_sample=4096, heads=range(16)),
+    "longctx_b8_t32768": dict(T_sample=4096, heads=range(16)),
+}
+BWD_KERNELS = ("gdn_prep_kernel+linear_chunk_kernel+gdn_bwd_rev_kernel+gdn_bwd_chunk_kernel+"
+               "swa_bwd_dq_kernel+swa_bwd_dkdv_kernel+swa_bwd_sink_kernel")
 
 
 # ------------------------------------------------------------- GPU legs
@@ -468,6 +520,39 @@ def bench_prefill(name, steps, warmup, parts=True):
     return res
 
 
+def bench_backward(name, reps=20, warmup=3):
+    """The backward pass at workload `name`'s shape (inputs, upstream
+    gradients and the workspace resident), event-timed per call, median of
+    `reps`."""
+    import torch
+    import swa_chunked_gated_amd as gl
+    from workloads import WORKLOADS, make_prefill_inputs
+
+    w = WORKLOADS[name]
+    inp = make_prefill_inputs(w, device="cuda")
+    gr = backward_grads(w, device="cuda")
+    nws = gl.prefill_backward_workspace_bytes(w.B, w.T, w.H, w.Hkv, w.d, w.n_sink, w.window)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+
+    def call():
+        gl.hybrid_prefill_backward(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], w.n_sink,
+                                   w.window, gr["d_o"], gr["d_state"], workspace=ws)
+
+    med, mean = time_call(call, max(20, reps), warmup)
+    flops = backward_flops(w)
+    achieved = flops / (med * 1e-3)
+    return {
+        "workload": f"{name} backward (B={w.B}, T={w.T}, H={w.H}, Hkv={w.Hkv}, d={w.d}, "
+                    f"budget {w.n_sink}+{w.window})",
+        "ms_per_step": med, "event_ms_mean": mean, "tokens_per_s": w.B * w.T / (med * 1e-3),
+        "algorithmic_gflop": flops / 1e9, "workspace_bytes": nws,
+        "roofline": {"kernel": BWD_KERNELS, "bound": "mfma", "achieved": achieved / 1e12,
+                     "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16,
+                     "traffic": None, "algorithmic_flops_per_launch": flops,
+                     "launch_ms_median": med},
+    }
+
+
 def bench_decode(steps=1000, warmup=10):
     import torch
     import swa_chunked_gated_amd as gl
@@ -589,7 +674,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default="all",
                     choices=["all", "headline", "longctx", "llama", "tiny", "dgd", "decode", "qwen32b",
-                             "qwen32b_decode", "copy"])
+                             "qwen32b_decode", "copy", "backward"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parts", action="store_true",
                     help="time the layer only, not its calls one by one (profiling runs)")
@@ -603,7 +688,7 @@ def main():
 
     # single-workload legs (profiling and counter runs)
     single = {"longctx": HEADLINE, "llama": "llama8b_t4096", "tiny": "tiny_fp32", "dgd": "dgd_b8_t8192"}
-    if args.only in single or args.only in ("decode", "qwen32b", "qwen32b_decode", "copy"):
+    if args.only in single or args.only in ("decode", "qwen32b", "qwen32b_decode", "copy", "backward"):
         import torch
         if not torch.cuda.is_available():
             print("bench.py needs a GPU", file=sys.stderr)
@@ -617,6 +702,10 @@ def main():
             out = bench_qwen_decode(steps=args.steps, warmup=args.warmup)
         elif args.only == "copy":
             out = bench_copy()
+        elif args.only == "backward":
+            for n in ("llama8b_t4096", HEADLINE):
+                print(json.dumps(bench_backward(n, args.steps, args.warmup)), flush=True)
+            return
         else:
             for n in ("qwen32b_t8192_gdn", "qwen32b_t8192_gla"):
                 print(json.dumps(bench_prefill(n, args.steps, args.warmup, parts=parts)), flush=True)
@@ -634,6 +723,11 @@ def main():
             cpu[n] = cpu_baseline(n, cores, **CPU_SAMPLES[n])
             print(f"# cpu_baseline {n}: {cpu[n]['value']:.1f} {cpu[n]['unit']} "
                   f"({cpu[n]['seconds']:.1f} s)", file=sys.stderr, flush=True)
+        if args.only == "all":
+            for n in CPU_BWD_SAMPLES:
+                cpu[n + "_backward"] = cpu_baseline(n, cores, backward=True, **CPU_BWD_SAMPLES[n])
+                print(f"# cpu_baseline {n} backward: {cpu[n + '_backward']['value']:.1f} tokens/s "
+                      f"({cpu[n + '_backward']['seconds']:.1f} s)", file=sys.stderr, flush=True)
 
     import torch
     if not torch.cuda.is_available():
@@ -649,6 +743,10 @@ def main():
             also[n] = bench_prefill(n, args.steps, args.warmup, parts=True)
             also[n]["cpu_baseline"] = cpu.get(n)
             print(f"# {n} done", file=sys.stderr, flush=True)
+        for n in CPU_BWD_SAMPLES:
+            also[n + "_backward"] = bench_backward(n)
+            also[n + "_backward"]["cpu_baseline"] = cpu.get(n + "_backward")
+            print(f"# {n} backward done", file=sys.stderr, flush=True)
         also["decode_b256"] = bench_decode()
         also["decode_b256"]["cpu_baseline"] = cpu.get("decode_b256")
         also["qwen32b_decode"] = bench_qwen_decode()
