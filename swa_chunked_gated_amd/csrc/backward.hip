@@ -172,26 +172,58 @@ __global__ __launch_bounds__(512) void gdn_bwd_rev_kernel(
     for (int i = 0; i < 4; ++i)
       dS[mt][i] = d_state ? d_state[(chain * bD + 16 * mt + 4 * g + i) * bD + v0 + j] : 0.f;
 
-  for (int c = nch - 1; c >= 0; --c) {
+  // the inputs of chunk c in registers (thread tid: pieces tid and tid + 512
+  // of K, Q, dO, piece tid of TB, gate value tid), committed to LDS when the
+  // chunk starts; the next chunk's are loaded while a chunk is computed
+  typedef bf16x8 V16;
+  V16 pk[2], pq[2], po[2], ptb;
+  float pg = 0.f;
+  auto fetch = [&](int c) {
     const int i0 = n_sink + c * bC;
     const int Cc = min(bC, iend - i0);
     const size_t ci = chain * nch + c;
-    // the gradient of the state after chunk c
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int n = tid + 512 * m;
+      const int r = n >> 4, cc = (n & 15) * 8;
+      pk[m] = *reinterpret_cast<const V16*>(k + ((size_t)(bi * T_ + min(i0 + r, T_ - 1)) * Hkv + gk) * bD + cc);
+      const size_t qr = (size_t)(bi * T_ + i0 + window + min(r, Cc - 1)) * H + h;
+      pq[m] = *reinterpret_cast<const V16*>(q + qr * bD + cc);
+      po[m] = *reinterpret_cast<const V16*>(d_o + qr * bD + cc);
+    }
+    ptb = *reinterpret_cast<const V16*>(w_tb + ci * (bC * bC) + (tid >> 3) * bC + (tid & 7) * 8);
+    if (tid < 2 * bC) pg = w_g[ci * (2 * bC) + tid];
+  };
+  auto commit = [&](int c) {
+    const int Cc = min(bC, iend - (n_sink + c * bC));
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int n = tid + 512 * m;
+      const int r = n >> 4, cc = (n & 15) * 8;
+      *reinterpret_cast<V16*>(Ks + r * bSR + cc) = pk[m];
+      *reinterpret_cast<V16*>(Qs + r * bSR + cc) = pq[m];
+      V16 x = po[m];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = static_cast<bf16>(r < Cc ? bf(x[e]) * w_lin : 0.f);
+      *reinterpret_cast<V16*>(Os + r * bSR + cc) = x;
+    }
+    *reinterpret_cast<V16*>(TBs + (tid >> 3) * bSC + (tid & 7) * 8) = ptb;
+    if (tid < 2 * bC) lg[tid] = pg;
+  };
+  if (nch > 0) fetch(nch - 1);
+
+  for (int c = nch - 1; c >= 0; --c) {
+    const size_t ci = chain * nch + c;
+    // the gradient of the state after chunk c, in tile order (16 x 16 tiles
+    // (row tile, column tile); in a tile, lane 16 g + j holds rows 4 g ..
+    // 4 g + 3 of column j)
     bf16* dst = ds1 + ci * (bD * bD);
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dst[(16 * mt + 4 * g + i) * bD + v0 + j] = static_cast<bf16>(dS[mt][i]);
+    for (int mt = 0; mt < 8; ++mt) put4(dst + (mt * 8 + wv) * 256 + 4 * lane, dS[mt]);
     __syncthreads();                       // the previous chunk's LDS reads are done
-    load_rows128(Ks, k + ((size_t)(bi * T_ + i0) * Hkv + gk) * bD, (size_t)Hkv * bD, T_ - i0, false, 1.f, tid, 512);
-    load_rows128(Qs, q + ((size_t)(bi * T_ + i0 + window) * H + h) * bD, (size_t)H * bD, Cc, false, 1.f, tid, 512);
-    load_rows128(Os, d_o + ((size_t)(bi * T_ + i0 + window) * H + h) * bD, (size_t)H * bD, Cc, true, w_lin, tid, 512);
-    {
-      const bf16x8 x = *reinterpret_cast<const bf16x8*>(w_tb + ci * (bC * bC) + (tid >> 3) * bC + (tid & 7) * 8);
-      *reinterpret_cast<bf16x8*>(TBs + (tid >> 3) * bSC + (tid & 7) * 8) = x;
-    }
-    if (tid < 2 * bC) lg[tid] = w_g[ci * (2 * bC) + tid];
+    commit(c);
     __syncthreads();
+    if (c > 0) fetch(c - 1);
     // diag(gamma) K
     for (int n = tid; n < bC * 16; n += 512) {
       const int r = n >> 4;
@@ -375,18 +407,34 @@ __global__ __launch_bounds__(512) void gdn_bwd_chunk_kernel(
       bb[tid] = t < iend ? bgate[((size_t)bi * T_ + t) * H + h] : 0.f;
     }
     if (tid < 6 * bC + 1) dgam[tid] = 0.f;   // dgam, ee, rk, dbs, ddr, ddc, sdot
-    auto load_blk = [&](bf16* dst, const bf16* src, int kb) {
-      const int r = tid >> 4, cc = (tid & 15) * 8;
-      *reinterpret_cast<bf16x8*>(dst + r * bSR + cc) = *reinterpret_cast<const bf16x8*>(src + (32 * kb + r) * bD + cc);
+    // rows 32 kb .. + 31 of a tile-order [128][128] matrix (16 x 16 tiles
+    // (row tile, column tile), lane 16 g + j of a tile holding rows 4 g ..
+    // 4 g + 3 of column j) into a row-major [32][bSR] block: the block's 16
+    // tiles are contiguous; thread tid takes lanes 2 (tid % 32) and + 1 of
+    // tile tid / 32 (4 rows x 2 columns)
+    auto get_blk = [&](const bf16* src, int kb) {
+      return *reinterpret_cast<const bf16x8*>(src + (size_t)kb * 4096 + 8 * tid);
     };
+    auto put_blk = [&](bf16* dst, const bf16x8& x) {
+      const int tl = tid >> 5;                  // tile 0..15 of the block
+      const int l0 = 2 * (tid & 31);            // its lanes l0, l0 + 1
+      const int r0 = 16 * (tl >> 3) + 4 * (l0 >> 4);
+      const int c0b = 16 * (tl & 7) + (l0 & 15);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[(r0 + (e & 3)) * bSR + c0b + (e >> 2)] = x[e];
+    };
+    // (each block is loaded into registers one block ahead, while the
+    // previous one is computed)
 
     // ---- S0 pass: KS = K S0 (owned tiles), P1 = dO S0^T -> dQ = diag(gamma) P1
     f32x4 KS[4], dQ[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) KS[u] = dQ[u] = zero4();
+    bf16x8 pa = get_blk(S0g, 0), pb;
     for (int kb = 0; kb < 4; ++kb) {
       __syncthreads();
-      load_blk(blkA, S0g, kb);
+      put_blk(blkA, pa);
+      if (kb < 3) pa = get_blk(S0g, kb + 1);
       __syncthreads();
 #pragma unroll
       for (int u = 0; u < 4; ++u) KS[u] = mfma(fr_row(Ks, bSR, 16 * om, 32 * kb, lane), fr_col(blkA, bSR, 0, 16 * on(u), lane), KS[u]);
@@ -451,10 +499,16 @@ __global__ __launch_bounds__(512) void gdn_bwd_chunk_kernel(
     f32x4 KdS[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) KdS[u] = zero4();
+    pa = get_blk(dS1g, 0);
+    pb = get_blk(S0g, 0);
     for (int kb = 0; kb < 4; ++kb) {
       __syncthreads();
-      load_blk(blkA, dS1g, kb);
-      load_blk(blkB, S0g, kb);
+      put_blk(blkA, pa);
+      put_blk(blkB, pb);
+      if (kb < 3) {
+        pa = get_blk(dS1g, kb + 1);
+        pb = get_blk(S0g, kb + 1);
+      }
       __syncthreads();
 #pragma unroll
       for (int u = 0; u < 4; ++u) KdS[u] = mfma(fr_row(Ks, bSR, 16 * om, 32 * kb, lane), fr_col(blkA, bSR, 0, 16 * on(u), lane), KdS[u]);
@@ -560,9 +614,11 @@ __global__ __launch_bounds__(512) void gdn_bwd_chunk_kernel(
     for (int u = 0; u < 4; ++u) put4(Xt + (16 * on(u) + j) * bSC + 16 * om + 4 * g, Zr[u]);   // Z^T
 
     // ---- S0 pass 2: Y = -Z S0^T -> dK += diag(b gamma) Y, rk = Y.k; Y^T
+    pa = get_blk(S0g, 0);
     for (int kb = 0; kb < 4; ++kb) {
       __syncthreads();
-      load_blk(blkA, S0g, kb);
+      put_blk(blkA, pa);
+      if (kb < 3) pa = get_blk(S0g, kb + 1);
       __syncthreads();
       f32x4 y = zero4();
 #pragma unroll
@@ -680,8 +736,8 @@ __global__ __launch_bounds__(512) void gdn_bwd_chunk_kernel(
 // Softmax branch, dq: one workgroup of 4 waves per (64-row query tile, query
 // head, sequence); wave w owns rows t0 + 16 w + j.  Keys come in blocks of
 // 32: the sink blocks (keys < n_sink, attended by rows t >= key) first, then
-// the window blocks from max(n_sink, t0 - window + 1) to t0 + 63.  Three
-// sweeps over the blocks: the row maxima, the sums and o (for D = do.o), then
+// the window blocks from max(n_sink, t0 - window + 1) to t0 + 63.  Two
+// sweeps over the blocks: the row maxima, sums and o (for D = do.o), then
 // dS = P (dP - D) into dq (and, on the sink blocks, the sinks' partial dK
 // and dV of the tile).  Scores s = q.k / sqrt(d); tiles S^T [key][row].
 constexpr int sQ = 0;                       // bf16 element offsets
@@ -760,24 +816,9 @@ __global__ __launch_bounds__(256) void swa_bwd_dq_kernel(
     }
   };
   const int nb = nsb + nwb;
-  // ---- sweep 1: row maxima
-  float m = -INFINITY;
-  for (int bidx = 0; bidx < nb; ++bidx) {
-    const int base = block_base(bidx);
-    __syncthreads();
-    load_block(base);
-    __syncthreads();
-    f32x4 st[2];
-    scores(st);
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (attended(bidx, base + 16 * hf + 4 * g + i)) m = fmaxf(m, st[hf][i]);
-  }
-  m = max_groups(m);
-  // ---- sweep 2: sums and o^T
-  float l = 0.f;
+  // ---- sweep 1: row maxima, sums and o^T (running maximum: o^T and the
+  // sum are rescaled when a block raises it)
+  float m = -INFINITY, l = 0.f;
   f32x4 ot[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) ot[dt] = zero4();
@@ -788,12 +829,26 @@ __global__ __launch_bounds__(256) void swa_bwd_dq_kernel(
     __syncthreads();
     f32x4 st[2];
     scores(st);
+    float bm = -INFINITY;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool on = attended(bidx, base + 16 * hf + 4 * g + i);
-        st[hf][i] = on ? __builtin_amdgcn_exp2f((st[hf][i] - m) * cs) : 0.f;
+        st[hf][i] = on ? st[hf][i] : -INFINITY;
+        bm = fmaxf(bm, st[hf][i]);
+      }
+    const float mn = fmaxf(m, max_groups(bm));
+    const float rs = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m - mn) * cs);
+    l *= rs;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) ot[dt] *= rs;
+    m = mn;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        st[hf][i] = st[hf][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((st[hf][i] - m) * cs);
         l += st[hf][i];
       }
     const Frag<bf16> pf = frag_from_acc<bf16>(st[0], st[1]);
@@ -808,13 +863,13 @@ __global__ __launch_bounds__(256) void swa_bwd_dq_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) Dr += ot[dt][i] * bf(Os[(16 * wv + j) * bSR + 16 * dt + 4 * g + i]);
   Dr = sum_groups(Dr) * inv_l;
-  const float lse = m * cs + __builtin_amdgcn_logf(l) * 1.f;   // log2 of the sum, m in score units
+  const float lse = m * cs + __builtin_amdgcn_logf(l);   // log2 units (v_log_f32 is base 2)
   if (g == 0 && t < T_) {
     float* sp = stats + (((size_t)bi * H + h) * T_ + t) * 2;
     sp[0] = lse;
     sp[1] = Dr;
   }
-  // ---- sweep 3: dS = P (dP - D): dq, and the sinks' partial dK, dV
+  // ---- sweep 2: dS = P (dP - D): dq, and the sinks' partial dK, dV
   f32x4 dqt[8];
 #pragma unroll
   for (int kt = 0; kt < 8; ++kt) dqt[kt] = zero4();

@@ -90,7 +90,9 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
     float w_lin, T* __restrict__ ckpt) {
   // w_lin weighs the linear branch in o (1 for the plain sum).  ckpt (the
   // backward pass's forward sweep): the state entering each chunk, in T,
-  // [d_k][d_v] row-major per (sequence, head, chunk).
+  // per (sequence, head, chunk) in tile order (16 x 16 tiles (row tile,
+  // column tile); in a tile, lane 16 g + j holds rows 4 g .. 4 g + 3 of
+  // column j).
   // chunk preparation results (workspace), per (sequence, head, chunk):
   //   GDN, light: w0 = Tm diag(b), wf = g (log2), gamma (w1 unused)
   //   GLA:        w0 = Q 2^G, w1 = (K 2^{G_C - G})^T, w2 = A, wf = 2^{G_C}
@@ -321,14 +323,21 @@ __global__ __launch_bounds__(64 * NW) void linear_chunk_kernel(
     const int i0 = n_sink + c * kC;
     const int Cc = min(kC, iend - i0);
     if (ckpt) {
+      // tile order: 16 x 16 tiles (row tile, column tile), lane l of a tile
+      // holding its 4 accumulator rows, so each lane stores 8 bytes per tile
       T* Sc = ckpt + (chain * nch + c) * (size_t)(D * D);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            Sc[(16 * mt + 4 * lg + i) * D + c0 + cw + 16 * nt + l16] = from_f32<T>(S[mt][nt][i]);
+        for (int nt = 0; nt < NT; ++nt) {
+          T* dst = Sc + ((mt * (D / 16) + (c0 + cw) / 16 + nt) * 256 + 4 * lane);
+          if constexpr (sizeof(T) == 2) {
+            *reinterpret_cast<bf16x4*>(dst) = bf16x4{from_f32<T>(S[mt][nt][0]), from_f32<T>(S[mt][nt][1]),
+                                                     from_f32<T>(S[mt][nt][2]), from_f32<T>(S[mt][nt][3])};
+          } else {
+            store4(dst, S[mt][nt]);
+          }
+        }
     }
     lds_barrier();          // previous chunk's LDS reads are done
     commit();
