@@ -676,6 +676,8 @@ def main():
                     choices=["all", "headline", "longctx", "llama", "tiny", "dgd", "decode", "qwen32b",
                              "qwen32b_decode", "copy", "backward"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bwd-workload", choices=["llama8b_t4096", "longctx_b8_t32768"], default=None,
+                    help="with --only backward: one workload (default: both)")
     ap.add_argument("--no-parts", action="store_true",
                     help="time the layer only, not its calls one by one (profiling runs)")
     args = ap.parse_args()
@@ -703,7 +705,7 @@ def main():
         elif args.only == "copy":
             out = bench_copy()
         elif args.only == "backward":
-            for n in ("llama8b_t4096", HEADLINE):
+            for n in ([args.bwd_workload] if args.bwd_workload else list(CPU_BWD_SAMPLES)):
                 print(json.dumps(bench_backward(n, args.steps, args.warmup)), flush=True)
             return
         else:
