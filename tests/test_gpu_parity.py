@@ -686,10 +686,19 @@ def test_decode_bitwise_deterministic():
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
-def test_split_calls_equal_fused_call_and_accumulate():
-    """LINEAR then SOFTMAX|ACCUMULATE reproduces the fused call bit for bit,
-    and ACCUMULATE adds the layer to what o holds."""
-    w = small(T=333, B=2, H=8, Hkv=2)
+@pytest.mark.parametrize("T,window,exact", [(250, 56, True), (333, 56, False), (333, 130, False)])
+def test_split_calls_equal_fused_call_and_accumulate(T, window, exact):
+    """LINEAR then SOFTMAX|ACCUMULATE reproduces the fused call, and
+    ACCUMULATE adds the layer to what o holds.  With three stream chunks
+    (T 250, window 56) the fused call runs the scan with softmax tiles adding
+    onto its published rows, the same operations in the same order as the two
+    split calls, and the two agree bit for bit.  With five chunks at window 56
+    the fused call takes the segmented scan, whose layer kernel sums both
+    branches in fp32 and rounds once; at window 130 the separate softmax
+    launch takes 32-row query tiles where the linked ones take 64, so the
+    keys' partial sums are combined in another order.  There the two agree to
+    the bf16 tolerance."""
+    w = small(T=T, B=2, H=8, Hkv=2, window=window)
     inp = to_dev(make_prefill_inputs(w, seed=9))
     fused, _ = run_prefill(inp, w, flags=ALL)
     o, _ = gl.hybrid_prefill(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], w.n_sink, w.window,
@@ -697,7 +706,10 @@ def test_split_calls_equal_fused_call_and_accumulate():
     gl.hybrid_prefill(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], w.n_sink, w.window,
                       flags=gl.BRANCH_SOFTMAX | gl.ACCUMULATE, o=o)
     torch.cuda.synchronize()
-    assert torch.equal(o, fused)
+    if exact:
+        assert torch.equal(o, fused)
+    else:
+        assert_close(f64(o), f64(fused), False, "split vs fused")
     base = torch.randn_like(fused, dtype=torch.float32).to(fused.dtype)
     acc = base.clone()
     gl.hybrid_prefill(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], w.n_sink, w.window,
