@@ -224,14 +224,16 @@ def test_strong_forget_gates(update, dtype, d, gate_mean):
 
 # ------------------------------------------------------------- short conv
 
-@pytest.mark.parametrize("dtype,d,T,flags,ks", [("bf16", 128, 200, 3, 8), ("f32", 64, 77, 3, 8),
-                                                ("f32", 128, 70, 1, 8), ("bf16", 64, 130, 2, 8),
-                                                ("f32", 64, 9, 0, 8), ("bf16", 128, 100, 3, 3),
-                                                ("f32", 64, 64, 3, 1), ("bf16", 128, 16, 3, 8),
-                                                ("f32", 128, 129, 3, 5)])
-def test_shortconv_small(dtype, d, T, flags, ks):
-    """Tiles of 64 tokens with a causal halo, 16-token blocks and ragged ends."""
-    w = small(T=T, d=d, dtype=dtype, shortconv=True, H=4, Hkv=2, B=2, conv_ks=ks)
+@pytest.mark.parametrize("dtype,d,T,flags,ks,H,Hkv", [
+    ("bf16", 128, 200, 3, 8, 4, 2), ("f32", 64, 77, 3, 8, 4, 2), ("f32", 128, 70, 1, 8, 4, 2),
+    ("bf16", 64, 130, 2, 8, 4, 2), ("f32", 64, 9, 0, 8, 4, 2), ("bf16", 128, 100, 3, 3, 4, 2),
+    ("f32", 64, 64, 3, 1, 4, 2), ("bf16", 128, 16, 3, 8, 4, 2), ("f32", 128, 129, 3, 5, 4, 2),
+    ("bf16", 128, 700, 3, 8, 3, 1), ("bf16", 64, 1000, 3, 8, 6, 3), ("f32", 128, 523, 3, 6, 3, 3)])
+def test_shortconv_small(dtype, d, T, flags, ks, H, Hkv):
+    """Tiles of 64 tokens with a causal halo (four consecutive tiles per
+    workgroup), 8-token blocks, ragged ends, and head counts that leave part
+    of a wave's head group empty."""
+    w = small(T=T, d=d, dtype=dtype, shortconv=True, H=H, Hkv=Hkv, B=2, conv_ks=ks)
     inp = to_dev(make_prefill_inputs(w, seed=4))
     qo, ko, vo = gl.shortconv_qkv(inp["q"], inp["k"], inp["v"], inp["wq"], inp["wk"], inp["wv"],
                                   rope_theta=1e6, pos0=3, flags=flags)
