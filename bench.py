@@ -168,9 +168,9 @@ CALL_KERNELS = {
     "llama8b_t4096": {"prepare": "gdn_prep_kernel", "layer2": SEGMENTED},
     "tiny_fp32": {"linear": "gdn_prep_kernel+linear_chunk_kernel", "softmax": "swa_kernel"},
     "qwen32b_t8192_gdn": {"shortconv": "shortconv_kernel",
-                          "linear": "gdn_prep_kernel+linear_chunk_kernel", "softmax": "swa_kernel"},
+                          "linear": "gdn_prep_kernel+linear_chunk_kernel", "softmax": "swa_long_kernel"},
     "qwen32b_t8192_gla": {"shortconv": "shortconv_kernel",
-                          "linear": "gla_prep_kernel+linear_chunk_kernel", "softmax": "swa_kernel"},
+                          "linear": "gla_prep_kernel+linear_chunk_kernel", "softmax": "swa_long_kernel"},
     "dgd_b8_t8192": {"linear": "gla_prep_kernel+linear_chunk_kernel", "softmax": "swa_ring_kernel"},
 }
 CSRC = "swa_chunked_gated_amd/csrc/"
@@ -184,6 +184,7 @@ KERNEL_SOURCES = {
     "gdn_scan_full_kernel": ("gdn_prep.h", "gdn_scan_full.hip", "swa_tile.h", "common.h"),
     "swa_ring_kernel": ("swa.hip", "swa_tile.h", "common.h"),
     "swa_kernel": ("swa.hip", "swa_tile.h", "common.h"),
+    "swa_long_kernel": ("swa_long.hip", "swa_tile.h", "common.h"),
     "shortconv_kernel": ("shortconv.hip", "common.h"),
     "decode_step_kernel+decode_commit_kernel": ("decode.hip", "common.h"),
 }

@@ -182,6 +182,11 @@ hipError_t launch_gla_prep(const PrefillArgs& a, int nch, hipStream_t s);
 // Softmax branch: writes every row of o, adding the value o already holds
 // on rows t >= add_from.
 hipError_t launch_swa_prefill(const PrefillArgs& a, int add_from, hipStream_t s);
+// The long-budget softmax kernel (bf16, d = 128, window >= 256): key blocks
+// reach LDS by direct loads three blocks ahead.  launch_swa_prefill routes
+// there when swa_long_applies.
+bool swa_long_applies(const PrefillArgs& a);
+hipError_t launch_swa_long(const PrefillArgs& a, int add_from, hipStream_t s);
 // Zero rows t < n_sink + window of o (linear-only output).
 hipError_t launch_zero_head_rows(const PrefillArgs& a, hipStream_t s);
 

@@ -130,6 +130,7 @@ hipError_t launch_swa_t(const PrefillArgs& p, int add_from, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_swa_prefill(const PrefillArgs& p, int add_from, hipStream_t s) {
+  if (swa_long_applies(p)) return launch_swa_long(p, add_from, s);
   if (p.bf16) return p.D == 64 ? launch_swa_t<bf16, 64>(p, add_from, s) : launch_swa_t<bf16, 128>(p, add_from, s);
   return p.D == 64 ? launch_swa_t<float, 64>(p, add_from, s) : launch_swa_t<float, 128>(p, add_from, s);
 }

@@ -15,6 +15,8 @@ The prefill probes are placed on the shapes that reach each kernel path:
     with few sequences), bf16 and fp32 key blocks;
   * swa_ring_kernel (resident key blocks: bf16, four query heads per KV head,
     at least four 64-row tiles per workgroup, many sequences);
+  * swa_long_kernel (bf16, d = 128, windows of 256 keys or more: key blocks
+    by direct loads, 8 waves over 1 to 8 query heads);
   * the softmax tiles linked into the one-launch few-chain layer kernel,
     and the softmax waves of the one-pass layer kernel run per segment by
     the segmented scan
@@ -103,10 +105,26 @@ def test_mask_probe_ring_kernel(n_sink, window):
 @pytest.mark.parametrize("n_sink,window", [(8, 56), (0, 129), (3, 200), (8, 888)])
 def test_mask_probe_swa_kernel(G, dtype, d, n_sink, window):
     """The two-buffer softmax kernel with 1, 2 or 4 query heads per
-    workgroup, both key-block sizes, short and long budgets."""
+    workgroup, both key-block sizes, short and long budgets (window 888 in
+    bf16 at d = 128 takes the long-budget kernel)."""
     B, Hkv = 2, 2
     T = 1100 if window == 888 else 400
     q, k, v, a, b = probe_inputs(B, T, G * Hkv, Hkv, d, dtype, seed=G * 7 + window)
+    o, _ = gl.hybrid_prefill(q, k, v, a, b, n_sink, window, flags=gl.BRANCH_SOFTMAX)
+    torch.cuda.synchronize()
+    check_counts(o, n_sink, window)
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("n_sink,window,T", [(8, 888, 1500), (0, 256, 1300), (70, 300, 1111), (3, 1000, 700)])
+def test_mask_probe_long_budget_kernel(G, n_sink, window, T):
+    """The long-budget softmax kernel (bf16, d = 128, window >= 256): key
+    blocks by direct loads into a four-slot ring, 8 waves of 32 query rows
+    over G = 8, 4, 2 or 1 query heads per KV head (tiles of 32 to 256 rows),
+    runs of up to 8 tiles per workgroup, two sink blocks (70 sinks), and a
+    sequence shorter than the budget."""
+    B, Hkv, d = 2, 2, 128
+    q, k, v, a, b = probe_inputs(B, T, G * Hkv, Hkv, d, torch.bfloat16, seed=G * 11 + window)
     o, _ = gl.hybrid_prefill(q, k, v, a, b, n_sink, window, flags=gl.BRANCH_SOFTMAX)
     torch.cuda.synchronize()
     check_counts(o, n_sink, window)

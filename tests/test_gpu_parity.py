@@ -327,6 +327,35 @@ def test_resident_key_blocks(n_sink, window, flags, T):
             assert_close(f64(st[bsel][:, heads]), S, False, f"state b{bsel} h{heads}")
 
 
+@pytest.mark.parametrize("H,Hkv,T,n_sink,window,flags", [
+    (16, 2, 1300, 8, 888, ALL | gl.WRITE_STATE), (8, 2, 1000, 8, 888, gl.BRANCH_SOFTMAX),
+    (4, 2, 777, 70, 300, ALL), (16, 2, 1500, 0, 256, gl.BRANCH_SOFTMAX | gl.ACCUMULATE),
+    (2, 2, 900, 8, 400, ALL)])
+def test_long_budget_softmax(H, Hkv, T, n_sink, window, flags):
+    """Windows of 256 keys or more in bf16 at d = 128 (the long-budget softmax
+    kernel): G = 8, 4, 2, 1, alone, added onto the linear branch's rows, and
+    accumulated onto what o holds; every row of sampled chains against the
+    oracle."""
+    w = small(B=2, H=H, Hkv=Hkv, d=128, T=T, n_sink=n_sink, window=window, sigma=1.0)
+    inp = to_dev(make_prefill_inputs(w, seed=window + T))
+    if flags & gl.ACCUMULATE:
+        base = torch.randn(w.B, w.T, w.H, w.d, device=DEV).to(torch.bfloat16)
+        o = base.clone()
+        gl.hybrid_prefill(inp["q"], inp["k"], inp["v"], inp["a"], inp["b"], n_sink, window,
+                          flags=flags, o=o)
+        torch.cuda.synchronize()
+    else:
+        o, st = run_prefill(inp, w, flags=flags)
+    G = H // Hkv
+    for bsel, heads in (([0], [0]), ([1], list(range(H - G, H)))):
+        ref, S = oracle_subset(inp, w, bsel, heads, flags=flags & ~gl.ACCUMULATE)
+        if flags & gl.ACCUMULATE:
+            ref = ref + f64(base[bsel][:, :, heads])
+        assert_close(f64(o[bsel][:, :, heads]), ref, False, f"o b{bsel} h{heads}")
+        if flags & gl.WRITE_STATE:
+            assert_close(f64(st[bsel][:, heads]), S, False, f"state b{bsel} h{heads}")
+
+
 @pytest.mark.parametrize("dtype,d,n_sink,window,T", [("bf16", 128, 0, 1, 100), ("bf16", 128, 8, 1, 150),
                                                      ("f32", 64, 0, 1, 90), ("bf16", 64, 0, 64, 64)])
 def test_degenerate_budgets(dtype, d, n_sink, window, T):
