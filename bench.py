@@ -517,7 +517,8 @@ def bench_prefill(name, steps, warmup, parts=True):
         gbs = c["algorithmic_bytes"] / (c["ms_median"] * 1e-3)
         res["shortconv_roofline"] = {"kernel": c["kernel"], "bound": "hbm", "achieved": gbs / 1e9,
                                      "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": gbs / PEAK_HBM,
-                                     "traffic": None}
+                                     "traffic": stored_traffic(c["kernel"], name),
+                                     "algorithmic_bytes_per_launch": c["algorithmic_bytes"]}
     return res
 
 
