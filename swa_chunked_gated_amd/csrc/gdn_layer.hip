@@ -157,11 +157,24 @@ __device__ __forceinline__ float sum_lane_groups(float x) {
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+// Max of attention scores in one instruction each.  Scores are never NaN
+// (finite or -inf; unused sink rows are zero), so the NaN quieting that fmaxf
+// needs in IEEE mode (an extra v_max per operand) is left out.
+__device__ __forceinline__ float score_max2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float score_max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 __device__ __forceinline__ float max_lane_groups(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = score_max2(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return score_max2(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // One 32-key block of the softmax of a wave's 16 query rows: keys kk0 ..
@@ -219,7 +232,7 @@ __device__ __forceinline__ float sm_scores(const KeyPair (&kp)[NP], f32x4 (&st)[
       }
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
-      m = fmaxf(fmaxf(m, fmaxf(st[pi][hf][0], st[pi][hf][1])), fmaxf(st[pi][hf][2], st[pi][hf][3]));
+      m = score_max3(score_max3(m, st[pi][hf][0], st[pi][hf][1]), st[pi][hf][2], st[pi][hf][3]);
   }
   m = max_lane_groups(m);
   return m == -INFINITY ? 0.f : m;   // a row with no key (past the sequence): weights 0
@@ -813,7 +826,7 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
     for (int sl = 0; sl < 6; ++sl)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
-        m = fmaxf(fmaxf(m, fmaxf(st[sl][hf][0], st[sl][hf][1])), fmaxf(st[sl][hf][2], st[sl][hf][3]));
+        m = score_max3(score_max3(m, st[sl][hf][0], st[sl][hf][1]), st[sl][hf][2], st[sl][hf][3]);
     m = max_lane_groups(m);
     m = m == -INFINITY ? 0.f : m;      // a row with no key (past the sequence): weights 0
     lds_barrier();                       // B1
