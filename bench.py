@@ -168,7 +168,7 @@ CALL_KERNELS = {
     "llama8b_t4096": {"prepare": "gdn_prep_kernel", "layer2": SEGMENTED},
     "tiny_fp32": {"linear": "gdn_prep_kernel+linear_chunk_kernel", "softmax": "swa_kernel"},
     "qwen32b_t8192_gdn": {"shortconv": "shortconv_kernel",
-                          "linear": "gdn_prep_kernel+linear_chunk_kernel", "softmax": "swa_long_kernel"},
+                          "linear": "gdn_prep_kernel+gdn_linear_layer_kernel", "softmax": "swa_long_kernel"},
     "qwen32b_t8192_gla": {"shortconv": "shortconv_kernel",
                           "linear": "gla_prep_kernel+linear_chunk_kernel", "softmax": "swa_long_kernel"},
     "dgd_b8_t8192": {"linear": "gla_prep_kernel+linear_chunk_kernel", "softmax": "swa_ring_kernel"},

@@ -283,7 +283,11 @@ __device__ __forceinline__ void sm_values(const KeyPair (&kp)[NP], const f32x4 (
 // q, k, v, w_tb and w_g are read through plain (not restrict) pointers on
 // purpose: the prefetch loads must stay where they are issued, ahead of the
 // chunk's barriers, rather than be moved next to their use.
-__global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
+// LIN_ONLY: the linear branch alone (windows past the ring, the softmax
+// branch added by its own launch afterwards): the softmax waves form only A
+// and keep the K, V, TB and gates prefetch; the state waves store w_lin o_lin.
+template <bool LIN_ONLY>
+__device__ __forceinline__ void gdn_layer_body(
     const bf16* q, const bf16* k, const bf16* v, const bf16* w_tb, const float* w_g,
     bf16* __restrict__ o,
     float* __restrict__ state_out, int B, int T_, int H, int Hkv, int n_sink, int window,
@@ -609,13 +613,20 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
         for (int rt = 0; rt < 4; ++rt) {
           // lane: row 16 rt + j, columns cw + 8 g .. + 7 (tile 0 then tile 1)
           const int r = 16 * rt + j;
-          const bf16x8 xs = *reinterpret_cast<const bf16x8*>(Xs + cw + l_x + 16 * rt * kSR);
           bf16x8 y;
+          if constexpr (LIN_ONLY) {
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              y[4 * nt + i] = static_cast<bf16>(__builtin_fmaf(ot[nt][rt][i], w_lin, static_cast<float>(xs[4 * nt + i])));
+              for (int i = 0; i < 4; ++i) y[4 * nt + i] = static_cast<bf16>(ot[nt][rt][i] * w_lin);
+          } else {
+            const bf16x8 xs = *reinterpret_cast<const bf16x8*>(Xs + cw + l_x + 16 * rt * kSR);
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                y[4 * nt + i] = static_cast<bf16>(__builtin_fmaf(ot[nt][rt][i], w_lin, static_cast<float>(xs[4 * nt + i])));
+          }
           typedef unsigned int u4 __attribute__((ext_vector_type(4)));
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, y), rs, (r * (int)qrow + cw + 8 * g) * 2, 0, 0);
         }
@@ -646,7 +657,7 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
   // prologue (first segment): rows t < n_sink + window carry no linear
   // branch and attend to every key t' <= t: the sinks and ring chunks 0 and
   // 1 hold them all
-  {
+  if constexpr (!LIN_ONLY) {
     const int nrow = sg == 0 ? min(n_sink + window, T_) : 0;
     for (int t0 = 16 * jq; t0 < nrow; t0 += 64) {
       Frag<bf16> qf[4];
@@ -756,6 +767,51 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
       for (int p = 0; p < 4; ++p) acc = mfma(f[p], qf[p], acc);
       return acc;
     };
+    if constexpr (LIN_ONLY) {
+      // A only: the chunk's own scores, decayed and masked; then the K, V
+      // prefetch of chunk c + 3 and the commits, at the same barriers
+      f32x4 sa[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        Frag<bf16> kx[4];
+        kfr(Kc, 16 * kt, kx);
+        sa[kt] = kmma(kx, zero4());
+      }
+      {
+        int jj = j;
+        asm volatile("" : "+v"(jj));
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          f32x4 x;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float dec = __builtin_amdgcn_exp2f(fminf(lr - ls[kt][i], 0.f));
+            x[i] = kt < jq || (kt == jq && 4 * g + i <= jj) ? dec * sa[kt][i] : 0.f;
+          }
+          store4(As + l_acc + 16 * jq * kSC + 32 * (kt >> 1) + 4 * (kt & 1), x);
+        }
+      }
+      lds_barrier();                     // B1
+      load_tile4(kb, kvrow, kv_row0(c + 3), ptid, pk);
+      load_tile4(vb, kvrow, kv_row0(c + 3), ptid, pv);
+      asm volatile("" ::: "memory");
+      lds_barrier();                     // B2
+#pragma unroll
+      for (int m2 = 0; m2 < 4; ++m2) {
+        put_row(KR + ((unsigned)c % 3u) * kC * kSR, ptid + 256 * m2, pk[m2]);
+        put_vrow(VR + ((unsigned)c % 3u) * kC * kSV, ptid + 256 * m2, pv[m2]);
+      }
+      if (c + 1 < ce) {
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2) {
+          const int n = ptid + 256 * m2;
+          *reinterpret_cast<V16*>(TBs + (n >> 3) * kSC + (n & 7) * 8) = pt[m2];
+        }
+        if (ptid < 64) put_gates(ptid, pg);
+      }
+      lds_barrier();                     // B3
+      continue;
+    }
     Frag<bf16> ka[4], kb2[4], kc[4], kd[4];
     f32x4 sa[4], st[6][2];
     kfr(Kc, 0, ka);
@@ -918,6 +974,24 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
     }
     lds_barrier();                       // B3: the softmax rows are read
   }
+}
+
+__global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
+    const bf16* q, const bf16* k, const bf16* v, const bf16* w_tb, const float* w_g,
+    bf16* __restrict__ o,
+    float* __restrict__ state_out, int B, int T_, int H, int Hkv, int n_sink, int window,
+    int nch, int write_state, float w_lin, float w_swa, int seg_len, const float* s_in) {
+  gdn_layer_body<false>(q, k, v, w_tb, w_g, o, state_out, B, T_, H, Hkv, n_sink, window, nch, write_state,
+                        w_lin, w_swa, seg_len, s_in);
+}
+
+__global__ __launch_bounds__(kThreads) void gdn_linear_layer_kernel(
+    const bf16* q, const bf16* k, const bf16* v, const bf16* w_tb, const float* w_g,
+    bf16* __restrict__ o,
+    float* __restrict__ state_out, int B, int T_, int H, int Hkv, int n_sink, int window,
+    int nch, int write_state, float w_lin) {
+  gdn_layer_body<true>(q, k, v, w_tb, w_g, o, state_out, B, T_, H, Hkv, n_sink, window, nch, write_state,
+                       w_lin, 0.f, nch, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -1290,6 +1364,34 @@ bool gdn_layer_applies(const PrefillArgs& p) {
   const int nch = gdn_stream_chunks(p.T, p.n_sink, p.window);
   return p.bf16 && !p.gla && p.D == kD && (p.flags & 3) == 3 && !(p.flags & 8) && nch >= 1 &&
          p.window <= 128 && p.n_sink <= kSinkRows && !gdn_full_prep(p.B, p.H, p.D, p.bf16);
+}
+
+bool gdn_linear_layer_applies(const PrefillArgs& p) {
+  // the linear branch (the softmax branch, if asked for, by its own launch
+  // afterwards: windows past the layer kernel's ring, or more sinks than it
+  // holds), overwriting o, many chains
+  const int nch = gdn_stream_chunks(p.T, p.n_sink, p.window);
+  return p.bf16 && !p.gla && !p.dgd && p.D == kD && (p.flags & 1) && !(p.flags & 8) && nch >= 1 &&
+         !gdn_layer_applies(p) && !gdn_segmented(p) && !gdn_full_prep(p.B, p.H, p.D, p.bf16);
+}
+
+hipError_t launch_gdn_linear_layer(const PrefillArgs& p, hipStream_t s) {
+  const int nch = gdn_stream_chunks(p.T, p.n_sink, p.window);
+  hipError_t e = p.prepared ? hipSuccess : launch_gdn_prep(p, nch, s);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)gdn_linear_layer_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kLdsBytes);
+  if (e != hipSuccess) return e;
+  const GdnWorkspace w = gdn_workspace_layout(p.workspace, p.B, p.H, nch, kD, sizeof(bf16), false);
+  const dim3 grid(xcd_grouped_grid((long long)p.B * p.Hkv, p.H / p.Hkv));
+  hipLaunchKernelGGL(gdn_linear_layer_kernel, grid, dim3(kThreads), kLdsBytes, s, (const bf16*)p.q,
+                     (const bf16*)p.k, (const bf16*)p.v, (const bf16*)w.tb, w.g, (bf16*)p.o,
+                     p.state_out, p.B, p.T, p.H, p.Hkv, p.n_sink, p.window, nch,
+                     (p.flags & 4) ? 1 : 0, p.w_lin);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // linear branch alone: rows t < n_sink + window carry no linear output
+  return (p.flags & 2) ? hipSuccess : launch_zero_head_rows(p, s);
 }
 
 hipError_t launch_gdn_layer(const PrefillArgs& p, hipStream_t s) {

@@ -148,6 +148,11 @@ bool separate_preparation(const PrefillArgs& p);
 hipError_t launch_preparation(const PrefillArgs& p, hipStream_t s);
 bool gdn_layer_applies(const PrefillArgs& p);
 hipError_t launch_gdn_layer(const PrefillArgs& p, hipStream_t s);
+// The same layer kernel for the linear branch alone (overwriting o; the
+// softmax branch, when asked for, runs as its own launch after it): bf16
+// GDN, d = 128, many chains, when the one-pass layer does not apply.
+bool gdn_linear_layer_applies(const PrefillArgs& p);
+hipError_t launch_gdn_linear_layer(const PrefillArgs& p, hipStream_t s);
 // Segmented scan (bf16 GDN at d = 128, both branches, no accumulation,
 // window <= 128, n_sink <= 16, too few chains to fill the GPU): each chain's
 // P segments of L chunks each; P = 1 when the chains fill the GPU.

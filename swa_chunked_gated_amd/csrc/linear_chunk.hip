@@ -735,6 +735,7 @@ hipError_t launch_linear_prefill(const PrefillArgs& p, hipStream_t s, bool* swa_
     if (swa_done) *swa_done = true;
     return launch_gdn_layer(p, s);
   }
+  if (gdn_linear_layer_applies(p)) return launch_gdn_linear_layer(p, s);
   if (nch > 0 && !p.prepared) {
     const hipError_t e = p.gla ? launch_gla_prep(p, nch, s) : launch_gdn_prep(p, nch, s);
     if (e != hipSuccess) return e;

@@ -327,6 +327,28 @@ def test_resident_key_blocks(n_sink, window, flags, T):
             assert_close(f64(st[bsel][:, heads]), S, False, f"state b{bsel} h{heads}")
 
 
+@pytest.mark.parametrize("B,H,Hkv,T,n_sink,window,flags", [
+    (4, 32, 8, 700, 8, 130, ALL | gl.WRITE_STATE), (2, 64, 8, 1100, 8, 888, ALL | gl.WRITE_STATE),
+    (4, 32, 4, 333, 20, 56, ALL), (8, 16, 4, 515, 3, 300, ALL | gl.WRITE_STATE),
+    (4, 32, 8, 700, 8, 130, gl.BRANCH_LINEAR | gl.WRITE_STATE), (4, 32, 8, 300, 8, 56, gl.BRANCH_LINEAR)])
+def test_many_chain_linear_layer_kernel(B, H, Hkv, T, n_sink, window, flags):
+    """Many chains (B*H*d/64 >= 256) with a window past the one-pass layer's
+    ring (or more sinks than it holds), or the linear branch alone: the layer
+    kernel runs the linear branch alone (its softmax waves form only the
+    decayed score tile; rows t < n_sink + window are zeroed when no softmax
+    launch follows), then the softmax launch adds its rows; sampled chains
+    against the oracle, every row and the final state, ragged last chunks."""
+    w = small(B=B, H=H, Hkv=Hkv, d=128, T=T, n_sink=n_sink, window=window, sigma=1.0)
+    inp = to_dev(make_prefill_inputs(w, seed=T + window))
+    o, st = run_prefill(inp, w, flags=flags)
+    G = H // Hkv
+    for bsel, heads in (([0], [0, 1]), ([B - 1], list(range(H - G, H)))):
+        ref, S = oracle_subset(inp, w, bsel, heads, flags=flags)
+        assert_close(f64(o[bsel][:, :, heads]), ref, False, f"o b{bsel} h{heads}")
+        if flags & gl.WRITE_STATE:
+            assert_close(f64(st[bsel][:, heads]), S, False, f"state b{bsel} h{heads}")
+
+
 @pytest.mark.parametrize("H,Hkv,T,n_sink,window,flags", [
     (16, 2, 1300, 8, 888, ALL | gl.WRITE_STATE), (8, 2, 1000, 8, 888, gl.BRANCH_SOFTMAX),
     (4, 2, 777, 70, 300, ALL), (16, 2, 1500, 0, 256, gl.BRANCH_SOFTMAX | gl.ACCUMULATE),
