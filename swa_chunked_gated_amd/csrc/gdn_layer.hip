@@ -286,7 +286,7 @@ __device__ __forceinline__ void sm_values(const KeyPair (&kp)[NP], const f32x4 (
 // LIN_ONLY: the linear branch alone (windows past the ring, the softmax
 // branch added by its own launch afterwards): the softmax waves form only A
 // and keep the K, V, TB and gates prefetch; the state waves store w_lin o_lin.
-template <bool LIN_ONLY>
+template <bool LIN_ONLY, int NT>
 __device__ __forceinline__ void gdn_layer_body(
     const bf16* q, const bf16* k, const bf16* v, const bf16* w_tb, const float* w_g,
     bf16* __restrict__ o,
@@ -307,11 +307,13 @@ __device__ __forceinline__ void gdn_layer_body(
   // the G query heads of a KV head are consecutive workgroups on one XCD
   // and share the K and V rows through its L2
   const int G = H / Hkv;
+  constexpr int HALVES = NT == 2 ? 1 : 2;    // workgroups per chain (state columns split)
   int unit, member;
-  if (!xcd_grouped(blockIdx.x, G, B * Hkv, unit, member)) return;
+  if (!xcd_grouped(blockIdx.x, G * HALVES, B * Hkv, unit, member)) return;
   const int bi = unit / Hkv;
   const int gk = unit % Hkv;
-  const int h = gk * G + member;
+  const int h = gk * G + member / HALVES;
+  const int half = member % HALVES;
   const size_t chain = (size_t)bi * H + h;
   // segment y of the chain: chunks cb .. ce - 1, entered with the state
   // s_in holds for it (segment 0, or no s_in: the zero state)
@@ -452,23 +454,26 @@ __device__ __forceinline__ void gdn_layer_body(
     // d_k = 32 (mt / 2) + 8 g + 4 (mt % 2) + i (see tr_frag_k), and column j
     // of tile nt is d_v = 32 wv + 8 (j / 4) + 4 nt + j % 4, so that a lane's
     // two output tiles hold 8 adjacent columns of a row (one 16-byte store)
-    const int cw = 32 * wv;
+    // (NT == 1: the workgroup's half of the columns, 16 per wave, column j
+    // of the single tile is d_v = cw + j and a lane stores 4 columns)
+    const int cw = NT == 2 ? 32 * wv : 64 * half + 16 * wv;
 
-    f32x4 S[8][2];
+    f32x4 S[8][NT];
     if (s_in && sg > 0) {
       const float* Si = s_in + ((size_t)sg * B * H + chain) * kD * kD;
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            S[mt][nt][i] = Si[tile_off(32 * (mt >> 1) + 8 * g + 4 * (mt & 1) + i, cw + 8 * (j >> 2) + 4 * nt + (j & 3))];
+            S[mt][nt][i] = Si[tile_off(32 * (mt >> 1) + 8 * g + 4 * (mt & 1) + i,
+                                       NT == 2 ? cw + 8 * (j >> 2) + 4 * nt + (j & 3) : cw + j)];
     } else {
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) S[mt][nt] = zero4();
+        for (int nt = 0; nt < NT; ++nt) S[mt][nt] = zero4();
     }
     V16 pq[4];
     for (int c = cb; c < ce; ++c) {
@@ -491,9 +496,9 @@ __device__ __forceinline__ void gdn_layer_body(
       // ---- O^T = S^T Q^T [dv tile nt][query tile rt] and KS = K S [token
       // tile mt][dv tile nt], one d-step at a time (the state's operand
       // fragments of a step are formed from its accumulators when needed)
-      f32x4 ot[2][4], KS[4][2];
+      f32x4 ot[NT][4], KS[4][NT];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
           ot[nt][rt] = zero4();
@@ -501,25 +506,25 @@ __device__ __forceinline__ void gdn_layer_body(
         }
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        Frag<bf16> sf[2], qf[4], kf[4];
+        Frag<bf16> sf[NT], qf[4], kf[4];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) sf[nt] = frag_from_acc<bf16>(S[2 * p][nt], S[2 * p + 1][nt]);
+        for (int nt = 0; nt < NT; ++nt) sf[nt] = frag_from_acc<bf16>(S[2 * p][nt], S[2 * p + 1][nt]);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) qf[rt] = lds_frag8(Qs + l_row + 16 * rt * kSR + 32 * p);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) ot[nt][rt] = mfma(sf[nt], qf[rt], ot[nt][rt]);
+          for (int nt = 0; nt < NT; ++nt) ot[nt][rt] = mfma(sf[nt], qf[rt], ot[nt][rt]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) kf[mt] = lds_frag8(Kc + l_row + 16 * mt * kSR + 32 * p);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) KS[mt][nt] = mfma(kf[mt], sf[nt], KS[mt][nt]);
+          for (int nt = 0; nt < NT; ++nt) KS[mt][nt] = mfma(kf[mt], sf[nt], KS[mt][nt]);
       }
       // ---- U = TB V - TB diag(gamma) KS   [token tile mt][dv tile nt];
       // diag(-gamma) is applied to KS's token rows as its fragments form
-      Frag<bf16> ksf[2][2];
+      Frag<bf16> ksf[2][NT];
       {
         const float* ngam = Gs + 2 * kC;
 #pragma unroll
@@ -527,30 +532,31 @@ __device__ __forceinline__ void gdn_layer_body(
           const f32x4 n0 = *reinterpret_cast<const f32x4*>(ngam + 32 * pp + 4 * g);
           const f32x4 n1 = *reinterpret_cast<const f32x4*>(ngam + 32 * pp + 16 + 4 * g);
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
+          for (int nt = 0; nt < NT; ++nt)
             ksf[pp][nt] = frag_from_acc_scaled<bf16>(KS[2 * pp][nt], KS[2 * pp + 1][nt], n0, n1);
         }
       }
-      f32x4 U[4][2];
+      f32x4 U[4][NT];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) U[mt][nt] = zero4();
+        for (int nt = 0; nt < NT; ++nt) U[mt][nt] = zero4();
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
-        Frag<bf16> tf[4], vf[2];
+        Frag<bf16> tf[4], vf[NT];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) tf[mt] = lds_frag8(TBs + l_acc + 16 * mt * kSC + 32 * pp);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) vf[nt] = tr_at(Vc + cw + l_tk, 32 * pp * kSR + 4 * nt);
+        for (int nt = 0; nt < NT; ++nt)
+          vf[nt] = NT == 2 ? tr_at(Vc + cw + l_tk, 32 * pp * kSR + 4 * nt) : tr_at(Vc + cw + l_tv, 32 * pp * kSR);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) U[mt][nt] = mfma(tf[mt], vf[nt], U[mt][nt]);
+          for (int nt = 0; nt < NT; ++nt) U[mt][nt] = mfma(tf[mt], vf[nt], U[mt][nt]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) U[mt][nt] = mfma(tf[mt], ksf[pp][nt], U[mt][nt]);
+          for (int nt = 0; nt < NT; ++nt) U[mt][nt] = mfma(tf[mt], ksf[pp][nt], U[mt][nt]);
       }
 
       lds_barrier();                     // B1: A is in LDS
@@ -560,17 +566,17 @@ __device__ __forceinline__ void gdn_layer_body(
       for (int rt = 0; rt < 4; ++rt) {
         const float gq = gam[16 * rt + j];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) ot[nt][rt] *= gq;
+        for (int nt = 0; nt < NT; ++nt) ot[nt][rt] *= gq;
       }
       const float gC = gam[kC - 1];
       const float* dec = Gs + 3 * kC;    // 2^(g_C - g_s)
-      Frag<bf16> uf[2][2], us[2][2];
+      Frag<bf16> uf[2][NT], us[2][NT];
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
         const f32x4 s0 = *reinterpret_cast<const f32x4*>(dec + 32 * pp + 4 * g);
         const f32x4 s1 = *reinterpret_cast<const f32x4*>(dec + 32 * pp + 16 + 4 * g);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
           uf[pp][nt] = frag_from_acc<bf16>(U[2 * pp][nt], U[2 * pp + 1][nt]);
           us[pp][nt] = frag_from_acc_scaled<bf16>(U[2 * pp][nt], U[2 * pp + 1][nt], s0, s1);
         }
@@ -583,13 +589,13 @@ __device__ __forceinline__ void gdn_layer_body(
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) ot[nt][rt] = mfma(uf[pp][nt], af[rt], ot[nt][rt]);
+          for (int nt = 0; nt < NT; ++nt) ot[nt][rt] = mfma(uf[pp][nt], af[rt], ot[nt][rt]);
       }
       // ---- S = gamma_C S + K^T diag(gamma_C / gamma) U
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) S[mt][nt] *= gC;
+        for (int nt = 0; nt < NT; ++nt) S[mt][nt] *= gC;
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
         Frag<bf16> kt[2];
@@ -599,7 +605,7 @@ __device__ __forceinline__ void gdn_layer_body(
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) S[mt][nt] = mfma(kt[pp], us[pp][nt], S[mt][nt]);
+          for (int nt = 0; nt < NT; ++nt) S[mt][nt] = mfma(kt[pp], us[pp][nt], S[mt][nt]);
       }
       lds_barrier();                     // B2: the softmax rows are in LDS
       // ---- o = w_lin o_lin + the softmax rows: buffer stores whose range
@@ -611,18 +617,27 @@ __device__ __forceinline__ void gdn_layer_body(
             ob + (size_t)(i0 + window) * qrow, 0, (int)min(left, 0x7fffffffLL), 0x00020000);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-          // lane: row 16 rt + j, columns cw + 8 g .. + 7 (tile 0 then tile 1)
+          // lane: row 16 rt + j, columns cw + 8 g .. + 7 (tile 0 then tile 1);
+          // NT == 1: columns cw + 4 g .. + 3
           const int r = 16 * rt + j;
+          if constexpr (NT == 1) {
+            static_assert(LIN_ONLY, "the column split serves the linear branch alone");
+            const bf16x4 y4{static_cast<bf16>(ot[0][rt][0] * w_lin), static_cast<bf16>(ot[0][rt][1] * w_lin),
+                            static_cast<bf16>(ot[0][rt][2] * w_lin), static_cast<bf16>(ot[0][rt][3] * w_lin)};
+            typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, y4), rs, (r * (int)qrow + cw + 4 * g) * 2, 0, 0);
+            continue;
+          }
           bf16x8 y;
           if constexpr (LIN_ONLY) {
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
               for (int i = 0; i < 4; ++i) y[4 * nt + i] = static_cast<bf16>(ot[nt][rt][i] * w_lin);
           } else {
             const bf16x8 xs = *reinterpret_cast<const bf16x8*>(Xs + cw + l_x + 16 * rt * kSR);
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
               for (int i = 0; i < 4; ++i)
                 y[4 * nt + i] = static_cast<bf16>(__builtin_fmaf(ot[nt][rt][i], w_lin, static_cast<float>(xs[4 * nt + i])));
@@ -642,11 +657,11 @@ __device__ __forceinline__ void gdn_layer_body(
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            Sg[(size_t)(32 * (mt >> 1) + 8 * g + 4 * (mt & 1) + i) * kD + cw + 8 * (j >> 2) + 4 * nt + (j & 3)] =
-                S[mt][nt][i];
+            Sg[(size_t)(32 * (mt >> 1) + 8 * g + 4 * (mt & 1) + i) * kD +
+               (NT == 2 ? cw + 8 * (j >> 2) + 4 * nt + (j & 3) : cw + j)] = S[mt][nt][i];
     }
     return;
   }
@@ -981,8 +996,8 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
     bf16* __restrict__ o,
     float* __restrict__ state_out, int B, int T_, int H, int Hkv, int n_sink, int window,
     int nch, int write_state, float w_lin, float w_swa, int seg_len, const float* s_in) {
-  gdn_layer_body<false>(q, k, v, w_tb, w_g, o, state_out, B, T_, H, Hkv, n_sink, window, nch, write_state,
-                        w_lin, w_swa, seg_len, s_in);
+  gdn_layer_body<false, 2>(q, k, v, w_tb, w_g, o, state_out, B, T_, H, Hkv, n_sink, window, nch, write_state,
+                           w_lin, w_swa, seg_len, s_in);
 }
 
 __global__ __launch_bounds__(kThreads) void gdn_linear_layer_kernel(
@@ -990,8 +1005,8 @@ __global__ __launch_bounds__(kThreads) void gdn_linear_layer_kernel(
     bf16* __restrict__ o,
     float* __restrict__ state_out, int B, int T_, int H, int Hkv, int n_sink, int window,
     int nch, int write_state, float w_lin) {
-  gdn_layer_body<true>(q, k, v, w_tb, w_g, o, state_out, B, T_, H, Hkv, n_sink, window, nch, write_state,
-                       w_lin, 0.f, nch, nullptr);
+  gdn_layer_body<true, 1>(q, k, v, w_tb, w_g, o, state_out, B, T_, H, Hkv, n_sink, window, nch, write_state,
+                          w_lin, 0.f, nch, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -1383,7 +1398,8 @@ hipError_t launch_gdn_linear_layer(const PrefillArgs& p, hipStream_t s) {
                           kLdsBytes);
   if (e != hipSuccess) return e;
   const GdnWorkspace w = gdn_workspace_layout(p.workspace, p.B, p.H, nch, kD, sizeof(bf16), false);
-  const dim3 grid(xcd_grouped_grid((long long)p.B * p.Hkv, p.H / p.Hkv));
+  // two workgroups per chain, each with half of the state's columns
+  const dim3 grid(xcd_grouped_grid((long long)p.B * p.Hkv, 2 * (p.H / p.Hkv)));
   hipLaunchKernelGGL(gdn_linear_layer_kernel, grid, dim3(kThreads), kLdsBytes, s, (const bf16*)p.q,
                      (const bf16*)p.k, (const bf16*)p.v, (const bf16*)w.tb, w.g, (bf16*)p.o,
                      p.state_out, p.B, p.T, p.H, p.Hkv, p.n_sink, p.window, nch,
