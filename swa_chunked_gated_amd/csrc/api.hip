@@ -226,6 +226,15 @@ int prefill_impl(const void* q, const void* k, const void* v, const float* a, co
   // overwrite, zeroes rows t < N itself; the softmax kernel then adds what o
   // holds on rows t >= add_from.
   const bool run_linear = wst || (lin && T > N);
+  // Both branches on the linear-only layer kernel (many chains, windows past
+  // the one-pass layer's ring): the softmax launch writes every row first,
+  // then the layer kernel adds the linear rows (its reads of o overlap its
+  // chunk work, where the softmax launch's would stall it).
+  if (swa && lin && T > N && gdn::gdn_linear_layer_applies(p)) {
+    int rc = launched(gdn::launch_swa_prefill(p, T, s));
+    if (rc) return rc;
+    return launched(gdn::launch_gdn_linear_layer(p, s, true));
+  }
   bool swa_done = false;
   if (run_linear) {
     int rc = launched(gdn::launch_linear_prefill(p, s, &swa_done));

@@ -291,7 +291,7 @@ __device__ __forceinline__ void gdn_layer_body(
     const bf16* q, const bf16* k, const bf16* v, const bf16* w_tb, const float* w_g,
     bf16* __restrict__ o,
     float* __restrict__ state_out, int B, int T_, int H, int Hkv, int n_sink, int window,
-    int nch, int write_state, float w_lin, float w_swa, int seg_len, const float* s_in) {
+    int nch, int write_state, float w_lin, float w_swa, int seg_len, const float* s_in, int add_o) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   bf16* sm = reinterpret_cast<bf16*>(smem_raw);
   bf16* KR = sm + oKR;
@@ -492,6 +492,21 @@ __device__ __forceinline__ void gdn_layer_body(
       // not committed), so that the memory counters the compiler waits on
       // are exact.
       load_tile4(qb, qrow, q_row0(min(c + 1, ce - 1)), tid, pq);
+      // the chunk's output rows, when the linear branch adds onto what o
+      // holds (the softmax branch, written first): read through the same
+      // bounded range as the stores (rows past the sequence read as 0)
+      typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+      u2 po[4];
+      if constexpr (NT == 1) {
+        const long long left = (long long)(T_ - i0 - window) * H * kD * 2;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            ob + (size_t)(i0 + window) * qrow, 0, (int)min(left, 0x7fffffffLL), 0x00020000);
+        if (add_o) {
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+            po[rt] = __builtin_amdgcn_raw_buffer_load_b64(rs, ((16 * rt + j) * (int)qrow + cw + 4 * g) * 2, 0, 0);
+        }
+      }
       asm volatile("" ::: "memory");     // issue them here, ahead of the products
       // ---- O^T = S^T Q^T [dv tile nt][query tile rt] and KS = K S [token
       // tile mt][dv tile nt], one d-step at a time (the state's operand
@@ -622,9 +637,14 @@ __device__ __forceinline__ void gdn_layer_body(
           const int r = 16 * rt + j;
           if constexpr (NT == 1) {
             static_assert(LIN_ONLY, "the column split serves the linear branch alone");
-            const bf16x4 y4{static_cast<bf16>(ot[0][rt][0] * w_lin), static_cast<bf16>(ot[0][rt][1] * w_lin),
-                            static_cast<bf16>(ot[0][rt][2] * w_lin), static_cast<bf16>(ot[0][rt][3] * w_lin)};
-            typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+            f32x4 yv = ot[0][rt] * w_lin;
+            if (add_o) {
+              const bf16x4 x = __builtin_bit_cast(bf16x4, po[rt]);
+              yv += f32x4{static_cast<float>(x[0]), static_cast<float>(x[1]), static_cast<float>(x[2]),
+                          static_cast<float>(x[3])};
+            }
+            const bf16x4 y4{static_cast<bf16>(yv[0]), static_cast<bf16>(yv[1]), static_cast<bf16>(yv[2]),
+                            static_cast<bf16>(yv[3])};
             __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, y4), rs, (r * (int)qrow + cw + 4 * g) * 2, 0, 0);
             continue;
           }
@@ -997,16 +1017,16 @@ __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
     float* __restrict__ state_out, int B, int T_, int H, int Hkv, int n_sink, int window,
     int nch, int write_state, float w_lin, float w_swa, int seg_len, const float* s_in) {
   gdn_layer_body<false, 2>(q, k, v, w_tb, w_g, o, state_out, B, T_, H, Hkv, n_sink, window, nch, write_state,
-                           w_lin, w_swa, seg_len, s_in);
+                           w_lin, w_swa, seg_len, s_in, 0);
 }
 
 __global__ __launch_bounds__(kThreads) void gdn_linear_layer_kernel(
     const bf16* q, const bf16* k, const bf16* v, const bf16* w_tb, const float* w_g,
     bf16* __restrict__ o,
     float* __restrict__ state_out, int B, int T_, int H, int Hkv, int n_sink, int window,
-    int nch, int write_state, float w_lin) {
+    int nch, int write_state, float w_lin, int add_o) {
   gdn_layer_body<true, 1>(q, k, v, w_tb, w_g, o, state_out, B, T_, H, Hkv, n_sink, window, nch, write_state,
-                          w_lin, 0.f, nch, nullptr);
+                          w_lin, 0.f, nch, nullptr, add_o);
 }
 
 // ---------------------------------------------------------------------------
@@ -1390,7 +1410,7 @@ bool gdn_linear_layer_applies(const PrefillArgs& p) {
          !gdn_layer_applies(p) && !gdn_segmented(p) && !gdn_full_prep(p.B, p.H, p.D, p.bf16);
 }
 
-hipError_t launch_gdn_linear_layer(const PrefillArgs& p, hipStream_t s) {
+hipError_t launch_gdn_linear_layer(const PrefillArgs& p, hipStream_t s, bool add_o) {
   const int nch = gdn_stream_chunks(p.T, p.n_sink, p.window);
   hipError_t e = p.prepared ? hipSuccess : launch_gdn_prep(p, nch, s);
   if (e != hipSuccess) return e;
@@ -1403,7 +1423,7 @@ hipError_t launch_gdn_linear_layer(const PrefillArgs& p, hipStream_t s) {
   hipLaunchKernelGGL(gdn_linear_layer_kernel, grid, dim3(kThreads), kLdsBytes, s, (const bf16*)p.q,
                      (const bf16*)p.k, (const bf16*)p.v, (const bf16*)w.tb, w.g, (bf16*)p.o,
                      p.state_out, p.B, p.T, p.H, p.Hkv, p.n_sink, p.window, nch,
-                     (p.flags & 4) ? 1 : 0, p.w_lin);
+                     (p.flags & 4) ? 1 : 0, p.w_lin, add_o ? 1 : 0);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // linear branch alone: rows t < n_sink + window carry no linear output

@@ -152,7 +152,9 @@ hipError_t launch_gdn_layer(const PrefillArgs& p, hipStream_t s);
 // softmax branch, when asked for, runs as its own launch after it): bf16
 // GDN, d = 128, many chains, when the one-pass layer does not apply.
 bool gdn_linear_layer_applies(const PrefillArgs& p);
-hipError_t launch_gdn_linear_layer(const PrefillArgs& p, hipStream_t s);
+// add_o: add the linear rows onto what o holds (the softmax branch, launched
+// before it) instead of storing them.
+hipError_t launch_gdn_linear_layer(const PrefillArgs& p, hipStream_t s, bool add_o = false);
 // Segmented scan (bf16 GDN at d = 128, both branches, no accumulation,
 // window <= 128, n_sink <= 16, too few chains to fill the GPU): each chain's
 // P segments of L chunks each; P = 1 when the chains fill the GPU.
