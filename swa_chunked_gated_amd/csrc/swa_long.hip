@@ -96,7 +96,9 @@ __device__ __forceinline__ float max_groups(float x) {
   return max2(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-template <int W, int NS, int HPW>
+// ADD: some rows add what o holds (rows t >= add_from < T); without it the
+// kernel keeps no registers for them.
+template <int W, int NS, int HPW, bool ADD>
 __global__ __launch_bounds__(64 * W, 8 / W) void swa_long_kernel(const bf16* __restrict__ q,
                                                               const bf16* __restrict__ k,
                                                               const bf16* __restrict__ v, bf16* __restrict__ o,
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void swa_long_kernel(const bf16* __r
     }
     typedef bf16x4 ORaw[kNQ][lD / 16];
     ORaw oraw;
-    const bool addl = qlast >= add_from && qb < T_;   // some row of the wave adds what o holds
+    const bool addl = ADD && qlast >= add_from && qb < T_;   // some row of the wave adds what o holds
 
     for (int b = 0; b < nblk; ++b, ++flat) {
       // block flat has landed once at most the blocks issued after it are
@@ -355,24 +357,52 @@ __global__ __launch_bounds__(64 * W, 8 / W) void swa_long_kernel(const bf16* __r
           }
         }
       }
+      // the next tile's K fragments are read before this tile's MFMAs (a
+      // skipped tile's are read too: in bounds, and the reads overlap); with
+      // the registers the rows of o take (ADD), one tile at a time
+      if constexpr (ADD) {
+#pragma unroll
+        for (int kt = 0; kt < lKB / 16; ++kt) {
+          if ((onmask >> kt) & 1) {
+            Frag<bf16> af[lD / 32];
+#pragma unroll
+            for (int p = 0; p < lD / 32; ++p) af[p] = lds_frag8(Kb + kofs + 16 * kt * lS + 32 * p);
+#pragma unroll
+            for (int p = 0; p < lD / 32; ++p)
+#pragma unroll
+              for (int nq = 0; nq < kNQ; ++nq) sacc[kt][nq] = mfma(af[p], qf[nq][p], sacc[kt][nq]);
+          }
+        }
+      } else {
+      Frag<bf16> afc[lD / 32], afn[lD / 32];
+#pragma unroll
+      for (int p = 0; p < lD / 32; ++p) afc[p] = lds_frag8(Kb + kofs + 32 * p);
 #pragma unroll
       for (int kt = 0; kt < lKB / 16; ++kt) {
-        if ((onmask >> kt) & 1) {
-          Frag<bf16> af[lD / 32];
+        if (kt + 1 < lKB / 16) {
 #pragma unroll
-          for (int p = 0; p < lD / 32; ++p) af[p] = lds_frag8(Kb + kofs + 16 * kt * lS + 32 * p);
+          for (int p = 0; p < lD / 32; ++p) afn[p] = lds_frag8(Kb + kofs + 16 * (kt + 1) * lS + 32 * p);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if ((onmask >> kt) & 1) {
 #pragma unroll
           for (int p = 0; p < lD / 32; ++p)
 #pragma unroll
-            for (int nq = 0; nq < kNQ; ++nq) sacc[kt][nq] = mfma(af[p], qf[nq][p], sacc[kt][nq]);
+            for (int nq = 0; nq < kNQ; ++nq) sacc[kt][nq] = mfma(afc[p], qf[nq][p], sacc[kt][nq]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + 1 < lKB / 16) {
+#pragma unroll
+          for (int p = 0; p < lD / 32; ++p) afc[p] = afn[p];
+        }
+      }
       }
 
       // the tile's last block: the next tile's queries (into the registers
       // of the fragments just used) and the rows of o to add onto, loaded
       // now so that they arrive during the rest of the block
       if (more) load_q(ti + 1, qnext);
-      if (last && addl) {
+      if (ADD && last && addl) {
 #pragma unroll
         for (int nq = 0; nq < kNQ; ++nq) {
           const int tr = min(qb + 16 * nq + j, T_ - 1);
@@ -464,7 +494,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void swa_long_kernel(const bf16* __r
 #pragma unroll
           for (int dt = 0; dt < lD / 16; ++dt) {
             f32x4 val = oacc[dt][nq] * inv;
-            if (add)
+            if (ADD && add)
               val += f32x4{static_cast<float>(oraw[nq][dt][0]), static_cast<float>(oraw[nq][dt][1]),
                            static_cast<float>(oraw[nq][dt][2]), static_cast<float>(oraw[nq][dt][3])};
             store4(orow + 16 * dt + 4 * g, val);
@@ -500,20 +530,21 @@ hipError_t launch_swa_long(const PrefillArgs& p, int add_from, hipStream_t s) {
   const long long units = (long long)p.B * (p.H / HPW);
   const long long grid = xcd_grouped_grid(units, nruns);
   if (grid > INT32_MAX || units > INT32_MAX) return hipErrorInvalidValue;
-#define GDN_LONG_LAUNCH(NH)                                                                             \
+#define GDN_LONG_LAUNCH(NH, AD)                                                                         \
   do {                                                                                                  \
-    hipError_t e = hipFuncSetAttribute((const void*)swa_long_kernel<W, NS, NH>,                         \
+    hipError_t e = hipFuncSetAttribute((const void*)swa_long_kernel<W, NS, NH, AD>,                     \
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);                \
     if (e != hipSuccess) return e;                                                                      \
-    hipLaunchKernelGGL((swa_long_kernel<W, NS, NH>), dim3((unsigned)grid), dim3(64 * W), lds, s,        \
+    hipLaunchKernelGGL((swa_long_kernel<W, NS, NH, AD>), dim3((unsigned)grid), dim3(64 * W), lds, s,    \
                        (const bf16*)p.q, (const bf16*)p.k, (const bf16*)p.v, (bf16*)p.o, p.T, p.H,      \
                        p.Hkv, p.n_sink, p.window, add_from, p.w_swa, tpw, nruns, (int)units);           \
   } while (0)
+  const bool add = add_from < p.T;
   switch (HPW) {
-    case 8: GDN_LONG_LAUNCH(8); break;
-    case 4: GDN_LONG_LAUNCH(4); break;
-    case 2: GDN_LONG_LAUNCH(2); break;
-    default: GDN_LONG_LAUNCH(1); break;
+    case 8: if (add) GDN_LONG_LAUNCH(8, true); else GDN_LONG_LAUNCH(8, false); break;
+    case 4: if (add) GDN_LONG_LAUNCH(4, true); else GDN_LONG_LAUNCH(4, false); break;
+    case 2: if (add) GDN_LONG_LAUNCH(2, true); else GDN_LONG_LAUNCH(2, false); break;
+    default: if (add) GDN_LONG_LAUNCH(1, true); else GDN_LONG_LAUNCH(1, false); break;
   }
 #undef GDN_LONG_LAUNCH
   return hipGetLastError();
