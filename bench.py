@@ -181,6 +181,7 @@ KERNEL_SOURCES = {
     "gdn_prep_kernel+linear_chunk_kernel": ("gdn_prep.h", "gdn_prep.hip", "gdn_scan_full.hip",
                                             "linear_chunk.hip", "common.h"),
     "gla_prep_kernel+linear_chunk_kernel": ("gla_prep.hip", "linear_chunk.hip", "common.h"),
+    "gdn_prep_kernel+gdn_linear_layer_kernel": ("gdn_prep.h", "gdn_prep.hip", "gdn_layer.hip", "common.h"),
     "gdn_scan_full_kernel": ("gdn_prep.h", "gdn_scan_full.hip", "swa_tile.h", "common.h"),
     "swa_ring_kernel": ("swa.hip", "swa_tile.h", "common.h"),
     "swa_kernel": ("swa.hip", "swa_tile.h", "common.h"),

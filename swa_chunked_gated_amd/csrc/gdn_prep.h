@@ -96,6 +96,21 @@ __device__ __forceinline__ void put4v(T* base, int off, const f32x4& x) {  // 4 
     store4(base + off, x);
   }
 }
+// Four values as T, stored nontemporally: the light preparation's tiles
+// stream out and are read back by the next launch, long after L2 would have
+// dropped them, so they should not take L2 lines from the K rows that the
+// other query heads of the chunk are about to read.
+template <class T>
+__device__ __forceinline__ void put4nt(T* base, int off, const f32x4& x) {
+  if constexpr (sizeof(T) == 2) {
+    const bf16x4 y = bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
+                            static_cast<bf16>(x[3])};
+    __builtin_nontemporal_store(__builtin_bit_cast(unsigned long long, y),
+                                reinterpret_cast<unsigned long long*>(base + off));
+  } else {
+    __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(base + off));
+  }
+}
 template <bool DEV>
 __device__ __forceinline__ void put1f(float* base, int off, float x) {
   if constexpr (DEV) {
@@ -459,7 +474,11 @@ __device__ __forceinline__ void gdn_prep_chunk(
       for (int m = 0; m < 4; ++m) {
         const int r = 16 * R + 4 * m + rr;
         const f32x4 x = (s0 >> 4) <= R ? tm[R][m] * bb : zero4();
-        put4v<DEV>(tb, r * kC + acc_pos(s0), x);
+        if constexpr (DEV) {
+          put4v<DEV>(tb, r * kC + acc_pos(s0), x);
+        } else {
+          put4nt(tb, r * kC + acc_pos(s0), x);
+        }
         if constexpr (TM) put4v<DEV>(wtm + ci * (kC * kC), r * kC + s0, (s0 >> 4) <= R ? tm[R][m] : zero4());
       }
   }

@@ -15,36 +15,59 @@ using prep::kC;
 using prep::PrepSmem;
 
 template <class T, int D, bool FULL, bool TM = false>
-__global__ __launch_bounds__(64) void gdn_prep_kernel(
+__global__ __launch_bounds__(256) void gdn_prep_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ a, const float* __restrict__ b, T* __restrict__ wtb,
     T* __restrict__ wwm, T* __restrict__ wktg, T* __restrict__ wa,
     float* __restrict__ wut, float* __restrict__ wg, int T_, int H, int Hkv, int n_sink,
     int window, int nch, T* __restrict__ wtm) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  // the G query heads of one (chunk, KV head) run on one XCD and share the
-  // chunk's K rows through its L2; y is the sequence
+  // The G query heads of one (chunk, KV head) read the same K rows: GW of
+  // them (blockDim.x / 64, a divisor of G) are the waves of one workgroup, so
+  // their reads meet on one compute unit, and the G / GW workgroups of the
+  // unit run on one XCD and share the rows through its L2; y is the sequence.
+  // Each wave works alone in its own slice of the LDS.
   const int G = H / Hkv;
+  const int GW = blockDim.x >> 6;
+  const int wv = wave_id();
   int unit, member;
-  if (!xcd_grouped(blockIdx.x, G, nch * Hkv, unit, member)) return;
+  if (!xcd_grouped(blockIdx.x, G / GW, nch * Hkv, unit, member)) return;
   const int c = unit % nch;
-  const int h = (unit / nch) * G + member;
+  const int h = (unit / nch) * G + member * GW + wv;
   prep::gdn_prep_chunk<T, D, FULL, false, TM>(q, k, v, a, b, wtb, wwm, wktg, wa, wut, wg, T_, H, Hkv,
-                                              n_sink, window, nch, c, h, blockIdx.y, smem_raw, wtm);
+                                              n_sink, window, nch, c, h, blockIdx.y,
+                                              smem_raw + wv * PrepSmem<T, D, FULL>::bytes, wtm);
+}
+
+// Waves per workgroup of the preparation kernel: query heads of one KV head,
+// up to 4 (48 KiB of LDS for the light preparation); one for the full
+// preparation, whose 45 KiB per wave leave no room for more.
+template <class T, int D, bool FULL>
+int prep_heads_per_workgroup(int G) {
+  if (FULL) return 1;
+  return G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
+}
+
+template <class T, int D, bool FULL, bool TM>
+hipError_t launch_prep_kernel(const PrefillArgs& p, int nch, void* tm, hipStream_t s) {
+  using SM = PrepSmem<T, D, FULL>;
+  auto kern = gdn_prep_kernel<T, D, FULL, TM>;
+  const int G = p.H / p.Hkv;
+  const int GW = prep_heads_per_workgroup<T, D, FULL>(G);
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     GW * SM::bytes);
+  if (e != hipSuccess) return e;
+  const GdnWorkspace w = gdn_workspace_layout(p.workspace, p.B, p.H, nch, D, sizeof(T), FULL);
+  const dim3 grid(xcd_grouped_grid((long long)nch * p.Hkv, G / GW), p.B);
+  hipLaunchKernelGGL(kern, grid, dim3(64 * GW), GW * SM::bytes, s, (const T*)p.q,
+                     (const T*)p.k, (const T*)p.v, p.a, p.b, (T*)w.tb, (T*)w.wm,
+                     (T*)w.ktg, (T*)w.a, w.ut, w.g, p.T, p.H, p.Hkv, p.n_sink, p.window, nch, (T*)tm);
+  return hipGetLastError();
 }
 
 template <class T, int D, bool FULL>
 hipError_t launch_prep_t(const PrefillArgs& p, int nch, hipStream_t s) {
-  using SM = PrepSmem<T, D, FULL>;
-  auto kern = gdn_prep_kernel<T, D, FULL>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, SM::bytes);
-  if (e != hipSuccess) return e;
-  const GdnWorkspace w = gdn_workspace_layout(p.workspace, p.B, p.H, nch, D, sizeof(T), FULL);
-  const dim3 grid(xcd_grouped_grid((long long)nch * p.Hkv, p.H / p.Hkv), p.B);
-  hipLaunchKernelGGL(kern, grid, dim3(64), SM::bytes, s, (const T*)p.q,
-                     (const T*)p.k, (const T*)p.v, p.a, p.b, (T*)w.tb, (T*)w.wm,
-                     (T*)w.ktg, (T*)w.a, w.ut, w.g, p.T, p.H, p.Hkv, p.n_sink, p.window, nch, (T*)nullptr);
-  return hipGetLastError();
+  return launch_prep_kernel<T, D, FULL, false>(p, nch, nullptr, s);
 }
 
 template <class T, int D>
@@ -94,17 +117,7 @@ GdnWorkspace gdn_workspace_layout(void* base, int B, int H, int nch, int D, size
 
 hipError_t launch_gdn_prep_tm(const PrefillArgs& p, int nch, void* tm, hipStream_t s) {
   if (!p.bf16 || p.D != 128) return hipErrorInvalidValue;
-  using SM = PrepSmem<bf16, 128, false>;
-  auto kern = gdn_prep_kernel<bf16, 128, false, true>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, SM::bytes);
-  if (e != hipSuccess) return e;
-  const GdnWorkspace w = gdn_workspace_layout(p.workspace, p.B, p.H, nch, 128, sizeof(bf16), false);
-  const dim3 grid(xcd_grouped_grid((long long)nch * p.Hkv, p.H / p.Hkv), p.B);
-  hipLaunchKernelGGL(kern, grid, dim3(64), SM::bytes, s, (const bf16*)p.q, (const bf16*)p.k,
-                     (const bf16*)p.v, p.a, p.b, (bf16*)w.tb, (bf16*)nullptr, (bf16*)nullptr,
-                     (bf16*)nullptr, (float*)nullptr, w.g, p.T, p.H, p.Hkv, p.n_sink, p.window, nch,
-                     (bf16*)tm);
-  return hipGetLastError();
+  return launch_prep_kernel<bf16, 128, false, true>(p, nch, tm, s);
 }
 
 hipError_t launch_gdn_prep(const PrefillArgs& p, int nch, hipStream_t s) {
