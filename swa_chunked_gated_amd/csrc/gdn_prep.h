@@ -269,15 +269,26 @@ struct PrepSmem {
 // workgroup barrier: the wave's own LDS operations complete in program order.
 // TM (light preparation only): also write Tm itself, [64][64] in natural
 // column order, to wtm (the backward pass needs Tm^T products).
-template <class T, int D, bool FULL, bool DEV = false, bool TM = false>
+// SH = 4 (light preparation only): the four waves of the workgroup take four
+// query heads of one KV head and the same chunk, whose K K^T they share:
+// smem_raw is then the workgroup's LDS, one PrepSmem slice per wave in wave
+// order, wv this wave's index; each wave forms a quarter of the ten 16x16
+// blocks of K K^T on and below the diagonal (loading only the K rows those
+// blocks need) and writes them, scaled by each head's gates, into every
+// wave's solve buffer, between two workgroup barriers.
+template <class T, int D, bool FULL, bool DEV = false, bool TM = false, int SH = 1>
 __device__ __forceinline__ void gdn_prep_chunk(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ a, const float* __restrict__ b, T* __restrict__ wtb,
     T* __restrict__ wwm, T* __restrict__ wktg, T* __restrict__ wa,
     float* __restrict__ wut, float* __restrict__ wg, int T_, int H, int Hkv, int n_sink, int window,
-    int nch, int c, int h, int bi, unsigned char* smem_raw, T* __restrict__ wtm = nullptr) {
+    int nch, int c, int h, int bi, unsigned char* smem_raw, T* __restrict__ wtm = nullptr,
+    int wv = 0) {
   static_assert(!(TM && FULL), "Tm is written by the light preparation");
+  static_assert(SH == 1 || (SH == 4 && !FULL), "shared K K^T: light preparation, four heads");
   using SM = PrepSmem<T, D, FULL>;
+  unsigned char* const wg_raw = smem_raw;      // SH = 4: the workgroup's slices
+  if constexpr (SH > 1) smem_raw += wv * SM::bytes;
   using LL = typename SM::LL;
   constexpr int EPC = 16 / (int)sizeof(T);     // elements per 16-byte piece
   constexpr int QV = 8 / EPC;                  // 16-byte pieces per fragment
@@ -317,12 +328,18 @@ __device__ __forceinline__ void gdn_prep_chunk(
   asm volatile("" ::: "memory");   // the gates' loads go out first
 
   // ---- operand pieces: lane holds rows 16 mt + l16, dims 32 p + 8 lg .. +7
-  V16 kr[4][KS][QV];
+  // (SH = 4: slot sl holds row block kblk(sl) of this wave's blocks; waves 0
+  // and 1 form blocks (m, m), (m+1, m), (m+1, m+1) of m = 2 wv from row blocks
+  // m, m+1, waves 2 and 3 blocks (wv, 0), (wv, 1) from row blocks 0, 1, wv)
+  constexpr int NKB = SH > 1 ? 3 : 4;
+  auto kblk = [&](int sl) { return SH == 1 ? sl : wv == 1 ? 2 + sl : sl < 2 ? sl : wv; };
+  V16 kr[NKB][KS][QV];
   V16 qr[FULL ? 4 : 1][FULL ? KS : 1][QV];
   const bool whole = i0 + kC <= iend;          // uniform: no row past the stream
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int r = min(16 * mt + l16, iend - 1 - i0);
+  for (int mt = 0; mt < NKB; ++mt) {
+    if (SH > 1 && mt == 2 && wv < 2) break;
+    const int r = min(16 * kblk(mt) + l16, iend - 1 - i0);
 #pragma unroll
     for (int p = 0; p < KS; ++p)
 #pragma unroll
@@ -371,8 +388,49 @@ __device__ __forceinline__ void gdn_prep_chunk(
 
   // ---- L = strictly lower (b_r 2^{g_r - g_s} k_r.k_s); full: also
   // A = [s <= r] 2^{g_r - g_s} q_r.k_s
+  if constexpr (SH > 1) {
+    __syncthreads();                           // every head's gates are in LDS
+    // block (mt, nt) of K K^T, scaled by the gates of each head of the
+    // workgroup into that head's solve buffer
+    auto emit = [&](int mt, int nt, const f32x4& acc) {
+      const int r0 = 16 * mt + 4 * lg;
+      const int s = 16 * nt + l16;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+      for (int hh = 0; hh < SH; ++hh) {
+        float* Lh = reinterpret_cast<float*>(wg_raw + hh * SM::bytes + SM::bytesT);
+        const float* lh = Lh + SM::nL;         // that head's g, then gamma, then b
+        const f32x4 lr = *reinterpret_cast<const f32x4*>(&lh[r0]);
+        const f32x4 br = *reinterpret_cast<const f32x4*>(&lh[2 * kC + r0]);
+        const float ls = lh[s];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = r0 + i;
+          const float dec = __builtin_amdgcn_exp2f(fminf(lr[i] - ls, 0.f));
+          Lh[lidx<LL>(r, s)] = s < r ? br[i] * dec * acc[i] : 0.f;
+        }
+      }
+    };
+    auto kkt = [&](int sm, int sn) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int p = 0; p < KS; ++p) acc = mfma(frag_of(kr[sm][p]), frag_of(kr[sn][p]), acc);
+      return acc;
+    };
+    if (wv < 2) {
+      const int m = 2 * wv;
+      const f32x4 t00 = kkt(0, 0), t10 = kkt(1, 0), t11 = kkt(1, 1);
+      emit(m, m, t00);
+      emit(m + 1, m, t10);
+      emit(m + 1, m + 1, t11);
+    } else {
+      const f32x4 t0 = kkt(2, 0), t1 = kkt(2, 1);
+      emit(wv, 0, t0);
+      emit(wv, 1, t1);
+    }
+    __syncthreads();                           // every block of this head's L is in LDS
+  }
+#pragma unroll
+  for (int mt = 0; mt < (SH > 1 ? 0 : 4); ++mt) {
     const int r0 = 16 * mt + 4 * lg;
     const f32x4 lr = *reinterpret_cast<const f32x4*>(&lgs[r0]);
     const f32x4 br = *reinterpret_cast<const f32x4*>(&bet[r0]);

@@ -14,7 +14,7 @@ namespace {
 using prep::kC;
 using prep::PrepSmem;
 
-template <class T, int D, bool FULL, bool TM = false>
+template <class T, int D, bool FULL, bool TM = false, int SH = 1>
 __global__ __launch_bounds__(256) void gdn_prep_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ a, const float* __restrict__ b, T* __restrict__ wtb,
@@ -26,7 +26,8 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
   // them (blockDim.x / 64, a divisor of G) are the waves of one workgroup, so
   // their reads meet on one compute unit, and the G / GW workgroups of the
   // unit run on one XCD and share the rows through its L2; y is the sequence.
-  // Each wave works alone in its own slice of the LDS.
+  // Each wave has its own slice of the LDS; with SH = 4 (GW = 4) the four
+  // waves also share the chunk's K K^T.
   const int G = H / Hkv;
   const int GW = blockDim.x >> 6;
   const int wv = wave_id();
@@ -34,9 +35,15 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
   if (!xcd_grouped(blockIdx.x, G / GW, nch * Hkv, unit, member)) return;
   const int c = unit % nch;
   const int h = (unit / nch) * G + member * GW + wv;
-  prep::gdn_prep_chunk<T, D, FULL, false, TM>(q, k, v, a, b, wtb, wwm, wktg, wa, wut, wg, T_, H, Hkv,
-                                              n_sink, window, nch, c, h, blockIdx.y,
-                                              smem_raw + wv * PrepSmem<T, D, FULL>::bytes, wtm);
+  if constexpr (SH > 1) {
+    prep::gdn_prep_chunk<T, D, FULL, false, TM, SH>(q, k, v, a, b, wtb, wwm, wktg, wa, wut, wg, T_, H,
+                                                    Hkv, n_sink, window, nch, c, h, blockIdx.y, smem_raw,
+                                                    wtm, wv);
+  } else {
+    prep::gdn_prep_chunk<T, D, FULL, false, TM>(q, k, v, a, b, wtb, wwm, wktg, wa, wut, wg, T_, H, Hkv,
+                                                n_sink, window, nch, c, h, blockIdx.y,
+                                                smem_raw + wv * PrepSmem<T, D, FULL>::bytes, wtm);
+  }
 }
 
 // Waves per workgroup of the preparation kernel: query heads of one KV head,
@@ -51,9 +58,12 @@ int prep_heads_per_workgroup(int G) {
 template <class T, int D, bool FULL, bool TM>
 hipError_t launch_prep_kernel(const PrefillArgs& p, int nch, void* tm, hipStream_t s) {
   using SM = PrepSmem<T, D, FULL>;
-  auto kern = gdn_prep_kernel<T, D, FULL, TM>;
   const int G = p.H / p.Hkv;
   const int GW = prep_heads_per_workgroup<T, D, FULL>(G);
+  auto kern = gdn_prep_kernel<T, D, FULL, TM>;
+  if constexpr (!FULL) {
+    if (GW == 4) kern = gdn_prep_kernel<T, D, FULL, TM, 4>;
+  }
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      GW * SM::bytes);
   if (e != hipSuccess) return e;
