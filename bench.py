@@ -52,6 +52,7 @@ PEAK_BF16 = 2.5e15      # dense bf16 MFMA FLOP/s
 PEAK_HBM = 8.0e12       # bytes/s
 CHUNK = 64
 HEADLINE = "longctx_b8_t32768"
+WARM_S = 0.25           # seconds of untimed warm-up steps for the workloads besides the headline
 
 
 # ------------------------------------------------------- algorithmic work
@@ -395,10 +396,13 @@ def time_call(fn, reps, warmup):
     return float(np.median(ms)), float(np.mean(ms))
 
 
-def bench_prefill(name, steps, warmup, parts=True):
+def bench_prefill(name, steps, warmup, parts=True, warm_s=0.0):
     """One workload's layer: K timed steps (wall clock between
     synchronisations, and per-step events), then each call of the split
-    layer event-timed on its own for the roofline."""
+    layer event-timed on its own for the roofline.  Warm-up: `warmup` untimed
+    steps, then (warm_s > 0) further untimed steps until warm_s seconds have
+    passed, so that the GPU's clocks have ramped up before the timed steps of
+    a short workload; the entry's "warmup" counts them all."""
     import torch
     import swa_chunked_gated_amd as gl
     from workloads import WORKLOADS, make_prefill_inputs
@@ -431,6 +435,15 @@ def bench_prefill(name, steps, warmup, parts=True):
 
     for _ in range(warmup):
         layer()
+    n_warm = warmup
+    if warm_s > 0:
+        torch.cuda.synchronize()
+        t_w = time.perf_counter()
+        while time.perf_counter() - t_w < warm_s:
+            for _ in range(4):
+                layer()
+            n_warm += 4
+            torch.cuda.synchronize()
     ev = _events(steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -445,7 +458,7 @@ def bench_prefill(name, steps, warmup, parts=True):
     res = {"workload": name, "B": w.B, "T": w.T, "H": w.H, "Hkv": w.Hkv, "d": w.d,
            "n_sink": w.n_sink, "window": w.window, "update": w.update, "dtype": w.dtype,
            "state_out": w.write_state, "shortconv": w.shortconv,
-           "steps": steps, "ms_per_step": sec * 1e3, "tokens_per_s": w.B * w.T / sec,
+           "steps": steps, "warmup": n_warm, "ms_per_step": sec * 1e3, "tokens_per_s": w.B * w.T / sec,
            "event_ms_median": float(np.median(ev_ms)), "event_ms_mean": float(np.mean(ev_ms)),
            "algorithmic_gflop": (f_lin + f_swa) / 1e9,
            "layer_frac_mfma": (f_lin + f_swa) / sec / PEAK_BF16}
@@ -674,7 +687,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default="all",
                     choices=["all", "headline", "longctx", "llama", "tiny", "dgd", "decode", "qwen32b",
                              "qwen32b_decode", "copy", "backward"])
@@ -700,7 +713,7 @@ def main():
             sys.exit(2)
         torch.cuda.set_device(0)
         if args.only in single:
-            out = bench_prefill(single[args.only], args.steps, args.warmup, parts=parts)
+            out = bench_prefill(single[args.only], args.steps, args.warmup, parts=parts, warm_s=WARM_S)
         elif args.only == "decode":
             out = bench_decode(steps=args.steps, warmup=args.warmup)
         elif args.only == "qwen32b_decode":
@@ -713,7 +726,8 @@ def main():
             return
         else:
             for n in ("qwen32b_t8192_gdn", "qwen32b_t8192_gla"):
-                print(json.dumps(bench_prefill(n, args.steps, args.warmup, parts=parts)), flush=True)
+                print(json.dumps(bench_prefill(n, args.steps, args.warmup, parts=parts, warm_s=WARM_S)),
+                      flush=True)
             return
         print(json.dumps(out), flush=True)
         return
@@ -745,7 +759,7 @@ def main():
     also = {}
     if args.only == "all":
         for n in ("tiny_fp32", "llama8b_t4096", "qwen32b_t8192_gdn", "qwen32b_t8192_gla", "dgd_b8_t8192"):
-            also[n] = bench_prefill(n, args.steps, args.warmup, parts=True)
+            also[n] = bench_prefill(n, args.steps, args.warmup, parts=True, warm_s=WARM_S)
             also[n]["cpu_baseline"] = cpu.get(n)
             print(f"# {n} done", file=sys.stderr, flush=True)
         for n in CPU_BWD_SAMPLES:
