@@ -286,7 +286,9 @@ __device__ __forceinline__ void sm_values(const KeyPair (&kp)[NP], const f32x4 (
 // LIN_ONLY: the linear branch alone (windows past the ring, the softmax
 // branch added by its own launch afterwards): the softmax waves form only A
 // and keep the K, V, TB and gates prefetch; the state waves store w_lin o_lin.
-template <bool LIN_ONLY, int NT>
+// NB: 32-key ring blocks a softmax row group reads besides the sinks: 5 for
+// windows up to 128, 3 for windows up to 64.
+template <bool LIN_ONLY, int NT, int NB = 5>
 __device__ __forceinline__ void gdn_layer_body(
     const bf16* q, const bf16* k, const bf16* v, const bf16* w_tb, const float* w_g,
     bf16* __restrict__ o,
@@ -731,7 +733,8 @@ __device__ __forceinline__ void gdn_layer_body(
   // A block needs the window mask iff some of its keys lie outside some
   // row's window; the other blocks are attended by all 16 rows.
   auto partial = [&](int b) { return !(32 * b >= 16 * jq + 16 && 32 * b + 31 <= 16 * jq + window); };
-  const bool mk0 = partial(pb), mk1 = partial(2), mk2 = partial(3), mk3 = partial(4), mk4 = partial(bX);
+  const bool mk0 = partial(pb), mk1 = partial(NB == 3 ? pb + 1 : 2), mk2 = partial(NB == 3 ? pb + 2 : 3),
+             mk3 = partial(4), mk4 = partial(bX);
   // key 16 hf + 4 g + i of block b is in row j's window iff
   // e0 + 32 b + 16 hf + i lies in [0, window)
   const int e0 = 4 * g - 16 * jq - j - 1;
@@ -862,8 +865,11 @@ __device__ __forceinline__ void gdn_layer_body(
     sa[2] = kmma(kc, zero4());
     sa[3] = kmma(kd, zero4());
     __builtin_amdgcn_sched_barrier(0);
-    kfr(K1, 32, kc);
-    kfr(K1, 48, kd);
+    // NB = 3: the third block pb + 2 is ring chunk c + 1's rows 32 pb .. (for
+    // pb = 0 the same rows as block 2, recomputed so that every wave runs the
+    // same code)
+    kfr(K1, NB == 3 ? 32 * pb : 32, kc);
+    kfr(K1, NB == 3 ? 32 * pb + 16 : 48, kd);
     st[1][0] = kmma(ka, zero4());
     st[1][1] = kmma(kb2, zero4());
     // A rows: [s <= r] 2^{g_r - g_s} q_r.k_s, columns in acc order; tile
@@ -883,24 +889,40 @@ __device__ __forceinline__ void gdn_layer_body(
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    kfr(K2, 0, ka);
-    kfr(K2, 16, kb2);
-    st[2][0] = kmma(kc, zero4());
-    st[2][1] = kmma(kd, zero4());
-    __builtin_amdgcn_sched_barrier(0);
-    kfr(KX, 32, kc);
-    kfr(KX, 48, kd);
-    st[3][0] = kmma(ka, zero4());
-    st[3][1] = kmma(kb2, zero4());
-    __builtin_amdgcn_sched_barrier(0);
-    kfr(KSk, 0, ka);
-    st[4][0] = kmma(kc, zero4());
-    st[4][1] = kmma(kd, zero4());
-    __builtin_amdgcn_sched_barrier(0);
-    st[5][0] = kmma(ka, sbias);
-    st[5][1] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if constexpr (NB == 3) {
+      kfr(KSk, 0, ka);
+      st[2][0] = kmma(kc, zero4());
+      st[2][1] = kmma(kd, zero4());
+      __builtin_amdgcn_sched_barrier(0);
+      st[5][0] = kmma(ka, sbias);
+      st[5][1] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      // slot 0: block pb (chunk c's own scores); slot 1: block pb + 1 (block
+      // 2 for pb = 1, chunk c's second half for pb = 0); slot 2: block pb + 2
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) st[0][hf] = pb ? sa[2 + hf] : sa[hf];
+      for (int hf = 0; hf < 2; ++hf) {
+        st[0][hf] = pb ? sa[2 + hf] : sa[hf];
+        st[1][hf] = pb ? st[1][hf] : sa[2 + hf];
+      }
+    } else {
+      kfr(K2, 0, ka);
+      kfr(K2, 16, kb2);
+      st[2][0] = kmma(kc, zero4());
+      st[2][1] = kmma(kd, zero4());
+      __builtin_amdgcn_sched_barrier(0);
+      kfr(KX, 32, kc);
+      kfr(KX, 48, kd);
+      st[3][0] = kmma(ka, zero4());
+      st[3][1] = kmma(kb2, zero4());
+      __builtin_amdgcn_sched_barrier(0);
+      kfr(KSk, 0, ka);
+      st[4][0] = kmma(kc, zero4());
+      st[4][1] = kmma(kd, zero4());
+      __builtin_amdgcn_sched_barrier(0);
+      st[5][0] = kmma(ka, sbias);
+      st[5][1] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) st[0][hf] = pb ? sa[2 + hf] : sa[hf];
+    }
     // ---- window masks (blocks with keys outside some row's window) and the
     // row maximum
     // (e0 passes through an empty asm so that the compares stay in the loop:
@@ -908,16 +930,23 @@ __device__ __forceinline__ void gdn_layer_body(
     int e = e0;
     asm volatile("" : "+v"(e));
     if (mk0) mask_block(st[0], pb, e);
-    if (mk1) mask_block(st[1], 2, e);
-    if (mk2) mask_block(st[2], 3, e);
-    if (mk3) mask_block(st[3], 4, e);
-    if (mk4) mask_block(st[4], bX, e);
+    if constexpr (NB == 3) {
+      if (mk1) mask_block(st[1], pb + 1, e);
+      if (mk2) mask_block(st[2], pb + 2, e);
+    } else {
+      if (mk1) mask_block(st[1], 2, e);
+      if (mk2) mask_block(st[2], 3, e);
+      if (mk3) mask_block(st[3], 4, e);
+      if (mk4) mask_block(st[4], bX, e);
+    }
     float m = -INFINITY;
 #pragma unroll
-    for (int sl = 0; sl < 6; ++sl)
+    for (int sl = 0; sl < 6; ++sl) {
+      if (NB == 3 && (sl == 3 || sl == 4)) continue;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
         m = score_max3(score_max3(m, st[sl][hf][0], st[sl][hf][1]), st[sl][hf][2], st[sl][hf][3]);
+    }
     m = max_lane_groups(m);
     m = m == -INFINITY ? 0.f : m;      // a row with no key (past the sequence): weights 0
     lds_barrier();                       // B1
@@ -955,22 +984,33 @@ __device__ __forceinline__ void gdn_layer_body(
     vfr(Vc, 32 * pb, va);
     pa = pfr(st[0]);
     __builtin_amdgcn_sched_barrier(0);
-    vfr(V1, 0, vb2);
-    pb2 = pfr(st[1]);
-    vmma(va, pa);
-    __builtin_amdgcn_sched_barrier(0);
-    vfr(V1, 32, va);
-    pa = pfr(st[2]);
-    vmma(vb2, pb2);
-    __builtin_amdgcn_sched_barrier(0);
-    vfr(V2, 0, vb2);
-    pb2 = pfr(st[3]);
-    vmma(va, pa);
-    __builtin_amdgcn_sched_barrier(0);
-    vfr(VX, 32, va);
-    pa = pfr(st[4]);
-    vmma(vb2, pb2);
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NB == 3) {
+      vfr(pb ? V1 : Vc, pb ? 0 : 32, vb2);     // block pb + 1
+      pb2 = pfr(st[1]);
+      vmma(va, pa);
+      __builtin_amdgcn_sched_barrier(0);
+      vfr(V1, 32 * pb, va);                    // block pb + 2
+      pa = pfr(st[2]);
+      vmma(vb2, pb2);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      vfr(V1, 0, vb2);
+      pb2 = pfr(st[1]);
+      vmma(va, pa);
+      __builtin_amdgcn_sched_barrier(0);
+      vfr(V1, 32, va);
+      pa = pfr(st[2]);
+      vmma(vb2, pb2);
+      __builtin_amdgcn_sched_barrier(0);
+      vfr(V2, 0, vb2);
+      pb2 = pfr(st[3]);
+      vmma(va, pa);
+      __builtin_amdgcn_sched_barrier(0);
+      vfr(VX, 32, va);
+      pa = pfr(st[4]);
+      vmma(vb2, pb2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // the sink block: 16 keys, read once and used for both halves (the
     // second half weighs 0)
 #pragma unroll
@@ -1011,13 +1051,18 @@ __device__ __forceinline__ void gdn_layer_body(
   }
 }
 
+template <int NB>
 __global__ __launch_bounds__(kThreads) void gdn_layer_kernel(
     const bf16* q, const bf16* k, const bf16* v, const bf16* w_tb, const float* w_g,
     bf16* __restrict__ o,
     float* __restrict__ state_out, int B, int T_, int H, int Hkv, int n_sink, int window,
     int nch, int write_state, float w_lin, float w_swa, int seg_len, const float* s_in) {
-  gdn_layer_body<false, 2>(q, k, v, w_tb, w_g, o, state_out, B, T_, H, Hkv, n_sink, window, nch, write_state,
-                           w_lin, w_swa, seg_len, s_in, 0);
+  gdn_layer_body<false, 2, NB>(q, k, v, w_tb, w_g, o, state_out, B, T_, H, Hkv, n_sink, window, nch,
+                               write_state, w_lin, w_swa, seg_len, s_in, 0);
+}
+// the instance for a window: three ring blocks per row group up to 64 keys
+inline decltype(&gdn_layer_kernel<5>) layer_kernel_for(int window) {
+  return window <= 64 ? gdn_layer_kernel<3> : gdn_layer_kernel<5>;
 }
 
 __global__ __launch_bounds__(kThreads) void gdn_linear_layer_kernel(
@@ -1434,11 +1479,12 @@ hipError_t launch_gdn_layer(const PrefillArgs& p, hipStream_t s) {
   const int nch = gdn_stream_chunks(p.T, p.n_sink, p.window);
   hipError_t e = p.prepared ? hipSuccess : launch_gdn_prep(p, nch, s);
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void*)gdn_layer_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  const auto kern = layer_kernel_for(p.window);
+  e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
   if (e != hipSuccess) return e;
   const GdnWorkspace w = gdn_workspace_layout(p.workspace, p.B, p.H, nch, kD, sizeof(bf16), false);
   const dim3 grid(xcd_grouped_grid((long long)p.B * p.Hkv, p.H / p.Hkv));
-  hipLaunchKernelGGL(gdn_layer_kernel, grid, dim3(kThreads), kLdsBytes, s, (const bf16*)p.q,
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), kLdsBytes, s, (const bf16*)p.q,
                      (const bf16*)p.k, (const bf16*)p.v, (const bf16*)w.tb, w.g, (bf16*)p.o,
                      p.state_out, p.B, p.T, p.H, p.Hkv, p.n_sink, p.window, nch,
                      (p.flags & 4) ? 1 : 0, p.w_lin, p.w_swa, nch, (const float*)nullptr);
@@ -1506,9 +1552,10 @@ hipError_t launch_gdn_segmented(const PrefillArgs& p, hipStream_t s) {
                      (const float*)w.n, w.s, p.state_out, C, pl.P, wst ? 1 : 0);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void*)gdn_layer_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  const auto kern = layer_kernel_for(p.window);
+  e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gdn_layer_kernel, dim3(gx, pl.P), dim3(kThreads), kLdsBytes, s, (const bf16*)p.q,
+  hipLaunchKernelGGL(kern, dim3(gx, pl.P), dim3(kThreads), kLdsBytes, s, (const bf16*)p.q,
                      (const bf16*)p.k, (const bf16*)p.v, (const bf16*)w.light.tb, w.light.g, (bf16*)p.o,
                      p.state_out, p.B, p.T, p.H, p.Hkv, p.n_sink, p.window, nch, 0, p.w_lin, p.w_swa,
                      pl.L, (const float*)w.s);

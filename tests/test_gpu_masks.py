@@ -269,7 +269,8 @@ def test_decode_b256_1000_steps_sampled():
 @pytest.mark.parametrize("B,H,Hkv,T,n_sink,window", [(32, 8, 2, 300, 8, 56), (16, 16, 4, 517, 8, 120),
                                                      (32, 8, 2, 400, 16, 128), (32, 8, 8, 250, 0, 1),
                                                      (64, 4, 1, 129, 3, 64), (32, 8, 2, 700, 0, 100),
-                                                     (16, 16, 2, 137, 8, 120)])
+                                                     (16, 16, 2, 137, 8, 120), (32, 8, 2, 333, 16, 63),
+                                                     (32, 8, 2, 270, 5, 65)])
 def test_mask_probe_one_pass_layer(B, H, Hkv, T, n_sink, window):
     """Both branches on many chains (B*H >= 128, window <= 128, n_sink <= 16):
     the layer runs as the one-pass kernel whose softmax rows read keys from a

@@ -293,7 +293,8 @@ def test_many_chain_full_wave_scan():
 @pytest.mark.parametrize("B,H,Hkv,T,n_sink,window", [(8, 32, 8, 300, 8, 56), (16, 16, 4, 517, 8, 120),
                                                      (32, 8, 2, 400, 16, 128), (32, 8, 8, 250, 0, 1),
                                                      (64, 4, 1, 129, 3, 64), (16, 8, 2, 700, 0, 100),
-                                                     (16, 16, 2, 200, 8, 120), (16, 8, 4, 193, 8, 120)])
+                                                     (16, 16, 2, 200, 8, 120), (16, 8, 4, 193, 8, 120),
+                                                     (16, 16, 4, 333, 5, 40), (32, 8, 2, 211, 16, 65)])
 def test_one_pass_layer(B, H, Hkv, T, n_sink, window):
     """Both branches on many chains: the one-pass kernel (state scan and the
     softmax rows of each chunk in one workgroup per chain, o written once);
