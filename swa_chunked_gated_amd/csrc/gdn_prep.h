@@ -96,19 +96,20 @@ __device__ __forceinline__ void put4v(T* base, int off, const f32x4& x) {  // 4 
     store4(base + off, x);
   }
 }
-// Four values as T, stored nontemporally: the light preparation's tiles
-// stream out and are read back by the next launch, long after L2 would have
-// dropped them, so they should not take L2 lines from the K rows that the
-// other query heads of the chunk are about to read.
+// Eight values as T (x then y), stored nontemporally: the light
+// preparation's tiles stream out and are read back by the next launch, long
+// after L2 would have dropped them, so they should not take L2 lines from
+// the K rows that the other query heads of the chunk are about to read.
 template <class T>
-__device__ __forceinline__ void put4nt(T* base, int off, const f32x4& x) {
+__device__ __forceinline__ void put8nt(T* base, int off, const f32x4& x, const f32x4& y) {
   if constexpr (sizeof(T) == 2) {
-    const bf16x4 y = bf16x4{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
-                            static_cast<bf16>(x[3])};
-    __builtin_nontemporal_store(__builtin_bit_cast(unsigned long long, y),
-                                reinterpret_cast<unsigned long long*>(base + off));
+    const bf16x8 v = bf16x8{static_cast<bf16>(x[0]), static_cast<bf16>(x[1]), static_cast<bf16>(x[2]),
+                            static_cast<bf16>(x[3]), static_cast<bf16>(y[0]), static_cast<bf16>(y[1]),
+                            static_cast<bf16>(y[2]), static_cast<bf16>(y[3])};
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(base + off));
   } else {
     __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(base + off));
+    __builtin_nontemporal_store(y, reinterpret_cast<f32x4*>(base + off + 4));
   }
 }
 template <bool DEV>
@@ -513,32 +514,38 @@ __device__ __forceinline__ void gdn_prep_chunk(
       store4(&TBGs[r * SC + acc_pos(s0)], x * gg);
     }
   } else {
-    // lane: columns s0 .. s0 + 3 of rows 16 R + 4 m + (lane / 16); every
-    // row's block row R is known at compile time, and the reads (all issued
-    // before the stores) stay inside the packed buffer: a column block above
-    // the diagonal reads some other row's values, which the select zeroes
-    const int s0 = (lane & 15) * 4;
-    const int rr = lane >> 4;
-    const f32x4 bb = *reinterpret_cast<const f32x4*>(&bet[s0]);
-    f32x4 tm[4][4];
+    // lane: the 8 positions 8 q .. 8 q + 7 (q = lane % 8) of rows 8 it +
+    // lane / 8 in acc order, which hold columns c0 .. c0 + 3 and c0 + 16 ..
+    // c0 + 19 (c0 = 32 (q / 4) + 4 (q % 4)): one 16-byte store per row.
+    // Every row's block row R = it / 2 is known at compile time, and the
+    // reads (all issued before the stores) stay inside the packed buffer: a
+    // column block above the diagonal reads some other row's values, which
+    // the select zeroes.
+    static_assert(!DEV, "the light preparation's tiles are read by later launches");
+    const int q8 = lane & 7;
+    const int c0 = 32 * (q8 >> 2) + 4 * (q8 & 3);
+    const int r8 = lane >> 3;
+    const f32x4 b0 = *reinterpret_cast<const f32x4*>(&bet[c0]);
+    const f32x4 b1 = *reinterpret_cast<const f32x4*>(&bet[c0 + 16]);
+    f32x4 t0[8], t1[8];
 #pragma unroll
-    for (int R = 0; R < 4; ++R)
+    for (int it = 0; it < 8; ++it) {
+      const float* row = &Lf[LL::row0(it >> 1) + (8 * (it & 1) + r8) * LL::stride(it >> 1)];
+      t0[it] = *reinterpret_cast<const f32x4*>(row + c0);
+      t1[it] = *reinterpret_cast<const f32x4*>(row + c0 + 16);
+    }
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
-        tm[R][m] = *reinterpret_cast<const f32x4*>(&Lf[LL::row0(R) + (4 * m + rr) * LL::stride(R) + s0]);
-#pragma unroll
-    for (int R = 0; R < 4; ++R)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int r = 16 * R + 4 * m + rr;
-        const f32x4 x = (s0 >> 4) <= R ? tm[R][m] * bb : zero4();
-        if constexpr (DEV) {
-          put4v<DEV>(tb, r * kC + acc_pos(s0), x);
-        } else {
-          put4nt(tb, r * kC + acc_pos(s0), x);
-        }
-        if constexpr (TM) put4v<DEV>(wtm + ci * (kC * kC), r * kC + s0, (s0 >> 4) <= R ? tm[R][m] : zero4());
+    for (int it = 0; it < 8; ++it) {
+      const int R = it >> 1;
+      const int r = 8 * it + r8;
+      const f32x4 x0 = (c0 >> 4) <= R ? t0[it] * b0 : zero4();
+      const f32x4 x1 = ((c0 + 16) >> 4) <= R ? t1[it] * b1 : zero4();
+      put8nt(tb, r * kC + 8 * q8, x0, x1);
+      if constexpr (TM) {
+        put4v<DEV>(wtm + ci * (kC * kC), r * kC + c0, (c0 >> 4) <= R ? t0[it] : zero4());
+        put4v<DEV>(wtm + ci * (kC * kC), r * kC + c0 + 16, ((c0 + 16) >> 4) <= R ? t1[it] : zero4());
       }
+    }
   }
   put1f<DEV>(wg + ci * (2 * kC), lane, lgs[lane]);
   put1f<DEV>(wg + ci * (2 * kC), kC + lane, gam[lane]);
