@@ -452,6 +452,11 @@ __device__ __forceinline__ void gdn_layer_body(
   // the prefetched TB and gates of chunk c+1 and K, V of chunk c+3; after
   // B3 they commit chunk c+1's queries.
   if (scan_wave) {
+    // Issue priority to the role whose work bounds the chunk step, when both
+    // waves of a SIMD are ready: the state waves when the softmax waves only
+    // form A (here), the softmax waves when they form the softmax rows
+    // (below).
+    if constexpr (LIN_ONLY) __builtin_amdgcn_s_setprio(2);
     // state columns 32 wv .. + 31; tile mt's accumulator row 4 g + i holds
     // d_k = 32 (mt / 2) + 8 g + 4 (mt % 2) + i (see tr_frag_k), and column j
     // of tile nt is d_v = 32 wv + 8 (j / 4) + 4 nt + j % 4, so that a lane's
@@ -690,6 +695,7 @@ __device__ __forceinline__ void gdn_layer_body(
 
   // ---------------------------------------------------------- softmax waves
   const int jq = wv - 4;              // rows 16 jq .. + 15 of each chunk
+  if constexpr (!LIN_ONLY) __builtin_amdgcn_s_setprio(3);
   const int ptid = tid - 256;         // prefetch pieces n = ptid + 256 m
   // prologue (first segment): rows t < n_sink + window carry no linear
   // branch and attend to every key t' <= t: the sinks and ring chunks 0 and
