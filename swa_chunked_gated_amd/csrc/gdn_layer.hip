@@ -452,10 +452,11 @@ __device__ __forceinline__ void gdn_layer_body(
   // the prefetched TB and gates of chunk c+1 and K, V of chunk c+3; after
   // B3 they commit chunk c+1's queries.
   if (scan_wave) {
-    // Issue priority to the role whose work bounds the chunk step, when both
+    // Issue priority to the role whose work bounds the phase, when both
     // waves of a SIMD are ready: the state waves when the softmax waves only
-    // form A (here), the softmax waves when they form the softmax rows
-    // (below).
+    // form A (here); the softmax waves when they form the softmax rows
+    // (below), except between B2 and B3, where the state waves' stores
+    // bound the phase and the softmax waves only commit prefetched tiles.
     if constexpr (LIN_ONLY) __builtin_amdgcn_s_setprio(2);
     // state columns 32 wv .. + 31; tile mt's accumulator row 4 g + i holds
     // d_k = 32 (mt / 2) + 8 g + 4 (mt % 2) + i (see tr_frag_k), and column j
@@ -1037,6 +1038,7 @@ __device__ __forceinline__ void gdn_layer_body(
       for (int dt = 0; dt < 8; ++dt) store4(Xs + l_row - 4 * g + 16 * jq * kSR + 16 * dt, oacc[dt] * f);
     }
     lds_barrier();                       // B2
+    __builtin_amdgcn_s_setprio(0);       // the state waves' stores bound this phase
     // ---- commit K, V of chunk c + 3 into the ring slot chunk c leaves (past
     // the sequence: its clamped last row, a key no row attends), then TB
     // and the gates of chunk c + 1 (their last reads were before B2)
@@ -1054,6 +1056,7 @@ __device__ __forceinline__ void gdn_layer_body(
       if (ptid < 64) put_gates(ptid, pg);
     }
     lds_barrier();                       // B3: the softmax rows are read
+    __builtin_amdgcn_s_setprio(3);
   }
 }
 
