@@ -326,6 +326,28 @@ __global__ __launch_bounds__(512) void gla_prep_kernel(
   }
   __syncthreads();
 
+  // ---- copy K^T 2^{G_C - G} and A out as 16-byte pieces (delta rule: by
+  // waves 1 .. 7 while wave 0 solves for TB; the solve and what follows it
+  // touch neither tile)
+  {
+    const int t0 = DELTA ? tid - 64 : tid;
+    const int nth = DELTA ? NTH - 64 : NTH;
+    if (t0 >= 0) {
+      T* ktg = wktg + ci * (D * kC);
+      T* aa = wa + ci * (kC * kC);
+      for (int i = t0; i < D * kC / VEC; i += nth) {
+        const int r = i / (kC / VEC);
+        const int pc = (i % (kC / VEC)) * VEC;
+        *reinterpret_cast<V16*>(ktg + r * kC + pc) = *reinterpret_cast<const V16*>(&KTs[r * SC + pc]);
+      }
+      for (int i = t0; i < kC * kC / VEC; i += nth) {
+        const int r = i / (kC / VEC);
+        const int pc = (i % (kC / VEC)) * VEC;
+        *reinterpret_cast<V16*>(aa + r * kC + pc) = *reinterpret_cast<const V16*>(&As[r * SC + pc]);
+      }
+    }
+  }
+
   if constexpr (DELTA) {
     // ---- TB = (I + L)^-1 diag(b) (one wave solves), then -Wm = -TB (K 2^G)
     if (wv == 0) prep::unit_lower_inverse_wave<prep::PackedL>(Lf, lane);
@@ -365,19 +387,6 @@ __global__ __launch_bounds__(512) void gla_prep_kernel(
     }
   }
 
-  // ---- copy K^T 2^{G_C - G} and A out as 16-byte pieces
-  T* ktg = wktg + ci * (D * kC);
-  T* aa = wa + ci * (kC * kC);
-  for (int i = tid; i < D * kC / VEC; i += NTH) {
-    const int r = i / (kC / VEC);
-    const int pc = (i % (kC / VEC)) * VEC;
-    *reinterpret_cast<V16*>(ktg + r * kC + pc) = *reinterpret_cast<const V16*>(&KTs[r * SC + pc]);
-  }
-  for (int i = tid; i < kC * kC / VEC; i += NTH) {
-    const int r = i / (kC / VEC);
-    const int pc = (i % (kC / VEC)) * VEC;
-    *reinterpret_cast<V16*>(aa + r * kC + pc) = *reinterpret_cast<const V16*>(&As[r * SC + pc]);
-  }
 }
 
 template <class T, int D, bool DELTA>
